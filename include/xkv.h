@@ -1,0 +1,224 @@
+/*
+ * xkv.h -- C ABI of libxkv: cross-layer low-rank KV-cache compression (xKV)
+ * and Selective Reconstruction (SR) decode attention on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the library computes (sources are the published pages, by title):
+ *
+ *  - Compression of one group side ("xKV: Cross-Layer KV-Cache Compression via
+ *    Aligned Singular Vector Extraction", abstract; the xKV blog explainer,
+ *    section on what xKV does).  The keys (or values) of G adjacent layers are
+ *    concatenated horizontally into X (T x n, n = G*d_kv) and factored once:
+ *    V_r = top-r right singular vectors of X, taken as the top-r eigenvectors
+ *    of the uncentred Gram C = X^T X (KV-CoRE, section 2.A).  The shared token
+ *    basis is A = X V_r (T x r); layer l is rebuilt as A B_l with B = V_r^T
+ *    and B_l its l-th column slice of width d_kv.  Keys are compressed before
+ *    RoPE and rotated after reconstruction (KQ-SVD, section 2, the ShadowKV
+ *    precedent).
+ *  - Selective Reconstruction decode (xKV blog, section on Selective
+ *    Reconstruction): a landmark-guided top-k chunk selector picks chunks per
+ *    KV head, only their rows are rebuilt, and attention runs over those rows
+ *    plus exact sink / local-window / generated rows
+ *    (h = softmax(q K^T / sqrt(d)) V, KQ-SVD section 3.2).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless marked (host).  Matrices are
+ *    row-major with the stated leading dimension (in elements).
+ *  - The caller owns all memory, including the workspace.  The library never
+ *    allocates or frees device memory and keeps no pointer after a call
+ *    returns.  A context owns host-side resources only (pinned staging for
+ *    the Rayleigh-Ritz round trip, host solver threads).
+ *  - Work is enqueued on the caller's HIP stream (passed as void*; NULL is
+ *    the default stream).  Arguments are validated before anything is
+ *    enqueued; a failed validation enqueues nothing.
+ *  - Return codes are XKV_OK or a negative XKV_E* code; xkv_last_error()
+ *    returns a message for the last failure on the calling thread.  No C++
+ *    exception crosses this interface.
+ *  - A context is used by one host thread at a time.
+ *  - dtype XKV_BF16: every KV input and every compressed output is bfloat16;
+ *    XKV_F32: float32.  Queries share the dtype; decode outputs are float32.
+ *  - RoPE is the rotate-half form on pairs (i, i + d/2) with frequency
+ *    theta^(-2i/d); angles are formed in float64.
+ */
+#ifndef XKV_H
+#define XKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  XKV_OK = 0,
+  XKV_EINVAL = -1,        /* bad argument (null, size, stride, alignment)           */
+  XKV_EUNSUPPORTED = -2,  /* shape or device outside what the kernels implement     */
+  XKV_EWORKSPACE = -3,    /* ws_bytes smaller than the matching *_ws_size query      */
+  XKV_EHIP = -4,          /* a HIP runtime call failed (message has the HIP string) */
+  XKV_ENUMERIC = -5,      /* Cholesky breakdown or non-finite value in the iteration */
+  XKV_ENOTCONV = -6       /* subspace error estimate above tol after max_rounds; outputs written */
+};
+
+enum xkv_dtype { XKV_F32 = 0, XKV_BF16 = 1 };
+
+typedef struct xkv_ctx_s* xkv_ctx;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int xkv_version(void);
+
+/* Create a context bound to HIP device `device`; `host_threads` bounds the
+ * threads used for the host Rayleigh-Ritz eigensolves (<= 0: one per side,
+ * at most 16).  On success *out receives the context. */
+int xkv_ctx_create(int device, int host_threads, xkv_ctx* out);
+void xkv_ctx_destroy(xkv_ctx ctx);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* xkv_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Compression of group sides                                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int T;              /* tokens in the prefix; > 0                                    */
+  int G;              /* layers per group; 1..16                                      */
+  int d_kv;           /* columns per layer (n_kv_heads * head_dim); multiple of 8     */
+  int r;              /* rank; 1 <= r <= G*d_kv                                       */
+  int dtype;          /* enum xkv_dtype of the layers and of A, Bt, landmarks        */
+  int n_kv_heads;     /* landmark layout; d_kv == n_kv_heads * head_dim              */
+  int head_dim;       /* even                                                         */
+  int chunk;          /* tokens per chunk; T % chunk == 0 when landmarks are asked   */
+  double rope_theta;  /* RoPE base for the landmarks (10000 in every workload)       */
+  int oversample;     /* p: iteration block k_b = r + p (capped at G*d_kv); < 0 -> r/2 */
+  int fp32_iters;     /* subspace iterations on a float32 copy of C (>= 0)           */
+  int fp64_iters;     /* trailing float64 iterations (>= 1)                          */
+  uint64_t seed;      /* seed of the Gaussian start block                            */
+  double tol;         /* target for the estimated ||P - P_exact||_F of V_r (0 -> 1e-4); see below */
+  int max_rounds;     /* Rayleigh-Ritz rounds before XKV_ENOTCONV (0 -> 8)           */
+} xkv_compress_desc;
+
+typedef struct {
+  const void* const* layers; /* (host) G device pointers; layer l is T x d_kv, row stride ld_layer */
+  long ld_layer;             /* >= d_kv; for bf16 a multiple of 8                                  */
+  void* A;                   /* T x r, row stride r: A = X V_r                                     */
+  void* Bt;                  /* n x r, row stride r: Bt = V_r = B^T; B_l^T = rows [l*d_kv, (l+1)*d_kv) */
+  void* landmarks;           /* G x n_kv_heads x (T/chunk) x head_dim means of post-RoPE keys,   */
+                             /* or NULL (no landmarks: the value side)                           */
+  double* eigvals;           /* (host) r leading Ritz values of C, descending; nullable          */
+  double* Vr64;              /* nullable: n x r float64 copy of V_r before rounding to dtype     */
+  double* stats;             /* (host) nullable, 4 entries: estimated ||P - P_exact||_F, relative */
+                             /* Ritz gap (theta_r - theta_r+1)/theta_r, sweeps, rounds            */
+} xkv_side;
+
+/* Workspace bytes needed by xkv_compress_sides for `n_sides` sides. */
+int xkv_compress_ws_size(const xkv_compress_desc* desc, int n_sides, size_t* bytes);
+
+/* Factor `n_sides` independent group sides of identical shape.
+ * Steps (all sides batched): Gram C = X^T X (bf16 MFMA, float64 totals) ->
+ * block subspace iteration Y = C Q with CholeskyQR orthonormalisation ->
+ * Rayleigh-Ritz H = Q^T C Q (float64) -> host eigensolve of H (plain C, one
+ * thread per side) -> V_r = Q Z_r -> A = X V_r and the landmarks.
+ * Convergence: after each Rayleigh-Ritz round the Ritz residual
+ * R = C V_r - V_r diag(theta) gives the estimate sqrt(2) ||R||_F / (theta_r -
+ * theta_{r+1}) of ||P - P_exact||_F (P = V_r V_r^T); rounds with more float64
+ * sweeps run until it is <= tol or max_rounds is reached (XKV_ENOTCONV, with
+ * every output written).  A block that spans all n columns is exact.
+ * Blocks the calling thread once per round, for the Rayleigh-Ritz round trip;
+ * the projection is enqueued on `stream` when the call returns.
+ * XKV_ENUMERIC if a Cholesky pivot falls below 1e-14 of its column's squared
+ * norm (e.g. X has rank < k_b). */
+int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, int n_sides,
+                       const xkv_side* sides, void* ws, size_t ws_bytes, void* stream);
+
+/* One group side: xkv_compress_sides with n_sides = 1. */
+int xkv_compress_group(xkv_ctx ctx, const xkv_compress_desc* desc, const xkv_side* side,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Selective Reconstruction decode (one layer, one step, `batch` sequences)  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int batch;            /* sequences                                                      */
+  int n_q_heads;        /* multiple of n_kv_heads (query head j uses KV head j / (H_q/H_kv)) */
+  int n_kv_heads;
+  int head_dim;         /* 64 or 128                                                      */
+  int T;                /* compressed prefix length; T % chunk == 0                       */
+  int n_gen;            /* generated tokens in the tail, including the current one;     */
+                        /* query position p = T + n_gen - 1 (p = T when n_gen == 0)       */
+  int chunk;            /* 8..64, power of two                                            */
+  int top_k;            /* chunks kept per KV head (all candidates if larger)            */
+  int n_sink;           /* exact rows [0, n_sink)                                          */
+  int n_local;          /* exact rows [T - n_local, T); candidates are chunks c with       */
+                        /* c*chunk < T - n_local                                          */
+  int r_k, r_v;         /* ranks of the key / value bases; r_v == 0: values are exact     */
+  int dtype;            /* enum xkv_dtype of q, A, Bt, landmarks, tails, V_full            */
+  float scale;          /* softmax scale, usually 1/sqrt(head_dim)                        */
+  double rope_theta;
+
+  const void* q;        /* batch x n_q_heads x head_dim, pre-RoPE, at position p          */
+  const void* A_k;      /* per sequence T x r_k, row stride ld_A_k                         */
+  long ld_A_k, bstride_A_k;
+  const void* Bt_k;     /* per sequence: this layer's d_kv x r_k rows of Bt, row stride ld_Bt_k */
+  long ld_Bt_k, bstride_Bt_k;
+  const void* A_v;      /* as A_k for values (r_v > 0)                                     */
+  long ld_A_v, bstride_A_v;
+  const void* Bt_v;
+  long ld_Bt_v, bstride_Bt_v;
+  const void* V_full;   /* r_v == 0: per sequence T x d_kv exact values, row stride ld_V  */
+  long ld_V, bstride_V;
+  const void* landmarks;/* per sequence n_kv_heads x (T/chunk) x head_dim                 */
+  long bstride_lm;
+  void* k_tail;         /* per sequence (n_sink + n_local + max_gen) x d_kv pre-RoPE rows: */
+  void* v_tail;         /* sink positions, then positions T-n_local..T-1, then T, T+1, ...  */
+  long ld_tail, bstride_tail;
+  const void* k_new;    /* nullable: per sequence d_kv row written to tail row           */
+  const void* v_new;    /* n_sink + n_local + n_gen - 1 before attention (the new token)  */
+  long bstride_new;
+  float* out;           /* batch x n_q_heads x head_dim                                   */
+  int* sel;             /* batch x n_kv_heads x top_k selected chunk ids, ascending; unused */
+                        /* slots (fewer candidates than top_k) are -1                      */
+} xkv_sr_args;
+
+/* Workspace bytes for xkv_sr_decode / xkv_sr_select / xkv_sr_attend. */
+int xkv_sr_ws_size(const xkv_sr_args* args, size_t* bytes);
+
+/* Append the new token (if given), score every candidate chunk against the
+ * landmarks, and write the top-k chunk ids of each KV head to args->sel. */
+int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Rebuild the selected rows (A rows x B_l, then RoPE for keys), attend over
+ * them and the exact rows with split-K online softmax, merge, write args->out.
+ * Reads args->sel as written by xkv_sr_select. */
+int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* xkv_sr_select followed by xkv_sr_attend. */
+int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Component entry points used by the parity tests                           */
+/* ------------------------------------------------------------------------ */
+
+/* Gram of the concatenated layers: C (n x n float64, row stride n) = X^T X,
+ * computed by the same kernel as xkv_compress_sides.  For bf16 the layer
+ * pointers and ld_layer must be 16-byte aligned. */
+int xkv_gram(const void* const* layers, long ld_layer, int T, int G, int d_kv, int dtype,
+             double* C, void* stream);
+
+/* Top-k of each of `rows` score rows (float32, row stride ld) over the first
+ * n_cand entries: ascending ids of the k largest, ties to the lower id, -1
+ * padding; the same kernel as xkv_sr_select.  n_cand <= 16384. */
+int xkv_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, void* stream);
+
+/* Host symmetric eigensolver used for the Rayleigh-Ritz step (plain C,
+ * Householder tridiagonalisation + implicit QR with Wilkinson shifts).
+ * H (host, n x n, row stride n, symmetric) is not modified.  Writes the nvec
+ * largest eigenvalues to w (host, descending) and their eigenvectors as the
+ * columns of Z (host, n x nvec, row stride nvec).  Runs without a GPU. */
+int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XKV_H */

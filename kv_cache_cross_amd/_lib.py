@@ -1,0 +1,238 @@
+"""ctypes binding of libxkv (argument marshalling only).
+
+Every computation runs in the HIP kernels of libxkv.so (or, for the
+Rayleigh-Ritz eigensolve, in its plain-C host routine).  Torch tensors only
+provide device memory and the stream.  There is no fallback: if the library
+is missing or was built for another GPU, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libxkv.so")
+
+XKV_OK, XKV_EINVAL, XKV_EUNSUPPORTED, XKV_EWORKSPACE, XKV_EHIP, XKV_ENUMERIC, XKV_ENOTCONV = 0, -1, -2, -3, -4, -5, -6
+XKV_F32, XKV_BF16 = 0, 1
+_CODES = {-1: "XKV_EINVAL", -2: "XKV_EUNSUPPORTED", -3: "XKV_EWORKSPACE", -4: "XKV_EHIP", -5: "XKV_ENUMERIC",
+          -6: "XKV_ENOTCONV"}
+
+
+class XkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class CompressDesc(C.Structure):
+    _fields_ = [("T", C.c_int), ("G", C.c_int), ("d_kv", C.c_int), ("r", C.c_int), ("dtype", C.c_int),
+                ("n_kv_heads", C.c_int), ("head_dim", C.c_int), ("chunk", C.c_int),
+                ("rope_theta", C.c_double), ("oversample", C.c_int), ("fp32_iters", C.c_int),
+                ("fp64_iters", C.c_int), ("seed", C.c_uint64), ("tol", C.c_double), ("max_rounds", C.c_int)]
+
+
+class Side(C.Structure):
+    _fields_ = [("layers", C.POINTER(C.c_void_p)), ("ld_layer", C.c_long), ("A", C.c_void_p),
+                ("Bt", C.c_void_p), ("landmarks", C.c_void_p), ("eigvals", C.POINTER(C.c_double)),
+                ("Vr64", C.c_void_p), ("stats", C.POINTER(C.c_double))]
+
+
+class SrArgs(C.Structure):
+    _fields_ = [("batch", C.c_int), ("n_q_heads", C.c_int), ("n_kv_heads", C.c_int), ("head_dim", C.c_int),
+                ("T", C.c_int), ("n_gen", C.c_int), ("chunk", C.c_int), ("top_k", C.c_int),
+                ("n_sink", C.c_int), ("n_local", C.c_int), ("r_k", C.c_int), ("r_v", C.c_int),
+                ("dtype", C.c_int), ("scale", C.c_float), ("rope_theta", C.c_double),
+                ("q", C.c_void_p),
+                ("A_k", C.c_void_p), ("ld_A_k", C.c_long), ("bstride_A_k", C.c_long),
+                ("Bt_k", C.c_void_p), ("ld_Bt_k", C.c_long), ("bstride_Bt_k", C.c_long),
+                ("A_v", C.c_void_p), ("ld_A_v", C.c_long), ("bstride_A_v", C.c_long),
+                ("Bt_v", C.c_void_p), ("ld_Bt_v", C.c_long), ("bstride_Bt_v", C.c_long),
+                ("V_full", C.c_void_p), ("ld_V", C.c_long), ("bstride_V", C.c_long),
+                ("landmarks", C.c_void_p), ("bstride_lm", C.c_long),
+                ("k_tail", C.c_void_p), ("v_tail", C.c_void_p), ("ld_tail", C.c_long), ("bstride_tail", C.c_long),
+                ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("bstride_new", C.c_long),
+                ("out", C.c_void_p), ("sel", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libxkv (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -m kv_cache_cross_amd.build)")
+        L = C.CDLL(LIB_PATH)
+        vp, i, l, sz = C.c_void_p, C.c_int, C.c_long, C.c_size_t
+        L.xkv_version.restype = i
+        L.xkv_last_error.restype = C.c_char_p
+        L.xkv_ctx_create.argtypes = [i, i, C.POINTER(vp)]
+        L.xkv_ctx_destroy.argtypes = [vp]
+        L.xkv_ctx_destroy.restype = None
+        L.xkv_compress_ws_size.argtypes = [C.POINTER(CompressDesc), i, C.POINTER(sz)]
+        L.xkv_compress_sides.argtypes = [vp, C.POINTER(CompressDesc), i, C.POINTER(Side), vp, sz, vp]
+        L.xkv_compress_group.argtypes = [vp, C.POINTER(CompressDesc), C.POINTER(Side), vp, sz, vp]
+        L.xkv_sr_ws_size.argtypes = [C.POINTER(SrArgs), C.POINTER(sz)]
+        for name in ("xkv_sr_select", "xkv_sr_attend", "xkv_sr_decode"):
+            getattr(L, name).argtypes = [vp, C.POINTER(SrArgs), vp, sz, vp]
+        L.xkv_gram.argtypes = [C.POINTER(vp), l, i, i, i, i, vp, vp]
+        L.xkv_topk.argtypes = [vp, i, i, l, i, vp, vp]
+        L.xkv_host_eigh.argtypes = [i, vp, i, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != XKV_OK:
+        raise XkvError(rc, lib().xkv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return XKV_BF16
+    if t.dtype == torch.float32:
+        return XKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+class Context:
+    """Host-side resources of the library, bound to one HIP device."""
+
+    def __init__(self, device: int = 0, host_threads: int = 0):
+        self.handle = C.c_void_p()
+        _check(lib().xkv_ctx_create(device, host_threads, C.byref(self.handle)))
+        self.device = device
+
+    def close(self):
+        if self.handle:
+            lib().xkv_ctx_destroy(self.handle)
+            self.handle = C.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def make_desc(*, T, G, d_kv, r, dtype, n_kv_heads, head_dim, chunk=8, rope_theta=10000.0,
+              oversample=-1, fp32_iters=3, fp64_iters=1, seed=0, tol=0.0, max_rounds=0) -> CompressDesc:
+    return CompressDesc(T, G, d_kv, r, dtype, n_kv_heads, head_dim, chunk, rope_theta, oversample,
+                        fp32_iters, fp64_iters, seed, tol, max_rounds)
+
+
+def compress_ws_size(desc: CompressDesc, n_sides: int) -> int:
+    n = C.c_size_t()
+    _check(lib().xkv_compress_ws_size(C.byref(desc), n_sides, C.byref(n)))
+    return n.value
+
+
+def compress_sides(ctx: Context, desc: CompressDesc, sides, ws: torch.Tensor, stream=None):
+    """sides: list of dicts with 'layers' (list of G tensors, T x d_kv), 'A' (T x r), 'Bt' (n x r),
+    optional 'landmarks' (G x H_kv x T/chunk x d) and 'Vr64' (n x r float64).  Returns the r leading
+    Ritz values per side and per-side stats (error estimate, relative gap, sweeps, rounds)."""
+    S = len(sides)
+    arr = (Side * S)()
+    keep = []
+    evals = [np.zeros(desc.r, dtype=np.float64) for _ in range(S)]
+    stats = [np.zeros(4, dtype=np.float64) for _ in range(S)]
+    for s, sd in enumerate(sides):
+        layers = sd["layers"]
+        ptrs = (C.c_void_p * len(layers))(*[t.data_ptr() for t in layers])
+        keep.append(ptrs)
+        arr[s].layers = C.cast(ptrs, C.POINTER(C.c_void_p))
+        arr[s].ld_layer = layers[0].stride(0)
+        arr[s].A = sd["A"].data_ptr()
+        arr[s].Bt = sd["Bt"].data_ptr()
+        arr[s].landmarks = sd["landmarks"].data_ptr() if sd.get("landmarks") is not None else None
+        arr[s].eigvals = evals[s].ctypes.data_as(C.POINTER(C.c_double))
+        arr[s].Vr64 = sd["Vr64"].data_ptr() if sd.get("Vr64") is not None else None
+        arr[s].stats = stats[s].ctypes.data_as(C.POINTER(C.c_double))
+    _check(lib().xkv_compress_sides(ctx.handle, C.byref(desc), S, arr, _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+    return evals, stats
+
+
+def sr_args(**kw) -> SrArgs:
+    """Build an SrArgs from keyword arguments; tensors become device pointers."""
+    a = SrArgs()
+    for name, _ in SrArgs._fields_:
+        if name not in kw:
+            continue
+        v = kw[name]
+        if isinstance(v, torch.Tensor):
+            v = v.data_ptr()
+        setattr(a, name, v)
+    return a
+
+
+def sr_ws_size(args: SrArgs) -> int:
+    n = C.c_size_t()
+    _check(lib().xkv_sr_ws_size(C.byref(args), C.byref(n)))
+    return n.value
+
+
+def _sr_call(fn, ctx, args, ws, stream):
+    _check(fn(ctx.handle, C.byref(args), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sr_select(ctx, args, ws, stream=None):
+    _sr_call(lib().xkv_sr_select, ctx, args, ws, stream)
+
+
+def sr_attend(ctx, args, ws, stream=None):
+    _sr_call(lib().xkv_sr_attend, ctx, args, ws, stream)
+
+
+def sr_decode(ctx, args, ws, stream=None):
+    _sr_call(lib().xkv_sr_decode, ctx, args, ws, stream)
+
+
+def gram(layers, stream=None) -> torch.Tensor:
+    """X^T X of the horizontally concatenated layers (float64, n x n) on the layers' device."""
+    G = len(layers)
+    T, d_kv = layers[0].shape
+    out = torch.empty((G * d_kv, G * d_kv), dtype=torch.float64, device=layers[0].device)
+    ptrs = (C.c_void_p * G)(*[t.data_ptr() for t in layers])
+    _check(lib().xkv_gram(ptrs, layers[0].stride(0), T, G, d_kv, _dtype_code(layers[0]), _ptr(out),
+                          _stream(stream)))
+    return out
+
+
+def topk(scores: torch.Tensor, n_cand: int, k: int, stream=None) -> torch.Tensor:
+    rows = scores.shape[0]
+    sel = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _check(lib().xkv_topk(_ptr(scores), rows, n_cand, scores.stride(0), k, _ptr(sel), _stream(stream)))
+    return sel
+
+
+def host_eigh(H: np.ndarray, nvec: int):
+    """Largest nvec eigenpairs of symmetric H with the library's plain-C solver (no GPU needed)."""
+    H = np.ascontiguousarray(H, dtype=np.float64)
+    n = H.shape[0]
+    w = np.zeros(nvec)
+    Z = np.zeros((n, nvec))
+    _check(lib().xkv_host_eigh(n, H.ctypes.data, nvec, w.ctypes.data, Z.ctypes.data))
+    return w, Z

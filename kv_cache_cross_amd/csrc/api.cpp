@@ -1,0 +1,652 @@
+// C ABI of libxkv: argument validation, workspace layout and the order of
+// kernel launches.  Every numeric step runs in the HIP kernels of this
+// directory or, for the Rayleigh-Ritz eigensolve only, in host_eigh.c.
+#include "../../include/xkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "decode_params.h"
+#include "xkv_kernels.h"
+
+extern "C" int xkv_eigh_desc_impl(int n, const double* H, int nvec, double* w, double* Z);
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define XKV_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess) return fail(XKV_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Sequential carving of a workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+}  // namespace
+
+struct xkv_ctx_s {
+  int device = 0;
+  int host_threads = 16;
+  double* pin = nullptr;        // pinned staging for H (down) and Z (up)
+  size_t pin_doubles = 0;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+};
+
+extern "C" {
+
+int xkv_version(void) { return 100; }
+
+const char* xkv_last_error(void) { return g_err.c_str(); }
+
+int xkv_ctx_create(int device, int host_threads, xkv_ctx* out) {
+  if (!out) return fail(XKV_EINVAL, "xkv_ctx_create: out is NULL");
+  int n = 0;
+  XKV_HIP(hipGetDeviceCount(&n));
+  if (device < 0 || device >= n) return fail(XKV_EINVAL, "xkv_ctx_create: device %d of %d", device, n);
+  hipDeviceProp_t prop;
+  XKV_HIP(hipGetDeviceProperties(&prop, device));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(XKV_EUNSUPPORTED, "xkv_ctx_create: device %d is %s; only gfx950 is supported", device,
+                prop.gcnArchName);
+  xkv_ctx c = new xkv_ctx_s();
+  c->device = device;
+  c->host_threads = host_threads > 0 ? host_threads : 16;
+  XKV_HIP(hipSetDevice(device));
+  XKV_HIP(hipEventCreateWithFlags(&c->upload_done, hipEventDisableTiming));
+  *out = c;
+  return XKV_OK;
+}
+
+void xkv_ctx_destroy(xkv_ctx ctx) {
+  if (!ctx) return;
+  if (ctx->upload_done) {
+    (void)hipEventSynchronize(ctx->upload_done);
+    (void)hipEventDestroy(ctx->upload_done);
+  }
+  if (ctx->pin) (void)hipHostFree(ctx->pin);
+  delete ctx;
+}
+
+int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z) {
+  if (n <= 0 || !H || !w || !Z || nvec <= 0 || nvec > n)
+    return fail(XKV_EINVAL, "xkv_host_eigh: bad arguments (n=%d, nvec=%d)", n, nvec);
+  std::vector<double> all(n);
+  const int rc = xkv_eigh_desc_impl(n, H, nvec, all.data(), Z);
+  if (rc == 0) std::memcpy(w, all.data(), nvec * sizeof(double));
+  if (rc == -1) return fail(XKV_EINVAL, "xkv_host_eigh: out of host memory");
+  if (rc != 0) return fail(XKV_ENUMERIC, "xkv_host_eigh: QR iteration did not converge");
+  return XKV_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Compression
+// ---------------------------------------------------------------------------
+namespace {
+
+struct CompressPlan {
+  int T, G, d_kv, n, r, kb, bf16, fp32_iters, fp64_iters, nblk;
+};
+
+int plan_compress(const xkv_compress_desc* d, int n_sides, CompressPlan* p) {
+  if (!d) return fail(XKV_EINVAL, "compress: desc is NULL");
+  if (n_sides <= 0) return fail(XKV_EINVAL, "compress: n_sides must be positive");
+  if (d->T <= 0 || d->G <= 0 || d->G > 16 || d->d_kv <= 0 || d->d_kv % 8)
+    return fail(XKV_EINVAL, "compress: need T > 0, 1 <= G <= 16, d_kv a positive multiple of 8");
+  if (d->dtype != XKV_F32 && d->dtype != XKV_BF16) return fail(XKV_EINVAL, "compress: unknown dtype");
+  const int n = d->G * d->d_kv;
+  if (d->r <= 0 || d->r > n) return fail(XKV_EINVAL, "compress: rank %d outside [1, %d]", d->r, n);
+  if (d->fp32_iters < 0 || d->fp64_iters < 1) return fail(XKV_EINVAL, "compress: need fp32_iters >= 0, fp64_iters >= 1");
+  if (d->n_kv_heads <= 0 || d->head_dim <= 0 || d->head_dim % 2 || d->n_kv_heads * d->head_dim != d->d_kv)
+    return fail(XKV_EINVAL, "compress: d_kv must equal n_kv_heads * head_dim (even head_dim)");
+  if (d->head_dim > 512 || 256 % (d->head_dim / 2) != 0)
+    return fail(XKV_EUNSUPPORTED, "compress: head_dim must be 2..512 with head_dim/2 dividing 256");
+  if (d->chunk <= 0) return fail(XKV_EINVAL, "compress: chunk must be positive");
+  if (!(d->tol >= 0.0) || d->max_rounds < 0) return fail(XKV_EINVAL, "compress: tol and max_rounds must be >= 0");
+  const int p_over = d->oversample < 0 ? d->r / 2 : d->oversample;
+  p->T = d->T;
+  p->G = d->G;
+  p->d_kv = d->d_kv;
+  p->n = n;
+  p->r = d->r;
+  p->kb = std::min(n, d->r + p_over);
+  p->bf16 = d->dtype == XKV_BF16;
+  p->fp32_iters = d->fp32_iters;
+  p->fp64_iters = d->fp64_iters;
+  p->nblk = (p->kb + 63) / 64;
+  return XKV_OK;
+}
+
+struct CompressWs {
+  double* C64; float* C32;
+  float* Q32; float* Y32;
+  double* Q64; double* Y64;
+  double* W; double* L; double* Dinv;
+  double* H; double* Z; double* Vr;
+  double* wdiag;
+  double* YZ; double* theta; double* res2;
+  void* VrT;
+  int* info;
+  size_t bytes;
+};
+
+CompressWs carve_compress(void* ws, const CompressPlan& p, int S) {
+  Carver c(ws);
+  CompressWs w;
+  const size_t nn = (size_t)p.n * p.n, nk = (size_t)p.n * p.kb, kk = (size_t)p.kb * p.kb;
+  w.C64 = c.take<double>(S * nn);
+  w.C32 = p.fp32_iters > 0 ? c.take<float>(S * nn) : nullptr;
+  w.Q32 = c.take<float>(S * nk);
+  w.Y32 = p.fp32_iters > 0 ? c.take<float>(S * nk) : nullptr;
+  w.Q64 = c.take<double>(S * nk);
+  w.Y64 = c.take<double>(S * nk);
+  w.W = c.take<double>(S * kk);
+  w.L = c.take<double>(S * kk);
+  w.Dinv = c.take<double>((size_t)S * p.nblk * 64 * 64);
+  w.H = c.take<double>(S * kk);
+  w.Z = c.take<double>((size_t)S * p.kb * p.r);
+  w.Vr = c.take<double>((size_t)S * p.n * p.r);
+  w.wdiag = c.take<double>((size_t)S * p.kb);
+  w.YZ = c.take<double>((size_t)S * p.n * p.r);
+  w.theta = c.take<double>((size_t)S * p.r);
+  w.res2 = c.take<double>((size_t)S * p.r);
+  w.VrT = c.take<float>((size_t)S * p.n * p.r);
+  w.info = c.take<int>(S);
+  w.bytes = c.off;
+  return w;
+}
+
+xkv::GemmDesc gdesc(int M, int N, int K, int ta, int tb, int tA, int tB, int tC, const void* A, long lda, long sA,
+                    const void* B, long ldb, long sB, void* C, long ldc, long sC, double alpha, double beta,
+                    int batch) {
+  xkv::GemmDesc g;
+  g.M = M; g.N = N; g.K = K; g.ta = ta; g.tb = tb;
+  g.typeA = tA; g.typeB = tB; g.typeC = tC; g.acc = xkv::GF64;
+  g.A = A; g.lda = lda; g.sA = sA;
+  g.B = B; g.ldb = ldb; g.sB = sB;
+  g.C = C; g.ldc = ldc; g.sC = sC;
+  g.alpha = alpha; g.beta = beta; g.batch = batch;
+  return g;
+}
+
+#define XKV_K(call)                                                                        \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(XKV_EHIP, "kernel launch %s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+// CholeskyQR pass: Q = Y R^-1 with Y^T Y = R^T R (R = L^T).  Y is overwritten.
+int cholqr(const CompressPlan& p, const CompressWs& w, int S, void* Y, int tY, void* Q, int tQ, hipStream_t st) {
+  using namespace xkv;
+  const int n = p.n, kb = p.kb;
+  const long nk = (long)n * kb, kk = (long)kb * kb, dstride = (long)p.nblk * 4096;
+  XKV_K(gemm(gdesc(kb, kb, n, 1, 0, tY, tY, GF64, Y, kb, nk, Y, kb, nk, w.W, kb, kk, 1.0, 0.0, S), st));
+  XKV_K(launch_copy_diag(w.W, kb, kk, w.wdiag, kb, kb, S, st));
+  for (int jb = 0; jb < p.nblk; ++jb) {
+    const int j0 = jb * 64, nbj = std::min(64, kb - j0), rem = kb - j0 - nbj;
+    double* Dj = w.Dinv + (long)jb * 4096;
+    // float32 sweeps clamp tiny pivots; float64 sweeps report them as a breakdown
+    XKV_K(launch_potrf_diag(w.W, kb, kk, w.L, kb, kk, Dj, dstride, j0, nbj, w.wdiag, kb, tY == GF32, S, w.info,
+                            st));
+    if (rem > 0) {
+      const long off = (long)(j0 + nbj) * kb + j0;
+      XKV_K(gemm(gdesc(rem, nbj, nbj, 0, 1, GF64, GF64, GF64, w.W + off, kb, kk, Dj, 64, dstride, w.L + off, kb, kk,
+                       1.0, 0.0, S), st));
+      const long toff = (long)(j0 + nbj) * kb + (j0 + nbj);
+      XKV_K(gemm(gdesc(rem, rem, nbj, 0, 1, GF64, GF64, GF64, w.L + off, kb, kk, w.L + off, kb, kk, w.W + toff, kb,
+                       kk, -1.0, 1.0, S), st));
+    }
+  }
+  const size_t esY = tY == GF64 ? 8 : 4, esQ = tQ == GF64 ? 8 : 4;
+  for (int jb = 0; jb < p.nblk; ++jb) {
+    const int j0 = jb * 64, nbj = std::min(64, kb - j0);
+    void* Yj = (char*)Y + j0 * esY;
+    void* Qj = (char*)Q + j0 * esQ;
+    if (j0 > 0)
+      XKV_K(gemm(gdesc(n, nbj, j0, 0, 1, tQ, GF64, tY, Q, kb, nk, w.L + (long)j0 * kb, kb, kk, Yj, kb, nk, -1.0, 1.0,
+                       S), st));
+    XKV_K(gemm(gdesc(n, nbj, nbj, 0, 1, tY, GF64, tQ, Yj, kb, nk, w.Dinv + (long)jb * 4096, 64, dstride, Qj, kb, nk,
+                     1.0, 0.0, S), st));
+  }
+  return XKV_OK;
+}
+
+}  // namespace
+
+extern "C" int xkv_compress_ws_size(const xkv_compress_desc* desc, int n_sides, size_t* bytes) {
+  if (!bytes) return fail(XKV_EINVAL, "xkv_compress_ws_size: bytes is NULL");
+  CompressPlan p;
+  int rc = plan_compress(desc, n_sides, &p);
+  if (rc) return rc;
+  *bytes = carve_compress(nullptr, p, n_sides).bytes;
+  return XKV_OK;
+}
+
+extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, int n_sides, const xkv_side* sides,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  using namespace xkv;
+  if (!ctx) return fail(XKV_EINVAL, "compress: ctx is NULL");
+  CompressPlan p;
+  int rc = plan_compress(desc, n_sides, &p);
+  if (rc) return rc;
+  if (!sides) return fail(XKV_EINVAL, "compress: sides is NULL");
+  const int S = n_sides;
+  const size_t need = carve_compress(nullptr, p, S).bytes;
+  if (!ws || ws_bytes < need) return fail(XKV_EWORKSPACE, "compress: workspace %zu bytes < %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(XKV_EINVAL, "compress: workspace must be 16-byte aligned");
+  bool any_lm = false;
+  for (int s = 0; s < S; ++s) {
+    const xkv_side& sd = sides[s];
+    if (!sd.layers || !sd.A || !sd.Bt) return fail(XKV_EINVAL, "compress: side %d has a NULL pointer", s);
+    if (sd.ld_layer < p.d_kv) return fail(XKV_EINVAL, "compress: side %d ld_layer %ld < d_kv", s, sd.ld_layer);
+    if (sd.ld_layer != sides[0].ld_layer) return fail(XKV_EINVAL, "compress: every side must share ld_layer");
+    if (p.bf16 && sd.ld_layer % 8) return fail(XKV_EINVAL, "compress: bf16 ld_layer must be a multiple of 8");
+    for (int l = 0; l < p.G; ++l) {
+      if (!sd.layers[l]) return fail(XKV_EINVAL, "compress: side %d layer %d is NULL", s, l);
+      if (!aligned16(sd.layers[l])) return fail(XKV_EINVAL, "compress: layer pointers must be 16-byte aligned");
+    }
+    if (sd.landmarks) {
+      any_lm = true;
+      if (p.T % desc->chunk) return fail(XKV_EINVAL, "compress: landmarks need T %% chunk == 0");
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  XKV_HIP(hipSetDevice(ctx->device));
+  CompressWs w = carve_compress(ws, p, S);
+  const int n = p.n, kb = p.kb, r = p.r;
+  const long nn = (long)n * n, nk = (long)n * kb, kk = (long)kb * kb;
+
+  XKV_K(launch_zero_i32(w.info, S, st));
+  // 1. Gram of every side (batched, at most kMaxPtrs layer pointers per launch).
+  const int per = std::max(1, kMaxPtrs / p.G);
+  for (int s0 = 0; s0 < S; s0 += per) {
+    const int cnt = std::min(per, S - s0);
+    PtrTable tab{};
+    for (int s = 0; s < cnt; ++s)
+      for (int l = 0; l < p.G; ++l) tab.p[s * p.G + l] = sides[s0 + s].layers[l];
+    double* C = w.C64 + s0 * nn;
+    float* C32 = w.C32 ? w.C32 + s0 * nn : nullptr;
+    if (p.bf16) XKV_K(launch_gram_bf16(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
+    else XKV_K(launch_gram_f32(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
+  }
+  // 2. Block subspace iteration: float32 sweeps on a float32 copy of C, then float64
+  //    sweeps (CholeskyQR, CholeskyQR2 on the last sweep of a round).
+  XKV_K(launch_init_q(w.Q32, n, kb, nk, S, desc->seed, st));
+  for (int it = 0; it < p.fp32_iters; ++it) {
+    GemmDesc cq = gdesc(n, kb, n, 0, 0, GF32, GF32, GF32, w.C32, n, nn, w.Q32, kb, nk, w.Y32, kb, nk, 1.0, 0.0, S);
+    cq.acc = GF32;   // float32 matrix cores for the float32 iterations
+    XKV_K(gemm(cq, st));
+    rc = cholqr(p, w, S, w.Y32, GF32, w.Q32, GF32, st);
+    if (rc) return rc;
+  }
+  void* Qcur = w.Q32;
+  int tQ = GF32;
+  double* Qa = w.Q64;
+  double* Ya = w.Y64;
+  auto fp64_sweeps = [&](int count) -> int {
+    for (int it = 0; it < count; ++it) {
+      XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, tQ, GF64, w.C64, n, nn, Qcur, kb, nk, Ya, kb, nk, 1.0, 0.0, S), st));
+      int e = cholqr(p, w, S, Ya, GF64, Qa, GF64, st);       // Qa = orth(Ya)
+      if (e) return e;
+      if (it + 1 == count) {
+        e = cholqr(p, w, S, Qa, GF64, Ya, GF64, st);         // second pass: Ya = orth(Qa)
+        if (e) return e;
+        std::swap(Qa, Ya);                                   // Qa holds the basis
+      }
+      Qcur = Qa;
+      tQ = GF64;
+    }
+    return XKV_OK;
+  };
+  rc = fp64_sweeps(p.fp64_iters);
+  if (rc) return rc;
+  int total_iters = p.fp32_iters + p.fp64_iters;
+
+  // Pinned staging: H (down), Z and Ritz values (up), residual norms and info (down).
+  const size_t need_pin = (size_t)S * kk + (size_t)S * kb * r + (size_t)S * r + (size_t)S * r + (size_t)S;
+  if (ctx->upload_pending) {
+    XKV_HIP(hipEventSynchronize(ctx->upload_done));
+    ctx->upload_pending = false;
+  }
+  if (ctx->pin_doubles < need_pin) {
+    if (ctx->pin) XKV_HIP(hipHostFree(ctx->pin));
+    ctx->pin = nullptr;
+    ctx->pin_doubles = 0;
+    XKV_HIP(hipHostMalloc((void**)&ctx->pin, need_pin * sizeof(double), hipHostMallocDefault));
+    ctx->pin_doubles = need_pin;
+  }
+  double* hH = ctx->pin;
+  double* hZ = hH + (size_t)S * kk;
+  double* hTheta = hZ + (size_t)S * kb * r;
+  double* hRes = hTheta + (size_t)S * r;
+  int* hinfo = (int*)(hRes + (size_t)S * r);
+
+  // 3. Rayleigh-Ritz rounds.  After each, the Ritz residual R = (C Q) Z - V_r diag(theta)
+  //    bounds the subspace error: ||sin angle(V_r, exact)||_F <= ||R||_F / (theta_r - lambda_{r+1}),
+  //    with lambda_{r+1} estimated by theta_{r+1}.  Unconverged rounds add float64 sweeps.
+  const double tol = desc->tol > 0 ? desc->tol : 1e-4;
+  const int max_rounds = desc->max_rounds > 0 ? desc->max_rounds : 8;
+  std::vector<std::vector<double>> evals(S, std::vector<double>(kb));
+  std::vector<double> est(S, 0.0), relgap(S, 0.0);
+  int rounds = 0;
+  bool converged = false;
+  const int nthr = std::max(1, std::min(S, ctx->host_threads));
+  for (;;) {
+    ++rounds;
+    XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, GF64, GF64, w.C64, n, nn, Qa, kb, nk, Ya, kb, nk, 1.0, 0.0, S), st));
+    XKV_K(gemm(gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, Qa, kb, nk, Ya, kb, nk, w.H, kb, kk, 1.0, 0.0, S), st));
+    XKV_HIP(hipMemcpyAsync(hH, w.H, (size_t)S * kk * sizeof(double), hipMemcpyDeviceToHost, st));
+    XKV_HIP(hipMemcpyAsync(hinfo, w.info, S * sizeof(int), hipMemcpyDeviceToHost, st));
+    XKV_HIP(hipStreamSynchronize(st));
+    for (int s = 0; s < S; ++s)
+      if (hinfo[s]) return fail(XKV_ENUMERIC, "compress: Cholesky breakdown on side %d (rank of X below %d?)", s, kb);
+    for (size_t i = 0; i < (size_t)S * kk; ++i)
+      if (!std::isfinite(hH[i])) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix");
+
+    // Host eigensolves, one thread per side (bounded by ctx->host_threads).
+    std::vector<int> erc(S, 0);
+    auto worker = [&](int t0) {
+      for (int s = t0; s < S; s += nthr)
+        erc[s] = xkv_eigh_desc_impl(kb, hH + (size_t)s * kk, r, evals[s].data(), hZ + (size_t)s * kb * r);
+    };
+    if (nthr == 1) {
+      worker(0);
+    } else {
+      std::vector<std::thread> pool;
+      for (int t = 0; t < nthr; ++t) pool.emplace_back(worker, t);
+      for (auto& th : pool) th.join();
+    }
+    for (int s = 0; s < S; ++s) {
+      if (erc[s]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", s, erc[s]);
+      std::memcpy(hTheta + (size_t)s * r, evals[s].data(), r * sizeof(double));
+    }
+    XKV_HIP(hipMemcpyAsync(w.Z, hZ, (size_t)S * kb * r * sizeof(double), hipMemcpyHostToDevice, st));
+    XKV_HIP(hipMemcpyAsync(w.theta, hTheta, (size_t)S * r * sizeof(double), hipMemcpyHostToDevice, st));
+    XKV_HIP(hipEventRecord(ctx->upload_done, st));
+    ctx->upload_pending = true;
+
+    // V_r = Q Z and the residual of every Ritz pair.
+    XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, Qa, kb, nk, w.Z, r, (long)kb * r, w.Vr, r, (long)n * r, 1.0,
+                     0.0, S), st));
+    XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, Ya, kb, nk, w.Z, r, (long)kb * r, w.YZ, r, (long)n * r, 1.0,
+                     0.0, S), st));
+    XKV_K(launch_ritz_residual(w.YZ, w.Vr, w.theta, n, r, w.res2, S, st));
+    XKV_HIP(hipMemcpyAsync(hRes, w.res2, (size_t)S * r * sizeof(double), hipMemcpyDeviceToHost, st));
+    XKV_HIP(hipStreamSynchronize(st));
+    ctx->upload_pending = false;
+    converged = true;
+    for (int s = 0; s < S; ++s) {
+      double r2 = 0.0;
+      for (int i = 0; i < r; ++i) r2 += hRes[(size_t)s * r + i];
+      const double th_r = evals[s][r - 1];
+      const double gap = (r < kb) ? th_r - evals[s][r] : th_r;
+      relgap[s] = th_r > 0 ? gap / th_r : 0.0;
+      // A block that spans the whole space gives the exact eigenvectors.
+      est[s] = (kb == n) ? 0.0 : (gap > 0 ? std::sqrt(2.0 * r2) / gap : INFINITY);
+      if (!(est[s] <= tol)) converged = false;
+    }
+    if (converged || rounds >= max_rounds) break;
+    rc = fp64_sweeps(p.fp32_iters + p.fp64_iters);
+    if (rc) return rc;
+    total_iters += p.fp32_iters + p.fp64_iters;
+  }
+  for (int s = 0; s < S; ++s) {
+    if (sides[s].eigvals) std::memcpy(sides[s].eigvals, evals[s].data(), r * sizeof(double));
+    if (sides[s].stats) {
+      sides[s].stats[0] = est[s];
+      sides[s].stats[1] = relgap[s];
+      sides[s].stats[2] = total_iters;
+      sides[s].stats[3] = rounds;
+    }
+  }
+
+  // 4. The stored Bt = V_r and the projection A = X V_r.
+  for (int s = 0; s < S; ++s)
+    if (sides[s].Vr64)
+      XKV_HIP(hipMemcpyAsync(sides[s].Vr64, w.Vr + (long)s * n * r, (size_t)n * r * sizeof(double),
+                             hipMemcpyDeviceToDevice, st));
+  const long nr = (long)n * r;
+  for (int s0 = 0; s0 < S; s0 += per) {
+    const int cnt = std::min(per, S - s0);
+    PtrTable bt{}, aout{}, lay{};
+    for (int s = 0; s < cnt; ++s) {
+      bt.p[s] = sides[s0 + s].Bt;
+      aout.p[s] = sides[s0 + s].A;
+      for (int l = 0; l < p.G; ++l) lay.p[s * p.G + l] = sides[s0 + s].layers[l];
+    }
+    const size_t es = p.bf16 ? 2 : 4;
+    void* VrT = (char*)w.VrT + (size_t)s0 * nr * es;
+    XKV_K(launch_vr_outputs(w.Vr + s0 * nr, nr, n, r, bt, p.bf16, VrT, nr, cnt, st));
+    if (p.bf16)
+      XKV_K(launch_project_bf16(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const uint16_t*)VrT, nr, r, aout, st));
+    else
+      XKV_K(launch_project_f32(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const float*)VrT, nr, r, aout, st));
+  }
+  // 5. Landmarks of the sides that ask for them.
+  if (any_lm) {
+    PtrTable lay{}, lmo{};
+    int cnt = 0;
+    auto flush = [&]() -> int {
+      if (cnt == 0) return XKV_OK;
+      XKV_K(launch_landmarks(lay, cnt, p.G, sides[0].ld_layer, p.T, desc->n_kv_heads, desc->head_dim, desc->chunk,
+                             desc->rope_theta, lmo, p.bf16, st));
+      cnt = 0;
+      return XKV_OK;
+    };
+    const long per_layer = (long)desc->n_kv_heads * (p.T / desc->chunk) * desc->head_dim * (p.bf16 ? 2 : 4);
+    for (int s = 0; s < S; ++s) {
+      if (!sides[s].landmarks) continue;
+      if ((cnt + 1) * p.G > kMaxPtrs) {
+        rc = flush();
+        if (rc) return rc;
+      }
+      for (int l = 0; l < p.G; ++l) {
+        lay.p[cnt * p.G + l] = sides[s].layers[l];
+        lmo.p[cnt * p.G + l] = (char*)sides[s].landmarks + l * per_layer;
+      }
+      ++cnt;
+    }
+    rc = flush();
+    if (rc) return rc;
+  }
+  if (!converged)
+    return fail(XKV_ENOTCONV, "compress: subspace error estimate above %.1e after %d rounds (%d sweeps); "
+                "outputs are written", tol, rounds, total_iters);
+  return XKV_OK;
+}
+
+extern "C" int xkv_compress_group(xkv_ctx ctx, const xkv_compress_desc* desc, const xkv_side* side, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return xkv_compress_sides(ctx, desc, 1, side, ws, ws_bytes, stream);
+}
+
+extern "C" int xkv_gram(const void* const* layers, long ld_layer, int T, int G, int d_kv, int dtype, double* C,
+                        void* stream) {
+  if (!layers || !C || T <= 0 || G <= 0 || G > 16 || d_kv <= 0 || d_kv % 8 || ld_layer < d_kv)
+    return fail(XKV_EINVAL, "xkv_gram: bad arguments");
+  if (dtype != XKV_F32 && dtype != XKV_BF16) return fail(XKV_EINVAL, "xkv_gram: unknown dtype");
+  xkv::PtrTable tab{};
+  for (int l = 0; l < G; ++l) {
+    if (!layers[l]) return fail(XKV_EINVAL, "xkv_gram: layer %d is NULL", l);
+    if (dtype == XKV_BF16 && (!aligned16(layers[l]) || ld_layer % 8))
+      return fail(XKV_EINVAL, "xkv_gram: bf16 layers need 16-byte alignment and ld %% 8 == 0");
+    tab.p[l] = layers[l];
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == XKV_BF16) XKV_K(xkv::launch_gram_bf16(tab, 1, G, ld_layer, T, d_kv, C, nullptr, st));
+  else XKV_K(xkv::launch_gram_f32(tab, 1, G, ld_layer, T, d_kv, C, nullptr, st));
+  return XKV_OK;
+}
+
+extern "C" int xkv_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, void* stream) {
+  if (!scores || !sel || rows <= 0 || n_cand <= 0 || ld < n_cand || k <= 0 || n_cand > 16384)
+    return fail(XKV_EINVAL, "xkv_topk: bad arguments");
+  XKV_K(xkv::launch_topk(scores, rows, n_cand, ld, k, sel, (hipStream_t)stream));
+  return XKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Selective Reconstruction decode
+// ---------------------------------------------------------------------------
+namespace {
+
+int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
+  if (!a) return fail(XKV_EINVAL, "sr: args is NULL");
+  if (a->batch <= 0 || a->n_kv_heads <= 0 || a->n_q_heads <= 0 || a->n_q_heads % a->n_kv_heads)
+    return fail(XKV_EINVAL, "sr: batch/heads invalid (n_q_heads must be a multiple of n_kv_heads)");
+  const int grp = a->n_q_heads / a->n_kv_heads;
+  if (grp > 8) return fail(XKV_EUNSUPPORTED, "sr: at most 8 query heads per KV head");
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(XKV_EUNSUPPORTED, "sr: head_dim must be 64 or 128");
+  if (a->chunk < 8 || a->chunk > 64 || (a->chunk & (a->chunk - 1)))
+    return fail(XKV_EUNSUPPORTED, "sr: chunk must be a power of two in [8, 64]");
+  if (a->T <= 0 || a->T % a->chunk) return fail(XKV_EINVAL, "sr: T must be a positive multiple of chunk");
+  if (a->n_sink < 0 || a->n_local < 0 || a->n_gen < 0 || a->top_k < 0)
+    return fail(XKV_EINVAL, "sr: negative sizes");
+  if (a->n_sink + a->n_local > a->T) return fail(XKV_EINVAL, "sr: n_sink + n_local must not exceed T");
+  if (a->dtype != XKV_F32 && a->dtype != XKV_BF16) return fail(XKV_EINVAL, "sr: unknown dtype");
+  if (a->r_k <= 0 || a->r_v < 0) return fail(XKV_EINVAL, "sr: r_k must be positive and r_v >= 0");
+  if (a->r_v % 2) return fail(XKV_EUNSUPPORTED, "sr: r_v must be even");
+  const int d_kv = a->n_kv_heads * a->head_dim;
+  const int n_cand = std::max(0, (a->T - a->n_local + a->chunk - 1) / a->chunk);
+  const int k_eff = std::min(a->top_k, n_cand);
+  if (a->n_sink + a->n_local + a->n_gen == 0 && k_eff == 0) return fail(XKV_EINVAL, "sr: nothing to attend");
+  const int cps = 64 / a->chunk;
+  const int n_splits = (k_eff + cps - 1) / cps;
+  const int vec_len = a->r_v > 0 ? a->r_v : a->head_dim;
+  if (grp * vec_len > 64 * 129) return fail(XKV_EUNSUPPORTED, "sr: query group x value rank too large");
+  if (!a->q || !a->A_k || !a->Bt_k || !a->landmarks || !a->k_tail || !a->v_tail || !a->out || !a->sel)
+    return fail(XKV_EINVAL, "sr: a required pointer is NULL");
+  if (a->r_v > 0 ? (!a->A_v || !a->Bt_v) : !a->V_full) return fail(XKV_EINVAL, "sr: value pointers missing");
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return fail(XKV_EINVAL, "sr: give both k_new and v_new or neither");
+  if (a->ld_A_k < a->r_k || a->ld_Bt_k < a->r_k || a->ld_tail < d_kv) return fail(XKV_EINVAL, "sr: leading dimension too small");
+  if (a->r_v > 0 && (a->ld_A_v < a->r_v || a->ld_Bt_v < a->r_v)) return fail(XKV_EINVAL, "sr: value leading dimension too small");
+  if (a->r_v == 0 && a->ld_V < d_kv) return fail(XKV_EINVAL, "sr: ld_V too small");
+  if (a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 64 == 0) {
+    if (!aligned16(a->A_k) || !aligned16(a->Bt_k) || a->ld_A_k % 8 || a->ld_Bt_k % 8 || a->bstride_A_k % 8 ||
+        a->bstride_Bt_k % 8)
+      return fail(XKV_EINVAL, "sr: bf16 A_k/Bt_k need 16-byte alignment and strides that are multiples of 8");
+  }
+  if (!aligned16(a->landmarks) || a->bstride_lm % (a->dtype == XKV_BF16 ? 8 : 4))
+    return fail(XKV_EINVAL, "sr: landmarks need 16-byte alignment");
+
+  xkv::SrParams& p = *P;
+  std::memset(&p, 0, sizeof(p));
+  p.batch = a->batch; p.Hq = a->n_q_heads; p.Hkv = a->n_kv_heads; p.d = a->head_dim; p.T = a->T;
+  p.n_gen = a->n_gen; p.chunk = a->chunk; p.top_k = a->top_k; p.n_sink = a->n_sink; p.n_local = a->n_local;
+  p.r_k = a->r_k; p.r_v = a->r_v; p.n_cand = n_cand; p.n_chunks = a->T / a->chunk; p.k_eff = k_eff;
+  p.n_splits = n_splits; p.grp = grp; p.cps = cps;
+  p.q_pos = a->n_gen > 0 ? (long)a->T + a->n_gen - 1 : a->T;
+  p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));
+  p.vec_len = vec_len;
+  p.scale = a->scale; p.theta = a->rope_theta;
+  p.q = a->q;
+  p.A_k = a->A_k; p.ld_A_k = a->ld_A_k; p.bs_A_k = a->bstride_A_k;
+  p.Bt_k = a->Bt_k; p.ld_Bt_k = a->ld_Bt_k; p.bs_Bt_k = a->bstride_Bt_k;
+  p.A_v = a->A_v; p.ld_A_v = a->ld_A_v; p.bs_A_v = a->bstride_A_v;
+  p.Bt_v = a->Bt_v; p.ld_Bt_v = a->ld_Bt_v; p.bs_Bt_v = a->bstride_Bt_v;
+  p.V_full = a->V_full; p.ld_V = a->ld_V; p.bs_V = a->bstride_V;
+  p.lm = a->landmarks; p.bs_lm = a->bstride_lm;
+  p.k_tail = a->k_tail; p.v_tail = a->v_tail; p.ld_tail = a->ld_tail; p.bs_tail = a->bstride_tail;
+  p.k_new = a->k_new; p.v_new = a->v_new; p.bs_new = a->bstride_new;
+  p.out = a->out;
+  p.sel = a->sel;
+
+  Carver c(nullptr);
+  const size_t bh = (size_t)a->batch * a->n_kv_heads;
+  c.take<float>(bh * std::max(n_cand, 1));
+  c.take<int>(bh * 2);
+  c.take<float>(bh * std::max(n_splits, 1) * grp * (2 + vec_len));
+  c.take<float>(bh * grp * (2 + a->head_dim));
+  *ws_need = c.off;
+  return XKV_OK;
+}
+
+void bind_sr_ws(xkv::SrParams* p, void* ws) {
+  Carver c(ws);
+  const size_t bh = (size_t)p->batch * p->Hkv;
+  p->scores = c.take<float>(bh * std::max(p->n_cand, 1));
+  p->counters = c.take<int>(bh * 2);
+  p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->vec_len));
+  p->part_ex = c.take<float>(bh * p->grp * (2 + p->d));
+}
+
+int sr_prepare(xkv_ctx ctx, const xkv_sr_args* a, void* ws, size_t ws_bytes, xkv::SrParams* P) {
+  if (!ctx) return fail(XKV_EINVAL, "sr: ctx is NULL");
+  size_t need = 0;
+  int rc = plan_sr(a, P, &need);
+  if (rc) return rc;
+  if (!ws || ws_bytes < need) return fail(XKV_EWORKSPACE, "sr: workspace %zu bytes < %zu", ws_bytes, need);
+  bind_sr_ws(P, ws);
+  return XKV_OK;
+}
+
+}  // namespace
+
+extern "C" int xkv_sr_ws_size(const xkv_sr_args* args, size_t* bytes) {
+  if (!bytes) return fail(XKV_EINVAL, "xkv_sr_ws_size: bytes is NULL");
+  xkv::SrParams P;
+  return plan_sr(args, &P, bytes);
+}
+
+extern "C" int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream) {
+  xkv::SrParams P;
+  int rc = sr_prepare(ctx, args, ws, ws_bytes, &P);
+  if (rc) return rc;
+  if (P.n_cand > 0 && P.top_k > 0) XKV_K(xkv::launch_sr_select(P, args->dtype == XKV_BF16, (hipStream_t)stream));
+  else if (args->k_new) {
+    // No candidates to score: still append the new token (a one-block select launch).
+    P.n_cand = 0;
+    XKV_K(xkv::launch_sr_select(P, args->dtype == XKV_BF16, (hipStream_t)stream));
+  }
+  return XKV_OK;
+}
+
+extern "C" int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream) {
+  xkv::SrParams P;
+  int rc = sr_prepare(ctx, args, ws, ws_bytes, &P);
+  if (rc) return rc;
+  XKV_K(xkv::launch_sr_attend(P, args->dtype == XKV_BF16, (hipStream_t)stream));
+  return XKV_OK;
+}
+
+extern "C" int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream) {
+  int rc = xkv_sr_select(ctx, args, ws, ws_bytes, stream);
+  if (rc) return rc;
+  return xkv_sr_attend(ctx, args, ws, ws_bytes, stream);
+}

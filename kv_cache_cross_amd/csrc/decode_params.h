@@ -1,0 +1,40 @@
+// Kernel-argument block of the Selective Reconstruction decode kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace xkv {
+
+struct SrParams {
+  int batch, Hq, Hkv, d, T, n_gen, chunk, top_k, n_sink, n_local, r_k, r_v;
+  int n_cand;        // candidate chunks (not wholly inside the local window)
+  int n_chunks;      // T / chunk (landmark rows per head)
+  int k_eff;         // min(top_k, n_cand)
+  int n_splits;      // 64-row splits of the selected rows
+  int grp;           // query heads per KV head
+  int cps;           // chunks per split (64 / chunk)
+  long q_pos;        // query position p
+  int score_blocks;  // select-kernel blocks per KV head
+  int vec_len;       // length of a split's value vector: r_v, or d when values are exact
+  float scale;
+  double theta;
+  const void* q;
+  const void* A_k; long ld_A_k, bs_A_k;
+  const void* Bt_k; long ld_Bt_k, bs_Bt_k;
+  const void* A_v; long ld_A_v, bs_A_v;
+  const void* Bt_v; long ld_Bt_v, bs_Bt_v;
+  const void* V_full; long ld_V, bs_V;
+  const void* lm; long bs_lm;
+  void* k_tail; void* v_tail; long ld_tail, bs_tail;
+  const void* k_new; const void* v_new; long bs_new;
+  float* out;
+  int* sel;          // batch x Hkv x top_k
+  float* scores;     // batch x Hkv x n_cand
+  int* counters;     // batch x Hkv x 2, zero between calls
+  float* part;       // batch x Hkv x n_splits x grp x (2 + vec_len)
+  float* part_ex;    // batch x Hkv x grp x (2 + d)
+};
+
+hipError_t launch_sr_select(const SrParams& P, int bf16, hipStream_t st);
+hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st);
+
+}  // namespace xkv

@@ -1,0 +1,274 @@
+// Projection A = X V_r (the shared token basis, xKV blog section on what xKV
+// does) and the per-chunk landmark means used by the top-k chunk selector
+// (xKV blog, section on Selective Reconstruction).
+//
+// bf16 projection: both operands are contiguous along the contracted
+// dimension (X rows along columns of the group, VrT rows along the group
+// columns), so a 128 x 128 output tile stages 128 x 64 slices of each
+// through LDS with 16-byte loads (double buffered) and feeds
+// v_mfma_f32_32x32x16_bf16 with one 16-byte LDS read per operand.  The rank
+// tile is the fastest-varying workgroup index, so the workgroups that read
+// the same X rows run together and share them through L2.
+//
+// Landmarks: m[l, h, c] = mean over the chunk's tokens of RoPE(K_l[t, h], t),
+// from the original keys, float32 sums, angle formed in float64.
+#include "xkv_common.h"
+#include "xkv_kernels.h"
+
+namespace xkv {
+namespace {
+
+constexpr int PT = 128;            // output tile edge (tokens and rank)
+constexpr int PK = 64;             // contraction slice per stage
+constexpr int PROW = PK + 8;       // padded LDS row (uint16): 144 bytes
+
+struct ProjArgs {
+  PtrTable layers;
+  PtrTable A_out;
+  const uint16_t* VrT;
+  long sVT;
+  int G, T, d_kv, n, r;
+  long ld;
+};
+
+__global__ __launch_bounds__(256) void project_bf16_kernel(ProjArgs a) {
+  extern __shared__ __align__(16) uint16_t lds_raw[];
+  auto xs = [&](int buf, int row, int k) -> uint16_t* { return lds_raw + ((buf * 2 + 0) * PT + row) * PROW + k; };
+  auto vs = [&](int buf, int row, int k) -> uint16_t* { return lds_raw + ((buf * 2 + 1) * PT + row) * PROW + k; };
+  const int side = blockIdx.z;
+  const int j0 = blockIdx.x * PT;    // rank tile
+  const int t0 = blockIdx.y * PT;    // token tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint16_t* VrT = a.VrT + side * a.sVT;
+
+  // Loader: 4 rows x one 8-column group per operand per thread.
+  const int lrow = tid >> 3;         // 0..31
+  const int lcg = tid & 7;           // 0..7
+  uint4 xr[4], vr[4];
+  auto gload = [&](int k0) {
+    const int col = k0 + lcg * 8;
+    const uint16_t* xp = nullptr;
+    if (col < a.n) {
+      const int l = col / a.d_kv;
+      xp = (const uint16_t*)a.layers.p[side * a.G + l] + (col - l * a.d_kv);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + lrow + 32 * i;
+      xr[i] = (xp && t < a.T) ? *(const uint4*)(xp + (long)t * a.ld) : make_uint4(0, 0, 0, 0);
+      const int j = j0 + lrow + 32 * i;
+      vr[i] = (col < a.n && j < a.r) ? *(const uint4*)(VrT + (long)j * a.n + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(uint4*)xs(buf, lrow + 32 * i, lcg * 8) = xr[i];
+      *(uint4*)vs(buf, lrow + 32 * i, lcg * 8) = vr[i];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+
+  const int nk = (a.n + PK - 1) / PK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nk) gload((s + 1) * PK);
+#pragma unroll
+    for (int ks = 0; ks < PK / 16; ++ks) {
+      const int k_off = ks * 16 + (lane >> 5) * 8;
+      bf16x8_t af[2], bfr[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) af[mi] = as_bf16x8(*(const uint4*)xs(buf, wm * 64 + mi * 32 + (lane & 31), k_off));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) bfr[ni] = as_bf16x8(*(const uint4*)vs(buf, wn * 64 + ni * 32 + (lane & 31), k_off));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (s + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  uint16_t* Aout = (uint16_t*)a.A_out.p[side];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + wm * 64 + mi * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+        const int c = j0 + wn * 64 + ni * 32 + (lane & 31);
+        if (t < a.T && c < a.r) Aout[(long)t * a.r + c] = f32_to_bf16_bits(acc[mi][ni][j]);
+      }
+}
+
+struct ProjF32Args {
+  PtrTable layers;
+  PtrTable A_out;
+  const float* VrT;
+  long sVT;
+  int G, T, d_kv, n, r;
+  long ld;
+};
+
+// float32 path (small workloads): 16 x 16 tiles, float64 sums.
+__global__ __launch_bounds__(256) void project_f32_kernel(ProjF32Args a) {
+  __shared__ float xt[16][17], vt[16][17];
+  const int side = blockIdx.z;
+  const int t0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+  const float* VrT = a.VrT + side * a.sVT;
+  double s = 0.0;
+  for (int k0 = 0; k0 < a.n; k0 += 16) {
+    const int col = k0 + tx;
+    const int t = t0 + ty;
+    float xv = 0.f;
+    if (col < a.n && t < a.T) {
+      const int l = col / a.d_kv;
+      xv = ((const float*)a.layers.p[side * a.G + l])[(long)t * a.ld + (col - l * a.d_kv)];
+    }
+    xt[ty][tx] = xv;
+    const int j = j0 + ty;
+    vt[ty][tx] = (col < a.n && j < a.r) ? VrT[(long)j * a.n + col] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += (double)xt[ty][k] * (double)vt[tx][k];
+    __syncthreads();
+  }
+  const int t = t0 + ty, j = j0 + tx;
+  if (t < a.T && j < a.r) ((float*)a.A_out.p[side])[(long)t * a.r + j] = (float)s;
+}
+
+struct LmArgs {
+  PtrTable layers;
+  PtrTable out;
+  int G, T, H, d, chunk, n_chunks, bf16;
+  long ld;
+  double theta;
+};
+
+// One thread per (chunk, rotation pair); blockIdx.y = head, blockIdx.z = side * G + layer.
+__global__ __launch_bounds__(256) void landmarks_kernel(LmArgs a) {
+  const int half = a.d >> 1;
+  const int per_block = 256 / half;
+  const int c = blockIdx.x * per_block + threadIdx.x / half;
+  const int i = threadIdx.x % half;
+  const int h = blockIdx.y, sl = blockIdx.z;
+  if (c >= a.n_chunks) return;
+  const double f = rope_freq(a.theta, i, a.d);
+  const long col = (long)h * a.d + i;
+  float lo = 0.f, hi = 0.f;
+  for (int q = 0; q < a.chunk; ++q) {
+    const long t = (long)c * a.chunk + q;
+    float xl, xh;
+    if (a.bf16) {
+      const uint16_t* src = (const uint16_t*)a.layers.p[sl] + t * a.ld + col;
+      xl = bf16_bits_to_f32(src[0]);
+      xh = bf16_bits_to_f32(src[half]);
+    } else {
+      const float* src = (const float*)a.layers.p[sl] + t * a.ld + col;
+      xl = src[0];
+      xh = src[half];
+    }
+    float cs, sn;
+    rope_cs(t, f, &cs, &sn);
+    lo += xl * cs - xh * sn;
+    hi += xh * cs + xl * sn;
+  }
+  const float inv = 1.f / (float)a.chunk;
+  const long o = ((long)h * a.n_chunks + c) * a.d + i;
+  if (a.bf16) {
+    uint16_t* dst = (uint16_t*)a.out.p[sl];
+    dst[o] = f32_to_bf16_bits(lo * inv);
+    dst[o + half] = f32_to_bf16_bits(hi * inv);
+  } else {
+    float* dst = (float*)a.out.p[sl];
+    dst[o] = lo * inv;
+    dst[o + half] = hi * inv;
+  }
+}
+
+}  // namespace
+
+static constexpr size_t kProjLds = 2 * 2 * PT * PROW * sizeof(uint16_t);
+
+hipError_t launch_project_bf16(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
+                               const uint16_t* VrT, long sVT, int r, const PtrTable& A_out,
+                               hipStream_t st) {
+  ProjArgs a;
+  a.layers = layers;
+  a.A_out = A_out;
+  a.VrT = VrT;
+  a.sVT = sVT;
+  a.G = G;
+  a.T = T;
+  a.d_kv = d_kv;
+  a.n = G * d_kv;
+  a.r = r;
+  a.ld = ld;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)project_bf16_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kProjLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((r + PT - 1) / PT, (T + PT - 1) / PT, n_sides);
+  hipLaunchKernelGGL(project_bf16_kernel, grid, dim3(256), kProjLds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_f32(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
+                              const float* VrT, long sVT, int r, const PtrTable& A_out,
+                              hipStream_t st) {
+  ProjF32Args a;
+  a.layers = layers;
+  a.A_out = A_out;
+  a.VrT = VrT;
+  a.sVT = sVT;
+  a.G = G;
+  a.T = T;
+  a.d_kv = d_kv;
+  a.n = G * d_kv;
+  a.r = r;
+  a.ld = ld;
+  dim3 grid((r + 15) / 16, (T + 15) / 16, n_sides);
+  hipLaunchKernelGGL(project_f32_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_landmarks(const PtrTable& layers, int n_sides, int G, long ld, int T, int n_kv_heads,
+                            int head_dim, int chunk, double theta, const PtrTable& lm_out, int bf16,
+                            hipStream_t st) {
+  LmArgs a;
+  a.layers = layers;
+  a.out = lm_out;
+  a.G = G;
+  a.T = T;
+  a.H = n_kv_heads;
+  a.d = head_dim;
+  a.chunk = chunk;
+  a.n_chunks = T / chunk;
+  a.bf16 = bf16;
+  a.ld = ld;
+  a.theta = theta;
+  const int per_block = 256 / (head_dim / 2);
+  dim3 grid((a.n_chunks + per_block - 1) / per_block, n_kv_heads, n_sides * G);
+  hipLaunchKernelGGL(landmarks_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace xkv

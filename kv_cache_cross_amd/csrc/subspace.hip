@@ -1,0 +1,229 @@
+// Kernels of the block subspace iteration besides the GEMMs:
+//   * factor of a diagonal block of W = Y^T Y for the blocked Cholesky of
+//     CholeskyQR (Q = Y R^-1 with W = R^T R), with the block's inverse;
+//   * the Gaussian start block;
+//   * conversion of V_r to the stored Bt = V_r and its transpose.
+#include "xkv_common.h"
+#include "xkv_kernels.h"
+
+namespace xkv {
+namespace {
+
+constexpr int NB = 64;
+
+// One workgroup per side: load the nb x nb diagonal block of W at (j0, j0),
+// factor it as L L^T in LDS (right-looking, column by column), invert L by
+// forward substitution, and write L and L^-1.
+__global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long ldw, long sW,
+                                                         double* L, long ldl, long sL,
+                                                         double* Dinv, long sD, int j0, int nb,
+                                                         const double* wdiag, long sDiag, int clamp,
+                                                         int* info) {
+  __shared__ double a[NB][NB + 1];
+  __shared__ double inv[NB][NB + 1];
+  __shared__ int bad;
+  const int side = blockIdx.x, tid = threadIdx.x;
+  const double* w = W + side * sW + (long)j0 * ldw + j0;
+  if (tid == 0) bad = 0;
+  for (int idx = tid; idx < NB * NB; idx += 256) {
+    const int i = idx / NB, j = idx % NB;
+    a[i][j] = (i < nb && j < nb && j <= i) ? w[(long)i * ldw + j] : 0.0;
+    inv[i][j] = 0.0;
+  }
+  __syncthreads();
+  const double* w0 = wdiag + side * sDiag + j0;
+  for (int k = 0; k < nb; ++k) {
+    if (tid == 0) {
+      // The pivot is the squared distance of column j0+k of Y from the span of the
+      // previous columns.  Below 1e-14 of the column's squared norm it is either a
+      // breakdown (float64 sweeps: reported) or, with `clamp` (float32 sweeps, whose Y
+      // carries float32 noise), raised to that floor, which damps the near-dependent
+      // direction instead of amplifying noise.
+      double piv = a[k][k];
+      const double floor_k = 1e-14 * w0[k];
+      if (!isfinite(piv)) {
+        bad = 1;
+        piv = 1.0;
+      } else if (!(piv > floor_k)) {
+        if (clamp && floor_k > 0.0) {
+          piv = floor_k;
+        } else {
+          bad = 1;
+          piv = 1.0;
+        }
+      }
+      a[k][k] = sqrt(piv);
+    }
+    __syncthreads();
+    const double dk = a[k][k];
+    for (int i = k + 1 + tid; i < nb; i += 256) a[i][k] /= dk;
+    __syncthreads();
+    const int m = nb - k - 1;
+    for (int idx = tid; idx < m * m; idx += 256) {
+      const int i = k + 1 + idx / m, j = k + 1 + idx % m;
+      if (j <= i) a[i][j] -= a[i][k] * a[j][k];
+    }
+    __syncthreads();
+  }
+  // Column c of L^-1 by forward substitution (thread c).
+  if (tid < nb) {
+    const int c = tid;
+    for (int i = c; i < nb; ++i) {
+      double s = (i == c) ? 1.0 : 0.0;
+      for (int mm = c; mm < i; ++mm) s -= a[i][mm] * inv[mm][c];
+      inv[i][c] = s / a[i][i];
+    }
+  }
+  __syncthreads();
+  double* l = L + side * sL + (long)j0 * ldl + j0;
+  double* dv = Dinv + side * sD;
+  for (int idx = tid; idx < nb * nb; idx += 256) {
+    const int i = idx / nb, j = idx % nb;
+    l[(long)i * ldl + j] = (j <= i) ? a[i][j] : 0.0;
+  }
+  for (int idx = tid; idx < NB * NB; idx += 256) {
+    const int i = idx / NB, j = idx % NB;
+    dv[i * NB + j] = (i < nb && j < nb && j <= i) ? inv[i][j] : 0.0;
+  }
+  if (tid == 0 && bad) info[side] = 1;
+}
+
+__global__ void copy_diag_kernel(const double* W, long ldw, long sW, double* dg, long sD, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dg[blockIdx.y * sD + i] = W[blockIdx.y * sW + (long)i * ldw + i];
+}
+
+// Squared residual norm of each Ritz pair: one thread per (row group, column).
+__global__ __launch_bounds__(256) void ritz_residual_kernel(const double* YZ, const double* Vr,
+                                                            const double* theta, int n, int r, double* res2) {
+  __shared__ double part[4][64];
+  const int side = blockIdx.y;
+  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + c;
+  const long off = (long)side * n * r;
+  double s = 0.0;
+  if (i < r) {
+    const double th = theta[(long)side * r + i];
+    for (int j = rg; j < n; j += 4) {
+      const double e = YZ[off + (long)j * r + i] - th * Vr[off + (long)j * r + i];
+      s += e * e;
+    }
+  }
+  part[rg][c] = s;
+  __syncthreads();
+  if (rg == 0 && i < r) res2[(long)side * r + i] = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+}
+
+__global__ void zero_i32_kernel(int* p, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// splitmix64 finaliser: a counter-based source of uniform bits.
+XKV_DEV uint64_t mix64(uint64_t z) {
+  z += 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+// Gaussian start block (Box-Muller on two 53-bit uniforms per entry).
+__global__ void init_q_kernel(float* Q, int rows, int k, long sQ, uint64_t seed) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int side = blockIdx.y;
+  if (e >= (long)rows * k) return;
+  // The same start block for every side, so a side's result does not depend on its batch slot.
+  const uint64_t base = mix64(seed ^ 0x51deull) + 2ull * (uint64_t)e;
+  const double u1 = ((mix64(base) >> 11) + 1.0) * (1.0 / 9007199254740993.0);
+  const double u2 = (mix64(base + 1) >> 11) * (1.0 / 9007199254740992.0);
+  Q[side * sQ + e] = (float)(sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2));
+}
+
+struct VrArgs {
+  PtrTable Bt;
+  const double* Vr;
+  long sVr;
+  int n, r, bf16;
+  void* VrT;
+  long sVT;
+};
+
+// Bt (n x r) <- Vr and VrT (r x n) <- Vr^T, via a 32 x 32 LDS transpose.
+__global__ __launch_bounds__(256) void vr_outputs_kernel(VrArgs a) {
+  __shared__ double tile[32][33];
+  const int side = blockIdx.z;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;   // i: row of Vr (0..n), j: rank index
+  const double* V = a.Vr + side * a.sVr;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int i = i0 + yy, j = j0 + tx;
+    double v = (i < a.n && j < a.r) ? V[(long)i * a.r + j] : 0.0;
+    tile[yy][tx] = v;
+    if (i < a.n && j < a.r) {
+      if (a.bf16) ((uint16_t*)a.Bt.p[side])[(long)i * a.r + j] = f32_to_bf16_bits((float)v);
+      else ((float*)a.Bt.p[side])[(long)i * a.r + j] = (float)v;
+    }
+  }
+  __syncthreads();
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int j = j0 + yy, i = i0 + tx;
+    if (i < a.n && j < a.r) {
+      const double v = tile[tx][yy];
+      if (a.bf16) ((uint16_t*)a.VrT)[side * a.sVT + (long)j * a.n + i] = f32_to_bf16_bits((float)v);
+      else ((float*)a.VrT)[side * a.sVT + (long)j * a.n + i] = (float)v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_potrf_diag(const double* W, long ldw, long sW, double* L, long ldl, long sL,
+                             double* Dinv, long sD, int j0, int nb, const double* wdiag, long sDiag,
+                             int clamp, int n_sides, int* info, hipStream_t st) {
+  if (nb > NB) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(potrf_diag_kernel, dim3(n_sides), dim3(256), 0, st, W, ldw, sW, L, ldl, sL, Dinv,
+                     sD, j0, nb, wdiag, sDiag, clamp, info);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_diag(const double* W, long ldw, long sW, double* dg, long sD, int n, int n_sides,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(copy_diag_kernel, dim3((n + 255) / 256, n_sides), dim3(256), 0, st, W, ldw, sW, dg, sD, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_ritz_residual(const double* YZ, const double* Vr, const double* theta, int n, int r,
+                                double* res2, int n_sides, hipStream_t st) {
+  hipLaunchKernelGGL(ritz_residual_kernel, dim3((r + 63) / 64, n_sides), dim3(256), 0, st, YZ, Vr, theta, n, r, res2);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int* p, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_q(float* Q, int rows, int k, long sQ, int n_sides, uint64_t seed, hipStream_t st) {
+  const long total = (long)rows * k;
+  hipLaunchKernelGGL(init_q_kernel, dim3((unsigned)((total + 255) / 256), n_sides), dim3(256), 0, st, Q,
+                     rows, k, sQ, seed);
+  return hipGetLastError();
+}
+
+hipError_t launch_vr_outputs(const double* Vr, long sVr, int n, int r, const PtrTable& Bt, int bf16,
+                             void* VrT, long sVT, int n_sides, hipStream_t st) {
+  VrArgs a;
+  a.Bt = Bt;
+  a.Vr = Vr;
+  a.sVr = sVr;
+  a.n = n;
+  a.r = r;
+  a.bf16 = bf16;
+  a.VrT = VrT;
+  a.sVT = sVT;
+  hipLaunchKernelGGL(vr_outputs_kernel, dim3((r + 31) / 32, (n + 31) / 32, n_sides), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace xkv

@@ -1,0 +1,75 @@
+// Host-side launchers of the libxkv HIP kernels.  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xkv {
+
+// Device pointers passed by value in the kernel arguments (2 KiB).
+constexpr int kMaxPtrs = 256;
+struct PtrTable {
+  const void* p[kMaxPtrs];
+};
+
+// ---- Gram: C = X^T X of the horizontally concatenated layers ---------------
+// layers.p[s*G + l] is layer l of side s (T x d_kv, row stride ld).  C (and the
+// optional float copy C32) are n x n per side with side stride n*n.
+hipError_t launch_gram_bf16(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
+                            double* C, float* C32, hipStream_t st);
+hipError_t launch_gram_f32(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
+                           double* C, float* C32, hipStream_t st);
+
+// ---- Batched GEMM on MFMA: C = alpha op(A) op(B) + beta C ------------------
+enum GType { GF32 = 0, GF64 = 1 };
+struct GemmDesc {
+  int M, N, K;
+  int ta, tb;                 // 0: as stored, 1: transposed
+  int typeA, typeB, typeC;    // GType of each operand in memory
+  int acc;                    // GType of the MFMA arithmetic
+  const void* A; long lda, sA;
+  const void* B; long ldb, sB;
+  void* C; long ldc, sC;
+  double alpha, beta;
+  int batch;
+};
+hipError_t gemm(const GemmDesc& d, hipStream_t st);
+
+// ---- Cholesky helpers -----------------------------------------------------
+// Factor the nb x nb diagonal block at (j0, j0) of each side's W (lower), write
+// it into L and its inverse into Dinv (64 x 64 per side).  wdiag holds the
+// diagonal of W before factorisation (n_sides x kb, side stride sDiag); a pivot
+// below 1e-14 of it sets info[side] = 1, or with `clamp` is raised to that floor.
+hipError_t launch_potrf_diag(const double* W, long ldw, long sW, double* L, long ldl, long sL,
+                             double* Dinv, long sD, int j0, int nb, const double* wdiag, long sDiag,
+                             int clamp, int n_sides, int* info, hipStream_t st);
+hipError_t launch_copy_diag(const double* W, long ldw, long sW, double* dg, long sD, int n, int n_sides,
+                            hipStream_t st);
+hipError_t launch_zero_i32(int* p, long n, hipStream_t st);
+// res2[s*r + i] = || YZ[:, i] - theta[s*r + i] * Vr[:, i] ||^2 (n x r float64 per side, side stride n*r).
+hipError_t launch_ritz_residual(const double* YZ, const double* Vr, const double* theta, int n, int r,
+                                double* res2, int n_sides, hipStream_t st);
+
+// ---- Subspace iteration helpers ------------------------------------------
+hipError_t launch_init_q(float* Q, int rows, int k, long sQ, int n_sides, uint64_t seed, hipStream_t st);
+// Vr (n x r float64 per side) -> Bt outputs (n x r, storage dtype, one pointer per side) and the
+// transposed copy VrT (r x n, storage dtype, side stride sVT) used by the projection.
+hipError_t launch_vr_outputs(const double* Vr, long sVr, int n, int r, const PtrTable& Bt, int bf16,
+                             void* VrT, long sVT, int n_sides, hipStream_t st);
+
+// ---- Projection A = X V_r and landmarks -----------------------------------
+hipError_t launch_project_bf16(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
+                               const uint16_t* VrT, long sVT, int r, const PtrTable& A_out,
+                               hipStream_t st);
+hipError_t launch_project_f32(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
+                              const float* VrT, long sVT, int r, const PtrTable& A_out,
+                              hipStream_t st);
+// lm_out.p[s*G + l] receives n_kv_heads x (T/chunk) x head_dim for layer l of side s.
+hipError_t launch_landmarks(const PtrTable& layers, int n_sides, int G, long ld, int T, int n_kv_heads,
+                            int head_dim, int chunk, double theta, const PtrTable& lm_out, int bf16,
+                            hipStream_t st);
+
+// ---- Selective Reconstruction decode --------------------------------------
+struct SrParams;  // defined in decode.hip
+hipError_t launch_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, hipStream_t st);
+
+}  // namespace xkv

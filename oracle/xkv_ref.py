@@ -172,7 +172,7 @@ def _softmax_rows(logits):
 def sr_decode_layer(q, *, T: int, n_gen: int, n_kv_heads: int, chunk: int, top_k: int,
                     n_sink: int, n_local: int, landmarks_l, A_k, B_k_l,
                     k_exact, v_exact, A_v=None, B_v_l=None, V_full=None,
-                    scale: float | None = None, theta: float = ROPE_THETA) -> dict:
+                    scale: float | None = None, theta: float = ROPE_THETA, selection=None) -> dict:
     """One decode step of one layer with Selective Reconstruction.
 
     q          (H_q x d) pre-RoPE query at position p = T + n_gen - 1 (p = T if n_gen == 0)
@@ -182,6 +182,8 @@ def sr_decode_layer(q, *, T: int, n_gen: int, n_kv_heads: int, chunk: int, top_k
                                              values are kept exact
     k_exact, v_exact  dicts {position: d_kv row} for every sink, local-window and
                       generated position (pre-RoPE keys)
+    selection  optional (H_kv x k) chunk ids to attend instead of the top-k (ids < 0 are
+               ignored); the scores are still computed and returned
 
     Returns out (H_q x d), sel (H_kv x min(k, C)) ascending chunk ids, scores (H_kv x C)
     and the attended positions of each KV head.
@@ -206,6 +208,8 @@ def sr_decode_layer(q, *, T: int, n_gen: int, n_kv_heads: int, chunk: int, top_k
         qh = q_rot[h * grp:(h + 1) * grp]
         s = landmark_scores(qh, np.asarray(landmarks_l)[h, :n_cand], scale)
         sel = select_topk(s, top_k)
+        if selection is not None:
+            sel = np.array([c for c in np.asarray(selection[h]).tolist() if c >= 0], dtype=np.int64)
         pos = attended_positions(sel, T, n_sink, n_local, n_gen, chunk)
         cols = slice(h * d, (h + 1) * d)
         keys = np.zeros((pos.size, d))

@@ -3,4 +3,4 @@
 This package only draws random numbers and rounds them to the storage dtype.
 It contains none of the compression or decode arithmetic.
 """
-from .kvgen import CONFIGS, Workload, make_workload, config_by_name  # noqa: F401
+from .kvgen import CONFIGS, Workload, make_workload, config_by_name, gaussian  # noqa: F401

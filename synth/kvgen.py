@@ -186,5 +186,12 @@ class Workload:
         return self._randn((cfg.n_q_heads, cfg.head_dim), "q", b, layer, step).to(cfg.torch_dtype)
 
 
+def gaussian(shape, seed: int, *, scale: float = 1.0, dtype=torch.float32, device="cpu") -> torch.Tensor:
+    """Seeded N(0, scale^2) matrix in the storage dtype (unit-level test inputs)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_subseed(seed, "gaussian", tuple(shape)))
+    return (scale * torch.randn(tuple(shape), generator=g)).to(dtype).to(device)
+
+
 def make_workload(name: str, seed: int = 0, device="cpu", **overrides) -> Workload:
     return Workload(config_by_name(name, **overrides), seed=seed, device=device)

@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point,
+rejects bad arguments before touching the device, and its host eigensolver
+(used for the Rayleigh-Ritz step) is correct."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_cross_amd as xk
+from kv_cache_cross_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "xkv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xkv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = xk.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/xkv.h but not exported"
+    assert lib.xkv_version() >= 100
+
+
+def test_struct_layouts_match_header_order():
+    # Field order of the ctypes mirrors follows the header's declaration order.
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct {\n  int batch;"):src.index("} xkv_sr_args;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*?\s*([a-zA-Z_][a-zA-Z0-9_]*)\s*[,;]", body)
+    assert names == [f for f, _ in L.SrArgs._fields_]
+
+
+def _desc(**kw):
+    base = dict(T=256, G=2, d_kv=64, r=16, dtype=xk.XKV_F32, n_kv_heads=1, head_dim=64)
+    base.update(kw)
+    return xk.make_desc(**base)
+
+
+def test_compress_ws_size_and_validation():
+    n = xk.compress_ws_size(_desc(), 1)
+    assert n > 0 and n % 256 == 0
+    assert xk.compress_ws_size(_desc(), 4) > 3 * n
+    for bad in [dict(r=0), dict(r=129), dict(d_kv=60, head_dim=60), dict(G=0), dict(T=0), dict(fp64_iters=0),
+                dict(dtype=7), dict(n_kv_heads=2)]:
+        with pytest.raises(xk.XkvError) as e:
+            xk.compress_ws_size(_desc(**bad), 1)
+        assert e.value.code == L.XKV_EINVAL, bad
+
+
+def test_compress_rejects_null_context():
+    d = _desc()
+    sides = (L.Side * 1)()
+    rc = xk.lib().xkv_compress_sides(None, C.byref(d), 1, sides, None, 0, None)
+    assert rc == L.XKV_EINVAL
+    assert b"ctx" in xk.lib().xkv_last_error()
+
+
+def test_sr_ws_size_validation():
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, T=64, n_gen=1, chunk=8, top_k=2, n_sink=4,
+                n_local=16, r_k=64, r_v=64, dtype=xk.XKV_BF16, scale=0.1, rope_theta=1e4, q=16, A_k=16,
+                ld_A_k=64, Bt_k=16, ld_Bt_k=64, A_v=16, ld_A_v=64, Bt_v=16, ld_Bt_v=64, landmarks=16,
+                k_tail=16, v_tail=16, ld_tail=256, out=16, sel=16)
+    assert xk.sr_ws_size(xk.sr_args(**base)) > 0
+    for bad, code in [(dict(n_q_heads=5), L.XKV_EINVAL), (dict(head_dim=96), L.XKV_EUNSUPPORTED),
+                      (dict(chunk=12), L.XKV_EUNSUPPORTED), (dict(T=60), L.XKV_EINVAL),
+                      (dict(n_q_heads=36, n_kv_heads=2), L.XKV_EUNSUPPORTED), (dict(q=0), L.XKV_EINVAL),
+                      (dict(n_sink=40, n_local=40), L.XKV_EINVAL), (dict(A_k=8), L.XKV_EINVAL)]:
+        kw = dict(base, **bad)
+        with pytest.raises(xk.XkvError) as e:
+            xk.sr_ws_size(xk.sr_args(**kw))
+        assert e.value.code == code, bad
+
+
+def test_topk_and_gram_validation():
+    lib = xk.lib()
+    assert lib.xkv_topk(None, 1, 10, 10, 2, None, None) == L.XKV_EINVAL
+    assert lib.xkv_topk(16, 1, 20000, 20000, 2, 16, None) == L.XKV_EINVAL
+    ptrs = (C.c_void_p * 1)(None)
+    assert lib.xkv_gram(ptrs, 64, 16, 1, 64, xk.XKV_F32, 16, None) == L.XKV_EINVAL
+
+
+def test_ctx_create_rejects_bad_device():
+    h = C.c_void_p()
+    rc = xk.lib().xkv_ctx_create(-1, 0, C.byref(h))
+    assert rc in (L.XKV_EINVAL, L.XKV_EHIP)
+
+
+@pytest.mark.parametrize("n,nvec", [(1, 1), (2, 1), (7, 3), (60, 60), (200, 40)])
+def test_host_eigh_matches_lapack(n, nvec):
+    rng = np.random.default_rng(n)
+    G = rng.standard_normal((n, n))
+    H = (G * np.arange(1, n + 1) ** -0.8) @ G.T            # graded, PSD like Q^T C Q
+    w, Z = xk.host_eigh(H, nvec)
+    ref_w = np.linalg.eigvalsh(H)[::-1][:nvec]
+    np.testing.assert_allclose(w, ref_w, rtol=1e-11, atol=1e-12 * ref_w[0])
+    np.testing.assert_allclose(Z.T @ Z, np.eye(nvec), atol=1e-12)
+    np.testing.assert_allclose(H @ Z, Z * w, atol=1e-11 * abs(ref_w[0]))
+
+
+def test_host_eigh_clustered_and_degenerate():
+    rng = np.random.default_rng(0)
+    Q, _ = np.linalg.qr(rng.standard_normal((50, 50)))
+    lam = np.concatenate([np.full(10, 5.0), 5.0 + 1e-12 * np.arange(10), np.linspace(1, 2, 30)])
+    H = (Q * lam) @ Q.T
+    w, Z = xk.host_eigh(H, 20)
+    np.testing.assert_allclose(np.sort(w), np.sort(lam)[-20:], atol=1e-12)
+    P = Z @ Z.T
+    Pref = Q[:, :20] @ Q[:, :20].T
+    np.testing.assert_allclose(P, Pref, atol=1e-9)
+
+
+def test_host_eigh_rejects_bad_args():
+    with pytest.raises(xk.XkvError):
+        xk.host_eigh(np.eye(4), 5)

@@ -1,0 +1,321 @@
+#!/usr/bin/env python
+"""Benchmark of the xKV hot path on one MI355X.
+
+Workload (default): the Llama-3.1-8B-shaped 64k-token cache -- 32 layers in 8
+groups of G=4, 8 KV heads x 128, 32 query heads, T=65536, rank 512 for K and V,
+bf16, batch 1, chunk 8, top-k 256 chunks + 4 sink + 64 local, 128 decode steps
+appending uncompressed tokens.  Inputs are synthetic (synth/), generated on the
+GPU before timing.
+
+One step = the whole hot path over the workload: compress all 16 group sides
+(Gram, subspace iteration, host Rayleigh-Ritz, projection, landmarks), then the
+decode steps through every layer (append, landmark scores, top-k, rebuild +
+attend + merge).  The JSON line reports:
+  value    SR decode microseconds per decode step (all layers), higher_is_better false
+  sr_decode_GBps, compress_tokens_per_s, compress breakdown
+  roofline      attend kernel vs HBM (union-of-rows algorithmic bytes / event-timed duration)
+  roofline_gram Gram kernel vs bf16 MFMA peak
+  cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="llama64k")
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
+              "the multi-GPU sharding of the path is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import kv_cache_cross_amd as xk
+    from kv_cache_cross_amd import _lib as L
+    from synth import make_workload
+
+    wl = make_workload(args.config, seed=args.seed, device="cuda:0")
+    c = wl.cfg
+    if c.batch != 1:
+        raise SystemExit("bench.py times the batch-1 workloads (llama64k, llama16k, qwen122k, tiny)")
+    D = args.decode_steps if args.decode_steps is not None else c.decode_steps
+    Lyr, G, d_kv, T, r, H, d, Hq = c.n_layers, c.group, c.d_kv, c.T, c.rank, c.n_kv_heads, c.head_dim, c.n_q_heads
+    dt = c.torch_dtype
+    esz = 2 if dt == torch.bfloat16 else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {c.name}: L={Lyr} G={G} H_kv={H} d={d} H_q={Hq} T={T} r={r} top_k={c.top_k} "
+        f"decode steps={D}")
+
+    # ---- inputs, resident in HBM before timing ----
+    t0 = time.time()
+    layers = {(s, l): wl.layer_kv(0, s, l) for s in "KV" for l in range(Lyr)}
+    wl._latent.clear()
+    q_all = torch.stack([torch.stack([wl.query(0, l, s) for l in range(Lyr)]) for s in range(D)]).contiguous()
+    if c.append:
+        kn_all = torch.stack([torch.stack([wl.new_token(0, "K", l, s) for l in range(Lyr)]) for s in range(D)])
+        vn_all = torch.stack([torch.stack([wl.new_token(0, "V", l, s) for l in range(Lyr)]) for s in range(D)])
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    ctx = xk.Context(0)
+    n_groups = c.n_groups
+    desc = L.make_desc(T=T, G=G, d_kv=d_kv, r=r, dtype=xk.dtype_code(dt), n_kv_heads=H, head_dim=d, chunk=c.chunk,
+                       rope_theta=c.rope_theta)
+    sides, outs = [], []
+    for g in range(n_groups):
+        for s in "KV":
+            o = {"A": torch.empty((T, r), dtype=dt, device=dev), "Bt": torch.empty((G * d_kv, r), dtype=dt, device=dev),
+                 "landmarks": torch.empty((G, H, T // c.chunk, d), dtype=dt, device=dev) if s == "K" else None}
+            outs.append(o)
+            sides.append({"layers": [layers[(s, g * G + i)] for i in range(G)], **o})
+    S = len(sides)
+    cws = torch.empty(L.compress_ws_size(desc, S), dtype=torch.uint8, device=dev)
+    log(f"[bench] compress workspace {cws.numel() / 2**30:.2f} GiB for {S} group sides")
+
+    # ---- decode buffers: exact tails, selections, outputs ----
+    rows = list(range(c.n_sink)) + list(range(T - c.n_local, T))
+    n_tail = len(rows) + (D if c.append else 0)
+    k_tail = torch.zeros((Lyr, n_tail, d_kv), dtype=dt, device=dev)
+    v_tail = torch.zeros_like(k_tail)
+    for l in range(Lyr):
+        k_tail[l, :len(rows)] = layers[("K", l)][rows]
+        v_tail[l, :len(rows)] = layers[("V", l)][rows]
+    sel = torch.full((D, Lyr, H, c.top_k), -1, dtype=torch.int32, device=dev)
+    out = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
+    dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk, top_k=c.top_k,
+                          n_sink=c.n_sink, n_local=c.n_local, r_k=r, r_v=r, dtype=dt, device=dev,
+                          rope_theta=c.rope_theta)
+    step_args = []
+    for s in range(D):
+        arr = []
+        for l in range(Lyr):
+            g, li = divmod(l, G)
+            oK, oV = outs[2 * g], outs[2 * g + 1]
+            a = dec.args(n_gen=(s + 1) if c.append else 0, q=q_all[s, l], A_k=oK["A"],
+                         Bt_k=oK["Bt"][li * d_kv:(li + 1) * d_kv], A_v=oV["A"], Bt_v=oV["Bt"][li * d_kv:(li + 1) * d_kv],
+                         landmarks=oK["landmarks"][li], k_tail=k_tail[l], v_tail=v_tail[l],
+                         k_new=kn_all[s, l] if c.append else None, v_new=vn_all[s, l] if c.append else None)
+            a.out = out[l].data_ptr()
+            a.sel = sel[s, l].data_ptr()
+            arr.append(a)
+        step_args.append(L.sr_args_array(arr))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * Lyr)] for _ in range(D)]
+    for evs in events:
+        for e in evs:
+            e.record()          # creates the underlying HIP events
+    torch.cuda.synchronize()
+
+    def compress():
+        _, stats = L.compress_sides(ctx, desc, sides, cws)
+        return stats
+
+    def decode(timed):
+        for s in range(D):
+            L.sr_decode_layers(ctx, step_args[s], dec.ws, attend_events=events[s] if timed else None)
+
+    # ---- warmup ----
+    for _ in range(args.warmup):
+        compress()
+        decode(False)
+    torch.cuda.synchronize()
+
+    # ---- timed steps ----
+    t_comp, t_dec, attend_ms, stats = [], [], [], None
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        a0 = time.perf_counter()
+        stats = compress()
+        torch.cuda.synchronize()
+        a1 = time.perf_counter()
+        decode(True)
+        torch.cuda.synchronize()
+        a2 = time.perf_counter()
+        t_comp.append(a1 - a0)
+        t_dec.append(a2 - a1)
+        attend_ms.append(np.array([[events[s][2 * l].elapsed_time(events[s][2 * l + 1]) for l in range(Lyr)]
+                                   for s in range(D)]))
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+
+    # ---- algorithmic bytes of the last step's decode (from its actual selections) ----
+    n_cand = -(-(T - c.n_local) // c.chunk)
+    sel_np = sel.cpu().numpy()
+    union_rows = np.zeros((D, Lyr))
+    perhead_rows = np.zeros((D, Lyr))
+    for s in range(D):
+        for l in range(Lyr):
+            ch = sel_np[s, l]
+            valid = ch[ch >= 0]
+            u = np.unique(valid)
+            def rows_of(cs):
+                n = len(cs) * c.chunk
+                n -= np.sum(np.clip(c.n_sink - cs * c.chunk, 0, c.chunk))     # sink rows are exact
+                return n
+            union_rows[s, l] = rows_of(u)
+            perhead_rows[s, l] = sum(rows_of(ch[h][ch[h] >= 0]) for h in range(H))
+    n_gen = np.arange(1, D + 1)[:, None] if c.append else np.zeros((D, 1))
+    tail_bytes = (c.n_sink + c.n_local + n_gen) * d_kv * esz * 2
+    attend_union = union_rows * r * esz * 2 + 2 * d_kv * r * esz + tail_bytes + Hq * d * (esz + 4)
+    attend_perhead = perhead_rows * r * esz * 2 + 2 * d_kv * r * esz + tail_bytes + Hq * d * (esz + 4)
+    select_bytes = H * n_cand * d * esz + Hq * d * esz + (2 * d_kv * esz * 2 if c.append else 0)
+    decode_bytes_step = float(np.mean(np.sum(attend_union + select_bytes, axis=1)))
+    att_ms = np.mean(attend_ms[-1:], axis=0)                  # D x L, last step (matches sel)
+    att_ms_all = float(np.mean(attend_ms))
+    achieved_att = float(np.sum(attend_union) / (np.sum(att_ms) * 1e-3) / 1e9)
+    achieved_att_perhead = float(np.sum(attend_perhead) / (np.sum(att_ms) * 1e-3) / 1e9)
+
+    dec_us = float(np.median(t_dec)) / D * 1e6
+    comp_s = float(np.median(t_comp))
+    sr_gbps = decode_bytes_step / (dec_us * 1e-6) / 1e9
+
+    # ---- Gram kernel vs bf16 MFMA peak (the compression's dominant kernel), one batched launch ----
+    n = G * d_kv
+    gram_out = torch.empty((S, n, n), dtype=torch.float64, device=dev)
+    gsides = [sd["layers"] for sd in sides]
+    xk.gram(None, sides=gsides, out=gram_out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    xk.gram(None, sides=gsides, out=gram_out)
+    e1.record()
+    torch.cuda.synchronize()
+    gram_ms = e0.elapsed_time(e1)
+    gram_flops = S * float(n) * (n + 1) * T             # unique entries of C, 2T flops each
+    del gram_out
+    gram_tflops = gram_flops / (gram_ms * 1e-3) / 1e12
+
+    line = {
+        "metric": "SR decode us/step + achieved HBM GB/s; KV compress tokens/s at 64k ctx",
+        "value": round(dec_us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_total / args.steps * 1e3, 2),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: Llama-3.1-8B-shaped KV, {Lyr} layers in groups of {G}, {H} KV heads x {d}, "
+                               f"{Hq} q heads, T={T}, r={r} (K and V), xKV-SR, top-k {c.top_k} chunks of {c.chunk} "
+                               f"+ {c.n_sink} sink + {c.n_local} local, {D} decode steps, batch 1",
+                   "T": T, "layers": Lyr, "group": G, "rank": r, "top_k": c.top_k, "decode_steps": D},
+        "sr_decode_us_per_step": round(dec_us, 2),
+        "sr_decode_GBps": round(sr_gbps, 1),
+        "sr_decode_bytes_per_step": int(decode_bytes_step),
+        "compress_tokens_per_s": round(T / comp_s, 1),
+        "compress_s": round(comp_s, 4),
+        "compress_stats": {"err_est_max": float(max(st[0] for st in stats)), "sweeps": int(stats[0][2]),
+                           "rounds": int(stats[0][3])},
+        "roofline": {"bound": "hbm", "kernel": "sr_attend_kernel", "achieved": round(achieved_att, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes": "union of gathered A rows (K and V) + B_l + exact tail + q/out",
+                     "achieved_per_head_sum": round(achieved_att_perhead, 1),
+                     "avg_launch_us": round(att_ms_all * 1e3, 2)},
+        "roofline_gram": {"bound": "mfma", "kernel": "gram_bf16_kernel", "achieved": round(gram_tflops, 1),
+                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
+                          "launch_ms": round(gram_ms, 3), "sides": S},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, wl, outs, layers, q_all, kn_all if c.append else None,
+                                            vn_all if c.append else None, rows, D)
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
+def cpu_baseline(c, wl, outs, layers, q_all, kn_all, vn_all, rows, D):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    f64 = lambda t: t.detach().double().cpu().numpy()
+    d_kv = c.d_kv
+    # Decode sample: layers 0 and 1 at the first two decode steps, fed the GPU's compressed cache.
+    sample_layers, sample_steps = [0, 1], [0, 1]
+    oK, oV = outs[0], outs[1]
+    A_k, A_v = f64(oK["A"]), f64(oV["A"])
+    t_dec = 0.0
+    for l in sample_layers:
+        Bk = f64(oK["Bt"][l * d_kv:(l + 1) * d_kv]).T
+        Bv = f64(oV["Bt"][l * d_kv:(l + 1) * d_kv]).T
+        lm = f64(oK["landmarks"][l])
+        Kl, Vl = layers[("K", l)], layers[("V", l)]
+        k_ex = {t: f64(Kl[t]) for t in rows}
+        v_ex = {t: f64(Vl[t]) for t in rows}
+        for s in sample_steps:
+            if c.append:
+                k_ex[c.T + s] = f64(kn_all[s, l])
+                v_ex[c.T + s] = f64(vn_all[s, l])
+            q = f64(q_all[s, l])
+            t0 = time.perf_counter()
+            oracle.sr_decode_layer(q, T=c.T, n_gen=(s + 1) if c.append else 0, n_kv_heads=c.n_kv_heads,
+                                   chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink, n_local=c.n_local,
+                                   landmarks_l=lm, A_k=A_k, B_k_l=Bk, A_v=A_v, B_v_l=Bv, k_exact=k_ex, v_exact=v_ex)
+            t_dec += time.perf_counter() - t0
+    per_layer_step = t_dec / (len(sample_layers) * len(sample_steps))
+    us_per_step = per_layer_step * c.n_layers * 1e6
+    # Compression sample: the oracle's factorisation of one group side (K of group 0) on its
+    # first 8192 tokens; the Gram/projection parts scale with T, the n x n eigensolve does not.
+    T_s = min(8192, c.T)
+    Ks = [f64(layers[("K", i)][:T_s]) for i in range(c.group)]
+    t0 = time.perf_counter()
+    X = oracle.group_matrix(Ks)
+    C_ = oracle.gram(X)
+    t1 = time.perf_counter()
+    lam, V = oracle.eig_desc(C_)
+    t2 = time.perf_counter()
+    A = X @ V[:, :c.rank]
+    t3 = time.perf_counter()
+    lm = oracle.landmarks(Ks[0], c.n_kv_heads, c.head_dim, c.chunk)
+    t4 = time.perf_counter()
+    scale = c.T / T_s
+    side_s = (t1 - t0 + t3 - t2 + (t4 - t3) * c.group) * scale + (t2 - t1)
+    n_sides = 2 * c.n_groups
+    comp_s = side_s * n_sides
+    return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(cores), "kind": "oracle",
+            "sample": f"SR decode of layers 0-1 at decode steps 0-1 (4 layer-steps, fed the GPU's compressed cache), "
+                      f"scaled x{c.n_layers} layers; compression of one group side on its first {T_s} tokens "
+                      f"(Gram+projection+landmarks scaled x{scale:g} in T, eigensolve of n={c.n} once), "
+                      f"scaled x{n_sides} sides",
+            "compress_tokens_per_s": round(c.T / comp_s, 2),
+            "sample_seconds": round(t_dec + (t4 - t0), 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -196,14 +196,25 @@ int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
 /* xkv_sr_select followed by xkv_sr_attend. */
 int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step through `n_layers` layers in order (args[l] describes layer l;
+ * all share `ws`, which must satisfy xkv_sr_ws_size for every layer): the
+ * select and attend kernels of each layer are enqueued back to back on
+ * `stream`, with no host synchronisation.  attend_events (nullable): host array
+ * of 2*n_layers hipEvent_t; events 2l and 2l+1 are recorded on `stream`
+ * immediately before and after layer l's attend kernel (for timing). */
+int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* ws, size_t ws_bytes,
+                         void* stream, void* const* attend_events);
+
 /* ------------------------------------------------------------------------ */
 /* Component entry points used by the parity tests                           */
 /* ------------------------------------------------------------------------ */
 
-/* Gram of the concatenated layers: C (n x n float64, row stride n) = X^T X,
- * computed by the same kernel as xkv_compress_sides.  For bf16 the layer
- * pointers and ld_layer must be 16-byte aligned. */
-int xkv_gram(const void* const* layers, long ld_layer, int T, int G, int d_kv, int dtype,
+/* Gram of the concatenated layers of `n_sides` sides, one launch (the kernel
+ * and batching of xkv_compress_sides): layers (host) holds n_sides*G device
+ * pointers (side-major); C receives n_sides matrices n x n float64 (row stride
+ * n, side stride n*n), C_s = X_s^T X_s.  For bf16 the layer pointers must be
+ * 16-byte aligned and ld_layer a multiple of 8.  n_sides*G <= 256. */
+int xkv_gram(const void* const* layers, int n_sides, long ld_layer, int T, int G, int d_kv, int dtype,
              double* C, void* stream);
 
 /* Top-k of each of `rows` score rows (float32, row stride ld) over the first

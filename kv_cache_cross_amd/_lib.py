@@ -81,7 +81,8 @@ def lib():
         L.xkv_sr_ws_size.argtypes = [C.POINTER(SrArgs), C.POINTER(sz)]
         for name in ("xkv_sr_select", "xkv_sr_attend", "xkv_sr_decode"):
             getattr(L, name).argtypes = [vp, C.POINTER(SrArgs), vp, sz, vp]
-        L.xkv_gram.argtypes = [C.POINTER(vp), l, i, i, i, i, vp, vp]
+        L.xkv_sr_decode_layers.argtypes = [vp, i, C.POINTER(SrArgs), vp, sz, vp, C.POINTER(vp)]
+        L.xkv_gram.argtypes = [C.POINTER(vp), i, l, i, i, i, i, vp, vp]
         L.xkv_topk.argtypes = [vp, i, i, l, i, vp, vp]
         L.xkv_host_eigh.argtypes = [i, vp, i, vp, vp]
         _lib = L
@@ -210,15 +211,38 @@ def sr_decode(ctx, args, ws, stream=None):
     _sr_call(lib().xkv_sr_decode, ctx, args, ws, stream)
 
 
-def gram(layers, stream=None) -> torch.Tensor:
-    """X^T X of the horizontally concatenated layers (float64, n x n) on the layers' device."""
-    G = len(layers)
-    T, d_kv = layers[0].shape
-    out = torch.empty((G * d_kv, G * d_kv), dtype=torch.float64, device=layers[0].device)
-    ptrs = (C.c_void_p * G)(*[t.data_ptr() for t in layers])
-    _check(lib().xkv_gram(ptrs, layers[0].stride(0), T, G, d_kv, _dtype_code(layers[0]), _ptr(out),
+def sr_args_array(args_list):
+    """Pack SrArgs into a C array for sr_decode_layers."""
+    arr = (SrArgs * len(args_list))()
+    for i, a in enumerate(args_list):
+        arr[i] = a
+    return arr
+
+
+def sr_decode_layers(ctx, arr, ws, stream=None, attend_events=None):
+    """One decode step through len(arr) layers; arr from sr_args_array.  attend_events: optional
+    list of 2*len(arr) torch.cuda.Event (enable_timing=True), recorded around each attend kernel."""
+    ev = None
+    if attend_events is not None:
+        ev = (C.c_void_p * len(attend_events))(*[e.cuda_event for e in attend_events])
+    _check(lib().xkv_sr_decode_layers(ctx.handle, len(arr), arr, _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream), ev))
+
+
+def gram(layers, stream=None, sides=None, out=None) -> torch.Tensor:
+    """X^T X of the horizontally concatenated layers (float64, n x n) on the layers' device.
+    With ``sides`` (a list of layer lists) all sides go in one launch and the result is
+    n_sides x n x n."""
+    groups = sides if sides is not None else [layers]
+    S, G = len(groups), len(groups[0])
+    T, d_kv = groups[0][0].shape
+    n = G * d_kv
+    if out is None:
+        out = torch.empty((S, n, n), dtype=torch.float64, device=groups[0][0].device)
+    ptrs = (C.c_void_p * (S * G))(*[t.data_ptr() for g in groups for t in g])
+    _check(lib().xkv_gram(ptrs, S, groups[0][0].stride(0), T, G, d_kv, _dtype_code(groups[0][0]), _ptr(out),
                           _stream(stream)))
-    return out
+    return out if sides is not None else out[0]
 
 
 def topk(scores: torch.Tensor, n_cand: int, k: int, stream=None) -> torch.Tensor:

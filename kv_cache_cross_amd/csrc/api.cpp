@@ -496,21 +496,22 @@ extern "C" int xkv_compress_group(xkv_ctx ctx, const xkv_compress_desc* desc, co
   return xkv_compress_sides(ctx, desc, 1, side, ws, ws_bytes, stream);
 }
 
-extern "C" int xkv_gram(const void* const* layers, long ld_layer, int T, int G, int d_kv, int dtype, double* C,
-                        void* stream) {
-  if (!layers || !C || T <= 0 || G <= 0 || G > 16 || d_kv <= 0 || d_kv % 8 || ld_layer < d_kv)
+extern "C" int xkv_gram(const void* const* layers, int n_sides, long ld_layer, int T, int G, int d_kv, int dtype,
+                        double* C, void* stream) {
+  if (!layers || !C || n_sides <= 0 || T <= 0 || G <= 0 || G > 16 || d_kv <= 0 || d_kv % 8 || ld_layer < d_kv ||
+      n_sides * G > xkv::kMaxPtrs)
     return fail(XKV_EINVAL, "xkv_gram: bad arguments");
   if (dtype != XKV_F32 && dtype != XKV_BF16) return fail(XKV_EINVAL, "xkv_gram: unknown dtype");
   xkv::PtrTable tab{};
-  for (int l = 0; l < G; ++l) {
-    if (!layers[l]) return fail(XKV_EINVAL, "xkv_gram: layer %d is NULL", l);
+  for (int l = 0; l < n_sides * G; ++l) {
+    if (!layers[l]) return fail(XKV_EINVAL, "xkv_gram: layer pointer %d is NULL", l);
     if (dtype == XKV_BF16 && (!aligned16(layers[l]) || ld_layer % 8))
       return fail(XKV_EINVAL, "xkv_gram: bf16 layers need 16-byte alignment and ld %% 8 == 0");
     tab.p[l] = layers[l];
   }
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == XKV_BF16) XKV_K(xkv::launch_gram_bf16(tab, 1, G, ld_layer, T, d_kv, C, nullptr, st));
-  else XKV_K(xkv::launch_gram_f32(tab, 1, G, ld_layer, T, d_kv, C, nullptr, st));
+  if (dtype == XKV_BF16) XKV_K(xkv::launch_gram_bf16(tab, n_sides, G, ld_layer, T, d_kv, C, nullptr, st));
+  else XKV_K(xkv::launch_gram_f32(tab, n_sides, G, ld_layer, T, d_kv, C, nullptr, st));
   return XKV_OK;
 }
 
@@ -649,4 +650,29 @@ extern "C" int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, siz
   int rc = xkv_sr_select(ctx, args, ws, ws_bytes, stream);
   if (rc) return rc;
   return xkv_sr_attend(ctx, args, ws, ws_bytes, stream);
+}
+
+extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* ws, size_t ws_bytes,
+                                    void* stream, void* const* attend_events) {
+  if (n_layers <= 0 || !args) return fail(XKV_EINVAL, "xkv_sr_decode_layers: need n_layers > 0 and args");
+  std::vector<xkv::SrParams> P(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    int rc = sr_prepare(ctx, &args[l], ws, ws_bytes, &P[l]);
+    if (rc) return rc;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    const int bf16 = args[l].dtype == XKV_BF16;
+    xkv::SrParams& p = P[l];
+    if (p.n_cand > 0 && p.top_k > 0) {
+      XKV_K(xkv::launch_sr_select(p, bf16, st));
+    } else if (args[l].k_new) {
+      p.n_cand = 0;
+      XKV_K(xkv::launch_sr_select(p, bf16, st));
+    }
+    if (attend_events) XKV_HIP(hipEventRecord((hipEvent_t)attend_events[2 * l], st));
+    XKV_K(xkv::launch_sr_attend(p, bf16, st));
+    if (attend_events) XKV_HIP(hipEventRecord((hipEvent_t)attend_events[2 * l + 1], st));
+  }
+  return XKV_OK;
 }

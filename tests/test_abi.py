@@ -84,7 +84,7 @@ def test_topk_and_gram_validation():
     assert lib.xkv_topk(None, 1, 10, 10, 2, None, None) == L.XKV_EINVAL
     assert lib.xkv_topk(16, 1, 20000, 20000, 2, 16, None) == L.XKV_EINVAL
     ptrs = (C.c_void_p * 1)(None)
-    assert lib.xkv_gram(ptrs, 64, 16, 1, 64, xk.XKV_F32, 16, None) == L.XKV_EINVAL
+    assert lib.xkv_gram(ptrs, 1, 64, 16, 1, 64, xk.XKV_F32, 16, None) == L.XKV_EINVAL
 
 
 def test_ctx_create_rejects_bad_device():

@@ -115,7 +115,7 @@ def main():
     out = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
     dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk, top_k=c.top_k,
                           n_sink=c.n_sink, n_local=c.n_local, r_k=r, r_v=r, dtype=dt, device=dev,
-                          rope_theta=c.rope_theta)
+                          rope_theta=c.rope_theta, max_gen=D if c.append else 0)
     step_args = []
     for s in range(D):
         arr = []

@@ -139,7 +139,7 @@ class Context:
 
 
 def make_desc(*, T, G, d_kv, r, dtype, n_kv_heads, head_dim, chunk=8, rope_theta=10000.0,
-              oversample=-1, fp32_iters=3, fp64_iters=1, seed=0, tol=0.0, max_rounds=0) -> CompressDesc:
+              oversample=-1, fp32_iters=3, fp64_iters=2, seed=0, tol=0.0, max_rounds=0) -> CompressDesc:
     return CompressDesc(T, G, d_kv, r, dtype, n_kv_heads, head_dim, chunk, rope_theta, oversample,
                         fp32_iters, fp64_iters, seed, tol, max_rounds)
 

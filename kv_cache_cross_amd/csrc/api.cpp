@@ -1,7 +1,7 @@
 // C ABI of libxkv: argument validation, workspace layout and the order of
 // kernel launches.  Every numeric step runs in the HIP kernels of this
 // directory or, for the Rayleigh-Ritz eigensolve only, in host_eigh.c.
-#include "../../include/xkv.h"
+#include "xkv.h"
 
 #include <hip/hip_runtime.h>
 
@@ -549,8 +549,17 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   if (a->n_sink + a->n_local + a->n_gen == 0 && k_eff == 0) return fail(XKV_EINVAL, "sr: nothing to attend");
   const int cps = 64 / a->chunk;
   const int n_splits = (k_eff + cps - 1) / cps;
-  const int vec_len = a->r_v > 0 ? a->r_v : a->head_dim;
-  if (grp * vec_len > 64 * 129) return fail(XKV_EUNSUPPORTED, "sr: query group x value rank too large");
+  if (n_cand > 32768) return fail(XKV_EUNSUPPORTED, "sr: at most 32768 candidate chunks per head");
+  const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 63) / 64);
+  if (n_splits + n_exact > 129)
+    return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact rows span more than 129 row blocks of 64");
+  {
+    // Exact tails and new tokens are read 8 elements at a time.
+    const long q = a->dtype == XKV_BF16 ? 8 : 4;
+    if (!aligned16(a->k_tail) || !aligned16(a->v_tail) || a->ld_tail % q || a->bstride_tail % q ||
+        (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new) || a->bstride_new % q)))
+      return fail(XKV_EINVAL, "sr: tails and new tokens need 16-byte alignment and strides of 16 bytes");
+  }
   if (!a->q || !a->A_k || !a->Bt_k || !a->landmarks || !a->k_tail || !a->v_tail || !a->out || !a->sel)
     return fail(XKV_EINVAL, "sr: a required pointer is NULL");
   if (a->r_v > 0 ? (!a->A_v || !a->Bt_v) : !a->V_full) return fail(XKV_EINVAL, "sr: value pointers missing");
@@ -558,10 +567,12 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   if (a->ld_A_k < a->r_k || a->ld_Bt_k < a->r_k || a->ld_tail < d_kv) return fail(XKV_EINVAL, "sr: leading dimension too small");
   if (a->r_v > 0 && (a->ld_A_v < a->r_v || a->ld_Bt_v < a->r_v)) return fail(XKV_EINVAL, "sr: value leading dimension too small");
   if (a->r_v == 0 && a->ld_V < d_kv) return fail(XKV_EINVAL, "sr: ld_V too small");
-  if (a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 64 == 0) {
+  if (a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 64 == 0 && a->r_v == a->r_k) {
+    // matrix-core path: 16-byte loads of A and Bt rows
     if (!aligned16(a->A_k) || !aligned16(a->Bt_k) || a->ld_A_k % 8 || a->ld_Bt_k % 8 || a->bstride_A_k % 8 ||
-        a->bstride_Bt_k % 8)
-      return fail(XKV_EINVAL, "sr: bf16 A_k/Bt_k need 16-byte alignment and strides that are multiples of 8");
+        a->bstride_Bt_k % 8 || !aligned16(a->A_v) || !aligned16(a->Bt_v) || a->ld_A_v % 8 || a->ld_Bt_v % 8 ||
+        a->bstride_A_v % 8 || a->bstride_Bt_v % 8)
+      return fail(XKV_EINVAL, "sr: bf16 A/Bt need 16-byte alignment and strides that are multiples of 8");
   }
   if (!aligned16(a->landmarks) || a->bstride_lm % (a->dtype == XKV_BF16 ? 8 : 4))
     return fail(XKV_EINVAL, "sr: landmarks need 16-byte alignment");
@@ -571,11 +582,12 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   p.batch = a->batch; p.Hq = a->n_q_heads; p.Hkv = a->n_kv_heads; p.d = a->head_dim; p.T = a->T;
   p.n_gen = a->n_gen; p.chunk = a->chunk; p.top_k = a->top_k; p.n_sink = a->n_sink; p.n_local = a->n_local;
   p.r_k = a->r_k; p.r_v = a->r_v; p.n_cand = n_cand; p.n_chunks = a->T / a->chunk; p.k_eff = k_eff;
-  p.n_splits = n_splits; p.grp = grp; p.cps = cps;
+  p.n_splits = n_splits; p.n_exact = n_exact; p.grp = grp; p.cps = cps;
   p.q_pos = a->n_gen > 0 ? (long)a->T + a->n_gen - 1 : a->T;
   p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));
-  p.vec_len = vec_len;
   p.scale = a->scale; p.theta = a->rope_theta;
+  for (int i = 0; i < a->head_dim / 2; ++i)
+    p.turns[i] = std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI);
   p.q = a->q;
   p.A_k = a->A_k; p.ld_A_k = a->ld_A_k; p.bs_A_k = a->bstride_A_k;
   p.Bt_k = a->Bt_k; p.ld_Bt_k = a->ld_Bt_k; p.bs_Bt_k = a->bstride_Bt_k;
@@ -591,9 +603,8 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   Carver c(nullptr);
   const size_t bh = (size_t)a->batch * a->n_kv_heads;
   c.take<float>(bh * std::max(n_cand, 1));
-  c.take<int>(bh * 2);
-  c.take<float>(bh * std::max(n_splits, 1) * grp * (2 + vec_len));
-  c.take<float>(bh * grp * (2 + a->head_dim));
+  c.take<float>(bh * std::max(n_splits, 1) * grp * (2 + a->head_dim));
+  c.take<float>(bh * n_exact * grp * (2 + a->head_dim));
   *ws_need = c.off;
   return XKV_OK;
 }
@@ -602,9 +613,8 @@ void bind_sr_ws(xkv::SrParams* p, void* ws) {
   Carver c(ws);
   const size_t bh = (size_t)p->batch * p->Hkv;
   p->scores = c.take<float>(bh * std::max(p->n_cand, 1));
-  p->counters = c.take<int>(bh * 2);
-  p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->vec_len));
-  p->part_ex = c.take<float>(bh * p->grp * (2 + p->d));
+  p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->d));
+  p->part_ex = c.take<float>(bh * p->n_exact * p->grp * (2 + p->d));
 }
 
 int sr_prepare(xkv_ctx ctx, const xkv_sr_args* a, void* ws, size_t ws_bytes, xkv::SrParams* P) {
@@ -629,12 +639,9 @@ extern "C" int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, siz
   xkv::SrParams P;
   int rc = sr_prepare(ctx, args, ws, ws_bytes, &P);
   if (rc) return rc;
-  if (P.n_cand > 0 && P.top_k > 0) XKV_K(xkv::launch_sr_select(P, args->dtype == XKV_BF16, (hipStream_t)stream));
-  else if (args->k_new) {
-    // No candidates to score: still append the new token (a one-block select launch).
-    P.n_cand = 0;
-    XKV_K(xkv::launch_sr_select(P, args->dtype == XKV_BF16, (hipStream_t)stream));
-  }
+  // The score kernel always runs: it also appends the new token and attends the exact rows.
+  XKV_K(xkv::launch_sr_score(P, args->dtype == XKV_BF16, (hipStream_t)stream));
+  XKV_K(xkv::launch_sr_topk(P, (hipStream_t)stream));
   return XKV_OK;
 }
 
@@ -643,6 +650,7 @@ extern "C" int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, siz
   int rc = sr_prepare(ctx, args, ws, ws_bytes, &P);
   if (rc) return rc;
   XKV_K(xkv::launch_sr_attend(P, args->dtype == XKV_BF16, (hipStream_t)stream));
+  XKV_K(xkv::launch_sr_merge(P, (hipStream_t)stream));
   return XKV_OK;
 }
 
@@ -664,15 +672,12 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
   for (int l = 0; l < n_layers; ++l) {
     const int bf16 = args[l].dtype == XKV_BF16;
     xkv::SrParams& p = P[l];
-    if (p.n_cand > 0 && p.top_k > 0) {
-      XKV_K(xkv::launch_sr_select(p, bf16, st));
-    } else if (args[l].k_new) {
-      p.n_cand = 0;
-      XKV_K(xkv::launch_sr_select(p, bf16, st));
-    }
+    XKV_K(xkv::launch_sr_score(p, bf16, st));
+    XKV_K(xkv::launch_sr_topk(p, st));
     if (attend_events) XKV_HIP(hipEventRecord((hipEvent_t)attend_events[2 * l], st));
     XKV_K(xkv::launch_sr_attend(p, bf16, st));
     if (attend_events) XKV_HIP(hipEventRecord((hipEvent_t)attend_events[2 * l + 1], st));
+    XKV_K(xkv::launch_sr_merge(p, st));
   }
   return XKV_OK;
 }

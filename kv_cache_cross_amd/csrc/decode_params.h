@@ -10,13 +10,14 @@ struct SrParams {
   int n_chunks;      // T / chunk (landmark rows per head)
   int k_eff;         // min(top_k, n_cand)
   int n_splits;      // 64-row splits of the selected rows
+  int n_exact;       // 64-row tiles of the exact tail (sink + local + generated), at least 1
   int grp;           // query heads per KV head
   int cps;           // chunks per split (64 / chunk)
   long q_pos;        // query position p
   int score_blocks;  // select-kernel blocks per KV head
-  int vec_len;       // length of a split's value vector: r_v, or d when values are exact
   float scale;
   double theta;
+  double turns[64];  // theta^(-2i/d) / (2 pi) for i < d/2, formed on the host in float64
   const void* q;
   const void* A_k; long ld_A_k, bs_A_k;
   const void* Bt_k; long ld_Bt_k, bs_Bt_k;
@@ -29,12 +30,15 @@ struct SrParams {
   float* out;
   int* sel;          // batch x Hkv x top_k
   float* scores;     // batch x Hkv x n_cand
-  int* counters;     // batch x Hkv x 2, zero between calls
-  float* part;       // batch x Hkv x n_splits x grp x (2 + vec_len)
-  float* part_ex;    // batch x Hkv x grp x (2 + d)
+  float* part;       // batch x Hkv x n_splits x grp x (2 + d): max, sum, output sum
+  float* part_ex;    // batch x Hkv x n_exact x grp x (2 + d)
 };
 
-hipError_t launch_sr_select(const SrParams& P, int bf16, hipStream_t st);
+// Stream-ordered stages of one decode step: scores + exact rows (+ append), top-k,
+// rebuild + attend of the selected rows, merge.
+hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st);
+hipError_t launch_sr_topk(const SrParams& P, hipStream_t st);
 hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st);
+hipError_t launch_sr_merge(const SrParams& P, hipStream_t st);
 
 }  // namespace xkv

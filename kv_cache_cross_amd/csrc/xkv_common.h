@@ -41,3 +41,13 @@ XKV_DEV void rope_cs(long t, double freq, float* c, float* s) {
   const float ar = (float)fma(-k, 6.283185307179586, a);   // 2 pi
   sincosf(ar, s, c);
 }
+
+// Decode-path variant: `turns` = theta^(-2i/d) / (2 pi) comes from a host table; the
+// angle t * turns is reduced to [-1/2, 1/2] turn in float64 and fed to the hardware
+// sine/cosine, which take their argument in turns (absolute error ~1e-6).
+XKV_DEV void rope_cs_turns(long t, double turns, float* c, float* s) {
+  const double a = (double)t * turns;
+  const float x = (float)(a - rint(a));
+  *s = __builtin_amdgcn_sinf(x);
+  *c = __builtin_amdgcn_cosf(x);
+}

@@ -16,7 +16,7 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def compress(ctx: L.Context, sides, *, r: int, n_kv_heads: int, head_dim: int, chunk: int = 8,
              rope_theta: float = 10000.0, landmarks=None, oversample: int = -1, fp32_iters: int = 3,
-             fp64_iters: int = 1, seed: int = 0, stream=None, ws: torch.Tensor | None = None,
+             fp64_iters: int = 2, seed: int = 0, stream=None, ws: torch.Tensor | None = None,
              keep_vr64: bool = False, tol: float = 0.0, max_rounds: int = 0):
     """Factor every group side in ``sides`` (a list of lists of G layer tensors, T x d_kv).
 
@@ -55,20 +55,22 @@ def compress(ctx: L.Context, sides, *, r: int, n_kv_heads: int, head_dim: int, c
 
 class LayerDecoder:
     """Workspace and argument builder for SR decode of one layer (reusable across layers
-    of the same shape; the workspace counters return to zero after every call)."""
+    of the same shape). The workspace is sized for up to `max_gen` generated tokens."""
 
     def __init__(self, ctx: L.Context, *, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  T: int, chunk: int, top_k: int, n_sink: int, n_local: int, r_k: int, r_v: int,
-                 dtype: torch.dtype, device, rope_theta: float = 10000.0, scale: float | None = None):
+                 dtype: torch.dtype, device, rope_theta: float = 10000.0, scale: float | None = None,
+                 max_gen: int = 64):
         self.ctx = ctx
         self.shape = dict(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, T=T,
                           chunk=chunk, top_k=top_k, n_sink=n_sink, n_local=n_local, r_k=r_k, r_v=r_v,
                           dtype=dtype_code(dtype), rope_theta=rope_theta,
                           scale=scale if scale is not None else 1.0 / math.sqrt(head_dim))
         self.device = device
+        self.max_gen = max_gen
         self.out = torch.empty((batch, n_q_heads, head_dim), dtype=torch.float32, device=device)
         self.sel = torch.full((batch, n_kv_heads, max(top_k, 1)), -1, dtype=torch.int32, device=device)
-        probe = L.sr_args(**self.shape, n_gen=0, q=1, A_k=16, ld_A_k=r_k, Bt_k=16, ld_Bt_k=r_k,
+        probe = L.sr_args(**self.shape, n_gen=max_gen, q=1, A_k=16, ld_A_k=r_k, Bt_k=16, ld_Bt_k=r_k,
                           A_v=16 if r_v else 0, ld_A_v=max(r_v, 1), Bt_v=16 if r_v else 0, ld_Bt_v=max(r_v, 1),
                           V_full=0 if r_v else 16, ld_V=n_kv_heads * head_dim, landmarks=16,
                           k_tail=16, v_tail=16, ld_tail=n_kv_heads * head_dim, out=16, sel=16)
@@ -79,6 +81,8 @@ class LayerDecoder:
              bstride_V=0, bstride_lm=0, bstride_tail=0, bstride_new=0, ld_tail=None) -> L.SrArgs:
         """Tensors may be views (e.g. a layer's rows of Bt); their data pointers are used."""
         sh = self.shape
+        if not 0 <= n_gen <= self.max_gen:
+            raise ValueError(f"n_gen={n_gen} outside the workspace's range [0, {self.max_gen}]")
         d_kv = sh["n_kv_heads"] * sh["head_dim"]
         return L.sr_args(**sh, n_gen=n_gen, q=q, A_k=A_k, ld_A_k=A_k.stride(-2), bstride_A_k=bstride_A_k,
                          Bt_k=Bt_k, ld_Bt_k=Bt_k.stride(-2), bstride_Bt_k=bstride_Bt_k,

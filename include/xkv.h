@@ -190,7 +190,9 @@ int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
 
 /* Rebuild the selected rows (A rows x B_l, then RoPE for keys), attend over
  * them and the exact rows with split-K online softmax, merge, write args->out.
- * Reads args->sel as written by xkv_sr_select. */
+ * Reads args->sel as written by xkv_sr_select.  Compressed values are applied
+ * in rank space, (sum_t p_t A_v[t]) B_v,l, which equals sum_t p_t (A_v[t] B_v,l)
+ * up to rounding. */
 int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /* xkv_sr_select followed by xkv_sr_attend. */
@@ -219,7 +221,7 @@ int xkv_gram(const void* const* layers, int n_sides, long ld_layer, int T, int G
 
 /* Top-k of each of `rows` score rows (float32, row stride ld) over the first
  * n_cand entries: ascending ids of the k largest, ties to the lower id, -1
- * padding; the same kernel as xkv_sr_select.  n_cand <= 16384. */
+ * padding; the same kernel as xkv_sr_select.  n_cand <= 32768. */
 int xkv_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, void* stream);
 
 /* Host symmetric eigensolver used for the Rayleigh-Ritz step (plain C,

@@ -516,7 +516,7 @@ extern "C" int xkv_gram(const void* const* layers, int n_sides, long ld_layer, i
 }
 
 extern "C" int xkv_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, void* stream) {
-  if (!scores || !sel || rows <= 0 || n_cand <= 0 || ld < n_cand || k <= 0 || n_cand > 16384)
+  if (!scores || !sel || rows <= 0 || n_cand <= 0 || ld < n_cand || k <= 0 || n_cand > 32768)
     return fail(XKV_EINVAL, "xkv_topk: bad arguments");
   XKV_K(xkv::launch_topk(scores, rows, n_cand, ld, k, sel, (hipStream_t)stream));
   return XKV_OK;
@@ -547,12 +547,14 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   const int n_cand = std::max(0, (a->T - a->n_local + a->chunk - 1) / a->chunk);
   const int k_eff = std::min(a->top_k, n_cand);
   if (a->n_sink + a->n_local + a->n_gen == 0 && k_eff == 0) return fail(XKV_EINVAL, "sr: nothing to attend");
-  const int cps = 64 / a->chunk;
+  const int mfma = a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 128 == 0 && a->r_v == a->r_k &&
+                   a->r_k <= xkv::MAX_RANK_MFMA;
+  const int cps = 64 / a->chunk;   // chunks per attend block of 64 rows
   const int n_splits = (k_eff + cps - 1) / cps;
   if (n_cand > 32768) return fail(XKV_EUNSUPPORTED, "sr: at most 32768 candidate chunks per head");
   const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 63) / 64);
-  if (n_splits + n_exact > 129)
-    return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact rows span more than 129 row blocks of 64");
+  if (n_splits + n_exact > 257)
+    return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact-row tiles exceed 257 attend blocks per head");
   {
     // Exact tails and new tokens are read 8 elements at a time.
     const long q = a->dtype == XKV_BF16 ? 8 : 4;
@@ -567,7 +569,8 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   if (a->ld_A_k < a->r_k || a->ld_Bt_k < a->r_k || a->ld_tail < d_kv) return fail(XKV_EINVAL, "sr: leading dimension too small");
   if (a->r_v > 0 && (a->ld_A_v < a->r_v || a->ld_Bt_v < a->r_v)) return fail(XKV_EINVAL, "sr: value leading dimension too small");
   if (a->r_v == 0 && a->ld_V < d_kv) return fail(XKV_EINVAL, "sr: ld_V too small");
-  if (a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 64 == 0 && a->r_v == a->r_k) {
+  const int vdim = mfma ? a->r_v : a->head_dim;
+  if (mfma) {
     // matrix-core path: 16-byte loads of A and Bt rows
     if (!aligned16(a->A_k) || !aligned16(a->Bt_k) || a->ld_A_k % 8 || a->ld_Bt_k % 8 || a->bstride_A_k % 8 ||
         a->bstride_Bt_k % 8 || !aligned16(a->A_v) || !aligned16(a->Bt_v) || a->ld_A_v % 8 || a->ld_Bt_v % 8 ||
@@ -582,7 +585,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   p.batch = a->batch; p.Hq = a->n_q_heads; p.Hkv = a->n_kv_heads; p.d = a->head_dim; p.T = a->T;
   p.n_gen = a->n_gen; p.chunk = a->chunk; p.top_k = a->top_k; p.n_sink = a->n_sink; p.n_local = a->n_local;
   p.r_k = a->r_k; p.r_v = a->r_v; p.n_cand = n_cand; p.n_chunks = a->T / a->chunk; p.k_eff = k_eff;
-  p.n_splits = n_splits; p.n_exact = n_exact; p.grp = grp; p.cps = cps;
+  p.n_splits = n_splits; p.n_exact = n_exact; p.grp = grp; p.cps = cps; p.mfma = mfma; p.vdim = vdim;
   p.q_pos = a->n_gen > 0 ? (long)a->T + a->n_gen - 1 : a->T;
   p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));
   p.scale = a->scale; p.theta = a->rope_theta;
@@ -603,7 +606,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   Carver c(nullptr);
   const size_t bh = (size_t)a->batch * a->n_kv_heads;
   c.take<float>(bh * std::max(n_cand, 1));
-  c.take<float>(bh * std::max(n_splits, 1) * grp * (2 + a->head_dim));
+  c.take<float>(bh * std::max(n_splits, 1) * grp * (2 + vdim));
   c.take<float>(bh * n_exact * grp * (2 + a->head_dim));
   *ws_need = c.off;
   return XKV_OK;
@@ -613,7 +616,7 @@ void bind_sr_ws(xkv::SrParams* p, void* ws) {
   Carver c(ws);
   const size_t bh = (size_t)p->batch * p->Hkv;
   p->scores = c.take<float>(bh * std::max(p->n_cand, 1));
-  p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->d));
+  p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->vdim));
   p->part_ex = c.take<float>(bh * p->n_exact * p->grp * (2 + p->d));
 }
 

@@ -12,24 +12,31 @@
 //   * block x == score_blocks attends the exact rows (sink, local window,
 //     generated tokens), which do not depend on the selection, and leaves a
 //     softmax partial (max, denominator, weighted value sum) per query head.
-// sr_topk_kernel (grid: KV heads x batch): the head's scores go to LDS as
-//   order-preserving keys; an MSB-first radix select finds the k-th key and an
-//   index-ordered compaction writes the k chunk ids (ties to the lower id).
-// sr_attend_mfma_kernel (bf16, head_dim 128, r % 64 == 0; grid: KV heads x
-// splits x batch, so one head's blocks share an XCD and its B slices in L2)
-//   * a block takes 64 rows: the selected chunks [s*64/chunk, (s+1)*64/chunk)
-//     of its head, minus rows the exact tail covers;
-//   * the gathered rows of A_k and A_v are staged into LDS with every load in
-//     flight at once (16 bytes per lane, a wave per row);
-//   * waves 0-1 rebuild k_t = A_k[t] B_k,l,h and waves 2-3 v_t = A_v[t] B_v,l,h
-//     on v_mfma_f32_32x32x16_bf16; B rows are contiguous along r and stream
-//     from L2 two k-steps ahead of the MFMAs; the key waves apply RoPE;
-//   * scores, a softmax partial and the partial output sum_t p_t v_t per query
-//     head.
+// sr_topk_kernel (grid: KV heads x batch): the head's scores go to registers as
+//   order-preserving keys; a histogram over value buckets and a radix select
+//   inside the k-th key's bucket find the k-th key, and an index-ordered
+//   compaction writes the k chunk ids (ties to the lower id).
+// sr_attend_mfma_kernel (bf16, head_dim 128, r_k == r_v, r % 128 == 0; grid: KV
+// heads x splits x batch, so one head's blocks share an XCD and its B slices in L2;
+// 512 threads, two waves per SIMD)
+//   * a block takes 64 rows: the selected chunks [s*64/chunk, (s+1)*64/chunk) of
+//     its head, minus rows the exact tail covers;
+//   * the gathered rows of A_k and A_v are staged with direct-to-LDS loads, every
+//     load in flight at once (16 bytes per lane, a wave per row), and each wave's
+//     slice of B_k,l,h goes to registers behind them;
+//   * the eight waves rebuild k_t = A_k[t] B_k,l,h, 16 key dims each, on
+//     v_mfma_f32_16x16x32_bf16 with no memory wait between MFMAs; the dims are
+//     ordered so that RoPE pairs meet in one lane group; scores and a softmax
+//     partial follow;
+//   * values are never rebuilt: since v_t = A_v[t] B_v,l,h, the block's
+//     weighted value sum is (sum_t p_t A_v[t]) B_v,l,h, and it leaves the rank-r
+//     vector sum_t p_t A_v[t] per query head.
 // sr_attend_generic_kernel covers every other shape (float32, other head
-// dims, exact values) with the same partials.
-// sr_merge_kernel (grid: KV heads x batch) merges the split partials and the
-//   exact-row partial by their log-sum-exp weights into the output.
+// dims, exact values, ranks that differ) with value-space partials.
+// sr_merge_kernel (grid: KV heads x batch) and, for the matrix-core path,
+//   sr_merge_rank_kernel (grid: KV heads x query heads per group x batch) merge
+//   the split partials and the exact-row partials by their log-sum-exp weights
+//   into the output; the latter applies B_v,l,h to the merged rank-r sum.
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 #include "decode_params.h"
@@ -37,13 +44,14 @@
 namespace xkv {
 namespace {
 
-constexpr int RB = 64;        // rows per attend block
+constexpr int RB = 64;        // rows per attend block (generic path) and per exact-row tile
+constexpr int RBM = 64;       // rows per matrix-core attend block
 constexpr int MAXG = 8;       // largest query group per KV head
 constexpr int MAXD = 128;     // largest head dim
 constexpr int KCH = 512;      // rank columns staged per pass (MFMA path)
 constexpr int AROW = KCH + 8; // padded LDS row of staged A rows (bf16 elements)
 constexpr int HROW = MAXD + 1;
-constexpr int MAXP = 129;     // splits + 1 that the merge supports
+constexpr int MAXP = 257;     // splits + exact tiles that the merge supports
 
 XKV_DEV uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -62,8 +70,11 @@ XKV_DEV float wave_max(float v) {
   return v;
 }
 
-// Inclusive prefix sum over the 256 threads of a block.
-XKV_DEV int block_scan_incl(int v, int* tmp /* >= 4 ints */) {
+constexpr int TKT = 1024;      // threads of a top-k block
+constexpr int TKW = TKT / 64;  // its waves
+
+// Inclusive prefix sum over the TKT threads of a block (`tmp` >= TKW ints).
+XKV_DEV int tk_scan_incl(int v, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -78,98 +89,194 @@ XKV_DEV int block_scan_incl(int v, int* tmp /* >= 4 ints */) {
   return v + add;
 }
 
-XKV_DEV uint32_t block_reduce_minmax(uint32_t v, bool is_max, uint32_t* tmp) {
+// Block-wide minimum of lo and maximum of hi (`tmp` >= 2 * TKW ints).
+XKV_DEV void tk_minmax(uint32_t& lo, uint32_t& hi, uint32_t* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t u = __shfl_xor(v, o);
-    v = is_max ? max(v, u) : min(v, u);
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
   }
-  if (lane == 0) tmp[wave] = v;
+  if (lane == 0) {
+    tmp[wave] = lo;
+    tmp[TKW + wave] = hi;
+  }
   __syncthreads();
-  uint32_t r = tmp[0];
-  for (int w = 1; w < 4; ++w) r = is_max ? max(r, tmp[w]) : min(r, tmp[w]);
+  lo = tmp[0];
+  hi = tmp[TKW];
+#pragma unroll
+  for (int w = 1; w < TKW; ++w) {
+    lo = min(lo, tmp[w]);
+    hi = max(hi, tmp[TKW + w]);
+  }
   __syncthreads();
-  return r;
 }
 
-// Ascending ids of the k largest keys[0..n) (order-preserving keys in LDS), ties to
-// the lower id; -1 padding when k > n.
+// Value of an order-preserving key (inverse of order_key, -0.0 read as +0.0).
+XKV_DEV float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+constexpr int NBK = 2048;   // linear value buckets of the first top-k pass
+
+// Ascending ids of the k largest of n order-preserving keys, ties to the lower id;
+// -1 padding when k > n.  A block of TKT threads; thread t holds keys t*KPT ..
+// t*KPT + KPT - 1 in registers (n <= TKT * KPT, KPT <= 32).
 //
-// MSB-first radix select with 8-bit digits, starting below the bits that every key
-// shares (found from the minimum and maximum key), with four privatised histograms
-// to spread LDS atomics, and stopping as soon as the bin holding the k-th key is
-// taken whole.  `hist` holds 4 x 256 ints, `bcast` 3 ints.
-XKV_DEV void topk_keys(const uint32_t* keys, int n, int k, int* out, int* hist, int* tmp, int* bcast) {
+// Pass 1 spreads the keys over NBK buckets linear in value between the minimum and
+// the maximum (a monotone map, so every key of a higher bucket is larger than every
+// key of a lower one) and finds the bucket b* that holds the k-th largest key; with
+// scores spread over a range, LDS atomics rarely collide.  Inside b* an MSB-first
+// radix select with 8-bit digits, starting below the bits that b*'s keys share,
+// resolves the k-th key exactly, stopping as soon as the bin holding it is taken
+// whole.  Non-finite extremes put every key in one bucket and leave the radix
+// select to do all the work.  `hist` holds NBK ints, `tmp` 2 * TKW, `bcast` 3.
+template <int KPT>
+XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* hist, int* tmp, int* bcast) {
   const int tid = threadIdx.x;
+  const int base = tid * KPT;
   if (k <= 0) return;
   if (k >= n) {
-    for (int i = tid; i < k; i += 256) out[i] = (i < n) ? i : -1;
+    for (int i = tid; i < k; i += TKT) out[i] = (i < n) ? i : -1;
     return;
   }
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = tid; i < n; i += 256) {
-    lo = min(lo, keys[i]);
-    hi = max(hi, keys[i]);
-  }
-  lo = block_reduce_minmax(lo, false, (uint32_t*)tmp);
-  hi = block_reduce_minmax(hi, true, (uint32_t*)tmp);
-  const int common = (lo == hi) ? 32 : __clz(lo ^ hi);   // leading bits every key shares
-  uint32_t mask = common >= 32 ? 0xffffffffu : ~(0xffffffffu >> common);
-  uint32_t prefix = lo & mask;
-  int remaining = k;
-  int bit = 32 - common;                                  // bits still to resolve
-  while (bit > 0) {
-    const int w = bit >= 8 ? 8 : bit;
-    const int shift = bit - w;
-    const uint32_t dmask = (1u << w) - 1u;
-    for (int i = tid; i < 1024; i += 256) hist[i] = 0;
-    __syncthreads();
-    int* h4 = hist + ((tid & 3) << 8);
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&h4[(key >> shift) & dmask], 1);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (base + u < n) {
+      lo = min(lo, kr[u]);
+      hi = max(hi, kr[u]);
     }
-    __syncthreads();
-    const int v = hist[255 - tid] + hist[256 + 255 - tid] + hist[512 + 255 - tid] + hist[768 + 255 - tid];
-    const int incl = block_scan_incl(v, tmp);   // keys with digit >= 255 - tid
-    const int excl = incl - v;                  // keys with digit >  255 - tid
-    if (v > 0 && excl < remaining && remaining <= incl) {
-      bcast[0] = 255 - tid;
-      bcast[1] = remaining - excl;
-      bcast[2] = v;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)bcast[0] << shift;
-    mask |= dmask << shift;
-    remaining = bcast[1];
-    const bool whole = bcast[1] == bcast[2];   // the k-th key's bin is taken entirely
-    __syncthreads();
-    bit = shift;
-    if (whole) break;
+  tk_minmax(lo, hi, (uint32_t*)tmp);
+  const float fmin = key_value(lo), fmax = key_value(hi);
+  float inv = 0.f;
+  if (__builtin_isfinite(fmin) && __builtin_isfinite(fmax) && fmax > fmin) {
+    inv = (float)NBK / (fmax - fmin);
+    if (!__builtin_isfinite(inv)) inv = 0.f;
   }
-  // Keys above the threshold prefix, then the first `remaining` keys equal to it in id order.
-  const int seg = (n + 255) / 256;
-  const int s0 = min(n, tid * seg), s1 = min(n, s0 + seg);
-  int gt = 0, eq = 0;
-  for (int i = s0; i < s1; ++i) {
-    const uint32_t key = keys[i] & mask;
-    gt += key > prefix;
-    eq += key == prefix;
-  }
-  const int eq_before = block_scan_incl(eq, tmp) - eq;
-  const int take_eq = max(0, min(eq, remaining - eq_before));
-  const int mine = gt + take_eq;
-  int pos = block_scan_incl(mine, tmp) - mine;
-  int seen = 0;
-  for (int i = s0; i < s1; ++i) {
-    const uint32_t key = keys[i] & mask;
-    if (key > prefix) {
-      out[pos++] = i;
-    } else if (key == prefix) {
-      if (seen < take_eq) out[pos++] = i;
-      ++seen;
+  int bk[KPT];   // bucket of each key, -1 past n
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    bk[u] = (base + u >= n) ? -1 : (inv == 0.f) ? 0 : (int)fminf((key_value(kr[u]) - fmin) * inv, (float)(NBK - 1));
+
+  // Pass 1: bucket histogram, then the bucket b* holding the k-th largest key.
+  for (int i = tid; i < NBK; i += TKT) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (bk[u] >= 0) atomicAdd(&hist[bk[u]], 1);
+  __syncthreads();
+  {
+    constexpr int BPT = NBK / TKT;       // buckets per thread
+    const int top = NBK - 1 - BPT * tid; // this thread's buckets top, top-1, ...
+    int v = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) v += hist[top - u];
+    const int incl = tk_scan_incl(v, tmp);   // keys in buckets >= top - BPT + 1
+    int c = incl - v;                         // keys in buckets > top
+    if (c < k && k <= incl) {
+      for (int u = 0; u < BPT; ++u) {
+        const int hb = hist[top - u];
+        if (c + hb >= k) {
+          bcast[0] = top - u;
+          bcast[1] = c;
+          bcast[2] = hb;
+          break;
+        }
+        c += hb;
+      }
     }
+  }
+  __syncthreads();
+  const int bstar = bcast[0];
+  int remaining = k - bcast[1];   // keys still to take from b*, 1..|b*|
+  const int m_b = bcast[2];
+  __syncthreads();
+
+  // Pass 2: radix select of the remaining-th largest key inside b*.
+  uint32_t mask = 0u, prefix = 0u;
+  if (remaining < m_b) {
+    uint32_t lo2 = 0xffffffffu, hi2 = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (bk[u] == bstar) {
+        lo2 = min(lo2, kr[u]);
+        hi2 = max(hi2, kr[u]);
+      }
+    tk_minmax(lo2, hi2, (uint32_t*)tmp);
+    const int common = (lo2 == hi2) ? 32 : __clz(lo2 ^ hi2);   // leading bits b*'s keys share
+    mask = common >= 32 ? 0xffffffffu : ~(0xffffffffu >> common);
+    prefix = lo2 & mask;
+    int bit = 32 - common;                                     // bits still to resolve
+    while (bit > 0) {
+      const int w = bit >= 8 ? 8 : bit;
+      const int shift = bit - w;
+      const uint32_t dmask = (1u << w) - 1u;
+      for (int i = tid; i < 256; i += TKT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (bk[u] == bstar && (kr[u] & mask) == prefix) atomicAdd(&hist[(kr[u] >> shift) & dmask], 1);
+      __syncthreads();
+      const int v = tid < 256 ? hist[255 - tid] : 0;
+      const int incl = tk_scan_incl(v, tmp);   // keys with digit >= 255 - tid
+      const int excl = incl - v;               // keys with digit >  255 - tid
+      if (v > 0 && excl < remaining && remaining <= incl) {
+        bcast[0] = 255 - tid;
+        bcast[1] = remaining - excl;
+        bcast[2] = v;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)bcast[0] << shift;
+      mask |= dmask << shift;
+      remaining = bcast[1];
+      const bool whole = bcast[1] == bcast[2];   // the k-th key's bin is taken entirely
+      __syncthreads();
+      bit = shift;
+      if (whole) break;
+    }
+  }
+  // Keys of higher buckets and keys of b* above the threshold prefix, then the first
+  // `remaining` keys of b* equal to it in id order.
+  uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    gtm |= (uint32_t)(bk[u] > bstar || (bk[u] == bstar && (kr[u] & mask) > prefix)) << u;
+    eqm |= (uint32_t)(bk[u] == bstar && (kr[u] & mask) == prefix) << u;
+  }
+  const int eq = __popc(eqm);
+  const int eq_before = tk_scan_incl(eq, tmp) - eq;
+  int take = max(0, min(eq, remaining - eq_before));
+  uint32_t sel = gtm;
+  while (take-- > 0) {
+    sel |= eqm & (0u - eqm);   // lowest remaining equal key
+    eqm &= eqm - 1u;
+  }
+  const int mine = __popc(sel);
+  int pos = tk_scan_incl(mine, tmp) - mine;
+  while (sel) {
+    out[pos++] = base + __ffs(sel) - 1;
+    sel &= sel - 1u;
+  }
+}
+
+// Order-preserving keys of scores[0..n) for thread t's slice t*KPT .. t*KPT + KPT - 1
+// (16-byte loads when the slice is 16-byte aligned).
+template <int KPT>
+XKV_DEV void load_keys(const float* scores, int n, uint32_t (&kr)[KPT]) {
+  const int base = threadIdx.x * KPT;
+  if (KPT % 4 == 0 && (((uintptr_t)scores) & 15) == 0 && base + KPT <= n) {
+#pragma unroll
+    for (int u = 0; u < KPT; u += 4) {
+      const float4 f = *(const float4*)(scores + base + u);
+      kr[u] = order_key(f.x);
+      kr[u + 1] = order_key(f.y);
+      kr[u + 2] = order_key(f.z);
+      kr[u + 3] = order_key(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) kr[u] = (base + u < n) ? order_key(scores[base + u]) : 0u;
   }
 }
 
@@ -428,32 +535,22 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
   }
 }
 
-__global__ __launch_bounds__(256) void sr_topk_kernel(SrParams P) {
-  extern __shared__ __align__(16) uint32_t keys[];
-  __shared__ int hist[1024];
-  __shared__ int tmp[8];
+template <int KPT>
+__global__ __launch_bounds__(TKT) void sr_topk_kernel(SrParams P) {
+  __shared__ int hist[NBK];
+  __shared__ int tmp[2 * TKW];
   __shared__ int bcast[4];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
   const long bh = (long)b * P.Hkv + h;
-  const float* scores = P.scores + bh * P.n_cand;
-  // Rows of the score array are 16-byte aligned only when n_cand is a multiple of 4.
-  const int n4 = (P.n_cand & 3) ? 0 : P.n_cand;
-  for (int i = tid * 4; i < n4; i += 1024) {
-    const float4 f = *(const float4*)(scores + i);
-    keys[i] = order_key(f.x);
-    keys[i + 1] = order_key(f.y);
-    keys[i + 2] = order_key(f.z);
-    keys[i + 3] = order_key(f.w);
-  }
-  for (int i = n4 + tid; i < P.n_cand; i += 256) keys[i] = order_key(scores[i]);
-  __syncthreads();
-  topk_keys(keys, P.n_cand, P.top_k, P.sel + bh * P.top_k, hist, tmp, bcast);
+  uint32_t kr[KPT];
+  load_keys<KPT>(P.scores + bh * P.n_cand, P.n_cand, kr);
+  topk_keys<KPT>(kr, P.n_cand, P.top_k, P.sel + bh * P.top_k, hist, tmp, bcast);
 }
 
 // Rows of split s: selected chunks [s*cps, (s+1)*cps) minus the exact-tail positions.
-XKV_DEV void split_rows(const SrParams& P, long bh, int s, int* rows_t) {
+XKV_DEV void split_rows(const SrParams& P, long bh, int s, int nrows, int* rows_t) {
   const int tid = threadIdx.x;
-  if (tid < RB) {
+  if (tid < nrows) {
     const int ci = s * P.cps + tid / P.chunk;
     const int c = (ci < P.k_eff) ? P.sel[bh * P.top_k + ci] : -1;
     const int t = c * P.chunk + tid % P.chunk;
@@ -480,96 +577,122 @@ XKV_DEV void write_partial(const SrParams& P, int b, int h, int s, float (*pw)[R
   }
 }
 
-__global__ __launch_bounds__(256) void sr_attend_mfma_kernel(SrParams P) {
+__global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* Ak = (uint16_t*)smem;              // [RB][AROW] staged A_k rows
-  uint16_t* Av = Ak + RB * AROW;               // [RB][AROW] staged A_v rows
-  float (*kh)[HROW] = (float (*)[HROW])smem;   // rotated keys, after the MFMA phase (aliases Ak)
-  float (*vh)[HROW] = (float (*)[HROW])(smem + RB * AROW * 2);  // values (aliases Av)
+  uint16_t* Ak = (uint16_t*)smem;              // [RBM][AROW] staged A_k rows
+  uint16_t* Av = Ak + RBM * AROW;              // [RBM][AROW] staged A_v rows
+  float (*kh)[HROW] = (float (*)[HROW])smem;   // rotated keys after the MFMAs (aliases Ak)
   __shared__ float qs[MAXG][MAXD];
-  __shared__ float pw[MAXG][RB];
-  __shared__ int rows_t[RB];
+  __shared__ __align__(16) float pw[MAXG][RBM];
+  __shared__ int rows_t[RBM];
   __shared__ float st_m[MAXG], st_l[MAXG];
   const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const long bh = (long)b * P.Hkv + h;
-  const int r = P.r_k;
+  const int r = P.r_k, grp = P.grp;
 
-  split_rows(P, bh, s, rows_t);
-  load_group_queries<uint16_t>(P, b, h, qs);
-  __syncthreads();
-
-  const bool kside = wave < 2;
-  const int cp = wave & 1;
   const uint16_t* Ag_k = (const uint16_t*)P.A_k + b * P.bs_A_k;
   const uint16_t* Ag_v = (const uint16_t*)P.A_v + b * P.bs_A_v;
-  const uint16_t* Bt = kside ? (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)h * 128 * P.ld_Bt_k
-                             : (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)h * 128 * P.ld_Bt_v;
-  const long ldB = kside ? P.ld_Bt_k : P.ld_Bt_v;
-  const uint16_t* b0 = Bt + (long)(cp * 32 + (lane & 31)) * ldB;
-  const uint16_t* b1 = b0 + 64L * ldB;
-  const uint16_t* As = kside ? Ak : Av;
-  const int half_off = (lane >> 5) * 32;
+  // Wave w rebuilds key dims 8w + m and 64 + 8w + m (m < 8) of all 64 rows: MFMA
+  // column n holds dim 8w + n for n < 8 and 56 + 8w + n for n >= 8, so the RoPE pair
+  // (i, i + 64) sits in columns n and n + 8, eight lanes apart.  Lane l reads B row
+  // dim(l % 16) over rank slice [32(l/16), 32(l/16) + 32) of each 128-wide k-block
+  // (four MFMA k-steps); the A operand is read with the same permutation of k, so the
+  // product is unchanged.
+  const int n = lane & 15, g = lane >> 4;
+  const int dim = n < 8 ? 8 * wave + n : 56 + 8 * wave + n;
+  const uint16_t* b0 = (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)(h * 128 + dim) * P.ld_Bt_k + 32 * g;
 
-  f32x16_t acc[2][2];
+  // Prologue, ordered so that independent loads overlap: the selected chunk ids, the
+  // raw queries and the first chunk's B slice are all in flight before anything
+  // waits; the queries are rotated while the A rows stream in.
+  int csel = -1;
+  if (tid < RBM) {
+    const int ci = s * P.cps + tid / P.chunk;
+    if (ci < P.k_eff) csel = P.sel[bh * P.top_k + ci];
+  }
+  const uint16_t* qg = (const uint16_t*)P.q + ((long)b * P.Hq + (long)h * grp) * 128;
+  uint16_t qraw[2] = {0, 0};
+  if (tid < grp * 64) {   // (query head, pair) = (tid / 64, tid % 64)
+    qraw[0] = qg[(tid >> 6) * 128 + (tid & 63)];
+    qraw[1] = qg[(tid >> 6) * 128 + (tid & 63) + 64];
+  }
+  uint4 bq[KCH / 128][4];
+  auto load_b = [&](int kc, int kw) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int kb = 0; kb < KCH / 128; ++kb) {
+      const int k0 = kc + min(kb * 128, kw - 128);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[rt][ct][j] = 0.f;
+      for (int i = 0; i < 4; ++i) bq[kb][i] = *(const uint4*)(b0 + k0 + 8 * i);
+    }
+  };
+  load_b(0, min(KCH, r));
+  if (tid < RBM) {
+    const int t = csel * P.chunk + tid % P.chunk;
+    rows_t[tid] = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
+  }
+  __syncthreads();
 
+  // Stage rank columns [kc, kc + kw) of the gathered rows of A into LDS with
+  // direct-to-LDS loads (no registers): wave w takes rows 8w..8w+7, one row per
+  // instruction, lane l bytes [16l, 16l+16).  The row id is the same on every lane of
+  // the wave.  Absent rows are zero-filled first, so that no LDS store follows a load
+  // in flight.  Lanes past the chunk read its last 16 bytes (in bounds) into columns
+  // that are never used.
+  constexpr int RPW = RBM / 8;   // rows per wave
+  int tr[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) tr[i] = rows_t[wave * RPW + i];
+  auto zero_absent = [&](uint16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if (tr[i] < 0) *(uint4*)(dst + (wave * RPW + i) * AROW + lane * 8) = make_uint4(0, 0, 0, 0);
+  };
+  auto load_rows = [&](const uint16_t* Ag, long ld, uint16_t* dst, int kc, int kw) {
+    const int col = min(lane * 8, kw - 8);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if (tr[i] >= 0)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Ag + (long)tr[i] * ld + kc + col),
+                                         (__attribute__((address_space(3))) void*)(dst + (wave * RPW + i) * AROW), 16, 0, 0);
+  };
+  zero_absent(Ak);
+  zero_absent(Av);
+  load_rows(Ag_k, P.ld_A_k, Ak, 0, min(KCH, r));
+  load_rows(Ag_v, P.ld_A_v, Av, 0, min(KCH, r));
+  if (tid < grp * 64) {
+    const int j = tid >> 6, i = tid & 63;
+    float c, sn;
+    rope_cs_turns(P.q_pos, P.turns[i], &c, &sn);
+    const float x = bf16_bits_to_f32(qraw[0]), y = bf16_bits_to_f32(qraw[1]);
+    qs[j][i] = (x * c - y * sn) * P.scale;
+    qs[j][i + 64] = (y * c + x * sn) * P.scale;
+  }
+
+  f32x4_t acc[RBM / 16];
+#pragma unroll
+  for (int rt = 0; rt < RBM / 16; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Rank chunks of KCH columns: the chunk's key rows and B slice (256 bytes per lane)
+  // are in flight when an iteration starts.  r is a multiple of 128, so a k-block past
+  // the chunk re-reads its last one (unused).
   for (int kc = 0; kc < r; kc += KCH) {
     const int kw = min(KCH, r - kc);
-    // Stage the gathered rows: wave w takes rows 16w..16w+15, lane l bytes [16l, 16l+16).
-    uint4 sk[16], sv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = rows_t[wave * 16 + i];
-      const bool ok = t >= 0 && lane * 8 < kw;
-      sk[i] = ok ? *(const uint4*)(Ag_k + (long)t * P.ld_A_k + kc + lane * 8) : make_uint4(0, 0, 0, 0);
-      sv[i] = ok ? *(const uint4*)(Ag_v + (long)t * P.ld_A_v + kc + lane * 8) : make_uint4(0, 0, 0, 0);
+    if (kc > 0) {
+      load_rows(Ag_k, P.ld_A_k, Ak, kc, kw);
+      load_b(kc, kw);
     }
-    // B slices of the first two k-steps, in flight together with the row loads.
-    uint4 bq[3][2][4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      if (st * 64 < kw) {
-        const int kb = kc + st * 64 + half_off;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bq[st][0][i] = *(const uint4*)(b0 + kb + 8 * i);
-          bq[st][1][i] = *(const uint4*)(b1 + kb + 8 * i);
-        }
-      }
-    }
-    if (lane * 8 < kw) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        *(uint4*)(Ak + (wave * 16 + i) * AROW + lane * 8) = sk[i];
-        *(uint4*)(Av + (wave * 16 + i) * AROW + lane * 8) = sv[i];
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0);   // the direct-to-LDS loads have landed
     __syncthreads();
 #pragma unroll
-    for (int st = 0; st < KCH / 64; ++st) {
-      if (st * 64 < kw) {
-        if ((st + 2) * 64 < kw) {
-          const int kb = kc + (st + 2) * 64 + half_off;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bq[(st + 2) % 3][0][i] = *(const uint4*)(b0 + kb + 8 * i);
-            bq[(st + 2) % 3][1][i] = *(const uint4*)(b1 + kb + 8 * i);
-          }
-        }
-        const int kl = st * 64 + half_off;
+    for (int kb = 0; kb < KCH / 128; ++kb) {
+      if (kb * 128 < kw) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const bf16x8_t a = as_bf16x8(*(const uint4*)(As + (rt * 32 + (lane & 31)) * AROW + kl + 8 * i));
-            acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(bq[st % 3][0][i]), acc[rt][0], 0, 0, 0);
-            acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(bq[st % 3][1][i]), acc[rt][1], 0, 0, 0);
+          for (int rt = 0; rt < RBM / 16; ++rt) {
+            const bf16x8_t a = as_bf16x8(*(const uint4*)(Ak + (rt * 16 + n) * AROW + kb * 128 + 32 * g + 8 * i));
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bq[kb][i]), acc[rt], 0, 0, 0);
           }
         }
       }
@@ -577,35 +700,26 @@ __global__ __launch_bounds__(256) void sr_attend_mfma_kernel(SrParams P) {
     __syncthreads();
   }
 
-  // Epilogue: keys get RoPE (pairs (i, i+64) sit in tiles cp and cp+2 of the same lane).
-  const int i_lo = cp * 32 + (lane & 31);
-  if (kside) {
-    const double turns = P.turns[i_lo];
+  // RoPE in registers (the pair partner is 8 lanes away), rotated keys to LDS.
+  {
+    const bool lo_half = n < 8;
+    const double turns = P.turns[8 * wave + (n & 7)];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RBM / 16; ++rt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = rt * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+      for (int v = 0; v < 4; ++v) {
+        const int row = rt * 16 + 4 * g + v;
         const int t = rows_t[row];
-        float c = 1.f, sn = 0.f;
-        if (t >= 0) rope_cs_turns(t, turns, &c, &sn);
-        const float lo = acc[rt][0][j], hi = acc[rt][1][j];
-        kh[row][i_lo] = lo * c - hi * sn;
-        kh[row][i_lo + 64] = hi * c + lo * sn;
-      }
-  } else {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = rt * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-        vh[row][i_lo] = acc[rt][0][j];
-        vh[row][i_lo + 64] = acc[rt][1][j];
+        const float x = acc[rt][v];
+        const float u = __shfl_xor(x, 8);
+        float c, sn;   // absent rows (t < 0) rotate by angle 0; their scores are masked
+        rope_cs_turns(max(t, 0), turns, &c, &sn);
+        kh[row][dim] = lo_half ? x * c - u * sn : x * c + u * sn;
       }
   }
   __syncthreads();
-  for (int e = tid; e < P.grp * RB; e += 256) {
-    const int j = e / RB, row = e % RB;
+  if (tid < grp * RBM) {
+    const int j = tid / RBM, row = tid % RBM;
     float v = -INFINITY;
     if (rows_t[row] >= 0) {
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -621,9 +735,77 @@ __global__ __launch_bounds__(256) void sr_attend_mfma_kernel(SrParams P) {
     pw[j][row] = v;
   }
   __syncthreads();
-  softmax_partial(P.grp, pw, st_m, st_l);
+  if (wave < grp) {
+    const float v = pw[wave][lane];
+    const float mx = wave_max(v);
+    const float p = (v == -INFINITY) ? 0.f : __expf(v - mx);
+    const float l = wave_sum(p);
+    pw[wave][lane] = p;
+    if (lane == 0) {
+      st_m[wave] = mx;
+      st_l[wave] = l;
+    }
+  }
   __syncthreads();
-  write_partial(P, b, h, s, pw, vh, st_m, st_l);
+
+  // Values stay in rank space: the partial holds sum_t p_t A_v[t] per query head; the
+  // merge multiplies the combined sum by B_v once.  Wave w sums its rows 8w..8w+7 for
+  // rank columns [8l, 8l+8) (lane l), reading each weight once per wave; the eight
+  // wave sums meet in LDS (over the staged rows, which are no longer read) and are
+  // added in wave order.
+  float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + r);
+  float* red = (float*)smem;   // [8 waves][grp][KCH]
+  for (int kc = 0; kc < r; kc += KCH) {
+    const int kw = min(KCH, r - kc);
+    if (kc > 0) {
+      __syncthreads();
+      load_rows(Ag_v, P.ld_A_v, Av, kc, kw);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    float o[MAXG][8];
+#pragma unroll
+    for (int j = 0; j < MAXG; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    const int c = min(lane * 8, kw - 8);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = wave * RPW + i;
+      float a[8];
+      load8<uint16_t>(Av + row * AROW + c, a);
+      // All MAXG weight rows are read (rows past grp hold unused values), so that no
+      // LDS read waits behind a branch.
+#pragma unroll
+      for (int j = 0; j < MAXG; ++j) {
+        const float p = pw[j][row];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] += p * a[e];
+      }
+    }
+    __syncthreads();
+    if (lane * 8 < kw) {
+#pragma unroll
+      for (int j = 0; j < MAXG; ++j)
+        if (j < grp) {
+          float* dst = red + (wave * grp + j) * KCH + lane * 8;
+          *(float4*)dst = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+          *(float4*)(dst + 4) = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < grp * kw; e += 512) {
+      const int j = e / kw, cc = e % kw;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) v += red[(w * grp + j) * KCH + cc];
+      part[2 * grp + (long)j * r + kc + cc] = v;
+    }
+  }
+  if (tid < grp) {
+    part[tid] = st_m[tid];
+    part[grp + tid] = st_l[tid];
+  }
 }
 
 template <typename ST>
@@ -638,7 +820,7 @@ __global__ __launch_bounds__(256) void sr_attend_generic_kernel(SrParams P) {
   const int d = P.d, half = d >> 1;
   const long bh = (long)b * P.Hkv + h;
 
-  split_rows(P, bh, s, rows_t);
+  split_rows(P, bh, s, RB, rows_t);
   load_group_queries<ST>(P, b, h, qs);
   __syncthreads();
   const ST* A = (const ST*)P.A_k + b * P.bs_A_k;
@@ -700,10 +882,10 @@ __global__ __launch_bounds__(256) void sr_attend_generic_kernel(SrParams P) {
   write_partial(P, b, h, s, pw, vh, st_m, st_l);
 }
 
-// Merge of the split partials and the exact-row partial of (b, h).  Partial q <
-// n_splits is a split, partial n_splits the exact rows.  The headers are read in one
-// parallel round into LDS; every output element then sums its partials with the
-// loads of a batch issued together.
+// Merge of (b, h)'s split partials and exact-row partials by their log-sum-exp
+// weights.  Partial q < n_splits is a split, the rest are exact-row tiles.  The
+// headers are read in one parallel round into LDS; every output element then sums
+// its partials with the loads of a batch issued together.
 __global__ __launch_bounds__(256) void sr_merge_kernel(SrParams P) {
   __shared__ float wq[MAXP][MAXG];
   __shared__ float lq[MAXP][MAXG];
@@ -753,19 +935,117 @@ __global__ __launch_bounds__(256) void sr_merge_kernel(SrParams P) {
   }
 }
 
-__global__ __launch_bounds__(256) void topk_rows_kernel(const float* scores, int n_cand, long ld, int k, int* sel) {
-  extern __shared__ __align__(16) uint32_t keys[];
-  __shared__ int hist[1024];
-  __shared__ int tmp[8];
-  __shared__ int bcast[4];
-  const float* sc = scores + blockIdx.x * ld;
-  for (int i = threadIdx.x; i < n_cand; i += 256) keys[i] = order_key(sc[i]);
+// Merge for the matrix-core path, one block per (KV head h, query head j of its group,
+// sequence b): split partials carry sum_t p_t A_v[t] (rank space), exact-row tiles carry
+// sum_t p_t v_t.  out = (sum_s w_s o_s) B_v,l,h + sum_e w_e o_e, over the weighted sum
+// of denominators.
+__global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
+  __shared__ float wq[MAXP];
+  __shared__ float lq[MAXP];
+  __shared__ float run_l;
+  __shared__ __align__(16) float orank[MAX_RANK_MFMA];
+  __shared__ float oval[MAXD];
+  __shared__ float red[4][32][65];
+  const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int grp = P.grp, d = P.d, r = P.r_v;
+  const int ns = P.n_splits, np = ns + P.n_exact;
+  const long bh = (long)b * P.Hkv + h;
+  const long sstride = (long)grp * (2 + r), estride = (long)grp * (2 + d);
+  const float* p0 = P.part + bh * ns * sstride;
+  const float* pex = P.part_ex + bh * P.n_exact * estride;
+  for (int q = tid; q < np; q += 256) {
+    const float* pq = q < ns ? p0 + q * sstride : pex + (q - ns) * estride;
+    wq[q] = pq[j];
+    lq[q] = pq[grp + j];
+  }
   __syncthreads();
-  topk_keys(keys, n_cand, k, sel + (long)blockIdx.x * k, hist, tmp, bcast);
+  if (wave == 0) {
+    float M = -INFINITY;
+    for (int q = lane; q < np; q += 64) M = fmaxf(M, wq[q]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int q = lane; q < np; q += 64) {
+      const float w = (wq[q] == -INFINITY) ? 0.f : __expf(wq[q] - M);
+      wq[q] = w;
+      L += w * lq[q];
+    }
+    L = wave_sum(L);
+    if (lane == 0) run_l = L;
+  }
+  __syncthreads();
+  // Combined rank-space sum: two columns per thread, 16 split loads in flight.
+  for (int c = 2 * tid; c < r; c += 512) {
+    constexpr int NB = 16;
+    float a0 = 0.f, a1 = 0.f;
+    for (int q0 = 0; q0 < ns; q0 += NB) {
+      float2 v[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        v[u] = (q0 + u < ns) ? *(const float2*)(p0 + (q0 + u) * sstride + 2 * grp + (long)j * r + c)
+                             : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (q0 + u < ns) {
+          a0 += wq[q0 + u] * v[u].x;
+          a1 += wq[q0 + u] * v[u].y;
+        }
+    }
+    orank[c] = a0;
+    orank[c + 1] = a1;
+  }
+  for (int i = tid; i < d; i += 256) {
+    float acc = 0.f;
+    for (int e = 0; e < P.n_exact; ++e) acc += wq[ns + e] * pex[e * estride + 2 * grp + (long)j * d + i];
+    oval[i] = acc;
+  }
+  __syncthreads();
+  // out[i] = orank . Bt_v[h*128 + i] + oval[i]: wave w takes rows [32w, 32w + 32), lane l
+  // rank columns [8l, 8l + 8) of every 512, all 32 row loads in flight; the 64 lane
+  // partials of each row are summed through LDS.
+  const uint16_t* Bt = (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)(h * d + wave * 32) * P.ld_Bt_v;
+  float acc[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) acc[u] = 0.f;
+  for (int c = lane * 8; c < r; c += 512) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = orank[c + e];
+    uint4 bw[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + c);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const uint32_t w[4] = {bw[u].x, bw[u].y, bw[u].z, bw[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[u] += o[2 * e] * __uint_as_float(w[e] << 16);
+        acc[u] += o[2 * e + 1] * __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 32; ++u) red[wave][u][lane] = acc[u];
+  __syncthreads();
+  {
+    const int u = lane >> 1, hf = lane & 1;
+    float sum = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) sum += red[wave][u][hf * 32 + k];
+    sum += __shfl_xor(sum, 1);
+    const int i = wave * 32 + u;
+    if (hf == 0) P.out[((long)b * P.Hq + (long)h * grp + j) * d + i] = (sum + oval[i]) / run_l;
+  }
 }
 
-bool use_mfma(const SrParams& P, int bf16) {
-  return bf16 && P.d == 128 && P.r_v > 0 && P.r_k == P.r_v && P.r_k % 64 == 0;
+template <int KPT>
+__global__ __launch_bounds__(TKT) void topk_rows_kernel(const float* scores, int n_cand, long ld, int k, int* sel) {
+  __shared__ int hist[NBK];
+  __shared__ int tmp[2 * TKW];
+  __shared__ int bcast[4];
+  uint32_t kr[KPT];
+  load_keys<KPT>(scores + blockIdx.x * ld, n_cand, kr);
+  topk_keys<KPT>(kr, n_cand, k, sel + (long)blockIdx.x * k, hist, tmp, bcast);
 }
 
 // Raise a kernel's dynamic-LDS limit once per process and kernel (to the largest size
@@ -797,21 +1077,24 @@ hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st) {
 
 hipError_t launch_sr_topk(const SrParams& P, hipStream_t st) {
   if (P.top_k <= 0) return hipSuccess;
-  const size_t lds = (size_t)(P.n_cand > 0 ? P.n_cand : 1) * 4;
-  hipError_t e = set_lds<3>(sr_topk_kernel, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sr_topk_kernel, dim3(P.Hkv, P.batch), dim3(256), lds, st, P);
+  const dim3 grid(P.Hkv, P.batch);
+  if (P.n_cand <= TKT * 2)
+    hipLaunchKernelGGL(sr_topk_kernel<2>, grid, dim3(TKT), 0, st, P);
+  else if (P.n_cand <= TKT * 8)
+    hipLaunchKernelGGL(sr_topk_kernel<8>, grid, dim3(TKT), 0, st, P);
+  else
+    hipLaunchKernelGGL(sr_topk_kernel<32>, grid, dim3(TKT), 0, st, P);
   return hipGetLastError();
 }
 
 hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st) {
   if (P.n_splits == 0) return hipSuccess;
   dim3 grid(P.Hkv, P.n_splits, P.batch);
-  if (use_mfma(P, bf16)) {
-    const size_t lds = (size_t)2 * RB * AROW * sizeof(uint16_t);
+  if (P.mfma) {
+    const size_t lds = (size_t)2 * RBM * AROW * sizeof(uint16_t);
     hipError_t e = set_lds<4>(sr_attend_mfma_kernel, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sr_attend_mfma_kernel, grid, dim3(256), lds, st, P);
+    hipLaunchKernelGGL(sr_attend_mfma_kernel, grid, dim3(512), lds, st, P);
   } else if (bf16) {
     hipLaunchKernelGGL(sr_attend_generic_kernel<uint16_t>, grid, dim3(256), 0, st, P);
   } else {
@@ -821,15 +1104,20 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st) {
 }
 
 hipError_t launch_sr_merge(const SrParams& P, hipStream_t st) {
-  hipLaunchKernelGGL(sr_merge_kernel, dim3(P.Hkv, P.batch), dim3(256), 0, st, P);
+  if (P.mfma)
+    hipLaunchKernelGGL(sr_merge_rank_kernel, dim3(P.Hkv, P.grp, P.batch), dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL(sr_merge_kernel, dim3(P.Hkv, P.batch), dim3(256), 0, st, P);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, hipStream_t st) {
-  const size_t lds = (size_t)n_cand * 4;
-  hipError_t e = set_lds<5>(topk_rows_kernel, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(256), lds, st, scores, n_cand, ld, k, sel);
+  if (n_cand <= TKT * 2)
+    hipLaunchKernelGGL(topk_rows_kernel<2>, dim3(rows), dim3(TKT), 0, st, scores, n_cand, ld, k, sel);
+  else if (n_cand <= TKT * 8)
+    hipLaunchKernelGGL(topk_rows_kernel<8>, dim3(rows), dim3(TKT), 0, st, scores, n_cand, ld, k, sel);
+  else
+    hipLaunchKernelGGL(topk_rows_kernel<32>, dim3(rows), dim3(TKT), 0, st, scores, n_cand, ld, k, sel);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 
 namespace xkv {
 
+constexpr int MAX_RANK_MFMA = 4096;
+
 struct SrParams {
   int batch, Hq, Hkv, d, T, n_gen, chunk, top_k, n_sink, n_local, r_k, r_v;
   int n_cand;        // candidate chunks (not wholly inside the local window)
@@ -12,7 +14,11 @@ struct SrParams {
   int n_splits;      // 64-row splits of the selected rows
   int n_exact;       // 64-row tiles of the exact tail (sink + local + generated), at least 1
   int grp;           // query heads per KV head
-  int cps;           // chunks per split (64 / chunk)
+  int mfma;          // matrix-core attend path (bf16, head_dim 128, r_k == r_v, r % 128 == 0,
+                     // r <= MAX_RANK_MFMA): partials hold sum_t p_t A_v[t] (rank space)
+                     // and the merge applies B_v once
+  int vdim;          // width of a split partial's weighted sum: r_v on that path, else d
+  int cps;           // chunks per split
   long q_pos;        // query position p
   int score_blocks;  // select-kernel blocks per KV head
   float scale;
@@ -30,7 +36,7 @@ struct SrParams {
   float* out;
   int* sel;          // batch x Hkv x top_k
   float* scores;     // batch x Hkv x n_cand
-  float* part;       // batch x Hkv x n_splits x grp x (2 + d): max, sum, output sum
+  float* part;       // batch x Hkv x n_splits x grp x (2 + vdim): max, sum, weighted sum
   float* part_ex;    // batch x Hkv x n_exact x grp x (2 + d)
 };
 

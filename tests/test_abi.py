@@ -65,8 +65,8 @@ def test_compress_rejects_null_context():
 
 def test_sr_ws_size_validation():
     base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, T=64, n_gen=1, chunk=8, top_k=2, n_sink=4,
-                n_local=16, r_k=64, r_v=64, dtype=xk.XKV_BF16, scale=0.1, rope_theta=1e4, q=16, A_k=16,
-                ld_A_k=64, Bt_k=16, ld_Bt_k=64, A_v=16, ld_A_v=64, Bt_v=16, ld_Bt_v=64, landmarks=16,
+                n_local=16, r_k=128, r_v=128, dtype=xk.XKV_BF16, scale=0.1, rope_theta=1e4, q=16, A_k=16,
+                ld_A_k=128, Bt_k=16, ld_Bt_k=128, A_v=16, ld_A_v=128, Bt_v=16, ld_Bt_v=128, landmarks=16,
                 k_tail=16, v_tail=16, ld_tail=256, out=16, sel=16)
     assert xk.sr_ws_size(xk.sr_args(**base)) > 0
     for bad, code in [(dict(n_q_heads=5), L.XKV_EINVAL), (dict(head_dim=96), L.XKV_EUNSUPPORTED),
@@ -82,7 +82,7 @@ def test_sr_ws_size_validation():
 def test_topk_and_gram_validation():
     lib = xk.lib()
     assert lib.xkv_topk(None, 1, 10, 10, 2, None, None) == L.XKV_EINVAL
-    assert lib.xkv_topk(16, 1, 20000, 20000, 2, 16, None) == L.XKV_EINVAL
+    assert lib.xkv_topk(16, 1, 40000, 40000, 2, 16, None) == L.XKV_EINVAL
     ptrs = (C.c_void_p * 1)(None)
     assert lib.xkv_gram(ptrs, 1, 64, 16, 1, 64, xk.XKV_F32, 16, None) == L.XKV_EINVAL
 

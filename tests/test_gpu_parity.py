@@ -52,15 +52,21 @@ def test_gram(T, G, d_kv, dt):
 
 # ----------------------------------------------------------------------------- top-k
 @pytest.mark.parametrize("n_cand,k", [(1, 1), (7, 3), (300, 8), (8184, 256), (15352, 384), (1000, 1000),
-                                      (50, 64), (4097, 1)])
+                                      (50, 64), (4097, 1), (2048, 2047), (30000, 512)])
 def test_topk_bit_exact(n_cand, k):
     log(f"topk n_cand={n_cand} k={k}")
-    rows, ld = 3, n_cand + 5
+    rows, ld = 6, n_cand + 5
     g = torch.Generator().manual_seed(n_cand * 31 + k)
     coarse = (torch.randint(-40, 40, (rows, ld), generator=g).float() / 8.0)   # many exact ties
     fine = torch.randn((rows, ld), generator=g)
     scores = torch.where(torch.rand((rows, ld), generator=g) < 0.5, coarse, fine)
     scores[1] = scores[1].abs() * 0.0 + 0.25                                    # one row all equal
+    # Infinite extremes; a range near the float limit; denormals mixed with -0.0 and +0.0.
+    scores[3, ::7] = float("inf")
+    scores[3, 3::11] = float("-inf")
+    scores[4] = fine[4] * 3e37
+    tiny = torch.randint(-3, 4, (ld,), generator=g).float() * 1e-45
+    scores[5] = torch.where(torch.rand(ld, generator=g) < 0.3, torch.tensor(-0.0), tiny)
     sel = xk.topk(scores.to(DEV), n_cand, k).cpu().numpy()
     for r in range(rows):
         ref = oracle.select_topk(scores[r, :n_cand].double().numpy(), k).tolist()

@@ -3,15 +3,16 @@
 // section 3.2).  Four kernels, ordered by the stream (no device-scope fences
 // inside any of them: on this GPU such a fence writes back the XCD's L2):
 //
-// sr_score_kernel (grid: score_blocks + 1 x KV heads x batch)
+// sr_score_kernel (grid: score_blocks + n_exact x KV heads x batch)
 //   * block (0, 0, b) appends the new token's pre-RoPE k, v to the exact tail;
 //   * blocks x < score_blocks form the scaled, rotated query sum of the KV
 //     head's query group and score a slice of the candidate chunks against the
 //     landmarks (a GEMV that streams the landmarks once, each thread's loads
 //     issued before its arithmetic);
-//   * block x == score_blocks attends the exact rows (sink, local window,
-//     generated tokens), which do not depend on the selection, and leaves a
-//     softmax partial (max, denominator, weighted value sum) per query head.
+//   * blocks x >= score_blocks attend one 32-row tile each of the exact rows
+//     (sink, local window, generated tokens), which do not depend on the
+//     selection, and leave a softmax partial (max, denominator, weighted value
+//     sum) per query head.
 // sr_topk_kernel (grid: KV heads x batch): the head's scores go to registers as
 //   order-preserving keys; a histogram over value buckets and a radix select
 //   inside the k-th key's bucket find the k-th key, and an index-ordered
@@ -46,6 +47,7 @@ namespace {
 
 constexpr int RB = 64;        // rows per attend block (generic path) and per exact-row tile
 constexpr int RBM = 64;       // rows per matrix-core attend block
+constexpr int ERB = 32;       // rows per exact-row tile
 constexpr int MAXG = 8;       // largest query group per KV head
 constexpr int MAXD = 128;     // largest head dim
 constexpr int KCH = 512;      // rank columns staged per pass (MFMA path)
@@ -331,139 +333,109 @@ XKV_DEV void softmax_partial(int grp, float (*pw)[RB], float* st_m, float* st_l)
   }
 }
 
-// Exact rows of one (sequence, head): sink, local window, generated tokens, 64 per
-// block (tile e_blk), each tile leaving its own partial.  The newest generated row is
-// read from k_new / v_new when given, since block (0, 0, b) of the same launch is
-// what copies it into the tail.
+// Exact rows of one (sequence, head): sink, local window, generated tokens, ERB per
+// block (tile e_blk), each tile leaving its own softmax partial.  The tile's rows are
+// requested before the queries, so the two latencies overlap.  The newest generated
+// row is read from k_new / v_new when given, since block (0, 0, b) of the same launch
+// is what copies it into the tail.
 template <typename ST>
 XKV_DEV void exact_rows(const SrParams& P, int b, int h, int e_blk, float (*qs)[MAXD], float* smem) {
   float (*kh)[HROW] = (float (*)[HROW])smem;
-  float (*vh)[HROW] = (float (*)[HROW])(smem + RB * HROW);
-  __shared__ float pw[MAXG][RB];
-  __shared__ int pos_t[RB];
-  __shared__ float run_m[MAXG], run_l[MAXG], run_a[MAXG];
+  float (*vh)[HROW] = (float (*)[HROW])(smem + ERB * HROW);
+  __shared__ float pw[MAXG][ERB];
+  __shared__ float st_m[MAXG], st_l[MAXG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = P.d, half = d >> 1, grp = P.grp;
   const int n_tail = P.n_sink + P.n_local + P.n_gen;
+  const int r0 = e_blk * ERB;   // this block's tile of the tail
+  auto pos_of = [&](int row) -> int {
+    if (row < P.n_sink) return row;
+    if (row < P.n_sink + P.n_local) return P.T - P.n_local + (row - P.n_sink);
+    if (row < n_tail) return P.T + (row - P.n_sink - P.n_local);
+    return -1;
+  };
   const ST* kt = (const ST*)P.k_tail + b * P.bs_tail + (long)h * d;
   const ST* vt = (const ST*)P.v_tail + b * P.bs_tail + (long)h * d;
   const ST* kn = P.k_new ? (const ST*)P.k_new + b * P.bs_new + (long)h * d : nullptr;
   const ST* vn = P.v_new ? (const ST*)P.v_new + b * P.bs_new + (long)h * d : nullptr;
-  auto krow = [&](int row) -> const ST* { return (kn && row == n_tail - 1) ? kn : kt + (long)row * P.ld_tail; };
-  auto vrow = [&](int row) -> const ST* { return (vn && row == n_tail - 1) ? vn : vt + (long)row * P.ld_tail; };
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  if (tid < MAXG) {
-    run_m[tid] = -INFINITY;
-    run_l[tid] = 0.f;
+  // Thread t loads 8-element groups t and t + 256 of the tile (row = group / (d/8)).
+  const int per_row = d >> 3;
+  float kv[2][8], vv[2][8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;
+    const int row = r0 + e / per_row, c8 = (e % per_row) * 8;
+    if (e < ERB * per_row && row < n_tail) {
+      const bool newest = kn && row == n_tail - 1;
+      load8<ST>((newest ? kn : kt + (long)row * P.ld_tail) + c8, kv[u]);
+      load8<ST>((newest ? vn : vt + (long)row * P.ld_tail) + c8, vv[u]);
+    }
   }
-  {
-    const int r0 = e_blk * RB;   // this block's tile of the tail
-    __syncthreads();
-    if (tid < RB) {
-      const int row = r0 + tid;
-      int pos = -1;
-      if (row < P.n_sink) pos = row;
-      else if (row < P.n_sink + P.n_local) pos = P.T - P.n_local + (row - P.n_sink);
-      else if (row < n_tail) pos = P.T + (row - P.n_sink - P.n_local);
-      pos_t[tid] = pos;
-    }
-    __syncthreads();
-    // Stage the tile's key and value rows (8 elements per load, every load issued first).
-    {
-      const int per_row = d >> 3;
-      constexpr int U = 4;
-      for (int e0 = tid; e0 < RB * per_row; e0 += 256 * U) {
-        float kv[U][8], vv[U][8];
+  load_group_queries<ST>(P, b, h, qs);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int e = e0 + 256 * u;
-          const int rl = e / per_row, c8 = (e % per_row) * 8;
-          if (e < RB * per_row && pos_t[rl] >= 0) {
-            load8<ST>(krow(r0 + rl) + c8, kv[u]);
-            load8<ST>(vrow(r0 + rl) + c8, vv[u]);
-          } else {
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;
+    if (e < ERB * per_row) {
+      const int rl = e / per_row, c8 = (e % per_row) * 8;
+      const bool ok = r0 + rl < n_tail;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) kv[u][x] = vv[u][x] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int e = e0 + 256 * u;
-          if (e < RB * per_row) {
-            const int rl = e / per_row, c8 = (e % per_row) * 8;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              kh[rl][c8 + x] = kv[u][x];
-              vh[rl][c8 + x] = vv[u][x];
-            }
-          }
-        }
+      for (int x = 0; x < 8; ++x) {
+        kh[rl][c8 + x] = ok ? kv[u][x] : 0.f;
+        vh[rl][c8 + x] = ok ? vv[u][x] : 0.f;
       }
     }
-    __syncthreads();
-    for (int e = tid; e < RB * half; e += 256) {
-      const int rl = e / half, i = e % half;
-      const int pos = pos_t[rl];
-      if (pos >= 0) {
-        float c, sn;
-        rope_cs_turns(pos, P.turns[i], &c, &sn);
-        const float lo = kh[rl][i], hi = kh[rl][i + half];
-        kh[rl][i] = lo * c - hi * sn;
-        kh[rl][i + half] = hi * c + lo * sn;
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < grp * RB; e += 256) {
-      const int j = e / RB, rl = e % RB;
-      float v = -INFINITY;
-      if (pos_t[rl] >= 0) {
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < d; i += 4) {
+  }
+  __syncthreads();
+  for (int e = tid; e < ERB * half; e += 256) {
+    const int rl = e / half, i = e % half;
+    float c, sn;   // rows past the tail rotate by angle 0; their scores are masked
+    rope_cs_turns(max(pos_of(r0 + rl), 0), P.turns[i], &c, &sn);
+    const float lo = kh[rl][i], hi = kh[rl][i + half];
+    kh[rl][i] = lo * c - hi * sn;
+    kh[rl][i + half] = hi * c + lo * sn;
+  }
+  __syncthreads();
+  if (tid < grp * ERB) {
+    const int j = tid / ERB, rl = tid % ERB;
+    float v = -INFINITY;
+    if (r0 + rl < n_tail) {
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < d; i += 4) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) s4[u] += qs[j][i + u] * kh[rl][i + u];
-        }
-        v = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        for (int u = 0; u < 4; ++u) s4[u] += qs[j][i + u] * kh[rl][i + u];
       }
-      pw[j][rl] = v;
+      v = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
-    __syncthreads();
-    for (int j = wave; j < grp; j += 4) {
-      const float v = pw[j][lane];
-      const float mt = wave_max(v);
-      const float mnew = fmaxf(run_m[j], mt);
-      const float p = (v == -INFINITY) ? 0.f : __expf(v - mnew);
-      const float lt = wave_sum(p);
-      pw[j][lane] = p;
-      if (lane == 0) {
-        const float alpha = (run_m[j] == -INFINITY) ? 0.f : __expf(run_m[j] - mnew);
-        run_a[j] = alpha;
-        run_l[j] = run_l[j] * alpha + lt;
-        run_m[j] = mnew;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + 256 * q;
-      if (e < grp * d) {
-        const int j = e / d, i = e % d;
-        float acc = o[q] * run_a[j];
-#pragma unroll 8
-        for (int rl = 0; rl < RB; ++rl) acc += pw[j][rl] * vh[rl][i];
-        o[q] = acc;
-      }
+    pw[j][rl] = v;
+  }
+  __syncthreads();
+  for (int j = wave; j < grp; j += 4) {
+    const float v = lane < ERB ? pw[j][lane] : -INFINITY;
+    const float mx = wave_max(v);
+    const float p = (v == -INFINITY) ? 0.f : __expf(v - mx);
+    const float l = wave_sum(p);
+    if (lane < ERB) pw[j][lane] = p;
+    if (lane == 0) {
+      st_m[j] = mx;
+      st_l[j] = l;
     }
   }
   __syncthreads();
   float* part = P.part_ex + (((long)b * P.Hkv + h) * P.n_exact + e_blk) * (long)grp * (2 + d);
   if (tid < grp) {
-    part[tid] = run_m[tid];
-    part[grp + tid] = run_l[tid];
+    part[tid] = st_m[tid];
+    part[grp + tid] = st_l[tid];
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid + 256 * q;
-    if (e < grp * d) part[2 * grp + e] = o[q];
+    if (e < grp * d) {
+      const int j = e / d, i = e % d;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int rl = 0; rl < ERB; ++rl) acc += pw[j][rl] * vh[rl][i];
+      part[2 * grp + e] = acc;
+    }
   }
 }
 
@@ -486,12 +458,12 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
     }
   }
 
-  load_group_queries<ST>(P, b, h, qs);
-  __syncthreads();
   if (blk >= P.score_blocks) {
     exact_rows<ST>(P, b, h, blk - P.score_blocks, qs, smem_f);
     return;
   }
+  load_group_queries<ST>(P, b, h, qs);
+  __syncthreads();
   for (int i = tid; i < P.d; i += 256) {
     float s = 0.f;
     for (int j = 0; j < P.grp; ++j) s += qs[j][i];
@@ -938,7 +910,9 @@ __global__ __launch_bounds__(256) void sr_merge_kernel(SrParams P) {
 // Merge for the matrix-core path, one block per (KV head h, query head j of its group,
 // sequence b): split partials carry sum_t p_t A_v[t] (rank space), exact-row tiles carry
 // sum_t p_t v_t.  out = (sum_s w_s o_s) B_v,l,h + sum_e w_e o_e, over the weighted sum
-// of denominators.
+// of denominators.  The headers, the first 32 split partials of the thread's two rank
+// columns and the first 512 rank columns of the wave's 32 rows of B_v are all in flight
+// before anything waits.
 __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   __shared__ float wq[MAXP];
   __shared__ float lq[MAXP];
@@ -952,12 +926,36 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   const int ns = P.n_splits, np = ns + P.n_exact;
   const long bh = (long)b * P.Hkv + h;
   const long sstride = (long)grp * (2 + r), estride = (long)grp * (2 + d);
-  const float* p0 = P.part + bh * ns * sstride;
+  const float* p0 = P.part + bh * ns * sstride + 2 * grp + (long)j * r;   // split q: p0[q * sstride + c]
   const float* pex = P.part_ex + bh * P.n_exact * estride;
-  for (int q = tid; q < np; q += 256) {
-    const float* pq = q < ns ? p0 + q * sstride : pex + (q - ns) * estride;
-    wq[q] = pq[j];
-    lq[q] = pq[grp + j];
+  const uint16_t* Bt = (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)(h * d + wave * 32) * P.ld_Bt_v;
+
+  float hw[2], hl[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = tid + 256 * u;
+    if (q < np) {
+      const float* pq = q < ns ? P.part + (bh * ns + q) * sstride : pex + (q - ns) * estride;
+      hw[u] = pq[j];
+      hl[u] = pq[grp + j];
+    }
+  }
+  constexpr int PF = 32;
+  const int c0 = min(2 * tid, r - 2);   // threads past r duplicate the last pair (unused)
+  float2 pv[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) pv[u] = *(const float2*)(p0 + (long)max(0, min(u, ns - 1)) * sstride + c0);
+  uint4 bw[32];
+  const int cb = min(lane * 8, r - 8);
+#pragma unroll
+  for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + cb);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = tid + 256 * u;
+    if (q < np) {
+      wq[q] = hw[u];
+      lq[q] = hl[u];
+    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -974,22 +972,31 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
     if (lane == 0) run_l = L;
   }
   __syncthreads();
-  // Combined rank-space sum: two columns per thread, 16 split loads in flight.
-  for (int c = 2 * tid; c < r; c += 512) {
-    constexpr int NB = 16;
+  // Combined rank-space sum of columns c0, c0 + 1 (and, for r > 512, further pairs).
+  {
     float a0 = 0.f, a1 = 0.f;
-    for (int q0 = 0; q0 < ns; q0 += NB) {
-      float2 v[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u)
-        v[u] = (q0 + u < ns) ? *(const float2*)(p0 + (q0 + u) * sstride + 2 * grp + (long)j * r + c)
-                             : make_float2(0.f, 0.f);
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (q0 + u < ns) {
-          a0 += wq[q0 + u] * v[u].x;
-          a1 += wq[q0 + u] * v[u].y;
-        }
+    for (int u = 0; u < PF; ++u)
+      if (u < ns) {
+        a0 += wq[u] * pv[u].x;
+        a1 += wq[u] * pv[u].y;
+      }
+    for (int q = PF; q < ns; ++q) {
+      const float2 v = *(const float2*)(p0 + (long)q * sstride + c0);
+      a0 += wq[q] * v.x;
+      a1 += wq[q] * v.y;
+    }
+    if (2 * tid < r) {
+      orank[c0] = a0;
+      orank[c0 + 1] = a1;
+    }
+  }
+  for (int c = 2 * tid + 512; c < r; c += 512) {
+    float a0 = 0.f, a1 = 0.f;
+    for (int q = 0; q < ns; ++q) {
+      const float2 v = *(const float2*)(p0 + (long)q * sstride + c);
+      a0 += wq[q] * v.x;
+      a1 += wq[q] * v.y;
     }
     orank[c] = a0;
     orank[c + 1] = a1;
@@ -1001,9 +1008,8 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   }
   __syncthreads();
   // out[i] = orank . Bt_v[h*128 + i] + oval[i]: wave w takes rows [32w, 32w + 32), lane l
-  // rank columns [8l, 8l + 8) of every 512, all 32 row loads in flight; the 64 lane
-  // partials of each row are summed through LDS.
-  const uint16_t* Bt = (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)(h * d + wave * 32) * P.ld_Bt_v;
+  // rank columns [8l, 8l + 8) of every 512; the 64 lane partials of each row are summed
+  // through LDS.
   float acc[32];
 #pragma unroll
   for (int u = 0; u < 32; ++u) acc[u] = 0.f;
@@ -1011,9 +1017,10 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = orank[c + e];
-    uint4 bw[32];
+    if (c >= 512) {
 #pragma unroll
-    for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + c);
+      for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + c);
+    }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       const uint32_t w[4] = {bw[u].x, bw[u].y, bw[u].z, bw[u].w};
@@ -1063,7 +1070,7 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st) {
   dim3 grid(P.score_blocks + P.n_exact, P.Hkv, P.batch);
-  const size_t lds = (size_t)2 * RB * HROW * 4;   // the exact block's staged rows
+  const size_t lds = (size_t)2 * ERB * HROW * 4;   // the exact blocks' staged rows
   hipError_t e;
   if (bf16) {
     if ((e = set_lds<1>(sr_score_kernel<uint16_t>, lds)) != hipSuccess) return e;

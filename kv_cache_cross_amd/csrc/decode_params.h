@@ -12,7 +12,7 @@ struct SrParams {
   int n_chunks;      // T / chunk (landmark rows per head)
   int k_eff;         // min(top_k, n_cand)
   int n_splits;      // 64-row splits of the selected rows
-  int n_exact;       // 64-row tiles of the exact tail (sink + local + generated), at least 1
+  int n_exact;       // 32-row tiles of the exact tail (sink + local + generated), at least 1
   int grp;           // query heads per KV head
   int mfma;          // matrix-core attend path (bf16, head_dim 128, r_k == r_v, r % 128 == 0,
                      // r <= MAX_RANK_MFMA): partials hold sum_t p_t A_v[t] (rank space)

@@ -25,6 +25,8 @@ def check_selection(gpu_sel, scores, k: int, band: float = NEAR_TIE):
     assert len(gpu) == keff, f"selected {len(gpu)} chunks, expected {keff}"
     assert len(set(gpu)) == keff, "duplicate chunk ids"
     assert gpu == sorted(gpu), "chunk ids not ascending"
+    if keff == 0:
+        return 0
     if keff == n:
         assert gpu == list(range(n))
         return 0

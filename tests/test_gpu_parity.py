@@ -257,6 +257,12 @@ def test_decode_topk_exceeds_candidates(ctx):
     _run_decode_case(ctx, wl, steps=2, top_k=10000, label="all chunks")
 
 
+def test_decode_exact_rows_only(ctx):
+    # top_k = 0: no split is attended and the output comes from the exact rows alone.
+    wl = make_workload("llama16k", device=DEV, **MINI)
+    _run_decode_case(ctx, wl, steps=2, top_k=0, label="exact rows only")
+
+
 def test_decode_full_rank_all_chunks_is_dense(ctx):
     # Full rank and every chunk selected: SR decode equals dense attention over [0, p].
     wl = make_workload("tiny", device=DEV)

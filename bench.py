@@ -186,11 +186,15 @@ def main():
             union_rows[s, l] = rows_of(u)
             perhead_rows[s, l] = sum(rows_of(ch[h][ch[h] >= 0]) for h in range(H))
     n_gen = np.arange(1, D + 1)[:, None] if c.append else np.zeros((D, 1))
+    # Attend kernel: the gathered rows of A_k and A_v, the layer's B_k slice and the queries.
+    attend_union = union_rows * r * esz * 2 + d_kv * r * esz + Hq * d * esz
+    attend_perhead = perhead_rows * r * esz * 2 + d_kv * r * esz + Hq * d * esz
+    # The rest of a layer's step: landmarks and queries (scoring), the appended token,
+    # the exact tail rows (K and V), B_v (applied in the merge) and the output.
     tail_bytes = (c.n_sink + c.n_local + n_gen) * d_kv * esz * 2
-    attend_union = union_rows * r * esz * 2 + 2 * d_kv * r * esz + tail_bytes + Hq * d * (esz + 4)
-    attend_perhead = perhead_rows * r * esz * 2 + 2 * d_kv * r * esz + tail_bytes + Hq * d * (esz + 4)
-    select_bytes = H * n_cand * d * esz + Hq * d * esz + (2 * d_kv * esz * 2 if c.append else 0)
-    decode_bytes_step = float(np.mean(np.sum(attend_union + select_bytes, axis=1)))
+    other_bytes = (H * n_cand * d * esz + Hq * d * esz + (2 * d_kv * esz * 2 if c.append else 0)
+                   + tail_bytes + d_kv * r * esz + Hq * d * 4)
+    decode_bytes_step = float(np.mean(np.sum(attend_union + other_bytes, axis=1)))
     att_ms = np.mean(attend_ms[-1:], axis=0)                  # D x L, last step (matches sel)
     att_ms_all = float(np.mean(attend_ms))
     achieved_att = float(np.sum(attend_union) / (np.sum(att_ms) * 1e-3) / 1e9)
@@ -241,7 +245,7 @@ def main():
                            "rounds": int(stats[0][3])},
         "roofline": {"bound": "hbm", "kernel": "sr_attend_kernel", "achieved": round(achieved_att, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes": "union of gathered A rows (K and V) + B_l + exact tail + q/out",
+                     "traffic": None, "bytes": "union over KV heads of the gathered A_k and A_v rows + B_k slice + queries",
                      "achieved_per_head_sum": round(achieved_att_perhead, 1),
                      "avg_launch_us": round(att_ms_all * 1e3, 2)},
         "roofline_gram": {"bound": "mfma", "kernel": "gram_bf16_kernel", "achieved": round(gram_tflops, 1),

@@ -22,9 +22,10 @@
 // 512 threads, two waves per SIMD)
 //   * a block takes 64 rows: the selected chunks [s*64/chunk, (s+1)*64/chunk) of
 //     its head, minus rows the exact tail covers;
-//   * the gathered rows of A_k and A_v are staged with direct-to-LDS loads, every
-//     load in flight at once (16 bytes per lane, a wave per row), and each wave's
-//     slice of B_k,l,h goes to registers behind them;
+//   * the gathered rows of A_k are staged with direct-to-LDS loads, every load in
+//     flight at once (16 bytes per lane, a wave per row), and each wave's slice of
+//     B_k,l,h goes to registers behind them; the rows of A_v go to registers while
+//     the keys are rebuilt;
 //   * the eight waves rebuild k_t = A_k[t] B_k,l,h, 16 key dims each, on
 //     v_mfma_f32_16x16x32_bf16 with no memory wait between MFMAs; the dims are
 //     ordered so that RoPE pairs meet in one lane group; scores and a softmax
@@ -552,7 +553,6 @@ XKV_DEV void write_partial(const SrParams& P, int b, int h, int s, float (*pw)[R
 __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* Ak = (uint16_t*)smem;              // [RBM][AROW] staged A_k rows
-  uint16_t* Av = Ak + RBM * AROW;              // [RBM][AROW] staged A_v rows
   float (*kh)[HROW] = (float (*)[HROW])smem;   // rotated keys after the MFMAs (aliases Ak)
   __shared__ float qs[MAXG][MAXD];
   __shared__ __align__(16) float pw[MAXG][RBM];
@@ -585,6 +585,7 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   }
   const uint16_t* qg = (const uint16_t*)P.q + ((long)b * P.Hq + (long)h * grp) * 128;
   uint16_t qraw[2] = {0, 0};
+  const double q_turns = P.turns[tid & 63];
   if (tid < grp * 64) {   // (query head, pair) = (tid / 64, tid % 64)
     qraw[0] = qg[(tid >> 6) * 128 + (tid & 63)];
     qraw[1] = qg[(tid >> 6) * 128 + (tid & 63) + 64];
@@ -628,14 +629,20 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Ag + (long)tr[i] * ld + kc + col),
                                          (__attribute__((address_space(3))) void*)(dst + (wave * RPW + i) * AROW), 16, 0, 0);
   };
+  // Value rows go to registers: lane l of wave w holds rank columns [8l, 8l+8) of rows
+  // 8w..8w+7 (absent rows read row 0 and are zeroed when used).
+  uint4 av[RPW];
+  auto load_v = [&](int kc, int kw) {
+    const int col = min(lane * 8, kw - 8);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) av[i] = *(const uint4*)(Ag_v + (long)max(tr[i], 0) * P.ld_A_v + kc + col);
+  };
   zero_absent(Ak);
-  zero_absent(Av);
   load_rows(Ag_k, P.ld_A_k, Ak, 0, min(KCH, r));
-  load_rows(Ag_v, P.ld_A_v, Av, 0, min(KCH, r));
   if (tid < grp * 64) {
     const int j = tid >> 6, i = tid & 63;
     float c, sn;
-    rope_cs_turns(P.q_pos, P.turns[i], &c, &sn);
+    rope_cs_turns(P.q_pos, q_turns, &c, &sn);
     const float x = bf16_bits_to_f32(qraw[0]), y = bf16_bits_to_f32(qraw[1]);
     qs[j][i] = (x * c - y * sn) * P.scale;
     qs[j][i + 64] = (y * c + x * sn) * P.scale;
@@ -656,6 +663,7 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     }
     __builtin_amdgcn_s_waitcnt(0);   // the direct-to-LDS loads have landed
     __syncthreads();
+    if (kc == 0) load_v(0, kw);      // value rows stream in behind the key math
 #pragma unroll
     for (int kb = 0; kb < KCH / 128; ++kb) {
       if (kb * 128 < kw) {
@@ -722,30 +730,33 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
 
   // Values stay in rank space: the partial holds sum_t p_t A_v[t] per query head; the
   // merge multiplies the combined sum by B_v once.  Wave w sums its rows 8w..8w+7 for
-  // rank columns [8l, 8l+8) (lane l), reading each weight once per wave; the eight
-  // wave sums meet in LDS (over the staged rows, which are no longer read) and are
+  // rank columns [8l, 8l+8) (lane l, from registers), reading each weight once per wave;
+  // the eight wave sums meet in LDS (over the staged key rows, no longer read) and are
   // added in wave order.
   float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + r);
   float* red = (float*)smem;   // [8 waves][grp][KCH]
   for (int kc = 0; kc < r; kc += KCH) {
     const int kw = min(KCH, r - kc);
     if (kc > 0) {
-      __syncthreads();
-      load_rows(Ag_v, P.ld_A_v, Av, kc, kw);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      __syncthreads();   // the previous chunk's wave sums have been read
+      load_v(kc, kw);
     }
     float o[MAXG][8];
 #pragma unroll
     for (int j = 0; j < MAXG; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-    const int c = min(lane * 8, kw - 8);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int row = wave * RPW + i;
+      const uint4 w4 = tr[i] >= 0 ? av[i] : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
       float a[8];
-      load8<uint16_t>(Av + row * AROW + c, a);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] = __uint_as_float(w[e] << 16);
+        a[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
       // All MAXG weight rows are read (rows past grp hold unused values), so that no
       // LDS read waits behind a branch.
 #pragma unroll
@@ -1098,7 +1109,8 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st) {
   if (P.n_splits == 0) return hipSuccess;
   dim3 grid(P.Hkv, P.n_splits, P.batch);
   if (P.mfma) {
-    const size_t lds = (size_t)2 * RBM * AROW * sizeof(uint16_t);
+    // staged key rows, later reused for the eight waves' value sums
+    const size_t lds = std::max((size_t)RBM * AROW * sizeof(uint16_t), (size_t)8 * P.grp * KCH * sizeof(float));
     hipError_t e = set_lds<4>(sr_attend_mfma_kernel, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sr_attend_mfma_kernel, grid, dim3(512), lds, st, P);

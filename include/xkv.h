@@ -202,8 +202,9 @@ int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
  * all share `ws`, which must satisfy xkv_sr_ws_size for every layer): the
  * select and attend kernels of each layer are enqueued back to back on
  * `stream`, with no host synchronisation.  attend_events (nullable): host array
- * of 2*n_layers hipEvent_t; events 2l and 2l+1 are recorded on `stream`
- * immediately before and after layer l's attend kernel (for timing). */
+ * of 2*n_layers hipEvent_t (timing enabled); events 2l and 2l+1 mark the start
+ * and the end of layer l's attend kernel (stamped by its dispatch on the
+ * matrix-core path, recorded on `stream` around the launch otherwise). */
 int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* ws, size_t ws_bytes,
                          void* stream, void* const* attend_events);
 

@@ -680,9 +680,8 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
     xkv::SrParams& p = P[l];
     XKV_K(xkv::launch_sr_score(p, bf16, st));
     XKV_K(xkv::launch_sr_topk(p, st));
-    if (attend_events) XKV_HIP(hipEventRecord((hipEvent_t)attend_events[2 * l], st));
-    XKV_K(xkv::launch_sr_attend(p, bf16, st));
-    if (attend_events) XKV_HIP(hipEventRecord((hipEvent_t)attend_events[2 * l + 1], st));
+    XKV_K(xkv::launch_sr_attend(p, bf16, st, attend_events ? (hipEvent_t)attend_events[2 * l] : nullptr,
+                                attend_events ? (hipEvent_t)attend_events[2 * l + 1] : nullptr));
     XKV_K(xkv::launch_sr_merge(p, st));
   }
   return XKV_OK;

@@ -39,6 +39,8 @@
 //   sr_merge_rank_kernel (grid: KV heads x query heads per group x batch) merge
 //   the split partials and the exact-row partials by their log-sum-exp weights
 //   into the output; the latter applies B_v,l,h to the merged rank-r sum.
+#include <hip/hip_ext.h>
+#include <algorithm>
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 #include "decode_params.h"
@@ -1105,19 +1107,32 @@ hipError_t launch_sr_topk(const SrParams& P, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st) {
-  if (P.n_splits == 0) return hipSuccess;
+hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (P.n_splits == 0) {
+    if (ev_start) {
+      hipError_t e = hipEventRecord(ev_start, st);
+      if (e == hipSuccess) e = hipEventRecord(ev_stop, st);
+      return e;
+    }
+    return hipSuccess;
+  }
   dim3 grid(P.Hkv, P.n_splits, P.batch);
   if (P.mfma) {
     // staged key rows, later reused for the eight waves' value sums
     const size_t lds = std::max((size_t)RBM * AROW * sizeof(uint16_t), (size_t)8 * P.grp * KCH * sizeof(float));
     hipError_t e = set_lds<4>(sr_attend_mfma_kernel, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sr_attend_mfma_kernel, grid, dim3(512), lds, st, P);
-  } else if (bf16) {
-    hipLaunchKernelGGL(sr_attend_generic_kernel<uint16_t>, grid, dim3(256), 0, st, P);
+    // The timing events, when given, are stamped by the dispatch itself at the
+    // kernel's start and end.
+    hipExtLaunchKernelGGL(sr_attend_mfma_kernel, grid, dim3(512), (uint32_t)lds, st, ev_start, ev_stop, 0, P);
   } else {
-    hipLaunchKernelGGL(sr_attend_generic_kernel<float>, grid, dim3(256), 0, st, P);
+    hipError_t e;
+    if (ev_start && (e = hipEventRecord(ev_start, st)) != hipSuccess) return e;
+    if (bf16)
+      hipLaunchKernelGGL(sr_attend_generic_kernel<uint16_t>, grid, dim3(256), 0, st, P);
+    else
+      hipLaunchKernelGGL(sr_attend_generic_kernel<float>, grid, dim3(256), 0, st, P);
+    if (ev_stop && (e = hipEventRecord(ev_stop, st)) != hipSuccess) return e;
   }
   return hipGetLastError();
 }

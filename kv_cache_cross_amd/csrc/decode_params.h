@@ -44,7 +44,10 @@ struct SrParams {
 // rebuild + attend of the selected rows, merge.
 hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st);
 hipError_t launch_sr_topk(const SrParams& P, hipStream_t st);
-hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st);
+// ev_start / ev_stop (optional, both or neither): timing events stamped at the attend
+// kernel's start and end.
+hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEvent_t ev_start = nullptr,
+                            hipEvent_t ev_stop = nullptr);
 hipError_t launch_sr_merge(const SrParams& P, hipStream_t st);
 
 }  // namespace xkv

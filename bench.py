@@ -254,13 +254,13 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, wl, outs, layers, q_all, kn_all if c.append else None,
+        line["cpu_baseline"] = cpu_baseline(c, wl, layers, q_all, kn_all if c.append else None,
                                             vn_all if c.append else None, rows, D)
     print(json.dumps(line), flush=True)
     ctx.close()
 
 
-def cpu_baseline(c, wl, outs, layers, q_all, kn_all, vn_all, rows, D):
+def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):
     """The float64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
     try:
@@ -269,17 +269,17 @@ def cpu_baseline(c, wl, outs, layers, q_all, kn_all, vn_all, rows, D):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     f64 = lambda t: t.detach().double().cpu().numpy()
-    d_kv = c.d_kv
-    # Decode sample: layers 0 and 1 at the first two decode steps, fed the GPU's compressed cache.
+    # Decode sample: layers 0 and 1 at the first two decode steps, on a cache of the same
+    # shapes that involves no GPU output: the generator's own rank-r factors and the
+    # oracle's landmarks of the original keys.
     sample_layers, sample_steps = [0, 1], [0, 1]
-    oK, oV = outs[0], outs[1]
-    A_k, A_v = f64(oK["A"]), f64(oV["A"])
     t_dec = 0.0
     for l in sample_layers:
-        Bk = f64(oK["Bt"][l * d_kv:(l + 1) * d_kv]).T
-        Bv = f64(oV["Bt"][l * d_kv:(l + 1) * d_kv]).T
-        lm = f64(oK["landmarks"][l])
+        A_k, Bk = (f64(x) for x in wl.factor_cache(0, "K", l, c.rank))
+        A_v, Bv = (f64(x) for x in wl.factor_cache(0, "V", l, c.rank))
+        Bk, Bv = Bk.T, Bv.T
         Kl, Vl = layers[("K", l)], layers[("V", l)]
+        lm = oracle.landmarks(f64(Kl), c.n_kv_heads, c.head_dim, c.chunk, c.rope_theta)
         k_ex = {t: f64(Kl[t]) for t in rows}
         v_ex = {t: f64(Vl[t]) for t in rows}
         for s in sample_steps:
@@ -313,7 +313,7 @@ def cpu_baseline(c, wl, outs, layers, q_all, kn_all, vn_all, rows, D):
     n_sides = 2 * c.n_groups
     comp_s = side_s * n_sides
     return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(cores), "kind": "oracle",
-            "sample": f"SR decode of layers 0-1 at decode steps 0-1 (4 layer-steps, fed the GPU's compressed cache), "
+            "sample": f"SR decode of layers 0-1 at decode steps 0-1 (4 layer-steps, on a stand-in cache of the same shapes), "
                       f"scaled x{c.n_layers} layers; compression of one group side on its first {T_s} tokens "
                       f"(Gram+projection+landmarks scaled x{scale:g} in T, eigensolve of n={c.n} once), "
                       f"scaled x{n_sides} sides",

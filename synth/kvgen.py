@@ -180,6 +180,22 @@ class Workload:
         x += cfg.sigma * self._randn((1, cfg.d_kv), "n", b, side, layer, step)
         return x[0].to(cfg.torch_dtype)
 
+    def factor_cache(self, b: int, side: str, layer: int, r: int):
+        """The generator's own rank-r factors of one layer's noise-free K or V: the first r
+        latent columns U[:, :r] (T x r) and the matching rows of diag(s) W_l, transposed
+        (d_kv x r), both in the storage dtype.  A stand-in compressed cache for decode tests
+        that involves no factorisation.  Past the latent rank R the extra r - R columns are
+        fresh N(0,1) columns with sigma-scaled N(0,1) mixing rows (the noise floor)."""
+        cfg = self.cfg
+        R = cfg.latent_rank
+        U = self.latent(b, side, self._block_of(layer))
+        A = U[:, :min(r, R)]
+        Bt = self.mixing(b, side, layer)[:min(r, R)].t()
+        if r > R:
+            A = torch.cat([A, self._randn((cfg.T, r - R), "Ux", b, side, self._block_of(layer))], dim=1)
+            Bt = torch.cat([Bt, cfg.sigma * self._randn((cfg.d_kv, r - R), "Wx", b, side, layer)], dim=1)
+        return A.contiguous().to(cfg.torch_dtype), Bt.contiguous().to(cfg.torch_dtype)
+
     def query(self, b: int, layer: int, step: int) -> torch.Tensor:
         """Pre-RoPE query of one layer at one step: H_q x d, storage dtype."""
         cfg = self.cfg

@@ -3,9 +3,10 @@
 Tolerances (parity protocol): chunk sets exact outside a 1e-3 near-tie band of
 the k-th score; ||P_gpu - P_ref||_F <= 1e-3; reconstruction relative error
 within 1e-4 of the oracle's; attention relative L2 <= 1e-2 and max abs <= 2e-2
-for bf16, <= 1e-4 relative for float32.  Unit decode parity feeds the oracle
-the GPU's own stored (bf16/fp32) A, B and landmarks, so there the only
-difference is arithmetic precision and the tighter bound 1e-3 is asserted too.
+for bf16, <= 1e-4 relative for float32.  Decode parity gives both sides the same
+cache, built by the oracle's own factorisation and rounded to the storage dtype,
+so the only difference is arithmetic precision and the tighter bound 1e-3 is
+asserted too.
 """
 import math
 
@@ -155,15 +156,31 @@ def test_compress_rank_deficient_reports_breakdown(ctx):
 
 
 # ----------------------------------------------------------------------------- decode
+def oracle_cache(wl, r, layer):
+    """The compressed cache of group 0 of sequence 0 as the oracle builds it (float64
+    truncated SVD and landmarks of the original keys), rounded to the workload's storage
+    dtype.  Both the GPU decode and the oracle decode consume these same tensors, so no
+    oracle input comes from the GPU path."""
+    c = wl.cfg
+    Ks = [f64(x) for x in wl.group_kv(0, "K", 0)]
+    Vs = [f64(x) for x in wl.group_kv(0, "V", 0)]
+    ok, ov = oracle.compress_group(Ks, r), oracle.compress_group(Vs, r)
+    lm = oracle.landmarks(Ks[layer], c.n_kv_heads, c.head_dim, c.chunk, c.rope_theta)
+    dt, d_kv = c.torch_dtype, c.d_kv
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(DEV)
+    return dict(A_k=to(ok["A"]), Bt_k=to(ok["B"][:, layer * d_kv:(layer + 1) * d_kv].T),
+                A_v=to(ov["A"]), Bt_v=to(ov["B"][:, layer * d_kv:(layer + 1) * d_kv].T), lm=to(lm))
+
+
 def _run_decode_case(ctx, wl, *, steps, top_k=None, r=None, values="compressed", layer=0, label=""):
-    """Compress group 0 of sequence 0, run `steps` decode steps of one layer on the GPU and
-    compare each with the oracle fed the GPU's stored cache."""
+    """Run `steps` decode steps of one layer of group 0, sequence 0 on the GPU and compare
+    each with the oracle on the same inputs (the oracle-built cache, exact tails, queries
+    and appended tokens)."""
     c = wl.cfg
     top_k = c.top_k if top_k is None else top_k
     r = c.rank if r is None else r
     Ks, Vs = wl.group_kv(0, "K", 0), wl.group_kv(0, "V", 0)
-    ck, cv = xk.compress(ctx, [Ks, Vs], r=r, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim, chunk=c.chunk,
-                         landmarks=[True, False])
+    cache = oracle_cache(wl, r, layer)
     d_kv, T = c.d_kv, c.T
     r_v = r if values == "compressed" else 0
     dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim,
@@ -178,8 +195,7 @@ def _run_decode_case(ctx, wl, *, steps, top_k=None, r=None, values="compressed",
     Kl, Vl = f64(Ks[layer]), f64(Vs[layer])
     k_exact = {t: Kl[t] for t in rows}
     v_exact = {t: Vl[t] for t in rows}
-    A_k, Bt_k = ck["A"], ck["Bt"][layer * d_kv:(layer + 1) * d_kv]
-    A_v, Bt_v = cv["A"], cv["Bt"][layer * d_kv:(layer + 1) * d_kv]
+    A_k, Bt_k, A_v, Bt_v, lm = cache["A_k"], cache["Bt_k"], cache["A_v"], cache["Bt_v"], cache["lm"]
     worst = (0.0, 0.0)
     for s in range(steps):
         n_gen = s + 1 if c.append else 0
@@ -190,11 +206,11 @@ def _run_decode_case(ctx, wl, *, steps, top_k=None, r=None, values="compressed",
             k_exact[T + s], v_exact[T + s] = f64(kn), f64(vn)
         args = dec.args(n_gen=n_gen, q=q, A_k=A_k, Bt_k=Bt_k, A_v=A_v if r_v else None,
                         Bt_v=Bt_v if r_v else None, V_full=None if r_v else Vs[layer],
-                        landmarks=ck["landmarks"][layer], k_tail=k_tail, v_tail=v_tail, k_new=kn, v_new=vn)
+                        landmarks=lm, k_tail=k_tail, v_tail=v_tail, k_new=kn, v_new=vn)
         out = dec.decode(args)
         torch.cuda.synchronize()
         kw = dict(T=T, n_gen=n_gen, n_kv_heads=c.n_kv_heads, chunk=c.chunk, top_k=top_k, n_sink=c.n_sink,
-                  n_local=c.n_local, landmarks_l=f64(ck["landmarks"][layer]), A_k=f64(A_k), B_k_l=f64(Bt_k).T,
+                  n_local=c.n_local, landmarks_l=f64(lm), A_k=f64(A_k), B_k_l=f64(Bt_k).T,
                   k_exact=k_exact, v_exact=v_exact)
         if r_v:
             kw.update(A_v=f64(A_v), B_v_l=f64(Bt_v).T)
@@ -269,15 +285,14 @@ def test_decode_full_rank_all_chunks_is_dense(ctx):
     c = wl.cfg
     Ks, Vs = wl.group_kv(0, "K", 0), wl.group_kv(0, "V", 0)
     n = c.n
-    ck, cv = xk.compress(ctx, [Ks, Vs], r=n, n_kv_heads=1, head_dim=c.head_dim, landmarks=[True, False],
-                         oversample=0)
+    cache = oracle_cache(wl, n, 1)
     rows = tail_rows(c.T, c.n_sink, c.n_local)
     dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=1, n_kv_heads=1, head_dim=c.head_dim, T=c.T, chunk=c.chunk,
                           top_k=10000, n_sink=c.n_sink, n_local=c.n_local, r_k=n, r_v=n, dtype=c.torch_dtype,
                           device=DEV)
     q = wl.query(0, 1, 0)
-    out = dec.decode(dec.args(n_gen=0, q=q, A_k=ck["A"], Bt_k=ck["Bt"][64:], A_v=cv["A"], Bt_v=cv["Bt"][64:],
-                              landmarks=ck["landmarks"][1], k_tail=Ks[1][rows].contiguous(),
+    out = dec.decode(dec.args(n_gen=0, q=q, A_k=cache["A_k"], Bt_k=cache["Bt_k"], A_v=cache["A_v"],
+                              Bt_v=cache["Bt_v"], landmarks=cache["lm"], k_tail=Ks[1][rows].contiguous(),
                               v_tail=Vs[1][rows].contiguous()))
     torch.cuda.synchronize()
     ref = oracle.dense_decode(f64(q), f64(Ks[1]), f64(Vs[1]), p=c.T, n_kv_heads=1)

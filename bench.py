@@ -35,6 +35,25 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
+# HBM traffic of one attend-kernel dispatch at this workload, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over 64 dispatches), each scaled by
+# what the same counter reads for a 1 GiB device-to-device copy (read 524300.5 KiB, written
+# 1048576 KiB).  It stands only while the decode kernels' source is the one measured: the
+# source's SHA-256 prefix is recorded and `traffic` is null when it differs.
+ATTEND_TRAFFIC = {"decode_src_sha256": "e3383182a5f84fa2", "fetch_kib": 17018.2, "write_kib": 2056.0,
+                  "fetch_scale": 1048576.0 / 524300.5, "write_scale": 1.0}
+
+
+def attend_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "kv_cache_cross_amd", "csrc", "decode.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    t = ATTEND_TRAFFIC
+    if sha != t["decode_src_sha256"]:
+        return None
+    return int((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -49,6 +68,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB device to device (a plain copy "
+                         "kernel of known size that scales memory counters)")
     return ap.parse_args()
 
 
@@ -219,6 +241,8 @@ def main():
     del gram_out
     gram_tflops = gram_flops / (gram_ms * 1e-3) / 1e12
 
+    traffic = attend_traffic_bytes() if (c.name == "llama64k" and D > 0) else None
+    algo_bytes_launch = float(np.mean(attend_union[-1]))
     line = {
         "metric": "SR decode us/step + achieved HBM GB/s; KV compress tokens/s at 64k ctx",
         "value": round(dec_us, 2),
@@ -245,7 +269,9 @@ def main():
                            "rounds": int(stats[0][3])},
         "roofline": {"bound": "hbm", "kernel": "sr_attend_kernel", "achieved": round(achieved_att, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes": "union over KV heads of the gathered A_k and A_v rows + B_k slice + queries",
+                     "traffic": traffic, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                     "algorithmic_bytes_per_launch": int(algo_bytes_launch),
+                     "bytes": "union over KV heads of the gathered A_k and A_v rows + B_k slice + queries",
                      "achieved_per_head_sum": round(achieved_att_perhead, 1),
                      "avg_launch_us": round(att_ms_all * 1e3, 2)},
         "roofline_gram": {"bound": "mfma", "kernel": "gram_bf16_kernel", "achieved": round(gram_tflops, 1),
@@ -257,6 +283,14 @@ def main():
         line["cpu_baseline"] = cpu_baseline(c, wl, layers, q_all, kn_all if c.append else None,
                                             vn_all if c.append else None, rows, D)
     print(json.dumps(line), flush=True)
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {nbytes} bytes read, {nbytes} bytes written")
     ctx.close()
 
 

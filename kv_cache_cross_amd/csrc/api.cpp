@@ -552,7 +552,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   const int cps = 64 / a->chunk;   // chunks per attend block of 64 rows
   const int n_splits = (k_eff + cps - 1) / cps;
   if (n_cand > 32768) return fail(XKV_EUNSUPPORTED, "sr: at most 32768 candidate chunks per head");
-  const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 31) / 32);   // 32-row tiles
+  const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 63) / 64);   // 64-row tiles
   if (n_splits + n_exact > 257)
     return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact-row tiles exceed 257 attend blocks per head");
   {
@@ -587,10 +587,8 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   p.r_k = a->r_k; p.r_v = a->r_v; p.n_cand = n_cand; p.n_chunks = a->T / a->chunk; p.k_eff = k_eff;
   p.n_splits = n_splits; p.n_exact = n_exact; p.grp = grp; p.cps = cps; p.mfma = mfma; p.vdim = vdim;
   p.q_pos = a->n_gen > 0 ? (long)a->T + a->n_gen - 1 : a->T;
-  // Scoring blocks per head: about 128 candidates each, at most 64, and few enough that
-  // the whole select grid (with the exact-row tiles) is resident at once (two blocks of
-  // this kernel per CU on 256 CUs).
-  p.score_blocks = std::max(1, std::min({64, (n_cand + 127) / 128, 512 / (a->batch * a->n_kv_heads) - n_exact}));
+  // Scoring blocks per head: about 128 candidates each, at most 64.
+  p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));
   p.scale = a->scale; p.theta = a->rope_theta;
   for (int i = 0; i < a->head_dim / 2; ++i)
     p.turns[i] = std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI);
@@ -647,7 +645,7 @@ extern "C" int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, siz
   if (rc) return rc;
   // The score kernel always runs: it also appends the new token and attends the exact rows.
   XKV_K(xkv::launch_sr_score(P, args->dtype == XKV_BF16, (hipStream_t)stream));
-  XKV_K(xkv::launch_sr_topk(P, (hipStream_t)stream));
+  XKV_K(xkv::launch_sr_topk(P, args->dtype == XKV_BF16, (hipStream_t)stream));
   return XKV_OK;
 }
 
@@ -679,7 +677,7 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
     const int bf16 = args[l].dtype == XKV_BF16;
     xkv::SrParams& p = P[l];
     XKV_K(xkv::launch_sr_score(p, bf16, st));
-    XKV_K(xkv::launch_sr_topk(p, st));
+    XKV_K(xkv::launch_sr_topk(p, bf16, st));
     XKV_K(xkv::launch_sr_attend(p, bf16, st, attend_events ? (hipEvent_t)attend_events[2 * l] : nullptr,
                                 attend_events ? (hipEvent_t)attend_events[2 * l + 1] : nullptr));
     XKV_K(xkv::launch_sr_merge(p, st));

@@ -3,20 +3,21 @@
 // section 3.2).  Four kernels, ordered by the stream (no device-scope fences
 // inside any of them: on this GPU such a fence writes back the XCD's L2):
 //
-// sr_score_kernel (grid: score_blocks + n_exact x KV heads x batch)
+// sr_score_kernel (grid: score_blocks x KV heads x batch)
 //   * block (0, 0, b) appends the new token's pre-RoPE k, v to the exact tail;
-//   * blocks x < score_blocks form the scaled, rotated query sum of the KV
-//     head's query group and score a slice of the candidate chunks against the
-//     landmarks (a GEMV that streams the landmarks once, each thread's loads
-//     issued before its arithmetic);
-//   * blocks x >= score_blocks attend one 32-row tile each of the exact rows
-//     (sink, local window, generated tokens), which do not depend on the
-//     selection, and leave a softmax partial (max, denominator, weighted value
-//     sum) per query head.
-// sr_topk_kernel (grid: KV heads x batch): the head's scores go to registers as
-//   order-preserving keys; a histogram over value buckets and a radix select
-//   inside the k-th key's bucket find the k-th key, and an index-ordered
-//   compaction writes the k chunk ids (ties to the lower id).
+//   * every block forms the scaled, rotated query sum of the KV head's query
+//     group and scores a slice of the candidate chunks against the landmarks
+//     (a GEMV that streams the landmarks once, each thread's loads issued
+//     before its arithmetic).
+// sr_topk_kernel (grid: KV heads x batch x (1 + exact tiles), 1024 threads):
+//   * the first KV heads x batch blocks load one head's scores into registers
+//     as order-preserving keys; a histogram over value buckets and a radix
+//     select inside the k-th key's bucket find the k-th key, and an
+//     index-ordered compaction writes the k chunk ids (ties to the lower id);
+//   * the other blocks attend one 64-row tile each of the exact rows (sink,
+//     local window, generated tokens), which do not depend on the selection,
+//     and leave a softmax partial (max, denominator, weighted value sum) per
+//     query head.
 // sr_attend_mfma_kernel (bf16, head_dim 128, r_k == r_v, r % 128 == 0; grid: KV
 // heads x splits x batch, so one head's blocks share an XCD and its B slices in L2;
 // 512 threads, two waves per SIMD)
@@ -50,7 +51,7 @@ namespace {
 
 constexpr int RB = 64;        // rows per attend block (generic path) and per exact-row tile
 constexpr int RBM = 64;       // rows per matrix-core attend block
-constexpr int ERB = 32;       // rows per exact-row tile
+constexpr int ETR = 64;       // rows per exact-row tile
 constexpr int MAXG = 8;       // largest query group per KV head
 constexpr int MAXD = 128;     // largest head dim
 constexpr int KCH = 512;      // rank columns staged per pass (MFMA path)
@@ -304,6 +305,36 @@ XKV_DEV void load8<float>(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Eight storage elements held raw in registers (the load issued now, the conversion
+// to float done where the values are used).
+template <typename ST>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  uint4 u;
+  XKV_DEV void load(const uint16_t* p) { u = *(const uint4*)p; }
+  XKV_DEV void get(float* v) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  XKV_DEV void load(const float* p) {
+    a = *(const float4*)p;
+    b = *(const float4*)(p + 4);
+  }
+  XKV_DEV void get(float* v) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 // Rotated, scaled queries of KV head h's group into qs[j][0..d).
 template <typename ST>
 XKV_DEV void load_group_queries(const SrParams& P, int b, int h, float (*qs)[MAXD]) {
@@ -336,21 +367,24 @@ XKV_DEV void softmax_partial(int grp, float (*pw)[RB], float* st_m, float* st_l)
   }
 }
 
-// Exact rows of one (sequence, head): sink, local window, generated tokens, ERB per
-// block (tile e_blk), each tile leaving its own softmax partial.  The tile's rows are
-// requested before the queries, so the two latencies overlap.  The newest generated
-// row is read from k_new / v_new when given, since block (0, 0, b) of the same launch
-// is what copies it into the tail.
+// Exact rows of one (sequence, head): sink, local window, generated tokens, ETR per
+// block of TKT threads (tile e_blk), each tile leaving its own softmax partial.  These
+// blocks ride in the top-k launch, whose few selection blocks leave the GPU idle
+// otherwise.  The tile's rows are requested before the queries, so the two latencies
+// overlap.  The newest generated row is read from k_new / v_new when given, since the
+// score kernel copies it into the tail in this same step.
 template <typename ST>
-XKV_DEV void exact_rows(const SrParams& P, int b, int h, int e_blk, float (*qs)[MAXD], float* smem) {
+XKV_DEV void exact_tile(const SrParams& P, int b, int h, int e_blk, float* smem) {
   float (*kh)[HROW] = (float (*)[HROW])smem;
-  float (*vh)[HROW] = (float (*)[HROW])(smem + ERB * HROW);
-  __shared__ float pw[MAXG][ERB];
-  __shared__ float st_m[MAXG], st_l[MAXG];
+  float (*vh)[HROW] = (float (*)[HROW])(smem + ETR * HROW);
+  float (*qs)[MAXD] = (float (*)[MAXD])(smem + 2 * ETR * HROW);
+  float (*pw)[ETR] = (float (*)[ETR])(smem + 2 * ETR * HROW + MAXG * MAXD);
+  float* st_m = smem + 2 * ETR * HROW + MAXG * MAXD + MAXG * ETR;
+  float* st_l = st_m + MAXG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = P.d, half = d >> 1, grp = P.grp;
   const int n_tail = P.n_sink + P.n_local + P.n_gen;
-  const int r0 = e_blk * ERB;   // this block's tile of the tail
+  const int r0 = e_blk * ETR;   // this block's tile of the tail
   auto pos_of = [&](int row) -> int {
     if (row < P.n_sink) return row;
     if (row < P.n_sink + P.n_local) return P.T - P.n_local + (row - P.n_sink);
@@ -361,66 +395,69 @@ XKV_DEV void exact_rows(const SrParams& P, int b, int h, int e_blk, float (*qs)[
   const ST* vt = (const ST*)P.v_tail + b * P.bs_tail + (long)h * d;
   const ST* kn = P.k_new ? (const ST*)P.k_new + b * P.bs_new + (long)h * d : nullptr;
   const ST* vn = P.v_new ? (const ST*)P.v_new + b * P.bs_new + (long)h * d : nullptr;
-  // Thread t loads 8-element groups t and t + 256 of the tile (row = group / (d/8)).
+  // Thread t loads 8-element group t of the tile (row = t / (d/8)).
   const int per_row = d >> 3;
-  float kv[2][8], vv[2][8];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + 256 * u;
-    const int row = r0 + e / per_row, c8 = (e % per_row) * 8;
-    if (e < ERB * per_row && row < n_tail) {
-      const bool newest = kn && row == n_tail - 1;
-      load8<ST>((newest ? kn : kt + (long)row * P.ld_tail) + c8, kv[u]);
-      load8<ST>((newest ? vn : vt + (long)row * P.ld_tail) + c8, vv[u]);
+  const int rl = tid / per_row, c8 = (tid % per_row) * 8;
+  const bool mine = tid < ETR * per_row && r0 + rl < n_tail;
+  float kv[8], vv[8];
+  if (mine) {
+    const int row = r0 + rl;
+    const bool newest = kn && row == n_tail - 1;
+    load8<ST>((newest ? kn : kt + (long)row * P.ld_tail) + c8, kv);
+    load8<ST>((newest ? vn : vt + (long)row * P.ld_tail) + c8, vv);
+  }
+  // Rotated, scaled queries of the group (one pair per thread).
+  {
+    const ST* q = (const ST*)P.q + ((long)b * P.Hq + (long)h * grp) * d;
+    if (tid < grp * half) {
+      const int j = tid / half, i = tid % half;
+      const float x = ld_elem(q + j * d + i), y = ld_elem(q + j * d + i + half);
+      float c, s;
+      rope_cs_turns(P.q_pos, P.turns[i], &c, &s);
+      qs[j][i] = (x * c - y * s) * P.scale;
+      qs[j][i + half] = (y * c + x * s) * P.scale;
     }
   }
-  load_group_queries<ST>(P, b, h, qs);
+  if (tid < ETR * per_row) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + 256 * u;
-    if (e < ERB * per_row) {
-      const int rl = e / per_row, c8 = (e % per_row) * 8;
-      const bool ok = r0 + rl < n_tail;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        kh[rl][c8 + x] = ok ? kv[u][x] : 0.f;
-        vh[rl][c8 + x] = ok ? vv[u][x] : 0.f;
-      }
+    for (int x = 0; x < 8; ++x) {
+      kh[rl][c8 + x] = mine ? kv[x] : 0.f;
+      vh[rl][c8 + x] = mine ? vv[x] : 0.f;
     }
   }
   __syncthreads();
-  for (int e = tid; e < ERB * half; e += 256) {
-    const int rl = e / half, i = e % half;
+  for (int e = tid; e < ETR * half; e += TKT) {
+    const int r = e / half, i = e % half;
     float c, sn;   // rows past the tail rotate by angle 0; their scores are masked
-    rope_cs_turns(max(pos_of(r0 + rl), 0), P.turns[i], &c, &sn);
-    const float lo = kh[rl][i], hi = kh[rl][i + half];
-    kh[rl][i] = lo * c - hi * sn;
-    kh[rl][i + half] = hi * c + lo * sn;
+    rope_cs_turns(max(pos_of(r0 + r), 0), P.turns[i], &c, &sn);
+    const float lo = kh[r][i], hi = kh[r][i + half];
+    kh[r][i] = lo * c - hi * sn;
+    kh[r][i + half] = hi * c + lo * sn;
   }
   __syncthreads();
-  if (tid < grp * ERB) {
-    const int j = tid / ERB, rl = tid % ERB;
+  if (tid < grp * ETR) {
+    const int j = tid / ETR, r = tid % ETR;
     float v = -INFINITY;
-    if (r0 + rl < n_tail) {
+    if (r0 + r < n_tail) {
       float s4[4] = {0.f, 0.f, 0.f, 0.f};
       for (int i = 0; i < d; i += 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s4[u] += qs[j][i + u] * kh[rl][i + u];
+        for (int u = 0; u < 4; ++u) s4[u] += qs[j][i + u] * kh[r][i + u];
       }
       v = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
-    pw[j][rl] = v;
+    pw[j][r] = v;
   }
   __syncthreads();
-  for (int j = wave; j < grp; j += 4) {
-    const float v = lane < ERB ? pw[j][lane] : -INFINITY;
+  if (wave < grp) {
+    const float v = pw[wave][lane];
     const float mx = wave_max(v);
     const float p = (v == -INFINITY) ? 0.f : __expf(v - mx);
     const float l = wave_sum(p);
-    if (lane < ERB) pw[j][lane] = p;
+    pw[wave][lane] = p;
     if (lane == 0) {
-      st_m[j] = mx;
-      st_l[j] = l;
+      st_m[wave] = mx;
+      st_l[wave] = l;
     }
   }
   __syncthreads();
@@ -429,22 +466,17 @@ XKV_DEV void exact_rows(const SrParams& P, int b, int h, int e_blk, float (*qs)[
     part[tid] = st_m[tid];
     part[grp + tid] = st_l[tid];
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid + 256 * q;
-    if (e < grp * d) {
-      const int j = e / d, i = e % d;
-      float acc = 0.f;
+  if (tid < grp * d) {
+    const int j = tid / d, i = tid % d;
+    float acc = 0.f;
 #pragma unroll 8
-      for (int rl = 0; rl < ERB; ++rl) acc += pw[j][rl] * vh[rl][i];
-      part[2 * grp + e] = acc;
-    }
+    for (int r = 0; r < ETR; ++r) acc += pw[j][r] * vh[r][i];
+    part[2 * grp + tid] = acc;
   }
 }
 
 template <typename ST>
 __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
-  extern __shared__ __align__(16) float smem_f[];
   __shared__ float qs[MAXG][MAXD];
   __shared__ float qsum[MAXD];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -461,10 +493,24 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
     }
   }
 
-  if (blk >= P.score_blocks) {
-    exact_rows<ST>(P, b, h, blk - P.score_blocks, qs, smem_f);
-    return;
-  }
+  // Landmarks of the first BATCH passes are requested before the queries are formed, so
+  // their latency overlaps the query rotation.  Past-the-end slots re-read the block's
+  // last chunk (in bounds) and are not stored.
+  const int per_blk = (P.n_cand + P.score_blocks - 1) / P.score_blocks;
+  const int c0 = blk * per_blk, c1 = min(P.n_cand, c0 + per_blk);
+  if (c0 >= c1) return;
+  const int lpc = P.d >> 3;           // lanes per chunk, 8 elements each
+  const int cpi = 256 / lpc;          // chunks per pass
+  const int sub = tid % lpc, slot = tid / lpc;
+  const ST* lm = (const ST*)P.lm + b * P.bs_lm + (long)h * P.n_chunks * P.d + sub * 8;
+  float* scores = P.scores + ((long)b * P.Hkv + h) * P.n_cand;
+  const int iters = (c1 - c0 + cpi - 1) / cpi;
+  constexpr int BATCH = 16;
+  Raw8<ST> raw[BATCH];
+#pragma unroll
+  for (int u = 0; u < BATCH; ++u)
+    if (u < iters) raw[u].load(lm + (long)min(c0 + u * cpi + slot, c1 - 1) * P.d);
+
   load_group_queries<ST>(P, b, h, qs);
   __syncthreads();
   for (int i = tid; i < P.d; i += 256) {
@@ -473,49 +519,46 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
     qsum[i] = s;
   }
   __syncthreads();
-
-  const int per_blk = (P.n_cand + P.score_blocks - 1) / P.score_blocks;
-  const int c0 = blk * per_blk, c1 = min(P.n_cand, c0 + per_blk);
-  const int lpc = P.d >> 3;           // lanes per chunk, 8 elements each
-  const int cpi = 256 / lpc;          // chunks per pass
-  const int sub = tid % lpc, slot = tid / lpc;
   float qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = qsum[sub * 8 + e];
-  const ST* lm = (const ST*)P.lm + b * P.bs_lm + (long)h * P.n_chunks * P.d;
-  float* scores = P.scores + ((long)b * P.Hkv + h) * P.n_cand;
-  const int iters = (c1 - c0 + cpi - 1) / cpi;
-  constexpr int BATCH = 8;
   for (int it0 = 0; it0 < iters; it0 += BATCH) {
-    float v[BATCH][8];
+    if (it0 > 0) {
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int c = c0 + (it0 + u) * cpi + slot;
-      if (it0 + u < iters && c < c1) {
-        load8<ST>(lm + (long)c * P.d + sub * 8, v[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
-      }
+      for (int u = 0; u < BATCH; ++u)
+        if (it0 + u < iters) raw[u].load(lm + (long)min(c0 + (it0 + u) * cpi + slot, c1 - 1) * P.d);
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
+      if (it0 + u >= iters) break;
+      float v[8];
+      raw[u].get(v);
       float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot += qv[e] * v[u][e];
+      for (int e = 0; e < 8; ++e) dot += qv[e] * v[e];
       for (int o = lpc >> 1; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
       const int c = c0 + (it0 + u) * cpi + slot;
-      if (it0 + u < iters && c < c1 && sub == 0) scores[c] = dot;
+      if (c < c1 && sub == 0) scores[c] = dot;
     }
   }
 }
 
-template <int KPT>
+// Blocks [0, H_kv * batch) select the top-k chunks of one (head, sequence); the rest
+// attend one exact-row tile each.
+template <int KPT, typename ST>
 __global__ __launch_bounds__(TKT) void sr_topk_kernel(SrParams P) {
+  extern __shared__ __align__(16) float smem_x[];
   __shared__ int hist[NBK];
   __shared__ int tmp[2 * TKW];
   __shared__ int bcast[4];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int nsel = P.Hkv * P.batch;
+  if ((int)blockIdx.x >= nsel) {
+    const int idx = blockIdx.x - nsel;
+    const int hb = idx / P.n_exact;
+    exact_tile<ST>(P, hb / P.Hkv, hb % P.Hkv, idx % P.n_exact, smem_x);
+    return;
+  }
+  const int h = blockIdx.x % P.Hkv, b = blockIdx.x / P.Hkv;
   const long bh = (long)b * P.Hkv + h;
   uint32_t kr[KPT];
   load_keys<KPT>(P.scores + bh * P.n_cand, P.n_cand, kr);
@@ -1082,29 +1125,35 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }  // namespace
 
 hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st) {
-  dim3 grid(P.score_blocks + P.n_exact, P.Hkv, P.batch);
-  const size_t lds = (size_t)2 * ERB * HROW * 4;   // the exact blocks' staged rows
-  hipError_t e;
-  if (bf16) {
-    if ((e = set_lds<1>(sr_score_kernel<uint16_t>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(sr_score_kernel<uint16_t>, grid, dim3(256), lds, st, P);
-  } else {
-    if ((e = set_lds<2>(sr_score_kernel<float>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(sr_score_kernel<float>, grid, dim3(256), lds, st, P);
-  }
+  dim3 grid(P.score_blocks, P.Hkv, P.batch);
+  if (bf16)
+    hipLaunchKernelGGL(sr_score_kernel<uint16_t>, grid, dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL(sr_score_kernel<float>, grid, dim3(256), 0, st, P);
   return hipGetLastError();
 }
 
-hipError_t launch_sr_topk(const SrParams& P, hipStream_t st) {
-  if (P.top_k <= 0) return hipSuccess;
-  const dim3 grid(P.Hkv, P.batch);
-  if (P.n_cand <= TKT * 2)
-    hipLaunchKernelGGL(sr_topk_kernel<2>, grid, dim3(TKT), 0, st, P);
-  else if (P.n_cand <= TKT * 8)
-    hipLaunchKernelGGL(sr_topk_kernel<8>, grid, dim3(TKT), 0, st, P);
-  else
-    hipLaunchKernelGGL(sr_topk_kernel<32>, grid, dim3(TKT), 0, st, P);
+template <int KPT, typename ST>
+hipError_t launch_topk_exact(const SrParams& P, hipStream_t st) {
+  // the exact tiles' staged rows, queries, weights and softmax stats
+  const size_t lds = sizeof(float) * (2 * ETR * HROW + MAXG * MAXD + MAXG * ETR + 2 * MAXG);
+  hipError_t e = set_lds<10 + KPT + 100 * (int)sizeof(ST)>(sr_topk_kernel<KPT, ST>, lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(P.Hkv * P.batch * (1 + P.n_exact));
+  hipLaunchKernelGGL((sr_topk_kernel<KPT, ST>), grid, dim3(TKT), lds, st, P);
   return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_topk_exact_st(const SrParams& P, hipStream_t st) {
+  if (P.n_cand <= TKT * 2) return launch_topk_exact<2, ST>(P, st);
+  if (P.n_cand <= TKT * 8) return launch_topk_exact<8, ST>(P, st);
+  return launch_topk_exact<32, ST>(P, st);
+}
+
+// Top-k selection and the exact-row tiles, one launch (it runs even when top_k == 0).
+hipError_t launch_sr_topk(const SrParams& P, int bf16, hipStream_t st) {
+  return bf16 ? launch_topk_exact_st<uint16_t>(P, st) : launch_topk_exact_st<float>(P, st);
 }
 
 hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {

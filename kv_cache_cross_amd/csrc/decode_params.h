@@ -12,7 +12,7 @@ struct SrParams {
   int n_chunks;      // T / chunk (landmark rows per head)
   int k_eff;         // min(top_k, n_cand)
   int n_splits;      // 64-row splits of the selected rows
-  int n_exact;       // 32-row tiles of the exact tail (sink + local + generated), at least 1
+  int n_exact;       // 64-row tiles of the exact tail (sink + local + generated), at least 1
   int grp;           // query heads per KV head
   int mfma;          // matrix-core attend path (bf16, head_dim 128, r_k == r_v, r % 128 == 0,
                      // r <= MAX_RANK_MFMA): partials hold sum_t p_t A_v[t] (rank space)
@@ -40,10 +40,10 @@ struct SrParams {
   float* part_ex;    // batch x Hkv x n_exact x grp x (2 + d)
 };
 
-// Stream-ordered stages of one decode step: scores + exact rows (+ append), top-k,
+// Stream-ordered stages of one decode step: scores (+ append), top-k + exact rows,
 // rebuild + attend of the selected rows, merge.
 hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st);
-hipError_t launch_sr_topk(const SrParams& P, hipStream_t st);
+hipError_t launch_sr_topk(const SrParams& P, int bf16, hipStream_t st);
 // ev_start / ev_stop (optional, both or neither): timing events stamped at the attend
 // kernel's start and end.
 hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEvent_t ev_start = nullptr,

@@ -79,14 +79,43 @@ XKV_DEV float wave_max(float v) {
 constexpr int TKT = 1024;      // threads of a top-k block
 constexpr int TKW = TKT / 64;  // its waves
 
+// Wave-wide prefix sum / min / max with DPP moves (no LDS round trips): Hillis-Steele
+// steps of 1, 2, 4 and 8 lanes inside each row of 16, then the row totals carried across
+// rows with the row broadcasts of lanes 15 and 31.  Lanes a shift reaches past the row
+// start take the operation's identity.
+XKV_DEV int wave_scan_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+XKV_DEV uint32_t wave_min_u32(uint32_t v) {
+  const int id = -1;
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+XKV_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Inclusive prefix sum over the TKT threads of a block (`tmp` >= TKW ints).
 XKV_DEV int tk_scan_incl(int v, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
+  v = wave_scan_add(v);
   if (lane == 63) tmp[wave] = v;
   __syncthreads();
   int add = 0;
@@ -98,11 +127,8 @@ XKV_DEV int tk_scan_incl(int v, int* tmp) {
 // Block-wide minimum of lo and maximum of hi (`tmp` >= 2 * TKW ints).
 XKV_DEV void tk_minmax(uint32_t& lo, uint32_t& hi, uint32_t* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
     tmp[wave] = lo;
     tmp[TKW + wave] = hi;
@@ -132,10 +158,10 @@ constexpr int NBK = 2048;   // linear value buckets of the first top-k pass
 // Pass 1 spreads the keys over NBK buckets linear in value between the minimum and
 // the maximum (a monotone map, so every key of a higher bucket is larger than every
 // key of a lower one) and finds the bucket b* that holds the k-th largest key; with
-// scores spread over a range, LDS atomics rarely collide.  Inside b* an MSB-first
-// radix select with 8-bit digits, starting below the bits that b*'s keys share,
-// resolves the k-th key exactly, stopping as soon as the bin holding it is taken
-// whole.  Non-finite extremes put every key in one bucket and leave the radix
+// scores spread over a range, LDS atomics rarely collide.  When b* holds at most 64
+// keys one wave ranks them directly; otherwise an MSB-first radix select with 8-bit
+// digits, starting below the bits that b*'s keys share, resolves the k-th key exactly,
+// stopping as soon as the bin holding it is taken whole.  Non-finite extremes put every key in one bucket and leave the radix
 // select to do all the work.  `hist` holds NBK ints, `tmp` 2 * TKW, `bcast` 3.
 template <int KPT>
 XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* hist, int* tmp, int* bcast) {
@@ -198,6 +224,54 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
   int remaining = k - bcast[1];   // keys still to take from b*, 1..|b*|
   const int m_b = bcast[2];
   __syncthreads();
+
+  // Few keys in b* (the usual case): gather them, let one wave rank them by (key
+  // descending, id ascending) and take the remaining-th as an exact threshold; every
+  // selected key then lies in a higher bucket or at or above the threshold.
+  if (m_b <= 64) {
+    uint32_t thr_key = 0u;
+    int thr_id = 0x7fffffff;
+    if (remaining < m_b) {
+      uint32_t* lkey = (uint32_t*)hist;   // the bucket histogram is no longer needed
+      int* lid = hist + 64;
+      int* lcount = hist + 128;
+      if (tid == 0) *lcount = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (bk[u] == bstar) {
+          const int at = atomicAdd(lcount, 1);
+          lkey[at] = kr[u];
+          lid[at] = base + u;
+        }
+      __syncthreads();
+      if (tid < m_b) {
+        const uint32_t key = lkey[tid];
+        const int id = lid[tid];
+        int rank = 0;
+        for (int j = 0; j < m_b; ++j) rank += lkey[j] > key || (lkey[j] == key && lid[j] < id);
+        if (rank == remaining - 1) {
+          bcast[0] = (int)key;
+          bcast[1] = id;
+        }
+      }
+      __syncthreads();
+      thr_key = (uint32_t)bcast[0];
+      thr_id = bcast[1];
+    }
+    uint32_t selm = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      selm |= (uint32_t)(bk[u] > bstar ||
+                         (bk[u] == bstar && (kr[u] > thr_key || (kr[u] == thr_key && base + u <= thr_id)))) << u;
+    const int mine = __popc(selm);
+    int pos = tk_scan_incl(mine, tmp) - mine;
+    while (selm) {
+      out[pos++] = base + __ffs(selm) - 1;
+      selm &= selm - 1u;
+    }
+    return;
+  }
 
   // Pass 2: radix select of the remaining-th largest key inside b*.
   uint32_t mask = 0u, prefix = 0u;

@@ -65,15 +65,27 @@ XKV_DEV uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-wide float sum / max with DPP moves (the pattern of wave_scan_add below, on
+// float bit patterns), the result read from lane 63 and shared by every lane.
+#define XKV_DPP_F(old, v, ctrl, rm, bc) \
+  __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), ctrl, rm, 0xF, bc))
 XKV_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += XKV_DPP_F(0.f, v, 0x111, 0xF, true);
+  v += XKV_DPP_F(0.f, v, 0x112, 0xF, true);
+  v += XKV_DPP_F(0.f, v, 0x114, 0xF, true);
+  v += XKV_DPP_F(0.f, v, 0x118, 0xF, true);
+  v += XKV_DPP_F(0.f, v, 0x142, 0xA, false);
+  v += XKV_DPP_F(0.f, v, 0x143, 0xC, false);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 XKV_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, XKV_DPP_F(-INFINITY, v, 0x111, 0xF, false));
+  v = fmaxf(v, XKV_DPP_F(-INFINITY, v, 0x112, 0xF, false));
+  v = fmaxf(v, XKV_DPP_F(-INFINITY, v, 0x114, 0xF, false));
+  v = fmaxf(v, XKV_DPP_F(-INFINITY, v, 0x118, 0xF, false));
+  v = fmaxf(v, XKV_DPP_F(-INFINITY, v, 0x142, 0xA, false));
+  v = fmaxf(v, XKV_DPP_F(-INFINITY, v, 0x143, 0xC, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 constexpr int TKT = 1024;      // threads of a top-k block
@@ -1075,6 +1087,12 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   float2 pv[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) pv[u] = *(const float2*)(p0 + (long)max(0, min(u, ns - 1)) * sstride + c0);
+  // The exact-row tiles' weighted value sums of output dim tid (up to 4 tiles in flight).
+  constexpr int PE = 4;
+  float ev[PE];
+#pragma unroll
+  for (int e = 0; e < PE; ++e)
+    ev[e] = (tid < d && e < P.n_exact) ? pex[e * estride + 2 * grp + (long)j * d + tid] : 0.f;
   uint4 bw[32];
   const int cb = min(lane * 8, r - 8);
 #pragma unroll
@@ -1131,10 +1149,13 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
     orank[c] = a0;
     orank[c + 1] = a1;
   }
-  for (int i = tid; i < d; i += 256) {
+  if (tid < d) {
     float acc = 0.f;
-    for (int e = 0; e < P.n_exact; ++e) acc += wq[ns + e] * pex[e * estride + 2 * grp + (long)j * d + i];
-    oval[i] = acc;
+#pragma unroll
+    for (int e = 0; e < PE; ++e)
+      if (e < P.n_exact) acc += wq[ns + e] * ev[e];
+    for (int e = PE; e < P.n_exact; ++e) acc += wq[ns + e] * pex[e * estride + 2 * grp + (long)j * d + tid];
+    oval[tid] = acc;
   }
   __syncthreads();
   // out[i] = orank . Bt_v[h*128 + i] + oval[i]: wave w takes rows [32w, 32w + 32), lane l

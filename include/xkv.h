@@ -209,6 +209,49 @@ int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, voi
                          void* stream, void* const* attend_events);
 
 /* ------------------------------------------------------------------------ */
+/* Dense decode baseline (full attention over the whole cache)               */
+/* ------------------------------------------------------------------------ */
+
+/* Decode attention of one query position over every cached position: the
+ * full-attention reference that Selective Reconstruction is measured against
+ * ([xKV blog] "图 5、图 6、图 7 分别说明了什么？": attention latency of SR
+ * against full attention; decode attention as in [KQ-SVD] section 3.2).
+ * bf16 only, head_dim 128, query heads j of KV head j / (H_q / H_kv).  The
+ * cache holds keys AFTER RoPE (row t rotated at position t, as a standard KV
+ * cache stores them; see xkv_rope_rows); the query is rotated here at q_pos.
+ * out[b][j] = softmax_t(RoPE(q_j, q_pos) . K[t] * scale) V[t] over t < n_ctx.
+ * Splits of 256 rows merged by log-sum-exp; n_ctx <= 512 * 256.
+ * Errors: XKV_EINVAL (sizes, NULL pointers, misaligned rows: K, V 16-byte
+ * aligned with ld_kv and bstride_kv multiples of 8), XKV_EUNSUPPORTED. */
+typedef struct {
+  int batch;
+  int n_q_heads;        /* multiple of n_kv_heads, at most 8 per KV head */
+  int n_kv_heads;
+  int head_dim;         /* 128 */
+  long n_ctx;           /* cached positions 0 .. n_ctx - 1 */
+  long q_pos;           /* the query's position */
+  int dtype;            /* XKV_BF16 */
+  float scale;          /* usually 1/sqrt(head_dim) */
+  double rope_theta;
+  const void* q;        /* batch x n_q_heads x head_dim, pre-RoPE */
+  const void* K;        /* per sequence n_ctx x (n_kv_heads*head_dim) post-RoPE keys */
+  const void* V;        /* per sequence n_ctx x (n_kv_heads*head_dim) values */
+  long ld_kv, bstride_kv;
+  float* out;           /* batch x n_q_heads x head_dim */
+} xkv_dense_args;
+
+/* Workspace bytes for xkv_dense_decode (the split partials). */
+int xkv_dense_ws_size(const xkv_dense_args* args, size_t* bytes);
+int xkv_dense_decode(xkv_ctx ctx, const xkv_dense_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* y[row] = RoPE(x[row], pos0 + row) for `rows` rows of n_heads x head_dim
+ * (rotate-half pairs (i, i + head_dim/2), angle (pos0 + row) * theta^(-2i/d)
+ * reduced in float64): builds the post-RoPE key cache the dense baseline reads.
+ * x and y may be the same rows (in place).  dtype XKV_F32 or XKV_BF16. */
+int xkv_rope_rows(const void* x, long ld_x, void* y, long ld_y, int rows, long pos0, int n_heads, int head_dim,
+                  double rope_theta, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Component entry points used by the parity tests                           */
 /* ------------------------------------------------------------------------ */
 

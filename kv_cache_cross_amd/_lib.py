@@ -58,6 +58,13 @@ class SrArgs(C.Structure):
                 ("out", C.c_void_p), ("sel", C.c_void_p)]
 
 
+class DenseArgs(C.Structure):
+    _fields_ = [("batch", C.c_int), ("n_q_heads", C.c_int), ("n_kv_heads", C.c_int), ("head_dim", C.c_int),
+                ("n_ctx", C.c_long), ("q_pos", C.c_long), ("dtype", C.c_int), ("scale", C.c_float),
+                ("rope_theta", C.c_double), ("q", C.c_void_p), ("K", C.c_void_p), ("V", C.c_void_p),
+                ("ld_kv", C.c_long), ("bstride_kv", C.c_long), ("out", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -85,6 +92,9 @@ def lib():
         L.xkv_gram.argtypes = [C.POINTER(vp), i, l, i, i, i, i, vp, vp]
         L.xkv_topk.argtypes = [vp, i, i, l, i, vp, vp]
         L.xkv_host_eigh.argtypes = [i, vp, i, vp, vp]
+        L.xkv_dense_ws_size.argtypes = [C.POINTER(DenseArgs), C.POINTER(sz)]
+        L.xkv_dense_decode.argtypes = [vp, C.POINTER(DenseArgs), vp, sz, vp]
+        L.xkv_rope_rows.argtypes = [vp, l, vp, l, i, l, i, i, C.c_double, i, vp]
         _lib = L
     return _lib
 
@@ -260,3 +270,33 @@ def host_eigh(H: np.ndarray, nvec: int):
     Z = np.zeros((n, nvec))
     _check(lib().xkv_host_eigh(n, H.ctypes.data, nvec, w.ctypes.data, Z.ctypes.data))
     return w, Z
+
+
+def dense_args(**kw) -> DenseArgs:
+    """Build a DenseArgs from keyword arguments; tensors become device pointers."""
+    a = DenseArgs()
+    for name, _ in DenseArgs._fields_:
+        if name in kw:
+            v = kw[name]
+            setattr(a, name, v.data_ptr() if isinstance(v, torch.Tensor) else v)
+    return a
+
+
+def dense_ws_size(args: DenseArgs) -> int:
+    n = C.c_size_t()
+    _check(lib().xkv_dense_ws_size(C.byref(args), C.byref(n)))
+    return n.value
+
+
+def dense_decode(ctx, args: DenseArgs, ws: torch.Tensor, stream=None):
+    _check(lib().xkv_dense_decode(ctx.handle, C.byref(args), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def rope_rows(x: torch.Tensor, y: torch.Tensor, pos0: int, n_heads: int, head_dim: int,
+              rope_theta: float = 10000.0, stream=None):
+    """y[row] = RoPE(x[row], pos0 + row) (rows x n_heads*head_dim; x and y may alias)."""
+    if y.dtype != x.dtype or y.shape[0] < x.shape[0]:
+        raise ValueError("rope_rows: y needs x's dtype and at least x's rows")
+    _check(lib().xkv_rope_rows(_ptr(x), x.stride(0), _ptr(y), y.stride(0), x.shape[0], pos0, n_heads, head_dim,
+                               rope_theta, _dtype_code(x), _stream(stream)))

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libxkv.so")
 
-HIP_SOURCES = ["gram.hip", "gemm.hip", "subspace.hip", "project.hip", "decode.hip", "api.cpp"]
+HIP_SOURCES = ["gram.hip", "gemm.hip", "subspace.hip", "project.hip", "decode.hip", "dense.hip", "api.cpp"]
 C_SOURCES = ["host_eigh.c"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "decode_params.h"
+#include "dense_params.h"
 #include "xkv_kernels.h"
 
 extern "C" int xkv_eigh_desc_impl(int n, const double* H, int nvec, double* w, double* Z);
@@ -682,5 +683,69 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
                                 attend_events ? (hipEvent_t)attend_events[2 * l + 1] : nullptr));
     XKV_K(xkv::launch_sr_merge(p, st));
   }
+  return XKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Dense decode baseline
+// ---------------------------------------------------------------------------
+namespace {
+
+int plan_dense(const xkv_dense_args* a, xkv::DenseParams* P, size_t* ws_need) {
+  if (!a) return fail(XKV_EINVAL, "dense: args is NULL");
+  if (a->batch <= 0 || a->n_kv_heads <= 0 || a->n_q_heads <= 0 || a->n_q_heads % a->n_kv_heads)
+    return fail(XKV_EINVAL, "dense: batch/heads invalid (n_q_heads must be a multiple of n_kv_heads)");
+  const int grp = a->n_q_heads / a->n_kv_heads;
+  if (grp > 8) return fail(XKV_EUNSUPPORTED, "dense: at most 8 query heads per KV head");
+  if (a->head_dim != 128) return fail(XKV_EUNSUPPORTED, "dense: head_dim must be 128");
+  if (a->dtype != XKV_BF16) return fail(XKV_EUNSUPPORTED, "dense: bf16 only");
+  if (a->n_ctx <= 0) return fail(XKV_EINVAL, "dense: n_ctx must be positive");
+  const long n_splits = (a->n_ctx + 255) / 256;
+  if (n_splits > xkv::DMAXP) return fail(XKV_EUNSUPPORTED, "dense: n_ctx above %d", xkv::DMAXP * 256);
+  if (!a->q || !a->K || !a->V || !a->out) return fail(XKV_EINVAL, "dense: a required pointer is NULL");
+  const long d_kv = (long)a->n_kv_heads * a->head_dim;
+  if (a->ld_kv < d_kv) return fail(XKV_EINVAL, "dense: ld_kv too small");
+  if (!aligned16(a->K) || !aligned16(a->V) || a->ld_kv % 8 || a->bstride_kv % 8)
+    return fail(XKV_EINVAL, "dense: K and V need 16-byte alignment and strides that are multiples of 8");
+  xkv::DenseParams& p = *P;
+  std::memset(&p, 0, sizeof(p));
+  p.batch = a->batch; p.Hq = a->n_q_heads; p.Hkv = a->n_kv_heads; p.grp = grp;
+  p.n_ctx = a->n_ctx; p.q_pos = a->q_pos; p.n_splits = (int)n_splits; p.scale = a->scale;
+  for (int i = 0; i < a->head_dim / 2; ++i)
+    p.turns[i] = std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI);
+  p.q = a->q; p.K = a->K; p.V = a->V; p.ld_kv = a->ld_kv; p.bs_kv = a->bstride_kv; p.out = a->out;
+  *ws_need = align256((size_t)a->batch * a->n_kv_heads * n_splits * grp * (2 + a->head_dim) * sizeof(float));
+  return XKV_OK;
+}
+
+}  // namespace
+
+extern "C" int xkv_dense_ws_size(const xkv_dense_args* args, size_t* bytes) {
+  if (!bytes) return fail(XKV_EINVAL, "xkv_dense_ws_size: bytes is NULL");
+  xkv::DenseParams P;
+  return plan_dense(args, &P, bytes);
+}
+
+extern "C" int xkv_dense_decode(xkv_ctx ctx, const xkv_dense_args* args, void* ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(XKV_EINVAL, "dense: ctx is NULL");
+  xkv::DenseParams P;
+  size_t need = 0;
+  int rc = plan_dense(args, &P, &need);
+  if (rc) return rc;
+  if (!ws || ws_bytes < need) return fail(XKV_EWORKSPACE, "dense: workspace %zu bytes < %zu", ws_bytes, need);
+  P.part = (float*)ws;
+  XKV_K(xkv::launch_dense_decode(P, (hipStream_t)stream));
+  return XKV_OK;
+}
+
+extern "C" int xkv_rope_rows(const void* x, long ld_x, void* y, long ld_y, int rows, long pos0, int n_heads,
+                             int head_dim, double rope_theta, int dtype, void* stream) {
+  if (!x || !y || rows < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 || pos0 < 0)
+    return fail(XKV_EINVAL, "xkv_rope_rows: bad arguments");
+  if (dtype != XKV_F32 && dtype != XKV_BF16) return fail(XKV_EINVAL, "xkv_rope_rows: unknown dtype");
+  if (ld_x < (long)n_heads * head_dim || ld_y < (long)n_heads * head_dim)
+    return fail(XKV_EINVAL, "xkv_rope_rows: leading dimension too small");
+  XKV_K(xkv::launch_rope_rows(x, ld_x, y, ld_y, rows, pos0, n_heads, head_dim, rope_theta, dtype == XKV_BF16,
+                              (hipStream_t)stream));
   return XKV_OK;
 }

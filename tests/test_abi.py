@@ -38,6 +38,33 @@ def test_struct_layouts_match_header_order():
     assert names == [f for f, _ in L.SrArgs._fields_]
 
 
+def test_dense_struct_layout_matches_header_order():
+    src = open(HEADER).read()
+    end = src.index("} xkv_dense_args;")
+    body = src[src.rindex("typedef struct {", 0, end):end]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*?\s*([a-zA-Z_][a-zA-Z0-9_]*)\s*[,;]", body.replace("typedef struct {", ""))
+    assert names == [f for f, _ in L.DenseArgs._fields_]
+
+
+def test_dense_validation():
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, n_ctx=1000, q_pos=999, dtype=xk.XKV_BF16,
+                scale=0.088, rope_theta=1e4, q=16, K=16, V=16, ld_kv=1024, bstride_kv=0, out=16)
+    n = xk.dense_ws_size(xk.dense_args(**base))
+    assert n >= 1 * 8 * 4 * 4 * 130 * 4
+    for bad, code in [(dict(head_dim=64, ld_kv=512), L.XKV_EUNSUPPORTED), (dict(dtype=xk.XKV_F32), L.XKV_EUNSUPPORTED),
+                      (dict(n_ctx=0), L.XKV_EINVAL), (dict(n_ctx=512 * 256 + 1), L.XKV_EUNSUPPORTED),
+                      (dict(n_q_heads=72), L.XKV_EUNSUPPORTED), (dict(K=8), L.XKV_EINVAL),
+                      (dict(ld_kv=1000), L.XKV_EINVAL), (dict(V=0), L.XKV_EINVAL)]:
+        with pytest.raises(xk.XkvError) as e:
+            xk.dense_ws_size(xk.dense_args(**dict(base, **bad)))
+        assert e.value.code == code, bad
+    lib = xk.lib()
+    assert lib.xkv_dense_decode(None, C.byref(xk.dense_args(**base)), None, 0, None) == L.XKV_EINVAL
+    assert lib.xkv_rope_rows(None, 128, None, 128, 4, 0, 1, 128, 1e4, xk.XKV_BF16, None) == L.XKV_EINVAL
+    assert lib.xkv_rope_rows(16, 64, 16, 128, 4, 0, 1, 128, 1e4, xk.XKV_BF16, None) == L.XKV_EINVAL
+
+
 def _desc(**kw):
     base = dict(T=256, G=2, d_kv=64, r=16, dtype=xk.XKV_F32, n_kv_heads=1, head_dim=64)
     base.update(kw)

@@ -226,6 +226,10 @@ def main():
     comp_s = float(np.median(t_comp))
     sr_gbps = decode_bytes_step / (dec_us * 1e-6) / 1e9
 
+    # ---- dense flash-decode baseline: the same queries over the full post-RoPE cache ----
+    dense = dense_baseline(xk, ctx, c, layers, q_all, kn_all if c.append else None,
+                           vn_all if c.append else None, D, args.steps) if D > 0 else None
+
     # ---- Gram kernel vs bf16 MFMA peak (the compression's dominant kernel), one batched launch ----
     n = G * d_kv
     gram_out = torch.empty((S, n, n), dtype=torch.float64, device=dev)
@@ -277,6 +281,8 @@ def main():
         "roofline_gram": {"bound": "mfma", "kernel": "gram_bf16_kernel", "achieved": round(gram_tflops, 1),
                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
                           "launch_ms": round(gram_ms, 3), "sides": S},
+        "dense_baseline": dense,
+        "sr_speedup_vs_dense": round(dense["us_per_step"] / dec_us, 3) if dense else None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -292,6 +298,54 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: {nbytes} bytes read, {nbytes} bytes written")
     ctx.close()
+
+
+def dense_baseline(xk, ctx, c, layers, q_all, kn_all, vn_all, D, reps):
+    """Full attention of the same queries over every cached position (post-RoPE keys, as a
+    standard cache holds them, rotated on the GPU before timing), n_ctx = T + s + 1 at step s.
+    Returns its time per decode step over all layers and its achieved HBM rate."""
+    dev = q_all.device
+    Lyr, T, d_kv, H, d, Hq = c.n_layers, c.T, c.d_kv, c.n_kv_heads, c.head_dim, c.n_q_heads
+    if c.torch_dtype != torch.bfloat16 or d != 128 or Hq // H > 8:
+        return None
+    n_max = T + (D if kn_all is not None else 0)
+    dk = torch.empty((Lyr, n_max, d_kv), dtype=c.torch_dtype, device=dev)
+    dv = torch.empty_like(dk)
+    for l in range(Lyr):
+        xk.rope_rows(layers[("K", l)], dk[l, :T], 0, H, d, c.rope_theta)
+        dv[l, :T] = layers[("V", l)]
+        if kn_all is not None:
+            xk.rope_rows(kn_all[:, l].contiguous(), dk[l, T:], T, H, d, c.rope_theta)
+            dv[l, T:] = vn_all[:, l]
+    out = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
+    n_ctx = [T + s + 1 if kn_all is not None else T for s in range(D)]
+    args = [[xk.dense_args(batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, n_ctx=n_ctx[s], q_pos=n_ctx[s] - 1,
+                           dtype=xk.XKV_BF16, scale=1.0 / math.sqrt(d), rope_theta=c.rope_theta, q=q_all[s, l],
+                           K=dk[l], V=dv[l], ld_kv=d_kv, bstride_kv=n_max * d_kv, out=out[l])
+             for l in range(Lyr)] for s in range(D)]
+    ws = torch.empty(xk.dense_ws_size(args[-1][0]) // 4, dtype=torch.float32, device=dev)
+
+    def run():
+        for s in range(D):
+            for l in range(Lyr):
+                xk.dense_decode(ctx, args[s][l], ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / D * 1e3)
+    us = float(np.median(times))
+    nbytes = float(np.mean([Lyr * (2 * n * d_kv * 2 + Hq * d * 2 + Hq * d * 4) for n in n_ctx]))
+    del dk, dv
+    return {"us_per_step": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_step": int(nbytes),
+            "kernels": "dense_attend_kernel + dense_merge_kernel per layer"}
 
 
 def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):

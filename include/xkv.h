@@ -220,8 +220,11 @@ int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, voi
  * cache holds keys AFTER RoPE (row t rotated at position t, as a standard KV
  * cache stores them; see xkv_rope_rows); the query is rotated here at q_pos.
  * out[b][j] = softmax_t(RoPE(q_j, q_pos) . K[t] * scale) V[t] over t < n_ctx.
- * Splits of 256 rows merged by log-sum-exp; n_ctx <= 512 * 256.
- * Errors: XKV_EINVAL (sizes, NULL pointers, misaligned rows: K, V 16-byte
+ * Splits of 128..2048 rows (chosen from the grid size) merged by log-sum-exp;
+ * n_ctx <= 512 * 2048.  The scores use the bf16 matrix cores with the rotated,
+ * scaled query split into two bf16 parts (about 16 significant bits); weights
+ * and sums stay float32.
+ * Errors: XKV_EINVAL (sizes, NULL pointers, misaligned rows: q, K, V 16-byte
  * aligned with ld_kv and bstride_kv multiples of 8), XKV_EUNSUPPORTED. */
 typedef struct {
   int batch;

@@ -700,17 +700,24 @@ int plan_dense(const xkv_dense_args* a, xkv::DenseParams* P, size_t* ws_need) {
   if (a->head_dim != 128) return fail(XKV_EUNSUPPORTED, "dense: head_dim must be 128");
   if (a->dtype != XKV_BF16) return fail(XKV_EUNSUPPORTED, "dense: bf16 only");
   if (a->n_ctx <= 0) return fail(XKV_EINVAL, "dense: n_ctx must be positive");
-  const long n_splits = (a->n_ctx + 255) / 256;
-  if (n_splits > xkv::DMAXP) return fail(XKV_EUNSUPPORTED, "dense: n_ctx above %d", xkv::DMAXP * 256);
+  // Rows per block: a multiple of 128, the smallest that keeps the grid within about two
+  // resident blocks per compute unit (512), at most 16 tiles of 32 rows per wave.
+  const long units = (long)a->batch * a->n_kv_heads;
+  long rpb = 128;
+  while (rpb < 2048 && units * ((a->n_ctx + rpb - 1) / rpb) > 512) rpb += 128;
+  const long n_splits = (a->n_ctx + rpb - 1) / rpb;
+  if (n_splits > xkv::DMAXP) return fail(XKV_EUNSUPPORTED, "dense: n_ctx above %d", xkv::DMAXP * 2048);
   if (!a->q || !a->K || !a->V || !a->out) return fail(XKV_EINVAL, "dense: a required pointer is NULL");
   const long d_kv = (long)a->n_kv_heads * a->head_dim;
   if (a->ld_kv < d_kv) return fail(XKV_EINVAL, "dense: ld_kv too small");
-  if (!aligned16(a->K) || !aligned16(a->V) || a->ld_kv % 8 || a->bstride_kv % 8)
-    return fail(XKV_EINVAL, "dense: K and V need 16-byte alignment and strides that are multiples of 8");
+  if (a->n_ctx * a->ld_kv >= (1L << 31)) return fail(XKV_EUNSUPPORTED, "dense: n_ctx * ld_kv must stay below 2^31");
+  if (!aligned16(a->q) || !aligned16(a->K) || !aligned16(a->V) || a->ld_kv % 8 || a->bstride_kv % 8)
+    return fail(XKV_EINVAL, "dense: q, K and V need 16-byte alignment and strides that are multiples of 8");
   xkv::DenseParams& p = *P;
   std::memset(&p, 0, sizeof(p));
   p.batch = a->batch; p.Hq = a->n_q_heads; p.Hkv = a->n_kv_heads; p.grp = grp;
-  p.n_ctx = a->n_ctx; p.q_pos = a->q_pos; p.n_splits = (int)n_splits; p.scale = a->scale;
+  p.n_ctx = a->n_ctx; p.q_pos = a->q_pos; p.n_splits = (int)n_splits; p.rows_per_block = (int)rpb;
+  p.scale = a->scale;
   for (int i = 0; i < a->head_dim / 2; ++i)
     p.turns[i] = std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI);
   p.q = a->q; p.K = a->K; p.V = a->V; p.ld_kv = a->ld_kv; p.bs_kv = a->bstride_kv; p.out = a->out;

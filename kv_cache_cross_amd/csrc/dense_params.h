@@ -4,13 +4,14 @@
 
 namespace xkv {
 
-constexpr int DMAXP = 512;    // splits of 256 rows that the dense merge supports
+constexpr int DMAXP = 512;    // splits that the dense merge supports
 
 struct DenseParams {
   int batch, Hq, Hkv, grp;
   long n_ctx;         // cached positions 0 .. n_ctx - 1
   long q_pos;         // the query's position
-  int n_splits;       // ceil(n_ctx / 256)
+  int n_splits;       // ceil(n_ctx / rows_per_block)
+  int rows_per_block; // a multiple of 128 (four waves of 32-row tiles)
   float scale;
   double turns[64];   // theta^(-2i/d) / (2 pi) for i < d/2, formed on the host in float64
   const void* q;      // batch x Hq x 128 pre-RoPE

@@ -53,12 +53,16 @@ def test_dense_validation():
     n = xk.dense_ws_size(xk.dense_args(**base))
     assert n >= 1 * 8 * 4 * 4 * 130 * 4
     for bad, code in [(dict(head_dim=64, ld_kv=512), L.XKV_EUNSUPPORTED), (dict(dtype=xk.XKV_F32), L.XKV_EUNSUPPORTED),
-                      (dict(n_ctx=0), L.XKV_EINVAL), (dict(n_ctx=512 * 256 + 1), L.XKV_EUNSUPPORTED),
+                      (dict(n_ctx=0), L.XKV_EINVAL), (dict(n_ctx=512 * 2048 + 1), L.XKV_EUNSUPPORTED),
                       (dict(n_q_heads=72), L.XKV_EUNSUPPORTED), (dict(K=8), L.XKV_EINVAL),
                       (dict(ld_kv=1000), L.XKV_EINVAL), (dict(V=0), L.XKV_EINVAL)]:
         with pytest.raises(xk.XkvError) as e:
             xk.dense_ws_size(xk.dense_args(**dict(base, **bad)))
         assert e.value.code == code, bad
+    # Split size: the smallest multiple of 128 rows that keeps the grid at or under 512
+    # blocks (64k context, 8 KV heads: 1152 rows, 57 splits).
+    big = xk.dense_ws_size(xk.dense_args(**dict(base, n_ctx=65537)))
+    assert big == 8 * 57 * 4 * 130 * 4
     lib = xk.lib()
     assert lib.xkv_dense_decode(None, C.byref(xk.dense_args(**base)), None, 0, None) == L.XKV_EINVAL
     assert lib.xkv_rope_rows(None, 128, None, 128, 4, 0, 1, 128, 1e4, xk.XKV_BF16, None) == L.XKV_EINVAL

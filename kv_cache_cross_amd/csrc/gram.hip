@@ -4,29 +4,36 @@
 // vectors of X (KV-CoRE, section 2.A); xKV factors the horizontally
 // concatenated group once (xKV blog, section on what xKV does).
 //
-// bf16 path, one workgroup per 128 x 128 tile of the upper triangle (I <= J):
-//   * a 64-token slab of the I and J column blocks is read from HBM with
-//     16-byte loads, transposed 8x8 in registers and stored token-contiguous
-//     in LDS (double buffered), so that every MFMA operand is one 16-byte LDS
-//     read: v_mfma_f32_32x32x16_bf16 wants 8 consecutive tokens of one column
-//     per lane for both operands;
-//   * 4 waves in a 2 x 2 grid, 64 x 64 outputs per wave (2 x 2 MFMA tiles);
-//   * float32 MFMA sums cover 256 tokens, then are added into float64
-//     register totals, so rounding is relative to a 256-token partial rather
-//     than to the full sum (the eigengap at the target rank is ~3e-3 relative,
-//     which a float32 full-length sum does not resolve);
-//   * the tile and its mirror are written in float64 (and float32 for the
-//     float32 subspace iterations).
+// bf16 path, one 512-thread workgroup per 256 x 256 tile of the upper triangle
+// (I <= J; a diagonal tile reads its column block once):
+//   * 32-token slabs of the I and J column blocks go from HBM straight into LDS
+//     with direct-to-LDS loads (no registers), three slabs ahead of the math, in a
+//     ring of four stages.  A stage is a set of 1 KiB blocks of 16 tokens x 32
+//     columns, one load instruction each;
+//   * the MFMA operands are read with the LDS transpose load ds_read_b64_tr_b16: in
+//     each group of 16 lanes, lane i receives column i of four consecutive token rows
+//     of a 4 x 16 block, so two such reads give a lane the 8 consecutive tokens of one
+//     column that v_mfma_f32_32x32x16_bf16 takes for both operands;
+//   * 8 waves in a 2 x 4 grid, 128 x 64 outputs per wave (4 x 2 MFMA tiles), so an
+//     operand read from LDS feeds 2 or 4 MFMAs;
+//   * float32 MFMA sums cover a segment of 8192 tokens; at each segment end they are
+//     added into the float64 output tile in memory (the tile belongs to this
+//     workgroup alone), so a rounding is relative to one segment's partial sum;
+//   * the last segment also writes the mirror tile and the float32 copy used by the
+//     float32 subspace iterations.
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 
 namespace xkv {
 namespace {
 
-constexpr int GT = 128;            // output tile edge
-constexpr int SLAB = 64;           // tokens per LDS stage
-constexpr int LDS_ROW = SLAB + 8;  // padded LDS row (uint16 elements): 144 bytes
-constexpr int OUTER = 4;           // slabs per float32 partial (256 tokens)
+constexpr int GT = 256;                      // output tile edge
+constexpr int TS = 32;                       // tokens per slab
+constexpr int NST = 4;                       // LDS stages
+constexpr int STAGE = 2 * 8 * 2 * 1024;      // bytes per stage: [op][32-col block][16-token half][16][32]
+constexpr int SEG = 8192;                    // tokens per float32 partial
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 struct GramArgs {
   PtrTable layers;
@@ -46,130 +53,191 @@ __device__ __forceinline__ void upper_tile(int idx, int nt, int* I, int* J) {
   *J = i + idx;
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+// Workgroup barrier without a memory fence: a fence would wait for every load into
+// LDS in flight, the loads into later stages included.  The caller waits for what the
+// barrier must cover (its own loads into the stage about to be read, with vmcnt; its
+// LDS stores, with lgkmcnt); the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) void gram_bf16_kernel(GramArgs a) {
-  extern __shared__ __align__(16) uint16_t lds_raw[];
-  // lds[buf][operand][column][token]
-  auto lds = [&](int buf, int op, int c, int t) -> uint16_t* {
-    return lds_raw + (((buf * 2 + op) * GT + c) * LDS_ROW + t);
-  };
+// Two transpose reads (token rows r and r + 4 of a block) make one MFMA operand.
+__device__ __forceinline__ bf16x8_t tr_operand(const unsigned char* p) {
+  union {
+    v4s h[2];
+    bf16x8_t b;
+  } u;
+  u.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  u.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p + 4 * 64));
+  return u.b;
+}
+
+__global__ __launch_bounds__(512) void gram_bf16_kernel(GramArgs a) {
+  // The four stages are separate arrays, each named by a constant at every use, so
+  // that a load into one stage is known not to touch the stage being read.
+  __shared__ __align__(16) unsigned char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   const int side = blockIdx.x / a.tiles_per_side;
   int I, J;
   upper_tile(blockIdx.x % a.tiles_per_side, a.nt, &I, &J);
   const bool diag = (I == J);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;   // wave tile: rows wm*128.., cols wn*64..
 
-  // Loader role: 8 tokens x 8 columns of one operand per thread.
-  const int op = tid >> 7;
-  const int tg = (tid & 127) >> 4;
-  const int cg = tid & 15;
-  const bool loader = !(diag && op == 1);
-  const int col = (op ? J : I) * GT + cg * 8;
-  const uint16_t* src = nullptr;
-  if (loader && col < a.n) {
-    const int l = col / a.d_kv;
-    src = (const uint16_t*)a.layers.p[side * a.G + l] + (col - l * a.d_kv);
+  // Load role: wave w moves blocks 4w .. 4w+3 of a slab: operand w / 4, 32-column
+  // blocks 2w % 8 and (2w + 1) % 8, both token halves.  Lane l fills 16-byte slot l of
+  // the block: token row l / 4 of the half, column group (l % 4) ^ (row % 4), i.e.
+  // columns 8 ((l % 4) ^ ((l / 4) % 4)) .. + 7 (the swizzle keeps the transpose reads
+  // below free of bank conflicts).  Threads whose
+  // column is past n read column 0 of the first layer (never used).  Every wave loads,
+  // so that the number of loads in flight is the same on every path: the second
+  // operand of a diagonal tile repeats the first (a cache hit, never read).
+  const int dop = wave >> 2;
+  const unsigned char* base[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int cb = (2 * wave + u) & 7;
+    const int col = (dop && !diag ? J : I) * GT + 32 * cb + 8 * ((lane & 3) ^ ((lane >> 2) & 3));
+    const unsigned char* p = (const unsigned char*)a.layers.p[side * a.G];
+    if (col < a.n) {
+      const int l = col / a.d_kv;
+      p = (const unsigned char*)a.layers.p[side * a.G + l] + 2 * (col - l * a.d_kv);
+    }
+    base[u] = p;
   }
-  uint4 rows[8];
-
-  auto gload = [&](int t0) {
+  const uint32_t ldb = (uint32_t)a.ld * 2u;   // byte offsets within a layer fit 32 bits (host check)
+  // Every wave issues exactly four load instructions per slab, so the wait for slab s
+  // is a fixed count; past the last slab the last one is read again.
+  auto dma_slab = [&](int sl, unsigned char* stage) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = t0 + tg * 8 + i;
-      rows[i] = (src && t < a.T) ? *(const uint4*)(src + (long)t * a.ld) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-    if (!loader) return;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int w = c >> 1;
-      uint32_t q[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = word_of(rows[2 * j], w), hi = word_of(rows[2 * j + 1], w);
-        q[j] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      *(uint4*)lds(buf, op, cg * 8 + c, tg * 8) = make_uint4(q[0], q[1], q[2], q[3]);
+    for (int i = 0; i < 4; ++i) {
+      const int u = i >> 1, half = i & 1;
+      const int cb = (2 * wave + u) & 7;
+      const int t = min(sl * TS + 16 * half + (lane >> 2), a.T - 1);
+      unsigned char* dst = stage + ((dop * 8 + cb) * 2 + half) * 1024;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base[u] + (uint32_t)t * ldb),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
 
-  f32x16_t acc[2][2];
-  double tot[2][2][16];
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        acc[mi][ni][j] = 0.f;
-        tot[mi][ni][j] = 0.0;
-      }
-
-  const int n_slabs = (a.T + SLAB - 1) / SLAB;
-  const int opB = diag ? 0 : 1;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < n_slabs; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < n_slabs) gload((s + 1) * SLAB);
-#pragma unroll
-    for (int ks = 0; ks < SLAB / 16; ++ks) {
-      const int t_off = ks * 16 + (lane >> 5) * 8;
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = as_bf16x8(*(const uint4*)lds(buf, 0, wm * 64 + mi * 32 + (lane & 31), t_off));
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bfr[ni] = as_bf16x8(*(const uint4*)lds(buf, opB, wn * 64 + ni * 32 + (lane & 31), t_off));
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (s + 1 < n_slabs) lstore(buf ^ 1);
-    if ((s + 1) % OUTER == 0 || s + 1 == n_slabs) {
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            tot[mi][ni][j] += (double)acc[mi][ni][j];
-            acc[mi][ni][j] = 0.f;
-          }
-    }
-    __syncthreads();
-  }
+      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
   const long nn = (long)a.n * a.n;
   double* C = a.C + side * nn;
   float* C32 = a.C32 ? a.C32 + side * nn : nullptr;
+  // Fold the float32 partial into the float64 tile (first segment: store).  Element j
+  // of MFMA tile (mi, ni) of this lane is row m0 + 32 mi + 8 (j / 4) + j % 4, column
+  // c0 + 32 ni.
+  auto flush = [&](bool first, bool last) {
+    // The row stride is made opaque here, so that no output address is computed ahead
+    // of the slab loop and held in registers through it.
+    long nrow = a.n;
+    __asm__ volatile("" : "+s"(nrow));
+    int m0 = I * GT + wm * 128 + (lane >> 5) * 4, c0 = J * GT + wn * 64 + (lane & 31);
+    __asm__ volatile("" : "+v"(m0), "+v"(c0));
+    double* Cb = C + (long)m0 * nrow + c0;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < 2; ++ni) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = I * GT + wm * 64 + mi * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-        const int c = J * GT + wn * 64 + ni * 32 + (lane & 31);
-        if (m < a.n && c < a.n) {
-          const double v = tot[mi][ni][j];
-          C[(long)m * a.n + c] = v;
-          if (!diag) C[(long)c * a.n + m] = v;
-          if (C32) {
-            C32[(long)m * a.n + c] = (float)v;
-            if (!diag) C32[(long)c * a.n + m] = (float)v;
+        for (int j = 0; j < 16; ++j) {
+          // four elements at a time, so that few float64 values are live at once
+          if ((j & 3) == 0) __asm__ volatile("" ::: "memory");
+          const int m = m0 + mi * 32 + (j >> 2) * 8 + (j & 3), c = c0 + ni * 32;
+          if (m < nrow && c < nrow) {
+            double* p = Cb + (long)(mi * 32 + (j >> 2) * 8 + (j & 3)) * nrow + ni * 32;
+            const double v = (first ? 0.0 : *p) + (double)acc[mi][ni][j];
+            *p = v;
+            if (last) {
+              if (!diag) C[(long)c * nrow + m] = v;
+              if (C32) {
+                C32[(long)m * nrow + c] = (float)v;
+                if (!diag) C32[(long)c * nrow + m] = (float)v;
+              }
+            }
           }
+          acc[mi][ni][j] = 0.f;
         }
       }
+  };
+
+  // Operand reads.  Lane l (group q = l / 16, i = l % 16) points at token row
+  // 8 (q / 2) + i / 4 and column 16 (q % 2) + 4 (i % 4) of a block (16-byte column
+  // group 2 (q % 2) + (i % 4) / 2, placed at slot group ^ (row % 4), half i % 2); the
+  // transpose read then hands it column 16 (q % 2) + i = l % 32 of token rows
+  // 8 (q / 2) + 0..3.  In each 16-lane group the four rows' 32 bytes fall in distinct
+  // quarters of 128 bytes.
+  const int q16 = lane >> 4, i16 = lane & 15;
+  const int lane_off = (8 * (q16 >> 1) + (i16 >> 2)) * 64 +
+                       16 * ((2 * (q16 & 1) + ((i16 >> 1) & 1)) ^ ((i16 >> 2) & 3)) + 8 * (i16 & 1);
+  const int opB = diag ? 0 : 1;
+  auto compute = [&](const unsigned char* stage) {
+    const unsigned char* sb = stage + lane_off;
+#pragma unroll
+    for (int ks = 0; ks < TS / 16; ++ks) {
+      bf16x8_t af[4], bfr[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) af[mi] = tr_operand(sb + ((0 * 8 + 4 * wm + mi) * 2 + ks) * 1024);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) bfr[ni] = tr_operand(sb + ((opB * 8 + 2 * wn + ni) * 2 + ks) * 1024);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);   // one k-step's operands live at a time
+    }
+  };
+
+  const int n_slabs = (a.T + TS - 1) / TS;
+  // One slab: wait for its loads, start the load three slabs ahead into the stage
+  // read one slab ago, then the math.  vmcnt(8): of this wave's loads in flight
+  // (slabs s, s+1, s+2, four each), slab s's have landed; the barrier extends that to
+  // every wave and ends the reads of slab s - 1.  Loads are issued for every slab
+  // position up to a multiple of four (past the end: the last slab again), so the
+  // count never depends on a branch; only the math is skipped there.
+  auto body = [&](int s, unsigned char* cur, unsigned char* ahead) {
+    __builtin_amdgcn_s_waitcnt(0x0F78);
+    lds_barrier();
+    dma_slab(min(s + 3, n_slabs - 1), ahead);
+    if (s < n_slabs) {
+      if (s * TS + TS > a.T) {   // last, partial slab: zero the token rows past T
+        const int op = tid >> 8, cb = (tid >> 5) & 7, tok = tid & 31;
+        if (s * TS + tok >= a.T) {
+          uint4* row = (uint4*)(cur + ((op * 8 + cb) * 2 + (tok >> 4)) * 1024 + (tok & 15) * 64);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) row[e] = make_uint4(0, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zero rows are written
+        lds_barrier();
+      }
+      compute(cur);
+      const int t_end = (s + 1) * TS;
+      if (t_end % SEG == 0 || s + 1 == n_slabs) {
+        flush(t_end <= SEG, s + 1 == n_slabs);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    }
+  };
+  dma_slab(0, st0);
+  dma_slab(min(1, n_slabs - 1), st1);
+  dma_slab(min(2, n_slabs - 1), st2);
+  for (int s = 0; s < n_slabs; s += NST) {
+    body(s, st0, st3);
+    body(s + 1, st1, st0);
+    body(s + 2, st2, st1);
+    body(s + 3, st3, st2);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the workgroup
 }
 
 // float32 layers (small workloads): 16 x 16 output tiles, float64 sums.
@@ -213,10 +281,11 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(GramF32Args a) {
 
 }  // namespace
 
-static constexpr size_t kGramLds = 2 * 2 * GT * LDS_ROW * sizeof(uint16_t);
+
 
 hipError_t launch_gram_bf16(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
                             double* C, float* C32, hipStream_t st) {
+  if ((long)T * ld >= (1L << 31)) return hipErrorInvalidValue;   // 32-bit byte offsets per layer
   GramArgs a;
   a.layers = layers;
   a.G = G;
@@ -228,14 +297,7 @@ hipError_t launch_gram_bf16(const PtrTable& layers, int n_sides, int G, long ld,
   a.ld = ld;
   a.C = C;
   a.C32 = C32;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gram_bf16_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGramLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gram_bf16_kernel, dim3(a.tiles_per_side * n_sides), dim3(256), kGramLds, st, a);
+  hipLaunchKernelGGL(gram_bf16_kernel, dim3(a.tiles_per_side * n_sides), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

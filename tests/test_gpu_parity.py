@@ -92,12 +92,17 @@ def _check_side(ctx, layers, r, *, with_lm, n_kv_heads, head_dim, chunk, label):
     log(f"  {label}: ||dP||_F={dP:.2e} orth={orth:.1e} rel_err gpu={rel_gpu:.6f} ref={ref['rel_err']:.6f} "
         f"eig rel={lam_err:.1e} stats={out['stats']}")
     # stats["err_est"] bounds the iteration error against the GPU's own Gram; the Gram's
-    # rounding (a floor of ~3e-5 here) is outside what that estimate can see.
+    # rounding (a floor of ~2e-4 here) is outside what that estimate can see.
     assert out["stats"]["err_est"] <= 1e-4
     assert dP <= PROJ_TOL
     assert orth <= 1e-10
     assert abs(rel_gpu - ref["rel_err"]) <= RECON_TOL
-    assert lam_err <= 1e-6
+    # Eigenvalue bar (not fixed by the pages; derived from the Gram's arithmetic): the
+    # Gram sums up to 8192 tokens in float32, 512 matrix-core accumulations of 16 tokens,
+    # each rounded to 2^-24 of the running partial; a random walk over them gives entry
+    # errors of ~sqrt(512) * 2^-24 ~ 1.3e-6 relative, which Weyl's bound carries to the
+    # eigenvalues.  1e-5 leaves a margin of ~5 over the ~2e-6 observed.
+    assert lam_err <= 1e-5
     if with_lm:
         d_kv = layers[0].shape[1]
         for l, K in enumerate(layers):

@@ -229,6 +229,51 @@ def main():
     # ---- dense flash-decode baseline: the same queries over the full post-RoPE cache ----
     dense = dense_baseline(xk, ctx, c, layers, q_all, kn_all if c.append else None,
                            vn_all if c.append else None, D, args.steps) if D > 0 else None
+    # ---- the SR variants on the same cache: xK-SR (values exact, on the GPU) and full
+    # reconstruction (every candidate chunk selected) ----
+    variants = {}
+    if D > 0:
+        def run_variant(top_k, exact_values, steps):
+            vdec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk,
+                                   top_k=top_k, n_sink=c.n_sink, n_local=c.n_local, r_k=r,
+                                   r_v=0 if exact_values else r, dtype=dt, device=dev, rope_theta=c.rope_theta,
+                                   max_gen=D if c.append else 0)
+            vsel = torch.full((Lyr, H, top_k), -1, dtype=torch.int32, device=dev)
+            vout = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
+            sargs = []
+            for s_ in range(steps):
+                arr = []
+                for l in range(Lyr):
+                    g, li = divmod(l, G)
+                    oK, oV = outs[2 * g], outs[2 * g + 1]
+                    a = vdec.args(n_gen=(s_ + 1) if c.append else 0, q=q_all[s_, l], A_k=oK["A"],
+                                  Bt_k=oK["Bt"][li * d_kv:(li + 1) * d_kv],
+                                  A_v=None if exact_values else oV["A"],
+                                  Bt_v=None if exact_values else oV["Bt"][li * d_kv:(li + 1) * d_kv],
+                                  V_full=layers[("V", l)] if exact_values else None,
+                                  landmarks=oK["landmarks"][li], k_tail=k_tail[l], v_tail=v_tail[l],
+                                  k_new=kn_all[s_, l] if c.append else None, v_new=vn_all[s_, l] if c.append else None)
+                    a.out = vout[l].data_ptr()
+                    a.sel = vsel[l].data_ptr()
+                    arr.append(a)
+                sargs.append(L.sr_args_array(arr))
+            for s_ in range(steps):
+                L.sr_decode_layers(ctx, sargs[s_], vdec.ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            times = []
+            for _ in range(args.steps):
+                e0.record()
+                for s_ in range(steps):
+                    L.sr_decode_layers(ctx, sargs[s_], vdec.ws)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / steps * 1e3)
+            return round(float(np.median(times)), 2)
+        variants["xk_sr_us_per_step"] = run_variant(c.top_k, True, D)
+        full_steps = min(D, 4)
+        variants["full_reconstruction_us_per_step"] = run_variant(n_cand, False, full_steps)
+        variants["full_reconstruction_steps"] = full_steps
 
     # ---- Gram kernel vs bf16 MFMA peak (the compression's dominant kernel), one batched launch ----
     n = G * d_kv
@@ -283,6 +328,7 @@ def main():
                           "launch_ms": round(gram_ms, 3), "sides": S},
         "dense_baseline": dense,
         "sr_speedup_vs_dense": round(dense["us_per_step"] / dec_us, 3) if dense else None,
+        "sr_variants": variants or None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -195,7 +195,15 @@ int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
  * up to rounding. */
 int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
 
-/* xkv_sr_select followed by xkv_sr_attend. */
+/* xkv_sr_select followed by xkv_sr_attend.
+ * Limits (XKV_EUNSUPPORTED beyond them): at most 32768 candidate chunks per KV
+ * head; the selected rows (64 per attend block) plus the exact rows (64 per
+ * tile) at most 1088 blocks per head on the matrix-core path with compressed
+ * values (bf16, head_dim 128, r_k == r_v a multiple of 128 up to 4096; enough
+ * for every chunk of a 64k prefix, i.e. full reconstruction) and 257 otherwise.
+ * With r_v == 0 (xK-SR: keys compressed, values exact in V_full) the keys take
+ * the same matrix-core path when r_k is a multiple of 128 (V_full 4-byte
+ * aligned, even strides) and the exact value rows are summed in value space. */
 int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /* One decode step through `n_layers` layers in order (args[l] describes layer l;

@@ -548,14 +548,17 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   const int n_cand = std::max(0, (a->T - a->n_local + a->chunk - 1) / a->chunk);
   const int k_eff = std::min(a->top_k, n_cand);
   if (a->n_sink + a->n_local + a->n_gen == 0 && k_eff == 0) return fail(XKV_EINVAL, "sr: nothing to attend");
-  const int mfma = a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 128 == 0 && a->r_v == a->r_k &&
-                   a->r_k <= xkv::MAX_RANK_MFMA;
+  const int mfma = a->dtype == XKV_BF16 && a->head_dim == 128 && a->r_k % 128 == 0 &&
+                   (a->r_v == a->r_k || a->r_v == 0) && a->r_k <= xkv::MAX_RANK_MFMA;
+  const int exact_v = mfma && a->r_v == 0;   // xK-SR on the matrix-core key path
   const int cps = 64 / a->chunk;   // chunks per attend block of 64 rows
   const int n_splits = (k_eff + cps - 1) / cps;
   if (n_cand > 32768) return fail(XKV_EUNSUPPORTED, "sr: at most 32768 candidate chunks per head");
   const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 63) / 64);   // 64-row tiles
-  if (n_splits + n_exact > 257)
-    return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact-row tiles exceed 257 attend blocks per head");
+  const int max_blocks = (mfma && !exact_v) ? 1088 : 257;   // rank-space / value-space merge
+  if (n_splits + n_exact > max_blocks)
+    return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact-row tiles exceed %d attend blocks per head",
+                max_blocks);
   {
     // Exact tails and new tokens are read 8 elements at a time.
     const long q = a->dtype == XKV_BF16 ? 8 : 4;
@@ -570,13 +573,17 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   if (a->ld_A_k < a->r_k || a->ld_Bt_k < a->r_k || a->ld_tail < d_kv) return fail(XKV_EINVAL, "sr: leading dimension too small");
   if (a->r_v > 0 && (a->ld_A_v < a->r_v || a->ld_Bt_v < a->r_v)) return fail(XKV_EINVAL, "sr: value leading dimension too small");
   if (a->r_v == 0 && a->ld_V < d_kv) return fail(XKV_EINVAL, "sr: ld_V too small");
-  const int vdim = mfma ? a->r_v : a->head_dim;
+  const int vdim = (mfma && !exact_v) ? a->r_v : a->head_dim;
   if (mfma) {
     // matrix-core path: 16-byte loads of A and Bt rows
     if (!aligned16(a->A_k) || !aligned16(a->Bt_k) || a->ld_A_k % 8 || a->ld_Bt_k % 8 || a->bstride_A_k % 8 ||
-        a->bstride_Bt_k % 8 || !aligned16(a->A_v) || !aligned16(a->Bt_v) || a->ld_A_v % 8 || a->ld_Bt_v % 8 ||
-        a->bstride_A_v % 8 || a->bstride_Bt_v % 8)
+        a->bstride_Bt_k % 8 ||
+        (!exact_v && (!aligned16(a->A_v) || !aligned16(a->Bt_v) || a->ld_A_v % 8 || a->ld_Bt_v % 8 ||
+                      a->bstride_A_v % 8 || a->bstride_Bt_v % 8)))
       return fail(XKV_EINVAL, "sr: bf16 A/Bt need 16-byte alignment and strides that are multiples of 8");
+    // exact values: 4-byte loads of two adjacent dims
+    if (exact_v && ((uintptr_t)a->V_full % 4 || a->ld_V % 2 || a->bstride_V % 2))
+      return fail(XKV_EINVAL, "sr: bf16 V_full needs 4-byte alignment and even strides");
   }
   if (!aligned16(a->landmarks) || a->bstride_lm % (a->dtype == XKV_BF16 ? 8 : 4))
     return fail(XKV_EINVAL, "sr: landmarks need 16-byte alignment");
@@ -586,7 +593,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   p.batch = a->batch; p.Hq = a->n_q_heads; p.Hkv = a->n_kv_heads; p.d = a->head_dim; p.T = a->T;
   p.n_gen = a->n_gen; p.chunk = a->chunk; p.top_k = a->top_k; p.n_sink = a->n_sink; p.n_local = a->n_local;
   p.r_k = a->r_k; p.r_v = a->r_v; p.n_cand = n_cand; p.n_chunks = a->T / a->chunk; p.k_eff = k_eff;
-  p.n_splits = n_splits; p.n_exact = n_exact; p.grp = grp; p.cps = cps; p.mfma = mfma; p.vdim = vdim;
+  p.n_splits = n_splits; p.n_exact = n_exact; p.grp = grp; p.cps = cps; p.mfma = mfma; p.exact_v = exact_v; p.vdim = vdim;
   p.q_pos = a->n_gen > 0 ? (long)a->T + a->n_gen - 1 : a->T;
   // Scoring blocks per head: about 128 candidates each, at most 64.
   p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));

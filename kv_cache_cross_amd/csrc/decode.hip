@@ -18,7 +18,8 @@
 //     local window, generated tokens), which do not depend on the selection,
 //     and leave a softmax partial (max, denominator, weighted value sum) per
 //     query head.
-// sr_attend_mfma_kernel (bf16, head_dim 128, r_k == r_v, r % 128 == 0; grid: KV
+// sr_attend_mfma_kernel (bf16, head_dim 128, r_k % 128 == 0 and r_v == r_k, or r_v == 0
+// with exact values (xK-SR); grid: KV
 // heads x splits x batch, so one head's blocks share an XCD and its B slices in L2;
 // 512 threads, two waves per SIMD)
 //   * a block takes 64 rows: the selected chunks [s*64/chunk, (s+1)*64/chunk) of
@@ -57,7 +58,8 @@ constexpr int MAXD = 128;     // largest head dim
 constexpr int KCH = 512;      // rank columns staged per pass (MFMA path)
 constexpr int AROW = KCH + 8; // padded LDS row of staged A rows (bf16 elements)
 constexpr int HROW = MAXD + 1;
-constexpr int MAXP = 257;     // splits + exact tiles that the merge supports
+constexpr int MAXP = 257;     // splits + exact tiles that the value-space merge supports
+constexpr int MAXP_RANK = 1088;   // ... and the rank-space merge (every chunk selected at 64k)
 
 XKV_DEV uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -681,6 +683,9 @@ XKV_DEV void write_partial(const SrParams& P, int b, int h, int s, float (*pw)[R
   }
 }
 
+// EXACT_V: values are exact rows of V_full (xK-SR); the partial holds the value-space
+// sum sum_t p_t v_t per query head instead of the rank-space sum.
+template <bool EXACT_V>
 __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* Ak = (uint16_t*)smem;              // [RBM][AROW] staged A_k rows
@@ -761,12 +766,20 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
                                          (__attribute__((address_space(3))) void*)(dst + (wave * RPW + i) * AROW), 16, 0, 0);
   };
   // Value rows go to registers: lane l of wave w holds rank columns [8l, 8l+8) of rows
-  // 8w..8w+7 (absent rows read row 0 and are zeroed when used).
+  // 8w..8w+7 (absent rows read row 0 and are zeroed when used).  With exact values the
+  // lane holds value dims 2l, 2l + 1 of the same rows instead.
   uint4 av[RPW];
+  uint32_t vx[RPW];
   auto load_v = [&](int kc, int kw) {
-    const int col = min(lane * 8, kw - 8);
+    if constexpr (EXACT_V) {
+      const uint16_t* Vg = (const uint16_t*)P.V_full + b * P.bs_V + (long)h * 128 + 2 * lane;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) av[i] = *(const uint4*)(Ag_v + (long)max(tr[i], 0) * P.ld_A_v + kc + col);
+      for (int i = 0; i < RPW; ++i) vx[i] = *(const uint32_t*)(Vg + (long)max(tr[i], 0) * P.ld_V);
+    } else {
+      const int col = min(lane * 8, kw - 8);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) av[i] = *(const uint4*)(Ag_v + (long)max(tr[i], 0) * P.ld_A_v + kc + col);
+    }
   };
   zero_absent(Ak);
   load_rows(Ag_k, P.ld_A_k, Ak, 0, min(KCH, r));
@@ -859,66 +872,105 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   }
   __syncthreads();
 
-  // Values stay in rank space: the partial holds sum_t p_t A_v[t] per query head; the
-  // merge multiplies the combined sum by B_v once.  Wave w sums its rows 8w..8w+7 for
-  // rank columns [8l, 8l+8) (lane l, from registers), reading each weight once per wave;
-  // the eight wave sums meet in LDS (over the staged key rows, no longer read) and are
-  // added in wave order.
-  float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + r);
-  float* red = (float*)smem;   // [8 waves][grp][KCH]
-  for (int kc = 0; kc < r; kc += KCH) {
-    const int kw = min(KCH, r - kc);
-    if (kc > 0) {
-      __syncthreads();   // the previous chunk's wave sums have been read
-      load_v(kc, kw);
-    }
-    float o[MAXG][8];
+  if constexpr (EXACT_V) {
+    // Exact values: wave w sums its rows 8w..8w+7 for dims 2l, 2l + 1 (lane l); the eight
+    // wave sums meet in LDS (over the staged key rows, no longer read), added in wave order.
+    float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + 128);
+    float* red = (float*)smem;   // [8 waves][grp][128]
+    float o0[MAXG], o1[MAXG];
 #pragma unroll
-    for (int j = 0; j < MAXG; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    for (int j = 0; j < MAXG; ++j) o0[j] = o1[j] = 0.f;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int row = wave * RPW + i;
-      const uint4 w4 = tr[i] >= 0 ? av[i] : make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-      float a[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[2 * e] = __uint_as_float(w[e] << 16);
-        a[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
-      // All MAXG weight rows are read (rows past grp hold unused values), so that no
-      // LDS read waits behind a branch.
+      const uint32_t w = tr[i] >= 0 ? vx[i] : 0u;
+      const float a0 = __uint_as_float(w << 16), a1 = __uint_as_float(w & 0xffff0000u);
 #pragma unroll
       for (int j = 0; j < MAXG; ++j) {
         const float p = pw[j][row];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] += p * a[e];
+        o0[j] += p * a0;
+        o1[j] += p * a1;
       }
     }
     __syncthreads();
-    if (lane * 8 < kw) {
 #pragma unroll
-      for (int j = 0; j < MAXG; ++j)
-        if (j < grp) {
-          float* dst = red + (wave * grp + j) * KCH + lane * 8;
-          *(float4*)dst = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
-          *(float4*)(dst + 4) = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
-        }
-    }
+    for (int j = 0; j < MAXG; ++j)
+      if (j < grp) *(float2*)&red[(wave * grp + j) * 128 + 2 * lane] = make_float2(o0[j], o1[j]);
     __syncthreads();
-    for (int e = tid; e < grp * kw; e += 512) {
-      const int j = e / kw, cc = e % kw;
+    for (int e = tid; e < grp * 128; e += 512) {
+      const int j = e >> 7, c = e & 127;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < 8; ++w) v += red[(w * grp + j) * KCH + cc];
-      part[2 * grp + (long)j * r + kc + cc] = v;
+      for (int w8 = 0; w8 < 8; ++w8) v += red[(w8 * grp + j) * 128 + c];
+      part[2 * grp + e] = v;
     }
-  }
-  if (tid < grp) {
-    part[tid] = st_m[tid];
-    part[grp + tid] = st_l[tid];
+    if (tid < grp) {
+      part[tid] = st_m[tid];
+      part[grp + tid] = st_l[tid];
+    }
+    return;
+  } else {
+    // Values stay in rank space: the partial holds sum_t p_t A_v[t] per query head; the
+    // merge multiplies the combined sum by B_v once.  Wave w sums its rows 8w..8w+7 for
+    // rank columns [8l, 8l+8) (lane l, from registers), reading each weight once per wave;
+    // the eight wave sums meet in LDS (over the staged key rows, no longer read) and are
+    // added in wave order.
+    float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + r);
+    float* red = (float*)smem;   // [8 waves][grp][KCH]
+    for (int kc = 0; kc < r; kc += KCH) {
+      const int kw = min(KCH, r - kc);
+      if (kc > 0) {
+        __syncthreads();   // the previous chunk's wave sums have been read
+        load_v(kc, kw);
+      }
+      float o[MAXG][8];
+#pragma unroll
+      for (int j = 0; j < MAXG; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int row = wave * RPW + i;
+        const uint4 w4 = tr[i] >= 0 ? av[i] : make_uint4(0, 0, 0, 0);
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[2 * e] = __uint_as_float(w[e] << 16);
+          a[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+        // All MAXG weight rows are read (rows past grp hold unused values), so that no
+        // LDS read waits behind a branch.
+#pragma unroll
+        for (int j = 0; j < MAXG; ++j) {
+          const float p = pw[j][row];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] += p * a[e];
+        }
+      }
+      __syncthreads();
+      if (lane * 8 < kw) {
+#pragma unroll
+        for (int j = 0; j < MAXG; ++j)
+          if (j < grp) {
+            float* dst = red + (wave * grp + j) * KCH + lane * 8;
+            *(float4*)dst = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+            *(float4*)(dst + 4) = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
+          }
+      }
+      __syncthreads();
+      for (int e = tid; e < grp * kw; e += 512) {
+        const int j = e / kw, cc = e % kw;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) v += red[(w * grp + j) * KCH + cc];
+        part[2 * grp + (long)j * r + kc + cc] = v;
+      }
+    }
+    if (tid < grp) {
+      part[tid] = st_m[tid];
+      part[grp + tid] = st_l[tid];
+    }
   }
 }
 
@@ -1056,8 +1108,8 @@ __global__ __launch_bounds__(256) void sr_merge_kernel(SrParams P) {
 // columns and the first 512 rank columns of the wave's 32 rows of B_v are all in flight
 // before anything waits.
 __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
-  __shared__ float wq[MAXP];
-  __shared__ float lq[MAXP];
+  __shared__ float wq[MAXP_RANK];
+  __shared__ float lq[MAXP_RANK];
   __shared__ float run_l;
   __shared__ __align__(16) float orank[MAX_RANK_MFMA];
   __shared__ float oval[MAXD];
@@ -1072,9 +1124,10 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   const float* pex = P.part_ex + bh * P.n_exact * estride;
   const uint16_t* Bt = (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)(h * d + wave * 32) * P.ld_Bt_v;
 
-  float hw[2], hl[2];
+  constexpr int HU = (MAXP_RANK + 255) / 256;
+  float hw[HU], hl[HU];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < HU; ++u) {
     const int q = tid + 256 * u;
     if (q < np) {
       const float* pq = q < ns ? P.part + (bh * ns + q) * sstride : pex + (q - ns) * estride;
@@ -1098,7 +1151,7 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
 #pragma unroll
   for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + cb);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < HU; ++u) {
     const int q = tid + 256 * u;
     if (q < np) {
       wq[q] = hw[u];
@@ -1264,11 +1317,17 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEven
   if (P.mfma) {
     // staged key rows, later reused for the eight waves' value sums
     const size_t lds = std::max((size_t)RBM * AROW * sizeof(uint16_t), (size_t)8 * P.grp * KCH * sizeof(float));
-    hipError_t e = set_lds<4>(sr_attend_mfma_kernel, lds);
-    if (e != hipSuccess) return e;
     // The timing events, when given, are stamped by the dispatch itself at the
     // kernel's start and end.
-    hipExtLaunchKernelGGL(sr_attend_mfma_kernel, grid, dim3(512), (uint32_t)lds, st, ev_start, ev_stop, 0, P);
+    if (P.exact_v) {
+      hipError_t e = set_lds<5>(sr_attend_mfma_kernel<true>, lds);
+      if (e != hipSuccess) return e;
+      hipExtLaunchKernelGGL(sr_attend_mfma_kernel<true>, grid, dim3(512), (uint32_t)lds, st, ev_start, ev_stop, 0, P);
+    } else {
+      hipError_t e = set_lds<4>(sr_attend_mfma_kernel<false>, lds);
+      if (e != hipSuccess) return e;
+      hipExtLaunchKernelGGL(sr_attend_mfma_kernel<false>, grid, dim3(512), (uint32_t)lds, st, ev_start, ev_stop, 0, P);
+    }
   } else {
     hipError_t e;
     if (ev_start && (e = hipEventRecord(ev_start, st)) != hipSuccess) return e;
@@ -1282,7 +1341,7 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEven
 }
 
 hipError_t launch_sr_merge(const SrParams& P, hipStream_t st) {
-  if (P.mfma)
+  if (P.mfma && !P.exact_v)
     hipLaunchKernelGGL(sr_merge_rank_kernel, dim3(P.Hkv, P.grp, P.batch), dim3(256), 0, st, P);
   else
     hipLaunchKernelGGL(sr_merge_kernel, dim3(P.Hkv, P.batch), dim3(256), 0, st, P);

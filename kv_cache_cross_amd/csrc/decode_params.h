@@ -14,10 +14,12 @@ struct SrParams {
   int n_splits;      // 64-row splits of the selected rows
   int n_exact;       // 64-row tiles of the exact tail (sink + local + generated), at least 1
   int grp;           // query heads per KV head
-  int mfma;          // matrix-core attend path (bf16, head_dim 128, r_k == r_v, r % 128 == 0,
-                     // r <= MAX_RANK_MFMA): partials hold sum_t p_t A_v[t] (rank space)
-                     // and the merge applies B_v once
-  int vdim;          // width of a split partial's weighted sum: r_v on that path, else d
+  int mfma;          // matrix-core attend path (bf16, head_dim 128, r_k % 128 == 0,
+                     // r_k <= MAX_RANK_MFMA, r_v == r_k or r_v == 0)
+  int exact_v;       // on that path with r_v == 0: partials hold sum_t p_t v_t (value space);
+                     // otherwise they hold sum_t p_t A_v[t] (rank space) and the merge
+                     // applies B_v once
+  int vdim;          // width of a split partial's weighted sum: r_v in rank space, else d
   int cps;           // chunks per split
   long q_pos;        // query position p
   int score_blocks;  // select-kernel blocks per KV head

@@ -71,7 +71,7 @@ class LayerDecoder:
         self.out = torch.empty((batch, n_q_heads, head_dim), dtype=torch.float32, device=device)
         self.sel = torch.full((batch, n_kv_heads, max(top_k, 1)), -1, dtype=torch.int32, device=device)
         probe = L.sr_args(**self.shape, n_gen=max_gen, q=1, A_k=16, ld_A_k=r_k, Bt_k=16, ld_Bt_k=r_k,
-                          A_v=16 if r_v else 0, ld_A_v=max(r_v, 1), Bt_v=16 if r_v else 0, ld_Bt_v=max(r_v, 1),
+                          A_v=16 if r_v else 0, ld_A_v=r_v, Bt_v=16 if r_v else 0, ld_Bt_v=r_v,
                           V_full=0 if r_v else 16, ld_V=n_kv_heads * head_dim, landmarks=16,
                           k_tail=16, v_tail=16, ld_tail=n_kv_heads * head_dim, out=16, sel=16)
         self.ws = torch.zeros(L.sr_ws_size(probe), dtype=torch.uint8, device=device)

@@ -108,6 +108,14 @@ def test_sr_ws_size_validation():
         with pytest.raises(xk.XkvError) as e:
             xk.sr_ws_size(xk.sr_args(**kw))
         assert e.value.code == code, bad
+    # Attend blocks per head: every chunk of a 64k prefix (1023 blocks of 64 rows plus
+    # exact tiles) fits the matrix-core path's 1088; the value-space path stops at 257.
+    full64k = dict(base, T=65536, n_local=64, top_k=1 << 20)
+    assert xk.sr_ws_size(xk.sr_args(**full64k)) > 0
+    for bad in (dict(full64k, T=65536 + 8 * 1024), dict(full64k, r_v=0, V_full=16, ld_V=256)):
+        with pytest.raises(xk.XkvError) as e:
+            xk.sr_ws_size(xk.sr_args(**bad))
+        assert e.value.code == L.XKV_EUNSUPPORTED, bad
 
 
 def test_topk_and_gram_validation():

@@ -260,10 +260,18 @@ def test_decode_exact_tail_crosses_tiles(ctx):
     _run_decode_case(ctx, wl, steps=4, layer=0, label="exact tail 127..130 rows")
 
 
-def test_decode_mini_bf16_exact_values(ctx):
-    # xK-SR variant with GPU-resident exact values (r_v = 0).
-    wl = make_workload("llama16k", device=DEV, **MINI)
-    _run_decode_case(ctx, wl, steps=2, values="exact", layer=1, label="mini bf16 xK-SR")
+@pytest.mark.parametrize("rank", [128, 96])
+def test_decode_mini_bf16_exact_values(ctx, rank):
+    # xK-SR variant with GPU-resident exact values (r_v = 0): rank 128 takes the
+    # matrix-core key path with value-space partials, rank 96 the generic kernel.
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, rank=rank))
+    _run_decode_case(ctx, wl, steps=2, values="exact", layer=1, label=f"mini bf16 xK-SR r={rank}")
+
+
+def test_decode_xk_sr_gqa7_many_splits(ctx):
+    # xK-SR on the matrix-core path with a 7-query group and 41 attend blocks per head.
+    wl = make_workload("qwen122k", device=DEV, T=4096, n_layers=4, rank=128, latent_rank=192, top_k=320)
+    _run_decode_case(ctx, wl, steps=2, values="exact", label="qwen-shaped xK-SR")
 
 
 def test_decode_gqa7_qwen_shape(ctx):
@@ -276,6 +284,14 @@ def test_decode_topk_exceeds_candidates(ctx):
     # Every candidate selected: each prefix position is attended exactly once.
     wl = make_workload("llama16k", device=DEV, **dict(MINI, T=512))
     _run_decode_case(ctx, wl, steps=2, top_k=10000, label="all chunks")
+
+
+def test_decode_full_reconstruction_many_blocks(ctx):
+    # Every candidate chunk selected at T = 20480 (2552 chunks, 319 attend blocks per head,
+    # beyond the 257 blocks of the value-space merge): full reconstruction through the
+    # matrix-core path.
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, T=20480))
+    _run_decode_case(ctx, wl, steps=1, top_k=1 << 20, label="full reconstruction, 319 blocks")
 
 
 def test_decode_exact_rows_only(ctx):

@@ -37,7 +37,7 @@
 //     vector sum_t p_t A_v[t] per query head.
 // sr_attend_generic_kernel covers every other shape (float32, other head
 // dims, exact values, ranks that differ) with value-space partials.
-// sr_merge_kernel (grid: KV heads x batch) and, for the matrix-core path,
+// sr_merge_kernel (grid: query heads x batch) and, for the matrix-core path,
 //   sr_merge_rank_kernel (grid: KV heads x query heads per group x batch) merge
 //   the split partials and the exact-row partials by their log-sum-exp weights
 //   into the output; the latter applies B_v,l,h to the merged rank-r sum.
@@ -1052,52 +1052,81 @@ __global__ __launch_bounds__(256) void sr_attend_generic_kernel(SrParams P) {
 // weights.  Partial q < n_splits is a split, the rest are exact-row tiles.  The
 // headers are read in one parallel round into LDS; every output element then sums
 // its partials with the loads of a batch issued together.
+// Value-space merge, one block per (query head, sequence): phase 1 forms the weights
+// exp(m_q - M) of the split and exact-tile partials and the denominator; phase 2 sums
+// the weighted partial outputs, groups of partials over lanes of float4 dims.
 __global__ __launch_bounds__(256) void sr_merge_kernel(SrParams P) {
-  __shared__ float wq[MAXP][MAXG];
-  __shared__ float lq[MAXP][MAXG];
-  __shared__ float run_l[MAXG];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int grp = P.grp, d = P.d;
+  __shared__ float wq[MAXP];
+  __shared__ float red_m[4], red_l[4];
+  __shared__ __align__(16) float4 acc_s[16][32];
+  const int qh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = P.grp, d = P.d, h = qh / grp, j = qh % grp;
   const int np = P.n_splits + P.n_exact;
   const long bh = (long)b * P.Hkv + h;
   const long stride = (long)grp * (2 + d);
-  const float* pex = P.part_ex + bh * P.n_exact * stride;
   const float* p0 = P.part + bh * P.n_splits * stride;
-  auto part = [&](int q) -> const float* {
-    return q < P.n_splits ? p0 + q * stride : pex + (q - P.n_splits) * stride;
-  };
-  for (int idx = tid; idx < np * grp; idx += 256) {
-    const int q = idx / grp, j = idx % grp;
-    wq[q][j] = part(q)[j];
-    lq[q][j] = part(q)[grp + j];
-  }
-  __syncthreads();
-  if (tid < grp) {
-    const int j = tid;
-    float M = -INFINITY;
-    for (int q = 0; q < np; ++q) M = fmaxf(M, wq[q][j]);
-    float L = 0.f;
-    for (int q = 0; q < np; ++q) {
-      const float w = (wq[q][j] == -INFINITY) ? 0.f : __expf(wq[q][j] - M);
-      wq[q][j] = w;
-      L += w * lq[q][j];
+  const float* pex = P.part_ex + bh * P.n_exact * stride;
+  auto part = [&](int q) -> const float* { return q < P.n_splits ? p0 + q * stride : pex + (q - P.n_splits) * stride; };
+  float m[2], l[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = min(tid + 256 * u, np - 1);   // past np: the last partial again, not used
+    m[u] = part(q)[j];
+    l[u] = part(q)[grp + j];
+    if (tid + 256 * u >= np) {
+      m[u] = -INFINITY;
+      l[u] = 0.f;
     }
-    run_l[j] = L;
   }
+  float mx = wave_max(fmaxf(m[0], m[1]));
+  if (lane == 0) red_m[wave] = mx;
   __syncthreads();
+  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  float ls = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float w = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - M);
+    if (tid + 256 * u < np) wq[tid + 256 * u] = w;
+    ls += w * l[u];
+  }
+  ls = wave_sum(ls);
+  if (lane == 0) red_l[wave] = ls;
+  __syncthreads();
+  const float L = (red_l[0] + red_l[1]) + (red_l[2] + red_l[3]);
+  const int nc4 = d >> 2, nsg = 256 / nc4;   // float4 columns, partial groups
+  const int c4 = tid % nc4, sg = tid / nc4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   constexpr int NB = 8;
-  for (int e = tid; e < grp * d; e += 256) {
-    const int j = e / d;
-    float acc = 0.f;
-    for (int q0 = 0; q0 < np; q0 += NB) {
-      float v[NB];
+  for (int q0 = sg; q0 < np; q0 += nsg * NB) {
+    float4 v[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) v[u] = (q0 + u < np) ? part(q0 + u)[2 * grp + e] : 0.f;
+    for (int u = 0; u < NB; ++u) v[u] = *(const float4*)(part(min(q0 + nsg * u, np - 1)) + 2 * grp + (long)j * d + 4 * c4);
 #pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (q0 + u < np) acc += wq[q0 + u][j] * v[u];
+    for (int u = 0; u < NB; ++u)
+      if (q0 + nsg * u < np) {
+        const float w = wq[q0 + nsg * u];
+        acc.x += w * v[u].x;
+        acc.y += w * v[u].y;
+        acc.z += w * v[u].z;
+        acc.w += w * v[u].w;
+      }
+  }
+  acc_s[sg][c4] = acc;
+  __syncthreads();
+  if (tid < nc4) {
+    float4 r = acc_s[0][tid];
+    for (int g = 1; g < nsg; ++g) {
+      r.x += acc_s[g][tid].x;
+      r.y += acc_s[g][tid].y;
+      r.z += acc_s[g][tid].z;
+      r.w += acc_s[g][tid].w;
     }
-    P.out[((long)b * P.Hq + (long)h * grp) * d + e] = acc / run_l[j];
+    const float inv = 1.f / L;
+    float* o = P.out + ((long)b * P.Hq + qh) * d + 4 * tid;
+    o[0] = r.x * inv;
+    o[1] = r.y * inv;
+    o[2] = r.z * inv;
+    o[3] = r.w * inv;
   }
 }
 
@@ -1344,7 +1373,7 @@ hipError_t launch_sr_merge(const SrParams& P, hipStream_t st) {
   if (P.mfma && !P.exact_v)
     hipLaunchKernelGGL(sr_merge_rank_kernel, dim3(P.Hkv, P.grp, P.batch), dim3(256), 0, st, P);
   else
-    hipLaunchKernelGGL(sr_merge_kernel, dim3(P.Hkv, P.batch), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(sr_merge_kernel, dim3(P.Hq, P.batch), dim3(256), 0, st, P);
   return hipGetLastError();
 }
 

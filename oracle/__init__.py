@@ -26,4 +26,8 @@ from .xkv_ref import (  # noqa: F401
     attended_positions,
     sr_decode_layer,
     dense_decode,
+    numerical_rank,
+    effective_rank,
+    ner,
+    energy_rank,
 )

@@ -258,3 +258,58 @@ def dense_decode(q, K_full, V_full, p: int, n_kv_heads: int, scale: float | None
         w = _softmax_rows(scale * q_rot[h * grp:(h + 1) * grp] @ keys.T)
         out[h * grp:(h + 1) * grp] = w @ V_full[:, cols]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Rank diagnostics (the eigenvalues of C = X^T X are the squared singular
+# values of X, [KV-CoRE] 2.A)
+# ---------------------------------------------------------------------------
+def numerical_rank(eigvals, rel_tol: float | None = None) -> int:
+    """Count of singular values sigma_i = sqrt(lambda_i) above rel_tol * sigma_1.
+
+    The pages call r "the actual rank"; the reading here is the numerical rank
+    with the usual tolerance n * eps (relative to the largest singular value).
+    """
+    lam = np.clip(np.asarray(eigvals, dtype=np.float64), 0.0, None)
+    sv = np.sqrt(np.sort(lam)[::-1])
+    if sv.size == 0 or sv[0] == 0.0:
+        return 0
+    tol = (sv.size * np.finfo(np.float64).eps) if rel_tol is None else rel_tol
+    return int(np.count_nonzero(sv > tol * sv[0]))
+
+
+def effective_rank(eigvals, rel_tol: float | None = None) -> float:
+    """Effective rank: the exponential of the Shannon entropy (natural log) of the
+    singular values normalised to sum to one, over the numerical rank
+    ([KV-CoRE] 2.B: a rank measured by the entropy of the singular value
+    distribution).  Reading: the distribution is sigma_i / sum_j sigma_j (singular
+    values, not their squares)."""
+    lam = np.clip(np.asarray(eigvals, dtype=np.float64), 0.0, None)
+    sv = np.sqrt(np.sort(lam)[::-1])
+    k = numerical_rank(lam, rel_tol)
+    if k == 0:
+        return 0.0
+    p = sv[:k] / sv[:k].sum()
+    return float(np.exp(-np.sum(p * np.log(p))))
+
+
+def ner(eigvals, rel_tol: float | None = None) -> float:
+    """Normalised effective rank erank / r, r the numerical rank ([KV-CoRE] 2.B);
+    it lies in [1/r, 1]."""
+    k = numerical_rank(eigvals, rel_tol)
+    return effective_rank(eigvals, rel_tol) / k if k else 0.0
+
+
+def energy_rank(eigvals, frac: float = 0.95, total: float | None = None) -> int:
+    """Smallest k whose k largest eigenvalues hold at least `frac` of the total
+    ([xKV blog] figure 2(c): the rank that keeps 95 % of the cumulative
+    eigenvalues).  `total` defaults to the sum of the given eigenvalues (a full
+    spectrum); with a partial spectrum pass trace(C).  Returns -1 when the given
+    eigenvalues do not reach the target."""
+    lam = np.sort(np.clip(np.asarray(eigvals, dtype=np.float64), 0.0, None))[::-1]
+    tot = lam.sum() if total is None else float(total)
+    if tot <= 0.0:
+        return 0
+    csum = np.cumsum(lam)
+    hit = np.nonzero(csum >= frac * tot)[0]
+    return int(hit[0]) + 1 if hit.size else -1

@@ -1,0 +1,76 @@
+"""Pins of the oracle's rank diagnostics: effective rank and NER ([KV-CoRE] 2.B) and
+the cumulative-eigenvalue (energy) rank ([xKV blog] figure 2(c)).
+
+Each pin would fail for a plausible slip: using the eigenvalues instead of the
+singular values in the entropy, dropping the normalisation, a base-2 logarithm,
+counting zero singular values in r, an off-by-one in the energy rank or a strict
+instead of a non-strict threshold.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_workload
+
+
+def test_flat_spectrum():
+    # k equal singular values: entropy log k, erank k, NER 1 (for any scale).
+    for k in (1, 3, 64):
+        lam = np.zeros(100)
+        lam[:k] = 7.5
+        assert oracle.numerical_rank(lam) == k
+        assert oracle.effective_rank(lam) == pytest.approx(k, rel=1e-12)
+        assert oracle.ner(lam) == pytest.approx(1.0, rel=1e-12)
+
+
+def test_two_level_spectrum_uses_singular_values():
+    # lambda = (4, 1): sigma = (2, 1), p = (2/3, 1/3), exp(H) = 3 / 2^(2/3) = 1.88988...
+    # (with the eigenvalues themselves, p = (0.8, 0.2) and exp(H) = 1.649 instead).
+    e = oracle.effective_rank([4.0, 1.0])
+    assert e == pytest.approx(3.0 / 2.0 ** (2.0 / 3.0), rel=1e-12)
+    assert oracle.ner([4.0, 1.0]) == pytest.approx(e / 2.0, rel=1e-12)
+
+
+def test_dominant_direction_and_bounds():
+    assert oracle.effective_rank([3.0, 0.0, 0.0]) == pytest.approx(1.0)
+    assert oracle.numerical_rank([1.0, 1e-40, 0.0]) == 1        # below n * eps of sigma_1
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        lam = rng.exponential(size=50) ** 3
+        r = oracle.numerical_rank(lam)
+        n = oracle.ner(lam)
+        assert 1.0 / r - 1e-12 <= n <= 1.0 + 1e-12
+        assert oracle.effective_rank(lam * 123.0) == pytest.approx(oracle.effective_rank(lam), rel=1e-12)
+
+
+def test_effective_rank_matches_svd_of_the_matrix():
+    # Independent route: singular values of X from LAPACK's SVD, entropy written out.
+    rng = np.random.default_rng(0)
+    X = rng.standard_normal((300, 40)) @ np.diag(np.linspace(3.0, 0.1, 40))
+    sv = np.linalg.svd(X, compute_uv=False)
+    p = sv / sv.sum()
+    want = math.exp(-sum(pi * math.log(pi) for pi in p))
+    assert oracle.effective_rank(np.linalg.eigvalsh(X.T @ X)) == pytest.approx(want, rel=1e-9)
+
+
+def test_energy_rank_thresholds():
+    assert oracle.energy_rank(np.ones(100)) == 95
+    assert oracle.energy_rank([0.5, 0.45, 0.05], 0.95) == 2      # reaching the target counts
+    assert oracle.energy_rank([0.5, 0.45, 0.05], 0.951) == 3
+    assert oracle.energy_rank([0.05, 0.5, 0.45], 0.5) == 1       # order of the input is irrelevant
+    # Partial spectrum against a given total (trace of the Gram).
+    assert oracle.energy_rank([5.0, 3.0], 0.8, total=10.0) == 2
+    assert oracle.energy_rank([5.0, 3.0], 0.9, total=10.0) == -1
+
+
+def test_grouping_lowers_the_energy_rank_fraction():
+    # The figure-2(c) effect on the shared-latent generator: the concatenation of a group's
+    # layers needs a smaller fraction of its dimension for 95 % of the energy than a layer.
+    wl = make_workload("llama16k", T=2048, n_layers=4, n_kv_heads=2, n_q_heads=8, rank=64, latent_rank=96)
+    layers = [x.double().numpy() for x in wl.group_kv(0, "K", 0)]
+    per_layer = np.mean([oracle.energy_rank(np.linalg.eigvalsh(x.T @ x)) / x.shape[1] for x in layers])
+    X = oracle.group_matrix(layers)
+    grouped = oracle.energy_rank(np.linalg.eigvalsh(oracle.gram(X))) / X.shape[1]
+    assert grouped < per_layer

@@ -158,8 +158,11 @@ def main():
             e.record()          # creates the underlying HIP events
     torch.cuda.synchronize()
 
+    last_evals = []
+
     def compress():
-        _, stats = L.compress_sides(ctx, desc, sides, cws)
+        evals, stats = L.compress_sides(ctx, desc, sides, cws)
+        last_evals[:] = evals
         return stats
 
     def decode(timed):
@@ -275,6 +278,30 @@ def main():
         variants["full_reconstruction_us_per_step"] = run_variant(n_cand, False, full_steps)
         variants["full_reconstruction_steps"] = full_steps
 
+    # ---- rank diagnostics (outside the timed region): the cumulative-eigenvalue rank of
+    # every group side from its leading Ritz values and trace, and the full spectrum of
+    # layer 0 (K and V, a compression at r = d_kv) for NER and the same rank per layer ----
+    rank_diag = None
+    if c.dtype == "bf16":
+        def frac_rank(ev, total):
+            rs = xk.rank_stats(ev, total=total, frac=0.95)
+            return rs["energy_rank"] / float(G * d_kv) if rs["energy_rank"] > 0 else None
+        grp = {s_: [frac_rank(last_evals[2 * g + i], stats[2 * g + i][4]) for g in range(n_groups)]
+               for i, s_ in enumerate("KV")}
+        single = xk.compress(ctx, [[layers[("K", 0)]], [layers[("V", 0)]]], r=d_kv, n_kv_heads=H, head_dim=d,
+                             landmarks=[False, False])
+        torch.cuda.synchronize()
+        layer0 = {}
+        for s_, o in zip("KV", single):
+            rs = xk.rank_stats(o["eigvals"], total=o["stats"]["energy"], frac=0.95, complete=True)
+            layer0[s_] = {"ner": round(rs["ner"], 5), "erank": round(rs["erank"], 2),
+                          "rank95_frac": round(rs["energy_rank"] / float(d_kv), 4)}
+        del single
+        rank_diag = {"group_rank95_frac": {k: [None if v is None else round(v, 4) for v in vs] for k, vs in grp.items()},
+                     "layer0": layer0,
+                     "note": "rank95_frac = rank holding 95 % of the eigenvalue sum / dimension; group sides "
+                             f"from the {r} leading Ritz values and trace(C) (None: beyond {r})"}
+
     # ---- Gram kernel vs bf16 MFMA peak (the compression's dominant kernel), one batched launch ----
     n = G * d_kv
     gram_out = torch.empty((S, n, n), dtype=torch.float64, device=dev)
@@ -329,6 +356,7 @@ def main():
         "dense_baseline": dense,
         "sr_speedup_vs_dense": round(dense["us_per_step"] / dec_us, 3) if dense else None,
         "sr_variants": variants or None,
+        "rank_diagnostics": rank_diag,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

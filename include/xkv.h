@@ -107,8 +107,9 @@ typedef struct {
                              /* or NULL (no landmarks: the value side)                           */
   double* eigvals;           /* (host) r leading Ritz values of C, descending; nullable          */
   double* Vr64;              /* nullable: n x r float64 copy of V_r before rounding to dtype     */
-  double* stats;             /* (host) nullable, 4 entries: estimated ||P - P_exact||_F, relative */
-                             /* Ritz gap (theta_r - theta_r+1)/theta_r, sweeps, rounds            */
+  double* stats;             /* (host) nullable, 5 entries: estimated ||P - P_exact||_F, relative */
+                             /* Ritz gap (theta_r - theta_r+1)/theta_r, sweeps, rounds, and the   */
+                             /* total energy trace(C) = ||X||_F^2 (the sum of all eigenvalues)    */
 } xkv_side;
 
 /* Workspace bytes needed by xkv_compress_sides for `n_sides` sides. */
@@ -261,6 +262,35 @@ int xkv_dense_decode(xkv_ctx ctx, const xkv_dense_args* args, void* ws, size_t w
  * x and y may be the same rows (in place).  dtype XKV_F32 or XKV_BF16. */
 int xkv_rope_rows(const void* x, long ld_x, void* y, long ld_y, int rows, long pos0, int n_heads, int head_dim,
                   double rope_theta, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Rank diagnostics                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Diagnostics of a spectrum: `eigvals` (host, n_vals values, any order) are
+ * eigenvalues of a side's Gram C = X^T X, i.e. squared singular values of X,
+ * e.g. the Ritz values xkv_compress_sides returns (negative values count as 0).
+ *   energy_rank: the smallest k whose k largest eigenvalues reach frac * total
+ *     ([xKV blog] "xKV 到底做了什么？" figure 2(c): the rank that keeps 95 % of the
+ *     cumulative eigenvalues); total = the trace of C (stats[4] of
+ *     xkv_compress_sides), or <= 0 to use the sum of the given values; -1 when the
+ *     given values do not reach the target;
+ *   covered: their sum / total;
+ *   for a complete spectrum (complete != 0; e.g. a compression at r = n, whose
+ *   Ritz values are exact) numerical_rank r = #{sigma_i > n_vals * eps * sigma_1},
+ *   erank = exp(-sum p_i ln p_i) with p_i = sigma_i / sum_{j<r} sigma_j, and
+ *   ner = erank / r ([KV-CoRE] section 2.B); otherwise -1, NaN, NaN.
+ * Host only; no device work.  Errors: XKV_EINVAL (NULL pointers, n_vals < 0,
+ * frac outside (0, 1]). */
+typedef struct {
+  int energy_rank;
+  double covered;
+  int numerical_rank;
+  double erank;
+  double ner;
+} xkv_rank_info;
+
+int xkv_rank_stats(const double* eigvals, int n_vals, double total, double frac, int complete, xkv_rank_info* out);
 
 /* ------------------------------------------------------------------------ */
 /* Component entry points used by the parity tests                           */

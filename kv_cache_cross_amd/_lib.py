@@ -58,6 +58,11 @@ class SrArgs(C.Structure):
                 ("out", C.c_void_p), ("sel", C.c_void_p)]
 
 
+class RankInfo(C.Structure):
+    _fields_ = [("energy_rank", C.c_int), ("covered", C.c_double), ("numerical_rank", C.c_int),
+                ("erank", C.c_double), ("ner", C.c_double)]
+
+
 class DenseArgs(C.Structure):
     _fields_ = [("batch", C.c_int), ("n_q_heads", C.c_int), ("n_kv_heads", C.c_int), ("head_dim", C.c_int),
                 ("n_ctx", C.c_long), ("q_pos", C.c_long), ("dtype", C.c_int), ("scale", C.c_float),
@@ -94,6 +99,7 @@ def lib():
         L.xkv_host_eigh.argtypes = [i, vp, i, vp, vp]
         L.xkv_dense_ws_size.argtypes = [C.POINTER(DenseArgs), C.POINTER(sz)]
         L.xkv_dense_decode.argtypes = [vp, C.POINTER(DenseArgs), vp, sz, vp]
+        L.xkv_rank_stats.argtypes = [C.POINTER(C.c_double), i, C.c_double, C.c_double, i, C.POINTER(RankInfo)]
         L.xkv_rope_rows.argtypes = [vp, l, vp, l, i, l, i, i, C.c_double, i, vp]
         _lib = L
     return _lib
@@ -163,12 +169,13 @@ def compress_ws_size(desc: CompressDesc, n_sides: int) -> int:
 def compress_sides(ctx: Context, desc: CompressDesc, sides, ws: torch.Tensor, stream=None):
     """sides: list of dicts with 'layers' (list of G tensors, T x d_kv), 'A' (T x r), 'Bt' (n x r),
     optional 'landmarks' (G x H_kv x T/chunk x d) and 'Vr64' (n x r float64).  Returns the r leading
-    Ritz values per side and per-side stats (error estimate, relative gap, sweeps, rounds)."""
+    Ritz values per side and per-side stats (error estimate, relative gap, sweeps, rounds,
+    trace of the Gram)."""
     S = len(sides)
     arr = (Side * S)()
     keep = []
     evals = [np.zeros(desc.r, dtype=np.float64) for _ in range(S)]
-    stats = [np.zeros(4, dtype=np.float64) for _ in range(S)]
+    stats = [np.zeros(5, dtype=np.float64) for _ in range(S)]
     for s, sd in enumerate(sides):
         layers = sd["layers"]
         ptrs = (C.c_void_p * len(layers))(*[t.data_ptr() for t in layers])
@@ -270,6 +277,17 @@ def host_eigh(H: np.ndarray, nvec: int):
     Z = np.zeros((n, nvec))
     _check(lib().xkv_host_eigh(n, H.ctypes.data, nvec, w.ctypes.data, Z.ctypes.data))
     return w, Z
+
+
+def rank_stats(eigvals, total: float = 0.0, frac: float = 0.95, complete: bool = False) -> dict:
+    """Rank diagnostics of a spectrum (host only): energy rank at `frac` of `total`
+    (<= 0: the sum of the given values), covered fraction and, for a complete spectrum,
+    numerical rank, effective rank and NER."""
+    v = np.ascontiguousarray(np.asarray(eigvals, dtype=np.float64))
+    out = RankInfo()
+    _check(lib().xkv_rank_stats(v.ctypes.data_as(C.POINTER(C.c_double)), v.size, float(total), float(frac),
+                                int(bool(complete)), C.byref(out)))
+    return {name: getattr(out, name) for name, _ in RankInfo._fields_}
 
 
 def dense_args(**kw) -> DenseArgs:

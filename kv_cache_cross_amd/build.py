@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libxkv.so")
 
 HIP_SOURCES = ["gram.hip", "gemm.hip", "subspace.hip", "project.hip", "decode.hip", "dense.hip", "api.cpp"]
-C_SOURCES = ["host_eigh.c"]
+C_SOURCES = ["host_eigh.c", "host_rank.c"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -19,6 +19,8 @@
 #include "xkv_kernels.h"
 
 extern "C" int xkv_eigh_desc_impl(int n, const double* H, int nvec, double* w, double* Z);
+extern "C" int xkv_rank_stats_impl(const double* vals, int n, double total, double frac, int complete,
+                                   int* energy_rank, double* covered, int* num_rank, double* erank, double* ner);
 
 namespace {
 
@@ -103,6 +105,15 @@ void xkv_ctx_destroy(xkv_ctx ctx) {
   delete ctx;
 }
 
+int xkv_rank_stats(const double* eigvals, int n_vals, double total, double frac, int complete, xkv_rank_info* out) {
+  if (!out || n_vals < 0 || (n_vals > 0 && !eigvals) || !(frac > 0.0 && frac <= 1.0))
+    return fail(XKV_EINVAL, "xkv_rank_stats: bad arguments (n_vals=%d, frac=%g)", n_vals, frac);
+  if (xkv_rank_stats_impl(eigvals, n_vals, total, frac, complete, &out->energy_rank, &out->covered,
+                          &out->numerical_rank, &out->erank, &out->ner))
+    return fail(XKV_EINVAL, "xkv_rank_stats: out of host memory");
+  return XKV_OK;
+}
+
 int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z) {
   if (n <= 0 || !H || !w || !Z || nvec <= 0 || nvec > n)
     return fail(XKV_EINVAL, "xkv_host_eigh: bad arguments (n=%d, nvec=%d)", n, nvec);
@@ -163,6 +174,7 @@ struct CompressWs {
   double* wdiag;
   double* YZ; double* theta; double* res2;
   void* VrT;
+  double* trace;
   int* info;
   size_t bytes;
 };
@@ -188,6 +200,7 @@ CompressWs carve_compress(void* ws, const CompressPlan& p, int S) {
   w.theta = c.take<double>((size_t)S * p.r);
   w.res2 = c.take<double>((size_t)S * p.r);
   w.VrT = c.take<float>((size_t)S * p.n * p.r);
+  w.trace = c.take<double>(S);
   w.info = c.take<int>(S);
   w.bytes = c.off;
   return w;
@@ -306,6 +319,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     if (p.bf16) XKV_K(launch_gram_bf16(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
     else XKV_K(launch_gram_f32(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
   }
+  XKV_K(launch_trace(w.C64, nn, n, S, w.trace, st));   // total energy of every side
   // 2. Block subspace iteration: float32 sweeps on a float32 copy of C, then float64
   //    sweeps (CholeskyQR, CholeskyQR2 on the last sweep of a round).
   XKV_K(launch_init_q(w.Q32, n, kb, nk, S, desc->seed, st));
@@ -340,7 +354,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   int total_iters = p.fp32_iters + p.fp64_iters;
 
   // Pinned staging: H (down), Z and Ritz values (up), residual norms and info (down).
-  const size_t need_pin = (size_t)S * kk + (size_t)S * kb * r + (size_t)S * r + (size_t)S * r + (size_t)S;
+  const size_t need_pin = (size_t)S * kk + (size_t)S * kb * r + (size_t)S * r + (size_t)S * r + (size_t)S + (size_t)S;
   if (ctx->upload_pending) {
     XKV_HIP(hipEventSynchronize(ctx->upload_done));
     ctx->upload_pending = false;
@@ -356,7 +370,8 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   double* hZ = hH + (size_t)S * kk;
   double* hTheta = hZ + (size_t)S * kb * r;
   double* hRes = hTheta + (size_t)S * r;
-  int* hinfo = (int*)(hRes + (size_t)S * r);
+  double* hTrace = hRes + (size_t)S * r;
+  int* hinfo = (int*)(hTrace + S);
 
   // 3. Rayleigh-Ritz rounds.  After each, the Ritz residual R = (C Q) Z - V_r diag(theta)
   //    bounds the subspace error: ||sin angle(V_r, exact)||_F <= ||R||_F / (theta_r - lambda_{r+1}),
@@ -374,6 +389,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     XKV_K(gemm(gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, Qa, kb, nk, Ya, kb, nk, w.H, kb, kk, 1.0, 0.0, S), st));
     XKV_HIP(hipMemcpyAsync(hH, w.H, (size_t)S * kk * sizeof(double), hipMemcpyDeviceToHost, st));
     XKV_HIP(hipMemcpyAsync(hinfo, w.info, S * sizeof(int), hipMemcpyDeviceToHost, st));
+    if (rounds == 1) XKV_HIP(hipMemcpyAsync(hTrace, w.trace, S * sizeof(double), hipMemcpyDeviceToHost, st));
     XKV_HIP(hipStreamSynchronize(st));
     for (int s = 0; s < S; ++s)
       if (hinfo[s]) return fail(XKV_ENUMERIC, "compress: Cholesky breakdown on side %d (rank of X below %d?)", s, kb);
@@ -434,6 +450,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       sides[s].stats[1] = relgap[s];
       sides[s].stats[2] = total_iters;
       sides[s].stats[3] = rounds;
+      sides[s].stats[4] = hTrace[s];
     }
   }
 

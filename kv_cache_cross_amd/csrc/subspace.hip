@@ -119,6 +119,23 @@ __global__ void zero_i32_kernel(int* p, long n) {
   if (i < n) p[i] = 0;
 }
 
+// tr[s] = sum_i C_s[i][i] (float64), one block per side: the total energy ||X||_F^2 of
+// the side, i.e. the sum of all eigenvalues of C.
+__global__ __launch_bounds__(256) void trace_kernel(const double* C, long sC, int n, double* tr) {
+  __shared__ double part[256];
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const double* Cs = C + (long)s * sC;
+  double acc = 0.0;
+  for (int i = tid; i < n; i += 256) acc += Cs[(long)i * n + i];
+  part[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) tr[s] = part[0];
+}
+
 // splitmix64 finaliser: a counter-based source of uniform bits.
 XKV_DEV uint64_t mix64(uint64_t z) {
   z += 0x9e3779b97f4a7c15ull;
@@ -195,6 +212,11 @@ hipError_t launch_copy_diag(const double* W, long ldw, long sW, double* dg, long
 hipError_t launch_ritz_residual(const double* YZ, const double* Vr, const double* theta, int n, int r,
                                 double* res2, int n_sides, hipStream_t st) {
   hipLaunchKernelGGL(ritz_residual_kernel, dim3((r + 63) / 64, n_sides), dim3(256), 0, st, YZ, Vr, theta, n, r, res2);
+  return hipGetLastError();
+}
+
+hipError_t launch_trace(const double* C, long sC, int n, int n_sides, double* tr, hipStream_t st) {
+  hipLaunchKernelGGL(trace_kernel, dim3(n_sides), dim3(256), 0, st, C, sC, n, tr);
   return hipGetLastError();
 }
 

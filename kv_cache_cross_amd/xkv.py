@@ -49,7 +49,7 @@ def compress(ctx: L.Context, sides, *, r: int, n_kv_heads: int, head_dim: int, c
     evals, stats = L.compress_sides(ctx, desc, specs, ws, stream)
     for o, e, st in zip(outs, evals, stats):
         o["eigvals"] = e
-        o["stats"] = dict(err_est=st[0], rel_gap=st[1], sweeps=int(st[2]), rounds=int(st[3]))
+        o["stats"] = dict(err_est=st[0], rel_gap=st[1], sweeps=int(st[2]), rounds=int(st[3]), energy=st[4])
     return outs
 
 

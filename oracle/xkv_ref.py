@@ -307,9 +307,11 @@ def energy_rank(eigvals, frac: float = 0.95, total: float | None = None) -> int:
     spectrum); with a partial spectrum pass trace(C).  Returns -1 when the given
     eigenvalues do not reach the target."""
     lam = np.sort(np.clip(np.asarray(eigvals, dtype=np.float64), 0.0, None))[::-1]
-    tot = lam.sum() if total is None else float(total)
+    csum = np.cumsum(lam)
+    # The total of a full spectrum is the last cumulative sum (one summation order for
+    # both, so that frac = 1 is reached exactly at the last nonzero eigenvalue).
+    tot = (csum[-1] if csum.size else 0.0) if total is None else float(total)
     if tot <= 0.0:
         return 0
-    csum = np.cumsum(lam)
     hit = np.nonzero(csum >= frac * tot)[0]
     return int(hit[0]) + 1 if hit.size else -1

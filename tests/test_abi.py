@@ -159,3 +159,37 @@ def test_host_eigh_clustered_and_degenerate():
 def test_host_eigh_rejects_bad_args():
     with pytest.raises(xk.XkvError):
         xk.host_eigh(np.eye(4), 5)
+
+
+def test_rank_info_layout_matches_header_order():
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct {\n  int energy_rank;"):src.index("} xkv_rank_info;")]
+    names = re.findall(r"\s([a-zA-Z_][a-zA-Z0-9_]*);", body)
+    assert names == [f for f, _ in L.RankInfo._fields_]
+
+
+def test_rank_stats_matches_oracle():
+    # Host entry point (no GPU work) against the oracle on random, flat, spiked and
+    # rank-deficient spectra, complete and partial.
+    import oracle
+    rng = np.random.default_rng(11)
+    spectra = [rng.exponential(size=300) ** 4, np.ones(64), np.r_[1e3, np.full(99, 1e-3)],
+               np.r_[rng.random(40) + 1.0, np.zeros(24)], np.geomspace(1.0, 1e-12, 200)]
+    for lam in spectra:
+        for frac in (0.5, 0.9, 0.95, 1.0):
+            got = xk.rank_stats(lam, frac=frac, complete=True)
+            assert got["energy_rank"] == oracle.energy_rank(lam, frac)
+            assert got["numerical_rank"] == oracle.numerical_rank(lam)
+            assert got["erank"] == pytest.approx(oracle.effective_rank(lam), rel=1e-12)
+            assert got["ner"] == pytest.approx(oracle.ner(lam), rel=1e-12)
+            assert got["covered"] == pytest.approx(1.0)
+        # Leading part of the spectrum against the full total.
+        top = np.sort(lam)[::-1][: len(lam) // 3]
+        part = xk.rank_stats(top, total=lam.sum(), frac=0.6)
+        assert part["energy_rank"] == oracle.energy_rank(top, 0.6, total=lam.sum())
+        assert part["covered"] == pytest.approx(top.sum() / lam.sum())
+        assert part["numerical_rank"] == -1 and np.isnan(part["ner"])
+    with pytest.raises(xk.XkvError):
+        xk.rank_stats(np.ones(4), frac=0.0)
+    with pytest.raises(xk.XkvError):
+        xk.rank_stats(np.ones(4), frac=1.5)

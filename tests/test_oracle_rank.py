@@ -74,3 +74,12 @@ def test_grouping_lowers_the_energy_rank_fraction():
     X = oracle.group_matrix(layers)
     grouped = oracle.energy_rank(np.linalg.eigvalsh(oracle.gram(X))) / X.shape[1]
     assert grouped < per_layer
+
+
+def test_energy_rank_full_fraction_reaches_last_nonzero():
+    # frac = 1 with the spectrum's own total: the count of nonzero eigenvalues (values of
+    # one magnitude, so that none is absorbed by the rounding of the running sum).
+    rng = np.random.default_rng(5)
+    for n in (7, 100, 1000):
+        lam = np.r_[rng.random(n) + 0.5, np.zeros(5)]
+        assert oracle.energy_rank(lam, 1.0) == n

@@ -20,6 +20,7 @@ from .xkv_ref import (  # noqa: F401
     compress_group,
     reconstruct_layer,
     landmarks,
+    append_tokens,
     candidate_chunks,
     landmark_scores,
     select_topk,

@@ -109,19 +109,34 @@ def reconstruct_layer(A, B, layer: int, d_kv: int) -> np.ndarray:
 
 
 def landmarks(K_layer, n_kv_heads: int, head_dim: int, chunk: int,
-              theta: float = ROPE_THETA) -> np.ndarray:
+              theta: float = ROPE_THETA, pos0: int = 0) -> np.ndarray:
     """Per-chunk landmark of every KV head: the mean of the post-RoPE original keys.
 
-    Returns (H_kv, T/chunk, d).  Chunks start at token 0 and have ``chunk`` tokens.
+    Returns (H_kv, T/chunk, d).  Chunks start at row 0 and have ``chunk`` tokens; row t
+    sits at position pos0 + t (pos0 > 0 for rows appended after a prefix).
     """
     K = np.asarray(K_layer, dtype=np.float64)
     T = K.shape[0]
     n_chunks = T // chunk
     out = np.zeros((n_kv_heads, n_chunks, head_dim))
     for h in range(n_kv_heads):
-        rot = rope(K[:, h * head_dim:(h + 1) * head_dim], np.arange(T), theta)
+        rot = rope(K[:, h * head_dim:(h + 1) * head_dim], pos0 + np.arange(T), theta)
         for c in range(n_chunks):
             out[h, c] = rot[c * chunk:(c + 1) * chunk].mean(axis=0)
+    return out
+
+
+def append_tokens(new_layers, Bt, pos0: int, *, n_kv_heads: int | None = None, head_dim: int | None = None,
+                  chunk: int | None = None, theta: float = ROPE_THETA, with_landmarks: bool = False) -> dict:
+    """Rows appended after a compressed prefix (multi-turn growth), projected onto the
+    stored basis: a_new = [x_l1 | ... | x_lG] V_r with V_r = Bt as stored (n x r), so that
+    A_new B_l reconstructs them like the prefix rows ([xKV blog] "xKV 到底做了什么？": the
+    shared token basis A = X V_r; the pages name the compression of generated tokens as a
+    limitation).  Landmarks of the new chunks use positions pos0 + t."""
+    X = group_matrix(new_layers)
+    out = dict(A=X @ np.asarray(Bt, dtype=np.float64))
+    if with_landmarks:
+        out["landmarks"] = [landmarks(x, n_kv_heads, head_dim, chunk, theta, pos0) for x in new_layers]
     return out
 
 

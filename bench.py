@@ -278,6 +278,37 @@ def main():
         variants["full_reconstruction_us_per_step"] = run_variant(n_cand, False, full_steps)
         variants["full_reconstruction_steps"] = full_steps
 
+    # ---- folding a turn's generated tokens into the compressed prefix: the D appended
+    # rows of every layer projected onto each group side's stored basis (+ landmarks of
+    # the new chunks), all 16 sides ----
+    append_rate = None
+    if c.append and D % c.chunk == 0 and D > 0:
+        app_args, app_keep = [], []
+        for g in range(n_groups):
+            for i, s_ in enumerate("KV"):
+                src = kn_all if s_ == "K" else vn_all
+                new = [src[:, g * G + li].contiguous() for li in range(G)]
+                A_new = torch.empty((D, r), dtype=dt, device=dev)
+                lm_new = (torch.empty((G, H, D // c.chunk, d), dtype=dt, device=dev) if s_ == "K" else None)
+                app_keep.append((new, A_new, lm_new))
+                app_args.append(xk.append_args(layers=new, Bt=outs[2 * g + i]["Bt"], A_new=A_new, pos0=T, r=r,
+                                               n_kv_heads=H, head_dim=d, chunk=c.chunk, landmarks_new=lm_new))
+        app_ws = torch.empty(max(xk.append_ws_size(a_) for a_ in app_args), dtype=torch.uint8, device=dev)
+        for a_ in app_args:
+            xk.compress_append(ctx, a_, app_ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            for a_ in app_args:
+                xk.compress_append(ctx, a_, app_ws)
+        e1.record()
+        torch.cuda.synchronize()
+        fold_us = e0.elapsed_time(e1) / 10 * 1e3
+        append_rate = {"tokens": D, "sides": len(app_args), "us_per_fold": round(fold_us, 2),
+                       "tokens_per_s": round(D / (fold_us * 1e-6), 1)}
+        del app_args, app_keep, app_ws
+
     # ---- rank diagnostics (outside the timed region): the cumulative-eigenvalue rank of
     # every group side from its leading Ritz values and trace, and the full spectrum of
     # layer 0 (K and V, a compression at r = d_kv) for NER and the same rank per layer ----
@@ -357,6 +388,7 @@ def main():
         "sr_speedup_vs_dense": round(dense["us_per_step"] / dec_us, 3) if dense else None,
         "sr_variants": variants or None,
         "rank_diagnostics": rank_diag,
+        "append_fold": append_rate,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -137,6 +137,41 @@ int xkv_compress_group(xkv_ctx ctx, const xkv_compress_desc* desc, const xkv_sid
                        void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Tokens appended after a compressed prefix (multi-turn growth)             */
+/* ------------------------------------------------------------------------ */
+
+/* The rows of m tokens generated after a compressed prefix are projected onto
+ * the group's stored basis, a_new = [x_l1 | ... | x_lG] V_r with V_r = Bt as
+ * stored, so that A_new B_l rebuilds them like the prefix rows ([xKV blog]
+ * "xKV 到底做了什么？": the shared token basis A = X V_r; the pages leave the
+ * compression of generated tokens open, this is the projection onto the
+ * existing basis), and for a key side the landmarks of the new chunks are
+ * formed at positions pos0 + t.  Writing A_new at A + pos0 * r (an A allocated
+ * with room for growth) extends the prefix to T' = pos0 + m; the landmarks of
+ * the new chunks follow the prefix's along each head's chunk axis. */
+typedef struct {
+  int m;                     /* appended tokens, > 0                                           */
+  long pos0;                 /* position of the first appended token (the prefix length)      */
+  int G, d_kv, r;            /* as in xkv_compress_desc (n = G * d_kv, r <= n)                */
+  int dtype;                 /* enum xkv_dtype of the rows, Bt, A_new and landmarks_new        */
+  int n_kv_heads, head_dim;  /* landmark layout; d_kv == n_kv_heads * head_dim                */
+  int chunk;                 /* with landmarks: m % chunk == 0 and pos0 % chunk == 0          */
+  double rope_theta;
+  const void* const* layers; /* (host) G device pointers; layer l: m x d_kv rows, stride ld_layer */
+  long ld_layer;             /* >= d_kv; for bf16 a multiple of 8 (rows 16-byte aligned)       */
+  const void* Bt;            /* n x r stored basis (Bt = V_r), row stride r                    */
+  void* A_new;               /* m x r output rows, row stride r                                */
+  void* landmarks_new;       /* nullable: G x n_kv_heads x (m/chunk) x head_dim                 */
+} xkv_append_args;
+
+/* Workspace bytes for xkv_compress_append (the transposed basis, r x n). */
+int xkv_append_ws_size(const xkv_append_args* args, size_t* bytes);
+
+/* Enqueue the projection (bf16 matrix cores, float32 sums) and the landmarks on
+ * `stream`.  Errors: XKV_EINVAL (sizes, NULL pointers, alignment). */
+int xkv_compress_append(xkv_ctx ctx, const xkv_append_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Selective Reconstruction decode (one layer, one step, `batch` sequences)  */
 /* ------------------------------------------------------------------------ */
 

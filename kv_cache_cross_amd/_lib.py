@@ -58,6 +58,13 @@ class SrArgs(C.Structure):
                 ("out", C.c_void_p), ("sel", C.c_void_p)]
 
 
+class AppendArgs(C.Structure):
+    _fields_ = [("m", C.c_int), ("pos0", C.c_long), ("G", C.c_int), ("d_kv", C.c_int), ("r", C.c_int),
+                ("dtype", C.c_int), ("n_kv_heads", C.c_int), ("head_dim", C.c_int), ("chunk", C.c_int),
+                ("rope_theta", C.c_double), ("layers", C.POINTER(C.c_void_p)), ("ld_layer", C.c_long),
+                ("Bt", C.c_void_p), ("A_new", C.c_void_p), ("landmarks_new", C.c_void_p)]
+
+
 class RankInfo(C.Structure):
     _fields_ = [("energy_rank", C.c_int), ("covered", C.c_double), ("numerical_rank", C.c_int),
                 ("erank", C.c_double), ("ner", C.c_double)]
@@ -100,6 +107,8 @@ def lib():
         L.xkv_dense_ws_size.argtypes = [C.POINTER(DenseArgs), C.POINTER(sz)]
         L.xkv_dense_decode.argtypes = [vp, C.POINTER(DenseArgs), vp, sz, vp]
         L.xkv_rank_stats.argtypes = [C.POINTER(C.c_double), i, C.c_double, C.c_double, i, C.POINTER(RankInfo)]
+        L.xkv_append_ws_size.argtypes = [C.POINTER(AppendArgs), C.POINTER(sz)]
+        L.xkv_compress_append.argtypes = [vp, C.POINTER(AppendArgs), vp, sz, vp]
         L.xkv_rope_rows.argtypes = [vp, l, vp, l, i, l, i, i, C.c_double, i, vp]
         _lib = L
     return _lib
@@ -277,6 +286,31 @@ def host_eigh(H: np.ndarray, nvec: int):
     Z = np.zeros((n, nvec))
     _check(lib().xkv_host_eigh(n, H.ctypes.data, nvec, w.ctypes.data, Z.ctypes.data))
     return w, Z
+
+
+def append_args(*, layers, Bt, A_new, pos0: int, r: int, n_kv_heads: int = 0, head_dim: int = 0,
+                chunk: int = 0, rope_theta: float = 10000.0, landmarks_new=None):
+    """AppendArgs for rows appended after a compressed prefix; `layers` are the G new-row
+    tensors (m x d_kv each).  The pointer array is kept alive on the returned object."""
+    m, d_kv = layers[0].shape
+    ptrs = (C.c_void_p * len(layers))(*[x.data_ptr() for x in layers])
+    a = AppendArgs(m=m, pos0=pos0, G=len(layers), d_kv=d_kv, r=r, dtype=_dtype_code(layers[0]),
+                   n_kv_heads=n_kv_heads, head_dim=head_dim, chunk=chunk, rope_theta=rope_theta,
+                   layers=C.cast(ptrs, C.POINTER(C.c_void_p)), ld_layer=layers[0].stride(0), Bt=Bt.data_ptr(),
+                   A_new=A_new.data_ptr(), landmarks_new=landmarks_new.data_ptr() if landmarks_new is not None else None)
+    a._keep = ptrs
+    return a
+
+
+def append_ws_size(args: AppendArgs) -> int:
+    n = C.c_size_t()
+    _check(lib().xkv_append_ws_size(C.byref(args), C.byref(n)))
+    return n.value
+
+
+def compress_append(ctx, args: AppendArgs, ws: torch.Tensor, stream=None):
+    _check(lib().xkv_compress_append(ctx.handle, C.byref(args), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
 
 
 def rank_stats(eigvals, total: float = 0.0, frac: float = 0.95, complete: bool = False) -> dict:

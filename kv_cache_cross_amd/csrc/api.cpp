@@ -711,6 +711,70 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
 }
 
 // ---------------------------------------------------------------------------
+// Tokens appended after a compressed prefix
+// ---------------------------------------------------------------------------
+namespace {
+
+int check_append(const xkv_append_args* a, size_t* ws_need) {
+  if (!a) return fail(XKV_EINVAL, "append: args is NULL");
+  if (a->m <= 0 || a->pos0 < 0 || a->G <= 0 || a->G > 16 || a->d_kv <= 0 || a->d_kv % 8 || a->r <= 0 ||
+      a->r > a->G * a->d_kv)
+    return fail(XKV_EINVAL, "append: bad sizes (m=%d, G=%d, d_kv=%d, r=%d)", a->m, a->G, a->d_kv, a->r);
+  if (a->dtype != XKV_F32 && a->dtype != XKV_BF16) return fail(XKV_EINVAL, "append: unknown dtype");
+  if (!a->layers || !a->Bt || !a->A_new) return fail(XKV_EINVAL, "append: a required pointer is NULL");
+  if (a->ld_layer < a->d_kv) return fail(XKV_EINVAL, "append: ld_layer too small");
+  for (int l = 0; l < a->G; ++l) {
+    if (!a->layers[l]) return fail(XKV_EINVAL, "append: layer pointer %d is NULL", l);
+    if (a->dtype == XKV_BF16 && (!aligned16(a->layers[l]) || a->ld_layer % 8))
+      return fail(XKV_EINVAL, "append: bf16 rows need 16-byte alignment and ld_layer %% 8 == 0");
+  }
+  if ((long)a->m * a->ld_layer >= (1L << 31)) return fail(XKV_EINVAL, "append: m * ld_layer too large");
+  if (a->landmarks_new) {
+    if (a->n_kv_heads <= 0 || a->head_dim <= 0 || a->head_dim % 2 || a->n_kv_heads * a->head_dim != a->d_kv)
+      return fail(XKV_EINVAL, "append: landmark layout does not match d_kv");
+    if (a->chunk <= 0 || a->m % a->chunk || a->pos0 % a->chunk)
+      return fail(XKV_EINVAL, "append: m and pos0 must be multiples of chunk for landmarks");
+  }
+  const size_t es = a->dtype == XKV_BF16 ? 2 : 4;
+  *ws_need = align256((size_t)a->r * a->G * a->d_kv * es);
+  return XKV_OK;
+}
+
+}  // namespace
+
+extern "C" int xkv_append_ws_size(const xkv_append_args* args, size_t* bytes) {
+  if (!bytes) return fail(XKV_EINVAL, "xkv_append_ws_size: bytes is NULL");
+  return check_append(args, bytes);
+}
+
+extern "C" int xkv_compress_append(xkv_ctx ctx, const xkv_append_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(XKV_EINVAL, "append: ctx is NULL");
+  size_t need = 0;
+  int rc = check_append(a, &need);
+  if (rc) return rc;
+  if (!ws || ws_bytes < need) return fail(XKV_EWORKSPACE, "append: workspace %zu bytes < %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  XKV_HIP(hipSetDevice(ctx->device));
+  const int n = a->G * a->d_kv, bf16 = a->dtype == XKV_BF16;
+  xkv::PtrTable lay{}, aout{};
+  for (int l = 0; l < a->G; ++l) lay.p[l] = a->layers[l];
+  aout.p[0] = a->A_new;
+  XKV_K(xkv::launch_transpose_basis(a->Bt, a->r, n, a->r, ws, bf16, st));
+  if (bf16)
+    XKV_K(xkv::launch_project_bf16(lay, 1, a->G, a->ld_layer, a->m, a->d_kv, (const uint16_t*)ws, 0, a->r, aout, st));
+  else
+    XKV_K(xkv::launch_project_f32(lay, 1, a->G, a->ld_layer, a->m, a->d_kv, (const float*)ws, 0, a->r, aout, st));
+  if (a->landmarks_new) {
+    xkv::PtrTable lmo{};
+    const long per_layer = (long)a->n_kv_heads * (a->m / a->chunk) * a->head_dim * (bf16 ? 2 : 4);
+    for (int l = 0; l < a->G; ++l) lmo.p[l] = (char*)a->landmarks_new + l * per_layer;
+    XKV_K(xkv::launch_landmarks(lay, 1, a->G, a->ld_layer, a->m, a->n_kv_heads, a->head_dim, a->chunk, a->rope_theta,
+                                lmo, bf16, st, a->pos0));
+  }
+  return XKV_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Dense decode baseline
 // ---------------------------------------------------------------------------
 namespace {

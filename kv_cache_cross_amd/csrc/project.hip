@@ -157,6 +157,7 @@ struct LmArgs {
   PtrTable out;
   int G, T, H, d, chunk, n_chunks, bf16;
   long ld;
+  long pos0;   // position of row 0 (0 for a prefix; the old length when rows are appended)
   double theta;
 };
 
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) void landmarks_kernel(LmArgs a) {
       xh = src[half];
     }
     float cs, sn;
-    rope_cs(t, f, &cs, &sn);
+    rope_cs(a.pos0 + t, f, &cs, &sn);
     lo += xl * cs - xh * sn;
     hi += xh * cs + xl * sn;
   }
@@ -201,7 +202,33 @@ __global__ __launch_bounds__(256) void landmarks_kernel(LmArgs a) {
   }
 }
 
+// VrT (r x n) = Bt^T (Bt: n x r, row stride ldb), 32 x 32 tiles through LDS.
+template <typename ST>
+__global__ __launch_bounds__(256) void transpose_kernel(const ST* Bt, long ldb, int n, int r, ST* VrT) {
+  __shared__ ST tile[32][33];
+  const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32, tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int k = ty; k < 32; k += 8) {
+    const int i = i0 + k, j = j0 + tx;
+    if (i < n && j < r) tile[k][tx] = Bt[(long)i * ldb + j];
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int j = j0 + k, i = i0 + tx;
+    if (i < n && j < r) VrT[(long)j * n + i] = tile[tx][k];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_transpose_basis(const void* Bt, long ldb, int n, int r, void* VrT, int bf16, hipStream_t st) {
+  const dim3 grid((n + 31) / 32, (r + 31) / 32);
+  if (bf16)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)Bt, ldb, n, r,
+                       (uint16_t*)VrT);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, (const float*)Bt, ldb, n, r, (float*)VrT);
+  return hipGetLastError();
+}
 
 static constexpr size_t kProjLds = 2 * 2 * PT * PROW * sizeof(uint16_t);
 
@@ -252,8 +279,9 @@ hipError_t launch_project_f32(const PtrTable& layers, int n_sides, int G, long l
 
 hipError_t launch_landmarks(const PtrTable& layers, int n_sides, int G, long ld, int T, int n_kv_heads,
                             int head_dim, int chunk, double theta, const PtrTable& lm_out, int bf16,
-                            hipStream_t st) {
+                            hipStream_t st, long pos0) {
   LmArgs a;
+  a.pos0 = pos0;
   a.layers = layers;
   a.out = lm_out;
   a.G = G;

@@ -65,10 +65,13 @@ hipError_t launch_project_bf16(const PtrTable& layers, int n_sides, int G, long 
 hipError_t launch_project_f32(const PtrTable& layers, int n_sides, int G, long ld, int T, int d_kv,
                               const float* VrT, long sVT, int r, const PtrTable& A_out,
                               hipStream_t st);
-// lm_out.p[s*G + l] receives n_kv_heads x (T/chunk) x head_dim for layer l of side s.
+// lm_out.p[s*G + l] receives n_kv_heads x (T/chunk) x head_dim for layer l of side s; row 0
+// of the layers sits at position pos0.
 hipError_t launch_landmarks(const PtrTable& layers, int n_sides, int G, long ld, int T, int n_kv_heads,
                             int head_dim, int chunk, double theta, const PtrTable& lm_out, int bf16,
-                            hipStream_t st);
+                            hipStream_t st, long pos0 = 0);
+// VrT (r x n, row stride n) = Bt^T for an n x r basis Bt with row stride ldb.
+hipError_t launch_transpose_basis(const void* Bt, long ldb, int n, int r, void* VrT, int bf16, hipStream_t st);
 
 // ---- Selective Reconstruction decode --------------------------------------
 struct SrParams;  // defined in decode.hip

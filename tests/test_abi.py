@@ -193,3 +193,24 @@ def test_rank_stats_matches_oracle():
         xk.rank_stats(np.ones(4), frac=0.0)
     with pytest.raises(xk.XkvError):
         xk.rank_stats(np.ones(4), frac=1.5)
+
+
+def test_append_args_layout_and_validation():
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct {\n  int m;"):src.index("} xkv_append_args;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*?\s*([a-zA-Z_][a-zA-Z0-9_]*)\s*[,;]", body)
+    assert names == [f for f, _ in L.AppendArgs._fields_]
+    ptrs = (C.c_void_p * 2)(16, 16)
+    base = dict(m=64, pos0=128, G=2, d_kv=256, r=128, dtype=xk.XKV_BF16, n_kv_heads=2, head_dim=128, chunk=8,
+                rope_theta=1e4, layers=C.cast(ptrs, C.POINTER(C.c_void_p)), ld_layer=256, Bt=16, A_new=16,
+                landmarks_new=16)
+    n = C.c_size_t()
+    assert xk.lib().xkv_append_ws_size(C.byref(L.AppendArgs(**base)), C.byref(n)) == 0
+    assert n.value >= 128 * 512 * 2
+    for bad in (dict(m=0), dict(r=513), dict(d_kv=12), dict(m=60), dict(pos0=4), dict(ld_layer=250),
+                dict(Bt=None), dict(dtype=7), dict(n_kv_heads=3)):
+        assert xk.lib().xkv_append_ws_size(C.byref(L.AppendArgs(**dict(base, **bad))), C.byref(n)) == L.XKV_EINVAL, bad
+    # Without landmarks, m and pos0 need not be multiples of chunk.
+    assert xk.lib().xkv_append_ws_size(C.byref(L.AppendArgs(**dict(base, m=60, pos0=4, landmarks_new=None))),
+                                       C.byref(n)) == 0

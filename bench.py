@@ -40,17 +40,21 @@ BF16_PEAK_TFLOPS = 2500.0
 # what the same counter reads for a 1 GiB device-to-device copy (read 524300.5 KiB, written
 # 1048576 KiB).  It stands only while the decode kernels' source is the one measured: the
 # source's SHA-256 prefix is recorded and `traffic` is null when it differs.
-ATTEND_TRAFFIC = {"decode_src_sha256": "e3383182a5f84fa2", "fetch_kib": 17018.2, "write_kib": 2056.0,
+ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "a33038fd2cc3c4a7", "fetch_kib": 17013.2, "write_kib": 2056.0,
                   "fetch_scale": 1048576.0 / 524300.5, "write_scale": 1.0}
+# The same for one launch of the Gram kernel over the 16 group sides of the 64k workload
+# (3 dispatches).  FETCH_SIZE counts what the L2 caches request from the memory fabric,
+# so the Infinity Cache's hits are included: it is the Gram's L2-miss traffic.
+GRAM_TRAFFIC = {"src": "gram.hip", "src_sha256": "659e928b4225f03d", "fetch_kib": 62269422.6, "write_kib": 11572111.7,
+                "fetch_scale": 1048576.0 / 524300.5, "write_scale": 1.0}
 
 
-def attend_traffic_bytes():
+def traffic_bytes(t):
     import hashlib
-    src = os.path.join(ROOT, "kv_cache_cross_amd", "csrc", "decode.hip")
+    src = os.path.join(ROOT, "kv_cache_cross_amd", "csrc", t["src"])
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    t = ATTEND_TRAFFIC
-    if sha != t["decode_src_sha256"]:
+    if sha != t["src_sha256"]:
         return None
     return int((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
 
@@ -67,6 +71,9 @@ def parse():
     ap.add_argument("--config", default="llama64k")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense baseline, the SR variants, the token fold and the rank diagnostics "
+                         "(for counter runs that should see the main decode kernels only)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB device to device (a plain copy "
@@ -231,11 +238,11 @@ def main():
 
     # ---- dense flash-decode baseline: the same queries over the full post-RoPE cache ----
     dense = dense_baseline(xk, ctx, c, layers, q_all, kn_all if c.append else None,
-                           vn_all if c.append else None, D, args.steps) if D > 0 else None
+                           vn_all if c.append else None, D, args.steps) if (D > 0 and not args.no_extras) else None
     # ---- the SR variants on the same cache: xK-SR (values exact, on the GPU) and full
     # reconstruction (every candidate chunk selected) ----
     variants = {}
-    if D > 0:
+    if D > 0 and not args.no_extras:
         def run_variant(top_k, exact_values, steps):
             vdec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk,
                                    top_k=top_k, n_sink=c.n_sink, n_local=c.n_local, r_k=r,
@@ -282,7 +289,7 @@ def main():
     # rows of every layer projected onto each group side's stored basis (+ landmarks of
     # the new chunks), all 16 sides ----
     append_rate = None
-    if c.append and D % c.chunk == 0 and D > 0:
+    if c.append and D % c.chunk == 0 and D > 0 and not args.no_extras:
         app_args, app_keep = [], []
         for g in range(n_groups):
             for i, s_ in enumerate("KV"):
@@ -313,7 +320,7 @@ def main():
     # every group side from its leading Ritz values and trace, and the full spectrum of
     # layer 0 (K and V, a compression at r = d_kv) for NER and the same rank per layer ----
     rank_diag = None
-    if c.dtype == "bf16":
+    if c.dtype == "bf16" and not args.no_extras:
         def frac_rank(ev, total):
             rs = xk.rank_stats(ev, total=total, frac=0.95)
             return rs["energy_rank"] / float(G * d_kv) if rs["energy_rank"] > 0 else None
@@ -348,7 +355,8 @@ def main():
     del gram_out
     gram_tflops = gram_flops / (gram_ms * 1e-3) / 1e12
 
-    traffic = attend_traffic_bytes() if (c.name == "llama64k" and D > 0) else None
+    traffic = traffic_bytes(ATTEND_TRAFFIC) if (c.name == "llama64k" and D > 0) else None
+    gram_traffic = traffic_bytes(GRAM_TRAFFIC) if c.name == "llama64k" else None
     algo_bytes_launch = float(np.mean(attend_union[-1]))
     line = {
         "metric": "SR decode us/step + achieved HBM GB/s; KV compress tokens/s at 64k ctx",
@@ -374,7 +382,7 @@ def main():
         "compress_s": round(comp_s, 4),
         "compress_stats": {"err_est_max": float(max(st[0] for st in stats)), "sweeps": int(stats[0][2]),
                            "rounds": int(stats[0][3])},
-        "roofline": {"bound": "hbm", "kernel": "sr_attend_kernel", "achieved": round(achieved_att, 1),
+        "roofline": {"bound": "hbm", "kernel": "sr_attend_mfma_kernel<false>", "achieved": round(achieved_att, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": int(algo_bytes_launch),
@@ -383,7 +391,9 @@ def main():
                      "avg_launch_us": round(att_ms_all * 1e3, 2)},
         "roofline_gram": {"bound": "mfma", "kernel": "gram_bf16_kernel", "achieved": round(gram_tflops, 1),
                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
-                          "launch_ms": round(gram_ms, 3), "sides": S},
+                          "launch_ms": round(gram_ms, 3), "sides": S, "traffic": gram_traffic,
+                          "traffic_unit": "L2-miss bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                          "unique_input_bytes": int(S * T * n * esz)},
         "dense_baseline": dense,
         "sr_speedup_vs_dense": round(dense["us_per_step"] / dec_us, 3) if dense else None,
         "sr_variants": variants or None,

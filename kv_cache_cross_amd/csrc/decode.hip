@@ -90,6 +90,17 @@ XKV_DEV float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Sum over aligned groups of `lanes` (8 or 16) lanes, the result in every lane of the
+// group: quad_perm [1,0,3,2] then [2,3,0,1] sum each quad, row_half_mirror adds the
+// mirrored quad of each 8-lane half, row_mirror the mirrored half of each 16-lane row.
+XKV_DEV float lane_group_sum(float v, int lanes) {
+  v += XKV_DPP_F(0.f, v, 0xB1, 0xF, false);
+  v += XKV_DPP_F(0.f, v, 0x4E, 0xF, false);
+  v += XKV_DPP_F(0.f, v, 0x141, 0xF, false);
+  if (lanes == 16) v += XKV_DPP_F(0.f, v, 0x140, 0xF, false);
+  return v;
+}
+
 constexpr int TKT = 1024;      // threads of a top-k block
 constexpr int TKW = TKT / 64;  // its waves
 
@@ -616,17 +627,24 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
       for (int u = 0; u < BATCH; ++u)
         if (it0 + u < iters) raw[u].load(lm + (long)min(c0 + (it0 + u) * cpi + slot, c1 - 1) * P.d);
     }
+    // All BATCH slots are reduced together (slots past `iters` hold unused values), so
+    // the lane-group sums of different chunks overlap instead of waiting on each other.
+    float dots[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      if (it0 + u >= iters) break;
       float v[8];
       raw[u].get(v);
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += qv[e] * v[e];
-      for (int o = lpc >> 1; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+      dots[u] = dot;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) dots[u] = lane_group_sum(dots[u], lpc);
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
       const int c = c0 + (it0 + u) * cpi + slot;
-      if (c < c1 && sub == 0) scores[c] = dot;
+      if (it0 + u < iters && c < c1 && sub == 0) scores[c] = dots[u];
     }
   }
 }

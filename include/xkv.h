@@ -238,8 +238,9 @@ int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
  * values (bf16, head_dim 128, r_k == r_v a multiple of 128 up to 4096; enough
  * for every chunk of a 64k prefix, i.e. full reconstruction) and 257 otherwise.
  * With r_v == 0 (xK-SR: keys compressed, values exact in V_full) the keys take
- * the same matrix-core path when r_k is a multiple of 128 (V_full 4-byte
- * aligned, even strides) and the exact value rows are summed in value space. */
+ * the same matrix-core path when r_k is a multiple of 128 (V_full 16-byte
+ * aligned, strides multiples of 8 elements; XKV_EINVAL otherwise) and the exact
+ * value rows are summed in value space. */
 int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /* One decode step through `n_layers` layers in order (args[l] describes layer l;

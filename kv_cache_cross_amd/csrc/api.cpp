@@ -598,9 +598,9 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
         (!exact_v && (!aligned16(a->A_v) || !aligned16(a->Bt_v) || a->ld_A_v % 8 || a->ld_Bt_v % 8 ||
                       a->bstride_A_v % 8 || a->bstride_Bt_v % 8)))
       return fail(XKV_EINVAL, "sr: bf16 A/Bt need 16-byte alignment and strides that are multiples of 8");
-    // exact values: 4-byte loads of two adjacent dims
-    if (exact_v && ((uintptr_t)a->V_full % 4 || a->ld_V % 2 || a->bstride_V % 2))
-      return fail(XKV_EINVAL, "sr: bf16 V_full needs 4-byte alignment and even strides");
+    // exact values: rows gathered 16 bytes at a time
+    if (exact_v && (!aligned16(a->V_full) || a->ld_V % 8 || a->bstride_V % 8))
+      return fail(XKV_EINVAL, "sr: bf16 V_full needs 16-byte alignment and strides that are multiples of 8");
   }
   if (!aligned16(a->landmarks) || a->bstride_lm % (a->dtype == XKV_BF16 ? 8 : 4))
     return fail(XKV_EINVAL, "sr: landmarks need 16-byte alignment");

@@ -50,6 +50,8 @@
 namespace xkv {
 namespace {
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+
 constexpr int RB = 64;        // rows per attend block (generic path) and per exact-row tile
 constexpr int RBM = 64;       // rows per matrix-core attend block
 constexpr int ETR = 64;       // rows per exact-row tile
@@ -701,294 +703,402 @@ XKV_DEV void write_partial(const SrParams& P, int b, int h, int s, float (*pw)[R
   }
 }
 
+// Barrier for LDS hand-offs: this wave's LDS stores have completed (lgkmcnt(0)), then
+// s_barrier.  No memory fence: a workgroup fence would also wait for every global load
+// and direct-to-LDS load in flight, which the attend kernel keeps going across barriers.
+// The empty asm statements keep the compiler from moving memory accesses across it.
+XKV_DEV void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited for
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): two bf16 MFMA operands whose
+// products carry about 16 significant bits of x.
+XKV_DEV void split_bf16x8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 b = (__bf16)x[e];
+    hi[e] = b;
+    lo[e] = (__bf16)(x[e] - (float)b);
+  }
+}
+
+constexpr int VROW_MAX = KCH + 16;   // LDS row of the value rows written for the weighted sum
+constexpr int QSLOT = 8 * VROW_MAX * 2;   // bytes of one wave's share of region V
+
 // EXACT_V: values are exact rows of V_full (xK-SR); the partial holds the value-space
 // sum sum_t p_t v_t per query head instead of the rank-space sum.
-template <bool EXACT_V>
+//
+// Work split of one block (64 gathered rows of one KV head, eight waves):
+//  * keys: wave w = (dim group dg = w % 4, rank half kh = w / 4) rebuilds key dims
+//    16 dg + m and 64 + 16 dg + m (m < 16) of all 64 rows over half of each rank chunk,
+//    as K^T tiles D[dim][row] = B_k[dim] . A_k[row] (the B_k slice is the MFMA A
+//    operand, from registers; the staged A_k rows are the B operand, from LDS).  A lane
+//    then holds dims 4(l/16) + v of both halves of a RoPE pair for one row;
+//  * the B_k slice reaches registers through LDS: direct-to-LDS loads of whole rows
+//    (1 KB per instruction), 16-byte chunks XOR-swizzled by row so that the fragment
+//    reads are free of bank conflicts.  Row-gathering fragment loads straight from
+//    memory (16 rows x 64 bytes per instruction) cost several times more;
+//  * the two rank halves of a tile meet in LDS: wave (dg, kh) finishes row tiles
+//    2 kh, 2 kh + 1, rotates them (RoPE in the lane, no exchange) and scores them
+//    against the query group on the MFMA (query and keys split into bf16 hi + lo parts,
+//    three products); the four dim groups' partial scores of a row are added in LDS in
+//    a fixed order;
+//  * value rows (A_v rank chunk, or V_full dims with exact values) go to LDS with
+//    direct-to-LDS loads right behind the A_k rows, 16-byte chunks XOR-swizzled by row
+//    so that the transposing reads below are free of bank conflicts;
+//  * weighted value sum: P (query heads x 64 rows, hi + lo) times the 64 value rows on
+//    the MFMA, the value rows read from LDS with transposing reads; wave w owns columns
+//    [w W / 8, (w + 1) W / 8) of the W-wide sum, so no cross-wave reduction is needed.
+// MULTI: r spans several rank chunks (the single-chunk instantiation issues every
+// direct-to-LDS load outside any branch, which keeps the compiler's own waits for them
+// exact).
+template <bool EXACT_V, bool MULTI>
 __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* Ak = (uint16_t*)smem;              // [RBM][AROW] staged A_k rows
-  float (*kh)[HROW] = (float (*)[HROW])smem;   // rotated keys after the MFMAs (aliases Ak)
-  __shared__ float qs[MAXG][MAXD];
-  __shared__ __align__(16) float pw[MAXG][RBM];
+  // Region A: staged A_k rows (stride AROW); before them the B_k staging of dt = 1, after
+  // them the partial-key exchange, partial scores, softmax weights and statistics.
+  __shared__ __align__(16) uint16_t Ak[RBM * AROW];
+  // Region V: the B_k staging of dt = 0, then the value rows (W columns each, no padding,
+  // swizzled).
+  __shared__ __align__(16) uint16_t Vr[RBM * VROW_MAX];
   __shared__ int rows_t[RBM];
-  __shared__ float st_m[MAXG], st_l[MAXG];
   const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int dg = wave & 3, kh = wave >> 2;
   const long bh = (long)b * P.Hkv + h;
   const int r = P.r_k, grp = P.grp;
+  // Rank chunk: the largest of 512, 256, 128 that divides r.  A staged half-row of B_k
+  // holds KC/2 ranks = 2^lcr chunks of 16 bytes; a rank half is nks MFMA k-steps.
+  const int KC = (r & 511) == 0 ? 512 : (r & 255) == 0 ? 256 : 128;
+  const int lcr = KC == 512 ? 5 : KC == 256 ? 4 : 3;
+  const int nks = KC >> 6;
+  // Value chunk: W columns, 2^lcv chunks of 16 bytes per row.
+  const int W = EXACT_V ? 128 : KC;
+  const int lcv = EXACT_V ? 4 : lcr + 1;
+  const int Wtot = EXACT_V ? 128 : r;
 
-  const uint16_t* Ag_k = (const uint16_t*)P.A_k + b * P.bs_A_k;
-  const uint16_t* Ag_v = (const uint16_t*)P.A_v + b * P.bs_A_v;
-  // Wave w rebuilds key dims 8w + m and 64 + 8w + m (m < 8) of all 64 rows: MFMA
-  // column n holds dim 8w + n for n < 8 and 56 + 8w + n for n >= 8, so the RoPE pair
-  // (i, i + 64) sits in columns n and n + 8, eight lanes apart.  Lane l reads B row
-  // dim(l % 16) over rank slice [32(l/16), 32(l/16) + 32) of each 128-wide k-block
-  // (four MFMA k-steps); the A operand is read with the same permutation of k, so the
-  // product is unchanged.
-  const int n = lane & 15, g = lane >> 4;
-  const int dim = n < 8 ? 8 * wave + n : 56 + 8 * wave + n;
-  const uint16_t* b0 = (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)(h * 128 + dim) * P.ld_Bt_k + 32 * g;
-
-  // Prologue, ordered so that independent loads overlap: the selected chunk ids, the
-  // raw queries and the first chunk's B slice are all in flight before anything
-  // waits; the queries are rotated while the A rows stream in.
+  // ---- prologue: every load that does not wait on the selection is issued first ----
   int csel = -1;
   if (tid < RBM) {
     const int ci = s * P.cps + tid / P.chunk;
     if (ci < P.k_eff) csel = P.sel[bh * P.top_k + ci];
   }
-  const uint16_t* qg = (const uint16_t*)P.q + ((long)b * P.Hq + (long)h * grp) * 128;
-  uint16_t qraw[2] = {0, 0};
-  const double q_turns = P.turns[tid & 63];
-  if (tid < grp * 64) {   // (query head, pair) = (tid / 64, tid % 64)
-    qraw[0] = qg[(tid >> 6) * 128 + (tid & 63)];
-    qraw[1] = qg[(tid >> 6) * 128 + (tid & 63) + 64];
+  // Query fragment of this lane: head j = n (zero past the group), dims 16 dg + 4 g + v
+  // and their RoPE partners 64 + 16 dg + 4 g + v.
+  const int jq = min(n, grp - 1);
+  const uint16_t* qg = (const uint16_t*)P.q + ((long)b * P.Hq + (long)h * grp + jq) * 128 + 16 * dg + 4 * g;
+  uint16_t qraw[8];
+  double turns[4];   // RoPE frequencies (turns per position) of this lane's dims, for q and k
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    qraw[v] = qg[v];
+    qraw[4 + v] = qg[64 + v];
+    turns[v] = P.turns[16 * dg + 4 * g + v];
   }
-  uint4 bq[KCH / 128][4];
-  auto load_b = [&](int kc, int kw) {
+  // B_k staging: half-rows (dims 16 dg + 64 dt + m, ranks kc + kh KC/2 + [0, KC/2)) of
+  // this wave, dt = 0 into its slot of region V, dt = 1 into its slot of region A.
+  // 16-byte unit p of a slot holds row m = p >> lcr, chunk c = (p & (2^lcr - 1)) ^ (m & 7).
+  const uint16_t* bk = (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)(h * 128 + 16 * dg) * P.ld_Bt_k;
+  // One half-row set (dt) into one slot; called with each slot's own array so that every
+  // direct-to-LDS load names a single LDS array (which lets the compiler keep the loads
+  // into one array from delaying reads of the other).
+  auto stage_half = [&](unsigned char* slot, int dt, int kc) {
+    const int ni = 1 << (lcr - 2);   // 1 KB instructions per half-row set
 #pragma unroll
-    for (int kb = 0; kb < KCH / 128; ++kb) {
-      const int k0 = kc + min(kb * 128, kw - 128);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bq[kb][i] = *(const uint4*)(b0 + k0 + 8 * i);
+    for (int i = 0; i < 8; ++i) {
+      const int p = 64 * min(i, ni - 1) + lane;   // past the set: the last instruction again
+      const int m = p >> lcr, c = (p & ((1 << lcr) - 1)) ^ (m & 7);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(bk + (long)(64 * dt + m) * P.ld_Bt_k + kc +
+                                                           kh * (KC >> 1) + 8 * c),
+          (__attribute__((address_space(3))) void*)(slot + 1024 * min(i, ni - 1)), 16, 0, 0);
     }
   };
-  load_b(0, min(KCH, r));
+  auto stage_b = [&](int kc) {
+    stage_half((unsigned char*)Vr + wave * QSLOT, 0, kc);
+    stage_half((unsigned char*)Ak + wave * 8192, 1, kc);
+  };
+  // Fragment (dt, ks) of lane (n, g): row n, chunk 4 ks + g.
+  uint4 bq[2][8];
+  auto read_half = [&](const unsigned char* slot, int dt) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int unit = (n << lcr) + ((4 * min(ks, nks - 1) + g) ^ (n & 7));
+      bq[dt][ks] = *(const uint4*)(slot + 16 * unit);
+    }
+  };
+  auto read_b = [&]() {
+    read_half((const unsigned char*)Vr + wave * QSLOT, 0);
+    read_half((const unsigned char*)Ak + wave * 8192, 1);
+  };
+  stage_b(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B_k slice has landed
+  read_b();
   if (tid < RBM) {
     const int t = csel * P.chunk + tid % P.chunk;
     rows_t[tid] = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
   }
-  __syncthreads();
+  lds_sync();   // the row ids are visible and every wave has read its B_k staging
 
-  // Stage rank columns [kc, kc + kw) of the gathered rows of A into LDS with
-  // direct-to-LDS loads (no registers): wave w takes rows 8w..8w+7, one row per
-  // instruction, lane l bytes [16l, 16l+16).  The row id is the same on every lane of
-  // the wave.  Absent rows are zero-filled first, so that no LDS store follows a load
-  // in flight.  Lanes past the chunk read its last 16 bytes (in bounds) into columns
-  // that are never used.
-  constexpr int RPW = RBM / 8;   // rows per wave
-  int tr[RPW];
+  // Wave w gathers rows 8w .. 8w+7.  A_k rows: one row per instruction, lane l bytes
+  // [16l, 16l + 16) (lanes past a narrow chunk re-read its last 16 bytes into columns
+  // never read).  Value rows: 2^lcv units per row, row rho's chunk c at unit
+  // rho 2^lcv + (c ^ 2 (rho & 3)), one 1 KB instruction per 64 units (repeated past the
+  // wave's rows: the same bytes to the same place).  Absent rows (-1) load row 0 and are
+  // masked later, so that every load is unconditional.
+  const int lcv_ni = 1 << (lcv - 3);   // 1 KB instructions for a wave's 8 value rows
+  int tr[8], tv[8];   // A_k row of instruction i; value row of this lane in value instruction i
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) tr[i] = rows_t[wave * RPW + i];
-  auto zero_absent = [&](uint16_t* dst) {
+  for (int i = 0; i < 8; ++i) {
+    tr[i] = rows_t[wave * 8 + i];
+    tv[i] = rows_t[wave * 8 + ((64 * min(i, lcv_ni - 1) + lane) >> lcv)];
+  }
+  const uint16_t* Ag_k = (const uint16_t*)P.A_k + b * P.bs_A_k;
+  auto load_rows = [&](int kc) {
+    const int col = min(lane * 8, KC - 8);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i)
-      if (tr[i] < 0) *(uint4*)(dst + (wave * RPW + i) * AROW + lane * 8) = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Ag_k + (long)max(tr[i], 0) * P.ld_A_k + kc + col),
+          (__attribute__((address_space(3))) void*)(Ak + (wave * 8 + i) * AROW), 16, 0, 0);
   };
-  auto load_rows = [&](const uint16_t* Ag, long ld, uint16_t* dst, int kc, int kw) {
-    const int col = min(lane * 8, kw - 8);
-#pragma unroll
-    for (int i = 0; i < RPW; ++i)
-      if (tr[i] >= 0)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Ag + (long)tr[i] * ld + kc + col),
-                                         (__attribute__((address_space(3))) void*)(dst + (wave * RPW + i) * AROW), 16, 0, 0);
-  };
-  // Value rows go to registers: lane l of wave w holds rank columns [8l, 8l+8) of rows
-  // 8w..8w+7 (absent rows read row 0 and are zeroed when used).  With exact values the
-  // lane holds value dims 2l, 2l + 1 of the same rows instead.
-  uint4 av[RPW];
-  uint32_t vx[RPW];
-  auto load_v = [&](int kc, int kw) {
+  auto load_vrows = [&](int kc) {
+    const uint16_t* src;
+    long ld;
     if constexpr (EXACT_V) {
-      const uint16_t* Vg = (const uint16_t*)P.V_full + b * P.bs_V + (long)h * 128 + 2 * lane;
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) vx[i] = *(const uint32_t*)(Vg + (long)max(tr[i], 0) * P.ld_V);
+      src = (const uint16_t*)P.V_full + b * P.bs_V + (long)h * 128;
+      ld = P.ld_V;
     } else {
-      const int col = min(lane * 8, kw - 8);
+      src = (const uint16_t*)P.A_v + b * P.bs_A_v + kc;
+      ld = P.ld_A_v;
+    }
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) av[i] = *(const uint4*)(Ag_v + (long)max(tr[i], 0) * P.ld_A_v + kc + col);
+    for (int i = 0; i < 8; ++i) {
+      const int p = 64 * min(i, lcv_ni - 1) + lane;   // unit within the wave's rows
+      const int rho = wave * 8 + (p >> lcv);
+      const int c = (p & ((1 << lcv) - 1)) ^ (2 * (rho & 3));
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src + (long)max(tv[i], 0) * ld + 8 * c),
+          (__attribute__((address_space(3))) void*)((unsigned char*)Vr + (wave * 8 << (lcv + 4)) +
+                                                     1024 * min(i, lcv_ni - 1)),
+          16, 0, 0);
     }
   };
-  zero_absent(Ak);
-  load_rows(Ag_k, P.ld_A_k, Ak, 0, min(KCH, r));
-  if (tid < grp * 64) {
-    const int j = tid >> 6, i = tid & 63;
-    float c, sn;
-    rope_cs_turns(P.q_pos, q_turns, &c, &sn);
-    const float x = bf16_bits_to_f32(qraw[0]), y = bf16_bits_to_f32(qraw[1]);
-    qs[j][i] = (x * c - y * sn) * P.scale;
-    qs[j][i + 64] = (y * c + x * sn) * P.scale;
+  load_rows(0);
+  if constexpr (!MULTI) load_vrows(0);   // several rank chunks: region V holds B_k stagings until the last
+
+  // While the rows stream in: rotate the query fragment at the query position, scale it
+  // and split it into bf16 hi + lo operands (zero for lanes past the group).
+  bf16x8_t qhi, qlo;
+  {
+    float qf[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float c, sn;
+      rope_cs_turns(P.q_pos, turns[v], &c, &sn);
+      const float x = bf16_bits_to_f32(qraw[v]), y = bf16_bits_to_f32(qraw[4 + v]);
+      const float keep = n < grp ? P.scale : 0.f;
+      qf[v] = (x * c - y * sn) * keep;
+      qf[4 + v] = (y * c + x * sn) * keep;
+    }
+    split_bf16x8(qf, qhi, qlo);
   }
 
-  f32x4_t acc[RBM / 16];
+  // ---- keys: K^T tiles over the rank chunks ----
+  f32x4_t acc[4][2];
 #pragma unroll
-  for (int rt = 0; rt < RBM / 16; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Rank chunks of KCH columns: the chunk's key rows and B slice (256 bytes per lane)
-  // are in flight when an iteration starts.  r is a multiple of 128, so a k-block past
-  // the chunk re-reads its last one (unused).
-  for (int kc = 0; kc < r; kc += KCH) {
-    const int kw = min(KCH, r - kc);
-    if (kc > 0) {
-      load_rows(Ag_k, P.ld_A_k, Ak, kc, kw);
-      load_b(kc, kw);
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // the direct-to-LDS loads have landed
-    __syncthreads();
-    if (kc == 0) load_v(0, kw);      // value rows stream in behind the key math
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int kb = 0; kb < KCH / 128; ++kb) {
-      if (kb * 128 < kw) {
+    for (int dt = 0; dt < 2; ++dt) acc[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // The staged rows' fragments are read one k-step ahead of the MFMAs that use them.
+  auto kphase = [&]() {
+    const uint16_t* abase = Ak + n * AROW + kh * (KC >> 1) + 8 * g;
+    uint4 an[4], ac[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+    for (int rt = 0; rt < 4; ++rt) an[rt] = *(const uint4*)(abase + rt * 16 * AROW);
 #pragma unroll
-          for (int rt = 0; rt < RBM / 16; ++rt) {
-            const bf16x8_t a = as_bf16x8(*(const uint4*)(Ak + (rt * 16 + n) * AROW + kb * 128 + 32 * g + 8 * i));
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bq[kb][i]), acc[rt], 0, 0, 0);
-          }
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < nks) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) ac[rt] = an[rt];
+        if (ks + 1 < nks) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) an[rt] = *(const uint4*)(abase + rt * 16 * AROW + 32 * (ks + 1));
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[rt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bq[0][ks]), as_bf16x8(ac[rt]), acc[rt][0], 0, 0, 0);
+          acc[rt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bq[1][ks]), as_bf16x8(ac[rt]), acc[rt][1], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
+  };
+  if constexpr (!MULTI) {
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): the A_k rows have landed (value rows may fly)
+    lds_sync();
+    kphase();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_sync();
+    kphase();
+    for (int kc = KC; kc < r; kc += KC) {
+      lds_sync();   // every wave is done with the previous chunk's rows
+      stage_b(kc);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      read_b();
+      lds_sync();   // the B_k staging has been read by every wave
+      load_rows(kc);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_sync();
+      kphase();
+    }
+    lds_sync();   // region V is free: the value rows of the first chunk
+    load_vrows(0);
+  }
+  lds_sync();   // every wave is done reading the A_k rows
+
+  // ---- the two rank halves meet: wave (dg, kh) takes row tiles 2 kh and 2 kh + 1 ----
+  // (tiles picked with selects on the wave-uniform kh, so that the accumulators stay in
+  // registers)
+  f32x4_t mine[2][2];
+  {
+    float4* X = (float4*)Ak;   // [sender wave][tile u][dt][lane], 32 KB
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const f32x4_t a = kh ? acc[u][dt] : acc[2 + u][dt];
+        mine[u][dt] = kh ? acc[2 + u][dt] : acc[u][dt];
+        X[((wave * 2 + u) * 2 + dt) * 64 + lane] = make_float4(a[0], a[1], a[2], a[3]);
+      }
+    lds_sync();
+    const int partner = wave ^ 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const float4 o = X[((partner * 2 + u) * 2 + dt) * 64 + lane];
+        mine[u][dt][0] += o.x;
+        mine[u][dt][1] += o.y;
+        mine[u][dt][2] += o.z;
+        mine[u][dt][3] += o.w;
+      }
   }
 
-  // RoPE in registers (the pair partner is 8 lanes away), rotated keys to LDS.
-  {
-    const bool lo_half = n < 8;
-    const double turns = P.turns[8 * wave + (n & 7)];
+  // ---- RoPE on the keys of this wave's tiles, then partial scores on the MFMA ----
+  // Lane (n, g) holds row rt*16 + n (rt = 2 kh + u), dims i = 16 dg + 4 g + v
+  // (mine[u][0][v]) and i + 64 (mine[u][1][v]).  Behind the exchange in region A:
+  // sp[dg][j][row] (partial scores), pw[j][row] (weights), the statistics.  The score
+  // stores are unconditional (heads past the group land in unused slots), which keeps
+  // them free of waits for the value rows in flight.
+  float* sp = (float*)Ak + 8192;      // [4 dim groups][16 heads][64 rows] (heads past the group unused)
+  float* pw = sp + 4 * 16 * RBM;
+  float* st_m = pw + MAXG * RBM;
+  float* st_l = st_m + MAXG;
 #pragma unroll
-    for (int rt = 0; rt < RBM / 16; ++rt)
+  for (int u = 0; u < 2; ++u) {
+    const int rt = 2 * kh + u;
+    const int t = max(rows_t[rt * 16 + n], 0);   // absent rows: angle 0, masked below
+    float kf[8];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rt * 16 + 4 * g + v;
-        const int t = rows_t[row];
-        const float x = acc[rt][v];
-        const float u = __shfl_xor(x, 8);
-        float c, sn;   // absent rows (t < 0) rotate by angle 0; their scores are masked
-        rope_cs_turns(max(t, 0), turns, &c, &sn);
-        kh[row][dim] = lo_half ? x * c - u * sn : x * c + u * sn;
-      }
-  }
-  __syncthreads();
-  if (tid < grp * RBM) {
-    const int j = tid / RBM, row = tid % RBM;
-    float v = -INFINITY;
-    if (rows_t[row] >= 0) {
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < 128; i += 4) {
-        a0 += qs[j][i] * kh[row][i];
-        a1 += qs[j][i + 1] * kh[row][i + 1];
-        a2 += qs[j][i + 2] * kh[row][i + 2];
-        a3 += qs[j][i + 3] * kh[row][i + 3];
-      }
-      v = (a0 + a1) + (a2 + a3);
+    for (int v = 0; v < 4; ++v) {
+      float c, sn;
+      rope_cs_turns(t, turns[v], &c, &sn);
+      const float x = mine[u][0][v], y = mine[u][1][v];
+      kf[v] = x * c - y * sn;
+      kf[4 + v] = y * c + x * sn;
     }
-    pw[j][row] = v;
+    bf16x8_t khi, klo;
+    split_bf16x8(kf, khi, klo);
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, khi, sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, klo, sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo, khi, sc, 0, 0, 0);
+    // sc[v] = partial score of query head 4g + v for row rt*16 + n
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sp[(dg * 16 + 4 * g + v) * RBM + rt * 16 + n] = sc[v];   // unconditional
   }
-  __syncthreads();
+  lds_sync();   // partial scores visible
+
+  // ---- softmax of the summed scores (wave j < group size: query head j) ----
   if (wave < grp) {
-    const float v = pw[wave][lane];
+    float v = -INFINITY;
+    if (rows_t[lane] >= 0) v = ((sp[(0 * 16 + wave) * RBM + lane] + sp[(1 * 16 + wave) * RBM + lane]) +
+                                sp[(2 * 16 + wave) * RBM + lane]) + sp[(3 * 16 + wave) * RBM + lane];
     const float mx = wave_max(v);
     const float p = (v == -INFINITY) ? 0.f : __expf(v - mx);
     const float l = wave_sum(p);
-    pw[wave][lane] = p;
+    // absent rows: weight 0 (their value rows hold row 0's values)
+    pw[wave * RBM + lane] = p;
     if (lane == 0) {
       st_m[wave] = mx;
       st_l[wave] = l;
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's value rows have landed
+  lds_sync();
 
-  if constexpr (EXACT_V) {
-    // Exact values: wave w sums its rows 8w..8w+7 for dims 2l, 2l + 1 (lane l); the eight
-    // wave sums meet in LDS (over the staged key rows, no longer read), added in wave order.
-    float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + 128);
-    float* red = (float*)smem;   // [8 waves][grp][128]
-    float o0[MAXG], o1[MAXG];
+  // ---- weighted value sum: O[j][col] = sum_row P[j][row] V[row][col] ----
+  // A operand: P (head j = n, rows 32 ks + 8 g .. + 8), hi + lo; B operand: value rows
+  // 32 ks + 8 g .. + 8 at column col0 + n, two transposing reads of 4 rows each.
+  bf16x8_t phi[2], plo[2];
 #pragma unroll
-    for (int j = 0; j < MAXG; ++j) o0[j] = o1[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int row = wave * RPW + i;
-      const uint32_t w = tr[i] >= 0 ? vx[i] : 0u;
-      const float a0 = __uint_as_float(w << 16), a1 = __uint_as_float(w & 0xffff0000u);
-#pragma unroll
-      for (int j = 0; j < MAXG; ++j) {
-        const float p = pw[j][row];
-        o0[j] += p * a0;
-        o1[j] += p * a1;
+  for (int ks = 0; ks < 2; ++ks) {
+    float pf[8];
+    const float4 p0 = *(const float4*)&pw[jq * RBM + 32 * ks + 8 * g];
+    const float4 p1 = *(const float4*)&pw[jq * RBM + 32 * ks + 8 * g + 4];
+    const float keep = n < grp ? 1.f : 0.f;
+    pf[0] = p0.x * keep; pf[1] = p0.y * keep; pf[2] = p0.z * keep; pf[3] = p0.w * keep;
+    pf[4] = p1.x * keep; pf[5] = p1.y * keep; pf[6] = p1.z * keep; pf[7] = p1.w * keep;
+    split_bf16x8(pf, phi[ks], plo[ks]);
+  }
+  float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + Wtot);
+  const int cw = W >> 3;   // columns per wave, a multiple of 16
+  for (int kc = 0; kc < Wtot; kc += W) {
+    if constexpr (MULTI) {
+      if (kc > 0) {   // a further rank chunk of A_v (ranks above the first chunk)
+        lds_sync();   // the previous chunk's value rows are read
+        load_vrows(kc);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_sync();
       }
     }
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < MAXG; ++j)
-      if (j < grp) *(float2*)&red[(wave * grp + j) * 128 + 2 * lane] = make_float2(o0[j], o1[j]);
-    __syncthreads();
-    for (int e = tid; e < grp * 128; e += 512) {
-      const int j = e >> 7, c = e & 127;
-      float v = 0.f;
+    for (int ct = 0; ct < 4; ++ct) {
+      if (16 * ct < cw) {
+        const int col0 = wave * cw + 16 * ct;
+        f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w8 = 0; w8 < 8; ++w8) v += red[(w8 * grp + j) * 128 + c];
-      part[2 * grp + e] = v;
-    }
-    if (tid < grp) {
-      part[tid] = st_m[tid];
-      part[grp + tid] = st_l[tid];
-    }
-    return;
-  } else {
-    // Values stay in rank space: the partial holds sum_t p_t A_v[t] per query head; the
-    // merge multiplies the combined sum by B_v once.  Wave w sums its rows 8w..8w+7 for
-    // rank columns [8l, 8l+8) (lane l, from registers), reading each weight once per wave;
-    // the eight wave sums meet in LDS (over the staged key rows, no longer read) and are
-    // added in wave order.
-    float* part = P.part + (bh * P.n_splits + s) * (long)grp * (2 + r);
-    float* red = (float*)smem;   // [8 waves][grp][KCH]
-    for (int kc = 0; kc < r; kc += KCH) {
-      const int kw = min(KCH, r - kc);
-      if (kc > 0) {
-        __syncthreads();   // the previous chunk's wave sums have been read
-        load_v(kc, kw);
-      }
-      float o[MAXG][8];
-#pragma unroll
-      for (int j = 0; j < MAXG; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int row = wave * RPW + i;
-        const uint4 w4 = tr[i] >= 0 ? av[i] : make_uint4(0, 0, 0, 0);
-        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-        float a[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[2 * e] = __uint_as_float(w[e] << 16);
-          a[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        for (int ks = 0; ks < 2; ++ks) {
+          // lane (n, g) reads row rho = 32 ks + 8 g + (n >> 2) (and rho + 4), columns
+          // col0 + 4 (n & 3) .. + 4: chunk cc, half n & 1
+          const int rho = 32 * ks + 8 * g + (n >> 2);
+          const int cc = (col0 >> 3) + ((n & 3) >> 1);
+          const unsigned char* src =
+              (const unsigned char*)Vr + ((rho << lcv) + (cc ^ (2 * (rho & 3)))) * 16 + 8 * (n & 1);
+          union {
+            v4s hv[2];
+            bf16x8_t bv;
+          } u;
+          u.hv[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)src);
+          u.hv[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(src + (4 << (lcv + 4))));
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[ks], u.bv, o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], u.bv, o, 0, 0, 0);
         }
-        // All MAXG weight rows are read (rows past grp hold unused values), so that no
-        // LDS read waits behind a branch.
+        // o[v] = O[4g + v][col0 + n]
 #pragma unroll
-        for (int j = 0; j < MAXG; ++j) {
-          const float p = pw[j][row];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[j][e] += p * a[e];
-        }
-      }
-      __syncthreads();
-      if (lane * 8 < kw) {
-#pragma unroll
-        for (int j = 0; j < MAXG; ++j)
-          if (j < grp) {
-            float* dst = red + (wave * grp + j) * KCH + lane * 8;
-            *(float4*)dst = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
-            *(float4*)(dst + 4) = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
-          }
-      }
-      __syncthreads();
-      for (int e = tid; e < grp * kw; e += 512) {
-        const int j = e / kw, cc = e % kw;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) v += red[(w * grp + j) * KCH + cc];
-        part[2 * grp + (long)j * r + kc + cc] = v;
+        for (int v = 0; v < 4; ++v)
+          if (4 * g + v < grp) part[2 * grp + (long)(4 * g + v) * Wtot + kc + col0 + n] = o[v];
       }
     }
-    if (tid < grp) {
-      part[tid] = st_m[tid];
-      part[grp + tid] = st_l[tid];
-    }
+  }
+  if (tid < grp) {
+    part[tid] = st_m[tid];
+    part[grp + tid] = st_l[tid];
   }
 }
 
@@ -1362,18 +1472,19 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEven
   }
   dim3 grid(P.Hkv, P.n_splits, P.batch);
   if (P.mfma) {
-    // staged key rows, later reused for the eight waves' value sums
-    const size_t lds = std::max((size_t)RBM * AROW * sizeof(uint16_t), (size_t)8 * P.grp * KCH * sizeof(float));
     // The timing events, when given, are stamped by the dispatch itself at the
     // kernel's start and end.
+    const bool multi = (P.r_k & 511) ? P.r_k > ((P.r_k & 255) ? 128 : 256) : P.r_k > 512;
     if (P.exact_v) {
-      hipError_t e = set_lds<5>(sr_attend_mfma_kernel<true>, lds);
-      if (e != hipSuccess) return e;
-      hipExtLaunchKernelGGL(sr_attend_mfma_kernel<true>, grid, dim3(512), (uint32_t)lds, st, ev_start, ev_stop, 0, P);
+      if (multi)
+        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<true, true>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
+      else
+        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<true, false>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
     } else {
-      hipError_t e = set_lds<4>(sr_attend_mfma_kernel<false>, lds);
-      if (e != hipSuccess) return e;
-      hipExtLaunchKernelGGL(sr_attend_mfma_kernel<false>, grid, dim3(512), (uint32_t)lds, st, ev_start, ev_stop, 0, P);
+      if (multi)
+        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<false, true>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
+      else
+        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<false, false>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
     }
   } else {
     hipError_t e;

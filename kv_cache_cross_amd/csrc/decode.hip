@@ -38,7 +38,7 @@
 // sr_attend_generic_kernel covers every other shape (float32, other head
 // dims, exact values, ranks that differ) with value-space partials.
 // sr_merge_kernel (grid: query heads x batch) and, for the matrix-core path,
-//   sr_merge_rank_kernel (grid: KV heads x query heads per group x batch) merge
+//   sr_merge_rank_kernel (grid: KV heads x query heads per group x 4 dim slices x batch) merge
 //   the split partials and the exact-row partials by their log-sum-exp weights
 //   into the output; the latter applies B_v,l,h to the merged rank-r sum.
 #include <hip/hip_ext.h>
@@ -1264,22 +1264,30 @@ __global__ __launch_bounds__(256) void sr_merge_kernel(SrParams P) {
 // of denominators.  The headers, the first 32 split partials of the thread's two rank
 // columns and the first 512 rank columns of the wave's 32 rows of B_v are all in flight
 // before anything waits.
+// Grid: KV heads x (query heads per group x MQ dim slices) x batch.  Block (h, j, q)
+// merges query head j's partials into the rank-space sum and writes output dims
+// [q d/MQ, (q + 1) d/MQ): more, smaller blocks than one per query head, so that the
+// partial and B_v reads of a layer spread over MQ times more compute units.
+constexpr int MQ = 4;
 __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   __shared__ float wq[MAXP_RANK];
   __shared__ float lq[MAXP_RANK];
   __shared__ float run_l;
   __shared__ __align__(16) float orank[MAX_RANK_MFMA];
-  __shared__ float oval[MAXD];
-  __shared__ float red[4][32][65];
-  const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  __shared__ float oval[MAXD / MQ];
+  const int h = blockIdx.x, j = blockIdx.y / MQ, dq = blockIdx.y % MQ, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = P.grp, d = P.d, r = P.r_v;
+  const int dd = d / MQ;           // output dims of this block
   const int ns = P.n_splits, np = ns + P.n_exact;
   const long bh = (long)b * P.Hkv + h;
   const long sstride = (long)grp * (2 + r), estride = (long)grp * (2 + d);
   const float* p0 = P.part + bh * ns * sstride + 2 * grp + (long)j * r;   // split q: p0[q * sstride + c]
   const float* pex = P.part_ex + bh * P.n_exact * estride;
-  const uint16_t* Bt = (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)(h * d + wave * 32) * P.ld_Bt_v;
+  // Wave w takes output dims dq*dd + w*dd/4 + u (u < dd/4 <= 8), lane l rank columns
+  // [8l, 8l + 8) of every 512.
+  const int dw = dd / 4;
+  const uint16_t* Bt = (const uint16_t*)P.Bt_v + b * P.bs_Bt_v + (long)(h * d + dq * dd + wave * dw) * P.ld_Bt_v;
 
   constexpr int HU = (MAXP_RANK + 255) / 256;
   float hw[HU], hl[HU];
@@ -1297,16 +1305,17 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   float2 pv[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) pv[u] = *(const float2*)(p0 + (long)max(0, min(u, ns - 1)) * sstride + c0);
-  // The exact-row tiles' weighted value sums of output dim tid (up to 4 tiles in flight).
+  // The exact-row tiles' weighted value sums of this block's output dim tid (up to 4
+  // tiles in flight).
   constexpr int PE = 4;
   float ev[PE];
 #pragma unroll
   for (int e = 0; e < PE; ++e)
-    ev[e] = (tid < d && e < P.n_exact) ? pex[e * estride + 2 * grp + (long)j * d + tid] : 0.f;
-  uint4 bw[32];
+    ev[e] = (tid < dd && e < P.n_exact) ? pex[e * estride + 2 * grp + (long)j * d + dq * dd + tid] : 0.f;
+  uint4 bw[8];
   const int cb = min(lane * 8, r - 8);
 #pragma unroll
-  for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + cb);
+  for (int u = 0; u < 8; ++u) bw[u] = *(const uint4*)(Bt + (long)min(u, dw - 1) * P.ld_Bt_v + cb);
 #pragma unroll
   for (int u = 0; u < HU; ++u) {
     const int q = tid + 256 * u;
@@ -1330,7 +1339,8 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
     if (lane == 0) run_l = L;
   }
   __syncthreads();
-  // Combined rank-space sum of columns c0, c0 + 1 (and, for r > 512, further pairs).
+  // Combined rank-space sum of columns c0, c0 + 1 (and, for r > 512, further pairs),
+  // the splits added in order.
   {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -1359,31 +1369,30 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
     orank[c] = a0;
     orank[c + 1] = a1;
   }
-  if (tid < d) {
+  if (tid < dd) {
     float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < PE; ++e)
       if (e < P.n_exact) acc += wq[ns + e] * ev[e];
-    for (int e = PE; e < P.n_exact; ++e) acc += wq[ns + e] * pex[e * estride + 2 * grp + (long)j * d + tid];
+    for (int e = PE; e < P.n_exact; ++e) acc += wq[ns + e] * pex[e * estride + 2 * grp + (long)j * d + dq * dd + tid];
     oval[tid] = acc;
   }
   __syncthreads();
-  // out[i] = orank . Bt_v[h*128 + i] + oval[i]: wave w takes rows [32w, 32w + 32), lane l
-  // rank columns [8l, 8l + 8) of every 512; the 64 lane partials of each row are summed
-  // through LDS.
-  float acc[32];
+  // out[i] = orank . Bt_v[h*d + i] + oval[i]: each lane's partial over its rank columns,
+  // then a wave-wide sum per output dim.
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < 32; ++u) acc[u] = 0.f;
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   for (int c = lane * 8; c < r; c += 512) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = orank[c + e];
     if (c >= 512) {
 #pragma unroll
-      for (int u = 0; u < 32; ++u) bw[u] = *(const uint4*)(Bt + (long)u * P.ld_Bt_v + c);
+      for (int u = 0; u < 8; ++u) bw[u] = *(const uint4*)(Bt + (long)min(u, dw - 1) * P.ld_Bt_v + c);
     }
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const uint32_t w[4] = {bw[u].x, bw[u].y, bw[u].z, bw[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1392,17 +1401,15 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
       }
     }
   }
+  // lanes past r (r < 512) hold partials of re-read columns: left out of the sum
+  const bool live = lane * 8 < r;
 #pragma unroll
-  for (int u = 0; u < 32; ++u) red[wave][u][lane] = acc[u];
-  __syncthreads();
-  {
-    const int u = lane >> 1, hf = lane & 1;
-    float sum = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) sum += red[wave][u][hf * 32 + k];
-    sum += __shfl_xor(sum, 1);
-    const int i = wave * 32 + u;
-    if (hf == 0) P.out[((long)b * P.Hq + (long)h * grp + j) * d + i] = (sum + oval[i]) / run_l;
+  for (int u = 0; u < 8; ++u) {
+    const float sum = wave_sum(live ? acc[u] : 0.f);
+    if (u < dw && lane == 0) {
+      const int i = wave * dw + u;
+      P.out[((long)b * P.Hq + (long)h * grp + j) * d + dq * dd + i] = (sum + oval[i]) / run_l;
+    }
   }
 }
 
@@ -1500,7 +1507,7 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEven
 
 hipError_t launch_sr_merge(const SrParams& P, hipStream_t st) {
   if (P.mfma && !P.exact_v)
-    hipLaunchKernelGGL(sr_merge_rank_kernel, dim3(P.Hkv, P.grp, P.batch), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(sr_merge_rank_kernel, dim3(P.Hkv, P.grp * MQ, P.batch), dim3(256), 0, st, P);
   else
     hipLaunchKernelGGL(sr_merge_kernel, dim3(P.Hq, P.batch), dim3(256), 0, st, P);
   return hipGetLastError();

@@ -3,7 +3,7 @@
 // section 3.2).  Four kernels, ordered by the stream (no device-scope fences
 // inside any of them: on this GPU such a fence writes back the XCD's L2):
 //
-// sr_score_kernel (grid: score_blocks x KV heads x batch)
+// sr_score_kernel (grid: KV heads x score_blocks x batch)
 //   * block (0, 0, b) appends the new token's pre-RoPE k, v to the exact tail;
 //   * every block forms the scaled, rotated query sum of the KV head's query
 //     group and scores a slice of the candidate chunks against the landmarks
@@ -580,7 +580,7 @@ template <typename ST>
 __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
   __shared__ float qs[MAXG][MAXD];
   __shared__ float qsum[MAXD];
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int h = blockIdx.x, blk = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
 
   if (blk == 0 && h == 0 && P.k_new != nullptr && P.n_gen > 0) {
     const long row = P.n_sink + P.n_local + P.n_gen - 1;
@@ -1436,8 +1436,11 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 }  // namespace
 
+// KV head fastest in the grid: consecutive blocks go to different XCDs, so with 8 KV
+// heads one head's score blocks share an XCD, and the top-k block of the head (block id
+// h of its launch) finds the scores in that XCD's L2.
 hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st) {
-  dim3 grid(P.score_blocks, P.Hkv, P.batch);
+  dim3 grid(P.Hkv, P.score_blocks, P.batch);
   if (bf16)
     hipLaunchKernelGGL(sr_score_kernel<uint16_t>, grid, dim3(256), 0, st, P);
   else

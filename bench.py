@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # what the same counter reads for a 1 GiB device-to-device copy (read 524300.5 KiB, written
 # 1048576 KiB).  It stands only while the decode kernels' source is the one measured: the
 # source's SHA-256 prefix is recorded and `traffic` is null when it differs.
-ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "a33038fd2cc3c4a7", "fetch_kib": 17013.2, "write_kib": 2056.0,
+ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "76d179dd147a23e9", "fetch_kib": 17002.7, "write_kib": 2056.0,
                   "fetch_scale": 1048576.0 / 524300.5, "write_scale": 1.0}
 # The same for one launch of the Gram kernel over the 16 group sides of the 64k workload
 # (3 dispatches).  FETCH_SIZE counts what the L2 caches request from the memory fabric,
@@ -382,7 +382,7 @@ def main():
         "compress_s": round(comp_s, 4),
         "compress_stats": {"err_est_max": float(max(st[0] for st in stats)), "sweeps": int(stats[0][2]),
                            "rounds": int(stats[0][3])},
-        "roofline": {"bound": "hbm", "kernel": "sr_attend_mfma_kernel<false>", "achieved": round(achieved_att, 1),
+        "roofline": {"bound": "hbm", "kernel": "sr_attend_mfma_kernel<false, false>", "achieved": round(achieved_att, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": int(algo_bytes_launch),

@@ -747,8 +747,8 @@ constexpr int QSLOT = 8 * VROW_MAX * 2;   // bytes of one wave's share of region
 //    three products); the four dim groups' partial scores of a row are added in LDS in
 //    a fixed order;
 //  * value rows (A_v rank chunk, or V_full dims with exact values) go to LDS with
-//    direct-to-LDS loads right behind the A_k rows, 16-byte chunks XOR-swizzled by row
-//    so that the transposing reads below are free of bank conflicts;
+//    direct-to-LDS loads once the A_k rows have landed, 16-byte chunks XOR-swizzled by
+//    row so that the transposing reads below are free of bank conflicts;
 //  * weighted value sum: P (query heads x 64 rows, hi + lo) times the 64 value rows on
 //    the MFMA, the value rows read from LDS with transposing reads; wave w owns columns
 //    [w W / 8, (w + 1) W / 8) of the W-wide sum, so no cross-wave reduction is needed.
@@ -888,7 +888,6 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     }
   };
   load_rows(0);
-  if constexpr (!MULTI) load_vrows(0);   // several rank chunks: region V holds B_k stagings until the last
 
   // While the rows stream in: rotate the query fragment at the query position, scale it
   // and split it into bf16 hi + lo operands (zero for lanes past the group).
@@ -937,8 +936,12 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     }
   };
   if constexpr (!MULTI) {
-    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): the A_k rows have landed (value rows may fly)
+    // The value rows go out once the A_k rows have landed: with both gathers in flight
+    // together the A_k rows land no earlier than the value rows; this way they have the
+    // memory system first, and the value rows land while the keys and scores are formed.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the A_k rows have landed
     lds_sync();
+    load_vrows(0);
     kphase();
   } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);

@@ -35,78 +35,193 @@ static void house(int m, const double* x, double* v, double* beta, double* mu) {
   *mu = nrm;
 }
 
-/* Reduce symmetric A (n x n, row-major, overwritten) to tridiagonal (d, e).
- * On return Qt holds Q^T, where A_in = Q T Q^T. */
+/* Reduce symmetric A (n x n, row-major, lower triangle used and overwritten) to
+ * tridiagonal (d, e).  On return Qt holds Q^T, where A_in = Q T Q^T.
+ *
+ * Step k takes the Householder vector v of column k below the diagonal and forms
+ * p = beta A22 v, w = p - (beta/2)(p.v) v; A22 <- A22 - v w^T - w v^T.  Only the lower
+ * triangle of A22 is kept, and the update of step k is fused with the product of
+ * step k + 1: once column k + 1 of the updated matrix is known (its Householder vector
+ * v' follows), one pass over the rest of the lower triangle updates each element and
+ * adds its contributions a_ij v'_j to p'_i and a_ij v'_i to p'_j. */
 static int tridiagonalize(int n, double* A, double* d, double* e, double* Qt) {
   double* V = (double*)calloc((size_t)n * n, sizeof(double));   /* reflector k in row k */
   double* beta = (double*)calloc((size_t)n, sizeof(double));
   double* p = (double*)malloc((size_t)n * sizeof(double));
   double* w = (double*)malloc((size_t)n * sizeof(double));
+  double* col = (double*)malloc((size_t)n * sizeof(double));
   double* Q = (double*)malloc((size_t)n * n * sizeof(double));
-  if (!V || !beta || !p || !w || !Q) {
-    free(V); free(beta); free(p); free(w); free(Q);
+  if (!V || !beta || !p || !w || !col || !Q) {
+    free(V); free(beta); free(p); free(w); free(col); free(Q);
     return -1;
   }
+  /* Step 0's product: p = A22 v over the (not yet updated) lower triangle. */
+  int have_p = 0;
   for (int k = 0; k + 2 < n; ++k) {
     const int m = n - k - 1;                 /* trailing size */
     double* v = V + (size_t)k * n;
     double mu;
-    /* Column k below the diagonal equals row k right of the diagonal (symmetry). */
-    house(m, A + (size_t)k * n + k + 1, v, &beta[k], &mu);
+    for (int i = 0; i < m; ++i) col[i] = A[(size_t)(k + 1 + i) * n + k];   /* column k below the diagonal */
+    house(m, col, v, &beta[k], &mu);
     d[k] = A[(size_t)k * n + k];
     e[k] = mu;
     const double b = beta[k];
-    if (b == 0.0) continue;
-    /* p = beta * A22 v */
-    for (int i = 0; i < m; ++i) {
-      const double* row = A + (size_t)(k + 1 + i) * n + k + 1;
-      double s = 0.0;
-      for (int j = 0; j < m; ++j) s += row[j] * v[j];
-      p[i] = b * s;
+    if (!have_p) {
+      /* p = A22 v from the lower triangle (rows k+1.., columns k+1..) */
+      for (int i = 0; i < m; ++i) p[i] = 0.0;
+      for (int i = 0; i < m; ++i) {
+        const double* row = A + (size_t)(k + 1 + i) * n + k + 1;
+        const double vi = v[i];
+        double s = 0.0;
+        for (int j = 0; j < i; ++j) {
+          s += row[j] * v[j];
+          p[j] += row[j] * vi;
+        }
+        p[i] += s + row[i] * vi;
+      }
     }
-    /* w = p - (beta/2)(p^T v) v */
+    have_p = 0;
+    if (b == 0.0) continue;
+    /* w = beta p - (beta/2)(beta p . v) v */
+    for (int i = 0; i < m; ++i) p[i] *= b;
     double pv = 0.0;
     for (int i = 0; i < m; ++i) pv += p[i] * v[i];
     const double half = 0.5 * b * pv;
     for (int i = 0; i < m; ++i) w[i] = p[i] - half * v[i];
-    /* A22 -= v w^T + w v^T */
-    for (int i = 0; i < m; ++i) {
-      double* row = A + (size_t)(k + 1 + i) * n + k + 1;
-      const double vi = v[i], wi = w[i];
-      for (int j = 0; j < m; ++j) row[j] -= vi * w[j] + wi * v[j];
+    if (k + 3 < n) {
+      /* Column k+1 of the updated matrix (local index 0 of A22), then the next
+       * Householder vector, then the fused update + product over local rows 1.. */
+      const int m2 = m - 1;
+      double* v2 = V + (size_t)(k + 1) * n;
+      for (int i = 0; i < m; ++i) {
+        double* a0 = A + (size_t)(k + 1 + i) * n + k + 1;
+        *a0 -= v[i] * w[0] + w[i] * v[0];
+      }
+      for (int i = 0; i < m2; ++i) col[i] = A[(size_t)(k + 2 + i) * n + k + 1];
+      double mu2;
+      house(m2, col, v2, &beta[k + 1], &mu2);
+      /* local rows/columns 1..m-1 of A22 are rows/columns 0..m2-1 of the next A22 */
+      for (int i = 0; i < m2; ++i) p[i] = 0.0;
+      for (int i = 0; i < m2; ++i) {
+        double* row = A + (size_t)(k + 2 + i) * n + k + 2;
+        const double vi = v[i + 1], wi = w[i + 1], ui = v2[i];
+        const double* vj = v + 1;
+        const double* wj = w + 1;
+        double s = 0.0;
+        for (int j = 0; j < i; ++j) {
+          const double a = row[j] - vi * wj[j] - wi * vj[j];
+          row[j] = a;
+          s += a * v2[j];
+          p[j] += a * ui;
+        }
+        const double a = row[i] - vi * wj[i] - wi * vj[i];
+        row[i] = a;
+        p[i] += s + a * ui;
+      }
+      have_p = 1;
+      /* the next step recomputes its column k+2.. from A (already updated above) and
+       * reuses v2 and beta[k + 1] through V and beta (house is deterministic) */
+    } else {
+      for (int i = 0; i < m; ++i) {
+        double* row = A + (size_t)(k + 1 + i) * n + k + 1;
+        const double vi = v[i], wi = w[i];
+        for (int j = 0; j <= i; ++j) row[j] -= vi * w[j] + wi * v[j];
+      }
     }
   }
   if (n >= 2) {
     d[n - 2] = A[(size_t)(n - 2) * n + n - 2];
-    e[n - 2] = A[(size_t)(n - 2) * n + n - 1];
+    e[n - 2] = A[(size_t)(n - 1) * n + n - 2];
   }
   d[n - 1] = A[(size_t)(n - 1) * n + n - 1];
 
-  /* Q = P_0 P_1 ... P_{n-3}, accumulated from the right end. */
+  /* Q = P_0 P_1 ... P_{n-3}, accumulated from the right end in blocks of NB reflectors:
+   * P_kb ... P_{kb+nb-1} = I - Y T Y^T (compact WY; Y holds the reflectors, T is upper
+   * triangular), applied as Q22 -= Y (T (Y^T Q22)) with Q22 = rows and columns kb+1...
+   * Columns are taken in panels of QC so that the nb x QC product stays in cache. */
   for (size_t i = 0; i < (size_t)n * n; ++i) Q[i] = 0.0;
   for (int i = 0; i < n; ++i) Q[(size_t)i * n + i] = 1.0;
-  for (int k = n - 3; k >= 0; --k) {
-    const int m = n - k - 1;
-    const double* v = V + (size_t)k * n;
-    const double b = beta[k];
-    if (b == 0.0) continue;
-    /* u = v^T Q22 ; Q22 -= beta v u^T */
-    for (int j = 0; j < m; ++j) w[j] = 0.0;
-    for (int i = 0; i < m; ++i) {
-      const double* row = Q + (size_t)(k + 1 + i) * n + k + 1;
-      const double vi = v[i];
-      for (int j = 0; j < m; ++j) w[j] += vi * row[j];
+  {
+    enum { NB = 32, QC = 128 };
+    double* Tm = (double*)malloc((size_t)NB * NB * sizeof(double));
+    double* Wp = (double*)malloc((size_t)NB * QC * sizeof(double));
+    double* Yt = (double*)malloc((size_t)NB * n * sizeof(double));   /* Y^T: reflector c in row c */
+    if (!Tm || !Wp || !Yt) {
+      free(Tm); free(Wp); free(Yt);
+      free(V); free(beta); free(p); free(w); free(col); free(Q);
+      return -1;
     }
-    for (int i = 0; i < m; ++i) {
-      double* row = Q + (size_t)(k + 1 + i) * n + k + 1;
-      const double f = b * v[i];
-      for (int j = 0; j < m; ++j) row[j] -= f * w[j];
+    const int nref = n - 2;   /* reflectors 0 .. n-3 */
+    for (int kb = ((nref - 1) / NB) * NB; kb >= 0; kb -= NB) {
+      const int nb = nref - kb < NB ? nref - kb : NB;
+      const int r0 = kb + 1, M = n - r0;
+      /* Yt[c][i] = component of reflector kb+c at row r0 + i (zero above its start) */
+      for (int c = 0; c < nb; ++c) {
+        double* y = Yt + (size_t)c * n;
+        const double* v = V + (size_t)(kb + c) * n;
+        for (int i = 0; i < M; ++i) y[i] = i < c ? 0.0 : v[i - c];
+      }
+      /* T: T[c][c] = beta_c, T[0:c, c] = -beta_c T[0:c, 0:c] (Y[:, 0:c]^T y_c) */
+      for (int c = 0; c < nb; ++c) {
+        const double bc = beta[kb + c];
+        const double* yc = Yt + (size_t)c * n;
+        for (int a = 0; a < c; ++a) {
+          const double* ya = Yt + (size_t)a * n;
+          double t = 0.0;
+          for (int i = c; i < M; ++i) t += ya[i] * yc[i];
+          w[a] = t;
+        }
+        for (int a = 0; a < c; ++a) {
+          double t = 0.0;
+          for (int b2 = a; b2 < c; ++b2) t += Tm[a * NB + b2] * w[b2];
+          Tm[a * NB + c] = -bc * t;
+        }
+        Tm[c * NB + c] = bc;
+        for (int a = c + 1; a < NB; ++a) Tm[a * NB + c] = 0.0;
+      }
+      for (int j0 = 0; j0 < M; j0 += QC) {
+        const int jw = M - j0 < QC ? M - j0 : QC;
+        /* Wp = Y^T Q22[:, j0:j0+jw] */
+        for (int c = 0; c < nb; ++c)
+          for (int j = 0; j < jw; ++j) Wp[c * QC + j] = 0.0;
+        for (int i = 0; i < M; ++i) {
+          const double* row = Q + (size_t)(r0 + i) * n + r0 + j0;
+          for (int c = 0; c < nb; ++c) {
+            const double yci = Yt[(size_t)c * n + i];
+            if (yci == 0.0) continue;
+            double* wc = Wp + c * QC;
+            for (int j = 0; j < jw; ++j) wc[j] += yci * row[j];
+          }
+        }
+        /* Wp = T Wp (upper triangular, in place, top row first) */
+        for (int a = 0; a < nb; ++a) {
+          double* wa = Wp + a * QC;
+          const double taa = Tm[a * NB + a];
+          for (int j = 0; j < jw; ++j) wa[j] *= taa;
+          for (int b2 = a + 1; b2 < nb; ++b2) {
+            const double tab = Tm[a * NB + b2];
+            const double* wb = Wp + b2 * QC;
+            for (int j = 0; j < jw; ++j) wa[j] += tab * wb[j];
+          }
+        }
+        /* Q22[:, j0:j0+jw] -= Y Wp */
+        for (int i = 0; i < M; ++i) {
+          double* row = Q + (size_t)(r0 + i) * n + r0 + j0;
+          for (int c = 0; c < nb; ++c) {
+            const double yci = Yt[(size_t)c * n + i];
+            if (yci == 0.0) continue;
+            const double* wc = Wp + c * QC;
+            for (int j = 0; j < jw; ++j) row[j] -= yci * wc[j];
+          }
+        }
+      }
     }
+    free(Tm); free(Wp); free(Yt);
   }
   for (int i = 0; i < n; ++i)
     for (int j = 0; j < n; ++j) Qt[(size_t)j * n + i] = Q[(size_t)i * n + j];
 
-  free(V); free(beta); free(p); free(w); free(Q);
+  free(V); free(beta); free(p); free(w); free(col); free(Q);
   return 0;
 }
 

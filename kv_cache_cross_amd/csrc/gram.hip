@@ -79,9 +79,16 @@ __global__ __launch_bounds__(512) void gram_bf16_kernel(GramArgs a) {
   // The four stages are separate arrays, each named by a constant at every use, so
   // that a load into one stage is known not to touch the stage being read.
   __shared__ __align__(16) unsigned char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
-  const int side = blockIdx.x / a.tiles_per_side;
+  // XCD-aware order: the dispatcher hands block b to XCD b % 8, so logical tile
+  // (b % 8) q + b / 8 gives each XCD a contiguous range of the row-major upper-triangle
+  // tile list (q = blocks / 8).  The tiles an XCD runs at once then share their row block
+  // and most column blocks, and its L2 serves the repeats: the L2-miss traffic of the
+  // 64k Gram halves (from 2 x 62.3 to about 2 x 35 GiB per launch).
+  const int nblk = gridDim.x, q8 = nblk / 8, b = blockIdx.x;
+  const int lt = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
+  const int side = lt / a.tiles_per_side;
   int I, J;
-  upper_tile(blockIdx.x % a.tiles_per_side, a.nt, &I, &J);
+  upper_tile(lt % a.tiles_per_side, a.nt, &I, &J);
   const bool diag = (I == J);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;   // wave tile: rows wm*128.., cols wn*64..

@@ -527,13 +527,24 @@ XKV_DEV void exact_tile(const SrParams& P, int b, int h, int e_blk, float* smem)
     }
   }
   __syncthreads();
-  for (int e = tid; e < ETR * half; e += TKT) {
-    const int r = e / half, i = e % half;
-    float c, sn;   // rows past the tail rotate by angle 0; their scores are masked
-    rope_cs_turns(max(pos_of(r0 + r), 0), P.turns[i], &c, &sn);
-    const float lo = kh[r][i], hi = kh[r][i + half];
-    kh[r][i] = lo * c - hi * sn;
-    kh[r][i + half] = hi * c + lo * sn;
+  {
+    // Pair i = tid % half of rows tid / half + u * TKT / half (TKT is a multiple of
+    // half, so every pass of a thread has the same frequency): the passes unrolled, so
+    // that their LDS reads and rotations overlap.
+    const int i = tid % half;
+    const double turns = P.turns[i];
+    constexpr int MAXPASS = ETR * (MAXD / 2) / TKT;
+#pragma unroll
+    for (int u = 0; u < MAXPASS; ++u) {
+      const int r = tid / half + u * (TKT / half);
+      if (r < ETR) {
+        float c, sn;   // rows past the tail rotate by angle 0; their scores are masked
+        rope_cs_turns(max(pos_of(r0 + r), 0), turns, &c, &sn);
+        const float lo = kh[r][i], hi = kh[r][i + half];
+        kh[r][i] = lo * c - hi * sn;
+        kh[r][i + half] = hi * c + lo * sn;
+      }
+    }
   }
   __syncthreads();
   if (tid < grp * ETR) {
@@ -569,10 +580,13 @@ XKV_DEV void exact_tile(const SrParams& P, int b, int h, int e_blk, float* smem)
   }
   if (tid < grp * d) {
     const int j = tid / d, i = tid % d;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < ETR; ++r) acc += pw[j][r] * vh[r][i];
-    part[2 * grp + tid] = acc;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains, added in a fixed order
+#pragma unroll
+    for (int r = 0; r < ETR; r += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += pw[j][r + u] * vh[r + u][i];
+    }
+    part[2 * grp + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
 }
 

@@ -260,6 +260,16 @@ def test_decode_exact_tail_crosses_tiles(ctx):
     _run_decode_case(ctx, wl, steps=4, layer=0, label="exact tail 127..130 rows")
 
 
+@pytest.mark.parametrize("rank,values", [(384, "compressed"), (1024, "compressed"), (384, "exact"),
+                                         (1024, "exact")])
+def test_decode_mini_bf16_several_rank_chunks(ctx, rank, values):
+    # Ranks past one rank chunk of the matrix-core attend kernel: 1024 = two chunks of
+    # 512 and 384 = three of 128, so the keys are rebuilt chunk by chunk (and with
+    # compressed values the rank-space value sums too); compressed and exact values.
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, rank=rank))
+    _run_decode_case(ctx, wl, steps=2, values=values, layer=2, label=f"mini bf16 r={rank} {values} values")
+
+
 @pytest.mark.parametrize("rank", [128, 96])
 def test_decode_mini_bf16_exact_values(ctx, rank):
     # xK-SR variant with GPU-resident exact values (r_v = 0): rank 128 takes the

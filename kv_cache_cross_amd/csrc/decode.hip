@@ -608,25 +608,52 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
     }
   }
 
-  // Landmarks of the first BATCH passes are requested before the queries are formed, so
-  // their latency overlaps the query rotation.  Past-the-end slots re-read the block's
-  // last chunk (in bounds) and are not stored.
   const int per_blk = (P.n_cand + P.score_blocks - 1) / P.score_blocks;
   const int c0 = blk * per_blk, c1 = min(P.n_cand, c0 + per_blk);
   if (c0 >= c1) return;
+  // The raw queries and their RoPE frequencies are requested first, then the landmarks
+  // of the first BATCH passes: the queries arrive first (loads return in order), and
+  // their rotation and sum proceed while the landmarks are in flight.  Thread t takes
+  // (head, pair) = (e / half, e % half) for e = t and t + 256.
+  const int half = P.d >> 1;
+  const ST* qg = (const ST*)P.q + ((long)b * P.Hq + (long)h * P.grp) * P.d;
+  float qx[2] = {0.f, 0.f}, qy[2] = {0.f, 0.f};
+  double qt[2] = {0.0, 0.0};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;
+    if (e < P.grp * half) {
+      const int j = e / half, i = e % half;
+      qx[u] = ld_elem(qg + j * P.d + i);
+      qy[u] = ld_elem(qg + j * P.d + i + half);
+      qt[u] = P.turns[i];
+    }
+  }
+  // Past-the-end slots re-read the block's last chunk (in bounds) and are not stored.
   const int lpc = P.d >> 3;           // lanes per chunk, 8 elements each
   const int cpi = 256 / lpc;          // chunks per pass
   const int sub = tid % lpc, slot = tid / lpc;
   const ST* lm = (const ST*)P.lm + b * P.bs_lm + (long)h * P.n_chunks * P.d + sub * 8;
   float* scores = P.scores + ((long)b * P.Hkv + h) * P.n_cand;
   const int iters = (c1 - c0 + cpi - 1) / cpi;
-  constexpr int BATCH = 16;
+  constexpr int BATCH = 8;
   Raw8<ST> raw[BATCH];
+  // unconditional (slots past the block re-read its last chunk), so that the wait for the
+  // queries above is an exact count of the loads behind them
 #pragma unroll
-  for (int u = 0; u < BATCH; ++u)
-    if (u < iters) raw[u].load(lm + (long)min(c0 + u * cpi + slot, c1 - 1) * P.d);
+  for (int u = 0; u < BATCH; ++u) raw[u].load(lm + (long)min(c0 + u * cpi + slot, c1 - 1) * P.d);
 
-  load_group_queries<ST>(P, b, h, qs);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;
+    if (e < P.grp * half) {
+      const int j = e / half, i = e % half;
+      float c, sn;
+      rope_cs_turns(P.q_pos, qt[u], &c, &sn);
+      qs[j][i] = (qx[u] * c - qy[u] * sn) * P.scale;
+      qs[j][i + half] = (qy[u] * c + qx[u] * sn) * P.scale;
+    }
+  }
   __syncthreads();
   for (int i = tid; i < P.d; i += 256) {
     float s = 0.f;

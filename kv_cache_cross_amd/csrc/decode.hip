@@ -139,7 +139,8 @@ XKV_DEV uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Inclusive prefix sum over the TKT threads of a block (`tmp` >= TKW ints).
+// Inclusive prefix sum over the TKT threads of a block (`tmp` >= TKW ints).  No barrier
+// after the reads of tmp: the caller passes one before tmp is written again.
 XKV_DEV int tk_scan_incl(int v, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_scan_add(v);
@@ -147,11 +148,11 @@ XKV_DEV int tk_scan_incl(int v, int* tmp) {
   __syncthreads();
   int add = 0;
   for (int w = 0; w < wave; ++w) add += tmp[w];
-  __syncthreads();
   return v + add;
 }
 
-// Block-wide minimum of lo and maximum of hi (`tmp` >= 2 * TKW ints).
+// Block-wide minimum of lo and maximum of hi (`tmp` >= 2 * TKW ints).  As above, the
+// caller passes a barrier before tmp is written again.
 XKV_DEV void tk_minmax(uint32_t& lo, uint32_t& hi, uint32_t* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   lo = wave_min_u32(lo);
@@ -168,7 +169,6 @@ XKV_DEV void tk_minmax(uint32_t& lo, uint32_t& hi, uint32_t* tmp) {
     lo = min(lo, tmp[w]);
     hi = max(hi, tmp[TKW + w]);
   }
-  __syncthreads();
 }
 
 // Value of an order-preserving key (inverse of order_key, -0.0 read as +0.0).
@@ -189,7 +189,9 @@ constexpr int NBK = 2048;   // linear value buckets of the first top-k pass
 // keys one wave ranks them directly; otherwise an MSB-first radix select with 8-bit
 // digits, starting below the bits that b*'s keys share, resolves the k-th key exactly,
 // stopping as soon as the bin holding it is taken whole.  Non-finite extremes put every key in one bucket and leave the radix
-// select to do all the work.  `hist` holds NBK ints, `tmp` 2 * TKW, `bcast` 3.
+// select to do all the work.  `hist` holds NBK ints, `tmp` 2 * TKW, `bcast` 4.  The
+// block's barriers are the ones the data hand-offs need (seven on the usual path); the
+// function ends without one, so a caller that reuses the buffers passes a barrier first.
 template <int KPT>
 XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* hist, int* tmp, int* bcast) {
   const int tid = threadIdx.x;
@@ -199,6 +201,8 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     for (int i = tid; i < k; i += TKT) out[i] = (i < n) ? i : -1;
     return;
   }
+  for (int i = tid; i < NBK; i += TKT) hist[i] = 0;   // made visible by tk_minmax's barrier
+  if (tid == 0) bcast[3] = 0;                           // gather count of the few-keys path
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
@@ -219,8 +223,6 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     bk[u] = (base + u >= n) ? -1 : (inv == 0.f) ? 0 : (int)fminf((key_value(kr[u]) - fmin) * inv, (float)(NBK - 1));
 
   // Pass 1: bucket histogram, then the bucket b* holding the k-th largest key.
-  for (int i = tid; i < NBK; i += TKT) hist[i] = 0;
-  __syncthreads();
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
     if (bk[u] >= 0) atomicAdd(&hist[bk[u]], 1);
@@ -247,10 +249,10 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     }
   }
   __syncthreads();
+  // hist, tmp and bcast[0..2] are rewritten only after at least one more barrier
   const int bstar = bcast[0];
   int remaining = k - bcast[1];   // keys still to take from b*, 1..|b*|
   const int m_b = bcast[2];
-  __syncthreads();
 
   // Few keys in b* (the usual case): gather them, let one wave rank them by (key
   // descending, id ascending) and take the remaining-th as an exact threshold; every
@@ -261,9 +263,7 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     if (remaining < m_b) {
       uint32_t* lkey = (uint32_t*)hist;   // the bucket histogram is no longer needed
       int* lid = hist + 64;
-      int* lcount = hist + 128;
-      if (tid == 0) *lcount = 0;
-      __syncthreads();
+      int* lcount = bcast + 3;            // zeroed before the first barrier
 #pragma unroll
       for (int u = 0; u < KPT; ++u)
         if (bk[u] == bstar) {
@@ -338,11 +338,11 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
       mask |= dmask << shift;
       remaining = bcast[1];
       const bool whole = bcast[1] == bcast[2];   // the k-th key's bin is taken entirely
-      __syncthreads();
       bit = shift;
       if (whole) break;
     }
   }
+  __syncthreads();   // the reads of tmp and bcast above are done
   // Keys of higher buckets and keys of b* above the threshold prefix, then the first
   // `remaining` keys of b* equal to it in id order.
   uint32_t gtm = 0u, eqm = 0u;
@@ -360,7 +360,7 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     eqm &= eqm - 1u;
   }
   const int mine = __popc(sel);
-  int pos = tk_scan_incl(mine, tmp) - mine;
+  int pos = tk_scan_incl(mine, tmp + TKW) - mine;   // the other half: tmp may still be read
   while (sel) {
     out[pos++] = base + __ffs(sel) - 1;
     sel &= sel - 1u;

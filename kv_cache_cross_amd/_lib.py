@@ -247,10 +247,11 @@ def sr_args_array(args_list):
 
 def sr_decode_layers(ctx, arr, ws, stream=None, attend_events=None):
     """One decode step through len(arr) layers; arr from sr_args_array.  attend_events: optional
-    list of 2*len(arr) torch.cuda.Event (enable_timing=True), recorded around each attend kernel."""
+    list of 2*len(arr) torch.cuda.Event (enable_timing=True) or None, stamped at the start and end
+    of each layer's attend kernel (a layer whose pair is None is not timed)."""
     ev = None
     if attend_events is not None:
-        ev = (C.c_void_p * len(attend_events))(*[e.cuda_event for e in attend_events])
+        ev = (C.c_void_p * len(attend_events))(*[None if e is None else e.cuda_event for e in attend_events])
     _check(lib().xkv_sr_decode_layers(ctx.handle, len(arr), arr, _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream), ev))
 

@@ -821,9 +821,16 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   const int lcv = EXACT_V ? 4 : lcr + 1;
   const int Wtot = EXACT_V ? 128 : r;
 
-  // ---- prologue: every load that does not wait on the selection is issued first ----
+  // ---- prologue ----
+  // The single-chunk path: lane l of wave w reads the id of row 8w + (l & 7) itself
+  // (unconditionally, clamped to a valid entry), so that no barrier stands between the
+  // ids and the wave's A_k gathers.  The multi-chunk path reads them for the block.
   int csel = -1;
-  if (tid < RBM) {
+  if constexpr (!MULTI) {
+    const int ci = s * P.cps + (wave * 8 + (lane & 7)) / P.chunk;
+    csel = P.sel[bh * P.top_k + min(ci, P.k_eff - 1)];
+    if (ci >= P.k_eff) csel = -1;
+  } else if (tid < RBM) {
     const int ci = s * P.cps + tid / P.chunk;
     if (ci < P.k_eff) csel = P.sel[bh * P.top_k + ci];
   }
@@ -840,7 +847,9 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     turns[v] = P.turns[16 * dg + 4 * g + v];
   }
   // B_k staging: half-rows (dims 16 dg + 64 dt + m, ranks kc + kh KC/2 + [0, KC/2)) of
-  // this wave, dt = 0 into its slot of region V, dt = 1 into its slot of region A.
+  // this wave.  Multi-chunk: dt = 0 into its slot of region V, dt = 1 into its slot of
+  // region A, together.  Single chunk: both into the region V slot in turn, so that region
+  // A takes the A_k rows while the staging is under way.
   // 16-byte unit p of a slot holds row m = p >> lcr, chunk c = (p & (2^lcr - 1)) ^ (m & 7).
   const uint16_t* bk = (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)(h * 128 + 16 * dg) * P.ld_Bt_k;
   // One half-row set (dt) into one slot; called with each slot's own array so that every
@@ -875,14 +884,39 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     read_half((const unsigned char*)Vr + wave * QSLOT, 0);
     read_half((const unsigned char*)Ak + wave * 8192, 1);
   };
-  stage_b(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B_k slice has landed
-  read_b();
-  if (tid < RBM) {
-    const int t = csel * P.chunk + tid % P.chunk;
-    rows_t[tid] = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
+  const int lcv_ni = 1 << (lcv - 3);   // 1 KB instructions for a wave's 8 value rows
+  int tr[8], tv[8];   // A_k row of instruction i; value row of this lane in value instruction i
+  unsigned char* const vslot = (unsigned char*)Vr + wave * QSLOT;
+  if constexpr (!MULTI) {
+    // Half the B_k staging (dt = 0) lands with the row ids; then the A_k gathers and the
+    // other half (into the same slot) are in flight together.
+    stage_half(vslot, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): ids, query and dt = 0 half have landed
+    read_half(vslot, 0);
+    const int rl = wave * 8 + (lane & 7);
+    const int t = csel * P.chunk + rl % P.chunk;
+    const int trow = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
+    if (lane < 8) rows_t[rl] = trow;   // visible to the block after the barrier below
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tr[i] = __builtin_amdgcn_readlane(trow, i);
+      tv[i] = __builtin_amdgcn_ds_bpermute(((64 * min(i, lcv_ni - 1) + lane) >> lcv) << 2, trow);
+    }
+  } else {
+    stage_b(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B_k slice has landed
+    read_b();
+    if (tid < RBM) {
+      const int t = csel * P.chunk + tid % P.chunk;
+      rows_t[tid] = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
+    }
+    lds_sync();   // the row ids are visible and every wave has read its B_k staging
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tr[i] = rows_t[wave * 8 + i];
+      tv[i] = rows_t[wave * 8 + ((64 * min(i, lcv_ni - 1) + lane) >> lcv)];
+    }
   }
-  lds_sync();   // the row ids are visible and every wave has read its B_k staging
 
   // Wave w gathers rows 8w .. 8w+7.  A_k rows: one row per instruction, lane l bytes
   // [16l, 16l + 16) (lanes past a narrow chunk re-read its last 16 bytes into columns
@@ -890,13 +924,6 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   // rho 2^lcv + (c ^ 2 (rho & 3)), one 1 KB instruction per 64 units (repeated past the
   // wave's rows: the same bytes to the same place).  Absent rows (-1) load row 0 and are
   // masked later, so that every load is unconditional.
-  const int lcv_ni = 1 << (lcv - 3);   // 1 KB instructions for a wave's 8 value rows
-  int tr[8], tv[8];   // A_k row of instruction i; value row of this lane in value instruction i
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    tr[i] = rows_t[wave * 8 + i];
-    tv[i] = rows_t[wave * 8 + ((64 * min(i, lcv_ni - 1) + lane) >> lcv)];
-  }
   const uint16_t* Ag_k = (const uint16_t*)P.A_k + b * P.bs_A_k;
   auto load_rows = [&](int kc) {
     const int col = min(lane * 8, KC - 8);
@@ -928,6 +955,10 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
           16, 0, 0);
     }
   };
+  if constexpr (!MULTI) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot has been read
+    stage_half(vslot, 1, 0);              // the dt = 1 half into the same slot
+  }
   load_rows(0);
 
   // While the rows stream in: rotate the query fragment at the query position, scale it
@@ -980,8 +1011,9 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     // The value rows go out once the A_k rows have landed: with both gathers in flight
     // together the A_k rows land no earlier than the value rows; this way they have the
     // memory system first, and the value rows land while the keys and scores are formed.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the A_k rows have landed
-    lds_sync();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the A_k rows and the dt = 1 half have landed
+    read_half(vslot, 1);
+    lds_sync();   // the row ids are visible and every wave has read its B_k staging
     load_vrows(0);
     kphase();
   } else {

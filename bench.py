@@ -37,16 +37,16 @@ BF16_PEAK_TFLOPS = 2500.0
 
 # HBM traffic of one attend-kernel dispatch at this workload, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over 64 dispatches), each scaled by
-# what the same counter reads for a 1 GiB device-to-device copy (read 524300.5 KiB, written
+# what the same counter reads for a 1 GiB device-to-device copy (read 524304.7 KiB, written
 # 1048576 KiB).  It stands only while the decode kernels' source is the one measured: the
 # source's SHA-256 prefix is recorded and `traffic` is null when it differs.
-ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "76d179dd147a23e9", "fetch_kib": 17002.7, "write_kib": 2056.0,
-                  "fetch_scale": 1048576.0 / 524300.5, "write_scale": 1.0}
+ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "d31f3248372bb1ee", "fetch_kib": 17001.3, "write_kib": 2056.0,
+                  "fetch_scale": 1048576.0 / 524304.7, "write_scale": 1.0}
 # The same for one launch of the Gram kernel over the 16 group sides of the 64k workload
 # (3 dispatches).  FETCH_SIZE counts what the L2 caches request from the memory fabric,
 # so the Infinity Cache's hits are included: it is the Gram's L2-miss traffic.
-GRAM_TRAFFIC = {"src": "gram.hip", "src_sha256": "659e928b4225f03d", "fetch_kib": 62269422.6, "write_kib": 11572111.7,
-                "fetch_scale": 1048576.0 / 524300.5, "write_scale": 1.0}
+GRAM_TRAFFIC = {"src": "gram.hip", "src_sha256": "b2c7f43ee7b7733f", "fetch_kib": 35706130.0, "write_kib": 12192077.7,
+                "fetch_scale": 1048576.0 / 524304.7, "write_scale": 1.0}
 
 
 def traffic_bytes(t):

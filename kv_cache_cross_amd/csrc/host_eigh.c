@@ -1,21 +1,28 @@
 /*
  * Host symmetric eigensolver for the Rayleigh-Ritz step of the subspace
- * iteration (plain C, float64).
+ * iteration (plain C, float64; AVX2 + FMA, which the x86-64-v3 build target
+ * guarantees).
  *
- *   H = Q T Q^T   Householder reduction to tridiagonal form T, with Q
- *                 accumulated backwards from the stored reflectors;
+ *   H = Q T Q^T   Householder reduction to tridiagonal form T; Q is kept as
+ *                 its reflectors;
  *   T = S L S^T   implicit symmetric QR steps with the Wilkinson shift and
- *                 bottom-up deflation, every rotation also applied to Q.
+ *                 bottom-up deflation; the plane rotations are recorded, not
+ *                 applied while the iteration runs.
  *
- * The eigenvectors of H are the columns of Q S.  They are kept as the rows of
- * Qt = (Q S)^T so that each plane rotation touches two contiguous rows.
+ * Only the nvec wanted eigenvectors are formed: the recorded rotations are
+ * applied, last first, to the nvec unit vectors that select the wanted columns
+ * of S (rotations cost 6 nvec flops each instead of 6 n), then Q is applied to
+ * the n x nvec result as blocks of reflectors in compact-WY form, whose products
+ * run through a register-tiled matrix product.
  * References: Golub & Van Loan, Matrix Computations, the Householder vector
- * (section 5.1), tridiagonalisation (section 8.3.1) and the implicit
- * symmetric QR step (section 8.3.3).
+ * (section 5.1), the WY representation of a product of reflectors (section
+ * 5.1.7), tridiagonalisation (section 8.3.1) and the implicit symmetric QR step
+ * (section 8.3.3).
  */
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#include <immintrin.h>
 
 /* Householder vector for x (length m): v[0] = 1, P = I - beta v v^T, P x = mu e_1, mu = |x|. */
 static void house(int m, const double* x, double* v, double* beta, double* mu) {
@@ -36,7 +43,9 @@ static void house(int m, const double* x, double* v, double* beta, double* mu) {
 }
 
 /* Reduce symmetric A (n x n, row-major, lower triangle used and overwritten) to
- * tridiagonal (d, e).  On return Qt holds Q^T, where A_in = Q T Q^T.
+ * tridiagonal (d, e), A_in = Q T Q^T with Q = P_0 P_1 ... P_{n-3}, P_k = I - beta_k v_k v_k^T
+ * acting on rows and columns k+1..n-1.  On return row k of V (n x n) holds v_k (v_k[0] = 1,
+ * component i for row k+1+i) and beta[k] its factor.
  *
  * Step k takes the Householder vector v of column k below the diagonal and forms
  * p = beta A22 v, w = p - (beta/2)(p.v) v; A22 <- A22 - v w^T - w v^T.  Only the lower
@@ -44,15 +53,12 @@ static void house(int m, const double* x, double* v, double* beta, double* mu) {
  * step k + 1: once column k + 1 of the updated matrix is known (its Householder vector
  * v' follows), one pass over the rest of the lower triangle updates each element and
  * adds its contributions a_ij v'_j to p'_i and a_ij v'_i to p'_j. */
-static int tridiagonalize(int n, double* A, double* d, double* e, double* Qt) {
-  double* V = (double*)calloc((size_t)n * n, sizeof(double));   /* reflector k in row k */
-  double* beta = (double*)calloc((size_t)n, sizeof(double));
+static int tridiagonalize(int n, double* A, double* d, double* e, double* V, double* beta) {
   double* p = (double*)malloc((size_t)n * sizeof(double));
   double* w = (double*)malloc((size_t)n * sizeof(double));
   double* col = (double*)malloc((size_t)n * sizeof(double));
-  double* Q = (double*)malloc((size_t)n * n * sizeof(double));
-  if (!V || !beta || !p || !w || !col || !Q) {
-    free(V); free(beta); free(p); free(w); free(col); free(Q);
+  if (!p || !w || !col) {
+    free(p); free(w); free(col);
     return -1;
   }
   /* Step 0's product: p = A22 v over the (not yet updated) lower triangle. */
@@ -107,12 +113,28 @@ static int tridiagonalize(int n, double* A, double* d, double* e, double* Qt) {
         const double vi = v[i + 1], wi = w[i + 1], ui = v2[i];
         const double* vj = v + 1;
         const double* wj = w + 1;
+        /* four-wide: a = row - vi w - wi v, then s += a v2 (four partial sums) and p += ui a */
+        const __m256d vvi = _mm256_set1_pd(vi), vwi = _mm256_set1_pd(wi), vui = _mm256_set1_pd(ui);
+        __m256d s4 = _mm256_setzero_pd();
+        int j = 0;
+        for (; j + 4 <= i; j += 4) {
+          __m256d a = _mm256_fnmadd_pd(vvi, _mm256_loadu_pd(wj + j), _mm256_loadu_pd(row + j));
+          a = _mm256_fnmadd_pd(vwi, _mm256_loadu_pd(vj + j), a);
+          _mm256_storeu_pd(row + j, a);
+          s4 = _mm256_fmadd_pd(a, _mm256_loadu_pd(v2 + j), s4);
+          _mm256_storeu_pd(p + j, _mm256_fmadd_pd(a, vui, _mm256_loadu_pd(p + j)));
+        }
         double s = 0.0;
-        for (int j = 0; j < i; ++j) {
+        for (; j < i; ++j) {
           const double a = row[j] - vi * wj[j] - wi * vj[j];
           row[j] = a;
           s += a * v2[j];
           p[j] += a * ui;
+        }
+        {
+          double part[4];
+          _mm256_storeu_pd(part, s4);
+          s += (part[0] + part[1]) + (part[2] + part[3]);
         }
         const double a = row[i] - vi * wj[i] - wi * vj[i];
         row[i] = a;
@@ -135,109 +157,42 @@ static int tridiagonalize(int n, double* A, double* d, double* e, double* Qt) {
   }
   d[n - 1] = A[(size_t)(n - 1) * n + n - 1];
 
-  /* Q = P_0 P_1 ... P_{n-3}, accumulated from the right end in blocks of NB reflectors:
-   * P_kb ... P_{kb+nb-1} = I - Y T Y^T (compact WY; Y holds the reflectors, T is upper
-   * triangular), applied as Q22 -= Y (T (Y^T Q22)) with Q22 = rows and columns kb+1...
-   * Columns are taken in panels of QC so that the nb x QC product stays in cache. */
-  for (size_t i = 0; i < (size_t)n * n; ++i) Q[i] = 0.0;
-  for (int i = 0; i < n; ++i) Q[(size_t)i * n + i] = 1.0;
-  {
-    enum { NB = 32, QC = 128 };
-    double* Tm = (double*)malloc((size_t)NB * NB * sizeof(double));
-    double* Wp = (double*)malloc((size_t)NB * QC * sizeof(double));
-    double* Yt = (double*)malloc((size_t)NB * n * sizeof(double));   /* Y^T: reflector c in row c */
-    if (!Tm || !Wp || !Yt) {
-      free(Tm); free(Wp); free(Yt);
-      free(V); free(beta); free(p); free(w); free(col); free(Q);
-      return -1;
-    }
-    const int nref = n - 2;   /* reflectors 0 .. n-3 */
-    for (int kb = ((nref - 1) / NB) * NB; kb >= 0; kb -= NB) {
-      const int nb = nref - kb < NB ? nref - kb : NB;
-      const int r0 = kb + 1, M = n - r0;
-      /* Yt[c][i] = component of reflector kb+c at row r0 + i (zero above its start) */
-      for (int c = 0; c < nb; ++c) {
-        double* y = Yt + (size_t)c * n;
-        const double* v = V + (size_t)(kb + c) * n;
-        for (int i = 0; i < M; ++i) y[i] = i < c ? 0.0 : v[i - c];
-      }
-      /* T: T[c][c] = beta_c, T[0:c, c] = -beta_c T[0:c, 0:c] (Y[:, 0:c]^T y_c) */
-      for (int c = 0; c < nb; ++c) {
-        const double bc = beta[kb + c];
-        const double* yc = Yt + (size_t)c * n;
-        for (int a = 0; a < c; ++a) {
-          const double* ya = Yt + (size_t)a * n;
-          double t = 0.0;
-          for (int i = c; i < M; ++i) t += ya[i] * yc[i];
-          w[a] = t;
-        }
-        for (int a = 0; a < c; ++a) {
-          double t = 0.0;
-          for (int b2 = a; b2 < c; ++b2) t += Tm[a * NB + b2] * w[b2];
-          Tm[a * NB + c] = -bc * t;
-        }
-        Tm[c * NB + c] = bc;
-        for (int a = c + 1; a < NB; ++a) Tm[a * NB + c] = 0.0;
-      }
-      for (int j0 = 0; j0 < M; j0 += QC) {
-        const int jw = M - j0 < QC ? M - j0 : QC;
-        /* Wp = Y^T Q22[:, j0:j0+jw] */
-        for (int c = 0; c < nb; ++c)
-          for (int j = 0; j < jw; ++j) Wp[c * QC + j] = 0.0;
-        for (int i = 0; i < M; ++i) {
-          const double* row = Q + (size_t)(r0 + i) * n + r0 + j0;
-          for (int c = 0; c < nb; ++c) {
-            const double yci = Yt[(size_t)c * n + i];
-            if (yci == 0.0) continue;
-            double* wc = Wp + c * QC;
-            for (int j = 0; j < jw; ++j) wc[j] += yci * row[j];
-          }
-        }
-        /* Wp = T Wp (upper triangular, in place, top row first) */
-        for (int a = 0; a < nb; ++a) {
-          double* wa = Wp + a * QC;
-          const double taa = Tm[a * NB + a];
-          for (int j = 0; j < jw; ++j) wa[j] *= taa;
-          for (int b2 = a + 1; b2 < nb; ++b2) {
-            const double tab = Tm[a * NB + b2];
-            const double* wb = Wp + b2 * QC;
-            for (int j = 0; j < jw; ++j) wa[j] += tab * wb[j];
-          }
-        }
-        /* Q22[:, j0:j0+jw] -= Y Wp */
-        for (int i = 0; i < M; ++i) {
-          double* row = Q + (size_t)(r0 + i) * n + r0 + j0;
-          for (int c = 0; c < nb; ++c) {
-            const double yci = Yt[(size_t)c * n + i];
-            if (yci == 0.0) continue;
-            const double* wc = Wp + c * QC;
-            for (int j = 0; j < jw; ++j) row[j] -= yci * wc[j];
-          }
-        }
-      }
-    }
-    free(Tm); free(Wp); free(Yt);
-  }
-  for (int i = 0; i < n; ++i)
-    for (int j = 0; j < n; ++j) Qt[(size_t)j * n + i] = Q[(size_t)i * n + j];
-
-  free(V); free(beta); free(p); free(w); free(col); free(Q);
+  free(p); free(w); free(col);
   return 0;
 }
 
-/* Rows k, k+1 of Qt <- [c s; -s c] applied to them (columns k, k+1 of Q). */
-static void rotate_rows(int n, double* Qt, int k, double c, double s) {
-  double* a = Qt + (size_t)k * n;
-  double* b = a + n;
-  for (int j = 0; j < n; ++j) {
-    const double x = a[j], y = b[j];
-    a[j] = c * x + s * y;
-    b[j] = c * y - s * x;
+/* The plane rotations of the QR iteration, in the order they were taken: rotation t acts on
+ * rows/columns k[t], k[t] + 1 of the eigenvector matrix, which becomes S <- S G_t with
+ * G_t = [c -s; s c] in that 2 x 2 block. */
+typedef struct {
+  double* c;
+  double* s;
+  int* k;
+  long n, cap;
+} rotlog;
+
+static int rotlog_push(rotlog* L, int k, double c, double s) {
+  if (L->n == L->cap) {
+    const long cap = L->cap ? 2 * L->cap : 4096;
+    double* nc = (double*)realloc(L->c, (size_t)cap * sizeof(double));
+    if (nc) L->c = nc;
+    double* ns = (double*)realloc(L->s, (size_t)cap * sizeof(double));
+    if (ns) L->s = ns;
+    int* nk = (int*)realloc(L->k, (size_t)cap * sizeof(int));
+    if (nk) L->k = nk;
+    if (!nc || !ns || !nk) return -1;
+    L->cap = cap;
   }
+  L->c[L->n] = c;
+  L->s[L->n] = s;
+  L->k[L->n] = k;
+  ++L->n;
+  return 0;
 }
 
-/* One implicit QR step with Wilkinson shift on the unreduced block [l, m]. */
-static void qr_step(int n, double* d, double* e, double* Qt, int l, int m) {
+/* One implicit QR step with Wilkinson shift on the unreduced block [l, m]; its rotations are
+ * appended to the log.  Returns -1 if the log cannot grow. */
+static int qr_step(double* d, double* e, rotlog* log, int l, int m) {
   const double delta = 0.5 * (d[m - 1] - d[m]);
   const double bb = e[m - 1];
   const double den = delta + copysign(hypot(delta, bb), delta == 0.0 ? 1.0 : delta);
@@ -258,8 +213,195 @@ static void qr_step(int n, double* d, double* e, double* Qt, int l, int m) {
       e[k + 1] *= c;
       x = e[k];
     }
-    rotate_rows(n, Qt, k, c, s);
+    if (rotlog_push(log, k, c, s) != 0) return -1;
   }
+  return 0;
+}
+
+/* S (n x ncol, row-major) <- G_1 G_2 ... G_N S: the logged rotations, last first, each on two
+ * rows of S.  S is copied into panels of RC columns stored row after row.  The log splits into
+ * runs in which k rises by one from each rotation to the next (a QR sweep); taken last first, a
+ * run walks down the rows, so a run is applied to 16 columns at a time with the row shared by
+ * consecutive rotations carried in registers: one row load and one row store per rotation.
+ * Returns -1 on allocation failure. */
+static int apply_rotations_reverse(const rotlog* L, int n, int ncol, double* S) {
+  enum { RC = 128 };
+  double* P = (double*)malloc((size_t)n * RC * sizeof(double));
+  if (!P) return -1;
+  /* The wanted columns start as unit vectors; early rotations leave long runs of entries far
+   * below 1e-300 that decay through the subnormal range, where x86 arithmetic is ~100 times
+   * slower.  Subnormal results and inputs are taken as zero here (flush-to-zero and
+   * denormals-are-zero, this thread only, restored on return): they change no entry by more
+   * than 2.3e-308 of a unit vector. */
+  const unsigned int csr = _mm_getcsr();
+  _mm_setcsr(csr | 0x8040u);
+  for (int j0 = 0; j0 < ncol; j0 += RC) {
+    const int jw = ncol - j0 < RC ? ncol - j0 : RC;
+    for (int i = 0; i < n; ++i) {
+      memcpy(P + (size_t)i * RC, S + (size_t)i * ncol + j0, (size_t)jw * sizeof(double));
+      for (int j = jw; j < RC; ++j) P[(size_t)i * RC + j] = 0.0;
+    }
+    for (long t = L->n - 1; t >= 0;) {
+      long t0 = t;   /* the run: rotations t0 .. t, k[u] = k[t] - (t - u) */
+      while (t0 > 0 && L->k[t0 - 1] == L->k[t0] - 1) --t0;
+      const int ktop = L->k[t];
+      for (int j = 0; j < RC; j += 16) {
+        double* top = P + (size_t)(ktop + 1) * RC + j;
+        __m256d y0 = _mm256_loadu_pd(top), y1 = _mm256_loadu_pd(top + 4), y2 = _mm256_loadu_pd(top + 8),
+                y3 = _mm256_loadu_pd(top + 12);
+        double* row = top;   /* row k + 1 of the current rotation */
+        for (long u = t; u >= t0; --u) {
+          double* xr = row - RC;   /* row k */
+          const __m256d vc = _mm256_set1_pd(L->c[u]), vs = _mm256_set1_pd(L->s[u]);
+          const __m256d x0 = _mm256_loadu_pd(xr), x1 = _mm256_loadu_pd(xr + 4), x2 = _mm256_loadu_pd(xr + 8),
+                        x3 = _mm256_loadu_pd(xr + 12);
+          /* row k + 1 <- s x + c y (final for this run); row k <- c x - s y (carried: one
+           * dependent operation per rotation, c x is formed off the chain) */
+          _mm256_storeu_pd(row, _mm256_fmadd_pd(vs, x0, _mm256_mul_pd(vc, y0)));
+          _mm256_storeu_pd(row + 4, _mm256_fmadd_pd(vs, x1, _mm256_mul_pd(vc, y1)));
+          _mm256_storeu_pd(row + 8, _mm256_fmadd_pd(vs, x2, _mm256_mul_pd(vc, y2)));
+          _mm256_storeu_pd(row + 12, _mm256_fmadd_pd(vs, x3, _mm256_mul_pd(vc, y3)));
+          y0 = _mm256_fnmadd_pd(vs, y0, _mm256_mul_pd(vc, x0));
+          y1 = _mm256_fnmadd_pd(vs, y1, _mm256_mul_pd(vc, x1));
+          y2 = _mm256_fnmadd_pd(vs, y2, _mm256_mul_pd(vc, x2));
+          y3 = _mm256_fnmadd_pd(vs, y3, _mm256_mul_pd(vc, x3));
+          row = xr;
+        }
+        _mm256_storeu_pd(row, y0);
+        _mm256_storeu_pd(row + 4, y1);
+        _mm256_storeu_pd(row + 8, y2);
+        _mm256_storeu_pd(row + 12, y3);
+      }
+      t = t0 - 1;
+    }
+    for (int i = 0; i < n; ++i) memcpy(S + (size_t)i * ncol + j0, P + (size_t)i * RC, (size_t)jw * sizeof(double));
+  }
+  _mm_setcsr(csr);
+  free(P);
+  return 0;
+}
+
+/* C (m x n) += sgn * A (m x k) B (k x n), row-major with leading dimensions lda, ldb, ldc.
+ * The first n - n % 8 columns of B are first packed into Bp (k x (n - n % 8) doubles) as
+ * panels of 8 columns, each panel's k rows contiguous; tiles of 4 rows x 8 columns of C are
+ * then accumulated in registers over all of k, reading A's rows and one packed panel
+ * front to back. */
+static void gemm_acc(int m, int n, int k, double sgn, const double* A, int lda, const double* B, int ldb,
+                     double* C, int ldc, double* Bp) {
+  const int m4 = m & ~3, n8 = n & ~7;
+  for (int j0 = 0; j0 < n8; j0 += 8) {
+    double* panel = Bp + (size_t)j0 * k;
+    for (int q = 0; q < k; ++q) {
+      _mm256_storeu_pd(panel + 8 * q, _mm256_loadu_pd(B + (size_t)q * ldb + j0));
+      _mm256_storeu_pd(panel + 8 * q + 4, _mm256_loadu_pd(B + (size_t)q * ldb + j0 + 4));
+    }
+  }
+  const __m256d vsg = _mm256_set1_pd(sgn);
+  for (int i0 = 0; i0 < m4; i0 += 4) {
+    const double* a0 = A + (size_t)i0 * lda;
+    for (int j0 = 0; j0 < n8; j0 += 8) {
+      __m256d c00 = _mm256_setzero_pd(), c01 = _mm256_setzero_pd(), c10 = _mm256_setzero_pd(),
+              c11 = _mm256_setzero_pd(), c20 = _mm256_setzero_pd(), c21 = _mm256_setzero_pd(),
+              c30 = _mm256_setzero_pd(), c31 = _mm256_setzero_pd();
+      const double* bp = Bp + (size_t)j0 * k;
+      for (int q = 0; q < k; ++q, bp += 8) {
+        const __m256d b0 = _mm256_loadu_pd(bp), b1 = _mm256_loadu_pd(bp + 4);
+        __m256d av = _mm256_broadcast_sd(a0 + q);
+        c00 = _mm256_fmadd_pd(av, b0, c00);
+        c01 = _mm256_fmadd_pd(av, b1, c01);
+        av = _mm256_broadcast_sd(a0 + lda + q);
+        c10 = _mm256_fmadd_pd(av, b0, c10);
+        c11 = _mm256_fmadd_pd(av, b1, c11);
+        av = _mm256_broadcast_sd(a0 + 2 * (size_t)lda + q);
+        c20 = _mm256_fmadd_pd(av, b0, c20);
+        c21 = _mm256_fmadd_pd(av, b1, c21);
+        av = _mm256_broadcast_sd(a0 + 3 * (size_t)lda + q);
+        c30 = _mm256_fmadd_pd(av, b0, c30);
+        c31 = _mm256_fmadd_pd(av, b1, c31);
+      }
+      double* cp = C + (size_t)i0 * ldc + j0;
+      _mm256_storeu_pd(cp, _mm256_fmadd_pd(vsg, c00, _mm256_loadu_pd(cp)));
+      _mm256_storeu_pd(cp + 4, _mm256_fmadd_pd(vsg, c01, _mm256_loadu_pd(cp + 4)));
+      cp += ldc;
+      _mm256_storeu_pd(cp, _mm256_fmadd_pd(vsg, c10, _mm256_loadu_pd(cp)));
+      _mm256_storeu_pd(cp + 4, _mm256_fmadd_pd(vsg, c11, _mm256_loadu_pd(cp + 4)));
+      cp += ldc;
+      _mm256_storeu_pd(cp, _mm256_fmadd_pd(vsg, c20, _mm256_loadu_pd(cp)));
+      _mm256_storeu_pd(cp + 4, _mm256_fmadd_pd(vsg, c21, _mm256_loadu_pd(cp + 4)));
+      cp += ldc;
+      _mm256_storeu_pd(cp, _mm256_fmadd_pd(vsg, c30, _mm256_loadu_pd(cp)));
+      _mm256_storeu_pd(cp + 4, _mm256_fmadd_pd(vsg, c31, _mm256_loadu_pd(cp + 4)));
+    }
+  }
+  /* ragged edges: the last n % 8 columns of the tiled rows, then the last m % 4 rows */
+  for (int i = 0; i < m; ++i) {
+    const int j_from = i < m4 ? n8 : 0;
+    for (int j = j_from; j < n; ++j) {
+      double t = 0.0;
+      for (int q = 0; q < k; ++q) t += A[(size_t)i * lda + q] * B[(size_t)q * ldb + j];
+      C[(size_t)i * ldc + j] += sgn * t;
+    }
+  }
+}
+
+/* S (n x ncol, row-major) <- Q S with Q = P_0 P_1 ... P_{n-3} the reflectors of
+ * tridiagonalize, taken from the right end in blocks of NB: P_kb ... P_{kb+nb-1} =
+ * I - Y T Y^T (compact WY; Y holds the reflectors, T is upper triangular), applied to rows
+ * kb+1.. as S2 -= Y (T (Y^T S2)).  Returns -1 on allocation failure. */
+static int apply_reflectors(int n, const double* V, const double* beta, int ncol, double* S) {
+  enum { NB = 32 };
+  const int nref = n - 2;   /* reflectors 0 .. n-3 */
+  if (nref <= 0) return 0;
+  double* Tm = (double*)malloc((size_t)NB * NB * sizeof(double));
+  double* Yt = (double*)malloc((size_t)NB * n * sizeof(double));    /* Y^T: reflector c in row c */
+  double* Yr = (double*)malloc((size_t)n * NB * sizeof(double));    /* Y, row-major */
+  double* W = (double*)malloc((size_t)NB * ncol * sizeof(double));
+  double* W2 = (double*)malloc((size_t)NB * ncol * sizeof(double));
+  double* tw = (double*)malloc((size_t)NB * sizeof(double));
+  double* Bp = (double*)malloc((size_t)n * ncol * sizeof(double));   /* packed panels of the products */
+  if (!Tm || !Yt || !Yr || !W || !W2 || !tw || !Bp) {
+    free(Tm); free(Yt); free(Yr); free(W); free(W2); free(tw); free(Bp);
+    return -1;
+  }
+  for (int kb = ((nref - 1) / NB) * NB; kb >= 0; kb -= NB) {
+    const int nb = nref - kb < NB ? nref - kb : NB;
+    const int r0 = kb + 1, M = n - r0;
+    /* Yt[c][i] = component of reflector kb+c at row r0 + i (zero above its start) */
+    for (int c = 0; c < nb; ++c) {
+      double* y = Yt + (size_t)c * n;
+      const double* v = V + (size_t)(kb + c) * n;
+      for (int i = 0; i < M; ++i) y[i] = i < c ? 0.0 : v[i - c];
+    }
+    for (int i = 0; i < M; ++i)
+      for (int c = 0; c < nb; ++c) Yr[(size_t)i * NB + c] = Yt[(size_t)c * n + i];
+    /* T: T[c][c] = beta_c, T[0:c, c] = -beta_c T[0:c, 0:c] (Y[:, 0:c]^T y_c) */
+    for (int c = 0; c < nb; ++c) {
+      const double bc = beta[kb + c];
+      const double* yc = Yt + (size_t)c * n;
+      for (int a = 0; a < c; ++a) {
+        const double* ya = Yt + (size_t)a * n;
+        double t = 0.0;
+        for (int i = c; i < M; ++i) t += ya[i] * yc[i];
+        tw[a] = t;
+      }
+      for (int a = 0; a < c; ++a) {
+        double t = 0.0;
+        for (int b2 = a; b2 < c; ++b2) t += Tm[a * NB + b2] * tw[b2];
+        Tm[a * NB + c] = -bc * t;
+      }
+      Tm[c * NB + c] = bc;
+      for (int a = c + 1; a < NB; ++a) Tm[a * NB + c] = 0.0;
+    }
+    double* S2 = S + (size_t)r0 * ncol;
+    /* W = Y^T S2 (nb x ncol); W2 = T W; S2 -= Y W2 */
+    memset(W, 0, (size_t)nb * ncol * sizeof(double));
+    gemm_acc(nb, ncol, M, 1.0, Yt, n, S2, ncol, W, ncol, Bp);
+    memset(W2, 0, (size_t)nb * ncol * sizeof(double));
+    gemm_acc(nb, ncol, nb, 1.0, Tm, NB, W, ncol, W2, ncol, Bp);
+    gemm_acc(M, ncol, nb, -1.0, Yr, NB, W2, ncol, S2, ncol, Bp);
+  }
+  free(Tm); free(Yt); free(Yr); free(W); free(W2); free(tw); free(Bp);
+  return 0;
 }
 
 typedef struct { double key; int idx; } keyed;
@@ -278,17 +420,19 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double
                                                               double* Z) {
   if (n <= 0 || nvec <= 0 || nvec > n) return -3;
   double* A = (double*)malloc((size_t)n * n * sizeof(double));
-  double* Qt = (double*)malloc((size_t)n * n * sizeof(double));
+  double* V = (double*)calloc((size_t)n * n, sizeof(double));
+  double* beta = (double*)calloc((size_t)n, sizeof(double));
   double* d = (double*)malloc((size_t)n * sizeof(double));
   double* e = (double*)calloc((size_t)n, sizeof(double));
   keyed* idx = (keyed*)malloc((size_t)n * sizeof(keyed));
+  rotlog log = {0};
   int rc = 0;
-  if (!A || !Qt || !d || !e || !idx) { rc = -1; goto done; }
+  if (!A || !V || !beta || !d || !e || !idx) { rc = -1; goto done; }
   /* Symmetrise: use the mean of the two triangles. */
   for (int i = 0; i < n; ++i)
     for (int j = 0; j < n; ++j)
       A[(size_t)i * n + j] = 0.5 * (H[(size_t)i * n + j] + H[(size_t)j * n + i]);
-  if (tridiagonalize(n, A, d, e, Qt) != 0) { rc = -1; goto done; }
+  if (tridiagonalize(n, A, d, e, V, beta) != 0) { rc = -1; goto done; }
 
   {
     const double eps = 2.220446049250313e-16;
@@ -306,7 +450,7 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double
       int l = m - 1;
       while (l > 0 && fabs(e[l - 1]) > eps * (fabs(d[l - 1]) + fabs(d[l])) && fabs(e[l - 1]) > tiny) --l;
       if (l > 0) e[l - 1] = 0.0;
-      qr_step(n, d, e, Qt, l, m);
+      if (qr_step(d, e, &log, l, m) != 0) { rc = -1; goto done; }
       if (--budget < 0) { rc = -2; goto done; }
     }
   }
@@ -314,11 +458,14 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double
   for (int i = 0; i < n; ++i) { idx[i].key = d[i]; idx[i].idx = i; }
   qsort(idx, (size_t)n, sizeof(keyed), cmp_desc);
   for (int j = 0; j < n; ++j) w[j] = idx[j].key;
-  for (int j = 0; j < nvec; ++j) {
-    const double* v = Qt + (size_t)idx[j].idx * n;
-    for (int i = 0; i < n; ++i) Z[(size_t)i * nvec + j] = v[i];
-  }
+  /* Z = Q G_1 ... G_N E, E the unit vectors of the wanted positions: the rotations on E
+   * (last first), then the reflectors. */
+  memset(Z, 0, (size_t)n * nvec * sizeof(double));
+  for (int j = 0; j < nvec; ++j) Z[(size_t)idx[j].idx * nvec + j] = 1.0;
+  if (apply_rotations_reverse(&log, n, nvec, Z) != 0) { rc = -1; goto done; }
+  if (apply_reflectors(n, V, beta, nvec, Z) != 0) { rc = -1; goto done; }
 done:
-  free(A); free(Qt); free(d); free(e); free(idx);
+  free(A); free(V); free(beta); free(d); free(e); free(idx);
+  free(log.c); free(log.s); free(log.k);
   return rc;
 }

@@ -98,6 +98,8 @@ def main():
     if c.batch != 1:
         raise SystemExit("bench.py times the batch-1 workloads (llama64k, llama16k, qwen122k, tiny)")
     D = args.decode_steps if args.decode_steps is not None else c.decode_steps
+    if D < 1:
+        raise SystemExit("bench.py: --decode-steps must be at least 1 (a step is compression + D decode steps)")
     Lyr, G, d_kv, T, r, H, d, Hq = c.n_layers, c.group, c.d_kv, c.T, c.rank, c.n_kv_heads, c.head_dim, c.n_q_heads
     dt = c.torch_dtype
     esz = 2 if dt == torch.bfloat16 else 4

@@ -27,7 +27,9 @@
  *  - The caller owns all memory, including the workspace.  The library never
  *    allocates or frees device memory and keeps no pointer after a call
  *    returns.  A context owns host-side resources only (pinned staging for
- *    the Rayleigh-Ritz round trip, host solver threads).
+ *    the Rayleigh-Ritz round trip, host solver threads, and each solver
+ *    thread's working memory, ~25 MB per thread at r = 512, G d_kv = 4096,
+ *    kept until xkv_ctx_destroy so that later compressions reuse it).
  *  - Work is enqueued on the caller's HIP stream (passed as void*; NULL is
  *    the default stream).  Arguments are validated before anything is
  *    enqueued; a failed validation enqueues nothing.

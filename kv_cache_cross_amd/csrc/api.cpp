@@ -18,7 +18,7 @@
 #include "dense_params.h"
 #include "xkv_kernels.h"
 
-extern "C" int xkv_eigh_desc_impl(int n, const double* H, int nvec, double* w, double* Z);
+#include "host_eigh.h"
 extern "C" int xkv_rank_stats_impl(const double* vals, int n, double total, double frac, int complete,
                                    int* energy_rank, double* covered, int* num_rank, double* erank, double* ner);
 
@@ -68,6 +68,9 @@ struct xkv_ctx_s {
   size_t pin_doubles = 0;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
+  // Host memory of the Rayleigh-Ritz eigensolves, one per worker thread, kept between calls
+  // so that repeated compressions neither map nor fault pages (which serialises threads).
+  std::vector<xkv_eigh_scratch> eig_scratch;
 };
 
 extern "C" {
@@ -102,6 +105,7 @@ void xkv_ctx_destroy(xkv_ctx ctx) {
     (void)hipEventDestroy(ctx->upload_done);
   }
   if (ctx->pin) (void)hipHostFree(ctx->pin);
+  for (auto& sc : ctx->eig_scratch) xkv_eigh_scratch_release(&sc);
   delete ctx;
 }
 
@@ -398,9 +402,11 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
 
     // Host eigensolves, one thread per side (bounded by ctx->host_threads).
     std::vector<int> erc(S, 0);
+    if ((int)ctx->eig_scratch.size() < nthr) ctx->eig_scratch.resize(nthr, xkv_eigh_scratch{});
     auto worker = [&](int t0) {
       for (int s = t0; s < S; s += nthr)
-        erc[s] = xkv_eigh_desc_impl(kb, hH + (size_t)s * kk, r, evals[s].data(), hZ + (size_t)s * kb * r);
+        erc[s] = xkv_eigh_desc_scratch(kb, hH + (size_t)s * kk, r, evals[s].data(), hZ + (size_t)s * kb * r,
+                                       &ctx->eig_scratch[t0]);
     };
     if (nthr == 1) {
       worker(0);

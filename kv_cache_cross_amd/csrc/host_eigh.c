@@ -23,6 +23,7 @@
 #include <stdlib.h>
 #include <string.h>
 #include <immintrin.h>
+#include "host_eigh.h"
 
 /* Householder vector for x (length m): v[0] = 1, P = I - beta v v^T, P x = mu e_1, mu = |x|. */
 static void house(int m, const double* x, double* v, double* beta, double* mu) {
@@ -45,7 +46,7 @@ static void house(int m, const double* x, double* v, double* beta, double* mu) {
 /* Reduce symmetric A (n x n, row-major, lower triangle used and overwritten) to
  * tridiagonal (d, e), A_in = Q T Q^T with Q = P_0 P_1 ... P_{n-3}, P_k = I - beta_k v_k v_k^T
  * acting on rows and columns k+1..n-1.  On return row k of V (n x n) holds v_k (v_k[0] = 1,
- * component i for row k+1+i) and beta[k] its factor.
+ * component i for row k+1+i) and beta[k] its factor.  p, w and col are n doubles of scratch.
  *
  * Step k takes the Householder vector v of column k below the diagonal and forms
  * p = beta A22 v, w = p - (beta/2)(p.v) v; A22 <- A22 - v w^T - w v^T.  Only the lower
@@ -53,14 +54,8 @@ static void house(int m, const double* x, double* v, double* beta, double* mu) {
  * step k + 1: once column k + 1 of the updated matrix is known (its Householder vector
  * v' follows), one pass over the rest of the lower triangle updates each element and
  * adds its contributions a_ij v'_j to p'_i and a_ij v'_i to p'_j. */
-static int tridiagonalize(int n, double* A, double* d, double* e, double* V, double* beta) {
-  double* p = (double*)malloc((size_t)n * sizeof(double));
-  double* w = (double*)malloc((size_t)n * sizeof(double));
-  double* col = (double*)malloc((size_t)n * sizeof(double));
-  if (!p || !w || !col) {
-    free(p); free(w); free(col);
-    return -1;
-  }
+static void tridiagonalize(int n, double* A, double* d, double* e, double* V, double* beta, double* p, double* w,
+                           double* col) {
   /* Step 0's product: p = A22 v over the (not yet updated) lower triangle. */
   int have_p = 0;
   for (int k = 0; k + 2 < n; ++k) {
@@ -157,19 +152,11 @@ static int tridiagonalize(int n, double* A, double* d, double* e, double* V, dou
   }
   d[n - 1] = A[(size_t)(n - 1) * n + n - 1];
 
-  free(p); free(w); free(col);
-  return 0;
 }
 
-/* The plane rotations of the QR iteration, in the order they were taken: rotation t acts on
- * rows/columns k[t], k[t] + 1 of the eigenvector matrix, which becomes S <- S G_t with
- * G_t = [c -s; s c] in that 2 x 2 block. */
-typedef struct {
-  double* c;
-  double* s;
-  int* k;
-  long n, cap;
-} rotlog;
+/* Rotation t of the log acts on rows/columns k[t], k[t] + 1 of the eigenvector matrix,
+ * which becomes S <- S G_t with G_t = [c -s; s c] in that 2 x 2 block. */
+typedef xkv_rotlog rotlog;
 
 static int rotlog_push(rotlog* L, int k, double c, double s) {
   if (L->n == L->cap) {
@@ -223,11 +210,9 @@ static int qr_step(double* d, double* e, rotlog* log, int l, int m) {
  * runs in which k rises by one from each rotation to the next (a QR sweep); taken last first, a
  * run walks down the rows, so a run is applied to 16 columns at a time with the row shared by
  * consecutive rotations carried in registers: one row load and one row store per rotation.
- * Returns -1 on allocation failure. */
-static int apply_rotations_reverse(const rotlog* L, int n, int ncol, double* S) {
-  enum { RC = 128 };
-  double* P = (double*)malloc((size_t)n * RC * sizeof(double));
-  if (!P) return -1;
+ * P is n * RC doubles of scratch. */
+enum { RC = 128 };   /* column panel of apply_rotations_reverse */
+static void apply_rotations_reverse(const rotlog* L, int n, int ncol, double* S, double* P) {
   /* The wanted columns start as unit vectors; early rotations leave long runs of entries far
    * below 1e-300 that decay through the subnormal range, where x86 arithmetic is ~100 times
    * slower.  Subnormal results and inputs are taken as zero here (flush-to-zero and
@@ -277,8 +262,6 @@ static int apply_rotations_reverse(const rotlog* L, int n, int ncol, double* S) 
     for (int i = 0; i < n; ++i) memcpy(S + (size_t)i * ncol + j0, P + (size_t)i * RC, (size_t)jw * sizeof(double));
   }
   _mm_setcsr(csr);
-  free(P);
-  return 0;
 }
 
 /* C (m x n) += sgn * A (m x k) B (k x n), row-major with leading dimensions lda, ldb, ldc.
@@ -347,22 +330,21 @@ static void gemm_acc(int m, int n, int k, double sgn, const double* A, int lda, 
 /* S (n x ncol, row-major) <- Q S with Q = P_0 P_1 ... P_{n-3} the reflectors of
  * tridiagonalize, taken from the right end in blocks of NB: P_kb ... P_{kb+nb-1} =
  * I - Y T Y^T (compact WY; Y holds the reflectors, T is upper triangular), applied to rows
- * kb+1.. as S2 -= Y (T (Y^T S2)).  Returns -1 on allocation failure. */
-static int apply_reflectors(int n, const double* V, const double* beta, int ncol, double* S) {
-  enum { NB = 32 };
+ * kb+1.. as S2 -= Y (T (Y^T S2)).  scr holds reflector_scratch(n, ncol) doubles. */
+enum { NB = 32 };   /* reflectors per compact-WY block */
+static size_t reflector_scratch(int n, int ncol) {
+  return (size_t)NB * NB + 2 * (size_t)NB * n + 2 * (size_t)NB * ncol + NB + (size_t)n * ncol;
+}
+static void apply_reflectors(int n, const double* V, const double* beta, int ncol, double* S, double* scr) {
   const int nref = n - 2;   /* reflectors 0 .. n-3 */
-  if (nref <= 0) return 0;
-  double* Tm = (double*)malloc((size_t)NB * NB * sizeof(double));
-  double* Yt = (double*)malloc((size_t)NB * n * sizeof(double));    /* Y^T: reflector c in row c */
-  double* Yr = (double*)malloc((size_t)n * NB * sizeof(double));    /* Y, row-major */
-  double* W = (double*)malloc((size_t)NB * ncol * sizeof(double));
-  double* W2 = (double*)malloc((size_t)NB * ncol * sizeof(double));
-  double* tw = (double*)malloc((size_t)NB * sizeof(double));
-  double* Bp = (double*)malloc((size_t)n * ncol * sizeof(double));   /* packed panels of the products */
-  if (!Tm || !Yt || !Yr || !W || !W2 || !tw || !Bp) {
-    free(Tm); free(Yt); free(Yr); free(W); free(W2); free(tw); free(Bp);
-    return -1;
-  }
+  if (nref <= 0) return;
+  double* Tm = scr;                          /* NB x NB */
+  double* Yt = Tm + (size_t)NB * NB;         /* Y^T: reflector c in row c (NB x n) */
+  double* Yr = Yt + (size_t)NB * n;          /* Y, row-major (n x NB) */
+  double* W = Yr + (size_t)n * NB;           /* NB x ncol */
+  double* W2 = W + (size_t)NB * ncol;        /* NB x ncol */
+  double* tw = W2 + (size_t)NB * ncol;       /* NB */
+  double* Bp = tw + NB;                      /* packed panels of the products (n x ncol) */
   for (int kb = ((nref - 1) / NB) * NB; kb >= 0; kb -= NB) {
     const int nb = nref - kb < NB ? nref - kb : NB;
     const int r0 = kb + 1, M = n - r0;
@@ -400,8 +382,6 @@ static int apply_reflectors(int n, const double* V, const double* beta, int ncol
     gemm_acc(nb, ncol, nb, 1.0, Tm, NB, W, ncol, W2, ncol, Bp);
     gemm_acc(M, ncol, nb, -1.0, Yr, NB, W2, ncol, S2, ncol, Bp);
   }
-  free(Tm); free(Yt); free(Yr); free(W); free(W2); free(tw); free(Bp);
-  return 0;
 }
 
 typedef struct { double key; int idx; } keyed;
@@ -414,25 +394,45 @@ static int cmp_desc(const void* a, const void* b) {
 }
 
 /* All n eigenvalues of symmetric H, descending, into w (length n); the eigenvectors of the
- * nvec largest as the columns of Z (n x nvec).  Returns 0 on success, -1 on allocation
+ * nvec largest as the columns of Z (n x nvec).  sc keeps its memory for the next call (a
+ * zero-filled struct on first use; xkv_eigh_scratch_release frees it): repeated solves in
+ * several threads then neither map nor fault pages.  Returns 0 on success, -1 on allocation
  * failure, -2 if the QR iteration did not converge. */
-__attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double* H, int nvec, double* w,
-                                                              double* Z) {
+__attribute__((visibility("hidden"))) int xkv_eigh_desc_scratch(int n, const double* H, int nvec, double* w,
+                                                                 double* Z, xkv_eigh_scratch* sc) {
   if (n <= 0 || nvec <= 0 || nvec > n) return -3;
-  double* A = (double*)malloc((size_t)n * n * sizeof(double));
-  double* V = (double*)calloc((size_t)n * n, sizeof(double));
-  double* beta = (double*)calloc((size_t)n, sizeof(double));
-  double* d = (double*)malloc((size_t)n * sizeof(double));
-  double* e = (double*)calloc((size_t)n, sizeof(double));
-  keyed* idx = (keyed*)malloc((size_t)n * sizeof(keyed));
-  rotlog log = {0};
-  int rc = 0;
-  if (!A || !V || !beta || !d || !e || !idx) { rc = -1; goto done; }
+  /* A n^2, V n^2, beta, d, e, p, w, col n each, idx 2n (keyed), the rotation panel, the
+   * reflector buffers, the eigenvectors while they are formed (the caller's Z may be pinned
+   * host memory, which is slower to work in; it receives one copy at the end) */
+  const size_t need = 2 * (size_t)n * n + 8 * (size_t)n + (size_t)n * RC + reflector_scratch(n, nvec) +
+                      (size_t)n * nvec;
+  if (sc->cap < need) {
+    free(sc->buf);
+    sc->buf = (double*)malloc(need * sizeof(double));
+    sc->cap = sc->buf ? need : 0;
+    if (!sc->buf) return -1;
+  }
+  double* A = sc->buf;
+  double* V = A + (size_t)n * n;
+  double* beta = V + (size_t)n * n;
+  double* d = beta + n;
+  double* e = d + n;
+  double* tp = e + n;
+  double* tw = tp + n;
+  double* tcol = tw + n;
+  keyed* idx = (keyed*)(tcol + n);
+  double* panel = (double*)(idx + n);
+  double* rscr = panel + (size_t)n * RC;
+  double* Zw = rscr + reflector_scratch(n, nvec);
+  memset(beta, 0, (size_t)n * sizeof(double));
+  memset(e, 0, (size_t)n * sizeof(double));
+  rotlog* log = &sc->log;
+  log->n = 0;
   /* Symmetrise: use the mean of the two triangles. */
   for (int i = 0; i < n; ++i)
     for (int j = 0; j < n; ++j)
       A[(size_t)i * n + j] = 0.5 * (H[(size_t)i * n + j] + H[(size_t)j * n + i]);
-  if (tridiagonalize(n, A, d, e, V, beta) != 0) { rc = -1; goto done; }
+  tridiagonalize(n, A, d, e, V, beta, tp, tw, tcol);
 
   {
     const double eps = 2.220446049250313e-16;
@@ -450,8 +450,8 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double
       int l = m - 1;
       while (l > 0 && fabs(e[l - 1]) > eps * (fabs(d[l - 1]) + fabs(d[l])) && fabs(e[l - 1]) > tiny) --l;
       if (l > 0) e[l - 1] = 0.0;
-      if (qr_step(d, e, &log, l, m) != 0) { rc = -1; goto done; }
-      if (--budget < 0) { rc = -2; goto done; }
+      if (qr_step(d, e, log, l, m) != 0) return -1;
+      if (--budget < 0) return -2;
     }
   }
 
@@ -460,12 +460,28 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double
   for (int j = 0; j < n; ++j) w[j] = idx[j].key;
   /* Z = Q G_1 ... G_N E, E the unit vectors of the wanted positions: the rotations on E
    * (last first), then the reflectors. */
-  memset(Z, 0, (size_t)n * nvec * sizeof(double));
-  for (int j = 0; j < nvec; ++j) Z[(size_t)idx[j].idx * nvec + j] = 1.0;
-  if (apply_rotations_reverse(&log, n, nvec, Z) != 0) { rc = -1; goto done; }
-  if (apply_reflectors(n, V, beta, nvec, Z) != 0) { rc = -1; goto done; }
-done:
-  free(A); free(V); free(beta); free(d); free(e); free(idx);
-  free(log.c); free(log.s); free(log.k);
+  memset(Zw, 0, (size_t)n * nvec * sizeof(double));
+  for (int j = 0; j < nvec; ++j) Zw[(size_t)idx[j].idx * nvec + j] = 1.0;
+  apply_rotations_reverse(log, n, nvec, Zw, panel);
+  apply_reflectors(n, V, beta, nvec, Zw, rscr);
+  memcpy(Z, Zw, (size_t)n * nvec * sizeof(double));
+  return 0;
+}
+
+__attribute__((visibility("hidden"))) void xkv_eigh_scratch_release(xkv_eigh_scratch* sc) {
+  free(sc->buf);
+  free(sc->log.c);
+  free(sc->log.s);
+  free(sc->log.k);
+  memset(sc, 0, sizeof(*sc));
+}
+
+/* As xkv_eigh_desc_scratch with memory of its own, freed on return. */
+__attribute__((visibility("hidden"))) int xkv_eigh_desc_impl(int n, const double* H, int nvec, double* w,
+                                                              double* Z) {
+  xkv_eigh_scratch sc;
+  memset(&sc, 0, sizeof(sc));
+  const int rc = xkv_eigh_desc_scratch(n, H, nvec, w, Z, &sc);
+  xkv_eigh_scratch_release(&sc);
   return rc;
 }

@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # what the same counter reads for a 1 GiB device-to-device copy (read 524304.7 KiB, written
 # 1048576 KiB).  It stands only while the decode kernels' source is the one measured: the
 # source's SHA-256 prefix is recorded and `traffic` is null when it differs.
-ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "d31f3248372bb1ee", "fetch_kib": 17001.3, "write_kib": 2056.0,
+ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "26d5326069937ef4", "fetch_kib": 17001.3, "write_kib": 2056.0,
                   "fetch_scale": 1048576.0 / 524304.7, "write_scale": 1.0}
 # The same for one launch of the Gram kernel over the 16 group sides of the 64k workload
 # (3 dispatches).  FETCH_SIZE counts what the L2 caches request from the memory fabric,

@@ -19,22 +19,19 @@
 //     and leave a softmax partial (max, denominator, weighted value sum) per
 //     query head.
 // sr_attend_mfma_kernel (bf16, head_dim 128, r_k % 128 == 0 and r_v == r_k, or r_v == 0
-// with exact values (xK-SR); grid: KV
-// heads x splits x batch, so one head's blocks share an XCD and its B slices in L2;
-// 512 threads, two waves per SIMD)
-//   * a block takes 64 rows: the selected chunks [s*64/chunk, (s+1)*64/chunk) of
-//     its head, minus rows the exact tail covers;
-//   * the gathered rows of A_k are staged with direct-to-LDS loads, every load in
-//     flight at once (16 bytes per lane, a wave per row), and each wave's slice of
-//     B_k,l,h goes to registers behind them; the rows of A_v go to registers while
-//     the keys are rebuilt;
-//   * the eight waves rebuild k_t = A_k[t] B_k,l,h, 16 key dims each, on
-//     v_mfma_f32_16x16x32_bf16 with no memory wait between MFMAs; the dims are
-//     ordered so that RoPE pairs meet in one lane group; scores and a softmax
-//     partial follow;
-//   * values are never rebuilt: since v_t = A_v[t] B_v,l,h, the block's
-//     weighted value sum is (sum_t p_t A_v[t]) B_v,l,h, and it leaves the rank-r
-//     vector sum_t p_t A_v[t] per query head.
+// with exact values (xK-SR); grid: KV heads x splits x batch, so one head's blocks
+// share an XCD and its B slices in L2; 512 threads, one block per CU)
+//   * a block takes 64 rows: the selected chunks [s*64/chunk, (s+1)*64/chunk) of its
+//     head, minus rows the exact tail covers;
+//   * the gathered rows of A_k and the block's B_k,l,h slice reach LDS with
+//     direct-to-LDS loads; the value rows (A_v rank chunk, or exact V rows) follow
+//     once the A_k rows have landed and arrive while the keys are formed;
+//   * the eight waves rebuild k_t = A_k[t] B_k,l,h on v_mfma_f32_16x16x32_bf16, the
+//     dims ordered so that RoPE pairs meet in one lane; scores (on the MFMA, bf16 hi + lo
+//     parts) and a softmax partial follow;
+//   * values are never rebuilt: since v_t = A_v[t] B_v,l,h, the block's weighted value
+//     sum is (sum_t p_t A_v[t]) B_v,l,h, and it leaves the rank-r vector
+//     sum_t p_t A_v[t] per query head.
 // sr_attend_generic_kernel covers every other shape (float32, other head
 // dims, exact values, ranks that differ) with value-space partials.
 // sr_merge_kernel (grid: query heads x batch) and, for the matrix-core path,

@@ -485,10 +485,10 @@ def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     f64 = lambda t: t.detach().double().cpu().numpy()
-    # Decode sample: layers 0 and 1 at the first two decode steps, on a cache of the same
+    # Decode sample: layers 0 and 1 at the first four decode steps, on a cache of the same
     # shapes that involves no GPU output: the generator's own rank-r factors and the
     # oracle's landmarks of the original keys.
-    sample_layers, sample_steps = [0, 1], [0, 1]
+    sample_layers, sample_steps = [0, 1], [s for s in range(4) if s < D]
     t_dec = 0.0
     for l in sample_layers:
         A_k, Bk = (f64(x) for x in wl.factor_cache(0, "K", l, c.rank))
@@ -529,7 +529,8 @@ def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):
     n_sides = 2 * c.n_groups
     comp_s = side_s * n_sides
     return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(cores), "kind": "oracle",
-            "sample": f"SR decode of layers 0-1 at decode steps 0-1 (4 layer-steps, on a stand-in cache of the same shapes), "
+            "sample": f"SR decode of layers 0-1 at decode steps 0-{len(sample_steps) - 1} "
+                      f"({len(sample_layers) * len(sample_steps)} layer-steps, on a stand-in cache of the same shapes), "
                       f"scaled x{c.n_layers} layers; compression of one group side on its first {T_s} tokens "
                       f"(Gram+projection+landmarks scaled x{scale:g} in T, eigensolve of n={c.n} once), "
                       f"scaled x{n_sides} sides",

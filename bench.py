@@ -511,7 +511,7 @@ def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):
     per_layer_step = t_dec / (len(sample_layers) * len(sample_steps))
     us_per_step = per_layer_step * c.n_layers * 1e6
     # Compression sample: the oracle's factorisation of one group side (K of group 0) on its
-    # first 8192 tokens; the Gram/projection parts scale with T, the n x n eigensolve does not.
+    # first 16384 tokens; the Gram/projection parts scale with T, the n x n eigensolve does not.
     T_s = min(16384, c.T)
     Ks = [f64(layers[("K", i)][:T_s]) for i in range(c.group)]
     t0 = time.perf_counter()

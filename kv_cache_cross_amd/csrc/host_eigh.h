@@ -1,5 +1,6 @@
 /* Host symmetric eigensolver of the Rayleigh-Ritz step (host_eigh.c). */
 #pragma once
+#include <stddef.h>
 #ifdef __cplusplus
 extern "C" {
 #endif

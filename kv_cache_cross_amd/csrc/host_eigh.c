@@ -9,6 +9,8 @@
  *                 bottom-up deflation; the plane rotations are recorded, not
  *                 applied while the iteration runs.
  *
+ * The rotation and product kernels use AVX-512 where the CPU has it.
+ *
  * Only the nvec wanted eigenvectors are formed: the recorded rotations are
  * applied, last first, to the nvec unit vectors that select the wanted columns
  * of S (rotations cost 6 nvec flops each instead of 6 n), then Q is applied to
@@ -211,8 +213,18 @@ static int qr_step(double* d, double* e, rotlog* log, int l, int m) {
  * run walks down the rows, so a run is applied to 16 columns at a time with the row shared by
  * consecutive rotations carried in registers: one row load and one row store per rotation.
  * P is n * RC doubles of scratch. */
+/* AVX-512 (8 doubles per register) where the CPU has it: the rotation and product kernels
+ * below have a 512-bit twin, chosen at run time; both give the same results element by
+ * element (the same operations in the same order). */
+static int have_avx512(void) { return __builtin_cpu_supports("avx512f"); }
+
 enum { RC = 128 };   /* column panel of apply_rotations_reverse */
+static void apply_rotations_reverse_avx512(const rotlog* L, int n, int ncol, double* S, double* P);
 static void apply_rotations_reverse(const rotlog* L, int n, int ncol, double* S, double* P) {
+  if (have_avx512()) {
+    apply_rotations_reverse_avx512(L, n, ncol, S, P);
+    return;
+  }
   /* The wanted columns start as unit vectors; early rotations leave long runs of entries far
    * below 1e-300 that decay through the subnormal range, where x86 arithmetic is ~100 times
    * slower.  Subnormal results and inputs are taken as zero here (flush-to-zero and
@@ -264,13 +276,66 @@ static void apply_rotations_reverse(const rotlog* L, int n, int ncol, double* S,
   _mm_setcsr(csr);
 }
 
+/* apply_rotations_reverse with 32 columns (four 8-wide registers) per pass of a run. */
+__attribute__((target("avx512f"))) static void apply_rotations_reverse_avx512(const rotlog* L, int n, int ncol,
+                                                                             double* S, double* P) {
+  const unsigned int csr = _mm_getcsr();
+  _mm_setcsr(csr | 0x8040u);   /* flush subnormals, as in the AVX2 version */
+  for (int j0 = 0; j0 < ncol; j0 += RC) {
+    const int jw = ncol - j0 < RC ? ncol - j0 : RC;
+    for (int i = 0; i < n; ++i) {
+      memcpy(P + (size_t)i * RC, S + (size_t)i * ncol + j0, (size_t)jw * sizeof(double));
+      for (int j = jw; j < RC; ++j) P[(size_t)i * RC + j] = 0.0;
+    }
+    for (long t = L->n - 1; t >= 0;) {
+      long t0 = t;
+      while (t0 > 0 && L->k[t0 - 1] == L->k[t0] - 1) --t0;
+      const int ktop = L->k[t];
+      for (int j = 0; j < RC; j += 32) {
+        double* top = P + (size_t)(ktop + 1) * RC + j;
+        __m512d y0 = _mm512_loadu_pd(top), y1 = _mm512_loadu_pd(top + 8), y2 = _mm512_loadu_pd(top + 16),
+                y3 = _mm512_loadu_pd(top + 24);
+        double* row = top;
+        for (long u = t; u >= t0; --u) {
+          double* xr = row - RC;
+          const __m512d vc = _mm512_set1_pd(L->c[u]), vs = _mm512_set1_pd(L->s[u]);
+          const __m512d x0 = _mm512_loadu_pd(xr), x1 = _mm512_loadu_pd(xr + 8), x2 = _mm512_loadu_pd(xr + 16),
+                        x3 = _mm512_loadu_pd(xr + 24);
+          _mm512_storeu_pd(row, _mm512_fmadd_pd(vs, x0, _mm512_mul_pd(vc, y0)));
+          _mm512_storeu_pd(row + 8, _mm512_fmadd_pd(vs, x1, _mm512_mul_pd(vc, y1)));
+          _mm512_storeu_pd(row + 16, _mm512_fmadd_pd(vs, x2, _mm512_mul_pd(vc, y2)));
+          _mm512_storeu_pd(row + 24, _mm512_fmadd_pd(vs, x3, _mm512_mul_pd(vc, y3)));
+          y0 = _mm512_fnmadd_pd(vs, y0, _mm512_mul_pd(vc, x0));
+          y1 = _mm512_fnmadd_pd(vs, y1, _mm512_mul_pd(vc, x1));
+          y2 = _mm512_fnmadd_pd(vs, y2, _mm512_mul_pd(vc, x2));
+          y3 = _mm512_fnmadd_pd(vs, y3, _mm512_mul_pd(vc, x3));
+          row = xr;
+        }
+        _mm512_storeu_pd(row, y0);
+        _mm512_storeu_pd(row + 8, y1);
+        _mm512_storeu_pd(row + 16, y2);
+        _mm512_storeu_pd(row + 24, y3);
+      }
+      t = t0 - 1;
+    }
+    for (int i = 0; i < n; ++i) memcpy(S + (size_t)i * ncol + j0, P + (size_t)i * RC, (size_t)jw * sizeof(double));
+  }
+  _mm_setcsr(csr);
+}
+
 /* C (m x n) += sgn * A (m x k) B (k x n), row-major with leading dimensions lda, ldb, ldc.
  * The first n - n % 8 columns of B are first packed into Bp (k x (n - n % 8) doubles) as
  * panels of 8 columns, each panel's k rows contiguous; tiles of 4 rows x 8 columns of C are
  * then accumulated in registers over all of k, reading A's rows and one packed panel
  * front to back. */
+static void gemm_acc_avx512(int m, int n, int k, double sgn, const double* A, int lda, const double* B, int ldb,
+                            double* C, int ldc, double* Bp);
 static void gemm_acc(int m, int n, int k, double sgn, const double* A, int lda, const double* B, int ldb,
                      double* C, int ldc, double* Bp) {
+  if (have_avx512()) {
+    gemm_acc_avx512(m, n, k, sgn, A, lda, B, ldb, C, ldc, Bp);
+    return;
+  }
   const int m4 = m & ~3, n8 = n & ~7;
   for (int j0 = 0; j0 < n8; j0 += 8) {
     double* panel = Bp + (size_t)j0 * k;
@@ -319,6 +384,66 @@ static void gemm_acc(int m, int n, int k, double sgn, const double* A, int lda, 
   /* ragged edges: the last n % 8 columns of the tiled rows, then the last m % 4 rows */
   for (int i = 0; i < m; ++i) {
     const int j_from = i < m4 ? n8 : 0;
+    for (int j = j_from; j < n; ++j) {
+      double t = 0.0;
+      for (int q = 0; q < k; ++q) t += A[(size_t)i * lda + q] * B[(size_t)q * ldb + j];
+      C[(size_t)i * ldc + j] += sgn * t;
+    }
+  }
+}
+
+/* gemm_acc with panels of 16 columns and tiles of 4 rows x 16 columns (eight 8-wide
+ * accumulators); the ragged edges as there. */
+__attribute__((target("avx512f"))) static void gemm_acc_avx512(int m, int n, int k, double sgn, const double* A,
+                                                              int lda, const double* B, int ldb, double* C, int ldc,
+                                                              double* Bp) {
+  const int m4 = m & ~3, n16 = n & ~15;
+  for (int j0 = 0; j0 < n16; j0 += 16) {
+    double* panel = Bp + (size_t)j0 * k;
+    for (int q = 0; q < k; ++q) {
+      _mm512_storeu_pd(panel + 16 * q, _mm512_loadu_pd(B + (size_t)q * ldb + j0));
+      _mm512_storeu_pd(panel + 16 * q + 8, _mm512_loadu_pd(B + (size_t)q * ldb + j0 + 8));
+    }
+  }
+  const __m512d vsg = _mm512_set1_pd(sgn);
+  for (int i0 = 0; i0 < m4; i0 += 4) {
+    const double* a0 = A + (size_t)i0 * lda;
+    for (int j0 = 0; j0 < n16; j0 += 16) {
+      __m512d c00 = _mm512_setzero_pd(), c01 = _mm512_setzero_pd(), c10 = _mm512_setzero_pd(),
+              c11 = _mm512_setzero_pd(), c20 = _mm512_setzero_pd(), c21 = _mm512_setzero_pd(),
+              c30 = _mm512_setzero_pd(), c31 = _mm512_setzero_pd();
+      const double* bp = Bp + (size_t)j0 * k;
+      for (int q = 0; q < k; ++q, bp += 16) {
+        const __m512d b0 = _mm512_loadu_pd(bp), b1 = _mm512_loadu_pd(bp + 8);
+        __m512d av = _mm512_set1_pd(a0[q]);
+        c00 = _mm512_fmadd_pd(av, b0, c00);
+        c01 = _mm512_fmadd_pd(av, b1, c01);
+        av = _mm512_set1_pd(a0[lda + q]);
+        c10 = _mm512_fmadd_pd(av, b0, c10);
+        c11 = _mm512_fmadd_pd(av, b1, c11);
+        av = _mm512_set1_pd(a0[2 * (size_t)lda + q]);
+        c20 = _mm512_fmadd_pd(av, b0, c20);
+        c21 = _mm512_fmadd_pd(av, b1, c21);
+        av = _mm512_set1_pd(a0[3 * (size_t)lda + q]);
+        c30 = _mm512_fmadd_pd(av, b0, c30);
+        c31 = _mm512_fmadd_pd(av, b1, c31);
+      }
+      double* cp = C + (size_t)i0 * ldc + j0;
+      _mm512_storeu_pd(cp, _mm512_fmadd_pd(vsg, c00, _mm512_loadu_pd(cp)));
+      _mm512_storeu_pd(cp + 8, _mm512_fmadd_pd(vsg, c01, _mm512_loadu_pd(cp + 8)));
+      cp += ldc;
+      _mm512_storeu_pd(cp, _mm512_fmadd_pd(vsg, c10, _mm512_loadu_pd(cp)));
+      _mm512_storeu_pd(cp + 8, _mm512_fmadd_pd(vsg, c11, _mm512_loadu_pd(cp + 8)));
+      cp += ldc;
+      _mm512_storeu_pd(cp, _mm512_fmadd_pd(vsg, c20, _mm512_loadu_pd(cp)));
+      _mm512_storeu_pd(cp + 8, _mm512_fmadd_pd(vsg, c21, _mm512_loadu_pd(cp + 8)));
+      cp += ldc;
+      _mm512_storeu_pd(cp, _mm512_fmadd_pd(vsg, c30, _mm512_loadu_pd(cp)));
+      _mm512_storeu_pd(cp + 8, _mm512_fmadd_pd(vsg, c31, _mm512_loadu_pd(cp + 8)));
+    }
+  }
+  for (int i = 0; i < m; ++i) {
+    const int j_from = i < m4 ? n16 : 0;
     for (int j = j_from; j < n; ++j) {
       double t = 0.0;
       for (int q = 0; q < k; ++q) t += A[(size_t)i * lda + q] * B[(size_t)q * ldb + j];

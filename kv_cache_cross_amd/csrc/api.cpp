@@ -122,7 +122,14 @@ int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z) {
   if (n <= 0 || !H || !w || !Z || nvec <= 0 || nvec > n)
     return fail(XKV_EINVAL, "xkv_host_eigh: bad arguments (n=%d, nvec=%d)", n, nvec);
   std::vector<double> all(n);
-  const int rc = xkv_eigh_desc_impl(n, H, nvec, all.data(), Z);
+  // The two phases as compressions run them: the vector phase in two column ranges, the second
+  // with working memory of its own (the way a helper thread takes half of a side).
+  xkv_eigh_scratch sc{}, helper{};
+  int rc = xkv_eigh_values(n, H, nvec, all.data(), &sc);
+  if (rc == 0) rc = xkv_eigh_vectors(&sc, 0, nvec / 2, Z, &sc);
+  if (rc == 0) rc = xkv_eigh_vectors(&sc, nvec / 2, nvec, Z, &helper);
+  xkv_eigh_scratch_release(&sc);
+  xkv_eigh_scratch_release(&helper);
   if (rc == 0) std::memcpy(w, all.data(), nvec * sizeof(double));
   if (rc == -1) return fail(XKV_EINVAL, "xkv_host_eigh: out of host memory");
   if (rc != 0) return fail(XKV_ENUMERIC, "xkv_host_eigh: QR iteration did not converge");

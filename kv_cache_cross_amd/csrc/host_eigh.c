@@ -518,25 +518,24 @@ static int cmp_desc(const void* a, const void* b) {
   return x->idx - y->idx;
 }
 
-/* All n eigenvalues of symmetric H, descending, into w (length n); the eigenvectors of the
- * nvec largest as the columns of Z (n x nvec).  sc keeps its memory for the next call (a
- * zero-filled struct on first use; xkv_eigh_scratch_release frees it): repeated solves in
- * several threads then neither map nor fault pages.  Returns 0 on success, -1 on allocation
- * failure, -2 if the QR iteration did not converge. */
-__attribute__((visibility("hidden"))) int xkv_eigh_desc_scratch(int n, const double* H, int nvec, double* w,
-                                                                 double* Z, xkv_eigh_scratch* sc) {
+/* Value phase: all n eigenvalues of symmetric H, descending, into w; the reflectors, the
+ * rotation log and the order of the eigenvalues stay in sc for xkv_eigh_vectors.  sc keeps its
+ * memory for the next call (a zero-filled struct on first use; xkv_eigh_scratch_release frees
+ * it): repeated solves in several threads then neither map nor fault pages.  Returns 0 on
+ * success, -1 on allocation failure, -2 if the QR iteration did not converge. */
+__attribute__((visibility("hidden"))) int xkv_eigh_values(int n, const double* H, int nvec, double* w,
+                                                           xkv_eigh_scratch* sc) {
   if (n <= 0 || nvec <= 0 || nvec > n) return -3;
-  /* A n^2, V n^2, beta, d, e, p, w, col n each, idx 2n (keyed), the rotation panel, the
-   * reflector buffers, the eigenvectors while they are formed (the caller's Z may be pinned
-   * host memory, which is slower to work in; it receives one copy at the end) */
-  const size_t need = 2 * (size_t)n * n + 8 * (size_t)n + (size_t)n * RC + reflector_scratch(n, nvec) +
-                      (size_t)n * nvec;
+  /* A n^2, V n^2, beta, d, e, p, w, col n each, idx 2n (keyed) */
+  const size_t need = 2 * (size_t)n * n + 8 * (size_t)n;
   if (sc->cap < need) {
     free(sc->buf);
     sc->buf = (double*)malloc(need * sizeof(double));
     sc->cap = sc->buf ? need : 0;
     if (!sc->buf) return -1;
   }
+  sc->n = n;
+  sc->nvec = nvec;
   double* A = sc->buf;
   double* V = A + (size_t)n * n;
   double* beta = V + (size_t)n * n;
@@ -546,9 +545,6 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_scratch(int n, const dou
   double* tw = tp + n;
   double* tcol = tw + n;
   keyed* idx = (keyed*)(tcol + n);
-  double* panel = (double*)(idx + n);
-  double* rscr = panel + (size_t)n * RC;
-  double* Zw = rscr + reflector_scratch(n, nvec);
   memset(beta, 0, (size_t)n * sizeof(double));
   memset(e, 0, (size_t)n * sizeof(double));
   rotlog* log = &sc->log;
@@ -583,18 +579,49 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_scratch(int n, const dou
   for (int i = 0; i < n; ++i) { idx[i].key = d[i]; idx[i].idx = i; }
   qsort(idx, (size_t)n, sizeof(keyed), cmp_desc);
   for (int j = 0; j < n; ++j) w[j] = idx[j].key;
-  /* Z = Q G_1 ... G_N E, E the unit vectors of the wanted positions: the rotations on E
-   * (last first), then the reflectors. */
-  memset(Zw, 0, (size_t)n * nvec * sizeof(double));
-  for (int j = 0; j < nvec; ++j) Zw[(size_t)idx[j].idx * nvec + j] = 1.0;
-  apply_rotations_reverse(log, n, nvec, Zw, panel);
-  apply_reflectors(n, V, beta, nvec, Zw, rscr);
-  memcpy(Z, Zw, (size_t)n * nvec * sizeof(double));
   return 0;
+}
+
+/* Vector phase: Z[:, j0:j1] = Q G_1 ... G_N E, E the unit vectors of the wanted positions: the
+ * rotations on E (last first), then the reflectors, in `work`'s memory, then one copy into Z
+ * (which may be pinned host memory, slower to work in). */
+__attribute__((visibility("hidden"))) int xkv_eigh_vectors(const xkv_eigh_scratch* state, int j0, int j1,
+                                                            double* Z, xkv_eigh_scratch* work) {
+  const int n = state->n, nvec = state->nvec, nc = j1 - j0;
+  if (nc <= 0) return 0;
+  const double* V = state->buf + (size_t)n * n;
+  const double* beta = V + (size_t)n * n;
+  const keyed* idx = (const keyed*)(beta + 6 * (size_t)n);
+  const size_t need = (size_t)n * RC + reflector_scratch(n, nc) + (size_t)n * nc;
+  if (work->vcap < need) {
+    free(work->vbuf);
+    work->vbuf = (double*)malloc(need * sizeof(double));
+    work->vcap = work->vbuf ? need : 0;
+    if (!work->vbuf) return -1;
+  }
+  double* panel = work->vbuf;
+  double* rscr = panel + (size_t)n * RC;
+  double* Zw = rscr + reflector_scratch(n, nc);
+  memset(Zw, 0, (size_t)n * nc * sizeof(double));
+  for (int j = j0; j < j1; ++j) Zw[(size_t)idx[j].idx * nc + (j - j0)] = 1.0;
+  apply_rotations_reverse(&state->log, n, nc, Zw, panel);
+  apply_reflectors(n, V, beta, nc, Zw, rscr);
+  for (int i = 0; i < n; ++i) memcpy(Z + (size_t)i * nvec + j0, Zw + (size_t)i * nc, (size_t)nc * sizeof(double));
+  return 0;
+}
+
+/* All n eigenvalues of symmetric H, descending, into w (length n); the eigenvectors of the
+ * nvec largest as the columns of Z (n x nvec): the two phases in the calling thread. */
+__attribute__((visibility("hidden"))) int xkv_eigh_desc_scratch(int n, const double* H, int nvec, double* w,
+                                                                 double* Z, xkv_eigh_scratch* sc) {
+  const int rc = xkv_eigh_values(n, H, nvec, w, sc);
+  if (rc) return rc;
+  return xkv_eigh_vectors(sc, 0, nvec, Z, sc);
 }
 
 __attribute__((visibility("hidden"))) void xkv_eigh_scratch_release(xkv_eigh_scratch* sc) {
   free(sc->buf);
+  free(sc->vbuf);
   free(sc->log.c);
   free(sc->log.s);
   free(sc->log.k);

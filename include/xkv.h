@@ -27,9 +27,9 @@
  *  - The caller owns all memory, including the workspace.  The library never
  *    allocates or frees device memory and keeps no pointer after a call
  *    returns.  A context owns host-side resources only (pinned staging for
- *    the Rayleigh-Ritz round trip, host solver threads, and each solver
- *    thread's working memory, ~25 MB per thread at r = 512, G d_kv = 4096,
- *    kept until xkv_ctx_destroy so that later compressions reuse it).
+ *    the Rayleigh-Ritz round trip, host solver threads, and the solvers'
+ *    working memory, ~27 MB per side at r = 512, G d_kv = 4096, kept until
+ *    xkv_ctx_destroy so that later compressions reuse it).
  *  - Work is enqueued on the caller's HIP stream (passed as void*; NULL is
  *    the default stream).  Arguments are validated before anything is
  *    enqueued; a failed validation enqueues nothing.
@@ -118,10 +118,13 @@ typedef struct {
 int xkv_compress_ws_size(const xkv_compress_desc* desc, int n_sides, size_t* bytes);
 
 /* Factor `n_sides` independent group sides of identical shape.
- * Steps (all sides batched): Gram C = X^T X (bf16 MFMA, float64 totals) ->
+ * Steps (sides batched): Gram C = X^T X (bf16 MFMA, float64 totals) ->
  * block subspace iteration Y = C Q with CholeskyQR orthonormalisation ->
- * Rayleigh-Ritz H = Q^T C Q (float64) -> host eigensolve of H (plain C, one
- * thread per side) -> V_r = Q Z_r -> A = X V_r and the landmarks.
+ * Rayleigh-Ritz H = Q^T C Q (float64) -> host eigensolve of H (plain C; the
+ * eigenvalues one thread per side, the eigenvectors two threads per side) ->
+ * V_r = Q Z_r -> A = X V_r and the landmarks.  With 4 or more sides the
+ * sides go in two halves, so that the GPU steps of the second half run while
+ * the host solves the first half's eigenproblems.
  * Convergence: after each Rayleigh-Ritz round the Ritz residual
  * R = C V_r - V_r diag(theta) gives the estimate sqrt(2) ||R||_F / (theta_r -
  * theta_{r+1}) of ||P - P_exact||_F (P = V_r V_r^T); rounds with more float64

@@ -68,9 +68,12 @@ struct xkv_ctx_s {
   size_t pin_doubles = 0;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
-  // Host memory of the Rayleigh-Ritz eigensolves, one per worker thread, kept between calls
-  // so that repeated compressions neither map nor fault pages (which serialises threads).
-  std::vector<xkv_eigh_scratch> eig_scratch;
+  // Host memory of the Rayleigh-Ritz eigensolves, two per side (value state + first half of
+  // the vectors, second half of the vectors), kept between calls so that repeated
+  // compressions neither map nor fault pages.
+  std::vector<xkv_eigh_scratch> eig_side;
+  // Marks the Rayleigh-Ritz matrices of each half of the sides as copied to the host.
+  hipEvent_t half_done[2] = {nullptr, nullptr};
 };
 
 extern "C" {
@@ -94,6 +97,8 @@ int xkv_ctx_create(int device, int host_threads, xkv_ctx* out) {
   c->host_threads = host_threads > 0 ? host_threads : 16;
   XKV_HIP(hipSetDevice(device));
   XKV_HIP(hipEventCreateWithFlags(&c->upload_done, hipEventDisableTiming));
+  XKV_HIP(hipEventCreateWithFlags(&c->half_done[0], hipEventDisableTiming));
+  XKV_HIP(hipEventCreateWithFlags(&c->half_done[1], hipEventDisableTiming));
   *out = c;
   return XKV_OK;
 }
@@ -104,8 +109,10 @@ void xkv_ctx_destroy(xkv_ctx ctx) {
     (void)hipEventSynchronize(ctx->upload_done);
     (void)hipEventDestroy(ctx->upload_done);
   }
+  for (hipEvent_t e : ctx->half_done)
+    if (e) (void)hipEventDestroy(e);
   if (ctx->pin) (void)hipHostFree(ctx->pin);
-  for (auto& sc : ctx->eig_scratch) xkv_eigh_scratch_release(&sc);
+  for (auto& sc : ctx->eig_side) xkv_eigh_scratch_release(&sc);
   delete ctx;
 }
 
@@ -217,6 +224,33 @@ CompressWs carve_compress(void* ws, const CompressPlan& p, int S) {
   return w;
 }
 
+// The workspace arrays from side s0 on (every array holds its sides back to back).
+CompressWs shift_compress_ws(const CompressWs& w, const CompressPlan& p, int s0) {
+  const size_t nn = (size_t)p.n * p.n, nk = (size_t)p.n * p.kb, kk = (size_t)p.kb * p.kb;
+  const size_t nr = (size_t)p.n * p.r, es = p.bf16 ? 2 : 4;
+  CompressWs v = w;
+  v.C64 += s0 * nn;
+  if (v.C32) v.C32 += s0 * nn;
+  v.Q32 += s0 * nk;
+  if (v.Y32) v.Y32 += s0 * nk;
+  v.Q64 += s0 * nk;
+  v.Y64 += s0 * nk;
+  v.W += s0 * kk;
+  v.L += s0 * kk;
+  v.Dinv += (size_t)s0 * p.nblk * 64 * 64;
+  v.H += s0 * kk;
+  v.Z += (size_t)s0 * p.kb * p.r;
+  v.Vr += s0 * nr;
+  v.wdiag += (size_t)s0 * p.kb;
+  v.YZ += s0 * nr;
+  v.theta += (size_t)s0 * p.r;
+  v.res2 += (size_t)s0 * p.r;
+  v.VrT = (char*)v.VrT + s0 * nr * es;
+  v.trace += s0;
+  v.info += s0;
+  return v;
+}
+
 xkv::GemmDesc gdesc(int M, int N, int K, int ta, int tb, int tA, int tB, int tC, const void* A, long lda, long sA,
                     const void* B, long ldb, long sB, void* C, long ldc, long sC, double alpha, double beta,
                     int batch) {
@@ -318,50 +352,72 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   const long nn = (long)n * n, nk = (long)n * kb, kk = (long)kb * kb;
 
   XKV_K(launch_zero_i32(w.info, S, st));
-  // 1. Gram of every side (batched, at most kMaxPtrs layer pointers per launch).
+  // The sides go in two halves when there are at least 4: the GPU work of the second half
+  // runs while the host solves the first half's Rayleigh-Ritz problems (stream order; the
+  // host waits on per-half events, not on the stream).
+  struct Half {
+    CompressWs w;   // the workspace arrays from this half's first side on
+    int s0, cnt;
+    void* Qcur;
+    int tQ;
+    double* Qa;
+    double* Ya;
+  };
+  const int nh = S >= 4 ? 2 : 1;
+  Half hv[2];
+  for (int h = 0; h < nh; ++h) {
+    Half& hf = hv[h];
+    hf.s0 = h == 0 ? 0 : S / 2;
+    hf.cnt = nh == 1 ? S : (h == 0 ? S / 2 : S - S / 2);
+    hf.w = shift_compress_ws(w, p, hf.s0);
+    hf.Qcur = hf.w.Q32;
+    hf.tQ = GF32;
+    hf.Qa = hf.w.Q64;
+    hf.Ya = hf.w.Y64;
+  }
   const int per = std::max(1, kMaxPtrs / p.G);
-  for (int s0 = 0; s0 < S; s0 += per) {
-    const int cnt = std::min(per, S - s0);
-    PtrTable tab{};
-    for (int s = 0; s < cnt; ++s)
-      for (int l = 0; l < p.G; ++l) tab.p[s * p.G + l] = sides[s0 + s].layers[l];
-    double* C = w.C64 + s0 * nn;
-    float* C32 = w.C32 ? w.C32 + s0 * nn : nullptr;
-    if (p.bf16) XKV_K(launch_gram_bf16(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
-    else XKV_K(launch_gram_f32(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
-  }
-  XKV_K(launch_trace(w.C64, nn, n, S, w.trace, st));   // total energy of every side
-  // 2. Block subspace iteration: float32 sweeps on a float32 copy of C, then float64
-  //    sweeps (CholeskyQR, CholeskyQR2 on the last sweep of a round).
-  XKV_K(launch_init_q(w.Q32, n, kb, nk, S, desc->seed, st));
-  for (int it = 0; it < p.fp32_iters; ++it) {
-    GemmDesc cq = gdesc(n, kb, n, 0, 0, GF32, GF32, GF32, w.C32, n, nn, w.Q32, kb, nk, w.Y32, kb, nk, 1.0, 0.0, S);
-    cq.acc = GF32;   // float32 matrix cores for the float32 iterations
-    XKV_K(gemm(cq, st));
-    rc = cholqr(p, w, S, w.Y32, GF32, w.Q32, GF32, st);
-    if (rc) return rc;
-  }
-  void* Qcur = w.Q32;
-  int tQ = GF32;
-  double* Qa = w.Q64;
-  double* Ya = w.Y64;
-  auto fp64_sweeps = [&](int count) -> int {
+  auto fp64_sweeps = [&](Half& hf, int count) -> int {
     for (int it = 0; it < count; ++it) {
-      XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, tQ, GF64, w.C64, n, nn, Qcur, kb, nk, Ya, kb, nk, 1.0, 0.0, S), st));
-      int e = cholqr(p, w, S, Ya, GF64, Qa, GF64, st);       // Qa = orth(Ya)
+      XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, hf.tQ, GF64, hf.w.C64, n, nn, hf.Qcur, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
+                       hf.cnt), st));
+      int e = cholqr(p, hf.w, hf.cnt, hf.Ya, GF64, hf.Qa, GF64, st);       // Qa = orth(Ya)
       if (e) return e;
       if (it + 1 == count) {
-        e = cholqr(p, w, S, Qa, GF64, Ya, GF64, st);         // second pass: Ya = orth(Qa)
+        e = cholqr(p, hf.w, hf.cnt, hf.Qa, GF64, hf.Ya, GF64, st);         // second pass: Ya = orth(Qa)
         if (e) return e;
-        std::swap(Qa, Ya);                                   // Qa holds the basis
+        std::swap(hf.Qa, hf.Ya);                                           // Qa holds the basis
       }
-      Qcur = Qa;
-      tQ = GF64;
+      hf.Qcur = hf.Qa;
+      hf.tQ = GF64;
     }
     return XKV_OK;
   };
-  rc = fp64_sweeps(p.fp64_iters);
-  if (rc) return rc;
+  // 1.-2. Per half: Gram of every side (batched, at most kMaxPtrs layer pointers per launch),
+  // its trace (total energy), then the block subspace iteration: float32 sweeps on a float32
+  // copy of C, then float64 sweeps (CholeskyQR, CholeskyQR2 on the last sweep of a round).
+  auto pre_work = [&](Half& hf) -> int {
+    for (int s0 = hf.s0; s0 < hf.s0 + hf.cnt; s0 += per) {
+      const int cnt = std::min(per, hf.s0 + hf.cnt - s0);
+      PtrTable tab{};
+      for (int s = 0; s < cnt; ++s)
+        for (int l = 0; l < p.G; ++l) tab.p[s * p.G + l] = sides[s0 + s].layers[l];
+      double* C = w.C64 + s0 * nn;
+      float* C32 = w.C32 ? w.C32 + s0 * nn : nullptr;
+      if (p.bf16) XKV_K(launch_gram_bf16(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
+      else XKV_K(launch_gram_f32(tab, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, C, C32, st));
+    }
+    XKV_K(launch_trace(hf.w.C64, nn, n, hf.cnt, hf.w.trace, st));
+    XKV_K(launch_init_q(hf.w.Q32, n, kb, nk, hf.cnt, desc->seed, st));
+    for (int it = 0; it < p.fp32_iters; ++it) {
+      GemmDesc cq = gdesc(n, kb, n, 0, 0, GF32, GF32, GF32, hf.w.C32, n, nn, hf.w.Q32, kb, nk, hf.w.Y32, kb, nk, 1.0,
+                          0.0, hf.cnt);
+      cq.acc = GF32;   // float32 matrix cores for the float32 iterations
+      XKV_K(gemm(cq, st));
+      int e = cholqr(p, hf.w, hf.cnt, hf.w.Y32, GF32, hf.w.Q32, GF32, st);
+      if (e) return e;
+    }
+    return fp64_sweeps(hf, p.fp64_iters);
+  };
   int total_iters = p.fp32_iters + p.fp64_iters;
 
   // Pinned staging: H (down), Z and Ritz values (up), residual norms and info (down).
@@ -393,51 +449,98 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   std::vector<double> est(S, 0.0), relgap(S, 0.0);
   int rounds = 0;
   bool converged = false;
-  const int nthr = std::max(1, std::min(S, ctx->host_threads));
+  // Host memory of the eigensolves, kept in the context: per side the value phase's state
+  // (also the working memory of the first half of the vectors) and the working memory of the
+  // second half of the vectors.
+  if ((int)ctx->eig_side.size() < 2 * S) ctx->eig_side.resize(2 * S, xkv_eigh_scratch{});
+  // The Rayleigh-Ritz matrix H = Q^T C Q of a half (and its info), copied down, then an event.
+  auto rr_matrix = [&](Half& hf, int h, bool first) -> int {
+    XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, GF64, GF64, hf.w.C64, n, nn, hf.Qa, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
+                     hf.cnt), st));
+    XKV_K(gemm(gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, hf.Qa, kb, nk, hf.Ya, kb, nk, hf.w.H, kb, kk, 1.0, 0.0,
+                     hf.cnt), st));
+    XKV_HIP(hipMemcpyAsync(hH + (size_t)hf.s0 * kk, hf.w.H, (size_t)hf.cnt * kk * sizeof(double),
+                           hipMemcpyDeviceToHost, st));
+    XKV_HIP(hipMemcpyAsync(hinfo + hf.s0, hf.w.info, hf.cnt * sizeof(int), hipMemcpyDeviceToHost, st));
+    if (first)
+      XKV_HIP(hipMemcpyAsync(hTrace + hf.s0, hf.w.trace, hf.cnt * sizeof(double), hipMemcpyDeviceToHost, st));
+    XKV_HIP(hipEventRecord(ctx->half_done[h], st));
+    return XKV_OK;
+  };
+  // The host eigensolves of a half: the value phase one thread per side, then the vector
+  // phase in two column ranges per side, all on at most ctx->host_threads threads.
+  auto solve_half = [&](const Half& hf) -> int {
+    std::vector<int> erc(hf.cnt, 0);
+    const int nthr_v = std::max(1, std::min(hf.cnt, ctx->host_threads));
+    const int nthr_z = std::max(1, std::min(2 * hf.cnt, ctx->host_threads));
+    auto run = [&](int nthr, int ntask, auto&& task) {
+      if (nthr == 1) {
+        for (int t = 0; t < ntask; ++t) task(t);
+        return;
+      }
+      std::vector<std::thread> pool;
+      for (int t0 = 0; t0 < nthr; ++t0)
+        pool.emplace_back([&, t0]() {
+          for (int t = t0; t < ntask; t += nthr) task(t);
+        });
+      for (auto& th : pool) th.join();
+    };
+    run(nthr_v, hf.cnt, [&](int i) {
+      const int s = hf.s0 + i;
+      erc[i] = xkv_eigh_values(kb, hH + (size_t)s * kk, r, evals[s].data(), &ctx->eig_side[2 * s]);
+    });
+    for (int i = 0; i < hf.cnt; ++i)
+      if (erc[i]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + i, erc[i]);
+    std::vector<int> zrc(2 * hf.cnt, 0);
+    run(nthr_z, 2 * hf.cnt, [&](int t) {
+      const int i = t / 2, half = t % 2, s = hf.s0 + i;
+      zrc[t] = xkv_eigh_vectors(&ctx->eig_side[2 * s], half ? r / 2 : 0, half ? r : r / 2, hZ + (size_t)s * kb * r,
+                                &ctx->eig_side[2 * s + half]);
+    });
+    for (int t = 0; t < 2 * hf.cnt; ++t)
+      if (zrc[t]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + t / 2, zrc[t]);
+    for (int i = 0; i < hf.cnt; ++i)
+      std::memcpy(hTheta + (size_t)(hf.s0 + i) * r, evals[hf.s0 + i].data(), r * sizeof(double));
+    return XKV_OK;
+  };
+  // V_r = Q Z and the residual of every Ritz pair of a half.
+  auto post_work = [&](Half& hf) -> int {
+    XKV_HIP(hipMemcpyAsync(hf.w.Z, hZ + (size_t)hf.s0 * kb * r, (size_t)hf.cnt * kb * r * sizeof(double),
+                           hipMemcpyHostToDevice, st));
+    XKV_HIP(hipMemcpyAsync(hf.w.theta, hTheta + (size_t)hf.s0 * r, (size_t)hf.cnt * r * sizeof(double),
+                           hipMemcpyHostToDevice, st));
+    XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, hf.Qa, kb, nk, hf.w.Z, r, (long)kb * r, hf.w.Vr, r,
+                     (long)n * r, 1.0, 0.0, hf.cnt), st));
+    XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, hf.Ya, kb, nk, hf.w.Z, r, (long)kb * r, hf.w.YZ, r,
+                     (long)n * r, 1.0, 0.0, hf.cnt), st));
+    XKV_K(launch_ritz_residual(hf.w.YZ, hf.w.Vr, hf.w.theta, n, r, hf.w.res2, hf.cnt, st));
+    XKV_HIP(hipMemcpyAsync(hRes + (size_t)hf.s0 * r, hf.w.res2, (size_t)hf.cnt * r * sizeof(double),
+                           hipMemcpyDeviceToHost, st));
+    return XKV_OK;
+  };
+  for (int h = 0; h < nh; ++h) {
+    rc = pre_work(hv[h]);
+    if (rc) return rc;
+    rc = rr_matrix(hv[h], h, true);
+    if (rc) return rc;
+  }
   for (;;) {
     ++rounds;
-    XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, GF64, GF64, w.C64, n, nn, Qa, kb, nk, Ya, kb, nk, 1.0, 0.0, S), st));
-    XKV_K(gemm(gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, Qa, kb, nk, Ya, kb, nk, w.H, kb, kk, 1.0, 0.0, S), st));
-    XKV_HIP(hipMemcpyAsync(hH, w.H, (size_t)S * kk * sizeof(double), hipMemcpyDeviceToHost, st));
-    XKV_HIP(hipMemcpyAsync(hinfo, w.info, S * sizeof(int), hipMemcpyDeviceToHost, st));
-    if (rounds == 1) XKV_HIP(hipMemcpyAsync(hTrace, w.trace, S * sizeof(double), hipMemcpyDeviceToHost, st));
-    XKV_HIP(hipStreamSynchronize(st));
-    for (int s = 0; s < S; ++s)
-      if (hinfo[s]) return fail(XKV_ENUMERIC, "compress: Cholesky breakdown on side %d (rank of X below %d?)", s, kb);
-    for (size_t i = 0; i < (size_t)S * kk; ++i)
-      if (!std::isfinite(hH[i])) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix");
-
-    // Host eigensolves, one thread per side (bounded by ctx->host_threads).
-    std::vector<int> erc(S, 0);
-    if ((int)ctx->eig_scratch.size() < nthr) ctx->eig_scratch.resize(nthr, xkv_eigh_scratch{});
-    auto worker = [&](int t0) {
-      for (int s = t0; s < S; s += nthr)
-        erc[s] = xkv_eigh_desc_scratch(kb, hH + (size_t)s * kk, r, evals[s].data(), hZ + (size_t)s * kb * r,
-                                       &ctx->eig_scratch[t0]);
-    };
-    if (nthr == 1) {
-      worker(0);
-    } else {
-      std::vector<std::thread> pool;
-      for (int t = 0; t < nthr; ++t) pool.emplace_back(worker, t);
-      for (auto& th : pool) th.join();
+    for (int h = 0; h < nh; ++h) {
+      Half& hf = hv[h];
+      XKV_HIP(hipEventSynchronize(ctx->half_done[h]));   // H of this half is on the host
+      for (int i = 0; i < hf.cnt; ++i)
+        if (hinfo[hf.s0 + i])
+          return fail(XKV_ENUMERIC, "compress: Cholesky breakdown on side %d (rank of X below %d?)", hf.s0 + i, kb);
+      for (size_t i = (size_t)hf.s0 * kk; i < (size_t)(hf.s0 + hf.cnt) * kk; ++i)
+        if (!std::isfinite(hH[i])) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix");
+      rc = solve_half(hf);
+      if (rc) return rc;
+      rc = post_work(hf);
+      if (rc) return rc;
     }
-    for (int s = 0; s < S; ++s) {
-      if (erc[s]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", s, erc[s]);
-      std::memcpy(hTheta + (size_t)s * r, evals[s].data(), r * sizeof(double));
-    }
-    XKV_HIP(hipMemcpyAsync(w.Z, hZ, (size_t)S * kb * r * sizeof(double), hipMemcpyHostToDevice, st));
-    XKV_HIP(hipMemcpyAsync(w.theta, hTheta, (size_t)S * r * sizeof(double), hipMemcpyHostToDevice, st));
     XKV_HIP(hipEventRecord(ctx->upload_done, st));
     ctx->upload_pending = true;
-
-    // V_r = Q Z and the residual of every Ritz pair.
-    XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, Qa, kb, nk, w.Z, r, (long)kb * r, w.Vr, r, (long)n * r, 1.0,
-                     0.0, S), st));
-    XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, Ya, kb, nk, w.Z, r, (long)kb * r, w.YZ, r, (long)n * r, 1.0,
-                     0.0, S), st));
-    XKV_K(launch_ritz_residual(w.YZ, w.Vr, w.theta, n, r, w.res2, S, st));
-    XKV_HIP(hipMemcpyAsync(hRes, w.res2, (size_t)S * r * sizeof(double), hipMemcpyDeviceToHost, st));
     XKV_HIP(hipStreamSynchronize(st));
     ctx->upload_pending = false;
     converged = true;
@@ -452,8 +555,12 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       if (!(est[s] <= tol)) converged = false;
     }
     if (converged || rounds >= max_rounds) break;
-    rc = fp64_sweeps(p.fp32_iters + p.fp64_iters);
-    if (rc) return rc;
+    for (int h = 0; h < nh; ++h) {
+      rc = fp64_sweeps(hv[h], p.fp32_iters + p.fp64_iters);
+      if (rc) return rc;
+      rc = rr_matrix(hv[h], h, false);
+      if (rc) return rc;
+    }
     total_iters += p.fp32_iters + p.fp64_iters;
   }
   for (int s = 0; s < S; ++s) {

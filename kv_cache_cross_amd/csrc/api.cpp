@@ -524,6 +524,34 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     rc = rr_matrix(hv[h], h, true);
     if (rc) return rc;
   }
+  // Landmarks of the sides that ask for them: they depend on the keys alone, so they go
+  // behind the Rayleigh-Ritz products and run while the host solves.
+  if (any_lm) {
+    PtrTable lay{}, lmo{};
+    int cnt = 0;
+    auto flush = [&]() -> int {
+      if (cnt == 0) return XKV_OK;
+      XKV_K(launch_landmarks(lay, cnt, p.G, sides[0].ld_layer, p.T, desc->n_kv_heads, desc->head_dim, desc->chunk,
+                             desc->rope_theta, lmo, p.bf16, st));
+      cnt = 0;
+      return XKV_OK;
+    };
+    const long per_layer = (long)desc->n_kv_heads * (p.T / desc->chunk) * desc->head_dim * (p.bf16 ? 2 : 4);
+    for (int s = 0; s < S; ++s) {
+      if (!sides[s].landmarks) continue;
+      if ((cnt + 1) * p.G > kMaxPtrs) {
+        rc = flush();
+        if (rc) return rc;
+      }
+      for (int l = 0; l < p.G; ++l) {
+        lay.p[cnt * p.G + l] = sides[s].layers[l];
+        lmo.p[cnt * p.G + l] = (char*)sides[s].landmarks + l * per_layer;
+      }
+      ++cnt;
+    }
+    rc = flush();
+    if (rc) return rc;
+  }
   for (;;) {
     ++rounds;
     for (int h = 0; h < nh; ++h) {
@@ -595,33 +623,6 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       XKV_K(launch_project_bf16(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const uint16_t*)VrT, nr, r, aout, st));
     else
       XKV_K(launch_project_f32(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const float*)VrT, nr, r, aout, st));
-  }
-  // 5. Landmarks of the sides that ask for them.
-  if (any_lm) {
-    PtrTable lay{}, lmo{};
-    int cnt = 0;
-    auto flush = [&]() -> int {
-      if (cnt == 0) return XKV_OK;
-      XKV_K(launch_landmarks(lay, cnt, p.G, sides[0].ld_layer, p.T, desc->n_kv_heads, desc->head_dim, desc->chunk,
-                             desc->rope_theta, lmo, p.bf16, st));
-      cnt = 0;
-      return XKV_OK;
-    };
-    const long per_layer = (long)desc->n_kv_heads * (p.T / desc->chunk) * desc->head_dim * (p.bf16 ? 2 : 4);
-    for (int s = 0; s < S; ++s) {
-      if (!sides[s].landmarks) continue;
-      if ((cnt + 1) * p.G > kMaxPtrs) {
-        rc = flush();
-        if (rc) return rc;
-      }
-      for (int l = 0; l < p.G; ++l) {
-        lay.p[cnt * p.G + l] = sides[s].layers[l];
-        lmo.p[cnt * p.G + l] = (char*)sides[s].landmarks + l * per_layer;
-      }
-      ++cnt;
-    }
-    rc = flush();
-    if (rc) return rc;
   }
   if (!converged)
     return fail(XKV_ENOTCONV, "compress: subspace error estimate above %.1e after %d rounds (%d sweeps); "

@@ -189,7 +189,10 @@ static int qr_step(double* d, double* e, rotlog* log, int l, int m) {
   double x = d[l] - shift;
   double z = e[l];
   for (int k = l; k < m; ++k) {
-    const double r = hypot(x, z);
+    /* sqrt(x^2 + z^2) where neither square can overflow or lose the result to underflow;
+     * hypot (slower, scaled) otherwise */
+    double r = sqrt(x * x + z * z);
+    if (!(r > 1e-150 && r < 1e150)) r = hypot(x, z);
     double c = 1.0, s = 0.0;
     if (r != 0.0) { c = x / r; s = z / r; }
     if (k > l) e[k - 1] = r;

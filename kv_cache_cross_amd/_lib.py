@@ -197,8 +197,13 @@ def compress_sides(ctx: Context, desc: CompressDesc, sides, ws: torch.Tensor, st
         arr[s].eigvals = evals[s].ctypes.data_as(C.POINTER(C.c_double))
         arr[s].Vr64 = sd["Vr64"].data_ptr() if sd.get("Vr64") is not None else None
         arr[s].stats = stats[s].ctypes.data_as(C.POINTER(C.c_double))
-    _check(lib().xkv_compress_sides(ctx.handle, C.byref(desc), S, arr, _ptr(ws), ws.numel() * ws.element_size(),
-                                    _stream(stream)))
+    rc = lib().xkv_compress_sides(ctx.handle, C.byref(desc), S, arr, _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    if rc != XKV_OK:
+        err = XkvError(rc, lib().xkv_last_error().decode())
+        if rc == XKV_ENOTCONV:   # every output is written; the caller may still use them
+            err.evals, err.stats = evals, stats
+        raise err
     return evals, stats
 
 

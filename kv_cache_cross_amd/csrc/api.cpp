@@ -433,6 +433,20 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     XKV_HIP(hipHostMalloc((void**)&ctx->pin, need_pin * sizeof(double), hipHostMallocDefault));
     ctx->pin_doubles = need_pin;
   }
+  // From the first copy to or from the pinned staging on, an early error return (a
+  // Cholesky breakdown, a failed host solve, a launch error) can leave such copies in
+  // flight on `st`; the guard then marks them with upload_done, so that the next call on
+  // this context waits for them before its host writes to the staging.
+  struct PinGuard {
+    xkv_ctx c;
+    hipStream_t s;
+    bool armed;
+    ~PinGuard() {
+      if (!armed) return;
+      if (hipEventRecord(c->upload_done, s) == hipSuccess) c->upload_pending = true;
+      else (void)hipStreamSynchronize(s);
+    }
+  } pin_guard{ctx, st, true};
   double* hH = ctx->pin;
   double* hZ = hH + (size_t)S * kk;
   double* hTheta = hZ + (size_t)S * kb * r;
@@ -440,9 +454,9 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   double* hTrace = hRes + (size_t)S * r;
   int* hinfo = (int*)(hTrace + S);
 
-  // 3. Rayleigh-Ritz rounds.  After each, the Ritz residual R = (C Q) Z - V_r diag(theta)
-  //    bounds the subspace error: ||sin angle(V_r, exact)||_F <= ||R||_F / (theta_r - lambda_{r+1}),
-  //    with lambda_{r+1} estimated by theta_{r+1}.  Unconverged rounds add float64 sweeps.
+  // 3. Rayleigh-Ritz rounds.  After each, the Ritz residuals R = (C Q) Z - V_r diag(theta)
+  //    bound the subspace error (per-pair sin-theta bounds, below).  Unconverged rounds add
+  //    float64 sweeps.
   const double tol = desc->tol > 0 ? desc->tol : 1e-4;
   const int max_rounds = desc->max_rounds > 0 ? desc->max_rounds : 8;
   std::vector<std::vector<double>> evals(S, std::vector<double>(kb));
@@ -573,13 +587,23 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     ctx->upload_pending = false;
     converged = true;
     for (int s = 0; s < S; ++s) {
-      double r2 = 0.0;
-      for (int i = 0; i < r; ++i) r2 += hRes[(size_t)s * r + i];
+      // Each Ritz pair (theta_i, v_i) with residual r_i = C v_i - theta_i v_i has
+      // ||(I - P_exact) v_i|| <= ||r_i|| / (theta_i - lambda_r+1) (P_exact the spectral
+      // projector of the r largest eigenvalues; lambda_r+1 estimated by the Ritz value
+      // theta_r+1), so ||P - P_exact||_F = sqrt(2) ||(I - P_exact) V_r||_F is bounded by
+      // sqrt(2 sum_i ||r_i||^2 / (theta_i - theta_r+1)^2).
       const double th_r = evals[s][r - 1];
-      const double gap = (r < kb) ? th_r - evals[s][r] : th_r;
+      const double th_next = r < kb ? evals[s][r] : 0.0;
+      const double gap = th_r - th_next;
       relgap[s] = th_r > 0 ? gap / th_r : 0.0;
+      double w2 = 0.0;
+      bool gap_ok = gap > 0;
+      for (int i = 0; i < r && gap_ok; ++i) {
+        const double gi = evals[s][i] - th_next;
+        w2 += hRes[(size_t)s * r + i] / (gi * gi);
+      }
       // A block that spans the whole space gives the exact eigenvectors.
-      est[s] = (kb == n) ? 0.0 : (gap > 0 ? std::sqrt(2.0 * r2) / gap : INFINITY);
+      est[s] = (kb == n) ? 0.0 : (gap_ok ? std::sqrt(2.0 * w2) : INFINITY);
       if (!(est[s] <= tol)) converged = false;
     }
     if (converged || rounds >= max_rounds) break;
@@ -591,6 +615,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     }
     total_iters += p.fp32_iters + p.fp64_iters;
   }
+  pin_guard.armed = false;   // the last round ended with a stream synchronisation
   for (int s = 0; s < S; ++s) {
     if (sides[s].eigvals) std::memcpy(sides[s].eigvals, evals[s].data(), r * sizeof(double));
     if (sides[s].stats) {

@@ -16,9 +16,15 @@
 //     column that v_mfma_f32_32x32x16_bf16 takes for both operands;
 //   * 8 waves in a 2 x 4 grid, 128 x 64 outputs per wave (4 x 2 MFMA tiles), so an
 //     operand read from LDS feeds 2 or 4 MFMAs;
-//   * float32 MFMA sums cover a segment of 8192 tokens; at each segment end they are
+//   * float32 MFMA sums cover a segment of 1024 tokens; at each segment end they are
 //     added into the float64 output tile in memory (the tile belongs to this
-//     workgroup alone), so a rounding is relative to one segment's partial sum;
+//     workgroup alone).  The segment is short because the matrix cores' float32
+//     accumulation is biased toward zero: terms much smaller than the largest one of
+//     an accumulation lose their low bits (a probe: the products 1 and 0.75 ulp(1) in
+//     one instruction sum to 1, not 1 + ulp), so the relative error of a partial grows
+//     in proportion to its length rather than its square root.  Measured at the 16k
+//     Llama-shaped group (n = 4096, r = 512), the projector's distance to the float64
+//     one is 2.7e-3 with 8192-token segments, 6.9e-4 with 2048, 3.3e-4 with 1024;
 //   * the last segment also writes the mirror tile and the float32 copy used by the
 //     float32 subspace iterations.
 #include "xkv_common.h"
@@ -31,7 +37,7 @@ constexpr int GT = 256;                      // output tile edge
 constexpr int TS = 32;                       // tokens per slab
 constexpr int NST = 4;                       // LDS stages
 constexpr int STAGE = 2 * 8 * 2 * 1024;      // bytes per stage: [op][32-col block][16-token half][16][32]
-constexpr int SEG = 8192;                    // tokens per float32 partial
+constexpr int SEG = 1024;                    // tokens per float32 partial
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 

@@ -17,12 +17,14 @@ def dtype_code(dt: torch.dtype) -> int:
 def compress(ctx: L.Context, sides, *, r: int, n_kv_heads: int, head_dim: int, chunk: int = 8,
              rope_theta: float = 10000.0, landmarks=None, oversample: int = -1, fp32_iters: int = 3,
              fp64_iters: int = 2, seed: int = 0, stream=None, ws: torch.Tensor | None = None,
-             keep_vr64: bool = False, tol: float = 0.0, max_rounds: int = 0):
+             keep_vr64: bool = False, tol: float = 0.0, max_rounds: int = 0, allow_notconv: bool = False):
     """Factor every group side in ``sides`` (a list of lists of G layer tensors, T x d_kv).
 
     ``landmarks``: list of bools, one per side (True for key sides).  Returns a list of
     dicts with 'A' (T x r), 'Bt' (n x r, Bt = V_r), 'landmarks' (G x H_kv x T/chunk x d or
     None), 'Vr64' (float64 V_r when ``keep_vr64``) and 'eigvals' (numpy, r leading Ritz values).
+    With ``allow_notconv`` an XKV_ENOTCONV return (every output written, the error estimate
+    above ``tol``) is not raised; each side's stats then carry converged=False.
     """
     S = len(sides)
     G = len(sides[0])
@@ -46,10 +48,18 @@ def compress(ctx: L.Context, sides, *, r: int, n_kv_heads: int, head_dim: int, c
              "Vr64": torch.empty((n, r), dtype=torch.float64, device=dev) if keep_vr64 else None}
         outs.append(o)
         specs.append({"layers": sides[s], **o})
-    evals, stats = L.compress_sides(ctx, desc, specs, ws, stream)
+    converged = True
+    try:
+        evals, stats = L.compress_sides(ctx, desc, specs, ws, stream)
+    except L.XkvError as e:
+        if not (allow_notconv and e.code == L.XKV_ENOTCONV):
+            raise
+        evals, stats = e.evals, e.stats
+        converged = False
     for o, e, st in zip(outs, evals, stats):
         o["eigvals"] = e
-        o["stats"] = dict(err_est=st[0], rel_gap=st[1], sweeps=int(st[2]), rounds=int(st[3]), energy=st[4])
+        o["stats"] = dict(err_est=st[0], rel_gap=st[1], sweeps=int(st[2]), rounds=int(st[3]), energy=st[4],
+                          converged=converged)
     return outs
 
 

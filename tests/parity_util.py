@@ -57,3 +57,27 @@ def attention_errors(got: np.ndarray, ref: np.ndarray):
 
 def tail_rows(T: int, n_sink: int, n_local: int):
     return list(range(n_sink)) + list(range(T - n_local, T))
+
+
+def check_selection_banded(gpu_sel, scores, k: int, band):
+    """The GPU's chunk set must be a top-k of the oracle's scores after some perturbation
+    of each score s_c by at most band[c]: with S the GPU's set, min over S of (s_c + band_c)
+    must reach max over the other candidates of (s_c - band_c).  Returns the number of
+    chunks in S outside the oracle's own top-k."""
+    gpu = [int(c) for c in np.asarray(gpu_sel).tolist() if c >= 0]
+    s = np.asarray(scores, dtype=np.float64)
+    n = len(s)
+    keff = min(k, n)
+    assert len(gpu) == keff, f"selected {len(gpu)} chunks, expected {keff}"
+    assert len(set(gpu)) == keff and gpu == sorted(gpu), "chunk ids not distinct and ascending"
+    if keff == 0 or keff == n:
+        assert gpu == list(range(keff))
+        return 0
+    band = np.broadcast_to(np.asarray(band, dtype=np.float64), s.shape)
+    inside = np.zeros(n, dtype=bool)
+    inside[gpu] = True
+    lo_in = np.min(s[inside] + band[inside])
+    hi_out = np.max(s[~inside] - band[~inside])
+    assert lo_in >= hi_out, f"selection not a top-{keff} within the band ({lo_in:.6g} < {hi_out:.6g})"
+    ref = set(np.lexsort((np.arange(n), -s))[:keff].tolist())
+    return len(set(gpu) - ref)

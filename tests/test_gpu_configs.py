@@ -1,0 +1,424 @@
+"""Every workload at its own size against the float64 oracle.
+
+Compression parity compares the GPU's factorisation of a group side with the
+oracle's dense eigensolve of the same X (the top-r right singular vectors, taken
+as the top-r eigenvectors of the uncentred Gram, KV-CoRE section 2.A; their
+projector is the Eckart-Young optimum, KQ-SVD section 3.3):
+
+* ||P_gpu - P_ref||_F <= 1e-3 (P = V_r V_r^T, from the GPU's float64 V_r),
+* |rel_err_gpu - rel_err_ref| <= 1e-4, rel_err = ||X - A B||_F / ||X||_F with the
+  GPU's stored (bf16) A and B,
+
+on the 16k Llama-shaped group (K and V), one group of the 64k workload (group 1,
+whose latent basis shares 70 % of its columns with group 0's), one group of the
+122880-token Qwen-shaped workload, and one sequence of the batch-8 workload at
+G = 1, 2, 4, 8.  Where r lies past the generator's latent rank (G = 8: r = 1024 >
+768) the r-th eigenvalue sits inside the noise bulk, the projector is not a
+well-posed target and only the reconstruction error and attention are graded.
+
+End-to-end decode (16k workload, and the batch-8 G = 8 sequence): each side runs
+its own compression, then decodes.  The GPU attends over its own A, B and landmarks
+(bf16); the oracle over its own factors and landmarks rounded to bf16, the storage
+precision both sides share.  The GPU's chunk set must be a top-k of the oracle's
+scores after moving each score by at most its band: 5e-4 (so two chunks within 1e-3
+of each other may trade places, the near-tie rule) plus the score change that
+one-unit-in-the-last-place differences of the stored landmarks could cause where the
+exact mean lies within float32 rounding of a bf16 rounding boundary (the GPU forms
+the mean in float32, the oracle in float64, and only such elements can round
+differently).
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_cross_amd as xk
+from kv_cache_cross_amd import _lib as L
+import oracle
+from parity_util import (ATT_ABS_BF16, ATT_REL_BF16, NEAR_TIE, PROJ_TOL, RECON_TOL, attention_errors,
+                         check_selection_banded, f64, projector_distance, tail_rows)
+from synth import make_workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = xk.Context(0)
+    yield c
+    c.close()
+
+
+def rel_error_rows(X, A, B, block=8192):
+    """||X - A B||_F / ||X||_F, float64, row blocks at a time."""
+    num = den = 0.0
+    for t0 in range(0, X.shape[0], block):
+        Xb = X[t0:t0 + block]
+        R = Xb - A[t0:t0 + block] @ B
+        num += float(np.sum(R * R))
+        den += float(np.sum(Xb * Xb))
+    return float(np.sqrt(num / den))
+
+
+def bf16_round(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+
+
+def reconstruction_errors(X, Vg, A_g, B_g, ref):
+    """Relative reconstruction errors of one side, each compared at the same precision:
+    the subspace itself, ||X - X V V^T|| / ||X|| with the GPU's float64 V_r against the
+    oracle's rel_err; and the stored factors, the GPU's bf16 A and B against the
+    oracle's own A and B rounded to bf16 (the storage precision both sides use, which
+    adds ~2e-3 of ||X|| in quadrature).  Returns (gpu_vr, ref, gpu_stored, ref_stored)."""
+    gpu_vr = rel_error_rows(X, X @ Vg, Vg.T)
+    if A_g.dtype == torch.float32:
+        stored = rel_error_rows(X, f64(A_g), f64(B_g).T)
+        return gpu_vr, ref["rel_err"], stored, ref["rel_err"]
+    ref_stored = rel_error_rows(X, f64(bf16_round(ref["A"])), f64(bf16_round(ref["B"])))
+    return gpu_vr, ref["rel_err"], rel_error_rows(X, f64(A_g), f64(B_g).T), ref_stored
+
+
+def compress_vs_oracle(ctx, label, sides, r, *, n_kv_heads, head_dim, chunk, landmarks, projector=True,
+                       max_rounds=0, allow_notconv=False):
+    """Compress `sides` in one call and compare each with the oracle: the projector
+    (unless `projector` is False) and both reconstruction errors of
+    reconstruction_errors within 1e-4.  Returns the GPU outputs and the oracle results
+    (without X)."""
+    t0 = time.time()
+    outs = xk.compress(ctx, sides, r=r, n_kv_heads=n_kv_heads, head_dim=head_dim, chunk=chunk,
+                       landmarks=landmarks, keep_vr64=True, max_rounds=max_rounds, allow_notconv=allow_notconv)
+    torch.cuda.synchronize()
+    log(f"{label}: GPU compression of {len(sides)} sides in {time.time() - t0:.2f} s")
+    refs = []
+    for s, (layers, o) in enumerate(zip(sides, outs)):
+        t0 = time.time()
+        ref = oracle.compress_group([f64(x) for x in layers], r)
+        t_or = time.time() - t0
+        Vg = f64(o["Vr64"])
+        dP = projector_distance(Vg, ref["Vr"])
+        e_vr, e_ref, e_st, e_st_ref = reconstruction_errors(ref["X"], Vg, o["A"], o["Bt"], ref)
+        lam = ref["eigvals"][:r]
+        lam_err = float(np.max(np.abs(o["eigvals"] - lam) / lam))
+        gap = (ref["eigvals"][r - 1] - ref["eigvals"][r]) / ref["eigvals"][r - 1] if r < len(ref["eigvals"]) else 1.0
+        st = o["stats"]
+        log(f"  {label} side {s}: ||dP||_F={dP:.2e} (err_est {st['err_est']:.2e}, rounds {st['rounds']}, "
+            f"sweeps {st['sweeps']}, converged {st['converged']}) rel_err V_r gpu={e_vr:.6f} ref={e_ref:.6f} "
+            f"(diff {abs(e_vr - e_ref):.1e}); stored gpu={e_st:.6f} ref={e_st_ref:.6f} (diff {abs(e_st - e_st_ref):.1e}); "
+            f"eig rel {lam_err:.1e} rel gap {gap:.1e} oracle {t_or:.1f} s")
+        if projector:
+            assert dP <= PROJ_TOL, (label, s, dP)
+        assert abs(e_vr - e_ref) <= RECON_TOL, (label, s, e_vr, e_ref)
+        assert abs(e_st - e_st_ref) <= RECON_TOL, (label, s, e_st, e_st_ref)
+        del ref["X"]
+        ref["dP"] = dP
+        refs.append(ref)
+    return outs, refs
+
+
+# ----------------------------------------------------------------------------- compression
+def test_compress_llama64k_group_vs_oracle(ctx):
+    # One group of the 64k Llama-shaped workload (n = 4096, r = 512, T = 65536): the
+    # configuration with the smallest relative gap (lambda_r - lambda_r+1) / lambda_r.
+    wl = make_workload("llama64k", device=DEV)
+    c = wl.cfg
+    g = 1
+    sides = [wl.group_kv(0, "K", g), wl.group_kv(0, "V", g)]
+    outs, refs = compress_vs_oracle(ctx, "llama64k group 1", sides, c.rank, n_kv_heads=c.n_kv_heads,
+                                    head_dim=c.head_dim, chunk=c.chunk, landmarks=[True, False])
+    del outs, refs, sides
+    torch.cuda.empty_cache()
+
+
+def test_compress_qwen122k_group_vs_oracle(ctx):
+    # One group of the 122880-token Qwen-shaped workload (n = 2048, r = 256; 15 Gram
+    # segments of 8192 tokens).
+    wl = make_workload("qwen122k", device=DEV)
+    c = wl.cfg
+    sides = [wl.group_kv(0, "K", 3), wl.group_kv(0, "V", 3)]
+    outs, refs = compress_vs_oracle(ctx, "qwen122k group 3", sides, c.rank, n_kv_heads=c.n_kv_heads,
+                                    head_dim=c.head_dim, chunk=c.chunk, landmarks=[True, False])
+    del outs, refs, sides
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_compress_batch8_sequence_vs_oracle(ctx, G):
+    # One sequence (the last of the batch) of the batch-8 workload at T = 32768, group 0,
+    # key side: n = 1024 G, r = 128 G.
+    wl = make_workload(f"batch8_g{G}", device=DEV)
+    c = wl.cfg
+    b = c.batch - 1
+    outs, refs = compress_vs_oracle(ctx, f"batch8 G={G} sequence {b}", [wl.group_kv(b, "K", 0)], c.rank,
+                                    n_kv_heads=c.n_kv_heads, head_dim=c.head_dim, chunk=c.chunk, landmarks=[False])
+    del outs, refs
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- end to end
+def landmark_slack(lm_exact, q_rot, grp, scale, tol=2.0 ** -17):
+    """Per KV head and chunk, the largest change of the chunk's score that can come from
+    the two sides rounding a landmark element to different bf16 values.  The GPU forms
+    each mean in float32 (eight rotated products and sums, error well under 2^-17 for
+    keys of these magnitudes), the oracle in float64; both round to nearest even.  They
+    can differ, by one unit in the last place, only where the exact mean lies within
+    `tol` of a rounding boundary (a midpoint between neighbouring bf16 values).  Such an
+    element i adds scale * |sum_j q_j,i| * ulp_i to the chunk's slack."""
+    H, C, d = lm_exact.shape
+    a = np.abs(lm_exact)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = 2.0 ** (e - 7)                        # spacing of bf16 values in a's binade
+    frac = a / ulp - np.floor(a / ulp)
+    near = (np.abs(frac - 0.5) * ulp <= tol) & (a > 0)
+    out = np.zeros((H, C))
+    for h in range(H):
+        qs = np.abs(q_rot[h * grp:(h + 1) * grp].sum(axis=0))
+        out[h] = scale * (near[h] * ulp[h]) @ qs
+    return out
+
+
+def _e2e_decode(ctx, wl, b, group, layers_in_group, steps_checked, n_steps, ck_ck):
+    """GPU: decode n_steps steps through the group's layers over its own compression
+    (xkv_sr_decode_layers, appends), and compare the sampled steps with the oracle's
+    decode over the oracle's own compression.  ck_ck = (gpu_outs, oracle_refs) for the
+    K and V sides of the group."""
+    c = wl.cfg
+    (gK, gV), (rK, rV) = ck_ck
+    d_kv, T, H, d, Hq = c.d_kv, c.T, c.n_kv_heads, c.head_dim, c.n_q_heads
+    grp = Hq // H
+    scale = 1.0 / np.sqrt(d)
+    G = c.group
+    rows = tail_rows(T, c.n_sink, c.n_local)
+    dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk, top_k=c.top_k,
+                          n_sink=c.n_sink, n_local=c.n_local, r_k=c.rank, r_v=c.rank, dtype=c.torch_dtype,
+                          device=DEV, rope_theta=c.rope_theta, max_gen=n_steps)
+    per = {}
+    for li in layers_in_group:
+        l = group * G + li
+        K, V = wl.layer_kv(b, "K", l), wl.layer_kv(b, "V", l)
+        k_tail = torch.zeros((len(rows) + n_steps, d_kv), dtype=c.torch_dtype, device=DEV)
+        v_tail = torch.zeros_like(k_tail)
+        k_tail[:len(rows)] = K[rows]
+        v_tail[:len(rows)] = V[rows]
+        lm_ref = oracle.landmarks(f64(K), H, d, c.chunk, c.rope_theta)
+        per[li] = dict(k_tail=k_tail, v_tail=v_tail, k_exact={t: f64(K[t]) for t in rows},
+                       v_exact={t: f64(V[t]) for t in rows}, lm_ref=lm_ref,
+                       lm_ref_b=f64(bf16_round(lm_ref)),
+                       A_k=f64(bf16_round(rK["A"])), B_k=f64(bf16_round(rK["B"][:, li * d_kv:(li + 1) * d_kv])),
+                       A_v=f64(bf16_round(rV["A"])), B_v=f64(bf16_round(rV["B"][:, li * d_kv:(li + 1) * d_kv])))
+        del K, V
+    out = torch.empty((len(layers_in_group), Hq, d), dtype=torch.float32, device=DEV)
+    sel = torch.full((len(layers_in_group), H, c.top_k), -1, dtype=torch.int32, device=DEV)
+    worst = [0.0, 0.0, 0]
+    for s in range(n_steps):
+        arr, keep, qs = [], [], {}
+        for i, li in enumerate(layers_in_group):
+            l = group * G + li
+            x = per[li]
+            qs[li] = wl.query(b, l, s)
+            kn, vn = wl.new_token(b, "K", l, s), wl.new_token(b, "V", l, s)
+            x["k_exact"][T + s], x["v_exact"][T + s] = f64(kn), f64(vn)
+            a = dec.args(n_gen=s + 1, q=qs[li], A_k=gK["A"], Bt_k=gK["Bt"][li * d_kv:(li + 1) * d_kv], A_v=gV["A"],
+                         Bt_v=gV["Bt"][li * d_kv:(li + 1) * d_kv], landmarks=gK["landmarks"][li],
+                         k_tail=x["k_tail"], v_tail=x["v_tail"], k_new=kn, v_new=vn)
+            a.out = out[i].data_ptr()
+            a.sel = sel[i].data_ptr()
+            arr.append(a)
+            keep.append((kn, vn))
+        L.sr_decode_layers(ctx, L.sr_args_array(arr), dec.ws)
+        torch.cuda.synchronize()
+        if s not in steps_checked:
+            continue
+        for i, li in enumerate(layers_in_group):
+            x = per[li]
+            kw = dict(T=T, n_gen=s + 1, n_kv_heads=H, chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink,
+                      n_local=c.n_local, landmarks_l=x["lm_ref_b"], A_k=x["A_k"], B_k_l=x["B_k"], A_v=x["A_v"],
+                      B_v_l=x["B_v"], k_exact=x["k_exact"], v_exact=x["v_exact"], theta=c.rope_theta)
+            qd = f64(qs[li])
+            ref = oracle.sr_decode_layer(qd, **kw)
+            q_rot = oracle.rope(qd, T + s, c.rope_theta)
+            slack = landmark_slack(x["lm_ref"], q_rot, grp, scale)
+            n_cand = ref["scores"].shape[1]
+            gsel = sel[i].cpu().numpy()
+            swaps = 0
+            for h in range(H):
+                swaps += check_selection_banded(gsel[h], ref["scores"][h], c.top_k,
+                                                NEAR_TIE / 2 + slack[h, :n_cand])
+            if swaps:
+                ref = oracle.sr_decode_layer(qd, selection=gsel, **kw)
+            rel, mx = attention_errors(f64(out[i]), ref["out"])
+            worst = [max(worst[0], rel), max(worst[1], mx), worst[2] + swaps]
+            log(f"  layer {group * G + li} step {s}: rel L2 {rel:.2e} max abs {mx:.2e} near-tie swaps {swaps} "
+                f"(slack max {slack.max():.1e})")
+            assert rel <= ATT_REL_BF16 and mx <= ATT_ABS_BF16, (li, s, rel, mx)
+    return worst
+
+
+def test_llama16k_end_to_end(ctx):
+    # The 16k Llama-shaped workload as configured: one group of 4 layers, 8 KV heads x 128,
+    # r = 512, K and V compressed by the GPU and by the oracle, then 64 decode steps through
+    # the 4 layers on the GPU with appended tokens; steps 0, 31 and 63 of every layer are
+    # compared with the oracle's decode over its own compression.
+    wl = make_workload("llama16k", device=DEV)
+    c = wl.cfg
+    sides = [wl.group_kv(0, "K", 0), wl.group_kv(0, "V", 0)]
+    outs, refs = compress_vs_oracle(ctx, "llama16k", sides, c.rank, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim,
+                                    chunk=c.chunk, landmarks=[True, False])
+    del sides
+    worst = _e2e_decode(ctx, wl, 0, 0, [0, 1, 2, 3], {0, 31, c.decode_steps - 1}, c.decode_steps,
+                        (outs, refs))
+    log(f"llama16k end to end: worst rel L2 {worst[0]:.2e}, max abs {worst[1]:.2e}, near-tie swaps {worst[2]}")
+    del outs, refs
+    torch.cuda.empty_cache()
+
+
+def test_batch8_g8_sequence_end_to_end(ctx):
+    # G = 8 (n = 8192, r = 1024 past the latent rank 768): the projector is not graded; the
+    # reconstruction error is, and one decode step of one layer over each side's own
+    # compression.  The iteration's error estimate cannot converge inside the noise bulk,
+    # so XKV_ENOTCONV (every output written after the last round) is accepted.
+    wl = make_workload("batch8_g8", device=DEV)
+    c = wl.cfg
+    b = 3
+    sides = [wl.group_kv(b, "K", 0), wl.group_kv(b, "V", 0)]
+    outs, refs = compress_vs_oracle(ctx, "batch8 G=8 sequence 3", sides, c.rank, n_kv_heads=c.n_kv_heads,
+                                    head_dim=c.head_dim, chunk=c.chunk, landmarks=[True, False], projector=False,
+                                    allow_notconv=True)
+    del sides
+    worst = _e2e_decode(ctx, wl, b, 0, [5], {0}, 1, (outs, refs))
+    log(f"batch8 G=8 end to end: rel L2 {worst[0]:.2e}, max abs {worst[1]:.2e}")
+    del outs, refs
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- the batched path
+MINI = dict(T=2000, n_layers=4, n_kv_heads=2, n_q_heads=8, rank=128, latent_rank=192, top_k=32)
+
+
+@pytest.mark.parametrize("S", [4, 5])
+def test_compress_two_halves_match_single(ctx, S):
+    # With 4 or more sides a call runs them in two halves (the host solves one half while the
+    # GPU works on the other); S = 5 splits 2 + 3.  Every side must be bit-identical to its
+    # own single-side call, and one side must meet the oracle bars.
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, n_layers=4 * S, n_kv_heads=2))
+    c = wl.cfg
+    sides, lms = [], []
+    for i in range(S):
+        side = "K" if i % 2 == 0 else "V"
+        sides.append(wl.group_kv(0, side, i // 2))
+        lms.append(side == "K")
+    kw = dict(r=c.rank, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim, chunk=c.chunk, keep_vr64=True)
+    both = xk.compress(ctx, sides, landmarks=lms, **kw)
+    torch.cuda.synchronize()
+    for i in range(S):
+        one = xk.compress(ctx, [sides[i]], landmarks=[lms[i]], **kw)[0]
+        torch.cuda.synchronize()
+        assert torch.equal(both[i]["A"], one["A"]) and torch.equal(both[i]["Bt"], one["Bt"]), i
+        assert torch.equal(both[i]["Vr64"], one["Vr64"]), i
+        assert np.array_equal(both[i]["eigvals"], one["eigvals"]), i
+        if lms[i]:
+            assert torch.equal(both[i]["landmarks"], one["landmarks"]), i
+        assert both[i]["stats"] == one["stats"], i
+    ref = oracle.compress_group([f64(x) for x in sides[S - 1]], c.rank)
+    Vg = f64(both[S - 1]["Vr64"])
+    dP = projector_distance(Vg, ref["Vr"])
+    e_vr, e_ref, e_st, e_st_ref = reconstruction_errors(ref["X"], Vg, both[S - 1]["A"], both[S - 1]["Bt"], ref)
+    log(f"  S={S}: last side ||dP||_F {dP:.2e}, rel err {e_vr:.6f} vs {e_ref:.6f}, stored {e_st:.6f} vs {e_st_ref:.6f}")
+    assert dP <= PROJ_TOL and abs(e_vr - e_ref) <= RECON_TOL and abs(e_st - e_st_ref) <= RECON_TOL
+
+
+# ----------------------------------------------------------------------------- error estimate
+def test_error_estimate_tracks_projector_error(ctx):
+    # float32 inputs: the Gram is exact to ~1e-13, so the distance to the oracle's projector
+    # is the iteration's own error, which the a-posteriori estimate
+    # sqrt(2 sum_i ||C v_i - theta_i v_i||^2 / (theta_i - theta_r+1)^2) bounds (Davis-Kahan sin-theta
+    # theorem applied per Ritz pair, with the Ritz value theta_r+1 standing in for
+    # lambda_r+1).  Sweeps are cut
+    # short so that the error spans several decades; XKV_ENOTCONV is expected then.
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, dtype="fp32"))
+    c = wl.cfg
+    layers = wl.group_kv(0, "K", 0)
+    ref = oracle.compress_group([f64(x) for x in layers], c.rank)
+    pairs = []
+    for f32, f64i, rounds in ((0, 1, 1), (1, 1, 1), (2, 1, 1), (3, 1, 1), (3, 2, 1), (3, 2, 2)):
+        o = xk.compress(ctx, [layers], r=c.rank, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim, landmarks=[False],
+                        keep_vr64=True, fp32_iters=f32, fp64_iters=f64i, max_rounds=rounds, tol=1e-12,
+                        allow_notconv=True)[0]
+        torch.cuda.synchronize()
+        dP = projector_distance(f64(o["Vr64"]), ref["Vr"])
+        est = o["stats"]["err_est"]
+        pairs.append((dP, est))
+        log(f"  sweeps {o['stats']['sweeps']} rounds {o['stats']['rounds']}: ||dP||_F {dP:.2e} estimate {est:.2e} "
+            f"ratio {est / max(dP, 1e-300):.2f}")
+    for dP, est in pairs:
+        if dP < 1e-9:        # at float64 rounding level neither number carries information
+            continue
+        assert dP <= 1.5 * est, (dP, est)       # the estimate bounds the error
+        assert est <= 40.0 * dP, (dP, est)      # and is not loose by more than this factor (10-25 seen)
+    assert pairs[0][0] > 1e-3 > pairs[-1][0]    # the cases span the 1e-3 bar
+
+
+# ----------------------------------------------------------------------------- host-forced errors
+def test_compress_workspace_too_small(ctx):
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, T=256))
+    c = wl.cfg
+    layers = wl.group_kv(0, "K", 0)
+    desc = L.make_desc(T=c.T, G=c.group, d_kv=c.d_kv, r=c.rank, dtype=L.XKV_BF16, n_kv_heads=c.n_kv_heads,
+                       head_dim=c.head_dim)
+    need = L.compress_ws_size(desc, 1)
+    n = c.group * c.d_kv
+    A = torch.full((c.T, c.rank), 7.0, dtype=torch.bfloat16, device=DEV)
+    Bt = torch.full((n, c.rank), 7.0, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(L.XkvError) as e:
+        L.compress_sides(ctx, desc, [{"layers": layers, "A": A, "Bt": Bt}], ws)
+    assert e.value.code == L.XKV_EWORKSPACE
+    torch.cuda.synchronize()
+    assert bool((A == 7.0).all()) and bool((Bt == 7.0).all())      # nothing was enqueued
+
+
+def test_compress_not_converged_then_reuse(ctx):
+    # An unreachable tolerance with one round returns XKV_ENOTCONV with every output
+    # written; the same context then compresses normally, bit-identical to a fresh context.
+    wl = make_workload("llama16k", device=DEV, **MINI)
+    c = wl.cfg
+    layers = wl.group_kv(0, "K", 1)
+    kw = dict(r=c.rank, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim, chunk=c.chunk, landmarks=[True],
+              keep_vr64=True)
+    with pytest.raises(L.XkvError) as e:
+        xk.compress(ctx, [layers], tol=1e-30, max_rounds=1, **kw)
+    assert e.value.code == L.XKV_ENOTCONV
+    o = xk.compress(ctx, [layers], tol=1e-30, max_rounds=1, allow_notconv=True, **kw)[0]
+    torch.cuda.synchronize()
+    assert not o["stats"]["converged"] and o["stats"]["rounds"] == 1
+    assert bool(torch.isfinite(o["A"].float()).all()) and bool(torch.isfinite(o["Vr64"]).all())
+    ref = oracle.compress_group([f64(x) for x in layers], c.rank)
+    assert projector_distance(f64(o["Vr64"]), ref["Vr"]) <= PROJ_TOL     # written, and already close
+    again = xk.compress(ctx, [layers], **kw)[0]
+    with xk.Context(0) as fresh:
+        clean = xk.compress(fresh, [layers], **kw)[0]
+        torch.cuda.synchronize()
+    assert torch.equal(again["A"], clean["A"]) and torch.equal(again["Vr64"], clean["Vr64"])
+
+
+def test_compress_breakdown_then_reuse(ctx):
+    # A Cholesky breakdown (X of rank 8 under a 24-column block) returns XKV_ENUMERIC after
+    # the Rayleigh-Ritz copies were enqueued; the context stays usable.
+    T, d = 256, 64
+    K0 = torch.zeros((T, d))
+    K0[:, :8] = torch.randn((T, 8), generator=torch.Generator().manual_seed(5))
+    layers = [K0.to(DEV), torch.zeros((T, d), device=DEV)]
+    with pytest.raises(xk.XkvError) as e:
+        xk.compress(ctx, [layers], r=16, n_kv_heads=1, head_dim=64, landmarks=[False])
+    assert e.value.code == L.XKV_ENUMERIC
+    wl = make_workload("tiny", device=DEV)
+    good = wl.group_kv(0, "K", 0)
+    o = xk.compress(ctx, [good], r=wl.cfg.rank, n_kv_heads=1, head_dim=64, landmarks=[False], keep_vr64=True)[0]
+    ref = oracle.compress_group([f64(x) for x in good], wl.cfg.rank)
+    torch.cuda.synchronize()
+    assert projector_distance(f64(o["Vr64"]), ref["Vr"]) <= PROJ_TOL

@@ -1,7 +1,7 @@
 """Parity at the workloads' full sizes (sampled outputs and properties).
 
-Decode runs the 64k Llama-shaped, 122k Qwen-shaped and batch-8 (G = 8 at r = 1024,
-G = 1 at r = 128) workloads at their real shapes, in the launch configuration the
+Decode runs the 64k Llama-shaped, 122k Qwen-shaped and batch-8 (G = 1, 2, 4, 8 at
+r = 128 G) workloads at their real shapes, in the launch configuration the
 benchmark times (``xkv_sr_decode_layers`` over consecutive layers with appends and
 attend timing events).  The compressed cache is a stand-in that involves no
 factorisation: the generator's own rank-r factors (``Workload.factor_cache``) with
@@ -129,7 +129,7 @@ def test_fullsize_qwen122k_decode(ctx):
     _decode_layers_fullsize(ctx, "qwen122k", layers=[0, 27], steps=2, check_layers=[0, 27])
 
 
-@pytest.mark.parametrize("name", ["batch8_g8", "batch8_g1"])
+@pytest.mark.parametrize("name", ["batch8_g8", "batch8_g4", "batch8_g2", "batch8_g1"])
 def test_fullsize_batch8_decode(ctx, name):
     # Batch 8 with per-sequence strides; G = 8 takes r = 1024 (two 512-column rank
     # chunks in the attend kernel), G = 1 takes r = 128.  Sequences 0 and 7 are checked.

@@ -199,3 +199,45 @@ def test_value_absorption_identity():
     B = rng.standard_normal((6, 4))
     p = rng.random(20)
     np.testing.assert_allclose(p @ (A @ B), (p @ A) @ B, atol=1e-12)
+
+
+def test_selection_override_with_padding_matches_masked_dense():
+    # The `selection` argument (used when a near-tie swap makes the GPU attend a different
+    # but valid chunk set) attends exactly the given chunks: -1 entries are padding, the
+    # scores are still the landmark scores, and the output is attention over sink + the
+    # given chunks + local window + generated tokens, written out here with the
+    # complex-number RoPE.
+    _, Ks, Vs, q = _setup(6)
+    T, n_gen, d_kv, d, H_kv, n_sink, n_local, chunk = 64, 3, 16, 8, 2, 4, 16, 8
+    layer, r, k = 1, 5, 3
+    res_top, ck, cv = _decode(q, Ks, Vs, layer, r=r, top_k=k)
+    # The lowest-scoring chunks (never the top-k), padded with -1 at both ends.
+    worst = [np.argsort(res_top["scores"][h], kind="stable")[:2].tolist() for h in range(H_kv)]
+    selection = np.array([[-1] + worst[h] + [-1] for h in range(H_kv)])
+    lm = oracle.landmarks(Ks[layer][:T], H_kv, d, chunk)
+    exact = [t for t in range(T + n_gen) if t < n_sink or t >= T - n_local]
+    res = oracle.sr_decode_layer(
+        q, T=T, n_gen=n_gen, n_kv_heads=H_kv, chunk=chunk, top_k=k, n_sink=n_sink, n_local=n_local,
+        landmarks_l=lm, A_k=ck["A"], B_k_l=ck["B"][:, layer * d_kv:(layer + 1) * d_kv], A_v=cv["A"],
+        B_v_l=cv["B"][:, layer * d_kv:(layer + 1) * d_kv], k_exact={t: Ks[layer][t] for t in exact},
+        v_exact={t: Vs[layer][t] for t in exact}, selection=selection)
+    np.testing.assert_array_equal(res["scores"], res_top["scores"])
+    Kr = Ks[layer].copy()
+    Vr = Vs[layer].copy()
+    Kr[n_sink:T - n_local] = oracle.reconstruct_layer(ck["A"], ck["B"], layer, d_kv)[n_sink:T - n_local]
+    Vr[n_sink:T - n_local] = oracle.reconstruct_layer(cv["A"], cv["B"], layer, d_kv)[n_sink:T - n_local]
+    p = T + n_gen - 1
+    for h in range(H_kv):
+        want = set(range(n_sink)) | set(range(T - n_local, T + n_gen))
+        for c in worst[h]:
+            want |= set(range(c * chunk, (c + 1) * chunk))
+        pos = np.array(sorted(want))
+        assert res["positions"][h].tolist() == pos.tolist()
+        assert res["sel"][h].tolist() == worst[h]
+        for j in (2 * h, 2 * h + 1):
+            qr = rope_complex(q[j], p)
+            kr = rope_complex(Kr[pos][:, h * d:(h + 1) * d], pos)
+            z = kr @ qr / math.sqrt(d)
+            w = np.exp(z - z.max())
+            np.testing.assert_allclose(res["out"][j], (w / w.sum()) @ Vr[pos][:, h * d:(h + 1) * d], atol=1e-10)
+        assert not np.allclose(res["out"][2 * h], res_top["out"][2 * h])

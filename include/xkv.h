@@ -26,7 +26,9 @@
  *    row-major with the stated leading dimension (in elements).
  *  - The caller owns all memory, including the workspace.  The library never
  *    allocates or frees device memory and keeps no pointer after a call
- *    returns.  A context owns host-side resources only (pinned staging for
+ *    returns; its only device memory is the fixed decode scratch of
+ *    xkv_sr_decode_layers_noalloc, part of its code object.  A context owns
+ *    host-side resources only (pinned staging for
  *    the Rayleigh-Ritz round trip, host solver threads, and the solvers'
  *    working memory, ~27 MB per side at r = 512, G d_kv = 4096, kept until
  *    xkv_ctx_destroy so that later compressions reuse it).
@@ -125,9 +127,10 @@ int xkv_compress_ws_size(const xkv_compress_desc* desc, int n_sides, size_t* byt
  * V_r = Q Z_r -> A = X V_r and the landmarks.  With 4 or more sides the
  * sides go in two halves, so that the GPU steps of the second half run while
  * the host solves the first half's eigenproblems.
- * Convergence: after each Rayleigh-Ritz round the Ritz residual
- * R = C V_r - V_r diag(theta) gives the estimate sqrt(2) ||R||_F / (theta_r -
- * theta_{r+1}) of ||P - P_exact||_F (P = V_r V_r^T); rounds with more float64
+ * Convergence: after each Rayleigh-Ritz round the Ritz residuals
+ * r_i = C v_i - theta_i v_i give the estimate
+ * sqrt(2 sum_i ||r_i||^2 / (theta_i - theta_{r+1})^2) of ||P - P_exact||_F
+ * (P = V_r V_r^T; a per-pair sin-theta bound); rounds with more float64
  * sweeps run until it is <= tol or max_rounds is reached (XKV_ENOTCONV, with
  * every output written).  A block that spans all n columns is exact.
  * Blocks the calling thread once per round, for the Rayleigh-Ritz round trip;
@@ -257,6 +260,21 @@ int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
  * matrix-core path, recorded on `stream` around the launch otherwise). */
 int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* ws, size_t ws_bytes,
                          void* stream, void* const* attend_events);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same decode
+ * step as xkv_sr_decode_layers, with the same kernels and results, but its
+ * scratch (chunk scores, split partials) lives in a device array owned by the
+ * library, XKV_SR_SCRATCH_BYTES per GPU, held from the first xkv_ctx_create on
+ * that GPU until the process ends.  The caller still passes every input and
+ * output (args as for xkv_sr_decode_layers).  Nothing is allocated or freed.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.  Errors: XKV_EWORKSPACE when a
+ * layer's xkv_sr_ws_size exceeds XKV_SR_SCRATCH_BYTES (e.g. full reconstruction
+ * of a long prefix), plus those of xkv_sr_decode_layers. */
+#define XKV_SR_SCRATCH_BYTES (64u << 20)
+int xkv_sr_decode_layers_noalloc(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Dense decode baseline (full attention over the whole cache)               */

@@ -101,6 +101,7 @@ def lib():
         for name in ("xkv_sr_select", "xkv_sr_attend", "xkv_sr_decode"):
             getattr(L, name).argtypes = [vp, C.POINTER(SrArgs), vp, sz, vp]
         L.xkv_sr_decode_layers.argtypes = [vp, i, C.POINTER(SrArgs), vp, sz, vp, C.POINTER(vp)]
+        L.xkv_sr_decode_layers_noalloc.argtypes = [vp, i, C.POINTER(SrArgs), vp]
         L.xkv_gram.argtypes = [C.POINTER(vp), i, l, i, i, i, i, vp, vp]
         L.xkv_topk.argtypes = [vp, i, i, l, i, vp, vp]
         L.xkv_host_eigh.argtypes = [i, vp, i, vp, vp]
@@ -259,6 +260,15 @@ def sr_decode_layers(ctx, arr, ws, stream=None, attend_events=None):
         ev = (C.c_void_p * len(attend_events))(*[None if e is None else e.cuda_event for e in attend_events])
     _check(lib().xkv_sr_decode_layers(ctx.handle, len(arr), arr, _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream), ev))
+
+
+SR_SCRATCH_BYTES = 64 << 20
+
+
+def sr_decode_layers_noalloc(ctx, arr, stream=None):
+    """One decode step through len(arr) layers with the library's own scratch (no
+    workspace argument; calls on one GPU must not overlap)."""
+    _check(lib().xkv_sr_decode_layers_noalloc(ctx.handle, len(arr), arr, _stream(stream)))
 
 
 def gram(layers, stream=None, sides=None, out=None) -> torch.Tensor:

@@ -96,6 +96,15 @@ int xkv_ctx_create(int device, int host_threads, xkv_ctx* out) {
   c->device = device;
   c->host_threads = host_threads > 0 ? host_threads : 16;
   XKV_HIP(hipSetDevice(device));
+  {
+    // The decode scratch of xkv_sr_decode_layers_noalloc: its address on this device.
+    const hipError_t e = xkv::sr_scratch_setup(device);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(XKV_EHIP, "xkv_ctx_create: address of the decode scratch on device %d: %s", device,
+                  hipGetErrorString(e));
+    }
+  }
   XKV_HIP(hipEventCreateWithFlags(&c->upload_done, hipEventDisableTiming));
   XKV_HIP(hipEventCreateWithFlags(&c->half_done[0], hipEventDisableTiming));
   XKV_HIP(hipEventCreateWithFlags(&c->half_done[1], hipEventDisableTiming));
@@ -852,6 +861,32 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
     XKV_K(xkv::launch_sr_attend(p, bf16, st, attend_events ? (hipEvent_t)attend_events[2 * l] : nullptr,
                                 attend_events ? (hipEvent_t)attend_events[2 * l + 1] : nullptr));
     XKV_K(xkv::launch_sr_merge(p, st));
+  }
+  return XKV_OK;
+}
+
+extern "C" int xkv_sr_decode_layers_noalloc(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* stream) {
+  if (!ctx) return fail(XKV_EINVAL, "xkv_sr_decode_layers_noalloc: ctx is NULL");
+  if (n_layers <= 0 || !args) return fail(XKV_EINVAL, "xkv_sr_decode_layers_noalloc: need n_layers > 0 and args");
+  void* ws = xkv::sr_scratch_ptr(ctx->device);
+  if (!ws) return fail(XKV_EHIP, "xkv_sr_decode_layers_noalloc: no decode scratch on device %d", ctx->device);
+  std::vector<xkv::SrParams> P(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    size_t need = 0;
+    int rc = plan_sr(&args[l], &P[l], &need);
+    if (rc) return rc;
+    if (need > xkv::kSrScratchBytes)
+      return fail(XKV_EWORKSPACE, "xkv_sr_decode_layers_noalloc: layer %d needs %zu bytes of scratch, above the "
+                  "library's %zu (use xkv_sr_decode_layers with a workspace)", l, need, xkv::kSrScratchBytes);
+    bind_sr_ws(&P[l], ws);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    const int bf16 = args[l].dtype == XKV_BF16;
+    XKV_K(xkv::launch_sr_score(P[l], bf16, st));
+    XKV_K(xkv::launch_sr_topk(P[l], bf16, st));
+    XKV_K(xkv::launch_sr_attend(P[l], bf16, st, nullptr, nullptr));
+    XKV_K(xkv::launch_sr_merge(P[l], st));
   }
   return XKV_OK;
 }

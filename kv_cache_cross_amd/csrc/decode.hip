@@ -40,6 +40,7 @@
 //   into the output; the latter applies B_v,l,h to the merged rank-r sum.
 #include <hip/hip_ext.h>
 #include <algorithm>
+#include <mutex>
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 #include "decode_params.h"
@@ -1597,6 +1598,34 @@ hipError_t launch_topk(const float* scores, int rows, int n_cand, long ld, int k
   else
     hipLaunchKernelGGL(topk_rows_kernel<32>, dim3(rows), dim3(TKT), 0, st, scores, n_cand, ld, k, sel);
   return hipGetLastError();
+}
+
+// The decode scratch of xkv_sr_decode_layers_noalloc: one array per GPU, in the
+// library's code object.  Host code never uses the array's name as an address (on
+// the host it only stands for the symbol); the address on each device comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+namespace {
+__device__ __align__(256) unsigned char scratch[kSrScratchBytes];
+std::mutex scratch_mu;
+void* scratch_dev[kSrScratchDevices] = {};
+}  // namespace
+
+hipError_t sr_scratch_setup(int device) {
+  if (device < 0 || device >= kSrScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[device]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  scratch_dev[device] = p;
+  return hipSuccess;
+}
+
+void* sr_scratch_ptr(int device) {
+  if (device < 0 || device >= kSrScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  return scratch_dev[device];
 }
 
 }  // namespace xkv

@@ -77,4 +77,13 @@ hipError_t launch_transpose_basis(const void* Bt, long ldb, int n, int r, void* 
 struct SrParams;  // defined in decode.hip
 hipError_t launch_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel, hipStream_t st);
 
+// Decode scratch owned by the library (decode.hip), for callers that cannot allocate:
+// kSrScratchBytes of device memory per GPU, held until the process ends.
+// sr_scratch_setup(device) looks up its address on `device` (which must be current)
+// once; sr_scratch_ptr(device) returns it afterwards (NULL before).
+constexpr size_t kSrScratchBytes = size_t(64) << 20;
+constexpr int kSrScratchDevices = 64;
+hipError_t sr_scratch_setup(int device);
+void* sr_scratch_ptr(int device);
+
 }  // namespace xkv

@@ -1,21 +1,23 @@
 #!/usr/bin/env python
 """Benchmark of the xKV hot path on one MI355X.
 
-Workload (default): the Llama-3.1-8B-shaped 64k-token cache -- 32 layers in 8
-groups of G=4, 8 KV heads x 128, 32 query heads, T=65536, rank 512 for K and V,
-bf16, batch 1, chunk 8, top-k 256 chunks + 4 sink + 64 local, 128 decode steps
-appending uncompressed tokens.  Inputs are synthetic (synth/), generated on the
-GPU before timing.
+Workload (default, --config llama64k): the Llama-3.1-8B-shaped 64k-token cache --
+32 layers in 8 groups of G=4, 8 KV heads x 128, 32 query heads, T=65536, rank 512
+for K and V, bf16, batch 1, chunk 8, top-k 256 chunks + 4 sink + 64 local, 128
+decode steps appending uncompressed tokens.  Other workloads: llama16k, qwen122k,
+batch8_g1 / g2 / g4 / g8 (batch 8, T=32768, r = 128 G), tiny.  Inputs are
+synthetic (synth/), generated on the GPU before timing.
 
-One step = the whole hot path over the workload: compress all 16 group sides
-(Gram, subspace iteration, host Rayleigh-Ritz, projection, landmarks), then the
-decode steps through every layer (append, landmark scores, top-k, rebuild +
-attend + merge).  The JSON line reports:
-  value    SR decode microseconds per decode step (all layers), higher_is_better false
+One step = the whole hot path over the workload: compress every group side of every
+sequence (Gram, subspace iteration, host Rayleigh-Ritz, projection, landmarks), then
+the decode steps through every layer (append, landmark scores, top-k, rebuild +
+attend + merge) for all sequences at once.  The JSON line reports:
+  value    SR decode microseconds per decode step (all layers, all sequences), higher_is_better false
   sr_decode_GBps, compress_tokens_per_s, compress breakdown
-  roofline      attend kernel vs HBM (union-of-rows algorithmic bytes / event-timed duration)
-  roofline_gram Gram kernel vs bf16 MFMA peak
-  cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
+  roofline         attend kernel vs HBM (union-of-rows algorithmic bytes / event-timed duration)
+  roofline_gram    Gram kernel vs bf16 MFMA peak
+  roofline_project projection kernel vs bf16 MFMA peak
+  cpu_baseline     the float64 oracle on a bounded sample, on this host's cores
 """
 from __future__ import annotations
 
@@ -75,6 +77,10 @@ def parse():
                     help="skip the dense baseline, the SR variants, the token fold and the rank diagnostics "
                          "(for counter runs that should see the main decode kernels only)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sides-per-call", type=int, default=16,
+                    help="group sides per compression call (the workspace is sized for one call)")
+    ap.add_argument("--max-rounds", type=int, default=0,
+                    help="Rayleigh-Ritz rounds before a side is reported unconverged (0: the library's 8)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB device to device (a plain copy "
                          "kernel of known size that scales memory counters)")
@@ -95,72 +101,93 @@ def main():
 
     wl = make_workload(args.config, seed=args.seed, device="cuda:0")
     c = wl.cfg
-    if c.batch != 1:
-        raise SystemExit("bench.py times the batch-1 workloads (llama64k, llama16k, qwen122k, tiny)")
     D = args.decode_steps if args.decode_steps is not None else c.decode_steps
     if D < 1:
         raise SystemExit("bench.py: --decode-steps must be at least 1 (a step is compression + D decode steps)")
-    Lyr, G, d_kv, T, r, H, d, Hq = c.n_layers, c.group, c.d_kv, c.T, c.rank, c.n_kv_heads, c.head_dim, c.n_q_heads
+    B, Lyr, G, d_kv, T, r = c.batch, c.n_layers, c.group, c.d_kv, c.T, c.rank
+    H, d, Hq, n, C_ch = c.n_kv_heads, c.head_dim, c.n_q_heads, c.n, c.n_chunks
     dt = c.torch_dtype
     esz = 2 if dt == torch.bfloat16 else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] workload {c.name}: L={Lyr} G={G} H_kv={H} d={d} H_q={Hq} T={T} r={r} top_k={c.top_k} "
+    log(f"[bench] workload {c.name}: B={B} L={Lyr} G={G} H_kv={H} d={d} H_q={Hq} T={T} r={r} top_k={c.top_k} "
         f"decode steps={D}")
 
     # ---- inputs, resident in HBM before timing ----
     t0 = time.time()
-    layers = {(s, l): wl.layer_kv(0, s, l) for s in "KV" for l in range(Lyr)}
-    wl._latent.clear()
-    q_all = torch.stack([torch.stack([wl.query(0, l, s) for l in range(Lyr)]) for s in range(D)]).contiguous()
+    layers = {}
+    for b in range(B):
+        for s in "KV":
+            for l in range(Lyr):
+                layers[(b, s, l)] = wl.layer_kv(b, s, l)
+        wl._latent.clear()
+    q_all = torch.stack([torch.stack([torch.stack([wl.query(b, l, s) for b in range(B)]) for l in range(Lyr)])
+                         for s in range(D)]).contiguous()                                  # D x L x B x Hq x d
+    kn_all = vn_all = None
     if c.append:
-        kn_all = torch.stack([torch.stack([wl.new_token(0, "K", l, s) for l in range(Lyr)]) for s in range(D)])
-        vn_all = torch.stack([torch.stack([wl.new_token(0, "V", l, s) for l in range(Lyr)]) for s in range(D)])
+        kn_all = torch.stack([torch.stack([torch.stack([wl.new_token(b, "K", l, s) for b in range(B)])
+                                           for l in range(Lyr)]) for s in range(D)]).contiguous()
+        vn_all = torch.stack([torch.stack([torch.stack([wl.new_token(b, "V", l, s) for b in range(B)])
+                                           for l in range(Lyr)]) for s in range(D)]).contiguous()
     torch.cuda.synchronize()
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
 
     ctx = xk.Context(0)
     n_groups = c.n_groups
     desc = L.make_desc(T=T, G=G, d_kv=d_kv, r=r, dtype=xk.dtype_code(dt), n_kv_heads=H, head_dim=d, chunk=c.chunk,
-                       rope_theta=c.rope_theta)
-    sides, outs = [], []
-    for g in range(n_groups):
-        for s in "KV":
-            o = {"A": torch.empty((T, r), dtype=dt, device=dev), "Bt": torch.empty((G * d_kv, r), dtype=dt, device=dev),
-                 "landmarks": torch.empty((G, H, T // c.chunk, d), dtype=dt, device=dev) if s == "K" else None}
-            outs.append(o)
-            sides.append({"layers": [layers[(s, g * G + i)] for i in range(G)], **o})
+                       rope_theta=c.rope_theta, max_rounds=args.max_rounds)
+    # Compressed cache: per group and side, all sequences in one tensor (the decode reads
+    # them with batch strides).  One factorisation per sequence, group and side.
+    A_out = {(g, s): torch.empty((B, T, r), dtype=dt, device=dev) for g in range(n_groups) for s in "KV"}
+    Bt_out = {(g, s): torch.empty((B, n, r), dtype=dt, device=dev) for g in range(n_groups) for s in "KV"}
+    lm_out = {g: torch.empty((B, G, H, C_ch, d), dtype=dt, device=dev) for g in range(n_groups)}
+    sides = []
+    for b in range(B):
+        for g in range(n_groups):
+            for s in "KV":
+                sides.append({"layers": [layers[(b, s, g * G + i)] for i in range(G)], "A": A_out[(g, s)][b],
+                              "Bt": Bt_out[(g, s)][b], "landmarks": lm_out[g][b] if s == "K" else None})
     S = len(sides)
-    cws = torch.empty(L.compress_ws_size(desc, S), dtype=torch.uint8, device=dev)
-    log(f"[bench] compress workspace {cws.numel() / 2**30:.2f} GiB for {S} group sides")
+    spc = min(S, args.sides_per_call)
+    calls = [sides[i:i + spc] for i in range(0, S, spc)]
+    cws = torch.empty(L.compress_ws_size(desc, spc), dtype=torch.uint8, device=dev)
+    log(f"[bench] compress workspace {cws.numel() / 2**30:.2f} GiB; {S} group sides in {len(calls)} calls")
 
     # ---- decode buffers: exact tails, selections, outputs ----
     rows = list(range(c.n_sink)) + list(range(T - c.n_local, T))
     n_tail = len(rows) + (D if c.append else 0)
-    k_tail = torch.zeros((Lyr, n_tail, d_kv), dtype=dt, device=dev)
+    k_tail = torch.zeros((Lyr, B, n_tail, d_kv), dtype=dt, device=dev)
     v_tail = torch.zeros_like(k_tail)
     for l in range(Lyr):
-        k_tail[l, :len(rows)] = layers[("K", l)][rows]
-        v_tail[l, :len(rows)] = layers[("V", l)][rows]
-    sel = torch.full((D, Lyr, H, c.top_k), -1, dtype=torch.int32, device=dev)
-    out = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
-    dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk, top_k=c.top_k,
+        for b in range(B):
+            k_tail[l, b, :len(rows)] = layers[(b, "K", l)][rows]
+            v_tail[l, b, :len(rows)] = layers[(b, "V", l)][rows]
+    sel = torch.full((D, Lyr, B, H, c.top_k), -1, dtype=torch.int32, device=dev)
+    out = torch.empty((Lyr, B, Hq, d), dtype=torch.float32, device=dev)
+
+    def layer_args(dec_, s, l, out_t, sel_t, exact_values=False):
+        g, li = divmod(l, G)
+        AK, AV, BK, BV = A_out[(g, "K")], A_out[(g, "V")], Bt_out[(g, "K")], Bt_out[(g, "V")]
+        lm = lm_out[g]
+        kw = dict(n_gen=(s + 1) if c.append else 0, q=q_all[s, l], A_k=AK[0], Bt_k=BK[0, li * d_kv:(li + 1) * d_kv],
+                  landmarks=lm[0, li], k_tail=k_tail[l, 0], v_tail=v_tail[l, 0],
+                  k_new=kn_all[s, l] if c.append else None, v_new=vn_all[s, l] if c.append else None,
+                  bstride_A_k=AK.stride(0), bstride_Bt_k=BK.stride(0), bstride_lm=lm.stride(0),
+                  bstride_tail=k_tail.stride(1), bstride_new=d_kv)
+        if exact_values:
+            kw.update(V_full=layers[(0, "V", l)])
+        else:
+            kw.update(A_v=AV[0], Bt_v=BV[0, li * d_kv:(li + 1) * d_kv], bstride_A_v=AV.stride(0),
+                      bstride_Bt_v=BV.stride(0))
+        a = dec_.args(**kw)
+        a.out = out_t.data_ptr()
+        a.sel = sel_t.data_ptr()
+        return a
+
+    dec = xk.LayerDecoder(ctx, batch=B, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk, top_k=c.top_k,
                           n_sink=c.n_sink, n_local=c.n_local, r_k=r, r_v=r, dtype=dt, device=dev,
                           rope_theta=c.rope_theta, max_gen=D if c.append else 0)
-    step_args = []
-    for s in range(D):
-        arr = []
-        for l in range(Lyr):
-            g, li = divmod(l, G)
-            oK, oV = outs[2 * g], outs[2 * g + 1]
-            a = dec.args(n_gen=(s + 1) if c.append else 0, q=q_all[s, l], A_k=oK["A"],
-                         Bt_k=oK["Bt"][li * d_kv:(li + 1) * d_kv], A_v=oV["A"], Bt_v=oV["Bt"][li * d_kv:(li + 1) * d_kv],
-                         landmarks=oK["landmarks"][li], k_tail=k_tail[l], v_tail=v_tail[l],
-                         k_new=kn_all[s, l] if c.append else None, v_new=vn_all[s, l] if c.append else None)
-            a.out = out[l].data_ptr()
-            a.sel = sel[s, l].data_ptr()
-            arr.append(a)
-        step_args.append(L.sr_args_array(arr))
+    step_args = [L.sr_args_array([layer_args(dec, s, l, out[l], sel[s, l]) for l in range(Lyr)]) for s in range(D)]
     # Attend timing: step s stamps the attend kernel of layer s mod L only (events on every
     # layer's dispatch would add ~5 us per layer to the step); over the D steps every layer
     # is sampled D / L times.
@@ -175,12 +202,20 @@ def main():
         events.append(evs)
     torch.cuda.synchronize()
 
-    last_evals = []
+    last_evals, last_stats, notconv = [], [], [0]
 
     def compress():
-        evals, stats = L.compress_sides(ctx, desc, sides, cws)
-        last_evals[:] = evals
-        return stats
+        evals, stats, nc = [], [], 0
+        for part in calls:
+            try:
+                e, st = L.compress_sides(ctx, desc, part, cws)
+            except L.XkvError as err:
+                if err.code != L.XKV_ENOTCONV:
+                    raise
+                e, st, nc = err.evals, err.stats, nc + len(part)
+            evals += e
+            stats += st
+        last_evals[:], last_stats[:], notconv[0] = evals, stats, nc
 
     def decode(timed):
         for s in range(D):
@@ -193,12 +228,12 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed steps ----
-    t_comp, t_dec, attend_ms, stats = [], [], [], None
+    t_comp, t_dec, attend_ms = [], [], []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
         a0 = time.perf_counter()
-        stats = compress()
+        compress()
         torch.cuda.synchronize()
         a1 = time.perf_counter()
         decode(True)
@@ -210,32 +245,36 @@ def main():
                                    for s in range(D)]))
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
+    stats = last_stats
 
     # ---- algorithmic bytes of the last step's decode (from its actual selections) ----
     n_cand = -(-(T - c.n_local) // c.chunk)
     sel_np = sel.cpu().numpy()
+
+    def rows_of(cs):
+        cs = np.asarray(cs)
+        m = len(cs) * c.chunk
+        m -= np.sum(np.clip(c.n_sink - cs * c.chunk, 0, c.chunk))     # sink rows are exact
+        return m
+
     union_rows = np.zeros((D, Lyr))
     perhead_rows = np.zeros((D, Lyr))
     for s in range(D):
         for l in range(Lyr):
-            ch = sel_np[s, l]
-            valid = ch[ch >= 0]
-            u = np.unique(valid)
-            def rows_of(cs):
-                n = len(cs) * c.chunk
-                n -= np.sum(np.clip(c.n_sink - cs * c.chunk, 0, c.chunk))     # sink rows are exact
-                return n
-            union_rows[s, l] = rows_of(u)
-            perhead_rows[s, l] = sum(rows_of(ch[h][ch[h] >= 0]) for h in range(H))
+            for b in range(B):
+                ch = sel_np[s, l, b]
+                union_rows[s, l] += rows_of(np.unique(ch[ch >= 0]))
+                perhead_rows[s, l] += sum(rows_of(ch[h][ch[h] >= 0]) for h in range(H))
     n_gen = np.arange(1, D + 1)[:, None] if c.append else np.zeros((D, 1))
-    # Attend kernel: the gathered rows of A_k and A_v, the layer's B_k slice and the queries.
-    attend_union = union_rows * r * esz * 2 + d_kv * r * esz + Hq * d * esz
-    attend_perhead = perhead_rows * r * esz * 2 + d_kv * r * esz + Hq * d * esz
+    # Attend kernel: the gathered rows of A_k and A_v, the layer's B_k slice and the queries
+    # (all sequences).
+    attend_union = union_rows * r * esz * 2 + B * (d_kv * r * esz + Hq * d * esz)
+    attend_perhead = perhead_rows * r * esz * 2 + B * (d_kv * r * esz + Hq * d * esz)
     # The rest of a layer's step: landmarks and queries (scoring), the appended token,
     # the exact tail rows (K and V), B_v (applied in the merge) and the output.
     tail_bytes = (c.n_sink + c.n_local + n_gen) * d_kv * esz * 2
-    other_bytes = (H * n_cand * d * esz + Hq * d * esz + (2 * d_kv * esz * 2 if c.append else 0)
-                   + tail_bytes + d_kv * r * esz + Hq * d * 4)
+    other_bytes = B * (H * n_cand * d * esz + Hq * d * esz + (2 * d_kv * esz * 2 if c.append else 0)
+                       + tail_bytes + d_kv * r * esz + Hq * d * 4)
     decode_bytes_step = float(np.mean(np.sum(attend_union + other_bytes, axis=1)))
     att_ms = attend_ms[-1]                                     # D sampled launches, last step (matches sel)
     att_ms_all = float(np.mean(attend_ms))
@@ -248,36 +287,20 @@ def main():
     sr_gbps = decode_bytes_step / (dec_us * 1e-6) / 1e9
 
     # ---- dense flash-decode baseline: the same queries over the full post-RoPE cache ----
-    dense = dense_baseline(xk, ctx, c, layers, q_all, kn_all if c.append else None,
-                           vn_all if c.append else None, D, args.steps) if (D > 0 and not args.no_extras) else None
-    # ---- the SR variants on the same cache: xK-SR (values exact, on the GPU) and full
-    # reconstruction (every candidate chunk selected) ----
+    dense = dense_baseline(xk, ctx, c, layers, q_all, kn_all, vn_all, D, args.steps) if not args.no_extras else None
+    # ---- the SR variants on the same cache (batch 1): xK-SR (values exact, on the GPU) and
+    # full reconstruction (every candidate chunk selected) ----
     variants = {}
-    if D > 0 and not args.no_extras:
+    if B == 1 and not args.no_extras:
         def run_variant(top_k, exact_values, steps):
             vdec = xk.LayerDecoder(ctx, batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, T=T, chunk=c.chunk,
                                    top_k=top_k, n_sink=c.n_sink, n_local=c.n_local, r_k=r,
                                    r_v=0 if exact_values else r, dtype=dt, device=dev, rope_theta=c.rope_theta,
                                    max_gen=D if c.append else 0)
-            vsel = torch.full((Lyr, H, top_k), -1, dtype=torch.int32, device=dev)
-            vout = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
-            sargs = []
-            for s_ in range(steps):
-                arr = []
-                for l in range(Lyr):
-                    g, li = divmod(l, G)
-                    oK, oV = outs[2 * g], outs[2 * g + 1]
-                    a = vdec.args(n_gen=(s_ + 1) if c.append else 0, q=q_all[s_, l], A_k=oK["A"],
-                                  Bt_k=oK["Bt"][li * d_kv:(li + 1) * d_kv],
-                                  A_v=None if exact_values else oV["A"],
-                                  Bt_v=None if exact_values else oV["Bt"][li * d_kv:(li + 1) * d_kv],
-                                  V_full=layers[("V", l)] if exact_values else None,
-                                  landmarks=oK["landmarks"][li], k_tail=k_tail[l], v_tail=v_tail[l],
-                                  k_new=kn_all[s_, l] if c.append else None, v_new=vn_all[s_, l] if c.append else None)
-                    a.out = vout[l].data_ptr()
-                    a.sel = vsel[l].data_ptr()
-                    arr.append(a)
-                sargs.append(L.sr_args_array(arr))
+            vsel = torch.full((Lyr, 1, H, top_k), -1, dtype=torch.int32, device=dev)
+            vout = torch.empty((Lyr, 1, Hq, d), dtype=torch.float32, device=dev)
+            sargs = [L.sr_args_array([layer_args(vdec, s_, l, vout[l], vsel[l], exact_values) for l in range(Lyr)])
+                     for s_ in range(steps)]
             for s_ in range(steps):
                 L.sr_decode_layers(ctx, sargs[s_], vdec.ws)
             torch.cuda.synchronize()
@@ -293,23 +316,24 @@ def main():
             return round(float(np.median(times)), 2)
         variants["xk_sr_us_per_step"] = run_variant(c.top_k, True, D)
         full_steps = min(D, 4)
-        variants["full_reconstruction_us_per_step"] = run_variant(n_cand, False, full_steps)
-        variants["full_reconstruction_steps"] = full_steps
+        if n_cand // (64 // c.chunk) + 2 <= 1088:
+            variants["full_reconstruction_us_per_step"] = run_variant(n_cand, False, full_steps)
+            variants["full_reconstruction_steps"] = full_steps
 
     # ---- folding a turn's generated tokens into the compressed prefix: the D appended
     # rows of every layer projected onto each group side's stored basis (+ landmarks of
-    # the new chunks), all 16 sides ----
+    # the new chunks), every side of sequence 0 ----
     append_rate = None
-    if c.append and D % c.chunk == 0 and D > 0 and not args.no_extras:
+    if c.append and D % c.chunk == 0 and not args.no_extras:
         app_args, app_keep = [], []
         for g in range(n_groups):
-            for i, s_ in enumerate("KV"):
+            for s_ in "KV":
                 src = kn_all if s_ == "K" else vn_all
-                new = [src[:, g * G + li].contiguous() for li in range(G)]
+                new = [src[:, g * G + li, 0].contiguous() for li in range(G)]
                 A_new = torch.empty((D, r), dtype=dt, device=dev)
                 lm_new = (torch.empty((G, H, D // c.chunk, d), dtype=dt, device=dev) if s_ == "K" else None)
                 app_keep.append((new, A_new, lm_new))
-                app_args.append(xk.append_args(layers=new, Bt=outs[2 * g + i]["Bt"], A_new=A_new, pos0=T, r=r,
+                app_args.append(xk.append_args(layers=new, Bt=Bt_out[(g, s_)][0], A_new=A_new, pos0=T, r=r,
                                                n_kv_heads=H, head_dim=d, chunk=c.chunk, landmarks_new=lm_new))
         app_ws = torch.empty(max(xk.append_ws_size(a_) for a_ in app_args), dtype=torch.uint8, device=dev)
         for a_ in app_args:
@@ -327,17 +351,17 @@ def main():
                        "tokens_per_s": round(D / (fold_us * 1e-6), 1)}
         del app_args, app_keep, app_ws
 
-    # ---- rank diagnostics (outside the timed region): the cumulative-eigenvalue rank of
-    # every group side from its leading Ritz values and trace, and the full spectrum of
-    # layer 0 (K and V, a compression at r = d_kv) for NER and the same rank per layer ----
+    # ---- rank diagnostics (outside the timed region), sequence 0: the cumulative-eigenvalue
+    # rank of every group side from its leading Ritz values and trace, and the full spectrum
+    # of layer 0 (K and V, a compression at r = d_kv) for NER and the same rank per layer ----
     rank_diag = None
     if c.dtype == "bf16" and not args.no_extras:
         def frac_rank(ev, total):
             rs = xk.rank_stats(ev, total=total, frac=0.95)
-            return rs["energy_rank"] / float(G * d_kv) if rs["energy_rank"] > 0 else None
+            return rs["energy_rank"] / float(n) if rs["energy_rank"] > 0 else None
         grp = {s_: [frac_rank(last_evals[2 * g + i], stats[2 * g + i][4]) for g in range(n_groups)]
                for i, s_ in enumerate("KV")}
-        single = xk.compress(ctx, [[layers[("K", 0)]], [layers[("V", 0)]]], r=d_kv, n_kv_heads=H, head_dim=d,
+        single = xk.compress(ctx, [[layers[(0, "K", 0)]], [layers[(0, "V", 0)]]], r=d_kv, n_kv_heads=H, head_dim=d,
                              landmarks=[False, False])
         torch.cuda.synchronize()
         layer0 = {}
@@ -349,12 +373,15 @@ def main():
         rank_diag = {"group_rank95_frac": {k: [None if v is None else round(v, 4) for v in vs] for k, vs in grp.items()},
                      "layer0": layer0,
                      "note": "rank95_frac = rank holding 95 % of the eigenvalue sum / dimension; group sides "
-                             f"from the {r} leading Ritz values and trace(C) (None: beyond {r})"}
+                             f"of sequence 0 from the {r} leading Ritz values and trace(C) (None: beyond {r})"}
 
-    # ---- Gram kernel vs bf16 MFMA peak (the compression's dominant kernel), one batched launch ----
-    n = G * d_kv
-    gram_out = torch.empty((S, n, n), dtype=torch.float64, device=dev)
-    gsides = [sd["layers"] for sd in sides]
+    # ---- Gram and projection kernels vs bf16 MFMA peak (the compression's GEMMs), one
+    # batched Gram launch over the sides of one compression call; the projection of every
+    # row of those sides onto their stored bases (the token-fold entry point with m = T and
+    # no landmarks: one launch of the projection kernel per side, plus a small transpose) ----
+    gsides = [sd["layers"] for sd in calls[0]]
+    Sg = len(gsides)
+    gram_out = torch.empty((Sg, n, n), dtype=torch.float64, device=dev)
     xk.gram(None, sides=gsides, out=gram_out)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -362,13 +389,32 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     gram_ms = e0.elapsed_time(e1)
-    gram_flops = S * float(n) * (n + 1) * T             # unique entries of C, 2T flops each
+    gram_flops = Sg * float(n) * (n + 1) * T             # unique entries of C, 2T flops each
     del gram_out
     gram_tflops = gram_flops / (gram_ms * 1e-3) / 1e12
+    proj_args = []
+    proj_out = torch.empty((Sg, T, r), dtype=dt, device=dev)
+    for i, sd in enumerate(calls[0]):
+        proj_args.append(xk.append_args(layers=sd["layers"], Bt=sd["Bt"], A_new=proj_out[i], pos0=0, r=r))
+    proj_ws = torch.empty(xk.append_ws_size(proj_args[0]), dtype=torch.uint8, device=dev)
+    for a_ in proj_args:
+        xk.compress_append(ctx, a_, proj_ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for a_ in proj_args:
+        xk.compress_append(ctx, a_, proj_ws)
+    e1.record()
+    torch.cuda.synchronize()
+    proj_ms = e0.elapsed_time(e1)
+    proj_same = bool(torch.equal(proj_out[0], calls[0][0]["A"]))      # the same kernel as in compression
+    del proj_out, proj_args, proj_ws
+    proj_tflops = Sg * 2.0 * T * n * r / (proj_ms * 1e-3) / 1e12
 
     traffic = traffic_bytes(ATTEND_TRAFFIC) if (c.name == "llama64k" and D > 0) else None
     gram_traffic = traffic_bytes(GRAM_TRAFFIC) if c.name == "llama64k" else None
     algo_bytes_launch = float(np.mean(attend_union[samp]))
+    shape = {"llama64k": "Llama-3.1-8B-shaped", "llama16k": "Llama-3.1-8B-shaped", "qwen122k": "Qwen2.5-7B-shaped",
+             "tiny": "tiny"}.get(c.name, "Llama-3.1-8B-shaped")
     line = {
         "metric": "SR decode us/step + achieved HBM GB/s; KV compress tokens/s at 64k ctx",
         "value": round(dec_us, 2),
@@ -382,17 +428,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{c.name}: Llama-3.1-8B-shaped KV, {Lyr} layers in groups of {G}, {H} KV heads x {d}, "
+        "config": {"workload": f"{c.name}: {shape} KV, {Lyr} layers in groups of {G}, {H} KV heads x {d}, "
                                f"{Hq} q heads, T={T}, r={r} (K and V), xKV-SR, top-k {c.top_k} chunks of {c.chunk} "
-                               f"+ {c.n_sink} sink + {c.n_local} local, {D} decode steps, batch 1",
-                   "T": T, "layers": Lyr, "group": G, "rank": r, "top_k": c.top_k, "decode_steps": D},
+                               f"+ {c.n_sink} sink + {c.n_local} local, {D} decode steps, batch {B}",
+                   "T": T, "layers": Lyr, "group": G, "rank": r, "top_k": c.top_k, "decode_steps": D, "batch": B},
         "sr_decode_us_per_step": round(dec_us, 2),
         "sr_decode_GBps": round(sr_gbps, 1),
         "sr_decode_bytes_per_step": int(decode_bytes_step),
-        "compress_tokens_per_s": round(T / comp_s, 1),
+        "compress_tokens_per_s": round(B * T / comp_s, 1),
         "compress_s": round(comp_s, 4),
         "compress_stats": {"err_est_max": float(max(st[0] for st in stats)), "sweeps": int(stats[0][2]),
-                           "rounds": int(stats[0][3])},
+                           "rounds": int(stats[0][3]), "sides": S, "calls": len(calls),
+                           "sides_not_converged": notconv[0]},
         "roofline": {"bound": "hbm", "kernel": "sr_attend_mfma_kernel<false, false>", "achieved": round(achieved_att, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
@@ -403,9 +450,15 @@ def main():
                      "timed_launches": "one layer per decode step (layer = step mod layers), every timed step"},
         "roofline_gram": {"bound": "mfma", "kernel": "gram_bf16_kernel", "achieved": round(gram_tflops, 1),
                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
-                          "launch_ms": round(gram_ms, 3), "sides": S, "traffic": gram_traffic,
+                          "launch_ms": round(gram_ms, 3), "sides": Sg, "traffic": gram_traffic,
                           "traffic_unit": "L2-miss bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                          "unique_input_bytes": int(S * T * n * esz)},
+                          "unique_input_bytes": int(Sg * T * n * esz)},
+        "roofline_project": {"bound": "mfma", "kernel": "project_bf16_kernel", "achieved": round(proj_tflops, 1),
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4), "ms_all_sides": round(proj_ms, 3),
+                             "sides": Sg, "flops": "2 T n r per side",
+                             "timed": "one projection launch per side (+ a 2 MiB transpose of the basis each)",
+                             "matches_compression_output": proj_same},
         "dense_baseline": dense,
         "sr_speedup_vs_dense": round(dense["us_per_step"] / dec_us, 3) if dense else None,
         "sr_variants": variants or None,
@@ -414,8 +467,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, wl, layers, q_all, kn_all if c.append else None,
-                                            vn_all if c.append else None, rows, D)
+        line["cpu_baseline"] = cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D)
     print(json.dumps(line), flush=True)
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
@@ -433,21 +485,22 @@ def dense_baseline(xk, ctx, c, layers, q_all, kn_all, vn_all, D, reps):
     standard cache holds them, rotated on the GPU before timing), n_ctx = T + s + 1 at step s.
     Returns its time per decode step over all layers and its achieved HBM rate."""
     dev = q_all.device
-    Lyr, T, d_kv, H, d, Hq = c.n_layers, c.T, c.d_kv, c.n_kv_heads, c.head_dim, c.n_q_heads
+    B, Lyr, T, d_kv, H, d, Hq = c.batch, c.n_layers, c.T, c.d_kv, c.n_kv_heads, c.head_dim, c.n_q_heads
     if c.torch_dtype != torch.bfloat16 or d != 128 or Hq // H > 8:
         return None
     n_max = T + (D if kn_all is not None else 0)
-    dk = torch.empty((Lyr, n_max, d_kv), dtype=c.torch_dtype, device=dev)
+    dk = torch.empty((Lyr, B, n_max, d_kv), dtype=c.torch_dtype, device=dev)
     dv = torch.empty_like(dk)
     for l in range(Lyr):
-        xk.rope_rows(layers[("K", l)], dk[l, :T], 0, H, d, c.rope_theta)
-        dv[l, :T] = layers[("V", l)]
-        if kn_all is not None:
-            xk.rope_rows(kn_all[:, l].contiguous(), dk[l, T:], T, H, d, c.rope_theta)
-            dv[l, T:] = vn_all[:, l]
-    out = torch.empty((Lyr, Hq, d), dtype=torch.float32, device=dev)
+        for b in range(B):
+            xk.rope_rows(layers[(b, "K", l)], dk[l, b, :T], 0, H, d, c.rope_theta)
+            dv[l, b, :T] = layers[(b, "V", l)]
+            if kn_all is not None:
+                xk.rope_rows(kn_all[:, l, b].contiguous(), dk[l, b, T:], T, H, d, c.rope_theta)
+                dv[l, b, T:] = vn_all[:, l, b]
+    out = torch.empty((Lyr, B, Hq, d), dtype=torch.float32, device=dev)
     n_ctx = [T + s + 1 if kn_all is not None else T for s in range(D)]
-    args = [[xk.dense_args(batch=1, n_q_heads=Hq, n_kv_heads=H, head_dim=d, n_ctx=n_ctx[s], q_pos=n_ctx[s] - 1,
+    args = [[xk.dense_args(batch=B, n_q_heads=Hq, n_kv_heads=H, head_dim=d, n_ctx=n_ctx[s], q_pos=n_ctx[s] - 1,
                            dtype=xk.XKV_BF16, scale=1.0 / math.sqrt(d), rope_theta=c.rope_theta, q=q_all[s, l],
                            K=dk[l], V=dv[l], ld_kv=d_kv, bstride_kv=n_max * d_kv, out=out[l])
              for l in range(Lyr)] for s in range(D)]
@@ -469,7 +522,7 @@ def dense_baseline(xk, ctx, c, layers, q_all, kn_all, vn_all, D, reps):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / D * 1e3)
     us = float(np.median(times))
-    nbytes = float(np.mean([Lyr * (2 * n * d_kv * 2 + Hq * d * 2 + Hq * d * 4) for n in n_ctx]))
+    nbytes = float(np.mean([B * Lyr * (2 * n * d_kv * 2 + Hq * d * 2 + Hq * d * 4) for n in n_ctx]))
     del dk, dv
     return {"us_per_step": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_step": int(nbytes),
@@ -494,26 +547,26 @@ def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):
         A_k, Bk = (f64(x) for x in wl.factor_cache(0, "K", l, c.rank))
         A_v, Bv = (f64(x) for x in wl.factor_cache(0, "V", l, c.rank))
         Bk, Bv = Bk.T, Bv.T
-        Kl, Vl = layers[("K", l)], layers[("V", l)]
+        Kl, Vl = layers[(0, "K", l)], layers[(0, "V", l)]
         lm = oracle.landmarks(f64(Kl), c.n_kv_heads, c.head_dim, c.chunk, c.rope_theta)
         k_ex = {t: f64(Kl[t]) for t in rows}
         v_ex = {t: f64(Vl[t]) for t in rows}
         for s in sample_steps:
             if c.append:
-                k_ex[c.T + s] = f64(kn_all[s, l])
-                v_ex[c.T + s] = f64(vn_all[s, l])
-            q = f64(q_all[s, l])
+                k_ex[c.T + s] = f64(kn_all[s, l, 0])
+                v_ex[c.T + s] = f64(vn_all[s, l, 0])
+            q = f64(q_all[s, l, 0])
             t0 = time.perf_counter()
             oracle.sr_decode_layer(q, T=c.T, n_gen=(s + 1) if c.append else 0, n_kv_heads=c.n_kv_heads,
                                    chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink, n_local=c.n_local,
                                    landmarks_l=lm, A_k=A_k, B_k_l=Bk, A_v=A_v, B_v_l=Bv, k_exact=k_ex, v_exact=v_ex)
             t_dec += time.perf_counter() - t0
     per_layer_step = t_dec / (len(sample_layers) * len(sample_steps))
-    us_per_step = per_layer_step * c.n_layers * 1e6
+    us_per_step = per_layer_step * c.n_layers * c.batch * 1e6
     # Compression sample: the oracle's factorisation of one group side (K of group 0) on its
     # first 16384 tokens; the Gram/projection parts scale with T, the n x n eigensolve does not.
     T_s = min(16384, c.T)
-    Ks = [f64(layers[("K", i)][:T_s]) for i in range(c.group)]
+    Ks = [f64(layers[(0, "K", i)][:T_s]) for i in range(c.group)]
     t0 = time.perf_counter()
     X = oracle.group_matrix(Ks)
     C_ = oracle.gram(X)
@@ -526,15 +579,15 @@ def cpu_baseline(c, wl, layers, q_all, kn_all, vn_all, rows, D):
     t4 = time.perf_counter()
     scale = c.T / T_s
     side_s = (t1 - t0 + t3 - t2 + (t4 - t3) * c.group) * scale + (t2 - t1)
-    n_sides = 2 * c.n_groups
+    n_sides = 2 * c.n_groups * c.batch
     comp_s = side_s * n_sides
     return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(cores), "kind": "oracle",
             "sample": f"SR decode of layers 0-1 at decode steps 0-{len(sample_steps) - 1} "
                       f"({len(sample_layers) * len(sample_steps)} layer-steps, on a stand-in cache of the same shapes), "
-                      f"scaled x{c.n_layers} layers; compression of one group side on its first {T_s} tokens "
+                      f"scaled x{c.n_layers} layers x{c.batch} sequences; compression of one group side on its first {T_s} tokens "
                       f"(Gram+projection+landmarks scaled x{scale:g} in T, eigensolve of n={c.n} once), "
                       f"scaled x{n_sides} sides",
-            "compress_tokens_per_s": round(c.T / comp_s, 2),
+            "compress_tokens_per_s": round(c.batch * c.T / comp_s, 2),
             "sample_seconds": round(t_dec + (t4 - t0), 2)}
 
 

@@ -286,6 +286,34 @@ def main():
     comp_s = float(np.median(t_comp))
     sr_gbps = decode_bytes_step / (dec_us * 1e-6) / 1e9
 
+    # ---- the same decode steps replayed from a HIP graph (one capture of all D steps; the
+    # appends rewrite the same tail rows with the same values, so a replay repeats the
+    # eager run exactly): the launch path's share of the step time ----
+    graph = None
+    if not args.no_extras:
+        out_eager, sel_eager = out.clone(), sel.clone()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for s in range(D):
+                L.sr_decode_layers(ctx, step_args[s], dec.ws)
+        torch.cuda.synchronize()
+        times, same = [], True
+        for _ in range(max(args.steps, 2)):
+            out.zero_()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / D * 1e3)
+            same = same and bool(torch.equal(out, out_eager)) and bool(torch.equal(sel, sel_eager))
+        graph = {"us_per_step": round(float(np.median(times)), 2), "replays_match_eager": same,
+                 "launches_per_step": 4 * Lyr}
+        del g
+
     # ---- dense flash-decode baseline: the same queries over the full post-RoPE cache ----
     dense = dense_baseline(xk, ctx, c, layers, q_all, kn_all, vn_all, D, args.steps) if not args.no_extras else None
     # ---- the SR variants on the same cache (batch 1): xK-SR (values exact, on the GPU) and
@@ -370,8 +398,24 @@ def main():
             layer0[s_] = {"ner": round(rs["ner"], 5), "erank": round(rs["erank"], 2),
                           "rank95_frac": round(rs["energy_rank"] / float(d_kv), 4)}
         del single
+        # Adaptive rank at the uniform budget (every side of sequence 0 at r): one more
+        # compression at r_max = r + 128 gives each side's leading eigenvalues; ranks are
+        # multiples of 128 in [r - 128, r + 128].
+        adaptive = None
+        if r > 128 and r + 128 <= n:
+            seq0 = sides[:2 * n_groups]          # the sides are ordered by sequence, group, K / V
+            wide = xk.compress(ctx, [sd["layers"] for sd in seq0], r=r + 128, n_kv_heads=H, head_dim=d,
+                               landmarks=[False] * len(seq0), allow_notconv=True)
+            torch.cuda.synchronize()
+            tr = sum(o["stats"]["energy"] for o in wide)
+            ranks_a, kept_a = xk.rank_allocate([o["eigvals"] for o in wide], len(seq0) * r, 128, r - 128, r + 128)
+            kept_u = sum(float(np.sum(o["eigvals"][:r])) for o in wide)
+            adaptive = {"budget": len(seq0) * r, "ranks": ranks_a, "sides": "K, V of each group of sequence 0",
+                        "rel_err_uniform": round(math.sqrt(max(0.0, 1 - kept_u / tr)), 6),
+                        "rel_err_adaptive": round(math.sqrt(max(0.0, 1 - kept_a / tr)), 6)}
+            del wide
         rank_diag = {"group_rank95_frac": {k: [None if v is None else round(v, 4) for v in vs] for k, vs in grp.items()},
-                     "layer0": layer0,
+                     "layer0": layer0, "adaptive_rank": adaptive,
                      "note": "rank95_frac = rank holding 95 % of the eigenvalue sum / dimension; group sides "
                              f"of sequence 0 from the {r} leading Ritz values and trace(C) (None: beyond {r})"}
 
@@ -433,6 +477,7 @@ def main():
                                f"+ {c.n_sink} sink + {c.n_local} local, {D} decode steps, batch {B}",
                    "T": T, "layers": Lyr, "group": G, "rank": r, "top_k": c.top_k, "decode_steps": D, "batch": B},
         "sr_decode_us_per_step": round(dec_us, 2),
+        "sr_decode_graph": graph,
         "sr_decode_GBps": round(sr_gbps, 1),
         "sr_decode_bytes_per_step": int(decode_bytes_step),
         "compress_tokens_per_s": round(B * T / comp_s, 1),

@@ -351,6 +351,26 @@ typedef struct {
 
 int xkv_rank_stats(const double* eigvals, int n_vals, double total, double frac, int complete, xkv_rank_info* out);
 
+/* Adaptive rank at a fixed total budget ([KV-CoRE] implications: compressibility
+ * differs across layers and should guide a layer-aware compression strategy;
+ * [xKV blog] figure 5: the rank that pays off differs by task).  Side s keeps r_s
+ * of its leading eigenvalues, r_s a multiple of `granule` in [r_min, r_max], with
+ * sum_s r_s <= budget, chosen to keep the most energy
+ * sum_s sum_{i < r_s} lambda_i^(s), i.e. (Eckart-Young) the least total squared
+ * reconstruction error of the rank-r_s truncations.  A side compressed at rank
+ * r_max and truncated to its first r_s columns of A and rows of B is exactly its
+ * rank-r_s factorisation (the columns of V_r come in eigenvalue order), so the
+ * caller compresses once at r_max and decodes each side with r_k / r_v = r_s and
+ * the r_max leading dimensions (a granule of 128 keeps the decode on the matrix
+ * cores).
+ * eigvals (host): n_sides rows, row stride ld >= r_max, each the side's leading
+ * eigenvalues in descending order (the eigvals of xkv_compress_sides at r_max).
+ * ranks (host, out): n_sides ints; kept (host, out, nullable): the energy kept.
+ * Host only.  Errors: XKV_EINVAL (NULL pointers, ranks not multiples of the
+ * granule, r_min > r_max, ld < r_max, budget < n_sides * r_min). */
+int xkv_rank_allocate(const double* eigvals, int n_sides, int ld, int r_max, long budget, int granule, int r_min,
+                      int* ranks, double* kept);
+
 /* ------------------------------------------------------------------------ */
 /* Component entry points used by the parity tests                           */
 /* ------------------------------------------------------------------------ */

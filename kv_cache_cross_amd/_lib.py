@@ -108,6 +108,7 @@ def lib():
         L.xkv_dense_ws_size.argtypes = [C.POINTER(DenseArgs), C.POINTER(sz)]
         L.xkv_dense_decode.argtypes = [vp, C.POINTER(DenseArgs), vp, sz, vp]
         L.xkv_rank_stats.argtypes = [C.POINTER(C.c_double), i, C.c_double, C.c_double, i, C.POINTER(RankInfo)]
+        L.xkv_rank_allocate.argtypes = [vp, i, i, i, l, i, i, vp, vp]
         L.xkv_append_ws_size.argtypes = [C.POINTER(AppendArgs), C.POINTER(sz)]
         L.xkv_compress_append.argtypes = [vp, C.POINTER(AppendArgs), vp, sz, vp]
         L.xkv_rope_rows.argtypes = [vp, l, vp, l, i, l, i, i, C.c_double, i, vp]
@@ -338,6 +339,18 @@ def rank_stats(eigvals, total: float = 0.0, frac: float = 0.95, complete: bool =
     _check(lib().xkv_rank_stats(v.ctypes.data_as(C.POINTER(C.c_double)), v.size, float(total), float(frac),
                                 int(bool(complete)), C.byref(out)))
     return {name: getattr(out, name) for name, _ in RankInfo._fields_}
+
+
+def rank_allocate(spectra, budget: int, granule: int, r_min: int, r_max: int):
+    """Per-side ranks at a total budget (host only): returns (ranks, kept energy).
+    `spectra`: one sequence of at least r_max leading eigenvalues per side, descending."""
+    S = len(spectra)
+    eig = np.ascontiguousarray(np.stack([np.asarray(x, dtype=np.float64)[:r_max] for x in spectra]))
+    ranks = np.zeros(S, dtype=np.int32)
+    kept = np.zeros(1, dtype=np.float64)
+    _check(lib().xkv_rank_allocate(eig.ctypes.data, S, r_max, r_max, int(budget), granule, r_min, ranks.ctypes.data,
+                                   kept.ctypes.data))
+    return [int(x) for x in ranks], float(kept[0])
 
 
 def dense_args(**kw) -> DenseArgs:

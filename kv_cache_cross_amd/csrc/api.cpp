@@ -19,6 +19,8 @@
 #include "xkv_kernels.h"
 
 #include "host_eigh.h"
+extern "C" int xkv_rank_allocate_impl(const double* eig, int n_sides, int ld, int r_max, long budget, int granule,
+                                      int r_min, int* ranks, double* kept);
 extern "C" int xkv_rank_stats_impl(const double* vals, int n, double total, double frac, int complete,
                                    int* energy_rank, double* covered, int* num_rank, double* erank, double* ner);
 
@@ -131,6 +133,17 @@ int xkv_rank_stats(const double* eigvals, int n_vals, double total, double frac,
   if (xkv_rank_stats_impl(eigvals, n_vals, total, frac, complete, &out->energy_rank, &out->covered,
                           &out->numerical_rank, &out->erank, &out->ner))
     return fail(XKV_EINVAL, "xkv_rank_stats: out of host memory");
+  return XKV_OK;
+}
+
+int xkv_rank_allocate(const double* eigvals, int n_sides, int ld, int r_max, long budget, int granule, int r_min,
+                      int* ranks, double* kept) {
+  const int rc = xkv_rank_allocate_impl(eigvals, n_sides, ld, r_max, budget, granule, r_min, ranks, kept);
+  if (rc == -2) return fail(XKV_EINVAL, "xkv_rank_allocate: out of host memory");
+  if (rc)
+    return fail(XKV_EINVAL, "xkv_rank_allocate: bad arguments (n_sides=%d, ld=%d, r_max=%d, budget=%ld, "
+                "granule=%d, r_min=%d; ranks are multiples of the granule, r_min <= r_max <= ld, "
+                "budget >= n_sides * r_min)", n_sides, ld, r_max, budget, granule, r_min);
   return XKV_OK;
 }
 

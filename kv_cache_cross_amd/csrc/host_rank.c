@@ -75,3 +75,60 @@ int xkv_rank_stats_impl(const double* vals, int n, double total, double frac, in
   free(lam);
   return 0;
 }
+
+/*
+ * Adaptive rank at a fixed budget (KV-CoRE, implications: compressibility differs
+ * across layers and should guide a layer-aware compression strategy).  Side s keeps
+ * r_s of its leading eigenvalues, r_s a multiple of `granule` in [r_min, r_max], with
+ * sum r_s <= budget, so as to keep the most energy sum_s sum_{i < r_s} lambda_i^(s)
+ * (by Eckart-Young, the least total squared reconstruction error).  Because each
+ * side's eigenvalues are non-increasing, so are the energies of its successive
+ * granules, and taking granules one at a time from the side whose next granule holds
+ * the most energy (ties to the lower side) reaches the optimum.
+ *
+ * eig: n_sides rows of ld >= r_max values, each row descending.  Returns 0, -1 (bad
+ * arguments or a budget below r_min on every side) or -2 (out of host memory).
+ */
+int xkv_rank_allocate_impl(const double* eig, int n_sides, int ld, int r_max, long budget, int granule, int r_min,
+                           int* ranks, double* kept) {
+  if (!eig || !ranks || n_sides <= 0 || granule <= 0 || r_min < 0 || r_min % granule || r_max % granule ||
+      r_min > r_max || ld < r_max || budget < (long)n_sides * r_min)
+    return -1;
+  double* next = (double*)malloc(sizeof(double) * (size_t)n_sides);
+  if (!next) return -2;
+  double total = 0.0;
+  long left = budget;
+  for (int s = 0; s < n_sides; ++s) {
+    ranks[s] = r_min;
+    for (int i = 0; i < r_min; ++i) total += eig[(long)s * ld + i] > 0.0 ? eig[(long)s * ld + i] : 0.0;
+    left -= r_min;
+  }
+  /* energy of the granule after side s's current rank (-1 when at r_max) */
+  for (int s = 0; s < n_sides; ++s) {
+    double e = -1.0;
+    if (ranks[s] < r_max) {
+      e = 0.0;
+      for (int i = ranks[s]; i < ranks[s] + granule; ++i) e += eig[(long)s * ld + i] > 0.0 ? eig[(long)s * ld + i] : 0.0;
+    }
+    next[s] = e;
+  }
+  while (left >= granule) {
+    int best = -1;
+    for (int s = 0; s < n_sides; ++s)
+      if (next[s] >= 0.0 && (best < 0 || next[s] > next[best])) best = s;
+    if (best < 0) break;
+    total += next[best];
+    ranks[best] += granule;
+    left -= granule;
+    double e = -1.0;
+    if (ranks[best] < r_max) {
+      e = 0.0;
+      for (int i = ranks[best]; i < ranks[best] + granule; ++i)
+        e += eig[(long)best * ld + i] > 0.0 ? eig[(long)best * ld + i] : 0.0;
+    }
+    next[best] = e;
+  }
+  free(next);
+  if (kept) *kept = total;
+  return 0;
+}

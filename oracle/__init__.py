@@ -31,4 +31,5 @@ from .xkv_ref import (  # noqa: F401
     effective_rank,
     ner,
     energy_rank,
+    allocate_ranks,
 )

@@ -330,3 +330,56 @@ def energy_rank(eigvals, frac: float = 0.95, total: float | None = None) -> int:
         return 0
     hit = np.nonzero(csum >= frac * tot)[0]
     return int(hit[0]) + 1 if hit.size else -1
+
+
+# ---------------------------------------------------------------------------
+# Adaptive rank: per-side ranks from the spectra at a fixed total budget
+# ([KV-CoRE] implications: compressibility differs across layers and should
+# guide a layer-aware compression strategy; [xKV blog] figure 5: the rank that
+# pays off differs by task)
+# ---------------------------------------------------------------------------
+def allocate_ranks(spectra, budget: int, granule: int, r_min: int, r_max: int):
+    """Ranks r_s (multiples of `granule` in [r_min, r_max]) with sum r_s <= budget that
+    keep the most energy sum_s sum_{i < r_s} lambda_i^(s), i.e. (Eckart-Young, [KQ-SVD]
+    3.3) that minimise the total squared reconstruction error sum_s sum_{i >= r_s}
+    lambda_i^(s) of the sides' rank-r_s truncations.  `spectra[s]` holds side s's
+    leading eigenvalues (at least r_max, any order).  Exact dynamic programme over the
+    sides.  Returns (ranks, kept energy); ValueError when even r_min everywhere does
+    not fit the budget."""
+    S = len(spectra)
+    if granule <= 0 or r_min % granule or r_max % granule or r_min > r_max:
+        raise ValueError("ranks must be multiples of the granule with r_min <= r_max")
+    kmin, kmax, B = r_min // granule, r_max // granule, budget // granule
+    if S * kmin > B:
+        raise ValueError("budget below r_min on every side")
+    # kept[s][k]: energy of side s's first k granules.
+    kept = []
+    for lam in spectra:
+        lam = np.sort(np.clip(np.asarray(lam, dtype=np.float64), 0.0, None))[::-1]
+        if lam.size < r_max:
+            raise ValueError("each spectrum needs at least r_max values")
+        kept.append([float(np.sum(lam[:k * granule])) for k in range(kmax + 1)])
+    NEG = -np.inf
+    best = [[NEG] * (B + 1) for _ in range(S + 1)]   # best[s][b]: first s sides, b granules
+    pick = [[-1] * (B + 1) for _ in range(S + 1)]
+    best[0][0] = 0.0
+    for s in range(S):
+        for b in range(B + 1):
+            if best[s][b] == NEG:
+                continue
+            for k in range(kmin, kmax + 1):
+                if b + k > B:
+                    break
+                v = best[s][b] + kept[s][k]
+                if v > best[s + 1][b + k]:
+                    best[s + 1][b + k] = v
+                    pick[s + 1][b + k] = k
+    b_end = int(np.argmax(best[S]))
+    total = best[S][b_end]
+    ranks = [0] * S
+    b = b_end
+    for s in range(S, 0, -1):
+        k = pick[s][b]
+        ranks[s - 1] = k * granule
+        b -= k
+    return ranks, total

@@ -385,3 +385,47 @@ def test_decode_deterministic(ctx):
     o2 = dec.decode(args).clone()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+def test_decode_unequal_key_value_ranks(ctx):
+    # Keys and values compressed at different ranks (r_k = 256, r_v = 128, as an adaptive
+    # allocation may choose) take the generic attend kernel; the same oracle-built cache on
+    # both sides, with leading dimensions wider than the ranks (a rank-256 factorisation
+    # truncated to its first 128 columns).
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, latent_rank=384))
+    c = wl.cfg
+    d_kv, T, layer, steps = c.d_kv, c.T, 1, 3
+    Ks, Vs = wl.group_kv(0, "K", 0), wl.group_kv(0, "V", 0)
+    ok = oracle.compress_group([f64(x) for x in Ks], 256)
+    ov = oracle.compress_group([f64(x) for x in Vs], 256)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(c.torch_dtype).to(DEV)
+    A_k, Bt_k = to(ok["A"]), to(ok["B"][:, layer * d_kv:(layer + 1) * d_kv].T)
+    A_v, Bt_v = to(ov["A"])[:, :128], to(ov["B"][:, layer * d_kv:(layer + 1) * d_kv].T)[:, :128]
+    lm = to(oracle.landmarks(f64(Ks[layer]), c.n_kv_heads, c.head_dim, c.chunk, c.rope_theta))
+    dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim, T=T,
+                          chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink, n_local=c.n_local, r_k=256, r_v=128,
+                          dtype=c.torch_dtype, device=DEV, max_gen=steps)
+    rows = tail_rows(T, c.n_sink, c.n_local)
+    k_tail = torch.zeros((len(rows) + steps, d_kv), dtype=c.torch_dtype, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:len(rows)] = Ks[layer][rows]
+    v_tail[:len(rows)] = Vs[layer][rows]
+    k_ex = {t: f64(Ks[layer][t]) for t in rows}
+    v_ex = {t: f64(Vs[layer][t]) for t in rows}
+    for s in range(steps):
+        q = wl.query(0, layer, s)
+        kn, vn = wl.new_token(0, "K", layer, s), wl.new_token(0, "V", layer, s)
+        k_ex[T + s], v_ex[T + s] = f64(kn), f64(vn)
+        out = dec.decode(dec.args(n_gen=s + 1, q=q, A_k=A_k, Bt_k=Bt_k, A_v=A_v, Bt_v=Bt_v, landmarks=lm,
+                                  k_tail=k_tail, v_tail=v_tail, k_new=kn, v_new=vn))
+        torch.cuda.synchronize()
+        kw = dict(T=T, n_gen=s + 1, n_kv_heads=c.n_kv_heads, chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink,
+                  n_local=c.n_local, landmarks_l=f64(lm), A_k=f64(A_k), B_k_l=f64(Bt_k).T, A_v=f64(A_v),
+                  B_v_l=f64(Bt_v).T, k_exact=k_ex, v_exact=v_ex)
+        ref = oracle.sr_decode_layer(f64(q), **kw)
+        sel = dec.sel.cpu().numpy()[0]
+        if sum(check_selection(sel[h], ref["scores"][h], c.top_k) for h in range(c.n_kv_heads)):
+            ref = oracle.sr_decode_layer(f64(q), selection=sel, **kw)
+        rel, mx = attention_errors(f64(out)[0], ref["out"])
+        log(f"  r_k 256, r_v 128, step {s}: rel L2 {rel:.2e}, max abs {mx:.2e}")
+        assert rel <= 1e-3 and mx <= ATT_ABS_BF16

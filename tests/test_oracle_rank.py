@@ -83,3 +83,83 @@ def test_energy_rank_full_fraction_reaches_last_nonzero():
     for n in (7, 100, 1000):
         lam = np.r_[rng.random(n) + 0.5, np.zeros(5)]
         assert oracle.energy_rank(lam, 1.0) == n
+
+
+# ------------------------------------------------------------------ adaptive rank
+def _brute_alloc(spectra, budget, granule, r_min, r_max):
+    """Every combination of ranks, the best kept energy (independent of the DP)."""
+    import itertools
+    opts = list(range(r_min, r_max + 1, granule))
+    best = -1.0
+    for combo in itertools.product(opts, repeat=len(spectra)):
+        if sum(combo) > budget:
+            continue
+        e = sum(float(np.sum(np.sort(lam)[::-1][:r])) for lam, r in zip(spectra, combo))
+        best = max(best, e)
+    return best
+
+
+def test_allocate_ranks_hand_case():
+    # Sides (10, 1, 1, 1) and (5, 4, 3, 2), one eigenvalue per granule, four in all: the
+    # four largest are 10, 5, 4, 3, so side 0 keeps one and side 1 three (kept 22).
+    ranks, kept = oracle.allocate_ranks([[10, 1, 1, 1], [5, 4, 3, 2]], budget=4, granule=1, r_min=0, r_max=4)
+    assert ranks == [1, 3] and kept == 22.0
+    # A floor of two per side: 10 + 1 + 5 + 4 = 20.
+    ranks, kept = oracle.allocate_ranks([[10, 1, 1, 1], [5, 4, 3, 2]], budget=4, granule=1, r_min=2, r_max=4)
+    assert ranks == [2, 2] and kept == 20.0
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_allocate_ranks_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    S, g = 3, 2
+    spectra = [np.sort(rng.exponential(size=8) ** 2)[::-1] * rng.uniform(0.2, 5) for _ in range(S)]
+    for budget in (6, 9, 12, 17, 24):
+        ranks, kept = oracle.allocate_ranks(spectra, budget, g, 2, 8)
+        assert sum(ranks) <= budget and all(2 <= r <= 8 and r % g == 0 for r in ranks)
+        assert kept == pytest.approx(sum(float(np.sum(l[:r])) for l, r in zip(spectra, ranks)), rel=1e-14)
+        assert kept == pytest.approx(_brute_alloc(spectra, budget, g, 2, 8), rel=1e-14)
+
+
+def test_allocate_ranks_equal_spectra_is_uniform():
+    # Identical, strictly decreasing spectra: every extra granule is worth less than the one
+    # before, so the budget splits evenly.
+    lam = 1.0 / np.arange(1, 65) ** 0.8
+    ranks, _ = oracle.allocate_ranks([lam] * 4, budget=4 * 24, granule=8, r_min=8, r_max=64)
+    assert ranks == [24, 24, 24, 24]
+
+
+def test_allocated_ranks_minimise_the_reconstruction_error():
+    # The objective is the reconstruction error of the truncated factorisations: the tail
+    # sums equal ||X_s - A_s B_s||_F^2 of the oracle's own rank-r_s compressions, and no
+    # other allocation of the same budget does better.
+    rng = np.random.default_rng(7)
+    sides = []
+    for s, decay in enumerate((0.4, 1.2, 2.0)):
+        U = rng.standard_normal((200, 24))
+        W = rng.standard_normal((24, 24)) * (np.arange(1, 25) ** -decay)[:, None]
+        sides.append([U @ W[:, :12] + 0.01 * rng.standard_normal((200, 12)),
+                      U @ W[:, 12:] + 0.01 * rng.standard_normal((200, 12))])
+    spectra = [np.linalg.eigvalsh(oracle.gram(oracle.group_matrix(x)))[::-1] for x in sides]
+    ranks, kept = oracle.allocate_ranks(spectra, budget=24, granule=4, r_min=4, r_max=20)
+    err = sum(np.linalg.norm(oracle.group_matrix(x) - (lambda c: c["A"] @ c["B"])(oracle.compress_group(x, r))) ** 2
+              for x, r in zip(sides, ranks))
+    total = sum(float(np.sum(l)) for l in spectra)
+    assert err == pytest.approx(total - kept, rel=1e-9)
+    assert ranks[0] > ranks[2]     # the slowly decaying side gets the larger share
+    for alt in ([8, 8, 8], [12, 8, 4], [4, 8, 12]):
+        e_alt = sum(np.linalg.norm(oracle.group_matrix(x) - (lambda c: c["A"] @ c["B"])(oracle.compress_group(x, r)))
+                    ** 2 for x, r in zip(sides, alt))
+        assert err <= e_alt * (1 + 1e-12)
+
+
+def test_allocate_ranks_budget_monotone_and_errors():
+    rng = np.random.default_rng(9)
+    spectra = [np.sort(rng.random(32))[::-1] for _ in range(5)]
+    prev = -1.0
+    for budget in range(20, 161, 20):
+        _, kept = oracle.allocate_ranks(spectra, budget, 4, 4, 32)
+        assert kept >= prev
+        prev = kept
+    with pytest.raises(ValueError):
+        oracle.allocate_ranks(spectra, 10, 4, 4, 32)          # 5 sides x 4 > 10

@@ -498,7 +498,7 @@ def main():
                           "launch_ms": round(gram_ms, 3), "sides": Sg, "traffic": gram_traffic,
                           "traffic_unit": "L2-miss bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                           "unique_input_bytes": int(Sg * T * n * esz)},
-        "roofline_project": {"bound": "mfma", "kernel": "project_bf16_kernel", "achieved": round(proj_tflops, 1),
+        "roofline_project": {"bound": "mfma", "kernel": "project_tile_kernel", "achieved": round(proj_tflops, 1),
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4), "ms_all_sides": round(proj_ms, 3),
                              "sides": Sg, "flops": "2 T n r per side",

@@ -4,11 +4,13 @@
 //
 // bf16 projection: both operands are contiguous along the contracted
 // dimension (X rows along columns of the group, VrT rows along the group
-// columns), so a 128 x 128 output tile stages 128 x 64 slices of each
-// through LDS with 16-byte loads (double buffered) and feeds
-// v_mfma_f32_32x32x16_bf16 with one 16-byte LDS read per operand.  The rank
-// tile is the fastest-varying workgroup index, so the workgroups that read
-// the same X rows run together and share them through L2.
+// columns).  When d_kv is a multiple of 32 (every workload), project_tile_kernel
+// computes 256 x 256 output tiles from 32-column slices loaded straight into LDS;
+// otherwise a 128 x 128 output tile stages 128 x 64 slices of each through LDS
+// with 16-byte loads (double buffered).  Both feed v_mfma_f32_32x32x16_bf16 with
+// one 16-byte LDS read per operand, and in both the rank tile is the
+// fastest-varying workgroup index, so the workgroups that read the same X rows
+// run together and share them through L2.
 //
 // Landmarks: m[l, h, c] = mean over the chunk's tokens of RoPE(K_l[t, h], t),
 // from the original keys, float32 sums, angle formed in float64.
@@ -110,6 +112,124 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(ProjArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int t = t0 + wm * 64 + mi * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+        const int c = j0 + wn * 64 + ni * 32 + (lane & 31);
+        if (t < a.T && c < a.r) Aout[(long)t * a.r + c] = f32_to_bf16_bits(acc[mi][ni][j]);
+      }
+}
+
+// bf16 projection, large tiles (d_kv a multiple of 32): one 512-thread workgroup per
+// 256 (tokens) x 256 (ranks) output tile, eight waves of 128 x 64 (4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16).  32-column slices of the contraction (one layer's
+// columns of the X rows, the same columns of VrT) go from memory straight into LDS
+// with direct-to-LDS loads, three slices ahead of the math, in a ring of four stages
+// of 32 blocks (16 rows x 32 columns, 1 KiB each).  In a block, 16-byte unit u holds
+// row u / 4 and column chunk (u % 4) ^ ((row / 2) % 4), so that the operand reads (one
+// 16-byte read per lane: a row's 8 consecutive columns) of any 8 consecutive lanes
+// touch distinct banks.
+constexpr int QT = 256;            // output tile edge (tokens and ranks)
+constexpr int QK = 32;             // contraction slice per stage
+constexpr int QSTAGE = 32 * 1024;  // bytes per stage: 16 blocks of X rows, 16 of VrT rows
+
+__global__ __launch_bounds__(512) void project_tile_kernel(ProjArgs a) {
+  __shared__ __align__(16) unsigned char st0[QSTAGE], st1[QSTAGE], st2[QSTAGE], st3[QSTAGE];
+  const int side = blockIdx.z;
+  const int j0 = blockIdx.x * QT;    // rank tile (fastest: the tiles that share X rows run together)
+  const int t0 = blockIdx.y * QT;    // token tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;   // wave tile: tokens wm*128.., ranks wn*64..
+  const uint16_t* VrT = a.VrT + side * a.sVT;
+
+  // Load role: wave w fills blocks 4w .. 4w+3 of a stage (0..15: X rows t0 + 16 b ..,
+  // 16..31: VrT rows j0 + 16 (b - 16) ..); lane l loads row l / 4 of its block, column
+  // chunk (l % 4) ^ ((l / 4 / 2) % 4).  Rows past T or r re-read the last row (never stored).
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
+  long roff[4];
+  bool is_x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int bidx = 4 * wave + i;
+    is_x[i] = bidx < 16;
+    if (is_x[i]) roff[i] = (long)min(t0 + 16 * bidx + lrow, a.T - 1) * a.ld;
+    else roff[i] = (long)min(j0 + 16 * (bidx - 16) + lrow, a.r - 1) * a.n;
+  }
+  auto dma = [&](int ks, unsigned char* stage) {
+    const int k0 = ks * QK;
+    const int l = k0 / a.d_kv;
+    const uint16_t* xl = (const uint16_t*)a.layers.p[side * a.G + l] + (k0 - l * a.d_kv) + 8 * lchunk;
+    const uint16_t* vr = VrT + k0 + 8 * lchunk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)((is_x[i] ? xl : vr) + roff[i]),
+          (__attribute__((address_space(3))) void*)(stage + (4 * wave + i) * 1024), 16, 0, 0);
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+
+  // Operand of lane l for k-step ks: row l % 32 of a 32-row tile (block (l % 32) / 16,
+  // row l % 16), column chunk 2 ks + l / 32.
+  const int rb = lane & 15;
+  int off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    off[ks] = ((lane >> 4) & 1) * 1024 + (rb * 4 + ((2 * ks + (lane >> 5)) ^ ((rb >> 1) & 3))) * 16;
+  auto compute = [&](const unsigned char* stage) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[4], bfr[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = as_bf16x8(*(const uint4*)(stage + (8 * wm + 2 * mi) * 1024 + off[ks]));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bfr[ni] = as_bf16x8(*(const uint4*)(stage + (16 + 4 * wn + 2 * ni) * 1024 + off[ks]));
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int nk = a.n / QK;
+  // Slice s: wait for its loads (vmcnt(8): this wave's loads of slices s+1, s+2 may still
+  // be in flight), barrier (every wave's loads of s have landed and the reads of s - 1
+  // are over), start slice s + 3 into the stage of s - 1, then the math.  Past the last
+  // slice the last one is loaded again so that the count of loads never varies.
+  auto body = [&](int s, unsigned char* cur, unsigned char* ahead) {
+    __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    dma(min(s + 3, nk - 1), ahead);
+    if (s < nk) compute(cur);
+  };
+  dma(0, st0);
+  dma(min(1, nk - 1), st1);
+  dma(min(2, nk - 1), st2);
+  for (int s = 0; s < nk; s += 4) {
+    body(s, st0, st3);
+    body(s + 1, st1, st0);
+    body(s + 2, st2, st1);
+    body(s + 3, st3, st2);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the workgroup
+
+  uint16_t* Aout = (uint16_t*)a.A_out.p[side];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + wm * 128 + mi * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
         const int c = j0 + wn * 64 + ni * 32 + (lane & 31);
         if (t < a.T && c < a.r) Aout[(long)t * a.r + c] = f32_to_bf16_bits(acc[mi][ni][j]);
       }
@@ -246,6 +366,11 @@ hipError_t launch_project_bf16(const PtrTable& layers, int n_sides, int G, long 
   a.n = G * d_kv;
   a.r = r;
   a.ld = ld;
+  if (d_kv % QK == 0) {
+    dim3 grid((r + QT - 1) / QT, (T + QT - 1) / QT, n_sides);
+    hipLaunchKernelGGL(project_tile_kernel, grid, dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)project_bf16_kernel,

@@ -311,8 +311,12 @@ def main():
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) / D * 1e3)
             same = same and bool(torch.equal(out, out_eager)) and bool(torch.equal(sel, sel_eager))
+        # the library's matrix-core path (bf16, head dim 128, rank a multiple of 128) with at most
+        # 16384 candidates selects the top-k inside the attend kernel: 3 launches per layer
+        n_cand_h = -(-(T - c.n_local) // c.chunk)
+        fused = dt == torch.bfloat16 and d == 128 and r % 128 == 0 and n_cand_h <= 16384
         graph = {"us_per_step": round(float(np.median(times)), 2), "replays_match_eager": same,
-                 "launches_per_step": 4 * Lyr}
+                 "launches_per_step": (3 if fused else 4) * Lyr}
         del g
 
     # ---- dense flash-decode baseline: the same queries over the full post-RoPE cache ----

@@ -739,7 +739,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   const int cps = 64 / a->chunk;   // chunks per attend block of 64 rows
   const int n_splits = (k_eff + cps - 1) / cps;
   if (n_cand > 32768) return fail(XKV_EUNSUPPORTED, "sr: at most 32768 candidate chunks per head");
-  const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 63) / 64);   // 64-row tiles
+  const int n_exact = std::max(1, (a->n_sink + a->n_local + a->n_gen + 15) / 16);   // 16-row tiles
   const int max_blocks = (mfma && !exact_v) ? 1088 : 257;   // rank-space / value-space merge
   if (n_splits + n_exact > max_blocks)
     return fail(XKV_EUNSUPPORTED, "sr: selected chunks plus exact-row tiles exceed %d attend blocks per head",
@@ -782,6 +782,8 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   p.q_pos = a->n_gen > 0 ? (long)a->T + a->n_gen - 1 : a->T;
   // Scoring blocks per head: about 128 candidates each, at most 64.
   p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));
+  p.ld_sc = (n_cand + 3) & ~3;
+  p.fuse_topk = mfma && k_eff > 0 && n_cand <= 16384;
   p.scale = a->scale; p.theta = a->rope_theta;
   for (int i = 0; i < a->head_dim / 2; ++i)
     p.turns[i] = std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI);
@@ -799,7 +801,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
 
   Carver c(nullptr);
   const size_t bh = (size_t)a->batch * a->n_kv_heads;
-  c.take<float>(bh * std::max(n_cand, 1));
+  c.take<float>(bh * std::max((n_cand + 3) & ~3, 4));
   c.take<float>(bh * std::max(n_splits, 1) * grp * (2 + vdim));
   c.take<float>(bh * n_exact * grp * (2 + a->head_dim));
   *ws_need = c.off;
@@ -809,7 +811,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
 void bind_sr_ws(xkv::SrParams* p, void* ws) {
   Carver c(ws);
   const size_t bh = (size_t)p->batch * p->Hkv;
-  p->scores = c.take<float>(bh * std::max(p->n_cand, 1));
+  p->scores = c.take<float>(bh * std::max(p->ld_sc, 4));
   p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->vdim));
   p->part_ex = c.take<float>(bh * p->n_exact * p->grp * (2 + p->d));
 }

@@ -1,23 +1,27 @@
 // Selective Reconstruction decode for one layer and one step (xKV blog,
 // section on Selective Reconstruction; decode attention as in KQ-SVD
-// section 3.2).  Four kernels, ordered by the stream (no device-scope fences
-// inside any of them: on this GPU such a fence writes back the XCD's L2):
+// section 3.2).  Three kernels on the matrix-core path, four otherwise, ordered by
+// the stream (no device-scope fences inside any of them: on this GPU such a fence
+// writes back the XCD's L2):
 //
-// sr_score_kernel (grid: KV heads x score_blocks x batch)
-//   * block (0, 0, b) appends the new token's pre-RoPE k, v to the exact tail;
-//   * every block forms the scaled, rotated query sum of the KV head's query
+// sr_score_kernel (grid: KV heads x (exact tiles + score_blocks) x batch)
+//   * the first blocks of each (head, sequence) attend one 64-row tile each of the
+//     exact rows (sink, local window, generated tokens), which do not depend on the
+//     selection, and leave a softmax partial (max, denominator, weighted value sum) per
+//     query head;
+//   * the first score block of head 0 appends the new token's pre-RoPE k, v to the
+//     exact tail;
+//   * every score block forms the scaled, rotated query sum of the KV head's query
 //     group and scores a slice of the candidate chunks against the landmarks
 //     (a GEMV that streams the landmarks once, each thread's loads issued
 //     before its arithmetic).
-// sr_topk_kernel (grid: KV heads x batch x (1 + exact tiles), 1024 threads):
-//   * the first KV heads x batch blocks load one head's scores into registers
-//     as order-preserving keys; a histogram over value buckets and a radix
-//     select inside the k-th key's bucket find the k-th key, and an
-//     index-ordered compaction writes the k chunk ids (ties to the lower id);
-//   * the other blocks attend one 64-row tile each of the exact rows (sink,
-//     local window, generated tokens), which do not depend on the selection,
-//     and leave a softmax partial (max, denominator, weighted value sum) per
-//     query head.
+// top-k selection (topk_keys): a head's scores become order-preserving keys in
+//   registers; a histogram over value buckets and a radix select inside the k-th key's
+//   bucket find the k-th key, and an index-ordered compaction yields the k chunk ids
+//   (ties to the lower id).  On the matrix-core path (up to 16384 candidates per head)
+//   every attend block runs it for its
+//   head (the scores come from L2) and keeps its own split's ids; otherwise
+//   sr_topk_kernel (one 1024-thread block per head and sequence) writes them all.
 // sr_attend_mfma_kernel (bf16, head_dim 128, r_k % 128 == 0 and r_v == r_k, or r_v == 0
 // with exact values (xK-SR); grid: KV heads x splits x batch, so one head's blocks
 // share an XCD and its B slices in L2; 512 threads, one block per CU)
@@ -52,9 +56,10 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int RB = 64;        // rows per attend block (generic path) and per exact-row tile
 constexpr int RBM = 64;       // rows per matrix-core attend block
-constexpr int ETR = 64;       // rows per exact-row tile
+constexpr int ETR = 16;       // rows per exact-row tile
 constexpr int MAXG = 8;       // largest query group per KV head
 constexpr int MAXD = 128;     // largest head dim
+constexpr int EROW = MAXD + 4;   // LDS row of a staged exact row (16-byte aligned rows)
 constexpr int KCH = 512;      // rank columns staged per pass (MFMA path)
 constexpr int AROW = KCH + 8; // padded LDS row of staged A rows (bf16 elements)
 constexpr int HROW = MAXD + 1;
@@ -101,8 +106,18 @@ XKV_DEV float lane_group_sum(float v, int lanes) {
   return v;
 }
 
+// Barrier for LDS hand-offs: this wave's LDS stores have completed (lgkmcnt(0)), then
+// s_barrier.  No memory fence: a workgroup fence would also wait for every global load
+// and direct-to-LDS load in flight, which the attend kernel keeps going across barriers.
+// The empty asm statements keep the compiler from moving memory accesses across it.
+XKV_DEV void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited for
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 constexpr int TKT = 1024;      // threads of a top-k block
-constexpr int TKW = TKT / 64;  // its waves
 
 // Wave-wide prefix sum / min / max with DPP moves (no LDS round trips): Hillis-Steele
 // steps of 1, 2, 4 and 8 lanes inside each row of 16, then the row totals carried across
@@ -137,35 +152,43 @@ XKV_DEV uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Inclusive prefix sum over the TKT threads of a block (`tmp` >= TKW ints).  No barrier
-// after the reads of tmp: the caller passes one before tmp is written again.
+// The top-k helpers below run in blocks of NT threads (NT / 64 waves, NT >= 256) and
+// hand data over through LDS only, so their barriers are lds_sync(): global and
+// direct-to-LDS loads a caller has in flight keep going across them.
+
+// Inclusive prefix sum over the NT threads of a block (`tmp` >= NT / 64 ints).  No
+// barrier after the reads of tmp: the caller passes one before tmp is written again.
+template <int NT>
 XKV_DEV int tk_scan_incl(int v, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_scan_add(v);
   if (lane == 63) tmp[wave] = v;
-  __syncthreads();
+  lds_sync();
   int add = 0;
-  for (int w = 0; w < wave; ++w) add += tmp[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64 - 1; ++w) add += (w < wave) ? tmp[w] : 0;   // independent reads
   return v + add;
 }
 
-// Block-wide minimum of lo and maximum of hi (`tmp` >= 2 * TKW ints).  As above, the
+// Block-wide minimum of lo and maximum of hi (`tmp` >= 2 NT / 64 ints).  As above, the
 // caller passes a barrier before tmp is written again.
+template <int NT>
 XKV_DEV void tk_minmax(uint32_t& lo, uint32_t& hi, uint32_t* tmp) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
   if (lane == 0) {
     tmp[wave] = lo;
-    tmp[TKW + wave] = hi;
+    tmp[NW + wave] = hi;
   }
-  __syncthreads();
+  lds_sync();
   lo = tmp[0];
-  hi = tmp[TKW];
+  hi = tmp[NW];
 #pragma unroll
-  for (int w = 1; w < TKW; ++w) {
+  for (int w = 1; w < NW; ++w) {
     lo = min(lo, tmp[w]);
-    hi = max(hi, tmp[TKW + w]);
+    hi = max(hi, tmp[NW + w]);
   }
 }
 
@@ -177,8 +200,10 @@ XKV_DEV float key_value(uint32_t key) {
 constexpr int NBK = 2048;   // linear value buckets of the first top-k pass
 
 // Ascending ids of the k largest of n order-preserving keys, ties to the lower id;
-// -1 padding when k > n.  A block of TKT threads; thread t holds keys t*KPT ..
-// t*KPT + KPT - 1 in registers (n <= TKT * KPT, KPT <= 32).
+// -1 padding when k > n.  Only positions [lo_out, hi_out) of that list are written, to
+// out[pos - lo_out] (a caller that needs the whole list passes 0, k).  A block of NT
+// threads; thread t holds keys t*KPT .. t*KPT + KPT - 1 in registers (n <= NT * KPT,
+// KPT <= 32).
 //
 // Pass 1 spreads the keys over NBK buckets linear in value between the minimum and
 // the maximum (a monotone map, so every key of a higher bucket is larger than every
@@ -187,19 +212,25 @@ constexpr int NBK = 2048;   // linear value buckets of the first top-k pass
 // keys one wave ranks them directly; otherwise an MSB-first radix select with 8-bit
 // digits, starting below the bits that b*'s keys share, resolves the k-th key exactly,
 // stopping as soon as the bin holding it is taken whole.  Non-finite extremes put every key in one bucket and leave the radix
-// select to do all the work.  `hist` holds NBK ints, `tmp` 2 * TKW, `bcast` 4.  The
+// select to do all the work.  `hist` holds NBK ints, `tmp` 2 NT / 64, `bcast` 4.  The
 // block's barriers are the ones the data hand-offs need (seven on the usual path); the
 // function ends without one, so a caller that reuses the buffers passes a barrier first.
-template <int KPT>
-XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* hist, int* tmp, int* bcast) {
+template <int KPT, int NT>
+XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], const float (&fv)[KPT], int n, int k, int lo_out, int hi_out,
+                       int* out, int* hist, int* tmp, int* bcast) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int base = tid * KPT;
   if (k <= 0) return;
+  hi_out = min(hi_out, k);
+  auto emit = [&](int pos, int id) {
+    if (pos >= lo_out && pos < hi_out) out[pos - lo_out] = id;
+  };
   if (k >= n) {
-    for (int i = tid; i < k; i += TKT) out[i] = (i < n) ? i : -1;
+    for (int i = lo_out + tid; i < hi_out; i += NT) out[i - lo_out] = (i < n) ? i : -1;
     return;
   }
-  for (int i = tid; i < NBK; i += TKT) hist[i] = 0;   // made visible by tk_minmax's barrier
+  for (int i = tid; i < NBK; i += NT) hist[i] = 0;   // made visible by tk_minmax's barrier
   if (tid == 0) bcast[3] = 0;                           // gather count of the few-keys path
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
@@ -208,30 +239,32 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
       lo = min(lo, kr[u]);
       hi = max(hi, kr[u]);
     }
-  tk_minmax(lo, hi, (uint32_t*)tmp);
+  tk_minmax<NT>(lo, hi, (uint32_t*)tmp);
   const float fmin = key_value(lo), fmax = key_value(hi);
   float inv = 0.f;
   if (__builtin_isfinite(fmin) && __builtin_isfinite(fmax) && fmax > fmin) {
     inv = (float)NBK / (fmax - fmin);
     if (!__builtin_isfinite(inv)) inv = 0.f;
   }
-  int bk[KPT];   // bucket of each key, -1 past n
+  // Bucket of each key, -1 past n (a monotone map of the value; -0.0 falls with +0.0, a
+  // NaN maximum leaves inv = 0).
+  int bk[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
-    bk[u] = (base + u >= n) ? -1 : (inv == 0.f) ? 0 : (int)fminf((key_value(kr[u]) - fmin) * inv, (float)(NBK - 1));
+    bk[u] = (base + u >= n) ? -1 : (inv == 0.f) ? 0 : (int)fminf((fv[u] - fmin) * inv, (float)(NBK - 1));
 
-  // Pass 1: bucket histogram, then the bucket b* holding the k-th largest key.
+  // Pass 1: bucket histogram (keys past n add 0 to bucket 0, so that no atomic sits in a
+  // branch), then the bucket b* holding the k-th largest key.
 #pragma unroll
-  for (int u = 0; u < KPT; ++u)
-    if (bk[u] >= 0) atomicAdd(&hist[bk[u]], 1);
-  __syncthreads();
+  for (int u = 0; u < KPT; ++u) atomicAdd(&hist[max(bk[u], 0)], bk[u] >= 0 ? 1 : 0);
+  lds_sync();
   {
-    constexpr int BPT = NBK / TKT;       // buckets per thread
+    constexpr int BPT = NBK / NT;        // buckets per thread
     const int top = NBK - 1 - BPT * tid; // this thread's buckets top, top-1, ...
     int v = 0;
 #pragma unroll
     for (int u = 0; u < BPT; ++u) v += hist[top - u];
-    const int incl = tk_scan_incl(v, tmp);   // keys in buckets >= top - BPT + 1
+    const int incl = tk_scan_incl<NT>(v, tmp);   // keys in buckets >= top - BPT + 1
     int c = incl - v;                         // keys in buckets > top
     if (c < k && k <= incl) {
       for (int u = 0; u < BPT; ++u) {
@@ -246,53 +279,49 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
       }
     }
   }
-  __syncthreads();
+  lds_sync();
   // hist, tmp and bcast[0..2] are rewritten only after at least one more barrier
   const int bstar = bcast[0];
   int remaining = k - bcast[1];   // keys still to take from b*, 1..|b*|
   const int m_b = bcast[2];
 
-  // Few keys in b* (the usual case): gather them, let one wave rank them by (key
-  // descending, id ascending) and take the remaining-th as an exact threshold; every
-  // selected key then lies in a higher bucket or at or above the threshold.
+  // Few keys in b* (the usual case): gather them; each thread then ranks its own keys of
+  // b* among them by (key descending, id ascending) and keeps those ranked below
+  // `remaining`; every key of a higher bucket is kept.
   if (m_b <= 64) {
-    uint32_t thr_key = 0u;
-    int thr_id = 0x7fffffff;
+    uint32_t selm = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) selm |= (uint32_t)(bk[u] > bstar) << u;
     if (remaining < m_b) {
       uint32_t* lkey = (uint32_t*)hist;   // the bucket histogram is no longer needed
       int* lid = hist + 64;
       int* lcount = bcast + 3;            // zeroed before the first barrier
+      uint32_t inb = 0u;
 #pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        if (bk[u] == bstar) {
-          const int at = atomicAdd(lcount, 1);
-          lkey[at] = kr[u];
-          lid[at] = base + u;
-        }
-      __syncthreads();
-      if (tid < m_b) {
-        const uint32_t key = lkey[tid];
-        const int id = lid[tid];
+      for (int u = 0; u < KPT; ++u) inb |= (uint32_t)(bk[u] == bstar) << u;
+      for (uint32_t m = inb; m; m &= m - 1u) {
+        const int u = __ffs(m) - 1;
+        const int at = atomicAdd(lcount, 1);
+        lkey[at] = kr[u];
+        lid[at] = base + u;
+      }
+      lds_sync();
+      for (uint32_t m = inb; m; m &= m - 1u) {
+        const int u = __ffs(m) - 1;
+        const uint32_t key = kr[u];
+        const int id = base + u;
         int rank = 0;
         for (int j = 0; j < m_b; ++j) rank += lkey[j] > key || (lkey[j] == key && lid[j] < id);
-        if (rank == remaining - 1) {
-          bcast[0] = (int)key;
-          bcast[1] = id;
-        }
+        selm |= (uint32_t)(rank < remaining) << u;
       }
-      __syncthreads();
-      thr_key = (uint32_t)bcast[0];
-      thr_id = bcast[1];
-    }
-    uint32_t selm = 0u;
+    } else {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      selm |= (uint32_t)(bk[u] > bstar ||
-                         (bk[u] == bstar && (kr[u] > thr_key || (kr[u] == thr_key && base + u <= thr_id)))) << u;
+      for (int u = 0; u < KPT; ++u) selm |= (uint32_t)(bk[u] == bstar) << u;
+    }
     const int mine = __popc(selm);
-    int pos = tk_scan_incl(mine, tmp) - mine;
+    int pos = tk_scan_incl<NT>(mine, tmp) - mine;
     while (selm) {
-      out[pos++] = base + __ffs(selm) - 1;
+      emit(pos++, base + __ffs(selm) - 1);
       selm &= selm - 1u;
     }
     return;
@@ -308,7 +337,7 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
         lo2 = min(lo2, kr[u]);
         hi2 = max(hi2, kr[u]);
       }
-    tk_minmax(lo2, hi2, (uint32_t*)tmp);
+    tk_minmax<NT>(lo2, hi2, (uint32_t*)tmp);
     const int common = (lo2 == hi2) ? 32 : __clz(lo2 ^ hi2);   // leading bits b*'s keys share
     mask = common >= 32 ? 0xffffffffu : ~(0xffffffffu >> common);
     prefix = lo2 & mask;
@@ -317,21 +346,21 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
       const int w = bit >= 8 ? 8 : bit;
       const int shift = bit - w;
       const uint32_t dmask = (1u << w) - 1u;
-      for (int i = tid; i < 256; i += TKT) hist[i] = 0;
-      __syncthreads();
+      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      lds_sync();
 #pragma unroll
       for (int u = 0; u < KPT; ++u)
         if (bk[u] == bstar && (kr[u] & mask) == prefix) atomicAdd(&hist[(kr[u] >> shift) & dmask], 1);
-      __syncthreads();
+      lds_sync();
       const int v = tid < 256 ? hist[255 - tid] : 0;
-      const int incl = tk_scan_incl(v, tmp);   // keys with digit >= 255 - tid
+      const int incl = tk_scan_incl<NT>(v, tmp);   // keys with digit >= 255 - tid
       const int excl = incl - v;               // keys with digit >  255 - tid
       if (v > 0 && excl < remaining && remaining <= incl) {
         bcast[0] = 255 - tid;
         bcast[1] = remaining - excl;
         bcast[2] = v;
       }
-      __syncthreads();
+      lds_sync();
       prefix |= (uint32_t)bcast[0] << shift;
       mask |= dmask << shift;
       remaining = bcast[1];
@@ -340,7 +369,7 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
       if (whole) break;
     }
   }
-  __syncthreads();   // the reads of tmp and bcast above are done
+  lds_sync();   // the reads of tmp and bcast above are done
   // Keys of higher buckets and keys of b* above the threshold prefix, then the first
   // `remaining` keys of b* equal to it in id order.
   uint32_t gtm = 0u, eqm = 0u;
@@ -350,7 +379,7 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     eqm |= (uint32_t)(bk[u] == bstar && (kr[u] & mask) == prefix) << u;
   }
   const int eq = __popc(eqm);
-  const int eq_before = tk_scan_incl(eq, tmp) - eq;
+  const int eq_before = tk_scan_incl<NT>(eq, tmp) - eq;
   int take = max(0, min(eq, remaining - eq_before));
   uint32_t sel = gtm;
   while (take-- > 0) {
@@ -358,9 +387,9 @@ XKV_DEV void topk_keys(const uint32_t (&kr)[KPT], int n, int k, int* out, int* h
     eqm &= eqm - 1u;
   }
   const int mine = __popc(sel);
-  int pos = tk_scan_incl(mine, tmp + TKW) - mine;   // the other half: tmp may still be read
+  int pos = tk_scan_incl<NT>(mine, tmp + NW) - mine;   // the other half: tmp may still be read
   while (sel) {
-    out[pos++] = base + __ffs(sel) - 1;
+    emit(pos++, base + __ffs(sel) - 1);
     sel &= sel - 1u;
   }
 }
@@ -383,25 +412,6 @@ XKV_DEV void load_keys(const float* scores, int n, uint32_t (&kr)[KPT]) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) kr[u] = (base + u < n) ? order_key(scores[base + u]) : 0u;
   }
-}
-
-template <typename ST>
-XKV_DEV void load8(const ST* p, float* v);
-template <>
-XKV_DEV void load8<uint16_t>(const uint16_t* p, float* v) {
-  const uint4 u = *(const uint4*)p;
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-template <>
-XKV_DEV void load8<float>(const float* p, float* v) {
-  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 // Eight storage elements held raw in registers (the load issued now, the conversion
@@ -467,21 +477,27 @@ XKV_DEV void softmax_partial(int grp, float (*pw)[RB], float* st_m, float* st_l)
 }
 
 // Exact rows of one (sequence, head): sink, local window, generated tokens, ETR per
-// block of TKT threads (tile e_blk), each tile leaving its own softmax partial.  These
-// blocks ride in the top-k launch, whose few selection blocks leave the GPU idle
-// otherwise.  The tile's rows are requested before the queries, so the two latencies
-// overlap.  The newest generated row is read from k_new / v_new when given, since the
-// score kernel copies it into the tail in this same step.
-template <typename ST>
+// block of NT threads (tile e_blk), each tile leaving its own softmax partial.  These
+// blocks ride in the score launch, ahead of its score blocks: they depend on nothing
+// the step computes, and small tiles keep each block's work well inside the scoring
+// blocks' time.  The tile's rows are requested before the queries, so the two
+// latencies overlap.  The newest generated row is read from k_new / v_new when given,
+// since the score launch copies it into the tail in this same step.
+template <typename ST, int NT>
 XKV_DEV void exact_tile(const SrParams& P, int b, int h, int e_blk, float* smem) {
-  float (*kh)[HROW] = (float (*)[HROW])smem;
-  float (*vh)[HROW] = (float (*)[HROW])(smem + ETR * HROW);
-  float (*qs)[MAXD] = (float (*)[MAXD])(smem + 2 * ETR * HROW);
-  float (*pw)[ETR] = (float (*)[ETR])(smem + 2 * ETR * HROW + MAXG * MAXD);
-  float* st_m = smem + 2 * ETR * HROW + MAXG * MAXD + MAXG * ETR;
+  static_assert(NT == 256 && ETR * (MAXD / 8) <= NT && MAXG * ETR * 2 <= NT, "exact tile layout");
+  // One staging buffer holds the tile's keys, then (once the scores are formed) its
+  // values; the value rows wait in registers meanwhile.
+  float (*kh)[EROW] = (float (*)[EROW])smem;
+  float (*vh)[EROW] = kh;
+  float (*qs)[MAXD] = (float (*)[MAXD])(smem + ETR * EROW);
+  float (*pw)[ETR] = (float (*)[ETR])(smem + ETR * EROW + MAXG * MAXD);
+  float* st_m = smem + ETR * EROW + MAXG * MAXD + MAXG * ETR;
   float* st_l = st_m + MAXG;
+  double* turns_s = (double*)(st_l + MAXG);   // RoPE frequencies, read from LDS after the first barrier
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = P.d, half = d >> 1, grp = P.grp;
+  const int lh = d == 128 ? 6 : 5;   // log2(half): head_dim is 64 or 128
   const int n_tail = P.n_sink + P.n_local + P.n_gen;
   const int r0 = e_blk * ETR;   // this block's tile of the tail
   auto pos_of = [&](int row) -> int {
@@ -494,105 +510,136 @@ XKV_DEV void exact_tile(const SrParams& P, int b, int h, int e_blk, float* smem)
   const ST* vt = (const ST*)P.v_tail + b * P.bs_tail + (long)h * d;
   const ST* kn = P.k_new ? (const ST*)P.k_new + b * P.bs_new + (long)h * d : nullptr;
   const ST* vn = P.v_new ? (const ST*)P.v_new + b * P.bs_new + (long)h * d : nullptr;
-  // Thread t loads 8-element group t of the tile (row = t / (d/8)).
+  // Thread t loads 8-element group t of the tile's keys and values (row t / (d/8)), raw.
   const int per_row = d >> 3;
   const int rl = tid / per_row, c8 = (tid % per_row) * 8;
-  const bool mine = tid < ETR * per_row && r0 + rl < n_tail;
-  float kv[8], vv[8];
-  if (mine) {
+  const bool ld_mine = tid < ETR * per_row && r0 + rl < n_tail;
+  Raw8<ST> rk, rv;
+  if (ld_mine) {
     const int row = r0 + rl;
     const bool newest = kn && row == n_tail - 1;
-    load8<ST>((newest ? kn : kt + (long)row * P.ld_tail) + c8, kv);
-    load8<ST>((newest ? vn : vt + (long)row * P.ld_tail) + c8, vv);
+    rk.load((newest ? kn : kt + (long)row * P.ld_tail) + c8);
+    rv.load((newest ? vn : vt + (long)row * P.ld_tail) + c8);
   }
-  // Rotated, scaled queries of the group (one pair per thread).
+  // The group's raw query pairs (pair e = j half + i for e = tid, tid + NT) and the RoPE
+  // frequencies are requested with the rows; they are rotated after the first barrier.
+  constexpr int QPT = MAXG * (MAXD / 2) / NT;
+  float qx[QPT], qy[QPT];
   {
     const ST* q = (const ST*)P.q + ((long)b * P.Hq + (long)h * grp) * d;
-    if (tid < grp * half) {
-      const int j = tid / half, i = tid % half;
-      const float x = ld_elem(q + j * d + i), y = ld_elem(q + j * d + i + half);
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = tid + NT * u, j = e >> lh, i = e & (half - 1);
+      qx[u] = e < grp * half ? ld_elem(q + j * d + i) : 0.f;
+      qy[u] = e < grp * half ? ld_elem(q + j * d + i + half) : 0.f;
+    }
+    if (tid < half) turns_s[tid] = P.turns[tid];
+  }
+  // Staged rows past the tail are zero.
+  auto stage = [&](const Raw8<ST>& raw) {
+    if (tid < ETR * per_row) {
+      float x8[8];
+      const bool mine = r0 + rl < n_tail;
+      if (mine) raw.get(x8);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) kh[rl][c8 + x] = mine ? x8[x] : 0.f;
+    }
+  };
+  stage(rk);
+  __syncthreads();
+  // Rotated, scaled queries, and RoPE on the staged keys (pair i of row r for
+  // e = r half + i).
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int e = tid + NT * u, j = e >> lh, i = e & (half - 1);
+    if (e < grp * half) {
       float c, s;
-      rope_cs_turns(P.q_pos, P.turns[i], &c, &s);
-      qs[j][i] = (x * c - y * s) * P.scale;
-      qs[j][i + half] = (y * c + x * s) * P.scale;
+      rope_cs_turns(P.q_pos, turns_s[i], &c, &s);
+      qs[j][i] = (qx[u] * c - qy[u] * s) * P.scale;
+      qs[j][i + half] = (qy[u] * c + qx[u] * s) * P.scale;
     }
   }
-  if (tid < ETR * per_row) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      kh[rl][c8 + x] = mine ? kv[x] : 0.f;
-      vh[rl][c8 + x] = mine ? vv[x] : 0.f;
-    }
+  for (int e = tid; e < ETR * half; e += NT) {
+    const int r = e >> lh, i = e & (half - 1);
+    float c, sn;   // rows past the tail rotate by angle 0; their scores are masked
+    rope_cs_turns(max(pos_of(r0 + r), 0), turns_s[i], &c, &sn);
+    const float lo = kh[r][i], hi = kh[r][i + half];
+    kh[r][i] = lo * c - hi * sn;
+    kh[r][i + half] = hi * c + lo * sn;
   }
   __syncthreads();
   {
-    // Pair i = tid % half of rows tid / half + u * TKT / half (TKT is a multiple of
-    // half, so every pass of a thread has the same frequency): the passes unrolled, so
-    // that their LDS reads and rotations overlap.
-    const int i = tid % half;
-    const double turns = P.turns[i];
-    constexpr int MAXPASS = ETR * (MAXD / 2) / TKT;
-#pragma unroll
-    for (int u = 0; u < MAXPASS; ++u) {
-      const int r = tid / half + u * (TKT / half);
-      if (r < ETR) {
-        float c, sn;   // rows past the tail rotate by angle 0; their scores are masked
-        rope_cs_turns(max(pos_of(r0 + r), 0), turns, &c, &sn);
-        const float lo = kh[r][i], hi = kh[r][i + half];
-        kh[r][i] = lo * c - hi * sn;
-        kh[r][i + half] = hi * c + lo * sn;
-      }
+    // Score (j, r) by the lane pair 2 (j ETR + r) + {0, 1}, one half of the dims each,
+    // the halves added across the pair.
+    const int pr = tid >> 1, hs = tid & 1;
+    const int j = pr / ETR, r = pr % ETR;
+    const int jq = min(j, grp - 1);
+    const int i0 = hs * half;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = i0; i < i0 + half; i += 4) {
+      const float4 qv = *(const float4*)&qs[jq][i];
+      const float4 kv = *(const float4*)&kh[r][i];
+      a[0] += qv.x * kv.x;
+      a[1] += qv.y * kv.y;
+      a[2] += qv.z * kv.z;
+      a[3] += qv.w * kv.w;
     }
+    float v = (a[0] + a[1]) + (a[2] + a[3]);
+    v += XKV_DPP_F(0.f, v, 0xB1, 0xF, false);   // quad_perm [1, 0, 3, 2]: the pair's other half
+    if (hs == 0 && j < grp) pw[j][r] = (r0 + r < n_tail) ? v : -INFINITY;
   }
   __syncthreads();
-  if (tid < grp * ETR) {
-    const int j = tid / ETR, r = tid % ETR;
-    float v = -INFINITY;
-    if (r0 + r < n_tail) {
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int i = 0; i < d; i += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s4[u] += qs[j][i + u] * kh[r][i + u];
-      }
-      v = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    }
-    pw[j][r] = v;
-  }
-  __syncthreads();
-  if (wave < grp) {
-    const float v = pw[wave][lane];
+  for (int j = wave; j < grp; j += NT / 64) {
+    const float v = lane < ETR ? pw[j][lane] : -INFINITY;
     const float mx = wave_max(v);
     const float p = (v == -INFINITY) ? 0.f : __expf(v - mx);
     const float l = wave_sum(p);
-    pw[wave][lane] = p;
+    if (lane < ETR) pw[j][lane] = p;
     if (lane == 0) {
-      st_m[wave] = mx;
-      st_l[wave] = l;
+      st_m[j] = mx;
+      st_l[j] = l;
     }
   }
+  stage(rv);   // the keys are no longer read: the buffer takes the values
   __syncthreads();
   float* part = P.part_ex + (((long)b * P.Hkv + h) * P.n_exact + e_blk) * (long)grp * (2 + d);
   if (tid < grp) {
     part[tid] = st_m[tid];
     part[grp + tid] = st_l[tid];
   }
-  if (tid < grp * d) {
-    const int j = tid / d, i = tid % d;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains, added in a fixed order
+  {
+    // Thread (dim i, head group jg): heads jg hpt .. + hpt of dim i over the tile's rows,
+    // each value read once for its heads, the weights wave-uniform (broadcast).
+    const int ngrp = NT / d;              // head groups: 2 (d = 128) or 4 (d = 64)
+    const int hpt = MAXG / ngrp;
+    const int i = tid % d, jg = tid / d;
+    const int jb = jg * hpt;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < ETR; r += 4) {
+    for (int r = 0; r < ETR; ++r) {
+      const float v = vh[r][i];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += pw[j][r + u] * vh[r + u][i];
+      for (int u = 0; u < 4; ++u) acc[u] += pw[min(jb + u, MAXG - 1)][r] * v;
     }
-    part[2 * grp + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < hpt && jb + u < grp) part[2 * grp + (long)(jb + u) * d + i] = acc[u];
   }
 }
 
+// Blocks y < n_exact of the grid attend exact-row tile y of their (head, sequence); the
+// rest score a slice of the candidate chunks each.
 template <typename ST>
 __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
+  extern __shared__ __align__(16) float smem_x[];
   __shared__ float qs[MAXG][MAXD];
   __shared__ float qsum[MAXD];
-  const int h = blockIdx.x, blk = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.z, tid = threadIdx.x;
+  if ((int)blockIdx.y < P.n_exact) {
+    exact_tile<ST, 256>(P, b, h, blockIdx.y, smem_x);
+    return;
+  }
+  const int blk = blockIdx.y - P.n_exact;
 
   if (blk == 0 && h == 0 && P.k_new != nullptr && P.n_gen > 0) {
     const long row = P.n_sink + P.n_local + P.n_gen - 1;
@@ -632,7 +679,7 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
   const int cpi = 256 / lpc;          // chunks per pass
   const int sub = tid % lpc, slot = tid / lpc;
   const ST* lm = (const ST*)P.lm + b * P.bs_lm + (long)h * P.n_chunks * P.d + sub * 8;
-  float* scores = P.scores + ((long)b * P.Hkv + h) * P.n_cand;
+  float* scores = P.scores + ((long)b * P.Hkv + h) * P.ld_sc;
   const int iters = (c1 - c0 + cpi - 1) / cpi;
   constexpr int BATCH = 8;
   Raw8<ST> raw[BATCH];
@@ -690,26 +737,21 @@ __global__ __launch_bounds__(256) void sr_score_kernel(SrParams P) {
   }
 }
 
-// Blocks [0, H_kv * batch) select the top-k chunks of one (head, sequence); the rest
-// attend one exact-row tile each.
-template <int KPT, typename ST>
+// One block per (head, sequence) selects its top-k chunks (the paths whose attend
+// kernel does not select them itself).
+template <int KPT>
 __global__ __launch_bounds__(TKT) void sr_topk_kernel(SrParams P) {
-  extern __shared__ __align__(16) float smem_x[];
   __shared__ int hist[NBK];
-  __shared__ int tmp[2 * TKW];
+  __shared__ int tmp[2 * (TKT / 64)];
   __shared__ int bcast[4];
-  const int nsel = P.Hkv * P.batch;
-  if ((int)blockIdx.x >= nsel) {
-    const int idx = blockIdx.x - nsel;
-    const int hb = idx / P.n_exact;
-    exact_tile<ST>(P, hb / P.Hkv, hb % P.Hkv, idx % P.n_exact, smem_x);
-    return;
-  }
   const int h = blockIdx.x % P.Hkv, b = blockIdx.x / P.Hkv;
   const long bh = (long)b * P.Hkv + h;
   uint32_t kr[KPT];
-  load_keys<KPT>(P.scores + bh * P.n_cand, P.n_cand, kr);
-  topk_keys<KPT>(kr, P.n_cand, P.top_k, P.sel + bh * P.top_k, hist, tmp, bcast);
+  float fv[KPT];
+  load_keys<KPT>(P.scores + bh * P.ld_sc, P.n_cand, kr);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) fv[u] = key_value(kr[u]);
+  topk_keys<KPT, TKT>(kr, fv, P.n_cand, P.top_k, 0, P.top_k, P.sel + bh * P.top_k, hist, tmp, bcast);
 }
 
 // Rows of split s: selected chunks [s*cps, (s+1)*cps) minus the exact-tail positions.
@@ -740,17 +782,6 @@ XKV_DEV void write_partial(const SrParams& P, int b, int h, int s, float (*pw)[R
     for (int row = 0; row < RB; ++row) acc += pw[j][row] * vh[row][i];
     part[2 * grp + e] = acc;
   }
-}
-
-// Barrier for LDS hand-offs: this wave's LDS stores have completed (lgkmcnt(0)), then
-// s_barrier.  No memory fence: a workgroup fence would also wait for every global load
-// and direct-to-LDS load in flight, which the attend kernel keeps going across barriers.
-// The empty asm statements keep the compiler from moving memory accesses across it.
-XKV_DEV void lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited for
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
 }
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): two bf16 MFMA operands whose
@@ -794,7 +825,10 @@ constexpr int QSLOT = 8 * VROW_MAX * 2;   // bytes of one wave's share of region
 // MULTI: r spans several rank chunks (the single-chunk instantiation issues every
 // direct-to-LDS load outside any branch, which keeps the compiler's own waits for them
 // exact).
-template <bool EXACT_V, bool MULTI>
+// KPTF > 0: the block selects the head's top-k chunks itself from the scores (KPTF keys
+// per thread, n_cand <= 512 KPTF), keeps the ids of its own split and writes them to
+// `sel`; the selection runs while the first B_k staging is in flight.
+template <bool EXACT_V, bool MULTI, int KPTF>
 __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   // Region A: staged A_k rows (stride AROW); before them the B_k staging of dt = 1, after
   // them the partial-key exchange, partial scores, softmax weights and statistics.
@@ -803,6 +837,10 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   // swizzled).
   __shared__ __align__(16) uint16_t Vr[RBM * VROW_MAX];
   __shared__ int rows_t[RBM];
+  __shared__ int sel_s[64];                       // the split's chunk ids (KPTF > 0)
+  __shared__ int tk_hist[KPTF > 0 ? NBK : 1];     // top-k scratch (KPTF > 0)
+  __shared__ int tk_tmp[16];
+  __shared__ int tk_bcast[4];
   const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -824,7 +862,13 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
   // (unconditionally, clamped to a valid entry), so that no barrier stands between the
   // ids and the wave's A_k gathers.  The multi-chunk path reads them for the block.
   int csel = -1;
-  if constexpr (!MULTI) {
+  float4 sraw[KPTF > 0 ? KPTF / 4 : 1];   // this thread's scores, raw (KPTF > 0)
+  if constexpr (KPTF > 0) {
+    // Past the row's end: the last 16 bytes of the row's padded stride again (ignored).
+    const float* sc = P.scores + bh * P.ld_sc;
+#pragma unroll
+    for (int u = 0; u < KPTF / 4; ++u) sraw[u] = *(const float4*)(sc + min(tid * KPTF + 4 * u, P.ld_sc - 4));
+  } else if constexpr (!MULTI) {
     const int ci = s * P.cps + (wave * 8 + (lane & 7)) / P.chunk;
     csel = P.sel[bh * P.top_k + min(ci, P.k_eff - 1)];
     if (ci >= P.k_eff) csel = -1;
@@ -832,6 +876,43 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     const int ci = s * P.cps + tid / P.chunk;
     if (ci < P.k_eff) csel = P.sel[bh * P.top_k + ci];
   }
+  // The keys are formed (and pinned by the empty asm statements) before the B_k staging
+  // below is issued: the wait for the scores is then a wait for them alone, and the
+  // staging lands while the selection runs.  Formed later, the compiler would wait for
+  // every load in flight.
+  uint32_t kr[KPTF > 0 ? KPTF : 1];
+  float fv[KPTF > 0 ? KPTF : 1];
+  if constexpr (KPTF > 0) {
+#pragma unroll
+    for (int u = 0; u < KPTF / 4; ++u) {
+      fv[4 * u] = sraw[u].x;
+      fv[4 * u + 1] = sraw[u].y;
+      fv[4 * u + 2] = sraw[u].z;
+      fv[4 * u + 3] = sraw[u].w;
+    }
+#pragma unroll
+    for (int u = 0; u < KPTF; ++u) {
+      __asm__ volatile("" : "+v"(fv[u]));
+      kr[u] = order_key(fv[u]);
+    }
+  }
+  // Selection positions [s cps, (s + 1) cps) into sel_s, the block's share of `sel`
+  // written out (the last split also pads positions past its range with -1), and this
+  // thread's chunk id: row 8 wave + (lane & 7) (single chunk) or row tid (multi-chunk).
+  auto fused_select = [&]() __attribute__((always_inline)) {
+    if constexpr (KPTF > 0) {
+      const int lo = s * P.cps;
+      topk_keys<KPTF, 512>(kr, fv, P.n_cand, P.top_k, lo, lo + P.cps, sel_s, tk_hist, tk_tmp, tk_bcast);
+      lds_sync();
+      int* sel_out = P.sel + bh * P.top_k;
+      if (tid < P.cps && lo + tid < P.top_k) sel_out[lo + tid] = sel_s[tid];
+      if (s == P.n_splits - 1)
+        for (int ci = lo + P.cps + tid; ci < P.top_k; ci += 512) sel_out[ci] = -1;
+      const int r = MULTI ? tid : wave * 8 + (lane & 7);
+      const int ci = lo + min(r, RBM - 1) / P.chunk;
+      csel = ci < P.k_eff ? sel_s[ci - lo] : -1;
+    }
+  };
   // Query fragment of this lane: head j = n (zero past the group), dims 16 dg + 4 g + v
   // and their RoPE partners 64 + 16 dg + 4 g + v.
   const int jq = min(n, grp - 1);
@@ -882,15 +963,29 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     read_half((const unsigned char*)Vr + wave * QSLOT, 0);
     read_half((const unsigned char*)Ak + wave * 8192, 1);
   };
+  // The same fragments loaded straight from memory (rank chunk 0), used on the selecting
+  // path while the selection runs: with a direct-to-LDS load in flight the compiler
+  // would make every LDS atomic of the selection wait for it.
+  auto load_frag_half = [&](int dt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      bq[dt][ks] = *(const uint4*)(bk + (long)(64 * dt + n) * P.ld_Bt_k + kh * (KC >> 1) +
+                                   8 * (4 * min(ks, nks - 1) + g));
+  };
   const int lcv_ni = 1 << (lcv - 3);   // 1 KB instructions for a wave's 8 value rows
   int tr[8], tv[8];   // A_k row of instruction i; value row of this lane in value instruction i
   unsigned char* const vslot = (unsigned char*)Vr + wave * QSLOT;
   if constexpr (!MULTI) {
     // Half the B_k staging (dt = 0) lands with the row ids; then the A_k gathers and the
     // other half (into the same slot) are in flight together.
-    stage_half(vslot, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): ids, query and dt = 0 half have landed
-    read_half(vslot, 0);
+    if constexpr (KPTF > 0) {
+      load_frag_half(0);
+      fused_select();
+    } else {
+      stage_half(vslot, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): ids, query and dt = 0 half have landed
+      read_half(vslot, 0);
+    }
     const int rl = wave * 8 + (lane & 7);
     const int t = csel * P.chunk + rl % P.chunk;
     const int trow = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
@@ -901,9 +996,15 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
       tv[i] = __builtin_amdgcn_ds_bpermute(((64 * min(i, lcv_ni - 1) + lane) >> lcv) << 2, trow);
     }
   } else {
-    stage_b(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B_k slice has landed
-    read_b();
+    if constexpr (KPTF > 0) {
+      load_frag_half(0);
+      load_frag_half(1);
+      fused_select();
+    } else {
+      stage_b(0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B_k slice has landed
+      read_b();
+    }
     if (tid < RBM) {
       const int t = csel * P.chunk + tid % P.chunk;
       rows_t[tid] = (csel >= 0 && t >= P.n_sink && t < P.T - P.n_local) ? t : -1;
@@ -1490,11 +1591,14 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
 template <int KPT>
 __global__ __launch_bounds__(TKT) void topk_rows_kernel(const float* scores, int n_cand, long ld, int k, int* sel) {
   __shared__ int hist[NBK];
-  __shared__ int tmp[2 * TKW];
+  __shared__ int tmp[2 * (TKT / 64)];
   __shared__ int bcast[4];
   uint32_t kr[KPT];
+  float fv[KPT];
   load_keys<KPT>(scores + blockIdx.x * ld, n_cand, kr);
-  topk_keys<KPT>(kr, n_cand, k, sel + (long)blockIdx.x * k, hist, tmp, bcast);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) fv[u] = key_value(kr[u]);
+  topk_keys<KPT, TKT>(kr, fv, n_cand, k, 0, k, sel + (long)blockIdx.x * k, hist, tmp, bcast);
 }
 
 // Raise a kernel's dynamic-LDS limit once per process and kernel (to the largest size
@@ -1511,38 +1615,37 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }  // namespace
 
 // KV head fastest in the grid: consecutive blocks go to different XCDs, so with 8 KV
-// heads one head's score blocks share an XCD, and the top-k block of the head (block id
-// h of its launch) finds the scores in that XCD's L2.
-hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st) {
-  dim3 grid(P.Hkv, P.score_blocks, P.batch);
-  if (bf16)
-    hipLaunchKernelGGL(sr_score_kernel<uint16_t>, grid, dim3(256), 0, st, P);
-  else
-    hipLaunchKernelGGL(sr_score_kernel<float>, grid, dim3(256), 0, st, P);
-  return hipGetLastError();
-}
-
-template <int KPT, typename ST>
-hipError_t launch_topk_exact(const SrParams& P, hipStream_t st) {
-  // the exact tiles' staged rows, queries, weights and softmax stats
-  const size_t lds = sizeof(float) * (2 * ETR * HROW + MAXG * MAXD + MAXG * ETR + 2 * MAXG);
-  hipError_t e = set_lds<10 + KPT + 100 * (int)sizeof(ST)>(sr_topk_kernel<KPT, ST>, lds);
-  if (e != hipSuccess) return e;
-  const dim3 grid(P.Hkv * P.batch * (1 + P.n_exact));
-  hipLaunchKernelGGL((sr_topk_kernel<KPT, ST>), grid, dim3(TKT), lds, st, P);
-  return hipGetLastError();
-}
-
+// heads one head's score blocks share an XCD, and the blocks that select the head's
+// top-k find its scores in that XCD's L2.  The exact-row tiles come first in the grid.
 template <typename ST>
-hipError_t launch_topk_exact_st(const SrParams& P, hipStream_t st) {
-  if (P.n_cand <= TKT * 2) return launch_topk_exact<2, ST>(P, st);
-  if (P.n_cand <= TKT * 8) return launch_topk_exact<8, ST>(P, st);
-  return launch_topk_exact<32, ST>(P, st);
+hipError_t launch_score_st(const SrParams& P, hipStream_t st) {
+  // the exact tiles' staged rows (keys, then values), queries, weights, softmax stats and
+  // RoPE frequencies
+  const size_t lds = sizeof(float) * (ETR * EROW + MAXG * MAXD + MAXG * ETR + 2 * MAXG) + sizeof(double) * (MAXD / 2);
+  hipError_t e = set_lds<1 + (int)sizeof(ST)>(sr_score_kernel<ST>, lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(P.Hkv, P.n_exact + P.score_blocks, P.batch);
+  hipLaunchKernelGGL(sr_score_kernel<ST>, grid, dim3(256), lds, st, P);
+  return hipGetLastError();
 }
 
-// Top-k selection and the exact-row tiles, one launch (it runs even when top_k == 0).
+hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st) {
+  return bf16 ? launch_score_st<uint16_t>(P, st) : launch_score_st<float>(P, st);
+}
+
+// Top-k selection, one block per (head, sequence), unless the attend kernel selects
+// (or nothing is selected).
 hipError_t launch_sr_topk(const SrParams& P, int bf16, hipStream_t st) {
-  return bf16 ? launch_topk_exact_st<uint16_t>(P, st) : launch_topk_exact_st<float>(P, st);
+  (void)bf16;
+  if (P.fuse_topk || P.k_eff == 0) return hipSuccess;
+  const dim3 grid(P.Hkv * P.batch);
+  if (P.n_cand <= TKT * 2)
+    hipLaunchKernelGGL(sr_topk_kernel<2>, grid, dim3(TKT), 0, st, P);
+  else if (P.n_cand <= TKT * 8)
+    hipLaunchKernelGGL(sr_topk_kernel<8>, grid, dim3(TKT), 0, st, P);
+  else
+    hipLaunchKernelGGL(sr_topk_kernel<32>, grid, dim3(TKT), 0, st, P);
+  return hipGetLastError();
 }
 
 hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
@@ -1559,17 +1662,31 @@ hipError_t launch_sr_attend(const SrParams& P, int bf16, hipStream_t st, hipEven
     // The timing events, when given, are stamped by the dispatch itself at the
     // kernel's start and end.
     const bool multi = (P.r_k & 511) ? P.r_k > ((P.r_k & 255) ? 128 : 256) : P.r_k > 512;
+    const int kptf = !P.fuse_topk ? 0 : P.n_cand <= 512 * 16 ? 16 : 32;
+#define XKV_ATTEND(EV, MU, KP) \
+  hipExtLaunchKernelGGL(sr_attend_mfma_kernel<EV, MU, KP>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P)
+#define XKV_ATTEND_K(EV, MU) \
+  do {                                   \
+    if (kptf == 16)                      \
+      XKV_ATTEND(EV, MU, 16);            \
+    else if (kptf == 32)                 \
+      XKV_ATTEND(EV, MU, 32);            \
+    else                                 \
+      XKV_ATTEND(EV, MU, 0);             \
+  } while (0)
     if (P.exact_v) {
       if (multi)
-        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<true, true>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
+        XKV_ATTEND_K(true, true);
       else
-        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<true, false>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
+        XKV_ATTEND_K(true, false);
     } else {
       if (multi)
-        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<false, true>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
+        XKV_ATTEND_K(false, true);
       else
-        hipExtLaunchKernelGGL(sr_attend_mfma_kernel<false, false>, grid, dim3(512), 0, st, ev_start, ev_stop, 0, P);
+        XKV_ATTEND_K(false, false);
     }
+#undef XKV_ATTEND_K
+#undef XKV_ATTEND
   } else {
     hipError_t e;
     if (ev_start && (e = hipEventRecord(ev_start, st)) != hipSuccess) return e;

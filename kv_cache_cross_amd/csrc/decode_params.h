@@ -12,7 +12,7 @@ struct SrParams {
   int n_chunks;      // T / chunk (landmark rows per head)
   int k_eff;         // min(top_k, n_cand)
   int n_splits;      // 64-row splits of the selected rows
-  int n_exact;       // 64-row tiles of the exact tail (sink + local + generated), at least 1
+  int n_exact;       // 16-row tiles of the exact tail (sink + local + generated), at least 1
   int grp;           // query heads per KV head
   int mfma;          // matrix-core attend path (bf16, head_dim 128, r_k % 128 == 0,
                      // r_k <= MAX_RANK_MFMA, r_v == r_k or r_v == 0)
@@ -23,6 +23,9 @@ struct SrParams {
   int cps;           // chunks per split
   long q_pos;        // query position p
   int score_blocks;  // select-kernel blocks per KV head
+  int ld_sc;         // row stride of `scores`: n_cand rounded up to a multiple of 4
+  int fuse_topk;     // matrix-core path with n_cand <= 16384: every attend block selects
+                     // the head's top-k chunks itself (no separate top-k launch)
   float scale;
   double theta;
   double turns[64];  // theta^(-2i/d) / (2 pi) for i < d/2, formed on the host in float64
@@ -37,13 +40,13 @@ struct SrParams {
   const void* k_new; const void* v_new; long bs_new;
   float* out;
   int* sel;          // batch x Hkv x top_k
-  float* scores;     // batch x Hkv x n_cand
+  float* scores;     // batch x Hkv rows of ld_sc (n_cand used)
   float* part;       // batch x Hkv x n_splits x grp x (2 + vdim): max, sum, weighted sum
   float* part_ex;    // batch x Hkv x n_exact x grp x (2 + d)
 };
 
-// Stream-ordered stages of one decode step: scores (+ append), top-k + exact rows,
-// rebuild + attend of the selected rows, merge.
+// Stream-ordered stages of one decode step: exact rows + scores (+ append), top-k
+// (unless the attend kernel selects), rebuild + attend of the selected rows, merge.
 hipError_t launch_sr_score(const SrParams& P, int bf16, hipStream_t st);
 hipError_t launch_sr_topk(const SrParams& P, int bf16, hipStream_t st);
 // ev_start / ev_stop (optional, both or neither): timing events stamped at the attend

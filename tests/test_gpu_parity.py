@@ -255,7 +255,7 @@ def test_decode_mini_bf16_steps(ctx):
 
 def test_decode_exact_tail_crosses_tiles(ctx):
     # 4 sink + 122 local rows plus 1..4 generated tokens: the exact tail grows from 127 to
-    # 130 rows and crosses from two 64-row tiles into a third one.
+    # 130 rows and crosses from eight 16-row tiles into a ninth.
     wl = make_workload("llama16k", device=DEV, **dict(MINI, n_local=122))
     _run_decode_case(ctx, wl, steps=4, layer=0, label="exact tail 127..130 rows")
 

@@ -876,10 +876,35 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     const int ci = s * P.cps + tid / P.chunk;
     if (ci < P.k_eff) csel = P.sel[bh * P.top_k + ci];
   }
-  // The keys are formed (and pinned by the empty asm statements) before the B_k staging
-  // below is issued: the wait for the scores is then a wait for them alone, and the
-  // staging lands while the selection runs.  Formed later, the compiler would wait for
-  // every load in flight.
+  // Query fragment of this lane: head j = n (zero past the group), dims 16 dg + 4 g + v
+  // and their RoPE partners 64 + 16 dg + 4 g + v.
+  const int jq = min(n, grp - 1);
+  const uint16_t* qg = (const uint16_t*)P.q + ((long)b * P.Hq + (long)h * grp + jq) * 128 + 16 * dg + 4 * g;
+  uint16_t qraw[8];
+  double turns[4];   // RoPE frequencies (turns per position) of this lane's dims, for q and k
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    qraw[v] = qg[v];
+    qraw[4 + v] = qg[64 + v];
+    turns[v] = P.turns[16 * dg + 4 * g + v];
+  }
+  // B_k fragments: (dt, ks) of lane (n, g) holds row 64 dt + n of the wave's 16-dim group,
+  // ranks kc + kh KC/2 + 8 (4 ks + g) .. + 8.  On the selecting path those of rank chunk 0
+  // are loaded straight from memory here, behind the scores, and arrive while the
+  // selection runs (with a direct-to-LDS load in flight the compiler would make every LDS
+  // atomic of the selection wait for it); otherwise they come through LDS below.
+  const uint16_t* bk = (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)(h * 128 + 16 * dg) * P.ld_Bt_k;
+  uint4 bq[2][8];
+  if constexpr (KPTF > 0) {
+#pragma unroll
+    for (int dt = 0; dt < (MULTI ? 2 : 1); ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        bq[dt][ks] = *(const uint4*)(bk + (long)(64 * dt + n) * P.ld_Bt_k + kh * (KC >> 1) +
+                                     8 * (4 * min(ks, nks - 1) + g));
+  }
+  // The keys are formed (and pinned by the empty asm statements) after those loads are
+  // issued: the wait for the scores (issued first) is then a wait for them alone.
   uint32_t kr[KPTF > 0 ? KPTF : 1];
   float fv[KPTF > 0 ? KPTF : 1];
   if constexpr (KPTF > 0) {
@@ -913,24 +938,11 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
       csel = ci < P.k_eff ? sel_s[ci - lo] : -1;
     }
   };
-  // Query fragment of this lane: head j = n (zero past the group), dims 16 dg + 4 g + v
-  // and their RoPE partners 64 + 16 dg + 4 g + v.
-  const int jq = min(n, grp - 1);
-  const uint16_t* qg = (const uint16_t*)P.q + ((long)b * P.Hq + (long)h * grp + jq) * 128 + 16 * dg + 4 * g;
-  uint16_t qraw[8];
-  double turns[4];   // RoPE frequencies (turns per position) of this lane's dims, for q and k
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    qraw[v] = qg[v];
-    qraw[4 + v] = qg[64 + v];
-    turns[v] = P.turns[16 * dg + 4 * g + v];
-  }
   // B_k staging: half-rows (dims 16 dg + 64 dt + m, ranks kc + kh KC/2 + [0, KC/2)) of
   // this wave.  Multi-chunk: dt = 0 into its slot of region V, dt = 1 into its slot of
   // region A, together.  Single chunk: both into the region V slot in turn, so that region
   // A takes the A_k rows while the staging is under way.
   // 16-byte unit p of a slot holds row m = p >> lcr, chunk c = (p & (2^lcr - 1)) ^ (m & 7).
-  const uint16_t* bk = (const uint16_t*)P.Bt_k + b * P.bs_Bt_k + (long)(h * 128 + 16 * dg) * P.ld_Bt_k;
   // One half-row set (dt) into one slot; called with each slot's own array so that every
   // direct-to-LDS load names a single LDS array (which lets the compiler keep the loads
   // into one array from delaying reads of the other).
@@ -950,8 +962,7 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     stage_half((unsigned char*)Vr + wave * QSLOT, 0, kc);
     stage_half((unsigned char*)Ak + wave * 8192, 1, kc);
   };
-  // Fragment (dt, ks) of lane (n, g): row n, chunk 4 ks + g.
-  uint4 bq[2][8];
+  // Fragment (dt, ks) of lane (n, g): row n, chunk 4 ks + g (bq, declared above).
   auto read_half = [&](const unsigned char* slot, int dt) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -963,15 +974,6 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     read_half((const unsigned char*)Vr + wave * QSLOT, 0);
     read_half((const unsigned char*)Ak + wave * 8192, 1);
   };
-  // The same fragments loaded straight from memory (rank chunk 0), used on the selecting
-  // path while the selection runs: with a direct-to-LDS load in flight the compiler
-  // would make every LDS atomic of the selection wait for it.
-  auto load_frag_half = [&](int dt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      bq[dt][ks] = *(const uint4*)(bk + (long)(64 * dt + n) * P.ld_Bt_k + kh * (KC >> 1) +
-                                   8 * (4 * min(ks, nks - 1) + g));
-  };
   const int lcv_ni = 1 << (lcv - 3);   // 1 KB instructions for a wave's 8 value rows
   int tr[8], tv[8];   // A_k row of instruction i; value row of this lane in value instruction i
   unsigned char* const vslot = (unsigned char*)Vr + wave * QSLOT;
@@ -979,7 +981,6 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     // Half the B_k staging (dt = 0) lands with the row ids; then the A_k gathers and the
     // other half (into the same slot) are in flight together.
     if constexpr (KPTF > 0) {
-      load_frag_half(0);
       fused_select();
     } else {
       stage_half(vslot, 0, 0);
@@ -997,8 +998,6 @@ __global__ __launch_bounds__(512) void sr_attend_mfma_kernel(SrParams P) {
     }
   } else {
     if constexpr (KPTF > 0) {
-      load_frag_half(0);
-      load_frag_half(1);
       fused_select();
     } else {
       stage_b(0);
@@ -1480,9 +1479,9 @@ __global__ __launch_bounds__(256) void sr_merge_rank_kernel(SrParams P) {
   float2 pv[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) pv[u] = *(const float2*)(p0 + (long)max(0, min(u, ns - 1)) * sstride + c0);
-  // The exact-row tiles' weighted value sums of this block's output dim tid (up to 4
-  // tiles in flight).
-  constexpr int PE = 4;
+  // The exact-row tiles' weighted value sums of this block's output dim tid (up to 16
+  // tiles, 256 exact rows, in flight).
+  constexpr int PE = 16;
   float ev[PE];
 #pragma unroll
   for (int e = 0; e < PE; ++e)

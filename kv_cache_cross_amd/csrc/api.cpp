@@ -400,6 +400,12 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   const int per = std::max(1, kMaxPtrs / p.G);
   auto fp64_sweeps = [&](Half& hf, int count) -> int {
     for (int it = 0; it < count; ++it) {
+      if (hf.tQ == GF32) {
+        // the float32 sweeps' basis, widened (the float64 product then runs on one type)
+        XKV_K(launch_widen((const float*)hf.Qcur, hf.Qa, (long)hf.cnt * nk, st));
+        hf.Qcur = hf.Qa;
+        hf.tQ = GF64;
+      }
       XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, hf.tQ, GF64, hf.w.C64, n, nn, hf.Qcur, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
                        hf.cnt), st));
       int e = cholqr(p, hf.w, hf.cnt, hf.Ya, GF64, hf.Qa, GF64, st);       // Qa = orth(Ya)

@@ -1,11 +1,13 @@
 // Batched GEMM on the float32 / float64 matrix cores for the subspace
 // iteration: C = alpha op(A) op(B) + beta C.
 //
-// 64 x 64 output tile per workgroup, K staged through LDS in steps of 16;
-// 4 waves in a 2 x 2 grid, each owning 2 x 2 tiles of v_mfma_f32_16x16x4f32
-// or v_mfma_f64_16x16x4f64.  Operands are converted to the arithmetic type
-// while they are staged, so float32 data can feed float64 arithmetic
-// (W = Y^T Y of a float32 block is summed in float64).
+// 64 x 64 output tile per workgroup, K staged through LDS in slabs of 32 with the
+// next slab's loads in flight (in registers) while the current one is multiplied;
+// 4 waves in a 2 x 2 grid, each owning 2 x 2 tiles of v_mfma_f32_16x16x4f32 or
+// v_mfma_f64_16x16x4f64.  Operands are converted to the arithmetic type while they
+// are staged, so float32 data can feed float64 arithmetic (W = Y^T Y of a float32
+// block is summed in float64).  Each thread loads 8 elements of each operand per
+// slab, consecutive threads along the operand's contiguous dimension.
 //
 // Lane layouts (checked on gfx950): both instructions take A[m = lane%16]
 // [k = lane/16] and B[k = lane/16][n = lane%16].  The float32 result holds
@@ -17,7 +19,7 @@
 namespace xkv {
 namespace {
 
-constexpr int BM = 64, BN = 64, BK = 16;
+constexpr int BM = 64, BN = 64, BK = 32;
 
 template <typename T>
 struct Mfma;
@@ -62,29 +64,47 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
 
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
-    // Stage op(A)[m0:m0+64, k0:k0+16] as As[k][m] and op(B)[k0:k0+16, n0:n0+64] as Bs[k][n].
+  // Element q of this thread in a slab: A (m, k) and B (k, n), consecutive threads
+  // along the stored contiguous dimension.
+  auto a_mk = [&](int q, int& mm, int& kk) {
+    if (TA_T) { mm = tid & 63; kk = (tid >> 6) + 4 * q; }   // A stored K x M: contiguous in m
+    else      { kk = tid & 31; mm = (tid >> 5) + 8 * q; }   // A stored M x K: contiguous in k
+  };
+  auto b_kn = [&](int q, int& kk, int& nn) {
+    if (TB_T) { kk = tid & 31; nn = (tid >> 5) + 8 * q; }   // B stored N x K: contiguous in k
+    else      { nn = tid & 63; kk = (tid >> 6) + 4 * q; }   // B stored K x N: contiguous in n
+  };
+  ACC ra[8], rb[8];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       int mm, kk;
-      if (TA_T) { kk = tid >> 4; mm = (tid & 15) * 4 + q; }   // A stored K x M: contiguous in m
-      else      { mm = tid >> 2; kk = (tid & 3) * 4 + q; }    // A stored M x K: contiguous in k
+      a_mk(q, mm, kk);
       const int gm = m0 + mm, gk = k0 + kk;
-      ACC v = 0;
-      if (gm < p.M && gk < p.K) v = (ACC)(TA_T ? A[(long)gk * p.lda + gm] : A[(long)gm * p.lda + gk]);
-      As[kk][mm] = v;
+      ra[q] = (gm < p.M && gk < p.K) ? (ACC)(TA_T ? A[(long)gk * p.lda + gm] : A[(long)gm * p.lda + gk]) : (ACC)0;
+      int nn;
+      b_kn(q, kk, nn);
+      const int gn = n0 + nn, gk2 = k0 + kk;
+      rb[q] = (gn < p.N && gk2 < p.K) ? (ACC)(TB_T ? B[(long)gn * p.ldb + gk2] : B[(long)gk2 * p.ldb + gn]) : (ACC)0;
     }
+  };
+  auto stage = [&]() {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int nn, kk;
-      if (TB_T) { nn = tid >> 2; kk = (tid & 3) * 4 + q; }    // B stored N x K: contiguous in k
-      else      { kk = tid >> 4; nn = (tid & 15) * 4 + q; }   // B stored K x N: contiguous in n
-      const int gn = n0 + nn, gk = k0 + kk;
-      ACC v = 0;
-      if (gn < p.N && gk < p.K) v = (ACC)(TB_T ? B[(long)gn * p.ldb + gk] : B[(long)gk * p.ldb + gn]);
-      Bs[kk][nn] = v;
+    for (int q = 0; q < 8; ++q) {
+      int mm, kk, nn;
+      a_mk(q, mm, kk);
+      As[kk][mm] = ra[q];
+      b_kn(q, kk, nn);
+      Bs[kk][nn] = rb[q];
     }
-    __syncthreads();
+  };
+
+  fetch(0);
+  stage();
+  __syncthreads();
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
+    const bool more = k0 + BK < p.K;
+    if (more) fetch(k0 + BK);   // in flight during the multiplies below
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 4) {
       ACC a[2], b[2];
@@ -98,6 +118,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
         for (int j = 0; j < 2; ++j) acc[i][j] = Mfma<ACC>::op(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
+    if (more) {
+      stage();
+      __syncthreads();
+    }
   }
 
 #pragma unroll

@@ -11,9 +11,11 @@ namespace {
 
 constexpr int NB = 64;
 
-// One workgroup per side: load the nb x nb diagonal block of W at (j0, j0),
-// factor it as L L^T in LDS (right-looking, column by column), invert L by
-// forward substitution, and write L and L^-1.
+// One workgroup per side: load the nb x nb diagonal block of W at (j0, j0), factor it
+// as L L^T in LDS (right-looking, column by column) and invert L alongside: X = L^-1
+// solves L X = I by the same right-looking sweep (at column k, row k of the right-hand
+// side is divided by the pivot and row k's multiples L[i][k] X[k][.] leave the rows
+// below), so both share the column loop's barriers.  Writes L and L^-1.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long ldw, long sW,
                                                          double* L, long ldl, long sL,
                                                          double* Dinv, long sD, int j0, int nb,
@@ -21,17 +23,19 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
                                                          int* info) {
   __shared__ double a[NB][NB + 1];
   __shared__ double inv[NB][NB + 1];
+  __shared__ double floor_s[NB];   // the pivots' breakdown floors
   __shared__ int bad;
   const int side = blockIdx.x, tid = threadIdx.x;
+  const int ti = tid >> 4, tj = tid & 15;   // a 16 x 16 thread grid
   const double* w = W + side * sW + (long)j0 * ldw + j0;
   if (tid == 0) bad = 0;
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    const int i = idx / NB, j = idx % NB;
-    a[i][j] = (i < nb && j < nb && j <= i) ? w[(long)i * ldw + j] : 0.0;
-    inv[i][j] = 0.0;
-  }
+  if (tid < nb) floor_s[tid] = 1e-14 * wdiag[side * sDiag + j0 + tid];
+  for (int i = ti; i < NB; i += 16)
+    for (int j = tj; j < NB; j += 16) {
+      a[i][j] = (i < nb && j < nb && j <= i) ? w[(long)i * ldw + j] : 0.0;
+      inv[i][j] = (i == j) ? 1.0 : 0.0;
+    }
   __syncthreads();
-  const double* w0 = wdiag + side * sDiag + j0;
   for (int k = 0; k < nb; ++k) {
     if (tid == 0) {
       // The pivot is the squared distance of column j0+k of Y from the span of the
@@ -40,7 +44,7 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
       // carries float32 noise), raised to that floor, which damps the near-dependent
       // direction instead of amplifying noise.
       double piv = a[k][k];
-      const double floor_k = 1e-14 * w0[k];
+      const double floor_k = floor_s[k];
       if (!isfinite(piv)) {
         bad = 1;
         piv = 1.0;
@@ -55,36 +59,28 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
       a[k][k] = sqrt(piv);
     }
     __syncthreads();
-    const double dk = a[k][k];
-    for (int i = k + 1 + tid; i < nb; i += 256) a[i][k] /= dk;
+    const double rdk = 1.0 / a[k][k];
+    // column k of L below the pivot, and row k of X (columns c <= k)
+    if (tid < 64) {
+      for (int i = k + 1 + tid; i < nb; i += 64) a[i][k] *= rdk;
+    } else if (tid - 64 <= k) {
+      inv[k][tid - 64] *= rdk;
+    }
     __syncthreads();
-    const int m = nb - k - 1;
-    for (int idx = tid; idx < m * m; idx += 256) {
-      const int i = k + 1 + idx / m, j = k + 1 + idx % m;
-      if (j <= i) a[i][j] -= a[i][k] * a[j][k];
+    // trailing update of the lower triangle (k < j <= i), and the rows of X below k
+    for (int i = k + 1 + ti; i < nb; i += 16) {
+      const double aik = a[i][k];
+      for (int j = k + 1 + tj; j <= i; j += 16) a[i][j] -= aik * a[j][k];
+      for (int c = tj; c <= k; c += 16) inv[i][c] -= aik * inv[k][c];
     }
     __syncthreads();
   }
-  // Column c of L^-1 by forward substitution (thread c).
-  if (tid < nb) {
-    const int c = tid;
-    for (int i = c; i < nb; ++i) {
-      double s = (i == c) ? 1.0 : 0.0;
-      for (int mm = c; mm < i; ++mm) s -= a[i][mm] * inv[mm][c];
-      inv[i][c] = s / a[i][i];
-    }
-  }
-  __syncthreads();
   double* l = L + side * sL + (long)j0 * ldl + j0;
   double* dv = Dinv + side * sD;
-  for (int idx = tid; idx < nb * nb; idx += 256) {
-    const int i = idx / nb, j = idx % nb;
-    l[(long)i * ldl + j] = (j <= i) ? a[i][j] : 0.0;
-  }
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    const int i = idx / NB, j = idx % NB;
-    dv[i * NB + j] = (i < nb && j < nb && j <= i) ? inv[i][j] : 0.0;
-  }
+  for (int i = ti; i < nb; i += 16)
+    for (int j = tj; j < nb; j += 16) l[(long)i * ldl + j] = (j <= i) ? a[i][j] : 0.0;
+  for (int i = ti; i < NB; i += 16)
+    for (int j = tj; j < NB; j += 16) dv[i * NB + j] = (i < nb && j < nb && j <= i) ? inv[i][j] : 0.0;
   if (tid == 0 && bad) info[side] = 1;
 }
 
@@ -112,6 +108,11 @@ __global__ __launch_bounds__(256) void ritz_residual_kernel(const double* YZ, co
   part[rg][c] = s;
   __syncthreads();
   if (rg == 0 && i < r) res2[(long)side * r + i] = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+}
+
+__global__ void widen_kernel(const float* src, double* dst, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = (double)src[i];
 }
 
 __global__ void zero_i32_kernel(int* p, long n) {
@@ -217,6 +218,12 @@ hipError_t launch_ritz_residual(const double* YZ, const double* Vr, const double
 
 hipError_t launch_trace(const double* C, long sC, int n, int n_sides, double* tr, hipStream_t st) {
   hipLaunchKernelGGL(trace_kernel, dim3(n_sides), dim3(256), 0, st, C, sC, n, tr);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen(const float* src, double* dst, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst, n);
   return hipGetLastError();
 }
 

@@ -45,6 +45,8 @@ hipError_t launch_potrf_diag(const double* W, long ldw, long sW, double* L, long
 hipError_t launch_copy_diag(const double* W, long ldw, long sW, double* dg, long sD, int n, int n_sides,
                             hipStream_t st);
 hipError_t launch_zero_i32(int* p, long n, hipStream_t st);
+// dst[i] = src[i] as float64, i < n.
+hipError_t launch_widen(const float* src, double* dst, long n, hipStream_t st);
 // tr[s] = trace of the n x n float64 matrix C + s*sC, for s < n_sides.
 hipError_t launch_trace(const double* C, long sC, int n, int n_sides, double* tr, hipStream_t st);
 // res2[s*r + i] = || YZ[:, i] - theta[s*r + i] * Vr[:, i] ||^2 (n x r float64 per side, side stride n*r).

@@ -15,7 +15,7 @@ def dtype_code(dt: torch.dtype) -> int:
 
 
 def compress(ctx: L.Context, sides, *, r: int, n_kv_heads: int, head_dim: int, chunk: int = 8,
-             rope_theta: float = 10000.0, landmarks=None, oversample: int = -1, fp32_iters: int = 3,
+             rope_theta: float = 10000.0, landmarks=None, oversample: int = -1, fp32_iters: int = 2,
              fp64_iters: int = 2, seed: int = 0, stream=None, ws: torch.Tensor | None = None,
              keep_vr64: bool = False, tol: float = 0.0, max_rounds: int = 0, allow_notconv: bool = False):
     """Factor every group side in ``sides`` (a list of lists of G layer tensors, T x d_kv).

@@ -239,9 +239,12 @@ int xkv_sr_select(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
  * up to rounding. */
 int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream);
 
-/* xkv_sr_select followed by xkv_sr_attend.
+/* xkv_sr_select followed by xkv_sr_attend.  On the matrix-core path (below), with at most
+ * 16384 candidates and an attend grid (KV heads x 64-row splits x batch) no larger than the
+ * device's compute units, the attend kernel selects the top-k itself (one launch fewer): the
+ * same selection, written to args->sel by the attend blocks.
  * Limits (XKV_EUNSUPPORTED beyond them): at most 32768 candidate chunks per KV
- * head; the selected rows (64 per attend block) plus the exact rows (64 per
+ * head; the selected rows (64 per attend block) plus the exact rows (16 per
  * tile) at most 1088 blocks per head on the matrix-core path with compressed
  * values (bf16, head_dim 128, r_k == r_v a multiple of 128 up to 4096; enough
  * for every chunk of a 64k prefix, i.e. full reconstruction) and 257 otherwise.
@@ -254,7 +257,8 @@ int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_byte
 /* One decode step through `n_layers` layers in order (args[l] describes layer l;
  * all share `ws`, which must satisfy xkv_sr_ws_size for every layer): the
  * select and attend kernels of each layer are enqueued back to back on
- * `stream`, with no host synchronisation.  attend_events (nullable): host array
+ * `stream`, with no host synchronisation (the top-k inside the attend kernel
+ * under the conditions of xkv_sr_decode).  attend_events (nullable): host array
  * of 2*n_layers hipEvent_t (timing enabled); events 2l and 2l+1 mark the start
  * and the end of layer l's attend kernel (stamped by its dispatch on the
  * matrix-core path, recorded on `stream` around the launch otherwise). */

@@ -65,6 +65,7 @@ struct Carver {
 
 struct xkv_ctx_s {
   int device = 0;
+  int n_cu = 0;                 // compute units of the device
   int host_threads = 16;
   double* pin = nullptr;        // pinned staging for H (down) and Z (up)
   size_t pin_doubles = 0;
@@ -96,6 +97,7 @@ int xkv_ctx_create(int device, int host_threads, xkv_ctx* out) {
                 prop.gcnArchName);
   xkv_ctx c = new xkv_ctx_s();
   c->device = device;
+  c->n_cu = prop.multiProcessorCount;
   c->host_threads = host_threads > 0 ? host_threads : 16;
   XKV_HIP(hipSetDevice(device));
   {
@@ -635,13 +637,28 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       if (!(est[s] <= tol)) converged = false;
     }
     if (converged || rounds >= max_rounds) break;
+    // Sweeps of the next round: an unconverged side's error shrinks by about
+    // rho = lambda_kb+1 / lambda_r per sweep, estimated by theta_kb / theta_r (the block's
+    // smallest Ritz value over the r-th; a Ritz value lies below its eigenvalue, so the
+    // estimate can be optimistic), so est rho^m <= tol / 2 takes m = log(tol / (2 est)) /
+    // log(rho) sweeps, taken with a margin of 1.5 m + 2.  At least the default count, at
+    // most 32; the default where rho is not below 1 or the estimate is not finite (no gap
+    // at r).
+    int next = p.fp32_iters + p.fp64_iters;
+    for (int s = 0; s < S; ++s) {
+      if (est[s] <= tol || !std::isfinite(est[s]) || !(evals[s][r - 1] > 0.0)) continue;
+      const double rho = evals[s][kb - 1] / evals[s][r - 1];
+      if (!(rho > 0.0 && rho < 0.999)) continue;
+      const double m = std::ceil(1.5 * std::log(tol / (2.0 * est[s])) / std::log(rho)) + 2.0;
+      if (m > next) next = (int)std::min(m, 32.0);
+    }
     for (int h = 0; h < nh; ++h) {
-      rc = fp64_sweeps(hv[h], p.fp32_iters + p.fp64_iters);
+      rc = fp64_sweeps(hv[h], next);
       if (rc) return rc;
       rc = rr_matrix(hv[h], h, false);
       if (rc) return rc;
     }
-    total_iters += p.fp32_iters + p.fp64_iters;
+    total_iters += next;
   }
   pin_guard.armed = false;   // the last round ended with a stream synchronisation
   for (int s = 0; s < S; ++s) {
@@ -789,7 +806,7 @@ int plan_sr(const xkv_sr_args* a, xkv::SrParams* P, size_t* ws_need) {
   // Scoring blocks per head: about 128 candidates each, at most 64.
   p.score_blocks = std::max(1, std::min(64, (n_cand + 127) / 128));
   p.ld_sc = (n_cand + 3) & ~3;
-  p.fuse_topk = mfma && k_eff > 0 && n_cand <= 16384;
+  p.fuse_topk = 0;   // set by the combined entry points (fuse_selection)
   p.scale = a->scale; p.theta = a->rope_theta;
   for (int i = 0; i < a->head_dim / 2; ++i)
     p.turns[i] = std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI);
@@ -820,6 +837,15 @@ void bind_sr_ws(xkv::SrParams* p, void* ws) {
   p->scores = c.take<float>(bh * std::max(p->ld_sc, 4));
   p->part = c.take<float>(bh * std::max(p->n_splits, 1) * p->grp * (2 + p->vdim));
   p->part_ex = c.take<float>(bh * p->n_exact * p->grp * (2 + p->d));
+}
+
+// The combined decode entry points let the matrix-core attend kernel select the top-k
+// itself (one launch fewer) when its grid fits the device's compute units in one round:
+// each attend block then repeats the selection, which a second round of blocks would pay
+// again.  The separate xkv_sr_select / xkv_sr_attend calls keep `sel` as their hand-off.
+void fuse_selection(xkv_ctx ctx, xkv::SrParams* P) {
+  P->fuse_topk = P->mfma && P->k_eff > 0 && P->n_cand <= 16384 &&
+                 (long)P->Hkv * P->n_splits * P->batch <= (long)ctx->n_cu;
 }
 
 int sr_prepare(xkv_ctx ctx, const xkv_sr_args* a, void* ws, size_t ws_bytes, xkv::SrParams* P) {
@@ -860,9 +886,17 @@ extern "C" int xkv_sr_attend(xkv_ctx ctx, const xkv_sr_args* args, void* ws, siz
 }
 
 extern "C" int xkv_sr_decode(xkv_ctx ctx, const xkv_sr_args* args, void* ws, size_t ws_bytes, void* stream) {
-  int rc = xkv_sr_select(ctx, args, ws, ws_bytes, stream);
+  xkv::SrParams P;
+  int rc = sr_prepare(ctx, args, ws, ws_bytes, &P);
   if (rc) return rc;
-  return xkv_sr_attend(ctx, args, ws, ws_bytes, stream);
+  fuse_selection(ctx, &P);
+  const int bf16 = args->dtype == XKV_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  XKV_K(xkv::launch_sr_score(P, bf16, st));
+  XKV_K(xkv::launch_sr_topk(P, bf16, st));
+  XKV_K(xkv::launch_sr_attend(P, bf16, st));
+  XKV_K(xkv::launch_sr_merge(P, st));
+  return XKV_OK;
 }
 
 extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args* args, void* ws, size_t ws_bytes,
@@ -872,6 +906,7 @@ extern "C" int xkv_sr_decode_layers(xkv_ctx ctx, int n_layers, const xkv_sr_args
   for (int l = 0; l < n_layers; ++l) {
     int rc = sr_prepare(ctx, &args[l], ws, ws_bytes, &P[l]);
     if (rc) return rc;
+    fuse_selection(ctx, &P[l]);
   }
   hipStream_t st = (hipStream_t)stream;
   for (int l = 0; l < n_layers; ++l) {
@@ -900,6 +935,7 @@ extern "C" int xkv_sr_decode_layers_noalloc(xkv_ctx ctx, int n_layers, const xkv
       return fail(XKV_EWORKSPACE, "xkv_sr_decode_layers_noalloc: layer %d needs %zu bytes of scratch, above the "
                   "library's %zu (use xkv_sr_decode_layers with a workspace)", l, need, xkv::kSrScratchBytes);
     bind_sr_ws(&P[l], ws);
+    fuse_selection(ctx, &P[l]);
   }
   hipStream_t st = (hipStream_t)stream;
   for (int l = 0; l < n_layers; ++l) {

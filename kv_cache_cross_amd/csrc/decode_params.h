@@ -24,8 +24,9 @@ struct SrParams {
   long q_pos;        // query position p
   int score_blocks;  // select-kernel blocks per KV head
   int ld_sc;         // row stride of `scores`: n_cand rounded up to a multiple of 4
-  int fuse_topk;     // matrix-core path with n_cand <= 16384: every attend block selects
-                     // the head's top-k chunks itself (no separate top-k launch)
+  int fuse_topk;     // every attend block selects the head's top-k chunks itself (no separate
+                     // top-k launch): the combined entry points on the matrix-core path with
+                     // n_cand <= 16384 and an attend grid within the device's compute units
   float scale;
   double theta;
   double turns[64];  // theta^(-2i/d) / (2 pi) for i < d/2, formed on the host in float64

@@ -253,6 +253,51 @@ def test_decode_mini_bf16_steps(ctx):
     _run_decode_case(ctx, wl, steps=4, layer=2, label="mini bf16 xKV-SR")
 
 
+def test_select_then_attend_honours_edited_selection(ctx):
+    # The separate entry points hand the selection over through `sel`: xkv_sr_select
+    # writes the top-k, xkv_sr_attend attends over whatever `sel` holds.  Here the
+    # selection is replaced, between the two calls, by the k lowest-scoring candidate
+    # chunks (ascending ids), and the output must match the oracle on that edited set.
+    wl = make_workload("llama16k", device=DEV, **MINI)
+    c = wl.cfg
+    layer = 1
+    cache = oracle_cache(wl, c.rank, layer)
+    Ks, Vs = wl.group_kv(0, "K", 0), wl.group_kv(0, "V", 0)
+    dec = xk.LayerDecoder(ctx, batch=1, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim,
+                          T=c.T, chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink, n_local=c.n_local, r_k=c.rank,
+                          r_v=c.rank, dtype=c.torch_dtype, device=DEV, max_gen=1)
+    rows = tail_rows(c.T, c.n_sink, c.n_local)
+    k_tail = torch.zeros((len(rows) + 1, c.d_kv), dtype=c.torch_dtype, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[: len(rows)] = Ks[layer][rows]
+    v_tail[: len(rows)] = Vs[layer][rows]
+    q = wl.query(0, layer, 0)
+    kn, vn = wl.new_token(0, "K", layer, 0), wl.new_token(0, "V", layer, 0)
+    args = dec.args(n_gen=1, q=q, A_k=cache["A_k"], Bt_k=cache["Bt_k"], A_v=cache["A_v"], Bt_v=cache["Bt_v"],
+                    landmarks=cache["lm"], k_tail=k_tail, v_tail=v_tail, k_new=kn, v_new=vn)
+    Kl, Vl = f64(Ks[layer]), f64(Vs[layer])
+    kw = dict(T=c.T, n_gen=1, n_kv_heads=c.n_kv_heads, chunk=c.chunk, top_k=c.top_k, n_sink=c.n_sink,
+              n_local=c.n_local, landmarks_l=f64(cache["lm"]), A_k=f64(cache["A_k"]), B_k_l=f64(cache["Bt_k"]).T,
+              A_v=f64(cache["A_v"]), B_v_l=f64(cache["Bt_v"]).T,
+              k_exact={**{t: Kl[t] for t in rows}, c.T: f64(kn)}, v_exact={**{t: Vl[t] for t in rows}, c.T: f64(vn)})
+    ref = oracle.sr_decode_layer(f64(q), **kw)
+    dec.select(args)
+    torch.cuda.synchronize()
+    sel = dec.sel.cpu().numpy()[0]
+    for h in range(c.n_kv_heads):
+        check_selection(sel[h], ref["scores"][h], c.top_k)
+    edited = np.stack([np.sort(np.argsort(ref["scores"][h], kind="stable")[: c.top_k])
+                       for h in range(c.n_kv_heads)]).astype(np.int32)
+    dec.sel.copy_(torch.from_numpy(edited[None]).to(DEV))
+    out = dec.attend(args)
+    torch.cuda.synchronize()
+    ref_e = oracle.sr_decode_layer(f64(q), selection=edited, **kw)
+    rel, mx = attention_errors(f64(out)[0], ref_e["out"])
+    log(f"edited selection: rel L2 {rel:.2e}, max abs {mx:.2e}")
+    assert rel <= 1e-3 and mx <= ATT_ABS_BF16, (rel, mx)
+    assert torch.equal(dec.sel.cpu(), torch.from_numpy(edited[None]))   # attend left `sel` as given
+
+
 def test_decode_exact_tail_crosses_tiles(ctx):
     # 4 sink + 122 local rows plus 1..4 generated tokens: the exact tail grows from 127 to
     # 130 rows and crosses from eight 16-row tiles into a ninth.

@@ -356,7 +356,10 @@ def test_error_estimate_tracks_projector_error(ctx):
         log(f"  sweeps {o['stats']['sweeps']} rounds {o['stats']['rounds']}: ||dP||_F {dP:.2e} estimate {est:.2e} "
             f"ratio {est / max(dP, 1e-300):.2f}")
     for dP, est in pairs:
-        if dP < 1e-9:        # at float64 rounding level neither number carries information
+        # The distance is sqrt(a + b - 2c) with a, b, c ~ r = 128 (projector_distance): its
+        # terms cancel to about r * 2^-52, so below ~1e-6 it measures its own rounding
+        # (~2e-7), not the subspace.
+        if dP < 1e-6:
             continue
         assert dP <= 1.5 * est, (dP, est)       # the estimate bounds the error
         assert est <= 40.0 * dP, (dP, est)      # and is not loose by more than this factor (10-25 seen)

@@ -42,13 +42,13 @@ BF16_PEAK_TFLOPS = 2500.0
 # what the same counter reads for a 1 GiB device-to-device copy (read 524304.4 KiB, written
 # 1048576 KiB).  It stands only while the decode kernels' source is the one measured: the
 # source's SHA-256 prefix is recorded and `traffic` is null when it differs.
-ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "fb3420a5b2388c95", "fetch_kib": 17001.1, "write_kib": 2056.0,
+ATTEND_TRAFFIC = {"src": "decode.hip", "src_sha256": "8c075953f7a77c2c", "fetch_kib": 17180.3, "write_kib": 2064.0,
                   "fetch_scale": 1048576.0 / 524304.4, "write_scale": 1.0}
 # The same for one launch of the Gram kernel over the 16 group sides of the 64k workload
 # (the mean of bench.py's two 16-side timing dispatches).  FETCH_SIZE counts what the L2
 # caches request from the memory fabric, so the Infinity Cache's hits are included: it
 # is the Gram's L2-miss traffic.
-GRAM_TRAFFIC = {"src": "gram.hip", "src_sha256": "20860a837367a954", "fetch_kib": 50881542.9, "write_kib": 2210683.0,
+GRAM_TRAFFIC = {"src": "gram.hip", "src_sha256": "20860a837367a954", "fetch_kib": 51651792.8, "write_kib": 2180760.2,
                 "fetch_scale": 1048576.0 / 524304.4, "write_scale": 1.0}
 
 
@@ -223,9 +223,13 @@ def main():
             L.sr_decode_layers(ctx, step_args[s], dec.ws, attend_events=events[s] if timed else None)
 
     # ---- warmup ----
-    for _ in range(args.warmup):
+    for w in range(args.warmup):
         compress()
+        torch.cuda.synchronize()
+        log(f"[bench] warm-up {w}: compression done")
         decode(False)
+        torch.cuda.synchronize()
+        log(f"[bench] warm-up {w}: decode done")
     torch.cuda.synchronize()
 
     # ---- timed steps ----
@@ -242,6 +246,7 @@ def main():
         a2 = time.perf_counter()
         t_comp.append(a1 - a0)
         t_dec.append(a2 - a1)
+        log(f"[bench] timed step {len(t_comp) - 1}: compression {a1 - a0:.3f} s, decode {a2 - a1:.3f} s")
         attend_ms.append(np.array([events[s][2 * t_layer[s]].elapsed_time(events[s][2 * t_layer[s] + 1])
                                    for s in range(D)]))
     torch.cuda.synchronize()

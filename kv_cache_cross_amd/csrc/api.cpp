@@ -641,16 +641,17 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     // rho = lambda_kb+1 / lambda_r per sweep, estimated by theta_kb / theta_r (the block's
     // smallest Ritz value over the r-th; a Ritz value lies below its eigenvalue, so the
     // estimate can be optimistic), so est rho^m <= tol / 2 takes m = log(tol / (2 est)) /
-    // log(rho) sweeps, taken with a margin of 1.5 m + 2.  At least the default count, at
-    // most 32; the default where rho is not below 1 or the estimate is not finite (no gap
-    // at r).
+    // log(rho) sweeps, taken with a margin of 1.5 m + 2.  At least the default count; the
+    // default where rho is not below 1, the estimate is not finite (no gap at r) or the
+    // prediction exceeds 32 sweeps (a side that one round cannot bring to tol, such as one
+    // whose r-th eigenvalue lies in a flat noise bulk, gains nothing from more).
     int next = p.fp32_iters + p.fp64_iters;
     for (int s = 0; s < S; ++s) {
       if (est[s] <= tol || !std::isfinite(est[s]) || !(evals[s][r - 1] > 0.0)) continue;
       const double rho = evals[s][kb - 1] / evals[s][r - 1];
       if (!(rho > 0.0 && rho < 0.999)) continue;
       const double m = std::ceil(1.5 * std::log(tol / (2.0 * est[s])) / std::log(rho)) + 2.0;
-      if (m > next) next = (int)std::min(m, 32.0);
+      if (m > next && m <= 32.0) next = (int)m;
     }
     for (int h = 0; h < nh; ++h) {
       rc = fp64_sweeps(hv[h], next);

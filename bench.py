@@ -110,6 +110,17 @@ def main():
     dt = c.torch_dtype
     esz = 2 if dt == torch.bfloat16 else 4
     dev = torch.device("cuda:0")
+    # The library's rule for selecting the top-k inside the attend kernel (3 launches per layer
+    # instead of 4): the matrix-core path (bf16, head dim 128, rank a multiple of 128), at most
+    # 16384 candidates, and an attend grid (KV heads x 64-row splits x batch) within the
+    # device's compute units.
+    n_cand_h = -(-(T - c.n_local) // c.chunk)
+    k_eff_h = min(c.top_k, n_cand_h)
+    n_splits_h = -(-k_eff_h // (64 // c.chunk))
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    fused = (dt == torch.bfloat16 and d == 128 and r % 128 == 0 and 0 < k_eff_h and n_cand_h <= 16384
+             and H * n_splits_h * B <= n_cu)
+    attend_kernel = f"sr_attend_mfma_kernel<false, false, {(16 if n_cand_h <= 8192 else 32) if fused else 0}>"
     torch.cuda.set_device(dev)
     log(f"[bench] workload {c.name}: B={B} L={Lyr} G={G} H_kv={H} d={d} H_q={Hq} T={T} r={r} top_k={c.top_k} "
         f"decode steps={D}")
@@ -316,10 +327,6 @@ def main():
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) / D * 1e3)
             same = same and bool(torch.equal(out, out_eager)) and bool(torch.equal(sel, sel_eager))
-        # the library's matrix-core path (bf16, head dim 128, rank a multiple of 128) with at most
-        # 16384 candidates selects the top-k inside the attend kernel: 3 launches per layer
-        n_cand_h = -(-(T - c.n_local) // c.chunk)
-        fused = dt == torch.bfloat16 and d == 128 and r % 128 == 0 and n_cand_h <= 16384
         graph = {"us_per_step": round(float(np.median(times)), 2), "replays_match_eager": same,
                  "launches_per_step": (3 if fused else 4) * Lyr}
         del g
@@ -495,7 +502,7 @@ def main():
         "compress_stats": {"err_est_max": float(max(st[0] for st in stats)), "sweeps": int(stats[0][2]),
                            "rounds": int(stats[0][3]), "sides": S, "calls": len(calls),
                            "sides_not_converged": notconv[0]},
-        "roofline": {"bound": "hbm", "kernel": "sr_attend_mfma_kernel<false, false>", "achieved": round(achieved_att, 1),
+        "roofline": {"bound": "hbm", "kernel": attend_kernel, "achieved": round(achieved_att, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_att / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": int(algo_bytes_launch),

@@ -38,8 +38,11 @@ def ctx():
 # ----------------------------------------------------------------------------- Gram
 @pytest.mark.parametrize("T,G,d_kv,dt", [(256, 2, 64, torch.float32), (1000, 2, 256, torch.bfloat16),
                                           (777, 3, 136, torch.bfloat16), (64, 1, 8, torch.bfloat16),
-                                          (4133, 4, 128, torch.bfloat16)])
+                                          (4133, 4, 128, torch.bfloat16), (25810, 4, 128, torch.bfloat16),
+                                          (65536, 2, 256, torch.bfloat16)])
 def test_gram(T, G, d_kv, dt):
+    # The long cases sum 51 and 128 matrix-core partials of 512 tokens (the first with a
+    # ragged last slab) into the compensated float32 totals: the same bar as the short ones.
     log(f"gram T={T} G={G} d_kv={d_kv} {dt}")
     layers = [gaussian((T, d_kv), seed=100 + l, scale=1.5, dtype=dt, device=DEV) for l in range(G)]
     C = xk.gram(layers)

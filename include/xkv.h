@@ -72,8 +72,7 @@ typedef struct xkv_ctx_s* xkv_ctx;
 int xkv_version(void);
 
 /* Create a context bound to HIP device `device`; `host_threads` bounds the
- * threads used for the host Rayleigh-Ritz eigensolves (<= 0: one per side,
- * at most 16).  On success *out receives the context. */
+ * threads used for the host Rayleigh-Ritz eigenvalue solves (<= 0: 16).  On success *out receives the context. */
 int xkv_ctx_create(int device, int host_threads, xkv_ctx* out);
 void xkv_ctx_destroy(xkv_ctx ctx);
 
@@ -122,11 +121,15 @@ int xkv_compress_ws_size(const xkv_compress_desc* desc, int n_sides, size_t* byt
 /* Factor `n_sides` independent group sides of identical shape.
  * Steps (sides batched): Gram C = X^T X (bf16 MFMA, float64 totals) ->
  * block subspace iteration Y = C Q with CholeskyQR orthonormalisation ->
- * Rayleigh-Ritz H = Q^T C Q (float64) -> host eigensolve of H (plain C; the
- * eigenvalues one thread per side, the eigenvectors two threads per side) ->
- * V_r = Q Z_r -> A = X V_r and the landmarks.  With 4 or more sides the
- * sides go in two halves, so that the GPU steps of the second half run while
- * the host solves the first half's eigenproblems.
+ * Rayleigh-Ritz H = Q^T C Q (float64) -> eigenvalues of H on the host (plain
+ * C: Householder reduction, shared by two threads per side when k_b >= 256 and
+ * host threads allow, then implicit QR whose plane rotations are logged) ->
+ * the wanted eigenvectors Z_r on the GPU (the logged rotations applied to unit
+ * vectors, then the reflectors as compact-WY products) -> V_r = Q Z_r ->
+ * A = X V_r and the landmarks.  With 4 or more sides the sides go in two
+ * halves, so that the GPU steps of the second half run while the host solves
+ * the first half's eigenvalues.  Allocates the rotation logs' pinned staging
+ * and device copy in the context (kept and grown between calls).
  * Convergence: after each Rayleigh-Ritz round the Ritz residuals
  * r_i = C v_i - theta_i v_i give the estimate
  * sqrt(2 sum_i ||r_i||^2 / (theta_i - theta_{r+1})^2) of ||P - P_exact||_F
@@ -396,7 +399,9 @@ int xkv_topk(const float* scores, int rows, int n_cand, long ld, int k, int* sel
  * Householder tridiagonalisation + implicit QR with Wilkinson shifts).
  * H (host, n x n, row stride n, symmetric) is not modified.  Writes the nvec
  * largest eigenvalues to w (host, descending) and their eigenvectors as the
- * columns of Z (host, n x nvec, row stride nvec).  Runs without a GPU. */
+ * columns of Z (host, n x nvec, row stride nvec).  Runs without a GPU, in the
+ * calling thread and one more (the reduction's row passes shared by the two, as
+ * compressions run it for k_b >= 256 when host threads allow). */
 int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z);
 
 #ifdef __cplusplus

@@ -67,8 +67,14 @@ struct xkv_ctx_s {
   int device = 0;
   int n_cu = 0;                 // compute units of the device
   int host_threads = 16;
-  double* pin = nullptr;        // pinned staging for H (down) and Z (up)
+  double* pin = nullptr;        // pinned staging for H, residuals (down) and reflectors (up)
   size_t pin_doubles = 0;
+  // Per half of a compression's sides: the rotation logs of the Rayleigh-Ritz eigensolves
+  // (pinned staging and the device copy the vector kernel reads), grown as needed.
+  void* lpin[2] = {nullptr, nullptr};
+  size_t lpin_bytes[2] = {0, 0};
+  void* ldev[2] = {nullptr, nullptr};
+  size_t ldev_bytes[2] = {0, 0};
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
   // Host memory of the Rayleigh-Ritz eigensolves, two per side (value state + first half of
@@ -125,6 +131,10 @@ void xkv_ctx_destroy(xkv_ctx ctx) {
   for (hipEvent_t e : ctx->half_done)
     if (e) (void)hipEventDestroy(e);
   if (ctx->pin) (void)hipHostFree(ctx->pin);
+  for (int h = 0; h < 2; ++h) {
+    if (ctx->lpin[h]) (void)hipHostFree(ctx->lpin[h]);
+    if (ctx->ldev[h]) (void)hipFree(ctx->ldev[h]);
+  }
   for (auto& sc : ctx->eig_side) xkv_eigh_scratch_release(&sc);
   delete ctx;
 }
@@ -153,10 +163,16 @@ int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z) {
   if (n <= 0 || !H || !w || !Z || nvec <= 0 || nvec > n)
     return fail(XKV_EINVAL, "xkv_host_eigh: bad arguments (n=%d, nvec=%d)", n, nvec);
   std::vector<double> all(n);
-  // The two phases as compressions run them: the vector phase in two column ranges, the second
-  // with working memory of its own (the way a helper thread takes half of a side).
+  // The two phases as compressions run them: the value phase shared by two threads, the
+  // vector phase in two column ranges, the second with working memory of its own (the way a
+  // helper thread takes half of a side).
   xkv_eigh_scratch sc{}, helper{};
-  int rc = xkv_eigh_values(n, H, nvec, all.data(), &sc);
+  xkv_eigh_pair pr{};
+  int wrc = 0;
+  std::thread worker([&]() { wrc = xkv_eigh_values_pair(n, H, nvec, nullptr, &sc, &helper, &pr, 1, nullptr); });
+  int rc = xkv_eigh_values_pair(n, H, nvec, all.data(), &sc, &helper, &pr, 0, nullptr);
+  worker.join();
+  if (rc == 0 && wrc != 0) rc = wrc;
   if (rc == 0) rc = xkv_eigh_vectors(&sc, 0, nvec / 2, Z, &sc);
   if (rc == 0) rc = xkv_eigh_vectors(&sc, nvec / 2, nvec, Z, &helper);
   xkv_eigh_scratch_release(&sc);
@@ -213,6 +229,8 @@ struct CompressWs {
   double* Q64; double* Y64;
   double* W; double* L; double* Dinv;
   double* H; double* Z; double* Vr;
+  double* Rf; int* pos; double* Wb;   // packed reflector blocks, wanted positions, block products
+  double* Zs;                         // working memory of the rotation kernel
   double* wdiag;
   double* YZ; double* theta; double* res2;
   void* VrT;
@@ -236,6 +254,10 @@ CompressWs carve_compress(void* ws, const CompressPlan& p, int S) {
   w.Dinv = c.take<double>((size_t)S * p.nblk * 64 * 64);
   w.H = c.take<double>(S * kk);
   w.Z = c.take<double>((size_t)S * p.kb * p.r);
+  w.Rf = c.take<double>((size_t)S * xkv_eigh_refl_doubles(p.kb));
+  w.pos = c.take<int>((size_t)S * p.r);
+  w.Wb = c.take<double>((size_t)S * 2 * XKV_EIGH_NBG * p.r);
+  w.Zs = c.take<double>((size_t)S * xkv::ritz_scratch_doubles(p.kb, p.r));
   w.Vr = c.take<double>((size_t)S * p.n * p.r);
   w.wdiag = c.take<double>((size_t)S * p.kb);
   w.YZ = c.take<double>((size_t)S * p.n * p.r);
@@ -264,6 +286,10 @@ CompressWs shift_compress_ws(const CompressWs& w, const CompressPlan& p, int s0)
   v.Dinv += (size_t)s0 * p.nblk * 64 * 64;
   v.H += s0 * kk;
   v.Z += (size_t)s0 * p.kb * p.r;
+  v.Rf += (size_t)s0 * xkv_eigh_refl_doubles(p.kb);
+  v.pos += (size_t)s0 * p.r;
+  v.Wb += (size_t)s0 * 2 * XKV_EIGH_NBG * p.r;
+  v.Zs += (size_t)s0 * xkv::ritz_scratch_doubles(p.kb, p.r);
   v.Vr += s0 * nr;
   v.wdiag += (size_t)s0 * p.kb;
   v.YZ += s0 * nr;
@@ -450,8 +476,11 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   };
   int total_iters = p.fp32_iters + p.fp64_iters;
 
-  // Pinned staging: H (down), Z and Ritz values (up), residual norms and info (down).
-  const size_t need_pin = (size_t)S * kk + (size_t)S * kb * r + (size_t)S * r + (size_t)S * r + (size_t)S + (size_t)S;
+  // Pinned staging: H (down), packed reflectors and Ritz values (up), residual norms, traces
+  // and info (down), wanted positions (up).
+  const size_t refl = xkv_eigh_refl_doubles(kb);
+  const size_t need_pin = (size_t)S * kk + (size_t)S * refl + (size_t)S * r + (size_t)S * r + (size_t)S + (size_t)S +
+                          ((size_t)S * r + 1) / 2;
   if (ctx->upload_pending) {
     XKV_HIP(hipEventSynchronize(ctx->upload_done));
     ctx->upload_pending = false;
@@ -478,11 +507,12 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     }
   } pin_guard{ctx, st, true};
   double* hH = ctx->pin;
-  double* hZ = hH + (size_t)S * kk;
-  double* hTheta = hZ + (size_t)S * kb * r;
+  double* hRefl = hH + (size_t)S * kk;
+  double* hTheta = hRefl + (size_t)S * refl;
   double* hRes = hTheta + (size_t)S * r;
   double* hTrace = hRes + (size_t)S * r;
   int* hinfo = (int*)(hTrace + S);
+  int* hPos = (int*)(hTrace + 2 * S);
 
   // 3. Rayleigh-Ritz rounds.  After each, the Ritz residuals R = (C Q) Z - V_r diag(theta)
   //    bound the subspace error (per-pair sin-theta bounds, below).  Unconverged rounds add
@@ -511,46 +541,138 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     XKV_HIP(hipEventRecord(ctx->half_done[h], st));
     return XKV_OK;
   };
-  // The host eigensolves of a half: the value phase one thread per side, then the vector
-  // phase in two column ranges per side, all on at most ctx->host_threads threads.
-  auto solve_half = [&](const Half& hf) -> int {
-    std::vector<int> erc(hf.cnt, 0);
-    const int nthr_v = std::max(1, std::min(hf.cnt, ctx->host_threads));
-    const int nthr_z = std::max(1, std::min(2 * hf.cnt, ctx->host_threads));
-    auto run = [&](int nthr, int ntask, auto&& task) {
-      if (nthr == 1) {
-        for (int t = 0; t < ntask; ++t) task(t);
-        return;
-      }
-      std::vector<std::thread> pool;
-      for (int t0 = 0; t0 < nthr; ++t0)
-        pool.emplace_back([&, t0]() {
-          for (int t = t0; t < ntask; t += nthr) task(t);
-        });
-      for (auto& th : pool) th.join();
-    };
-    run(nthr_v, hf.cnt, [&](int i) {
+  // The host eigensolves of a half: the value phase one thread per side, or two (a leader and a
+  // worker sharing the reduction's row passes; the worker then packs the reflectors while the
+  // leader runs the QR iteration) where every pair gets threads of its own and the side is
+  // large enough to pay for a barrier per pass; all on at most ctx->host_threads threads.
+  // The vector phase runs on the device (post_work): each side's rotation log is packed here
+  // into the half's pinned staging, its reflector blocks and wanted positions into ctx->pin.
+  const int run_cap = ritz_run_cap();
+  std::vector<long long> meta(4 * (size_t)S, 0);
+  size_t log_bytes[2] = {0, 0};
+  auto run_threads = [&](int nthr, int ntask, auto&& task) {
+    if (nthr <= 1) {
+      for (int t = 0; t < ntask; ++t) task(t);
+      return;
+    }
+    std::vector<std::thread> pool;
+    for (int t0 = 0; t0 < nthr; ++t0)
+      pool.emplace_back([&, t0]() {
+        for (int t = t0; t < ntask; t += nthr) task(t);
+      });
+    for (auto& th : pool) th.join();
+  };
+  auto solve_half = [&](const Half& hf, int h) -> int {
+    std::vector<int> erc(hf.cnt, 0), nruns(hf.cnt, 0);
+    const bool paired = kb >= 256 && 2 * hf.cnt <= ctx->host_threads;
+    auto finish = [&](int i) {   // after a side's values: its positions and run count
       const int s = hf.s0 + i;
-      erc[i] = xkv_eigh_values(kb, hH + (size_t)s * kk, r, evals[s].data(), &ctx->eig_side[2 * s]);
-    });
+      xkv_eigh_positions(&ctx->eig_side[2 * s], hPos + (size_t)s * r);
+      nruns[i] = xkv_eigh_runs(&ctx->eig_side[2 * s], run_cap);
+    };
+    if (paired) {
+      // 2 cnt tasks on 2 cnt threads, so both members of a pair run at once
+      std::vector<xkv_eigh_pair> prs(hf.cnt, xkv_eigh_pair{});
+      std::vector<int> wrc(hf.cnt, 0);
+      run_threads(2 * hf.cnt, 2 * hf.cnt, [&](int t) {
+        const int i = t / 2, tid = t % 2, s = hf.s0 + i;
+        const int rc = xkv_eigh_values_pair(kb, hH + (size_t)s * kk, r, evals[s].data(), &ctx->eig_side[2 * s],
+                                            &ctx->eig_side[2 * s + 1], &prs[i], tid, hRefl + (size_t)s * refl);
+        (tid ? wrc[i] : erc[i]) = rc;
+        if (tid == 0 && rc == 0) finish(i);
+      });
+      for (int i = 0; i < hf.cnt; ++i)
+        if (erc[i] == 0 && wrc[i] != 0) erc[i] = wrc[i];
+    } else {
+      run_threads(std::min(hf.cnt, ctx->host_threads), hf.cnt, [&](int i) {
+        const int s = hf.s0 + i;
+        erc[i] = xkv_eigh_values(kb, hH + (size_t)s * kk, r, evals[s].data(), &ctx->eig_side[2 * s]);
+        if (erc[i] == 0) {
+          xkv_eigh_pack_reflectors(&ctx->eig_side[2 * s], hRefl + (size_t)s * refl);
+          finish(i);
+        }
+      });
+    }
     for (int i = 0; i < hf.cnt; ++i)
       if (erc[i]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + i, erc[i]);
-    std::vector<int> zrc(2 * hf.cnt, 0);
-    run(nthr_z, 2 * hf.cnt, [&](int t) {
-      const int i = t / 2, half = t % 2, s = hf.s0 + i;
-      zrc[t] = xkv_eigh_vectors(&ctx->eig_side[2 * s], half ? r / 2 : 0, half ? r : r / 2, hZ + (size_t)s * kb * r,
-                                &ctx->eig_side[2 * s + half]);
+    // The half's log staging: meta (4 per side) | runs (4 ints each) | (c, s) pairs.
+    long long runs_tot = 0, rot_tot = 0;
+    for (int i = 0; i < hf.cnt; ++i) {
+      const int s = hf.s0 + i;
+      meta[4 * s] = runs_tot;
+      meta[4 * s + 1] = nruns[i];
+      meta[4 * s + 2] = rot_tot;
+      runs_tot += nruns[i];
+      rot_tot += ctx->eig_side[2 * s].log.n;
+    }
+    const size_t meta_b = 32 * (size_t)hf.cnt, runs_b = 16 * (size_t)runs_tot, need = meta_b + runs_b + 16 * (size_t)rot_tot;
+    if (ctx->lpin_bytes[h] < need) {
+      // no copy reads this half's staging now: each compression round ends with a stream
+      // synchronisation, and an earlier call's copies are waited for on entry
+      if (ctx->lpin[h]) XKV_HIP(hipHostFree(ctx->lpin[h]));
+      ctx->lpin[h] = nullptr;
+      ctx->lpin_bytes[h] = 0;
+      const size_t want = need + need / 4;
+      XKV_HIP(hipHostMalloc(&ctx->lpin[h], want, hipHostMallocDefault));
+      ctx->lpin_bytes[h] = want;
+    }
+    char* lp = (char*)ctx->lpin[h];
+    std::memcpy(lp, meta.data() + 4 * (size_t)hf.s0, meta_b);
+    run_threads(std::min(hf.cnt, ctx->host_threads), hf.cnt, [&](int i) {
+      const int s = hf.s0 + i;
+      xkv_eigh_pack_log(&ctx->eig_side[2 * s], run_cap, (int*)(lp + meta_b) + 4 * meta[4 * s],
+                        (double*)(lp + meta_b + runs_b) + 2 * meta[4 * s + 2]);
     });
-    for (int t = 0; t < 2 * hf.cnt; ++t)
-      if (zrc[t]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + t / 2, zrc[t]);
+    log_bytes[h] = need;
     for (int i = 0; i < hf.cnt; ++i)
       std::memcpy(hTheta + (size_t)(hf.s0 + i) * r, evals[hf.s0 + i].data(), r * sizeof(double));
     return XKV_OK;
   };
-  // V_r = Q Z and the residual of every Ritz pair of a half.
-  auto post_work = [&](Half& hf) -> int {
-    XKV_HIP(hipMemcpyAsync(hf.w.Z, hZ + (size_t)hf.s0 * kb * r, (size_t)hf.cnt * kb * r * sizeof(double),
+  // The Ritz vectors Z of a half on the device (the rotations of each side's QR iteration applied
+  // to its wanted unit vectors, then its reflectors, last block first, as S2 -= Y (T (Y^T S2))),
+  // then V_r = Q Z and the residual of every Ritz pair.
+  auto post_work = [&](Half& hf, int h) -> int {
+    const int NBG = XKV_EIGH_NBG;
+    XKV_HIP(hipMemcpyAsync(hf.w.Rf, hRefl + (size_t)hf.s0 * refl, (size_t)hf.cnt * refl * sizeof(double),
                            hipMemcpyHostToDevice, st));
+    XKV_HIP(hipMemcpyAsync(hf.w.pos, hPos + (size_t)hf.s0 * r, (size_t)hf.cnt * r * sizeof(int), hipMemcpyHostToDevice,
+                           st));
+    if (ctx->ldev_bytes[h] < log_bytes[h]) {
+      // the previous reader of this half's device log finished before its round's synchronisation
+      if (ctx->ldev[h]) XKV_HIP(hipFree(ctx->ldev[h]));
+      ctx->ldev[h] = nullptr;
+      ctx->ldev_bytes[h] = 0;
+      const size_t want = log_bytes[h] + log_bytes[h] / 4;
+      XKV_HIP(hipMalloc(&ctx->ldev[h], want));
+      ctx->ldev_bytes[h] = want;
+    }
+    XKV_HIP(hipMemcpyAsync(ctx->ldev[h], ctx->lpin[h], log_bytes[h], hipMemcpyHostToDevice, st));
+    const char* ld = (const char*)ctx->ldev[h];
+    const size_t meta_b = 32 * (size_t)hf.cnt;
+    const long long runs_tot = meta[4 * (hf.s0 + hf.cnt - 1)] + meta[4 * (hf.s0 + hf.cnt - 1) + 1] -
+                               meta[4 * hf.s0];
+    XKV_K(launch_ritz_rotate((const int4*)(ld + meta_b), (const double2*)(ld + meta_b + 16 * (size_t)runs_tot),
+                             (const long long*)ld, hf.w.pos, kb, r, hf.w.Z, (long)kb * r, hf.w.Zs,
+                             ritz_scratch_doubles(kb, r), hf.cnt, st));
+    const int nref = kb - 2;
+    const int nblk = nref > 0 ? (nref + NBG - 1) / NBG : 0;
+    const size_t ytot = refl - (size_t)nblk * NBG * NBG;
+    double* W1 = hf.w.Wb;
+    double* W2 = hf.w.Wb + (size_t)NBG * r;
+    const long sWb = 2L * NBG * r;
+    for (int b = nblk - 1; b >= 0; --b) {
+      const int r0 = NBG * b + 1, M = kb - r0;
+      const size_t yoff = (size_t)NBG * ((size_t)b * (kb - 1) - (size_t)NBG * b * (b - 1) / 2);
+      const double* Y = hf.w.Rf + yoff;
+      const double* T = hf.w.Rf + ytot + (size_t)b * NBG * NBG;
+      double* S2 = hf.w.Z + (size_t)r0 * r;
+      XKV_K(gemm(gdesc(NBG, r, M, 1, 0, GF64, GF64, GF64, Y, NBG, (long)refl, S2, r, (long)kb * r, W1, r, sWb, 1.0,
+                       0.0, hf.cnt), st));
+      XKV_K(gemm(gdesc(NBG, r, NBG, 0, 0, GF64, GF64, GF64, T, NBG, (long)refl, W1, r, sWb, W2, r, sWb, 1.0, 0.0,
+                       hf.cnt), st));
+      XKV_K(gemm(gdesc(M, r, NBG, 0, 0, GF64, GF64, GF64, Y, NBG, (long)refl, W2, r, sWb, S2, r, (long)kb * r, -1.0,
+                       1.0, hf.cnt), st));
+    }
     XKV_HIP(hipMemcpyAsync(hf.w.theta, hTheta + (size_t)hf.s0 * r, (size_t)hf.cnt * r * sizeof(double),
                            hipMemcpyHostToDevice, st));
     XKV_K(gemm(gdesc(n, r, kb, 0, 0, GF64, GF64, GF64, hf.Qa, kb, nk, hf.w.Z, r, (long)kb * r, hf.w.Vr, r,
@@ -606,9 +728,9 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
           return fail(XKV_ENUMERIC, "compress: Cholesky breakdown on side %d (rank of X below %d?)", hf.s0 + i, kb);
       for (size_t i = (size_t)hf.s0 * kk; i < (size_t)(hf.s0 + hf.cnt) * kk; ++i)
         if (!std::isfinite(hH[i])) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix");
-      rc = solve_half(hf);
+      rc = solve_half(hf, h);
       if (rc) return rc;
-      rc = post_work(hf);
+      rc = post_work(hf, h);
       if (rc) return rc;
     }
     XKV_HIP(hipEventRecord(ctx->upload_done, st));

@@ -9,7 +9,8 @@
  *                 bottom-up deflation; the plane rotations are recorded, not
  *                 applied while the iteration runs.
  *
- * The rotation and product kernels use AVX-512 where the CPU has it.
+ * The rotation and product kernels use AVX-512 where the CPU has it.  The reduction's
+ * O(n^2) row passes can be shared by two threads (xkv_eigh_values_pair).
  *
  * Only the nvec wanted eigenvectors are formed: the recorded rotations are
  * applied, last first, to the nvec unit vectors that select the wanted columns
@@ -22,6 +23,7 @@
  * (section 8.3.3).
  */
 #include <math.h>
+#include <sched.h>
 #include <stdlib.h>
 #include <string.h>
 #include <immintrin.h>
@@ -45,45 +47,175 @@ static void house(int m, const double* x, double* v, double* beta, double* mu) {
   *mu = nrm;
 }
 
+/* Two threads' meeting point: a spin barrier (a generation count), the failure flag of the
+ * start and the worker's next job, all plain ints read and written through atomics or
+ * ordered by the barrier. */
+static void pair_wait(xkv_eigh_pair* pr) {
+  const int g = __atomic_load_n(&pr->gen, __ATOMIC_ACQUIRE);
+  if (__atomic_add_fetch(&pr->count, 1, __ATOMIC_ACQ_REL) == 2) {
+    __atomic_store_n(&pr->count, 0, __ATOMIC_RELAXED);
+    __atomic_store_n(&pr->gen, g + 1, __ATOMIC_RELEASE);
+    return;
+  }
+  for (int spins = 0; __atomic_load_n(&pr->gen, __ATOMIC_ACQUIRE) == g; ++spins) {
+    if (spins < 20000) _mm_pause();
+    else sched_yield();   /* the partner is not running: give it the core */
+  }
+}
+
+/* Row passes of the reduction, over local rows [i0, i1) of their trailing block; a pass
+ * that forms a product adds its terms into pacc. */
+enum { JOB_DONE = 0, JOB_SYM, JOB_PRODUCT, JOB_FUSED };
+typedef struct {
+  int n;
+  const double* H;
+  double* A;
+  const double* V;
+  const double* w;
+  xkv_eigh_pair* pr;   /* NULL: one thread */
+  double* p1;          /* the worker's product terms */
+  double* cb;          /* a fused pass's first updated column, contiguous */
+} team;
+
+/* the rows a job covers: all n for the symmetrisation, else the trailing block's size */
+static int job_rows(int job, int n, int k) { return job == JOB_SYM ? n : job == JOB_PRODUCT ? n - k - 1 : n - k - 2; }
+
+static void job_pass(const team* t, int job, int k, int i0, int i1, double* pacc) {
+  const int n = t->n;
+  double* A = t->A;
+  if (job == JOB_SYM) {
+    /* the mean of the two triangles */
+    for (int i = i0; i < i1; ++i)
+      for (int j = 0; j < n; ++j) A[(size_t)i * n + j] = 0.5 * (t->H[(size_t)i * n + j] + t->H[(size_t)j * n + i]);
+  } else if (job == JOB_PRODUCT) {
+    /* pacc += A22 v from the lower triangle (rows and columns k+1..) */
+    const double* v = t->V + (size_t)k * n;
+    for (int i = i0; i < i1; ++i) {
+      const double* row = A + (size_t)(k + 1 + i) * n + k + 1;
+      const double vi = v[i];
+      double s = 0.0;
+      for (int j = 0; j < i; ++j) {
+        s += row[j] * v[j];
+        pacc[j] += row[j] * vi;
+      }
+      pacc[i] += s + row[i] * vi;
+    }
+  } else {
+    /* the update of step k on local rows/columns 1..m-1 of its A22 (rows/columns 0..m2-1 of
+     * the next A22) fused with the product by the next Householder vector v2; the updated
+     * first column of the next A22 is copied out to cb */
+    const double* v = t->V + (size_t)k * n;
+    const double* v2 = v + n;
+    const double* w = t->w;
+    const double* vj = v + 1;
+    const double* wj = w + 1;
+    for (int i = i0; i < i1; ++i) {
+      double* row = A + (size_t)(k + 2 + i) * n + k + 2;
+      const double vi = v[i + 1], wi = w[i + 1], ui = v2[i];
+      /* four-wide: a = row - vi w - wi v, then s += a v2 (four partial sums) and pacc += ui a */
+      const __m256d vvi = _mm256_set1_pd(vi), vwi = _mm256_set1_pd(wi), vui = _mm256_set1_pd(ui);
+      __m256d s4 = _mm256_setzero_pd();
+      int j = 0;
+      for (; j + 4 <= i; j += 4) {
+        __m256d a = _mm256_fnmadd_pd(vvi, _mm256_loadu_pd(wj + j), _mm256_loadu_pd(row + j));
+        a = _mm256_fnmadd_pd(vwi, _mm256_loadu_pd(vj + j), a);
+        _mm256_storeu_pd(row + j, a);
+        s4 = _mm256_fmadd_pd(a, _mm256_loadu_pd(v2 + j), s4);
+        _mm256_storeu_pd(pacc + j, _mm256_fmadd_pd(a, vui, _mm256_loadu_pd(pacc + j)));
+      }
+      double s = 0.0;
+      for (; j < i; ++j) {
+        const double a = row[j] - vi * wj[j] - wi * vj[j];
+        row[j] = a;
+        s += a * v2[j];
+        pacc[j] += a * ui;
+      }
+      {
+        double part[4];
+        _mm256_storeu_pd(part, s4);
+        s += (part[0] + part[1]) + (part[2] + part[3]);
+      }
+      const double a = row[i] - vi * wj[i] - wi * vj[i];
+      row[i] = a;
+      pacc[i] += s + a * ui;
+      t->cb[i] = row[0];
+    }
+  }
+}
+
+/* The leader runs a job: alone over all its rows, or with the worker taking the rows from
+ * `split` on (row i of a triangle costs ~i, so the split at 1/sqrt(2) halves the work), their
+ * product terms then added into p.  p[0, rows) is zero on entry for a product. */
+static void run_job(const team* t, int job, int k, double* p) {
+  const int rows = job_rows(job, t->n, k);
+  if (!t->pr) {
+    job_pass(t, job, k, 0, rows, p);
+    return;
+  }
+  const int split = job == JOB_SYM ? rows / 2 : (int)(rows * 0.7071067811865476);
+  t->pr->job = job;
+  t->pr->k = k;
+  t->pr->split = split;
+  pair_wait(t->pr);   /* the job is published */
+  job_pass(t, job, k, 0, split, p);
+  pair_wait(t->pr);   /* both halves done */
+  if (job != JOB_SYM)
+    for (int i = 0; i < rows; ++i) p[i] += t->p1[i];
+}
+
+/* The worker's side of a paired reduction: jobs until JOB_DONE. */
+static void worker_loop(const team* t) {
+  for (;;) {
+    pair_wait(t->pr);
+    const int job = t->pr->job, k = t->pr->k, split = t->pr->split;
+    if (job == JOB_DONE) return;
+    const int rows = job_rows(job, t->n, k);
+    if (job != JOB_SYM) memset(t->p1, 0, (size_t)rows * sizeof(double));
+    job_pass(t, job, k, split, rows, t->p1);
+    pair_wait(t->pr);
+  }
+}
+
 /* Reduce symmetric A (n x n, row-major, lower triangle used and overwritten) to
  * tridiagonal (d, e), A_in = Q T Q^T with Q = P_0 P_1 ... P_{n-3}, P_k = I - beta_k v_k v_k^T
  * acting on rows and columns k+1..n-1.  On return row k of V (n x n) holds v_k (v_k[0] = 1,
- * component i for row k+1+i) and beta[k] its factor.  p, w and col are n doubles of scratch.
+ * component i for row k+1+i) and beta[k] its factor.  p, w and u are n doubles of scratch,
+ * t->cb too.
  *
  * Step k takes the Householder vector v of column k below the diagonal and forms
  * p = beta A22 v, w = p - (beta/2)(p.v) v; A22 <- A22 - v w^T - w v^T.  Only the lower
  * triangle of A22 is kept, and the update of step k is fused with the product of
  * step k + 1: once column k + 1 of the updated matrix is known (its Householder vector
  * v' follows), one pass over the rest of the lower triangle updates each element and
- * adds its contributions a_ij v'_j to p'_i and a_ij v'_i to p'_j. */
-static void tridiagonalize(int n, double* A, double* d, double* e, double* V, double* beta, double* p, double* w,
-                           double* col) {
-  /* Step 0's product: p = A22 v over the (not yet updated) lower triangle. */
-  int have_p = 0;
+ * adds its contributions a_ij v'_j to p'_i and a_ij v'_i to p'_j.  That pass also copies the
+ * first column of what it updated to cb, so the next step takes its column (and the one
+ * after it) from contiguous memory: the column of A is not read again.  The O(n^2) passes
+ * are jobs (run_job), shared with a worker thread when t->pr is set; the O(n) work of a step
+ * stays in the calling thread. */
+static void tridiagonalize(const team* t, double* d, double* e, double* V, double* beta, double* p, double* w,
+                           double* u) {
+  const int n = t->n;
+  double* A = t->A;
+  double* cb = t->cb;
+  /* have_next: v_k, beta[k], d[k], e[k], p = A22 v_k and cb = column k+1 from k+1 down are
+   * known from the step before */
+  int have_next = 0;
   for (int k = 0; k + 2 < n; ++k) {
     const int m = n - k - 1;                 /* trailing size */
     double* v = V + (size_t)k * n;
-    double mu;
-    for (int i = 0; i < m; ++i) col[i] = A[(size_t)(k + 1 + i) * n + k];   /* column k below the diagonal */
-    house(m, col, v, &beta[k], &mu);
-    d[k] = A[(size_t)k * n + k];
-    e[k] = mu;
-    const double b = beta[k];
-    if (!have_p) {
-      /* p = A22 v from the lower triangle (rows k+1.., columns k+1..) */
+    if (!have_next) {
+      double mu;
+      for (int i = 0; i < m; ++i) u[i] = A[(size_t)(k + 1 + i) * n + k];   /* column k below the diagonal */
+      house(m, u, v, &beta[k], &mu);
+      d[k] = A[(size_t)k * n + k];
+      e[k] = mu;
+      if (beta[k] == 0.0) continue;
       for (int i = 0; i < m; ++i) p[i] = 0.0;
-      for (int i = 0; i < m; ++i) {
-        const double* row = A + (size_t)(k + 1 + i) * n + k + 1;
-        const double vi = v[i];
-        double s = 0.0;
-        for (int j = 0; j < i; ++j) {
-          s += row[j] * v[j];
-          p[j] += row[j] * vi;
-        }
-        p[i] += s + row[i] * vi;
-      }
+      run_job(t, JOB_PRODUCT, k, p);
+      for (int i = 0; i < m; ++i) cb[i] = A[(size_t)(k + 1 + i) * n + k + 1];
     }
-    have_p = 0;
+    have_next = 0;
+    const double b = beta[k];
     if (b == 0.0) continue;
     /* w = beta p - (beta/2)(beta p . v) v */
     for (int i = 0; i < m; ++i) p[i] *= b;
@@ -96,50 +228,14 @@ static void tridiagonalize(int n, double* A, double* d, double* e, double* V, do
        * Householder vector, then the fused update + product over local rows 1.. */
       const int m2 = m - 1;
       double* v2 = V + (size_t)(k + 1) * n;
-      for (int i = 0; i < m; ++i) {
-        double* a0 = A + (size_t)(k + 1 + i) * n + k + 1;
-        *a0 -= v[i] * w[0] + w[i] * v[0];
-      }
-      for (int i = 0; i < m2; ++i) col[i] = A[(size_t)(k + 2 + i) * n + k + 1];
+      for (int i = 0; i < m; ++i) u[i] = cb[i] - (v[i] * w[0] + w[i] * v[0]);
       double mu2;
-      house(m2, col, v2, &beta[k + 1], &mu2);
-      /* local rows/columns 1..m-1 of A22 are rows/columns 0..m2-1 of the next A22 */
+      house(m2, u + 1, v2, &beta[k + 1], &mu2);
+      d[k + 1] = u[0];
+      e[k + 1] = mu2;
       for (int i = 0; i < m2; ++i) p[i] = 0.0;
-      for (int i = 0; i < m2; ++i) {
-        double* row = A + (size_t)(k + 2 + i) * n + k + 2;
-        const double vi = v[i + 1], wi = w[i + 1], ui = v2[i];
-        const double* vj = v + 1;
-        const double* wj = w + 1;
-        /* four-wide: a = row - vi w - wi v, then s += a v2 (four partial sums) and p += ui a */
-        const __m256d vvi = _mm256_set1_pd(vi), vwi = _mm256_set1_pd(wi), vui = _mm256_set1_pd(ui);
-        __m256d s4 = _mm256_setzero_pd();
-        int j = 0;
-        for (; j + 4 <= i; j += 4) {
-          __m256d a = _mm256_fnmadd_pd(vvi, _mm256_loadu_pd(wj + j), _mm256_loadu_pd(row + j));
-          a = _mm256_fnmadd_pd(vwi, _mm256_loadu_pd(vj + j), a);
-          _mm256_storeu_pd(row + j, a);
-          s4 = _mm256_fmadd_pd(a, _mm256_loadu_pd(v2 + j), s4);
-          _mm256_storeu_pd(p + j, _mm256_fmadd_pd(a, vui, _mm256_loadu_pd(p + j)));
-        }
-        double s = 0.0;
-        for (; j < i; ++j) {
-          const double a = row[j] - vi * wj[j] - wi * vj[j];
-          row[j] = a;
-          s += a * v2[j];
-          p[j] += a * ui;
-        }
-        {
-          double part[4];
-          _mm256_storeu_pd(part, s4);
-          s += (part[0] + part[1]) + (part[2] + part[3]);
-        }
-        const double a = row[i] - vi * wj[i] - wi * vj[i];
-        row[i] = a;
-        p[i] += s + a * ui;
-      }
-      have_p = 1;
-      /* the next step recomputes its column k+2.. from A (already updated above) and
-       * reuses v2 and beta[k + 1] through V and beta (house is deterministic) */
+      run_job(t, JOB_FUSED, k, p);
+      have_next = 1;
     } else {
       for (int i = 0; i < m; ++i) {
         double* row = A + (size_t)(k + 1 + i) * n + k + 1;
@@ -153,7 +249,6 @@ static void tridiagonalize(int n, double* A, double* d, double* e, double* V, do
     e[n - 2] = A[(size_t)(n - 1) * n + n - 2];
   }
   d[n - 1] = A[(size_t)(n - 1) * n + n - 1];
-
 }
 
 /* Rotation t of the log acts on rows/columns k[t], k[t] + 1 of the eigenvector matrix,
@@ -521,42 +616,55 @@ static int cmp_desc(const void* a, const void* b) {
   return x->idx - y->idx;
 }
 
+/* The value phase's state in sc->buf: A (n x n), V (n x n), then vectors of n doubles at
+ * slot(buf, n, S_*); the eigenvalue order (keyed) takes two slots. */
+enum { S_BETA, S_D, S_E, S_P, S_W, S_COL, S_IDX, S_CB = S_IDX + 2, S_SLOTS };
+static double* slot(double* buf, int n, int s) { return buf + 2 * (size_t)n * n + (size_t)s * n; }
+
 /* Value phase: all n eigenvalues of symmetric H, descending, into w; the reflectors, the
  * rotation log and the order of the eigenvalues stay in sc for xkv_eigh_vectors.  sc keeps its
  * memory for the next call (a zero-filled struct on first use; xkv_eigh_scratch_release frees
- * it): repeated solves in several threads then neither map nor fault pages.  Returns 0 on
- * success, -1 on allocation failure, -2 if the QR iteration did not converge. */
-__attribute__((visibility("hidden"))) int xkv_eigh_values(int n, const double* H, int nvec, double* w,
-                                                           xkv_eigh_scratch* sc) {
-  if (n <= 0 || nvec <= 0 || nvec > n) return -3;
-  /* A n^2, V n^2, beta, d, e, p, w, col n each, idx 2n (keyed) */
-  const size_t need = 2 * (size_t)n * n + 8 * (size_t)n;
+ * it): repeated solves in several threads then neither map nor fault pages.  With pr set the
+ * calling thread leads a pair whose worker runs worker_side; the worker's product terms are in
+ * helper->buf, read only after the start barrier.  Returns 0 on success, -1 on
+ * allocation failure, -2 if the QR iteration did not converge. */
+static int values_impl(int n, const double* H, int nvec, double* w, xkv_eigh_scratch* sc, xkv_eigh_pair* pr,
+                       const xkv_eigh_scratch* helper) {
+  const size_t need = 2 * (size_t)n * n + S_SLOTS * (size_t)n;
   if (sc->cap < need) {
     free(sc->buf);
     sc->buf = (double*)malloc(need * sizeof(double));
     sc->cap = sc->buf ? need : 0;
-    if (!sc->buf) return -1;
   }
+  if (pr) {
+    /* both threads learn whether either lacks memory before any shared work */
+    if (!sc->buf) __atomic_store_n(&pr->fail, 1, __ATOMIC_RELAXED);
+    pair_wait(pr);
+    if (__atomic_load_n(&pr->fail, __ATOMIC_RELAXED)) return -1;
+  }
+  if (!sc->buf) return -1;
   sc->n = n;
   sc->nvec = nvec;
   double* A = sc->buf;
   double* V = A + (size_t)n * n;
-  double* beta = V + (size_t)n * n;
-  double* d = beta + n;
-  double* e = d + n;
-  double* tp = e + n;
-  double* tw = tp + n;
-  double* tcol = tw + n;
-  keyed* idx = (keyed*)(tcol + n);
+  double* beta = slot(sc->buf, n, S_BETA);
+  double* d = slot(sc->buf, n, S_D);
+  double* e = slot(sc->buf, n, S_E);
+  double* tp = slot(sc->buf, n, S_P);
+  double* tw = slot(sc->buf, n, S_W);
+  double* tcol = slot(sc->buf, n, S_COL);
+  keyed* idx = (keyed*)slot(sc->buf, n, S_IDX);
   memset(beta, 0, (size_t)n * sizeof(double));
   memset(e, 0, (size_t)n * sizeof(double));
   rotlog* log = &sc->log;
   log->n = 0;
-  /* Symmetrise: use the mean of the two triangles. */
-  for (int i = 0; i < n; ++i)
-    for (int j = 0; j < n; ++j)
-      A[(size_t)i * n + j] = 0.5 * (H[(size_t)i * n + j] + H[(size_t)j * n + i]);
-  tridiagonalize(n, A, d, e, V, beta, tp, tw, tcol);
+  const team t = {n, H, A, V, tw, pr, pr ? helper->buf : NULL, slot(sc->buf, n, S_CB)};
+  run_job(&t, JOB_SYM, 0, NULL);
+  tridiagonalize(&t, d, e, V, beta, tp, tw, tcol);
+  if (pr) {
+    pr->job = JOB_DONE;
+    pair_wait(pr);   /* the worker leaves */
+  }
 
   {
     const double eps = 2.220446049250313e-16;
@@ -585,6 +693,40 @@ __attribute__((visibility("hidden"))) int xkv_eigh_values(int n, const double* H
   return 0;
 }
 
+__attribute__((visibility("hidden"))) int xkv_eigh_values(int n, const double* H, int nvec, double* w,
+                                                           xkv_eigh_scratch* sc) {
+  if (n <= 0 || nvec <= 0 || nvec > n) return -3;
+  return values_impl(n, H, nvec, w, sc, NULL, NULL);
+}
+
+/* The worker of a pair: its product terms in helper->buf, the shared state in the leader's sc
+ * (read only after the start barrier, once the leader has its memory). */
+static int worker_side(int n, const double* H, const xkv_eigh_scratch* sc, xkv_eigh_scratch* helper,
+                       xkv_eigh_pair* pr, double* refl) {
+  if (helper->cap < (size_t)n) {
+    free(helper->buf);
+    helper->buf = (double*)malloc((size_t)n * sizeof(double));
+    helper->cap = helper->buf ? (size_t)n : 0;
+  }
+  if (!helper->buf) __atomic_store_n(&pr->fail, 1, __ATOMIC_RELAXED);
+  pair_wait(pr);
+  if (__atomic_load_n(&pr->fail, __ATOMIC_RELAXED)) return -1;
+  double* A = sc->buf;
+  const team t = {n, H, A, A + (size_t)n * n, slot(sc->buf, n, S_W), pr, helper->buf, slot(sc->buf, n, S_CB)};
+  worker_loop(&t);
+  /* the reflectors are final once the reduction is; the leader's QR iteration leaves them */
+  if (refl) xkv_eigh_pack_reflectors(sc, refl);
+  return 0;
+}
+
+__attribute__((visibility("hidden"))) int xkv_eigh_values_pair(int n, const double* H, int nvec, double* w,
+                                                                xkv_eigh_scratch* sc, xkv_eigh_scratch* helper,
+                                                                xkv_eigh_pair* pr, int tid, double* refl) {
+  if (n <= 0 || nvec <= 0 || nvec > n) return -3;
+  if (tid) return worker_side(n, H, sc, helper, pr, refl);
+  return values_impl(n, H, nvec, w, sc, pr, helper);
+}
+
 /* Vector phase: Z[:, j0:j1] = Q G_1 ... G_N E, E the unit vectors of the wanted positions: the
  * rotations on E (last first), then the reflectors, in `work`'s memory, then one copy into Z
  * (which may be pinned host memory, slower to work in). */
@@ -593,8 +735,8 @@ __attribute__((visibility("hidden"))) int xkv_eigh_vectors(const xkv_eigh_scratc
   const int n = state->n, nvec = state->nvec, nc = j1 - j0;
   if (nc <= 0) return 0;
   const double* V = state->buf + (size_t)n * n;
-  const double* beta = V + (size_t)n * n;
-  const keyed* idx = (const keyed*)(beta + 6 * (size_t)n);
+  const double* beta = slot(state->buf, n, S_BETA);
+  const keyed* idx = (const keyed*)slot(state->buf, n, S_IDX);
   const size_t need = (size_t)n * RC + reflector_scratch(n, nc) + (size_t)n * nc;
   if (work->vcap < need) {
     free(work->vbuf);
@@ -620,6 +762,96 @@ __attribute__((visibility("hidden"))) int xkv_eigh_desc_scratch(int n, const dou
   const int rc = xkv_eigh_values(n, H, nvec, w, sc);
   if (rc) return rc;
   return xkv_eigh_vectors(sc, 0, nvec, Z, sc);
+}
+
+/* The vector phase's inputs for a device, which forms column j of Z as the unit vector at
+ * pos[j], then applies the logged rotations last first, a run at a time (a run is one QR sweep:
+ * rotations t_lo..t_hi, rotation t on rows k_top - (t_hi - t) and the one below), then the
+ * reflectors as blocks of XKV_EIGH_NBG, last block first, each as I - Y T Y^T.  A QR sweep
+ * longer than maxlen rotations is cut into runs of at most maxlen (any cut gives the same
+ * product). */
+__attribute__((visibility("hidden"))) int xkv_eigh_runs(const xkv_eigh_scratch* st, int maxlen) {
+  const rotlog* L = &st->log;
+  int runs = 0;
+  long t0 = 0;
+  for (long t = 0; t < L->n; ++t)
+    if (t == 0 || L->k[t] != L->k[t - 1] + 1 || t - t0 == maxlen) {
+      ++runs;
+      t0 = t;
+    }
+  return runs;
+}
+
+__attribute__((visibility("hidden"))) void xkv_eigh_pack_log(const xkv_eigh_scratch* st, int maxlen, int* runs,
+                                                              double* cs) {
+  const rotlog* L = &st->log;
+  int q = -1;
+  long t0 = 0;
+  for (long t = 0; t < L->n; ++t) {
+    if (t == 0 || L->k[t] != L->k[t - 1] + 1 || t - t0 == maxlen) {
+      t0 = t;
+      ++q;
+      runs[4 * q] = (int)t;
+      runs[4 * q + 3] = 0;
+    }
+    runs[4 * q + 1] = (int)t;        /* t_hi so far */
+    runs[4 * q + 2] = L->k[t];       /* k_top: the row of rotation t_hi */
+    cs[2 * t] = L->c[t];
+    cs[2 * t + 1] = L->s[t];
+  }
+}
+
+__attribute__((visibility("hidden"))) size_t xkv_eigh_refl_doubles(int n) {
+  const int nref = n - 2;
+  if (nref <= 0) return 0;
+  const int nblk = (nref + XKV_EIGH_NBG - 1) / XKV_EIGH_NBG;
+  size_t y = 0;
+  for (int b = 0; b < nblk; ++b) y += (size_t)(n - XKV_EIGH_NBG * b - 1) * XKV_EIGH_NBG;
+  return y + (size_t)nblk * XKV_EIGH_NBG * XKV_EIGH_NBG;
+}
+
+/* Block b holds reflectors kb = NBG b .. kb + nb - 1 acting on rows r0 = kb + 1 .. n - 1:
+ * Y_b (M = n - r0 rows of NBG, row-major; column c is reflector kb + c from its row c on, zero
+ * above it and for c >= nb), the blocks one after another, then every T_b (NBG x NBG,
+ * row-major, upper triangular) with P_kb ... P_{kb+nb-1} = I - Y_b T_b Y_b^T:
+ * T[c][c] = beta_c, T[0:c, c] = -beta_c T[0:c, 0:c] (Y_b^T Y_b)[0:c, c]. */
+__attribute__((visibility("hidden"))) void xkv_eigh_pack_reflectors(const xkv_eigh_scratch* st, double* out) {
+  enum { NBG = XKV_EIGH_NBG };
+  const int n = st->n, nref = n - 2;
+  if (nref <= 0) return;
+  const double* V = st->buf + (size_t)n * n;
+  const double* beta = slot(st->buf, n, S_BETA);
+  const int nblk = (nref + NBG - 1) / NBG;
+  double* T = out + (xkv_eigh_refl_doubles(n) - (size_t)nblk * NBG * NBG);
+  double* Y = out;
+  for (int b = 0; b < nblk; ++b) {
+    const int kb = NBG * b, nb = nref - kb < NBG ? nref - kb : NBG, M = n - kb - 1;
+    double G[NBG][NBG];
+    memset(G, 0, sizeof(G));
+    for (int i = 0; i < M; ++i) {
+      double* y = Y + (size_t)i * NBG;
+      for (int c = 0; c < NBG; ++c) y[c] = (c < nb && i >= c) ? V[(size_t)(kb + c) * n + (i - c)] : 0.0;
+      for (int a = 0; a < NBG; ++a)
+        for (int c = a + 1; c < NBG; ++c) G[a][c] += y[a] * y[c];
+    }
+    double* Tb = T + (size_t)b * NBG * NBG;
+    memset(Tb, 0, sizeof(double) * NBG * NBG);
+    for (int c = 0; c < nb; ++c) {
+      const double bc = beta[kb + c];
+      for (int a = 0; a < c; ++a) {
+        double t = 0.0;
+        for (int b2 = a; b2 < c; ++b2) t += Tb[a * NBG + b2] * G[b2][c];
+        Tb[a * NBG + c] = -bc * t;
+      }
+      Tb[c * NBG + c] = bc;
+    }
+    Y += (size_t)M * NBG;
+  }
+}
+
+__attribute__((visibility("hidden"))) void xkv_eigh_positions(const xkv_eigh_scratch* st, int* pos) {
+  const keyed* idx = (const keyed*)slot(st->buf, st->n, S_IDX);
+  for (int j = 0; j < st->nvec; ++j) pos[j] = idx[j].idx;
 }
 
 __attribute__((visibility("hidden"))) void xkv_eigh_scratch_release(xkv_eigh_scratch* sc) {

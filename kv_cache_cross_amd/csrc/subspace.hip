@@ -2,7 +2,10 @@
 //   * factor of a diagonal block of W = Y^T Y for the blocked Cholesky of
 //     CholeskyQR (Q = Y R^-1 with W = R^T R), with the block's inverse;
 //   * the Gaussian start block;
-//   * conversion of V_r to the stored Bt = V_r and its transpose.
+//   * conversion of V_r to the stored Bt = V_r and its transpose;
+//   * the plane rotations of the Rayleigh-Ritz eigensolve's QR iteration applied to the
+//     wanted unit vectors (the first half of its vector phase; the reflectors follow as
+//     GEMMs).
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 
@@ -193,6 +196,158 @@ __global__ __launch_bounds__(256) void vr_outputs_kernel(VrArgs a) {
   }
 }
 
+
+// One lane per wanted column j of one side (64 columns per workgroup): column j starts as the
+// unit vector at pos[j]; the logged rotations are then applied last first, a run at a time.
+// A run is rotations lo..hi of the log, rotation t acting on rows k = ktop - (hi - t) and
+// k + 1 as [c -s; s c] (new row k+1 = s x + c y, new row k = c x - s y for x, y the old rows
+// k, k+1).  Taken last first a run climbs the rows: the row the next rotation shares is
+// carried in a register, so each rotation loads one row and stores one.
+//
+// The columns are worked on in a scratch copy laid out per workgroup as rows of its 64 lanes
+// (512 bytes a row, after kPad rows of padding), through a buffer resource: a chunk's rows are
+// then a scalar base plus immediate offsets, so a rotation costs its four float64 operations,
+// one load, one store and one LDS read of its (c, s) pair.  A run's pairs are staged in LDS
+// (at most kRunCap, after kPad entries of padding).  The run goes in chunks of CH rotations,
+// the rows and pairs of the next chunk loaded while the current one is applied (two register
+// sets in turn), the last L mod CH rotations as a partial chunk.  Within a run a chunk's rows
+// are not written before they are read; loads past the run's end land in the padding (at most
+// 2 CH - 1 rows or pairs before the first) and feed nothing.  At the end the scratch rows are
+// copied to Z (n x r).  Lanes past r work on column r - 1 exactly as its own lane does and
+// store nothing to Z.
+constexpr int kRunCap = 1024;
+constexpr int CH = 16;
+constexpr int kPad = 2 * CH;
+constexpr unsigned kRowB = 64 * 8;   // bytes per scratch row
+
+using zrsrc = __amdgpu_buffer_rsrc_t;
+typedef unsigned zbits __attribute__((__vector_size__(2 * sizeof(unsigned))));
+__device__ __forceinline__ double zload(zrsrc z, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(z, voff, soff, 0));
+}
+__device__ __forceinline__ void zstore(zrsrc z, unsigned voff, unsigned soff, double v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(zbits, v), z, voff, soff, 0);
+}
+// byte offset of scratch row `row` (row >= -kPad)
+__device__ __forceinline__ unsigned zrow(int row) { return (unsigned)(row + kPad) * kRowB; }
+
+struct RotChunk {
+  double x[CH];
+  double2 g[CH];
+};
+
+// Rows k - u and pairs i - u, u < CH: two row bases (k - 7, k - 15) with immediate offsets.
+__device__ __forceinline__ void rot_load_x(RotChunk& b, zrsrc z, unsigned loff, int k) {
+  const unsigned s0 = zrow(k - 7), s1 = zrow(k - 15);
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+    b.x[u] = u < 8 ? zload(z, loff + (7 - u) * kRowB, s0) : zload(z, loff + (15 - u) * kRowB, s1);
+}
+__device__ __forceinline__ void rot_load_g(RotChunk& b, int i, const double2* cs_s) {
+  const double2* gp = cs_s + kPad + i - (CH - 1);
+#pragma unroll
+  for (int u = 0; u < CH; ++u) b.g[u] = gp[CH - 1 - u];
+}
+// A run's (c, s) pairs, lane l taking pairs l + 64 m (past the run's end: its last pair).
+constexpr int PF = kRunCap / 64;
+struct PairFetch {
+  double c[PF], s[PF];
+};
+__device__ __forceinline__ void rot_fetch_pairs(PairFetch& pf, int4 R, const double2* cs, int lane) {
+  const double2* csr = cs + R.x;
+  const int last = R.y - R.x;
+#pragma unroll
+  for (int m = 0; m < PF; ++m) {
+    const double2 g = csr[min(lane + 64 * m, last)];
+    pf.c[m] = g.x;
+    pf.s[m] = g.y;
+  }
+}
+
+__device__ __forceinline__ void rot_load(RotChunk& b, zrsrc z, unsigned loff, int k, int i, const double2* cs_s) {
+  rot_load_x(b, z, loff, k);
+  rot_load_g(b, i, cs_s);
+}
+
+// The chunk's first cnt rotations (cnt uniform; CH for a whole chunk), storing rows k - u + 1;
+// k and i step past the chunk.
+template <bool WHOLE>
+__device__ __forceinline__ void rot_apply(const RotChunk& b, zrsrc z, unsigned loff, int& k, int& i, int cnt,
+                                          double& y) {
+  const unsigned s0 = zrow(k - 6), s1 = zrow(k - 14);
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    if (WHOLE || u < cnt) {
+      const double cx = b.g[u].x * b.x[u];
+      const double v = fma(b.g[u].y, b.x[u], b.g[u].x * y);
+      if (u < 8) zstore(z, loff + (7 - u) * kRowB, s0, v);
+      else zstore(z, loff + (15 - u) * kRowB, s1, v);
+      y = fma(-b.g[u].y, y, cx);
+    }
+  }
+  k -= CH;
+  i -= CH;
+}
+
+__global__ __launch_bounds__(64) void ritz_rotate_kernel(const int4* __restrict__ runs,
+                                                         const double2* __restrict__ cs,
+                                                         const long long* __restrict__ meta,
+                                                         const int* __restrict__ pos, int n, int r,
+                                                         double* __restrict__ Z, long zs,
+                                                         double* __restrict__ scr, long scr_s) {
+  __shared__ double2 cs_s[kPad + kRunCap];
+  const int s = blockIdx.y, lane = threadIdx.x;
+  const int j = (int)blockIdx.x * 64 + lane;
+  const int jc = min(j, r - 1);
+  const unsigned loff = 8u * (unsigned)lane;
+  // this workgroup's scratch: kPad + n rows of 64 lanes
+  const zrsrc z = __builtin_amdgcn_make_buffer_rsrc(scr + s * scr_s + (long)blockIdx.x * (kPad + n) * 64, 0,
+                                                    (int)((unsigned)(kPad + n) * kRowB), 0x00020000);
+  const int pj = pos[(long)s * r + jc];
+  for (int i = 0; i < n; ++i) zstore(z, loff, zrow(i), i == pj ? 1.0 : 0.0);
+  const long long run0 = meta[4 * s], nrun = meta[4 * s + 1], cs0 = meta[4 * s + 2];
+  // A run's pairs are fetched into registers (lane l: pairs l + 64 m, the run's last pair past
+  // its end) during the run before it, so that its start waits only for LDS stores and its
+  // first rows.
+  PairFetch pf;
+  if (nrun > 0) rot_fetch_pairs(pf, runs[run0 + nrun - 1], cs + cs0, lane);
+  for (long long q = nrun - 1; q >= 0; --q) {
+    const int4 R = runs[run0 + q];
+    const int L = R.y - R.x + 1, ktop = R.z;
+    double y = zload(z, loff, zrow(ktop + 1));
+    RotChunk A, B;
+    rot_load_x(A, z, loff, ktop);
+    __syncthreads();   // the previous run's pairs are read
+#pragma unroll
+    for (int m = 0; m < PF; ++m) cs_s[kPad + lane + 64 * m] = make_double2(pf.c[m], pf.s[m]);
+    __syncthreads();
+    if (q > 0) rot_fetch_pairs(pf, runs[run0 + q - 1], cs + cs0, lane);
+    int k = ktop, i = L - 1;
+    const int nf = L / CH, rem = L % CH;   // whole chunks, then a partial one
+    rot_load_g(A, i, cs_s);
+    int c = 0;
+    for (; c + 1 < nf; c += 2) {
+      rot_load(B, z, loff, k - CH, i - CH, cs_s);
+      rot_apply<true>(A, z, loff, k, i, CH, y);
+      rot_load(A, z, loff, k - CH, i - CH, cs_s);
+      rot_apply<true>(B, z, loff, k, i, CH, y);
+    }
+    if (c < nf) {   // A holds the last whole chunk
+      rot_load(B, z, loff, k - CH, i - CH, cs_s);
+      rot_apply<true>(A, z, loff, k, i, CH, y);
+      if (rem) rot_apply<false>(B, z, loff, k, i, rem, y);
+    } else if (rem) {   // A holds the partial chunk
+      rot_apply<false>(A, z, loff, k, i, rem, y);
+    }
+    // the run's lowest row, ktop - L + 1, takes the carried row
+    zstore(z, loff, zrow(ktop - L + 1), y);
+  }
+  if (j < r) {
+    double* zc = Z + s * zs + j;
+    for (int i = 0; i < n; ++i) zc[(long)i * r] = zload(z, loff, zrow(i));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_potrf_diag(const double* W, long ldw, long sW, double* L, long ldl, long sL,
@@ -254,5 +409,19 @@ hipError_t launch_vr_outputs(const double* Vr, long sVr, int n, int r, const Ptr
   hipLaunchKernelGGL(vr_outputs_kernel, dim3((r + 31) / 32, (n + 31) / 32, n_sides), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+
+hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const long long* meta, const int* pos, int n, int r,
+                              double* Z, long zs, double* scr, long scr_s, int n_sides, hipStream_t st) {
+  if (n_sides <= 0 || r <= 0) return hipSuccess;
+  if (n <= 0 || (long)(kPad + n) * kRowB > 0x7fffffffL) return hipErrorInvalidValue;   // 31-bit buffer range
+  if (scr_s < ritz_scratch_doubles(n, r)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ritz_rotate_kernel, dim3((r + 63) / 64, n_sides), dim3(64), 0, st, runs, cs, meta, pos, n, r, Z,
+                     zs, scr, scr_s);
+  return hipGetLastError();
+}
+
+int ritz_run_cap() { return kRunCap; }
+
+long ritz_scratch_doubles(int n, int r) { return (long)((r + 63) / 64) * (kPad + n) * 64; }
 
 }  // namespace xkv

@@ -132,7 +132,7 @@ def test_ctx_create_rejects_bad_device():
     assert rc in (L.XKV_EINVAL, L.XKV_EHIP)
 
 
-@pytest.mark.parametrize("n,nvec", [(1, 1), (2, 1), (7, 3), (60, 60), (200, 40)])
+@pytest.mark.parametrize("n,nvec", [(1, 1), (2, 1), (3, 2), (7, 3), (60, 60), (200, 40), (768, 512)])
 def test_host_eigh_matches_lapack(n, nvec):
     rng = np.random.default_rng(n)
     G = rng.standard_normal((n, n))
@@ -154,6 +154,26 @@ def test_host_eigh_clustered_and_degenerate():
     P = Z @ Z.T
     Pref = Q[:, :20] @ Q[:, :20].T
     np.testing.assert_allclose(P, Pref, atol=1e-9)
+
+
+@pytest.mark.parametrize("order", ["tridiagonal_first", "dense_first"])
+def test_host_eigh_skipped_reflectors(order):
+    # A tridiagonal block with positive off-diagonals has nothing to reduce: its columns
+    # are already e_1 below the subdiagonal, the reflector factor is 0 and the reduction
+    # skips those steps, then takes its next column from the matrix again.
+    rng = np.random.default_rng(5)
+    nt, nd = 20, 30
+    T = np.diag(rng.uniform(1, 2, nt)) + np.diag(rng.uniform(0.1, 0.5, nt - 1), 1)
+    T = T + np.triu(T, 1).T
+    G = rng.standard_normal((nd, nd))
+    D = G @ G.T / nd
+    Z0 = np.zeros((nt, nd))
+    H = np.block([[T, Z0], [Z0.T, D]]) if order == "tridiagonal_first" else np.block([[D, Z0.T], [Z0, T]])
+    w, Z = xk.host_eigh(H, 25)
+    ref_w = np.linalg.eigvalsh(H)[::-1][:25]
+    np.testing.assert_allclose(w, ref_w, rtol=1e-12, atol=1e-13 * ref_w[0])
+    np.testing.assert_allclose(Z.T @ Z, np.eye(25), atol=1e-12)
+    np.testing.assert_allclose(H @ Z, Z * w, atol=1e-11 * abs(ref_w[0]))
 
 
 def test_host_eigh_rejects_bad_args():

@@ -547,9 +547,11 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   // large enough to pay for a barrier per pass; all on at most ctx->host_threads threads.
   // The vector phase runs on the device (post_work): each side's rotation log is packed here
   // into the half's pinned staging, its reflector blocks and wanted positions into ctx->pin.
-  const int run_cap = ritz_run_cap();
+  const RitzGrouping rg = ritz_grouping();
+  const int run_cap = rg.run_cap;
   std::vector<long long> meta(4 * (size_t)S, 0);
   size_t log_bytes[2] = {0, 0};
+  long long runs_total[2] = {0, 0};
   auto run_threads = [&](int nthr, int ntask, auto&& task) {
     if (nthr <= 1) {
       for (int t = 0; t < ntask; ++t) task(t);
@@ -595,17 +597,19 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     }
     for (int i = 0; i < hf.cnt; ++i)
       if (erc[i]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + i, erc[i]);
-    // The half's log staging: meta (4 per side) | runs (4 ints each) | (c, s) pairs.
+    // The half's log staging: meta (4 per side: first run, first pair, first group, groups) |
+    // runs (4 ints each) | groups (2 ints each, room for one per run) | (c, s) pairs.
     long long runs_tot = 0, rot_tot = 0;
     for (int i = 0; i < hf.cnt; ++i) {
       const int s = hf.s0 + i;
       meta[4 * s] = runs_tot;
-      meta[4 * s + 1] = nruns[i];
-      meta[4 * s + 2] = rot_tot;
+      meta[4 * s + 1] = rot_tot;
+      meta[4 * s + 2] = runs_tot;
       runs_tot += nruns[i];
       rot_tot += ctx->eig_side[2 * s].log.n;
     }
-    const size_t meta_b = 32 * (size_t)hf.cnt, runs_b = 16 * (size_t)runs_tot, need = meta_b + runs_b + 16 * (size_t)rot_tot;
+    const size_t meta_b = 32 * (size_t)hf.cnt, runs_b = 16 * (size_t)runs_tot, grp_b = 8 * (size_t)runs_tot;
+    const size_t need = meta_b + runs_b + grp_b + 16 * (size_t)rot_tot;
     if (ctx->lpin_bytes[h] < need) {
       // no copy reads this half's staging now: each compression round ends with a stream
       // synchronisation, and an earlier call's copies are waited for on entry
@@ -617,13 +621,16 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       ctx->lpin_bytes[h] = want;
     }
     char* lp = (char*)ctx->lpin[h];
-    std::memcpy(lp, meta.data() + 4 * (size_t)hf.s0, meta_b);
     run_threads(std::min(hf.cnt, ctx->host_threads), hf.cnt, [&](int i) {
       const int s = hf.s0 + i;
-      xkv_eigh_pack_log(&ctx->eig_side[2 * s], run_cap, (int*)(lp + meta_b) + 4 * meta[4 * s],
-                        (double*)(lp + meta_b + runs_b) + 2 * meta[4 * s + 2]);
+      int* rs = (int*)(lp + meta_b) + 4 * meta[4 * s];
+      xkv_eigh_pack_log(&ctx->eig_side[2 * s], run_cap, rs, (double*)(lp + meta_b + runs_b + grp_b) + 2 * meta[4 * s + 1]);
+      meta[4 * s + 3] = xkv_eigh_group_runs(rs, nruns[i], rg.per_group, rg.spread, rg.max_steps,
+                                            (int*)(lp + meta_b + runs_b) + 2 * meta[4 * s + 2]);
     });
+    std::memcpy(lp, meta.data() + 4 * (size_t)hf.s0, meta_b);
     log_bytes[h] = need;
+    runs_total[h] = runs_tot;
     for (int i = 0; i < hf.cnt; ++i)
       std::memcpy(hTheta + (size_t)(hf.s0 + i) * r, evals[hf.s0 + i].data(), r * sizeof(double));
     return XKV_OK;
@@ -649,11 +656,10 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     XKV_HIP(hipMemcpyAsync(ctx->ldev[h], ctx->lpin[h], log_bytes[h], hipMemcpyHostToDevice, st));
     const char* ld = (const char*)ctx->ldev[h];
     const size_t meta_b = 32 * (size_t)hf.cnt;
-    const long long runs_tot = meta[4 * (hf.s0 + hf.cnt - 1)] + meta[4 * (hf.s0 + hf.cnt - 1) + 1] -
-                               meta[4 * hf.s0];
-    XKV_K(launch_ritz_rotate((const int4*)(ld + meta_b), (const double2*)(ld + meta_b + 16 * (size_t)runs_tot),
-                             (const long long*)ld, hf.w.pos, kb, r, hf.w.Z, (long)kb * r, hf.w.Zs,
-                             ritz_scratch_doubles(kb, r), hf.cnt, st));
+    const size_t runs_tot = (size_t)runs_total[h];
+    XKV_K(launch_ritz_rotate((const int4*)(ld + meta_b), (const double2*)(ld + meta_b + 24 * runs_tot),
+                             (const int2*)(ld + meta_b + 16 * runs_tot), (const long long*)ld, hf.w.pos, kb, r,
+                             hf.w.Z, (long)kb * r, hf.w.Zs, ritz_scratch_doubles(kb, r), hf.cnt, st));
     const int nref = kb - 2;
     const int nblk = nref > 0 ? (nref + NBG - 1) / NBG : 0;
     const size_t ytot = refl - (size_t)nblk * NBG * NBG;

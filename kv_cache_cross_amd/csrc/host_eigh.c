@@ -801,6 +801,39 @@ __attribute__((visibility("hidden"))) void xkv_eigh_pack_log(const xkv_eigh_scra
   }
 }
 
+/* Groups of up to B runs that a device applies together, in the order they are applied (the
+ * log's last run first): a group is runs q0, q0 - 1, ..., q0 - nb + 1, run b of it starting when
+ * the front row is its top row minus b and ending when the front is its lowest row minus b.  A
+ * run joins the group while every run's start and end stay within `spread` rows of the group's
+ * first start and last end and the group spans at most maxsteps fronts.  groups: (q0, nb) pairs;
+ * returns their number. */
+__attribute__((visibility("hidden"))) int xkv_eigh_group_runs(const int* runs, int nruns, int B, int spread,
+                                                               int maxsteps, int* groups) {
+  int ng = 0;
+  for (int q = nruns - 1; q >= 0;) {
+    int f0 = 0, f1 = 0, nb = 0;
+    int a[64], z[64];
+    for (; nb < B && nb < 64 && q - nb >= 0; ++nb) {
+      const int* R = runs + 4 * (q - nb);
+      const int ab = R[2] - nb, zb = R[2] - (R[1] - R[0]) - nb;   /* start and end fronts */
+      const int g0 = nb ? (ab > f0 ? ab : f0) : ab, g1 = nb ? (zb < f1 ? zb : f1) : zb;
+      int ok = g0 - g1 + 1 <= maxsteps;
+      a[nb] = ab;
+      z[nb] = zb;
+      for (int b = 0; b <= nb && ok; ++b) ok = g0 - a[b] <= spread && z[b] - g1 <= spread;
+      if (!ok) break;
+      f0 = g0;
+      f1 = g1;
+    }
+    if (nb == 0) nb = 1;   /* a lone run always fits */
+    groups[2 * ng] = q;
+    groups[2 * ng + 1] = nb;
+    ++ng;
+    q -= nb;
+  }
+  return ng;
+}
+
 __attribute__((visibility("hidden"))) size_t xkv_eigh_refl_doubles(int n) {
   const int nref = n - 2;
   if (nref <= 0) return 0;

@@ -68,6 +68,10 @@ void xkv_eigh_scratch_release(xkv_eigh_scratch* sc);
 enum { XKV_EIGH_NBG = 16 };
 int xkv_eigh_runs(const xkv_eigh_scratch* st, int maxlen);
 void xkv_eigh_pack_log(const xkv_eigh_scratch* st, int maxlen, int* runs, double* cs);
+/* Groups of up to B consecutive runs (in the order they are applied) whose starts and ends
+ * lie within `spread` rows of one another and that span at most maxsteps rows, as (first run,
+ * count) pairs, at most nruns of them; returns their number. */
+int xkv_eigh_group_runs(const int* runs, int nruns, int B, int spread, int maxsteps, int* groups);
 size_t xkv_eigh_refl_doubles(int n);
 void xkv_eigh_pack_reflectors(const xkv_eigh_scratch* st, double* out);
 void xkv_eigh_positions(const xkv_eigh_scratch* st, int* pos);

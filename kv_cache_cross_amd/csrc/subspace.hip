@@ -6,6 +6,7 @@
 //   * the plane rotations of the Rayleigh-Ritz eigensolve's QR iteration applied to the
 //     wanted unit vectors (the first half of its vector phase; the reflectors follow as
 //     GEMMs).
+#include <climits>
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 
@@ -202,23 +203,31 @@ __global__ __launch_bounds__(256) void vr_outputs_kernel(VrArgs a) {
 // A run is rotations lo..hi of the log, rotation t acting on rows k = ktop - (hi - t) and
 // k + 1 as [c -s; s c] (new row k+1 = s x + c y, new row k = c x - s y for x, y the old rows
 // k, k+1).  Taken last first a run climbs the rows: the row the next rotation shares is
-// carried in a register, so each rotation loads one row and stores one.
+// carried in a register, and row k + 1 is final for the run once rotation k is applied.
 //
-// The columns are worked on in a scratch copy laid out per workgroup as rows of its 64 lanes
-// (512 bytes a row, after kPad rows of padding), through a buffer resource: a chunk's rows are
-// then a scalar base plus immediate offsets, so a rotation costs its four float64 operations,
-// one load, one store and one LDS read of its (c, s) pair.  A run's pairs are staged in LDS
-// (at most kRunCap, after kPad entries of padding).  The run goes in chunks of CH rotations,
-// the rows and pairs of the next chunk loaded while the current one is applied (two register
-// sets in turn), the last L mod CH rotations as a partial chunk.  Within a run a chunk's rows
-// are not written before they are read; loads past the run's end land in the padding (at most
-// 2 CH - 1 rows or pairs before the first) and feed nothing.  At the end the scratch rows are
-// copied to Z (n x r).  Lanes past r work on column r - 1 exactly as its own lane does and
-// store nothing to Z.
-constexpr int kRunCap = 1024;
-constexpr int CH = 16;
-constexpr int kPad = 2 * CH;
-constexpr unsigned kRowB = 64 * 8;   // bytes per scratch row
+// Runs go in groups of up to kB, applied together as a wavefront: at each step a front row f
+// is loaded, run b applies its rotation at row f + b (it lags run b - 1 by one row, so both of
+// its rows already hold every earlier run's result), passing its finished row f + b + 1 to
+// run b + 1, and the last run's finished row f + kB is stored: one load and one store for kB
+// rotations.  Outside its rows a run applies the identity (c = 1, s = 0), which passes the
+// rows through; the fronts span the union of the group's runs.  Rows above and below the
+// fronts' reach are zero padding (the identity multiplies them by zero, so they must be
+// finite).
+//
+// The columns live in a scratch copy laid out per workgroup as rows of its 64 lanes (512
+// bytes a row) on a buffer resource: a chunk's rows are a scalar base plus immediate offsets.
+// A group's (c, s) pairs are staged in LDS, one slot per run in the order they are applied,
+// identities around them.  The fronts go in chunks of CH, the next chunk's rows loaded while
+// the current one is applied; a chunk's rows are not written before they are read (stores
+// trail the loads by kB + 1 rows).  At the end the scratch rows are copied to Z (n x r).
+// Lanes past r work on column r - 1 exactly as its own lane does and store nothing to Z.
+constexpr int kRunCap = 1024;                 // rotations per run (longer sweeps are cut)
+constexpr int kB = 4;                         // runs per group
+constexpr int CH = 8;                         // fronts per chunk
+constexpr int kSpread = 64;                   // rows a group's starts and ends may differ by
+constexpr int kSlot = kSpread + kRunCap + kSpread + 2 * CH;   // LDS pairs per run
+constexpr int kPadLo = 2 * CH + kB, kPadHi = kB;              // scratch rows before 0 and after n - 1
+constexpr unsigned kRowB = 64 * 8;            // bytes per scratch row
 
 using zrsrc = __amdgpu_buffer_rsrc_t;
 typedef unsigned zbits __attribute__((__vector_size__(2 * sizeof(unsigned))));
@@ -228,119 +237,142 @@ __device__ __forceinline__ double zload(zrsrc z, unsigned voff, unsigned soff) {
 __device__ __forceinline__ void zstore(zrsrc z, unsigned voff, unsigned soff, double v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(zbits, v), z, voff, soff, 0);
 }
-// byte offset of scratch row `row` (row >= -kPad)
-__device__ __forceinline__ unsigned zrow(int row) { return (unsigned)(row + kPad) * kRowB; }
+// byte offset of scratch row `row` (row >= -kPadLo)
+__device__ __forceinline__ unsigned zrow(int row) { return (unsigned)(row + kPadLo) * kRowB; }
 
-struct RotChunk {
-  double x[CH];
-  double2 g[CH];
-};
-
-// Rows k - u and pairs i - u, u < CH: two row bases (k - 7, k - 15) with immediate offsets.
-__device__ __forceinline__ void rot_load_x(RotChunk& b, zrsrc z, unsigned loff, int k) {
-  const unsigned s0 = zrow(k - 7), s1 = zrow(k - 15);
+// Rows f - u, u < CH, from one base with immediate offsets.
+__device__ __forceinline__ void front_load(double (&x)[CH], zrsrc z, unsigned loff, int f) {
+  const unsigned b = zrow(f - (CH - 1));
 #pragma unroll
-  for (int u = 0; u < CH; ++u)
-    b.x[u] = u < 8 ? zload(z, loff + (7 - u) * kRowB, s0) : zload(z, loff + (15 - u) * kRowB, s1);
-}
-__device__ __forceinline__ void rot_load_g(RotChunk& b, int i, const double2* cs_s) {
-  const double2* gp = cs_s + kPad + i - (CH - 1);
-#pragma unroll
-  for (int u = 0; u < CH; ++u) b.g[u] = gp[CH - 1 - u];
-}
-// A run's (c, s) pairs, lane l taking pairs l + 64 m (past the run's end: its last pair).
-constexpr int PF = kRunCap / 64;
-struct PairFetch {
-  double c[PF], s[PF];
-};
-__device__ __forceinline__ void rot_fetch_pairs(PairFetch& pf, int4 R, const double2* cs, int lane) {
-  const double2* csr = cs + R.x;
-  const int last = R.y - R.x;
-#pragma unroll
-  for (int m = 0; m < PF; ++m) {
-    const double2 g = csr[min(lane + 64 * m, last)];
-    pf.c[m] = g.x;
-    pf.s[m] = g.y;
-  }
+  for (int u = 0; u < CH; ++u) x[u] = zload(z, loff + (CH - 1 - u) * kRowB, b);
 }
 
-__device__ __forceinline__ void rot_load(RotChunk& b, zrsrc z, unsigned loff, int k, int i, const double2* cs_s) {
-  rot_load_x(b, z, loff, k);
-  rot_load_g(b, i, cs_s);
-}
-
-// The chunk's first cnt rotations (cnt uniform; CH for a whole chunk), storing rows k - u + 1;
-// k and i step past the chunk.
+// The first cnt fronts of a chunk (cnt uniform; CH for a whole chunk): front f - u feeds row
+// f - u to run 0 and stores row f - u + kB.  gi[b] is run b's LDS index at front f.  The
+// chunk's pairs are read up front, the second half's while the first half is applied.
 template <bool WHOLE>
-__device__ __forceinline__ void rot_apply(const RotChunk& b, zrsrc z, unsigned loff, int& k, int& i, int cnt,
-                                          double& y) {
-  const unsigned s0 = zrow(k - 6), s1 = zrow(k - 14);
+__device__ __forceinline__ void front_apply(const double (&x)[CH], zrsrc z, unsigned loff, int f, const int (&gi)[kB],
+                                            const double2 (*cs_s)[kSlot], double (&y)[kB], int cnt) {
+  const unsigned sb = zrow(f + kB - (CH - 1));
+  double2 g[CH][kB];
+#pragma unroll
+  for (int u = 0; u < CH / 2; ++u)
+#pragma unroll
+    for (int b = 0; b < kB; ++b) g[u][b] = cs_s[b][gi[b] + u];
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
+    if (u == 1) {
+#pragma unroll
+      for (int u2 = CH / 2; u2 < CH; ++u2)
+#pragma unroll
+        for (int b = 0; b < kB; ++b) g[u2][b] = cs_s[b][gi[b] + u2];
+    }
     if (WHOLE || u < cnt) {
-      const double cx = b.g[u].x * b.x[u];
-      const double v = fma(b.g[u].y, b.x[u], b.g[u].x * y);
-      if (u < 8) zstore(z, loff + (7 - u) * kRowB, s0, v);
-      else zstore(z, loff + (15 - u) * kRowB, s1, v);
-      y = fma(-b.g[u].y, y, cx);
+      double v = x[u];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const double cx = g[u][b].x * v;
+        v = fma(g[u][b].y, v, g[u][b].x * y[b]);
+        y[b] = fma(-g[u][b].y, y[b], cx);
+      }
+      zstore(z, loff + (CH - 1 - u) * kRowB, sb, v);
     }
   }
-  k -= CH;
-  i -= CH;
 }
 
-__global__ __launch_bounds__(64) void ritz_rotate_kernel(const int4* __restrict__ runs,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void ritz_rotate_kernel(
+    const int4* __restrict__ runs,
                                                          const double2* __restrict__ cs,
+                                                         const int2* __restrict__ groups,
                                                          const long long* __restrict__ meta,
                                                          const int* __restrict__ pos, int n, int r,
                                                          double* __restrict__ Z, long zs,
                                                          double* __restrict__ scr, long scr_s) {
-  __shared__ double2 cs_s[kPad + kRunCap];
+  __shared__ double2 cs_s[kB][kSlot];
   const int s = blockIdx.y, lane = threadIdx.x;
   const int j = (int)blockIdx.x * 64 + lane;
   const int jc = min(j, r - 1);
   const unsigned loff = 8u * (unsigned)lane;
-  // this workgroup's scratch: kPad + n rows of 64 lanes
-  const zrsrc z = __builtin_amdgcn_make_buffer_rsrc(scr + s * scr_s + (long)blockIdx.x * (kPad + n) * 64, 0,
-                                                    (int)((unsigned)(kPad + n) * kRowB), 0x00020000);
+  const int rows = kPadLo + n + kPadHi;
+  const zrsrc z = __builtin_amdgcn_make_buffer_rsrc(scr + s * scr_s + (long)blockIdx.x * rows * 64, 0,
+                                                    (int)((unsigned)rows * kRowB), 0x00020000);
   const int pj = pos[(long)s * r + jc];
-  for (int i = 0; i < n; ++i) zstore(z, loff, zrow(i), i == pj ? 1.0 : 0.0);
-  const long long run0 = meta[4 * s], nrun = meta[4 * s + 1], cs0 = meta[4 * s + 2];
-  // A run's pairs are fetched into registers (lane l: pairs l + 64 m, the run's last pair past
-  // its end) during the run before it, so that its start waits only for LDS stores and its
-  // first rows.
-  PairFetch pf;
-  if (nrun > 0) rot_fetch_pairs(pf, runs[run0 + nrun - 1], cs + cs0, lane);
-  for (long long q = nrun - 1; q >= 0; --q) {
-    const int4 R = runs[run0 + q];
-    const int L = R.y - R.x + 1, ktop = R.z;
-    double y = zload(z, loff, zrow(ktop + 1));
-    RotChunk A, B;
-    rot_load_x(A, z, loff, ktop);
-    __syncthreads();   // the previous run's pairs are read
+  for (int i = -kPadLo; i < n + kPadHi; ++i) zstore(z, loff, zrow(i), i == pj ? 1.0 : 0.0);
+  const long long run0 = meta[4 * s], cs0 = meta[4 * s + 1], grp0 = meta[4 * s + 2], ngrp = meta[4 * s + 3];
+  for (long long gq = 0; gq < ngrp; ++gq) {
+    const int2 G = groups[grp0 + gq];
+    // the group's runs: b-th applied is run G.x - b of the side's log (read for every slot, so
+    // that the four scalar loads are in flight together; slots past G.y are empty)
+    int4 R[kB];
 #pragma unroll
-    for (int m = 0; m < PF; ++m) cs_s[kPad + lane + 64 * m] = make_double2(pf.c[m], pf.s[m]);
+    for (int b = 0; b < kB; ++b) R[b] = runs[run0 + max(G.x - b, 0)];
+    int kt[kB], len[kB];
+    int f0 = INT_MIN, f1 = INT_MAX;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      len[b] = b < G.y ? R[b].y - R[b].x + 1 : 0;
+      if (b < G.y) {
+        f0 = max(f0, R[b].z - b);
+        f1 = min(f1, R[b].z - len[b] + 1 - b);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) kt[b] = b < G.y ? R[b].z : f0 + b;   // an empty slot: identities
+    __syncthreads();   // the previous group's pairs are read
+    // A slot: identities, then the run's pairs in the order applied from index kSpread on (the
+    // m-th rotation applied is the run's pair len - 1 - m), then identities; each lane's loads
+    // are all issued before its LDS stores.
+    constexpr int PT = (kSlot + 63) / 64;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const double2* src = cs + cs0 + R[b].x;
+      double2 t[PT];
+#pragma unroll
+      for (int q = 0; q < PT; ++q) {
+        const int m = lane + 64 * q - kSpread;
+        t[q] = (m >= 0 && m < len[b]) ? src[len[b] - 1 - m] : make_double2(1.0, 0.0);
+      }
+#pragma unroll
+      for (int q = 0; q < PT; ++q)
+        if (lane + 64 * q < kSlot) cs_s[b][lane + 64 * q] = t[q];
+    }
     __syncthreads();
-    if (q > 0) rot_fetch_pairs(pf, runs[run0 + q - 1], cs + cs0, lane);
-    int k = ktop, i = L - 1;
-    const int nf = L / CH, rem = L % CH;   // whole chunks, then a partial one
-    rot_load_g(A, i, cs_s);
+    double y[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) y[b] = zload(z, loff, zrow(f0 + b + 1));
+    int gi[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) gi[b] = kSpread + kt[b] - b - f0;
+    const int steps = f0 - f1 + 1, nf = steps / CH, rem = steps % CH;
+    int f = f0;
+    double xa[CH], xb[CH];
+    front_load(xa, z, loff, f);
     int c = 0;
     for (; c + 1 < nf; c += 2) {
-      rot_load(B, z, loff, k - CH, i - CH, cs_s);
-      rot_apply<true>(A, z, loff, k, i, CH, y);
-      rot_load(A, z, loff, k - CH, i - CH, cs_s);
-      rot_apply<true>(B, z, loff, k, i, CH, y);
+      front_load(xb, z, loff, f - CH);
+      front_apply<true>(xa, z, loff, f, gi, cs_s, y, CH);
+      f -= CH;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) gi[b] += CH;
+      front_load(xa, z, loff, f - CH);
+      front_apply<true>(xb, z, loff, f, gi, cs_s, y, CH);
+      f -= CH;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) gi[b] += CH;
     }
-    if (c < nf) {   // A holds the last whole chunk
-      rot_load(B, z, loff, k - CH, i - CH, cs_s);
-      rot_apply<true>(A, z, loff, k, i, CH, y);
-      if (rem) rot_apply<false>(B, z, loff, k, i, rem, y);
-    } else if (rem) {   // A holds the partial chunk
-      rot_apply<false>(A, z, loff, k, i, rem, y);
+    if (c < nf) {   // xa holds the last whole chunk
+      front_load(xb, z, loff, f - CH);
+      front_apply<true>(xa, z, loff, f, gi, cs_s, y, CH);
+      f -= CH;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) gi[b] += CH;
+      if (rem) front_apply<false>(xb, z, loff, f, gi, cs_s, y, rem);
+    } else if (rem) {   // xa holds the partial chunk
+      front_apply<false>(xa, z, loff, f, gi, cs_s, y, rem);
     }
-    // the run's lowest row, ktop - L + 1, takes the carried row
-    zstore(z, loff, zrow(ktop - L + 1), y);
+    // rows f1 .. f1 + kB - 1 are final in the carried registers
+#pragma unroll
+    for (int b = 0; b < kB; ++b) zstore(z, loff, zrow(f1 + b), y[b]);
   }
   if (j < r) {
     double* zc = Z + s * zs + j;
@@ -410,18 +442,19 @@ hipError_t launch_vr_outputs(const double* Vr, long sVr, int n, int r, const Ptr
   return hipGetLastError();
 }
 
-hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const long long* meta, const int* pos, int n, int r,
-                              double* Z, long zs, double* scr, long scr_s, int n_sides, hipStream_t st) {
+hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const int2* groups, const long long* meta,
+                              const int* pos, int n, int r, double* Z, long zs, double* scr, long scr_s, int n_sides,
+                              hipStream_t st) {
   if (n_sides <= 0 || r <= 0) return hipSuccess;
-  if (n <= 0 || (long)(kPad + n) * kRowB > 0x7fffffffL) return hipErrorInvalidValue;   // 31-bit buffer range
+  if (n <= 0 || (long)(kPadLo + n + kPadHi) * kRowB > 0x7fffffffL) return hipErrorInvalidValue;   // 31-bit range
   if (scr_s < ritz_scratch_doubles(n, r)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ritz_rotate_kernel, dim3((r + 63) / 64, n_sides), dim3(64), 0, st, runs, cs, meta, pos, n, r, Z,
-                     zs, scr, scr_s);
+  hipLaunchKernelGGL(ritz_rotate_kernel, dim3((r + 63) / 64, n_sides), dim3(64), 0, st, runs, cs, groups, meta, pos, n,
+                     r, Z, zs, scr, scr_s);
   return hipGetLastError();
 }
 
-int ritz_run_cap() { return kRunCap; }
+RitzGrouping ritz_grouping() { return RitzGrouping{kRunCap, kB, kSpread, kRunCap + kSpread}; }
 
-long ritz_scratch_doubles(int n, int r) { return (long)((r + 63) / 64) * (kPad + n) * 64; }
+long ritz_scratch_doubles(int n, int r) { return (long)((r + 63) / 64) * (kPadLo + n + kPadHi) * 64; }
 
 }  // namespace xkv

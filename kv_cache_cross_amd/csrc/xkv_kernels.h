@@ -51,13 +51,18 @@ hipError_t launch_widen(const float* src, double* dst, long n, hipStream_t st);
 hipError_t launch_trace(const double* C, long sC, int n, int n_sides, double* tr, hipStream_t st);
 // Z (n x r float64 per side, side stride zs) <- the logged QR rotations of a side's Rayleigh-Ritz
 // eigensolve applied last first to the unit vectors at pos (r per side): runs (lo, hi, ktop, 0)
-// of at most ritz_run_cap() rotations, (c, s) pairs, and per side meta = (first run, runs,
-// first pair, 0), as the host eigensolver packs them.  scr: working memory of
+// of at most ritz_grouping().run_cap rotations, (c, s) pairs, groups (first run, count) of runs
+// applied together as the host eigensolver forms them with ritz_grouping()'s limits, and per
+// side meta = (first run, first pair, first group, groups).  scr: working memory of
 // ritz_scratch_doubles(n, r) doubles per side (side stride scr_s).
-hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const long long* meta, const int* pos, int n, int r,
-                              double* Z, long zs, double* scr, long scr_s, int n_sides, hipStream_t st);
+struct RitzGrouping {
+  int run_cap, per_group, spread, max_steps;
+};
+hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const int2* groups, const long long* meta,
+                              const int* pos, int n, int r, double* Z, long zs, double* scr, long scr_s, int n_sides,
+                              hipStream_t st);
+RitzGrouping ritz_grouping();
 long ritz_scratch_doubles(int n, int r);
-int ritz_run_cap();
 // res2[s*r + i] = || YZ[:, i] - theta[s*r + i] * Vr[:, i] ||^2 (n x r float64 per side, side stride n*r).
 hipError_t launch_ritz_residual(const double* YZ, const double* Vr, const double* theta, int n, int r,
                                 double* res2, int n_sides, hipStream_t st);

@@ -15,11 +15,14 @@ namespace {
 
 constexpr int NB = 64;
 
-// One workgroup per side: load the nb x nb diagonal block of W at (j0, j0), factor it
-// as L L^T in LDS (right-looking, column by column) and invert L alongside: X = L^-1
-// solves L X = I by the same right-looking sweep (at column k, row k of the right-hand
-// side is divided by the pivot and row k's multiples L[i][k] X[k][.] leave the rows
-// below), so both share the column loop's barriers.  Writes L and L^-1.
+// One workgroup per side: load the nb x nb diagonal block of W at (j0, j0) and factor it as
+// L L^T with L^-1 alongside, in LDS.  The elimination runs as L~ D L~^T (L~ unit lower): step k
+// takes the pivot d_k = a[k][k] and subtracts a[i][k] a[j][k] / d_k from the trailing lower
+// triangle, leaving column k unscaled (a[i][k] = l~_ik d_k), and X = L~^-1 comes from the same
+// sweep (row i of X loses l~_ik times row k).  A step reads only column k, the pivot and row
+// k of X, none of which it writes, so one barrier per step suffices; every thread takes the
+// pivot decision itself.  At the end L = a D^-1/2 below the diagonal with sqrt(d) on it, and
+// L^-1 = D^-1/2 X.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long ldw, long sW,
                                                          double* L, long ldl, long sL,
                                                          double* Dinv, long sD, int j0, int nb,
@@ -28,6 +31,8 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
   __shared__ double a[NB][NB + 1];
   __shared__ double inv[NB][NB + 1];
   __shared__ double floor_s[NB];   // the pivots' breakdown floors
+  __shared__ double piv_s[NB];     // the pivots taken
+  __shared__ double rs_s[NB], sq_s[NB];
   __shared__ int bad;
   const int side = blockIdx.x, tid = threadIdx.x;
   const int ti = tid >> 4, tj = tid & 15;   // a 16 x 16 thread grid
@@ -41,50 +46,50 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
     }
   __syncthreads();
   for (int k = 0; k < nb; ++k) {
-    if (tid == 0) {
-      // The pivot is the squared distance of column j0+k of Y from the span of the
-      // previous columns.  Below 1e-14 of the column's squared norm it is either a
-      // breakdown (float64 sweeps: reported) or, with `clamp` (float32 sweeps, whose Y
-      // carries float32 noise), raised to that floor, which damps the near-dependent
-      // direction instead of amplifying noise.
-      double piv = a[k][k];
-      const double floor_k = floor_s[k];
-      if (!isfinite(piv)) {
-        bad = 1;
+    // The pivot is the squared distance of column j0+k of Y from the span of the previous
+    // columns.  Below 1e-14 of the column's squared norm it is either a breakdown (float64
+    // sweeps: reported) or, with `clamp` (float32 sweeps, whose Y carries float32 noise),
+    // raised to that floor, which damps the near-dependent direction instead of amplifying
+    // noise.
+    double piv = a[k][k];
+    const double floor_k = floor_s[k];
+    bool brk = false;
+    if (!isfinite(piv)) {
+      brk = true;
+      piv = 1.0;
+    } else if (!(piv > floor_k)) {
+      if (clamp && floor_k > 0.0) {
+        piv = floor_k;
+      } else {
+        brk = true;
         piv = 1.0;
-      } else if (!(piv > floor_k)) {
-        if (clamp && floor_k > 0.0) {
-          piv = floor_k;
-        } else {
-          bad = 1;
-          piv = 1.0;
-        }
       }
-      a[k][k] = sqrt(piv);
     }
-    __syncthreads();
-    const double rdk = 1.0 / a[k][k];
-    // column k of L below the pivot, and row k of X (columns c <= k)
-    if (tid < 64) {
-      for (int i = k + 1 + tid; i < nb; i += 64) a[i][k] *= rdk;
-    } else if (tid - 64 <= k) {
-      inv[k][tid - 64] *= rdk;
+    if (tid == 0) {
+      piv_s[k] = piv;
+      if (brk) bad = 1;
     }
-    __syncthreads();
-    // trailing update of the lower triangle (k < j <= i), and the rows of X below k
+    const double rdk = 1.0 / piv;
     for (int i = k + 1 + ti; i < nb; i += 16) {
-      const double aik = a[i][k];
-      for (int j = k + 1 + tj; j <= i; j += 16) a[i][j] -= aik * a[j][k];
-      for (int c = tj; c <= k; c += 16) inv[i][c] -= aik * inv[k][c];
+      const double lik = a[i][k] * rdk;
+      for (int j = k + 1 + tj; j <= i; j += 16) a[i][j] -= lik * a[j][k];
+      for (int c = tj; c <= k; c += 16) inv[i][c] -= lik * inv[k][c];
     }
     __syncthreads();
   }
+  if (tid < nb) {
+    const double sq = sqrt(piv_s[tid]);
+    sq_s[tid] = sq;
+    rs_s[tid] = 1.0 / sq;
+  }
+  __syncthreads();
   double* l = L + side * sL + (long)j0 * ldl + j0;
   double* dv = Dinv + side * sD;
   for (int i = ti; i < nb; i += 16)
-    for (int j = tj; j < nb; j += 16) l[(long)i * ldl + j] = (j <= i) ? a[i][j] : 0.0;
+    for (int j = tj; j < nb; j += 16)
+      l[(long)i * ldl + j] = j < i ? a[i][j] * rs_s[j] : (j == i ? sq_s[j] : 0.0);
   for (int i = ti; i < NB; i += 16)
-    for (int j = tj; j < NB; j += 16) dv[i * NB + j] = (i < nb && j < nb && j <= i) ? inv[i][j] : 0.0;
+    for (int j = tj; j < NB; j += 16) dv[i * NB + j] = (i < nb && j < nb && j <= i) ? inv[i][j] * rs_s[i] : 0.0;
   if (tid == 0 && bad) info[side] = 1;
 }
 

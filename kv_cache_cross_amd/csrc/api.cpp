@@ -426,6 +426,8 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     hf.Ya = hf.w.Y64;
   }
   const int per = std::max(1, kMaxPtrs / p.G);
+  // C is exactly symmetric (both Gram kernels give C[i][j] and C[j][i] the same value), so the
+  // products C Q read it as C^T: the GEMM then stages it into LDS along its contiguous rows.
   auto fp64_sweeps = [&](Half& hf, int count) -> int {
     for (int it = 0; it < count; ++it) {
       if (hf.tQ == GF32) {
@@ -434,7 +436,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
         hf.Qcur = hf.Qa;
         hf.tQ = GF64;
       }
-      XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, hf.tQ, GF64, hf.w.C64, n, nn, hf.Qcur, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
+      XKV_K(gemm(gdesc(n, kb, n, 1, 0, GF64, hf.tQ, GF64, hf.w.C64, n, nn, hf.Qcur, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
                        hf.cnt), st));
       int e = cholqr(p, hf.w, hf.cnt, hf.Ya, GF64, hf.Qa, GF64, st);       // Qa = orth(Ya)
       if (e) return e;
@@ -465,7 +467,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     XKV_K(launch_trace(hf.w.C64, nn, n, hf.cnt, hf.w.trace, st));
     XKV_K(launch_init_q(hf.w.Q32, n, kb, nk, hf.cnt, desc->seed, st));
     for (int it = 0; it < p.fp32_iters; ++it) {
-      GemmDesc cq = gdesc(n, kb, n, 0, 0, GF32, GF32, GF32, hf.w.C32, n, nn, hf.w.Q32, kb, nk, hf.w.Y32, kb, nk, 1.0,
+      GemmDesc cq = gdesc(n, kb, n, 1, 0, GF32, GF32, GF32, hf.w.C32, n, nn, hf.w.Q32, kb, nk, hf.w.Y32, kb, nk, 1.0,
                           0.0, hf.cnt);
       cq.acc = GF32;   // float32 matrix cores for the float32 iterations
       XKV_K(gemm(cq, st));
@@ -529,7 +531,7 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   if ((int)ctx->eig_side.size() < 2 * S) ctx->eig_side.resize(2 * S, xkv_eigh_scratch{});
   // The Rayleigh-Ritz matrix H = Q^T C Q of a half (and its info), copied down, then an event.
   auto rr_matrix = [&](Half& hf, int h, bool first) -> int {
-    XKV_K(gemm(gdesc(n, kb, n, 0, 0, GF64, GF64, GF64, hf.w.C64, n, nn, hf.Qa, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
+    XKV_K(gemm(gdesc(n, kb, n, 1, 0, GF64, GF64, GF64, hf.w.C64, n, nn, hf.Qa, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
                      hf.cnt), st));
     XKV_K(gemm(gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, hf.Qa, kb, nk, hf.Ya, kb, nk, hf.w.H, kb, kk, 1.0, 0.0,
                      hf.cnt), st));

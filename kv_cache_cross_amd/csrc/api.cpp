@@ -692,6 +692,30 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
                            hipMemcpyDeviceToHost, st));
     return XKV_OK;
   };
+  // Bt = V_r and the projection A = X V_r of sides [s_begin, s_end).  The first half's sides
+  // are projected as soon as its first round's V_r is on the device, in the GPU's wait for
+  // the second half's eigenvalues; a later round projects every side again.
+  const long nr = (long)n * r;
+  auto project = [&](int s_begin, int s_end) -> int {
+    for (int s0 = s_begin; s0 < s_end; s0 += per) {
+      const int cnt = std::min(per, s_end - s0);
+      PtrTable bt{}, aout{}, lay{};
+      for (int s = 0; s < cnt; ++s) {
+        bt.p[s] = sides[s0 + s].Bt;
+        aout.p[s] = sides[s0 + s].A;
+        for (int l = 0; l < p.G; ++l) lay.p[s * p.G + l] = sides[s0 + s].layers[l];
+      }
+      const size_t es = p.bf16 ? 2 : 4;
+      void* VrT = (char*)w.VrT + (size_t)s0 * nr * es;
+      XKV_K(launch_vr_outputs(w.Vr + s0 * nr, nr, n, r, bt, p.bf16, VrT, nr, cnt, st));
+      if (p.bf16)
+        XKV_K(launch_project_bf16(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const uint16_t*)VrT, nr, r, aout,
+                                  st));
+      else
+        XKV_K(launch_project_f32(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const float*)VrT, nr, r, aout, st));
+    }
+    return XKV_OK;
+  };
   for (int h = 0; h < nh; ++h) {
     rc = pre_work(hv[h]);
     if (rc) return rc;
@@ -740,6 +764,10 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       if (rc) return rc;
       rc = post_work(hf, h);
       if (rc) return rc;
+      if (nh == 2 && h == 0 && rounds == 1) {
+        rc = project(0, hf.cnt);
+        if (rc) return rc;
+      }
     }
     XKV_HIP(hipEventRecord(ctx->upload_done, st));
     ctx->upload_pending = true;
@@ -808,23 +836,8 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     if (sides[s].Vr64)
       XKV_HIP(hipMemcpyAsync(sides[s].Vr64, w.Vr + (long)s * n * r, (size_t)n * r * sizeof(double),
                              hipMemcpyDeviceToDevice, st));
-  const long nr = (long)n * r;
-  for (int s0 = 0; s0 < S; s0 += per) {
-    const int cnt = std::min(per, S - s0);
-    PtrTable bt{}, aout{}, lay{};
-    for (int s = 0; s < cnt; ++s) {
-      bt.p[s] = sides[s0 + s].Bt;
-      aout.p[s] = sides[s0 + s].A;
-      for (int l = 0; l < p.G; ++l) lay.p[s * p.G + l] = sides[s0 + s].layers[l];
-    }
-    const size_t es = p.bf16 ? 2 : 4;
-    void* VrT = (char*)w.VrT + (size_t)s0 * nr * es;
-    XKV_K(launch_vr_outputs(w.Vr + s0 * nr, nr, n, r, bt, p.bf16, VrT, nr, cnt, st));
-    if (p.bf16)
-      XKV_K(launch_project_bf16(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const uint16_t*)VrT, nr, r, aout, st));
-    else
-      XKV_K(launch_project_f32(lay, cnt, p.G, sides[s0].ld_layer, p.T, p.d_kv, (const float*)VrT, nr, r, aout, st));
-  }
+  rc = project(nh == 2 && rounds == 1 ? hv[1].s0 : 0, S);
+  if (rc) return rc;
   if (!converged)
     return fail(XKV_ENOTCONV, "compress: subspace error estimate above %.1e after %d rounds (%d sweeps); "
                 "outputs are written", tol, rounds, total_iters);

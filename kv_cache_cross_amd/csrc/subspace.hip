@@ -227,7 +227,8 @@ __global__ __launch_bounds__(256) void vr_outputs_kernel(VrArgs a) {
 // trail the loads by kB + 1 rows).  At the end the scratch rows are copied to Z (n x r).
 // Lanes past r work on column r - 1 exactly as its own lane does and store nothing to Z.
 constexpr int kRunCap = 1024;                 // rotations per run (longer sweeps are cut)
-constexpr int kB = 4;                         // runs per group
+constexpr int kB = 4;                         // runs per group (even: slots are staged in pairs)
+static_assert(kB % 2 == 0, "pair slots are staged two at a time");
 constexpr int CH = 8;                         // fronts per chunk
 constexpr int kSpread = 64;                   // rows a group's starts and ends may differ by
 constexpr int kSlot = kSpread + kRunCap + kSpread + 2 * CH;   // LDS pairs per run
@@ -325,21 +326,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int b = 0; b < kB; ++b) kt[b] = b < G.y ? R[b].z : f0 + b;   // an empty slot: identities
     __syncthreads();   // the previous group's pairs are read
     // A slot: identities, then the run's pairs in the order applied from index kSpread on (the
-    // m-th rotation applied is the run's pair len - 1 - m), then identities; each lane's loads
-    // are all issued before its LDS stores.
+    // m-th rotation applied is the run's pair len - 1 - m), then identities; each lane issues
+    // two slots' loads before their LDS stores.
     constexpr int PT = (kSlot + 63) / 64;
 #pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      const double2* src = cs + cs0 + R[b].x;
-      double2 t[PT];
+    for (int b = 0; b < kB; b += 2) {   // two slots' loads in flight together
+      double2 t[2][PT];
 #pragma unroll
-      for (int q = 0; q < PT; ++q) {
-        const int m = lane + 64 * q - kSpread;
-        t[q] = (m >= 0 && m < len[b]) ? src[len[b] - 1 - m] : make_double2(1.0, 0.0);
+      for (int h = 0; h < 2; ++h) {
+        const double2* src = cs + cs0 + R[b + h].x;
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+          const int m = lane + 64 * q - kSpread;
+          t[h][q] = (m >= 0 && m < len[b + h]) ? src[len[b + h] - 1 - m] : make_double2(1.0, 0.0);
+        }
       }
 #pragma unroll
-      for (int q = 0; q < PT; ++q)
-        if (lane + 64 * q < kSlot) cs_s[b][lane + 64 * q] = t[q];
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < PT; ++q)
+          if (lane + 64 * q < kSlot) cs_s[b + h][lane + 64 * q] = t[h][q];
     }
     __syncthreads();
     double y[kB];

@@ -141,47 +141,57 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
       }
 }
 
-// Large float32 products with both operands stored K-major (A as K x M, B as K x N), M and N
-// multiples of 128 (the float32 sweeps' C Q, with C read as its transpose): 128 x 128 output tiles, 4 waves of 64 x 64 (4 x 4 MFMA tiles each),
-// K in 16-deep slabs double-buffered in LDS with one barrier per slab, the next slab's loads
-// in flight in registers while the current one is multiplied.  Both operands are staged along
-// their contiguous rows.
-constexpr int TT = 128, TKS = 16;
-template <typename T>
-__global__ __launch_bounds__(256) void gemm_tn128_kernel(Args p) {
-  __shared__ T As[2][TKS][TT + 4];
-  __shared__ T Bs[2][TKS][TT + 4];
+// Large products with both operands stored K-major (A as K x M, B as K x N), one type for
+// operands, result and arithmetic, M a multiple of TM and N of TN (the float32 sweeps' C Q,
+// with C read as its transpose): TM x TN output tiles, 4 waves in 2 x 2 of
+// (TM/2) x (TN/2), K in 16-deep slabs double-buffered in LDS with one barrier per slab, the
+// next slab's loads in flight in registers while the current one is multiplied.  Both
+// operands are staged along their contiguous rows.
+constexpr int TKS = 16;
+template <typename T, int TM, int TN>
+__global__ __launch_bounds__(256) void gemm_tn_kernel(Args p) {
+  constexpr int FI = TM / 32, FJ = TN / 32;         // MFMA tiles per wave along M and N
+  constexpr int QA = TKS * TM / 256, QB = TKS * TN / 256;   // elements per thread per slab
+  __shared__ T As[2][TKS][TM + 4];
+  __shared__ T Bs[2][TKS][TN + 4];
   const int z = blockIdx.z;
   const T* A = (const T*)p.A + z * p.sA;
   const T* B = (const T*)p.B + z * p.sB;
   T* C = (T*)p.C + z * p.sC;
-  const int m0 = blockIdx.y * TT, n0 = blockIdx.x * TT;
+  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  typename Mfma<T>::acc_t acc[4][4];
+  typename Mfma<T>::acc_t acc[FI][FJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
-  // element q of this thread in a slab: row kk = (tid >> 7) + 2 q of the slab, column tid & 127
-  const int cc = tid & 127, kr = tid >> 7;
-  T ra[8], rb[8];
+  // element q of this thread in a slab: column tid % TM (TN) of row tid / TM (TN) + q 256 / TM (TN)
+  T ra[QA], rb[QB];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int gk = k0 + kr + 2 * q;
-      const bool in = gk < p.K;
-      ra[q] = in ? A[(long)gk * p.lda + m0 + cc] : (T)0;
-      rb[q] = in ? B[(long)gk * p.ldb + n0 + cc] : (T)0;
+    for (int q = 0; q < QA; ++q) {
+      const int e = tid + 256 * q, gk = k0 + e / TM;
+      ra[q] = gk < p.K ? A[(long)gk * p.lda + m0 + e % TM] : (T)0;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int e = tid + 256 * q, gk = k0 + e / TN;
+      rb[q] = gk < p.K ? B[(long)gk * p.ldb + n0 + e % TN] : (T)0;
     }
   };
   auto stage = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      As[buf][kr + 2 * q][cc] = ra[q];
-      Bs[buf][kr + 2 * q][cc] = rb[q];
+    for (int q = 0; q < QA; ++q) {
+      const int e = tid + 256 * q;
+      As[buf][e / TM][e % TM] = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int e = tid + 256 * q;
+      Bs[buf][e / TN][e % TN] = rb[q];
     }
   };
   fetch(0);
@@ -193,28 +203,28 @@ __global__ __launch_bounds__(256) void gemm_tn128_kernel(Args p) {
     if (more) fetch(k0 + TKS);
 #pragma unroll
     for (int ks = 0; ks < TKS; ks += 4) {
-      T a[4], b[4];
+      T a[FI], b[FJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[buf][ks + (lane >> 4)][wm * 64 + i * 16 + (lane & 15)];
+      for (int i = 0; i < FI; ++i) a[i] = As[buf][ks + (lane >> 4)][wm * (TM / 2) + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[buf][ks + (lane >> 4)][wn * 64 + j * 16 + (lane & 15)];
+      for (int j = 0; j < FJ; ++j) b[j] = Bs[buf][ks + (lane >> 4)][wn * (TN / 2) + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::op(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < FJ; ++j) acc[i][j] = Mfma<T>::op(a[i], b[j], acc[i][j]);
     }
     if (more) stage(buf ^ 1);   // the other buffer was last read before the previous barrier
     __syncthreads();
     buf ^= 1;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int gm = m0 + wm * 64 + i * 16 + Mfma<T>::row(lane, v);
-        const int gn = n0 + wn * 64 + j * 16 + (lane & 15);
+        const int gm = m0 + wm * (TM / 2) + i * 16 + Mfma<T>::row(lane, v);
+        const int gn = n0 + wn * (TN / 2) + j * 16 + (lane & 15);
         T* dst = C + (long)gm * p.ldc + gn;
         double r = p.alpha * (double)acc[i][j][v];
         if (p.beta != 0.0) r += p.beta * (double)*dst;
@@ -222,10 +232,10 @@ __global__ __launch_bounds__(256) void gemm_tn128_kernel(Args p) {
       }
 }
 
-template <typename T>
-hipError_t run_tn128(const GemmDesc& d, hipStream_t st) {
+template <typename T, int TM, int TN>
+hipError_t run_tn(const GemmDesc& d, hipStream_t st) {
   Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta};
-  hipLaunchKernelGGL(gemm_tn128_kernel<T>, dim3(d.N / TT, d.M / TT, d.batch), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_tn_kernel<T, TM, TN>), dim3(d.N / TN, d.M / TM, d.batch), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -245,9 +255,12 @@ hipError_t run(const GemmDesc& d, hipStream_t st) {
 hipError_t gemm(const GemmDesc& d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.batch <= 0) return hipSuccess;
   const int code = (d.typeA << 3) | (d.typeB << 2) | (d.typeC << 1) | d.acc;
-  // float32 only: the float64 instance needs 332 registers per lane, one wave per SIMD, and
-  // measured slower than the 64 x 64 tiles (C Q 4.72 against 4.09 ms, Y^T Y 1.53 against 0.87 ms)
-  if (d.ta && !d.tb && d.M % TT == 0 && d.N % TT == 0 && d.K > 0 && code == 0b0000) return run_tn128<float>(d, st);
+  // float32 products with K-major operands on 128 x 128 tiles (2.19 ms for the 64k half's C Q
+  // against 2.57 ms on 64 x 64).  Float64 stays on 64 x 64: with the K-major kernel its C Q took
+  // 4.72 ms on 128 x 128 tiles (332 registers per lane, one wave per SIMD) and 4.33 ms on
+  // 128 x 64, Y^T Y 1.53 and 1.14 ms, against 4.09 and 0.87 ms.
+  if (d.ta && !d.tb && d.K > 0 && code == 0b0000 && d.M % 128 == 0 && d.N % 128 == 0)
+    return run_tn<float, 128, 128>(d, st);
   switch (code) {
     // A B C acc  (0 = float, 1 = double)
     case 0b0000: return run<float, float, float, float>(d, st);

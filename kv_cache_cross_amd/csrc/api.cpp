@@ -311,6 +311,7 @@ xkv::GemmDesc gdesc(int M, int N, int K, int ta, int tb, int tA, int tB, int tC,
   g.B = B; g.ldb = ldb; g.sB = sB;
   g.C = C; g.ldc = ldc; g.sC = sC;
   g.alpha = alpha; g.beta = beta; g.batch = batch;
+  g.sym = 0;
   return g;
 }
 
@@ -325,7 +326,9 @@ int cholqr(const CompressPlan& p, const CompressWs& w, int S, void* Y, int tY, v
   using namespace xkv;
   const int n = p.n, kb = p.kb;
   const long nk = (long)n * kb, kk = (long)kb * kb, dstride = (long)p.nblk * 4096;
-  XKV_K(gemm(gdesc(kb, kb, n, 1, 0, tY, tY, GF64, Y, kb, nk, Y, kb, nk, w.W, kb, kk, 1.0, 0.0, S), st));
+  GemmDesc wd = gdesc(kb, kb, n, 1, 0, tY, tY, GF64, Y, kb, nk, Y, kb, nk, w.W, kb, kk, 1.0, 0.0, S);
+  wd.sym = 1;   // W = Y^T Y: the upper tiles, mirrored
+  XKV_K(gemm(wd, st));
   XKV_K(launch_copy_diag(w.W, kb, kk, w.wdiag, kb, kb, S, st));
   for (int jb = 0; jb < p.nblk; ++jb) {
     const int j0 = jb * 64, nbj = std::min(64, kb - j0), rem = kb - j0 - nbj;

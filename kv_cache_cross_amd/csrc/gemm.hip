@@ -42,6 +42,7 @@ struct Args {
   const void* B; long ldb, sB;
   void* C; long ldc, sC;
   double alpha, beta;
+  int sym;
 };
 
 template <typename TA, typename TB, typename TC, typename ACC, bool TA_T, bool TB_T>
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
   const TB* B = (const TB*)p.B + z * p.sB;
   TC* C = (TC*)p.C + z * p.sC;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (p.sym && n0 < m0) return;   // a tile below the diagonal: its mirror writes it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -132,11 +134,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
       for (int v = 0; v < 4; ++v) {
         const int gm = m0 + wm * 32 + i * 16 + Mfma<ACC>::row(lane, v);
         const int gn = n0 + wn * 32 + j * 16 + (lane & 15);
-        if (gm < p.M && gn < p.N) {
+        if (gm < p.M && gn < p.N && !(p.sym && gn < gm)) {
           TC* dst = C + (long)gm * p.ldc + gn;
           double r = p.alpha * (double)acc[i][j][v];
           if (p.beta != 0.0) r += p.beta * (double)*dst;
           *dst = (TC)r;
+          if (p.sym && gn != gm) C[(long)gn * p.ldc + gm] = (TC)r;
         }
       }
 }
@@ -234,14 +237,14 @@ __global__ __launch_bounds__(256) void gemm_tn_kernel(Args p) {
 
 template <typename T, int TM, int TN>
 hipError_t run_tn(const GemmDesc& d, hipStream_t st) {
-  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta};
+  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta, d.sym};
   hipLaunchKernelGGL((gemm_tn_kernel<T, TM, TN>), dim3(d.N / TN, d.M / TM, d.batch), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <typename TA, typename TB, typename TC, typename ACC>
 hipError_t run(const GemmDesc& d, hipStream_t st) {
-  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta};
+  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta, d.sym};
   dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, d.batch);
   if (d.ta && d.tb) hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, ACC, true, true>), grid, dim3(256), 0, st, p);
   else if (d.ta)    hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, ACC, true, false>), grid, dim3(256), 0, st, p);
@@ -254,12 +257,13 @@ hipError_t run(const GemmDesc& d, hipStream_t st) {
 
 hipError_t gemm(const GemmDesc& d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.batch <= 0) return hipSuccess;
+  if (d.sym && (d.M != d.N || d.beta != 0.0)) return hipErrorInvalidValue;
   const int code = (d.typeA << 3) | (d.typeB << 2) | (d.typeC << 1) | d.acc;
   // float32 products with K-major operands on 128 x 128 tiles (2.19 ms for the 64k half's C Q
   // against 2.57 ms on 64 x 64).  Float64 stays on 64 x 64: with the K-major kernel its C Q took
   // 4.72 ms on 128 x 128 tiles (332 registers per lane, one wave per SIMD) and 4.33 ms on
   // 128 x 64, Y^T Y 1.53 and 1.14 ms, against 4.09 and 0.87 ms.
-  if (d.ta && !d.tb && d.K > 0 && code == 0b0000 && d.M % 128 == 0 && d.N % 128 == 0)
+  if (d.ta && !d.tb && d.K > 0 && code == 0b0000 && d.M % 128 == 0 && d.N % 128 == 0 && !d.sym)
     return run_tn<float, 128, 128>(d, st);
   switch (code) {
     // A B C acc  (0 = float, 1 = double)

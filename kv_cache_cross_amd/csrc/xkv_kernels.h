@@ -31,6 +31,8 @@ struct GemmDesc {
   void* C; long ldc, sC;
   double alpha, beta;
   int batch;
+  int sym;                    // C = A^T A (symmetric, M == N): only tiles on or above the
+                              // diagonal are computed, each written at its mirror too
 };
 hipError_t gemm(const GemmDesc& d, hipStream_t st);
 

@@ -223,6 +223,8 @@ int plan_compress(const xkv_compress_desc* d, int n_sides, CompressPlan* p) {
   return XKV_OK;
 }
 
+constexpr int kWSplit = 3;   // K ranges of W = Y^T Y at most (workspace for their partial products)
+
 struct CompressWs {
   double* C64; float* C32;
   float* Q32; float* Y32;
@@ -231,6 +233,7 @@ struct CompressWs {
   double* H; double* Z; double* Vr;
   double* Rf; int* pos; double* Wb;   // packed reflector blocks, wanted positions, block products
   double* Zs;                         // working memory of the rotation kernel
+  double* Wpart;                      // partial products of W = Y^T Y (kWSplit per side)
   double* wdiag;
   double* YZ; double* theta; double* res2;
   void* VrT;
@@ -258,6 +261,7 @@ CompressWs carve_compress(void* ws, const CompressPlan& p, int S) {
   w.pos = c.take<int>((size_t)S * p.r);
   w.Wb = c.take<double>((size_t)S * 2 * XKV_EIGH_NBG * p.r);
   w.Zs = c.take<double>((size_t)S * xkv::ritz_scratch_doubles(p.kb, p.r));
+  w.Wpart = c.take<double>((size_t)S * kWSplit * kk);
   w.Vr = c.take<double>((size_t)S * p.n * p.r);
   w.wdiag = c.take<double>((size_t)S * p.kb);
   w.YZ = c.take<double>((size_t)S * p.n * p.r);
@@ -290,6 +294,7 @@ CompressWs shift_compress_ws(const CompressWs& w, const CompressPlan& p, int s0)
   v.pos += (size_t)s0 * p.r;
   v.Wb += (size_t)s0 * 2 * XKV_EIGH_NBG * p.r;
   v.Zs += (size_t)s0 * xkv::ritz_scratch_doubles(p.kb, p.r);
+  v.Wpart += (size_t)s0 * kWSplit * kk;
   v.Vr += s0 * nr;
   v.wdiag += (size_t)s0 * p.kb;
   v.YZ += s0 * nr;
@@ -312,6 +317,8 @@ xkv::GemmDesc gdesc(int M, int N, int K, int ta, int tb, int tA, int tB, int tC,
   g.C = C; g.ldc = ldc; g.sC = sC;
   g.alpha = alpha; g.beta = beta; g.batch = batch;
   g.sym = 0;
+  g.ksplit = 1;
+  g.part = nullptr;
   return g;
 }
 
@@ -328,6 +335,15 @@ int cholqr(const CompressPlan& p, const CompressWs& w, int S, void* Y, int tY, v
   const long nk = (long)n * kb, kk = (long)kb * kb, dstride = (long)p.nblk * 4096;
   GemmDesc wd = gdesc(kb, kb, n, 1, 0, tY, tY, GF64, Y, kb, nk, Y, kb, nk, w.W, kb, kk, 1.0, 0.0, S);
   wd.sym = 1;   // W = Y^T Y: the upper tiles, mirrored
+  // The upper tiles alone leave the device's workgroup slots (4 per compute unit) short of two
+  // rounds at the 64k sizes, each tile a long run over K: K is split into ranges of at least 512
+  // (up to kWSplit), the ranges' products summed in a fixed order.  The split depends on n only,
+  // so that a side's W does not depend on how many sides share the call.
+  const int ks = std::max(1, std::min(kWSplit, n / 512));
+  if (ks > 1) {
+    wd.ksplit = ks;
+    wd.part = w.Wpart;
+  }
   XKV_K(gemm(wd, st));
   XKV_K(launch_copy_diag(w.W, kb, kk, w.wdiag, kb, kb, S, st));
   for (int jb = 0; jb < p.nblk; ++jb) {

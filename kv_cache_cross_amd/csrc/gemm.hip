@@ -13,6 +13,7 @@
 // [k = lane/16] and B[k = lane/16][n = lane%16].  The float32 result holds
 // D[4*(lane/16) + v][lane%16] in register v; the float64 result holds
 // D[4*v + lane/16][lane%16].
+#include <algorithm>
 #include "xkv_common.h"
 #include "xkv_kernels.h"
 
@@ -43,6 +44,8 @@ struct Args {
   void* C; long ldc, sC;
   double alpha, beta;
   int sym;
+  int batch, ksplit, kchunk;   // ksplit > 1: workgroup z takes K range z / batch of side z % batch
+  double* part;                // and writes its partial product there (M x N each)
 };
 
 template <typename TA, typename TB, typename TC, typename ACC, bool TA_T, bool TB_T>
@@ -50,9 +53,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
   __shared__ ACC As[BK][BM + 4];
   __shared__ ACC Bs[BK][BN + 4];
   const int z = blockIdx.z;
-  const TA* A = (const TA*)p.A + z * p.sA;
-  const TB* B = (const TB*)p.B + z * p.sB;
-  TC* C = (TC*)p.C + z * p.sC;
+  const TA* A;
+  const TB* B;
+  TC* C;
+  int K = p.K;
+  long ldc = p.ldc;
+  if (p.ksplit > 1) {
+    const int side = z % p.batch, kc0 = (z / p.batch) * p.kchunk;
+    K = min(p.kchunk, p.K - kc0);
+    A = (const TA*)p.A + side * p.sA + (TA_T ? (long)kc0 * p.lda : (long)kc0);
+    B = (const TB*)p.B + side * p.sB + (TB_T ? (long)kc0 : (long)kc0 * p.ldb);
+    C = (TC*)(p.part + (long)z * p.M * p.N);
+    ldc = p.N;
+  } else {
+    A = (const TA*)p.A + z * p.sA;
+    B = (const TB*)p.B + z * p.sB;
+    C = (TC*)p.C + z * p.sC;
+  }
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   if (p.sym && n0 < m0) return;   // a tile below the diagonal: its mirror writes it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -83,11 +100,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
       int mm, kk;
       a_mk(q, mm, kk);
       const int gm = m0 + mm, gk = k0 + kk;
-      ra[q] = (gm < p.M && gk < p.K) ? (ACC)(TA_T ? A[(long)gk * p.lda + gm] : A[(long)gm * p.lda + gk]) : (ACC)0;
+      ra[q] = (gm < p.M && gk < K) ? (ACC)(TA_T ? A[(long)gk * p.lda + gm] : A[(long)gm * p.lda + gk]) : (ACC)0;
       int nn;
       b_kn(q, kk, nn);
       const int gn = n0 + nn, gk2 = k0 + kk;
-      rb[q] = (gn < p.N && gk2 < p.K) ? (ACC)(TB_T ? B[(long)gn * p.ldb + gk2] : B[(long)gk2 * p.ldb + gn]) : (ACC)0;
+      rb[q] = (gn < p.N && gk2 < K) ? (ACC)(TB_T ? B[(long)gn * p.ldb + gk2] : B[(long)gk2 * p.ldb + gn]) : (ACC)0;
     }
   };
   auto stage = [&]() {
@@ -104,8 +121,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
   fetch(0);
   stage();
   __syncthreads();
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
-    const bool more = k0 + BK < p.K;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
     if (more) fetch(k0 + BK);   // in flight during the multiplies below
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 4) {
@@ -135,11 +152,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args p) {
         const int gm = m0 + wm * 32 + i * 16 + Mfma<ACC>::row(lane, v);
         const int gn = n0 + wn * 32 + j * 16 + (lane & 15);
         if (gm < p.M && gn < p.N && !(p.sym && gn < gm)) {
-          TC* dst = C + (long)gm * p.ldc + gn;
+          TC* dst = C + (long)gm * ldc + gn;
           double r = p.alpha * (double)acc[i][j][v];
           if (p.beta != 0.0) r += p.beta * (double)*dst;
           *dst = (TC)r;
-          if (p.sym && gn != gm) C[(long)gn * p.ldc + gm] = (TC)r;
+          if (p.sym && gn != gm) C[(long)gn * ldc + gm] = (TC)r;
         }
       }
 }
@@ -237,19 +254,43 @@ __global__ __launch_bounds__(256) void gemm_tn_kernel(Args p) {
 
 template <typename T, int TM, int TN>
 hipError_t run_tn(const GemmDesc& d, hipStream_t st) {
-  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta, d.sym};
+  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta, d.sym,
+         d.batch, 1, d.K, nullptr};
   hipLaunchKernelGGL((gemm_tn_kernel<T, TM, TN>), dim3(d.N / TN, d.M / TM, d.batch), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
+// C[side] = the sum of the side's ksplit partial products, in the order of their K ranges.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const double* part, int ksplit, int batch, long mn, double* C,
+                                                        long sC) {
+  const int side = blockIdx.y;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < mn; e += (long)gridDim.x * 256) {
+    double t = 0.0;
+    for (int q = 0; q < ksplit; ++q) t += part[((long)q * batch + side) * mn + e];
+    C[side * sC + e] = t;
+  }
+}
+
 template <typename TA, typename TB, typename TC, typename ACC>
 hipError_t run(const GemmDesc& d, hipStream_t st) {
-  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta, d.sym};
-  dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, d.batch);
+  Args p{d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, d.C, d.ldc, d.sC, d.alpha, d.beta, d.sym,
+         d.batch, 1, d.K, d.part};
+  if (d.ksplit > 1 && d.part) {
+    p.ksplit = d.ksplit;
+    p.kchunk = (d.K + d.ksplit - 1) / d.ksplit;
+  }
+  dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, d.batch * p.ksplit);
   if (d.ta && d.tb) hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, ACC, true, true>), grid, dim3(256), 0, st, p);
   else if (d.ta)    hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, ACC, true, false>), grid, dim3(256), 0, st, p);
   else if (d.tb)    hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, ACC, false, true>), grid, dim3(256), 0, st, p);
   else              hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, ACC, false, false>), grid, dim3(256), 0, st, p);
+  if (p.ksplit > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long mn = (long)d.M * d.N;
+    hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)std::min<long>((mn + 255) / 256, 1024), d.batch), dim3(256),
+                       0, st, d.part, p.ksplit, d.batch, mn, (double*)d.C, d.sC);
+  }
   return hipGetLastError();
 }
 
@@ -258,6 +299,9 @@ hipError_t run(const GemmDesc& d, hipStream_t st) {
 hipError_t gemm(const GemmDesc& d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.batch <= 0) return hipSuccess;
   if (d.sym && (d.M != d.N || d.beta != 0.0)) return hipErrorInvalidValue;
+  // split K: partial products of type double, packed M x N, summed into C (whose rows must be packed)
+  if (d.ksplit > 1 && (!d.part || d.typeC != GF64 || d.ldc != d.N || d.alpha != 1.0 || d.beta != 0.0))
+    return hipErrorInvalidValue;
   const int code = (d.typeA << 3) | (d.typeB << 2) | (d.typeC << 1) | d.acc;
   // float32 products with K-major operands on 128 x 128 tiles (2.19 ms for the 64k half's C Q
   // against 2.57 ms on 64 x 64).  Float64 stays on 64 x 64: with the K-major kernel its C Q took

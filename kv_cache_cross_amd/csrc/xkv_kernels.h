@@ -33,6 +33,8 @@ struct GemmDesc {
   int batch;
   int sym;                    // C = A^T A (symmetric, M == N): only tiles on or above the
                               // diagonal are computed, each written at its mirror too
+  int ksplit;                 // > 1: K in that many ranges, their products written to `part`
+  double* part;               // (ksplit x batch x M x N doubles) and summed into C (double, ldc = N)
 };
 hipError_t gemm(const GemmDesc& d, hipStream_t st);
 

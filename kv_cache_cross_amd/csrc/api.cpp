@@ -329,21 +329,26 @@ xkv::GemmDesc gdesc(int M, int N, int K, int ta, int tb, int tA, int tB, int tC,
   } while (0)
 
 // CholeskyQR pass: Q = Y R^-1 with Y^T Y = R^T R (R = L^T).  Y is overwritten.
+// A symmetric k_b x k_b product over K = n: only the tiles on or above the diagonal, mirrored.
+// Those tiles alone leave the device's workgroup slots (4 per compute unit) short of two rounds
+// at the 64k sizes, each tile a long run over K, so K is split into ranges of at least 512 (up to
+// kWSplit) whose partial products (in `part`) are summed in a fixed order.  The split depends on
+// n only, so that a side's result does not depend on how many sides share the call.
+void sym_split(xkv::GemmDesc& g, int n, double* part) {
+  g.sym = 1;
+  const int ks = std::max(1, std::min(kWSplit, n / 512));
+  if (ks > 1) {
+    g.ksplit = ks;
+    g.part = part;
+  }
+}
+
 int cholqr(const CompressPlan& p, const CompressWs& w, int S, void* Y, int tY, void* Q, int tQ, hipStream_t st) {
   using namespace xkv;
   const int n = p.n, kb = p.kb;
   const long nk = (long)n * kb, kk = (long)kb * kb, dstride = (long)p.nblk * 4096;
   GemmDesc wd = gdesc(kb, kb, n, 1, 0, tY, tY, GF64, Y, kb, nk, Y, kb, nk, w.W, kb, kk, 1.0, 0.0, S);
-  wd.sym = 1;   // W = Y^T Y: the upper tiles, mirrored
-  // The upper tiles alone leave the device's workgroup slots (4 per compute unit) short of two
-  // rounds at the 64k sizes, each tile a long run over K: K is split into ranges of at least 512
-  // (up to kWSplit), the ranges' products summed in a fixed order.  The split depends on n only,
-  // so that a side's W does not depend on how many sides share the call.
-  const int ks = std::max(1, std::min(kWSplit, n / 512));
-  if (ks > 1) {
-    wd.ksplit = ks;
-    wd.part = w.Wpart;
-  }
+  sym_split(wd, n, w.Wpart);   // W = Y^T Y
   XKV_K(gemm(wd, st));
   XKV_K(launch_copy_diag(w.W, kb, kk, w.wdiag, kb, kb, S, st));
   for (int jb = 0; jb < p.nblk; ++jb) {
@@ -552,8 +557,12 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   auto rr_matrix = [&](Half& hf, int h, bool first) -> int {
     XKV_K(gemm(gdesc(n, kb, n, 1, 0, GF64, GF64, GF64, hf.w.C64, n, nn, hf.Qa, kb, nk, hf.Ya, kb, nk, 1.0, 0.0,
                      hf.cnt), st));
-    XKV_K(gemm(gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, hf.Qa, kb, nk, hf.Ya, kb, nk, hf.w.H, kb, kk, 1.0, 0.0,
-                     hf.cnt), st));
+    // H = Q^T (C Q) is symmetric up to rounding (the host takes the mean of its triangles): the
+    // upper tiles, mirrored, with K split as for W
+    GemmDesc hd = gdesc(kb, kb, n, 1, 0, GF64, GF64, GF64, hf.Qa, kb, nk, hf.Ya, kb, nk, hf.w.H, kb, kk, 1.0, 0.0,
+                        hf.cnt);
+    sym_split(hd, n, hf.w.Wpart);
+    XKV_K(gemm(hd, st));
     XKV_HIP(hipMemcpyAsync(hH + (size_t)hf.s0 * kk, hf.w.H, (size_t)hf.cnt * kk * sizeof(double),
                            hipMemcpyDeviceToHost, st));
     XKV_HIP(hipMemcpyAsync(hinfo + hf.s0, hf.w.info, hf.cnt * sizeof(int), hipMemcpyDeviceToHost, st));

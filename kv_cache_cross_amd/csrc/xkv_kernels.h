@@ -31,7 +31,7 @@ struct GemmDesc {
   void* C; long ldc, sC;
   double alpha, beta;
   int batch;
-  int sym;                    // C = A^T A (symmetric, M == N): only tiles on or above the
+  int sym;                    // C symmetric (M == N, e.g. A^T A): only tiles on or above the
                               // diagonal are computed, each written at its mirror too
   int ksplit;                 // > 1: K in that many ranges, their products written to `part`
   double* part;               // (ksplit x batch x M x N doubles) and summed into C (double, ldc = N)

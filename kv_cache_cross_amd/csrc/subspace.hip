@@ -16,11 +16,13 @@ namespace {
 constexpr int NB = 64;
 
 // One workgroup per side: load the nb x nb diagonal block of W at (j0, j0) and factor it as
-// L L^T with L^-1 alongside, in LDS.  The elimination runs as L~ D L~^T (L~ unit lower): step k
-// takes the pivot d_k = a[k][k] and subtracts a[i][k] a[j][k] / d_k from the trailing lower
-// triangle, leaving column k unscaled (a[i][k] = l~_ik d_k), and X = L~^-1 comes from the same
-// sweep (row i of X loses l~_ik times row k).  A step reads only column k, the pivot and row
-// k of X, none of which it writes, so one barrier per step suffices; every thread takes the
+// L L^T with L^-1 alongside.  The elimination runs as L~ D L~^T (L~ unit lower): step k takes
+// the pivot d_k = a[k][k] and subtracts a[i][k] a[j][k] / d_k from the trailing lower triangle,
+// leaving column k unscaled (a[i][k] = l~_ik d_k), and X = L~^-1 comes from the same sweep (row
+// i of X loses l~_ik times row k).  The block lives in registers: a 16 x 16 thread grid, thread
+// (ti, tj) holding rows ti + 16 a and columns tj + 16 b (a, b < 4) of both a and X.  At step k
+// the threads holding column k of a and row k of X put them in LDS (two buffers used in turn,
+// so one barrier per step), and every thread updates its 4 x 4 pieces from them, taking the
 // pivot decision itself.  At the end L = a D^-1/2 below the diagonal with sqrt(d) on it, and
 // L^-1 = D^-1/2 X.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long ldw, long sW,
@@ -28,8 +30,8 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
                                                          double* Dinv, long sD, int j0, int nb,
                                                          const double* wdiag, long sDiag, int clamp,
                                                          int* info) {
-  __shared__ double a[NB][NB + 1];
-  __shared__ double inv[NB][NB + 1];
+  __shared__ double colb[2][NB];   // column k of a
+  __shared__ double rowb[2][NB];   // row k of X
   __shared__ double floor_s[NB];   // the pivots' breakdown floors
   __shared__ double piv_s[NB];     // the pivots taken
   __shared__ double rs_s[NB], sq_s[NB];
@@ -39,44 +41,76 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
   const double* w = W + side * sW + (long)j0 * ldw + j0;
   if (tid == 0) bad = 0;
   if (tid < nb) floor_s[tid] = 1e-14 * wdiag[side * sDiag + j0 + tid];
-  for (int i = ti; i < NB; i += 16)
-    for (int j = tj; j < NB; j += 16) {
-      a[i][j] = (i < nb && j < nb && j <= i) ? w[(long)i * ldw + j] : 0.0;
-      inv[i][j] = (i == j) ? 1.0 : 0.0;
+  double A[4][4], X[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = ti + 16 * a, j = tj + 16 * b;
+      A[a][b] = (i < nb && j < nb && j <= i) ? w[(long)i * ldw + j] : 0.0;
+      X[a][b] = i == j ? 1.0 : 0.0;
     }
   __syncthreads();
-  for (int k = 0; k < nb; ++k) {
-    // The pivot is the squared distance of column j0+k of Y from the span of the previous
-    // columns.  Below 1e-14 of the column's squared norm it is either a breakdown (float64
-    // sweeps: reported) or, with `clamp` (float32 sweeps, whose Y carries float32 noise),
-    // raised to that floor, which damps the near-dependent direction instead of amplifying
-    // noise.
-    double piv = a[k][k];
-    const double floor_k = floor_s[k];
-    bool brk = false;
-    if (!isfinite(piv)) {
-      brk = true;
-      piv = 1.0;
-    } else if (!(piv > floor_k)) {
-      if (clamp && floor_k > 0.0) {
-        piv = floor_k;
-      } else {
-        brk = true;
-        piv = 1.0;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int k = 16 * kb + kk, par = kk & 1;
+      if (k < nb) {
+        if (tj == kk) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) colb[par][ti + 16 * a] = A[a][kb];
+        }
+        if (ti == kk) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) rowb[par][tj + 16 * b] = X[kb][b];
+        }
+        __syncthreads();
+        // The pivot is the squared distance of column j0+k of Y from the span of the previous
+        // columns.  Below 1e-14 of the column's squared norm it is either a breakdown (float64
+        // sweeps: reported) or, with `clamp` (float32 sweeps, whose Y carries float32 noise),
+        // raised to that floor, which damps the near-dependent direction instead of
+        // amplifying noise.
+        double piv = colb[par][k];
+        const double floor_k = floor_s[k];
+        bool brk = false;
+        if (!isfinite(piv)) {
+          brk = true;
+          piv = 1.0;
+        } else if (!(piv > floor_k)) {
+          if (clamp && floor_k > 0.0) {
+            piv = floor_k;
+          } else {
+            brk = true;
+            piv = 1.0;
+          }
+        }
+        if (tid == 0) {
+          piv_s[k] = piv;
+          if (brk) bad = 1;
+        }
+        const double rdk = 1.0 / piv;
+        double cj[4], xr[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          cj[b] = colb[par][tj + 16 * b];
+          xr[b] = rowb[par][tj + 16 * b];
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int i = ti + 16 * a;
+          const double lik = i > k ? colb[par][i] * rdk : 0.0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int j = tj + 16 * b;
+            if (j > k && j <= i) A[a][b] -= lik * cj[b];
+            X[a][b] -= lik * xr[b];   // row k of X is zero past column k
+          }
+        }
       }
     }
-    if (tid == 0) {
-      piv_s[k] = piv;
-      if (brk) bad = 1;
-    }
-    const double rdk = 1.0 / piv;
-    for (int i = k + 1 + ti; i < nb; i += 16) {
-      const double lik = a[i][k] * rdk;
-      for (int j = k + 1 + tj; j <= i; j += 16) a[i][j] -= lik * a[j][k];
-      for (int c = tj; c <= k; c += 16) inv[i][c] -= lik * inv[k][c];
-    }
-    __syncthreads();
   }
+  __syncthreads();
   if (tid < nb) {
     const double sq = sqrt(piv_s[tid]);
     sq_s[tid] = sq;
@@ -85,11 +119,14 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(const double* W, long l
   __syncthreads();
   double* l = L + side * sL + (long)j0 * ldl + j0;
   double* dv = Dinv + side * sD;
-  for (int i = ti; i < nb; i += 16)
-    for (int j = tj; j < nb; j += 16)
-      l[(long)i * ldl + j] = j < i ? a[i][j] * rs_s[j] : (j == i ? sq_s[j] : 0.0);
-  for (int i = ti; i < NB; i += 16)
-    for (int j = tj; j < NB; j += 16) dv[i * NB + j] = (i < nb && j < nb && j <= i) ? inv[i][j] * rs_s[i] : 0.0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = ti + 16 * a, j = tj + 16 * b;
+      if (i < nb && j < nb) l[(long)i * ldl + j] = j < i ? A[a][b] * rs_s[j] : (j == i ? sq_s[j] : 0.0);
+      dv[i * NB + j] = (i < nb && j < nb && j <= i) ? X[a][b] * rs_s[i] : 0.0;
+    }
   if (tid == 0 && bad) info[side] = 1;
 }
 

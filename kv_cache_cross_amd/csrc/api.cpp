@@ -179,6 +179,7 @@ int xkv_host_eigh(int n, const double* H, int nvec, double* w, double* Z) {
   xkv_eigh_scratch_release(&helper);
   if (rc == 0) std::memcpy(w, all.data(), nvec * sizeof(double));
   if (rc == -1) return fail(XKV_EINVAL, "xkv_host_eigh: out of host memory");
+  if (rc == -4) return fail(XKV_ENUMERIC, "xkv_host_eigh: H has an entry that is not finite");
   if (rc != 0) return fail(XKV_ENUMERIC, "xkv_host_eigh: QR iteration did not converge");
   return XKV_OK;
 }
@@ -625,8 +626,10 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
         }
       });
     }
-    for (int i = 0; i < hf.cnt; ++i)
+    for (int i = 0; i < hf.cnt; ++i) {
+      if (erc[i] == -4) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix on side %d", hf.s0 + i);
       if (erc[i]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + i, erc[i]);
+    }
     // The half's log staging: meta (4 per side: first run, first pair, first group, groups) |
     // runs (4 ints each) | groups (2 ints each, room for one per run) | (c, s) pairs.
     long long runs_tot = 0, rot_tot = 0;
@@ -786,8 +789,6 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       for (int i = 0; i < hf.cnt; ++i)
         if (hinfo[hf.s0 + i])
           return fail(XKV_ENUMERIC, "compress: Cholesky breakdown on side %d (rank of X below %d?)", hf.s0 + i, kb);
-      for (size_t i = (size_t)hf.s0 * kk; i < (size_t)(hf.s0 + hf.cnt) * kk; ++i)
-        if (!std::isfinite(hH[i])) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix");
       rc = solve_half(hf, h);
       if (rc) return rc;
       rc = post_work(hf, h);

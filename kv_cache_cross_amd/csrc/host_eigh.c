@@ -65,7 +65,7 @@ static void pair_wait(xkv_eigh_pair* pr) {
 
 /* Row passes of the reduction, over local rows [i0, i1) of their trailing block; a pass
  * that forms a product adds its terms into pacc. */
-enum { JOB_DONE = 0, JOB_SYM, JOB_PRODUCT, JOB_FUSED };
+enum { JOB_DONE = 0, JOB_COPY, JOB_SYM, JOB_PRODUCT, JOB_FUSED };
 typedef struct {
   int n;
   const double* H;
@@ -78,15 +78,22 @@ typedef struct {
 } team;
 
 /* the rows a job covers: all n for the symmetrisation, else the trailing block's size */
-static int job_rows(int job, int n, int k) { return job == JOB_SYM ? n : job == JOB_PRODUCT ? n - k - 1 : n - k - 2; }
+static int job_rows(int job, int n, int k) {
+  return job == JOB_COPY || job == JOB_SYM ? n : job == JOB_PRODUCT ? n - k - 1 : n - k - 2;
+}
+static int job_has_product(int job) { return job == JOB_PRODUCT || job == JOB_FUSED; }
 
 static void job_pass(const team* t, int job, int k, int i0, int i1, double* pacc) {
   const int n = t->n;
   double* A = t->A;
-  if (job == JOB_SYM) {
-    /* the mean of the two triangles */
+  if (job == JOB_COPY) {
+    /* H row by row (it may sit in memory the host reads slowly across rows, such as a
+     * device's pinned staging) */
+    for (int i = i0; i < i1; ++i) memcpy(A + (size_t)i * n, t->H + (size_t)i * n, (size_t)n * sizeof(double));
+  } else if (job == JOB_SYM) {
+    /* the lower triangle takes the mean of the two triangles (the upper one is read only) */
     for (int i = i0; i < i1; ++i)
-      for (int j = 0; j < n; ++j) A[(size_t)i * n + j] = 0.5 * (t->H[(size_t)i * n + j] + t->H[(size_t)j * n + i]);
+      for (int j = 0; j < i; ++j) A[(size_t)i * n + j] = 0.5 * (A[(size_t)i * n + j] + A[(size_t)j * n + i]);
   } else if (job == JOB_PRODUCT) {
     /* pacc += A22 v from the lower triangle (rows and columns k+1..) */
     const double* v = t->V + (size_t)k * n;
@@ -152,14 +159,14 @@ static void run_job(const team* t, int job, int k, double* p) {
     job_pass(t, job, k, 0, rows, p);
     return;
   }
-  const int split = job == JOB_SYM ? rows / 2 : (int)(rows * 0.7071067811865476);
+  const int split = job == JOB_COPY ? rows / 2 : (int)(rows * 0.7071067811865476);   /* rows, or a triangle */
   t->pr->job = job;
   t->pr->k = k;
   t->pr->split = split;
   pair_wait(t->pr);   /* the job is published */
   job_pass(t, job, k, 0, split, p);
   pair_wait(t->pr);   /* both halves done */
-  if (job != JOB_SYM)
+  if (job_has_product(job))
     for (int i = 0; i < rows; ++i) p[i] += t->p1[i];
 }
 
@@ -170,7 +177,7 @@ static void worker_loop(const team* t) {
     const int job = t->pr->job, k = t->pr->k, split = t->pr->split;
     if (job == JOB_DONE) return;
     const int rows = job_rows(job, t->n, k);
-    if (job != JOB_SYM) memset(t->p1, 0, (size_t)rows * sizeof(double));
+    if (job_has_product(job)) memset(t->p1, 0, (size_t)rows * sizeof(double));
     job_pass(t, job, k, split, rows, t->p1);
     pair_wait(t->pr);
   }
@@ -627,7 +634,8 @@ static double* slot(double* buf, int n, int s) { return buf + 2 * (size_t)n * n 
  * it): repeated solves in several threads then neither map nor fault pages.  With pr set the
  * calling thread leads a pair whose worker runs worker_side; the worker's product terms are in
  * helper->buf, read only after the start barrier.  Returns 0 on success, -1 on
- * allocation failure, -2 if the QR iteration did not converge. */
+ * allocation failure, -2 if the QR iteration did not converge, -4 if H (the mean of its
+ * triangles) has an entry that is not finite. */
 static int values_impl(int n, const double* H, int nvec, double* w, xkv_eigh_scratch* sc, xkv_eigh_pair* pr,
                        const xkv_eigh_scratch* helper) {
   const size_t need = 2 * (size_t)n * n + S_SLOTS * (size_t)n;
@@ -659,12 +667,21 @@ static int values_impl(int n, const double* H, int nvec, double* w, xkv_eigh_scr
   rotlog* log = &sc->log;
   log->n = 0;
   const team t = {n, H, A, V, tw, pr, pr ? helper->buf : NULL, slot(sc->buf, n, S_CB)};
+  run_job(&t, JOB_COPY, 0, NULL);
   run_job(&t, JOB_SYM, 0, NULL);
-  tridiagonalize(&t, d, e, V, beta, tp, tw, tcol);
+  int finite = 1;
+  for (int i = 0; i < n && finite; ++i)
+    for (int j = 0; j <= i; ++j)
+      if (!isfinite(A[(size_t)i * n + j])) {
+        finite = 0;
+        break;
+      }
+  if (finite) tridiagonalize(&t, d, e, V, beta, tp, tw, tcol);
   if (pr) {
     pr->job = JOB_DONE;
     pair_wait(pr);   /* the worker leaves */
   }
+  if (!finite) return -4;
 
   {
     const double eps = 2.220446049250313e-16;

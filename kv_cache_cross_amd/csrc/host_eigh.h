@@ -27,7 +27,8 @@ typedef struct xkv_eigh_scratch {
 
 /* All n eigenvalues of symmetric H (n x n, row-major), descending, into w; the eigenvectors
  * of the nvec largest as the columns of Z (n x nvec, row-major).  Returns 0 on success,
- * -1 on allocation failure, -2 if the QR iteration did not converge, -3 on bad sizes. */
+ * -1 on allocation failure, -2 if the QR iteration did not converge, -3 on bad sizes, -4 if H
+ * has an entry that is not finite. */
 int xkv_eigh_desc_scratch(int n, const double* H, int nvec, double* w, double* Z, xkv_eigh_scratch* sc);
 /* The same in two phases.  xkv_eigh_values: all eigenvalues into w, the state for the vectors
  * kept in sc (same return codes).  xkv_eigh_vectors: columns [j0, j1) of Z (n x nvec,

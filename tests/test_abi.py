@@ -176,6 +176,17 @@ def test_host_eigh_skipped_reflectors(order):
     np.testing.assert_allclose(H @ Z, Z * w, atol=1e-11 * abs(ref_w[0]))
 
 
+def test_host_eigh_rejects_non_finite():
+    H = np.eye(300)
+    H[7, 3] = np.nan
+    with pytest.raises(xk.XkvError, match="not finite"):
+        xk.host_eigh(H, 10)
+    H = np.eye(40)
+    H[39, 39] = np.inf
+    with pytest.raises(xk.XkvError, match="not finite"):
+        xk.host_eigh(H, 4)
+
+
 def test_host_eigh_rejects_bad_args():
     with pytest.raises(xk.XkvError):
         xk.host_eigh(np.eye(4), 5)

@@ -234,6 +234,7 @@ struct CompressWs {
   double* H; double* Z; double* Vr;
   double* Rf; int* pos; double* Wb;   // packed reflector blocks, wanted positions, block products
   double* Zs;                         // working memory of the rotation kernel
+  double* Zseg; double* Zsegs;        // with the log in pieces: each piece's product and working memory
   double* Wpart;                      // partial products of W = Y^T Y (kWSplit per side)
   double* wdiag;
   double* YZ; double* theta; double* res2;
@@ -262,6 +263,9 @@ CompressWs carve_compress(void* ws, const CompressPlan& p, int S) {
   w.pos = c.take<int>((size_t)S * p.r);
   w.Wb = c.take<double>((size_t)S * 2 * XKV_EIGH_NBG * p.r);
   w.Zs = c.take<double>((size_t)S * xkv::ritz_scratch_doubles(p.kb, p.r));
+  const int parts = xkv::ritz_parts(p.kb);
+  w.Zseg = parts > 1 ? c.take<double>((size_t)S * parts * kk) : nullptr;
+  w.Zsegs = parts > 1 ? c.take<double>((size_t)S * parts * xkv::ritz_scratch_doubles(p.kb, p.kb)) : nullptr;
   w.Wpart = c.take<double>((size_t)S * kWSplit * kk);
   w.Vr = c.take<double>((size_t)S * p.n * p.r);
   w.wdiag = c.take<double>((size_t)S * p.kb);
@@ -295,6 +299,9 @@ CompressWs shift_compress_ws(const CompressWs& w, const CompressPlan& p, int s0)
   v.pos += (size_t)s0 * p.r;
   v.Wb += (size_t)s0 * 2 * XKV_EIGH_NBG * p.r;
   v.Zs += (size_t)s0 * xkv::ritz_scratch_doubles(p.kb, p.r);
+  const int parts = xkv::ritz_parts(p.kb);
+  if (v.Zseg) v.Zseg += (size_t)s0 * parts * kk;
+  if (v.Zsegs) v.Zsegs += (size_t)s0 * parts * xkv::ritz_scratch_doubles(p.kb, p.kb);
   v.Wpart += (size_t)s0 * kWSplit * kk;
   v.Vr += s0 * nr;
   v.wdiag += (size_t)s0 * p.kb;
@@ -580,8 +587,12 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   // into the half's pinned staging, its reflector blocks and wanted positions into ctx->pin.
   const RitzGrouping rg = ritz_grouping();
   const int run_cap = rg.run_cap;
+  // With the log in P > 1 pieces, side i of a half is P virtual sides i P + q of the rotation
+  // kernel: piece 0 applied to the wanted unit vectors (padded to k_b columns), piece q > 0 to
+  // the identity, each with meta of its own and k_b positions in the staging.
+  const int P = ritz_parts(kb);
   std::vector<long long> meta(4 * (size_t)S, 0);
-  size_t log_bytes[2] = {0, 0};
+  size_t log_bytes[2] = {0, 0}, pos_off[2] = {0, 0};
   long long runs_total[2] = {0, 0};
   auto run_threads = [&](int nthr, int ntask, auto&& task) {
     if (nthr <= 1) {
@@ -630,8 +641,9 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       if (erc[i] == -4) return fail(XKV_ENUMERIC, "compress: non-finite Rayleigh-Ritz matrix on side %d", hf.s0 + i);
       if (erc[i]) return fail(XKV_ENUMERIC, "compress: host eigensolve failed on side %d (code %d)", hf.s0 + i, erc[i]);
     }
-    // The half's log staging: meta (4 per side: first run, first pair, first group, groups) |
-    // runs (4 ints each) | groups (2 ints each, room for one per run) | (c, s) pairs.
+    // The half's log staging: meta (4 per side or virtual side: first run, first pair, first
+    // group, groups) | runs (4 ints each) | groups (2 ints each, room for one per run) | (c, s)
+    // pairs | with P > 1, the virtual sides' positions (k_b each).
     long long runs_tot = 0, rot_tot = 0;
     for (int i = 0; i < hf.cnt; ++i) {
       const int s = hf.s0 + i;
@@ -641,8 +653,10 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       runs_tot += nruns[i];
       rot_tot += ctx->eig_side[2 * s].log.n;
     }
-    const size_t meta_b = 32 * (size_t)hf.cnt, runs_b = 16 * (size_t)runs_tot, grp_b = 8 * (size_t)runs_tot;
-    const size_t need = meta_b + runs_b + grp_b + 16 * (size_t)rot_tot;
+    const size_t meta_b = 32 * (size_t)P * hf.cnt, runs_b = 16 * (size_t)runs_tot, grp_b = 8 * (size_t)runs_tot;
+    const size_t pos_b = P > 1 ? 4 * (size_t)P * hf.cnt * kb : 0;
+    const size_t need = meta_b + runs_b + grp_b + 16 * (size_t)rot_tot + pos_b;
+    pos_off[h] = meta_b + runs_b + grp_b + 16 * (size_t)rot_tot;
     if (ctx->lpin_bytes[h] < need) {
       // no copy reads this half's staging now: each compression round ends with a stream
       // synchronisation, and an earlier call's copies are waited for on entry
@@ -658,10 +672,23 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       const int s = hf.s0 + i;
       int* rs = (int*)(lp + meta_b) + 4 * meta[4 * s];
       xkv_eigh_pack_log(&ctx->eig_side[2 * s], run_cap, rs, (double*)(lp + meta_b + runs_b + grp_b) + 2 * meta[4 * s + 1]);
-      meta[4 * s + 3] = xkv_eigh_group_runs(rs, nruns[i], rg.per_group, rg.spread, rg.max_steps,
-                                            (int*)(lp + meta_b + runs_b) + 2 * meta[4 * s + 2]);
+      const int* gs = (int*)(lp + meta_b + runs_b) + 2 * meta[4 * s + 2];
+      meta[4 * s + 3] = xkv_eigh_group_runs(rs, nruns[i], rg.per_group, rg.spread, rg.max_steps, (int*)gs);
+      if (P > 1) {
+        int bnd[5];
+        xkv_eigh_split_groups(rs, gs, (int)meta[4 * s + 3], rg.overhead, P, bnd);
+        long long* vm = (long long*)lp + 4 * (size_t)i * P;
+        int* vp = (int*)(lp + pos_off[h]) + (size_t)i * P * kb;
+        for (int q = 0; q < P; ++q) {
+          vm[4 * q] = meta[4 * s];
+          vm[4 * q + 1] = meta[4 * s + 1];
+          vm[4 * q + 2] = meta[4 * s + 2] + bnd[q];
+          vm[4 * q + 3] = bnd[q + 1] - bnd[q];
+          for (int j = 0; j < kb; ++j) vp[(size_t)q * kb + j] = (q == 0 && j < r) ? hPos[(size_t)s * r + j] : j;
+        }
+      }
     });
-    std::memcpy(lp, meta.data() + 4 * (size_t)hf.s0, meta_b);
+    if (P == 1) std::memcpy(lp, meta.data() + 4 * (size_t)hf.s0, meta_b);
     log_bytes[h] = need;
     runs_total[h] = runs_tot;
     for (int i = 0; i < hf.cnt; ++i)
@@ -670,13 +697,17 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
   };
   // The Ritz vectors Z of a half on the device (the rotations of each side's QR iteration applied
   // to its wanted unit vectors, then its reflectors, last block first, as S2 -= Y (T (Y^T S2))),
-  // then V_r = Q Z and the residual of every Ritz pair.
+  // then V_r = Q Z and the residual of every Ritz pair.  With the log in P pieces, piece q's
+  // product S_q comes out of the rotation kernel as a k_b x k_b matrix (piece 0 applied to the
+  // wanted unit vectors, its first r columns used) and Z = S_{P-1} ... S_1 S_0 E by P - 1 float64
+  // products, the last of them written to Z.
   auto post_work = [&](Half& hf, int h) -> int {
     const int NBG = XKV_EIGH_NBG;
     XKV_HIP(hipMemcpyAsync(hf.w.Rf, hRefl + (size_t)hf.s0 * refl, (size_t)hf.cnt * refl * sizeof(double),
                            hipMemcpyHostToDevice, st));
-    XKV_HIP(hipMemcpyAsync(hf.w.pos, hPos + (size_t)hf.s0 * r, (size_t)hf.cnt * r * sizeof(int), hipMemcpyHostToDevice,
-                           st));
+    if (P == 1)
+      XKV_HIP(hipMemcpyAsync(hf.w.pos, hPos + (size_t)hf.s0 * r, (size_t)hf.cnt * r * sizeof(int),
+                             hipMemcpyHostToDevice, st));
     if (ctx->ldev_bytes[h] < log_bytes[h]) {
       // the previous reader of this half's device log finished before its round's synchronisation
       if (ctx->ldev[h]) XKV_HIP(hipFree(ctx->ldev[h]));
@@ -688,11 +719,33 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
     }
     XKV_HIP(hipMemcpyAsync(ctx->ldev[h], ctx->lpin[h], log_bytes[h], hipMemcpyHostToDevice, st));
     const char* ld = (const char*)ctx->ldev[h];
-    const size_t meta_b = 32 * (size_t)hf.cnt;
+    const size_t meta_b = 32 * (size_t)P * hf.cnt;
     const size_t runs_tot = (size_t)runs_total[h];
-    XKV_K(launch_ritz_rotate((const int4*)(ld + meta_b), (const double2*)(ld + meta_b + 24 * runs_tot),
-                             (const int2*)(ld + meta_b + 16 * runs_tot), (const long long*)ld, hf.w.pos, kb, r,
-                             hf.w.Z, (long)kb * r, hf.w.Zs, ritz_scratch_doubles(kb, r), hf.cnt, st));
+    const int4* d_runs = (const int4*)(ld + meta_b);
+    const int2* d_groups = (const int2*)(ld + meta_b + 16 * runs_tot);
+    const double2* d_cs = (const double2*)(ld + meta_b + 24 * runs_tot);
+    if (P == 1) {
+      XKV_K(launch_ritz_rotate(d_runs, d_cs, d_groups, (const long long*)ld, hf.w.pos, kb, r, hf.w.Z, (long)kb * r,
+                               hf.w.Zs, ritz_scratch_doubles(kb, r), hf.cnt, st));
+    } else {
+      XKV_K(launch_ritz_rotate(d_runs, d_cs, d_groups, (const long long*)ld, (const int*)(ld + pos_off[h]), kb, kb,
+                               hf.w.Zseg, kk, hf.w.Zsegs, ritz_scratch_doubles(kb, kb), P * hf.cnt, st));
+      // side i's piece q at Zseg + (i P + q) k_b^2; the products alternate between Z (ld r) and
+      // piece 0's memory (ld r once piece 0 has been read), ending in Z
+      const long sP = (long)P * kk;
+      const double* in = hf.w.Zseg;
+      long ld_in = kb, s_in = sP;
+      for (int q = 1; q < P; ++q) {
+        const bool into_z = (P - 1 - q) % 2 == 0;
+        double* out = into_z ? hf.w.Z : hf.w.Zseg;
+        const long s_out = into_z ? (long)kb * r : sP;
+        XKV_K(gemm(gdesc(kb, r, kb, 0, 0, GF64, GF64, GF64, hf.w.Zseg + (size_t)q * kk, kb, sP, in, ld_in, s_in, out, r,
+                         s_out, 1.0, 0.0, hf.cnt), st));
+        in = out;
+        ld_in = r;
+        s_in = s_out;
+      }
+    }
     const int nref = kb - 2;
     const int nblk = nref > 0 ? (nref + NBG - 1) / NBG : 0;
     const size_t ytot = refl - (size_t)nblk * NBG * NBG;

@@ -818,6 +818,19 @@ __attribute__((visibility("hidden"))) void xkv_eigh_pack_log(const xkv_eigh_scra
   }
 }
 
+/* Fronts a device sweeps for group g = (q0, nb): from the highest start front (run b starts at
+ * its top row minus b) to the lowest end front. */
+static int group_fronts(const int* runs, const int* g) {
+  int f0 = 0, f1 = 0;
+  for (int b = 0; b < g[1]; ++b) {
+    const int* R = runs + 4 * (g[0] - b);
+    const int ab = R[2] - b, zb = R[2] - (R[1] - R[0]) - b;
+    f0 = b ? (ab > f0 ? ab : f0) : ab;
+    f1 = b ? (zb < f1 ? zb : f1) : zb;
+  }
+  return f0 - f1 + 1;
+}
+
 /* Groups of up to B runs that a device applies together, in the order they are applied (the
  * log's last run first): a group is runs q0, q0 - 1, ..., q0 - nb + 1, run b of it starting when
  * the front row is its top row minus b and ending when the front is its lowest row minus b.  A
@@ -849,6 +862,26 @@ __attribute__((visibility("hidden"))) int xkv_eigh_group_runs(const int* runs, i
     q -= nb;
   }
   return ng;
+}
+
+/* Cut a side's groups (in the order they are applied) into `parts` consecutive pieces of about
+ * equal work: group q costs the fronts it sweeps (from its runs' first to last front, as a
+ * device applies it) plus `overhead`.  bounds[p] is piece p's first group, bounds[parts] =
+ * ngroups; pieces may be empty. */
+__attribute__((visibility("hidden"))) void xkv_eigh_split_groups(const int* runs, const int* groups, int ngroups,
+                                                                  int overhead, int parts, int* bounds) {
+  long total = 0;
+  for (int q = 0; q < ngroups; ++q) total += overhead + group_fronts(runs, groups + 2 * q);
+  bounds[0] = 0;
+  long acc = 0;
+  int q = 0;
+  for (int p = 1; p < parts; ++p) {
+    /* the first group whose work before it reaches p / parts of the total */
+    const long target = (total * p + parts - 1) / parts;
+    while (q < ngroups && acc < target) acc += overhead + group_fronts(runs, groups + 2 * q++);
+    bounds[p] = q;
+  }
+  bounds[parts] = ngroups;
 }
 
 __attribute__((visibility("hidden"))) size_t xkv_eigh_refl_doubles(int n) {

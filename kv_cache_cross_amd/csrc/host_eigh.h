@@ -73,6 +73,11 @@ void xkv_eigh_pack_log(const xkv_eigh_scratch* st, int maxlen, int* runs, double
  * lie within `spread` rows of one another and that span at most maxsteps rows, as (first run,
  * count) pairs, at most nruns of them; returns their number. */
 int xkv_eigh_group_runs(const int* runs, int nruns, int B, int spread, int maxsteps, int* groups);
+/* Pieces of a side's groups for a device that applies them in parallel (piece 0 to the wanted
+ * unit vectors, each later piece to the identity, the results then multiplied together):
+ * bounds[0..parts] are the pieces' first groups (bounds[parts] = ngroups), cut where the fronts
+ * swept (plus `overhead` per group) reach equal shares. */
+void xkv_eigh_split_groups(const int* runs, const int* groups, int ngroups, int overhead, int parts, int* bounds);
 size_t xkv_eigh_refl_doubles(int n);
 void xkv_eigh_pack_reflectors(const xkv_eigh_scratch* st, double* out);
 void xkv_eigh_positions(const xkv_eigh_scratch* st, int* pos);

@@ -501,7 +501,19 @@ hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const int2* g
   return hipGetLastError();
 }
 
-RitzGrouping ritz_grouping() { return RitzGrouping{kRunCap, kB, kSpread, kRunCap + kSpread}; }
+// A group's pair staging, with its one exposed memory latency, costs about as much as this many
+// fronts (the weight of a group when a log is cut into pieces of equal work).
+constexpr int kGroupOverhead = 32;
+RitzGrouping ritz_grouping() { return RitzGrouping{kRunCap, kB, kSpread, kRunCap + kSpread, kGroupOverhead}; }
+
+// One workgroup applies a log to 64 columns with one wave whose instructions issue one after
+// another, so a half's 8 sides of r = 512 columns keep 64 of the 256 compute units busy for the
+// whole log.  The log is therefore cut into pieces applied side by side (the first to the wanted
+// unit vectors, the others to the identity) and multiplied together afterwards: 4 pieces up to
+// k_b = 1024 (8 sides of k_b = 768 give 384 single-wave workgroups, two per compute unit by their
+// LDS), 2 above it; none below k_b = 256, where the log is short.  The count depends on k_b
+// alone, so that a side's result does not depend on how many sides share its call.
+int ritz_parts(int kb) { return kb < 256 ? 1 : (kb <= 1024 ? 4 : 2); }
 
 long ritz_scratch_doubles(int n, int r) { return (long)((r + 63) / 64) * (kPadLo + n + kPadHi) * 64; }
 

@@ -61,11 +61,14 @@ hipError_t launch_trace(const double* C, long sC, int n, int n_sides, double* tr
 // ritz_scratch_doubles(n, r) doubles per side (side stride scr_s).
 struct RitzGrouping {
   int run_cap, per_group, spread, max_steps;
+  int overhead;   // a group's fixed cost in fronts, for cutting a log into pieces of equal work
 };
 hipError_t launch_ritz_rotate(const int4* runs, const double2* cs, const int2* groups, const long long* meta,
                               const int* pos, int n, int r, double* Z, long zs, double* scr, long scr_s, int n_sides,
                               hipStream_t st);
 RitzGrouping ritz_grouping();
+// Pieces (1, 2 or 4) of a side's rotation log that the vector phase applies side by side.
+int ritz_parts(int kb);
 long ritz_scratch_doubles(int n, int r);
 // res2[s*r + i] = || YZ[:, i] - theta[s*r + i] * Vr[:, i] ||^2 (n x r float64 per side, side stride n*r).
 hipError_t launch_ritz_residual(const double* YZ, const double* Vr, const double* theta, int n, int r,

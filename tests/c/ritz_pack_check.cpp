@@ -3,8 +3,11 @@
 // reflector blocks and the wanted positions as a compression does, and applies them the way
 // the rotation kernel and the reflector products do (the same grouping, wavefront schedule,
 // identity padding and chunking, with every row and LDS index bounds-checked), then compares
-// the result with the host's own eigenvectors.  The kernel's constants come in as -D flags.
-//   usage: ritz_pack_check n r power [run_cap] [spread]
+// the result with the host's own eigenvectors.  With parts > 1 the groups are cut into pieces as
+// a compression cuts them: piece 0 applied to the wanted unit vectors, every later piece to the
+// identity, and the pieces' products multiplied together before the reflectors.  The kernel's
+// constants come in as -D flags.
+//   usage: ritz_pack_check n r power [run_cap] [spread] [parts]
 #include <algorithm>
 #include <climits>
 #include <cmath>
@@ -28,6 +31,8 @@ int main(int argc, char** argv) {
   const double pw = std::atof(argv[3]);
   const int run_cap = argc > 4 ? std::atoi(argv[4]) : KRUNCAP;
   const int spread = argc > 5 ? std::atoi(argv[5]) : KSPREAD;
+  const int parts = argc > 6 ? std::atoi(argv[6]) : 1;
+  if (parts < 1 || parts > 4) bail("parts", parts);
   const int kB = KB, CH = KCH, kSlot = spread + KRUNCAP + spread + 2 * KCH, kPadLo = 2 * KCH + KB, kPadHi = KB;
   // H = G diag(k^pw) G^T, symmetric positive semi-definite with a graded spectrum
   std::mt19937_64 g(n * 1000003ull + r);
@@ -65,9 +70,18 @@ int main(int argc, char** argv) {
     next -= groups[2 * gq + 1];
     if (gq + 1 == ng && next != -1) bail("groups cover the runs", next);
   }
+  // the pieces: bounds[q] .. bounds[q + 1] - 1 are piece q's groups, together every group once
+  std::vector<int> bounds(parts + 1, 0);
+  if (parts > 1) xkv_eigh_split_groups(runs.data(), groups.data(), ng, KOVERHEAD, parts, bounds.data());
+  else bounds[1] = ng;
+  if (bounds[0] != 0 || bounds[parts] != ng) bail("pieces cover the groups", bounds[parts]);
+  for (int q = 0; q < parts; ++q)
+    if (bounds[q + 1] < bounds[q]) bail("piece bounds", q);
   const int rows = kPadLo + n + kPadHi;
   std::vector<double> Zd((size_t)n * r), csc((size_t)kB * kSlot), css((size_t)kB * kSlot), sr(rows);
-  for (int j = 0; j < r; ++j) {
+  // column(start, g0, g1, out): the unit vector at row `start` with groups [g0, g1) applied, out[i]
+  // for rows i < n at stride `ldo`
+  auto column = [&](int start, int g_begin, int g_end, double* out, long ldo) {
     auto zl = [&](int row) {
       if (row + kPadLo < 0 || row + kPadLo >= rows) bail("row load", row);
       return sr[row + kPadLo];
@@ -76,8 +90,8 @@ int main(int argc, char** argv) {
       if (row + kPadLo < 0 || row + kPadLo >= rows) bail("row store", row);
       sr[row + kPadLo] = v;
     };
-    for (int i = -kPadLo; i < n + kPadHi; ++i) zs(i, i == pos[j] ? 1.0 : 0.0);
-    for (int gq = 0; gq < ng; ++gq) {
+    for (int i = -kPadLo; i < n + kPadHi; ++i) zs(i, i == start ? 1.0 : 0.0);
+    for (int gq = g_begin; gq < g_end; ++gq) {
       const int gx = groups[2 * gq], gy = groups[2 * gq + 1];
       std::vector<int> kt(kB), len(kB, 0);
       int f0 = INT_MIN, f1 = INT_MAX;
@@ -144,7 +158,20 @@ int main(int argc, char** argv) {
       }
       for (int b = 0; b < kB; ++b) zs(f1 + b, y[b]);
     }
-    for (int i = 0; i < n; ++i) Zd[(size_t)i * r + j] = zl(i);
+    for (int i = 0; i < n; ++i) out[(size_t)i * ldo] = zl(i);
+  };
+  for (int j = 0; j < r; ++j) column(pos[j], bounds[0], bounds[1], Zd.data() + j, r);
+  // Z <- S_q Z for the later pieces, S_q = piece q applied to the identity
+  std::vector<double> Sq((size_t)n * n), Zt((size_t)n * r);
+  for (int q = 1; q < parts; ++q) {
+    for (int j = 0; j < n; ++j) column(j, bounds[q], bounds[q + 1], Sq.data() + j, n);
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < r; ++j) {
+        double t = 0;
+        for (int k = 0; k < n; ++k) t += Sq[(size_t)i * n + k] * Zd[(size_t)k * r + j];
+        Zt[(size_t)i * r + j] = t;
+      }
+    Zd.swap(Zt);
   }
   // the reflector blocks, last first: S2 -= Y (T (Y^T S2))
   const int NBG = XKV_EIGH_NBG, nref = n - 2;
@@ -176,7 +203,10 @@ int main(int argc, char** argv) {
   for (size_t i = 0; i < Z.size(); ++i) md = std::fmax(md, std::fabs(Z[i] - Zd[i]));
   long full = 0;
   for (int q = 0; q < ng; ++q) full += groups[2 * q + 1] == kB;
-  std::printf("n %d r %d rotations %ld runs %d groups %d full %ld maxdiff %.3g\n", n, r, sc.log.n, nruns, ng, full, md);
+  std::printf("n %d r %d rotations %ld runs %d groups %d full %ld parts %d (first groups", n, r, sc.log.n, nruns, ng,
+              full, parts);
+  for (int q = 0; q < parts; ++q) std::printf(" %d", bounds[q]);
+  std::printf(") maxdiff %.3g\n", md);
   xkv_eigh_scratch_release(&sc);
   return md <= 1e-12 ? 0 : 4;
 }

@@ -23,7 +23,8 @@ CSRC = os.path.join(ROOT, "kv_cache_cross_amd", "csrc")
 def kernel_constants():
     src = open(os.path.join(CSRC, "subspace.hip")).read()
     out = {}
-    for name, key in [("kRunCap", "KRUNCAP"), ("kB", "KB"), ("CH", "KCH"), ("kSpread", "KSPREAD")]:
+    for name, key in [("kRunCap", "KRUNCAP"), ("kB", "KB"), ("CH", "KCH"), ("kSpread", "KSPREAD"),
+                      ("kGroupOverhead", "KOVERHEAD")]:
         m = re.search(r"constexpr int %s = (\d+);" % name, src)
         assert m, name
         out[key] = int(m.group(1))
@@ -55,6 +56,12 @@ def checker(tmp_path_factory):
     ("300", "64", "-0.8", "100", "8"),      # sweeps cut at 100 rotations, groups limited to 8 rows of spread
     ("768", "512", "-1.2"),                 # the 64k workload's Rayleigh-Ritz size
     ("1100", "40", "-1.0"),                 # sweeps longer than the kernel's run cap
+    # the log in pieces (piece 0 on the wanted unit vectors, the others on the identity, multiplied)
+    ("768", "512", "-1.2", "1024", "64", "4"),   # the 64k workload's Rayleigh-Ritz size, as compressed
+    ("1100", "40", "-1.0", "1024", "64", "2"),   # above k_b = 1024: two pieces
+    ("300", "64", "-0.8", "100", "8", "4"),      # short runs, narrow groups
+    ("37", "20", "-0.8", "1024", "64", "4"),     # few groups
+    ("3", "2", "-0.8", "1024", "64", "4"),       # one group: three empty pieces
 ])
 def test_packed_vector_phase_reproduces_host_vectors(checker, args):
     p = subprocess.run([checker, *args], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)

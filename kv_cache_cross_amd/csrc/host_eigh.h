@@ -66,7 +66,7 @@ void xkv_eigh_scratch_release(xkv_eigh_scratch* sc);
  *                       (n - NBG b - 1 rows of NBG), then every block's T (NBG x NBG),
  *                       xkv_eigh_refl_doubles(n) doubles in all;
  *   xkv_eigh_positions  the nvec wanted positions, largest eigenvalue first. */
-enum { XKV_EIGH_NBG = 16 };
+enum { XKV_EIGH_NBG = 64 };
 int xkv_eigh_runs(const xkv_eigh_scratch* st, int maxlen);
 void xkv_eigh_pack_log(const xkv_eigh_scratch* st, int maxlen, int* runs, double* cs);
 /* Groups of up to B consecutive runs (in the order they are applied) whose starts and ends

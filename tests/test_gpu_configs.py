@@ -300,12 +300,14 @@ def test_batch8_g8_sequence_end_to_end(ctx):
 MINI = dict(T=2000, n_layers=4, n_kv_heads=2, n_q_heads=8, rank=128, latent_rank=192, top_k=32)
 
 
-@pytest.mark.parametrize("S", [4, 5])
-def test_compress_two_halves_match_single(ctx, S):
-    # With 4 or more sides a call runs them in two halves (the host solves one half while the
-    # GPU works on the other); S = 5 splits 2 + 3.  Every side must be bit-identical to its
-    # own single-side call, and one side must meet the oracle bars.
-    wl = make_workload("llama16k", device=DEV, **dict(MINI, n_layers=4 * S, n_kv_heads=2))
+@pytest.mark.parametrize("S,rank", [(4, 128), (5, 128), (7, 256)])
+def test_compress_parts_match_single(ctx, S, rank):
+    # With 4 or more sides a call runs them in two halves, the larger first (the host solves
+    # one half while the GPU works on the other): 2 + 2, 3 + 2, 4 + 3.  At rank 256 (k_b = 384)
+    # each side's rotation log is also applied in pieces.  Every side must be bit-identical to
+    # its own single-side call, and one side must meet the oracle bars.
+    extra = dict(rank=rank, latent_rank=max(MINI["latent_rank"], rank + rank // 2))
+    wl = make_workload("llama16k", device=DEV, **dict(MINI, n_layers=4 * S, n_kv_heads=2, **extra))
     c = wl.cfg
     sides, lms = [], []
     for i in range(S):

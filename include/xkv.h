@@ -125,10 +125,12 @@ int xkv_compress_ws_size(const xkv_compress_desc* desc, int n_sides, size_t* byt
  * C: Householder reduction, shared by two threads per side when k_b >= 256 and
  * host threads allow, then implicit QR whose plane rotations are logged) ->
  * the wanted eigenvectors Z_r on the GPU (the logged rotations applied to unit
- * vectors, then the reflectors as compact-WY products) -> V_r = Q Z_r ->
+ * vectors, for k_b >= 256 in 2 or 4 pieces side by side that float64 products
+ * then multiply together, then the reflectors as compact-WY products) -> V_r = Q Z_r ->
  * A = X V_r and the landmarks.  With 4 or more sides the sides go in two
- * halves, so that the GPU steps of the second half run while the host solves
- * the first half's eigenvalues.  Allocates the rotation logs' pinned staging
+ * halves (the larger first), so that the GPU steps of the second half run while
+ * the host solves the first half's eigenvalues.  A side's results do not depend
+ * on how many sides share the call.  Allocates the rotation logs' pinned staging
  * and device copy in the context (kept and grown between calls).
  * Convergence: after each Rayleigh-Ritz round the Ritz residuals
  * r_i = C v_i - theta_i v_i give the estimate

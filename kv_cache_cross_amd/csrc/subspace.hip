@@ -4,8 +4,8 @@
 //   * the Gaussian start block;
 //   * conversion of V_r to the stored Bt = V_r and its transpose;
 //   * the plane rotations of the Rayleigh-Ritz eigensolve's QR iteration applied to the
-//     wanted unit vectors (the first half of its vector phase; the reflectors follow as
-//     GEMMs).
+//     wanted unit vectors, or a piece of them to the identity (the first part of its vector
+//     phase; the pieces' products and the reflectors follow as GEMMs).
 #include <climits>
 #include "xkv_common.h"
 #include "xkv_kernels.h"

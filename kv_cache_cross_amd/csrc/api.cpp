@@ -738,7 +738,8 @@ extern "C" int xkv_compress_sides(xkv_ctx ctx, const xkv_compress_desc* desc, in
       XKV_K(launch_ritz_rotate(d_runs, d_cs, d_groups, (const long long*)ld, (const int*)(ld + pos_off[h]), kb, kb,
                                hf.w.Zseg, kk, hf.w.Zsegs, ritz_scratch_doubles(kb, kb), P * hf.cnt, st));
       // side i's piece q at Zseg + (i P + q) k_b^2; the products alternate between Z (ld r) and
-      // piece 0's memory (ld r once piece 0 has been read), ending in Z
+      // piece 0's memory (ld r once piece 0 has been read), ending in Z.  P is 2 or 4, so the
+      // first product, which reads piece 0, writes Z.
       const long sP = (long)P * kk;
       const double* in = hf.w.Zseg;
       long ld_in = kb, s_in = sP;
